@@ -1,0 +1,219 @@
+"""CPU oracle for decode attention over a KV cache -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never imports, links
+or calls it, and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, two-pass softmax; see
+its header for the passages of the pages each function follows).  This
+module only builds it with gcc and marshals numpy arrays into it.
+
+Every function here has a pin in ``tests/test_oracle_*.py`` (printed values
+of the pages, closed forms, invariants, torch's library attention on small
+inputs); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def threads() -> int:
+    """Threads OpenMP will use for the oracle's row loop."""
+    n = os.environ.get("OMP_NUM_THREADS")
+    return int(n) if n else (os.cpu_count() or 1)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = C.CDLL(_LIB)
+        P, I, D = C.c_void_p, C.c_int, C.c_double
+        lib.ref_kv_cell_bytes.restype = C.c_ulonglong
+        lib.ref_kv_cell_bytes.argtypes = [I, I, I, I]
+        lib.ref_mla_cell_bytes.restype = C.c_ulonglong
+        lib.ref_mla_cell_bytes.argtypes = [I, I, I, I]
+        lib.ref_gqa_decode.restype = I
+        lib.ref_gqa_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, D]
+        lib.ref_mla_absorbed.restype = I
+        lib.ref_mla_absorbed.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                         I, I, I, D]
+        lib.ref_mla_explicit.restype = I
+        lib.ref_mla_explicit.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                         I, I, D]
+        lib.ref_kv_append.restype = I
+        lib.ref_kv_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _stored(a: np.ndarray, b: int) -> np.ndarray:
+    want = np.uint16 if b == 2 else np.float32
+    if a.dtype != want:
+        raise TypeError(f"expected stored dtype {want} for b={b}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _check_table(block_table, n_rows, block_size, s):
+    """Host-side guard: every mapped block id must be inside the pool."""
+    if block_table is None:
+        return
+    for bi, n in enumerate(s):
+        nb = (int(n) + block_size - 1) // block_size
+        ids = block_table[bi, :nb]
+        if nb and (ids.min() < 0 or ids.max() * block_size >= n_rows):
+            raise ValueError(f"block table row {bi} maps outside the pool")
+
+
+def kv_cell_bytes(L: int, h_kv: int, d_h: int, b: int) -> int:
+    """Bytes per token over all layers: 2 * L * h_kv * d_h * b."""
+    return int(_load().ref_kv_cell_bytes(L, h_kv, d_h, b))
+
+
+def mla_cell_bytes(L: int, d_c: int, d_R: int, b: int) -> int:
+    """Bytes per token over all layers for an MLA latent cache: L * (d_c + d_R) * b."""
+    return int(_load().ref_mla_cell_bytes(L, d_c, d_R, b))
+
+
+def gqa_decode(q, K, V, s, b, block_table=None, block_size=16, scale=None):
+    """Reference decode attention (MHA / GQA / MQA).
+
+    q [B,h,d_h]; K, V [B,s_max,h_kv,d_h] (contiguous) or
+    [N_blk,block_size,h_kv,d_h] with block_table [B,max_blocks]; s [B].
+    Arrays hold stored bits (uint16 bf16 or float32).  Returns (out [B,h,d_h]
+    float64, lse [B,h] float64).
+    """
+    q, K, V = _stored(q, b), _stored(K, b), _stored(V, b)
+    B, h, d_h = q.shape
+    h_kv = K.shape[2]
+    s = _i32(s)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max = K.shape[1]
+        max_blocks, bs = 0, 0
+    else:
+        s_max = 0
+        max_blocks, bs = bt.shape[1], block_size
+        _check_table(bt, K.shape[0] * K.shape[1], bs, s)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    out = np.zeros((B, h, d_h), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    rc = _load().ref_gqa_decode(_ptr(out), _ptr(lse), _ptr(q), _ptr(K), _ptr(V), _ptr(s),
+                                _ptr(bt), max_blocks, bs, B, s_max, h, h_kv, d_h, b,
+                                float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_gqa_decode rejected its arguments ({rc})")
+    return out, lse
+
+
+def _mla_args(q_nope, q_rope, w_uk, w_uv, cache, s, b, block_table, block_size):
+    q_nope, q_rope = _stored(q_nope, b), _stored(q_rope, b)
+    w_uk, w_uv, cache = _stored(w_uk, b), _stored(w_uv, b), _stored(cache, b)
+    B, h, d_nope = q_nope.shape
+    d_R = q_rope.shape[2]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    if cache.shape[-1] != d_c + d_R:
+        raise ValueError("cache row width must be d_c + d_R")
+    s = _i32(s)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max, max_blocks, bs = cache.shape[1], 0, 0
+    else:
+        s_max, max_blocks, bs = 0, bt.shape[1], block_size
+        _check_table(bt, cache.shape[0] * cache.shape[1], bs, s)
+    return q_nope, q_rope, w_uk, w_uv, cache, s, bt, B, h, d_nope, d_R, d_c, d_v, s_max, \
+        max_blocks, bs
+
+
+def mla_absorbed(q_nope, q_rope, w_uk, w_uv, cache, s, b=2, block_table=None, block_size=16,
+                 scale=None):
+    """Reference MLA decode, absorbed form.  Returns (out [B,h,d_v], u_latent [B,h,d_c], lse [B,h])."""
+    (q_nope, q_rope, w_uk, w_uv, cache, s, bt, B, h, d_nope, d_R, d_c, d_v, s_max, max_blocks,
+     bs) = _mla_args(q_nope, q_rope, w_uk, w_uv, cache, s, b, block_table, block_size)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_nope + d_R)
+    out = np.zeros((B, h, d_v), dtype=np.float64)
+    ul = np.zeros((B, h, d_c), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    rc = _load().ref_mla_absorbed(_ptr(out), _ptr(ul), _ptr(lse), _ptr(q_nope), _ptr(q_rope),
+                                  _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(s), _ptr(bt),
+                                  max_blocks, bs, B, s_max, h, d_c, d_R, d_nope, d_v, b,
+                                  float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_mla_absorbed rejected its arguments ({rc})")
+    return out, ul, lse
+
+
+def mla_explicit(q_nope, q_rope, w_uk, w_uv, cache, s, b=2, block_table=None, block_size=16,
+                 scale=None):
+    """Reference MLA decode by explicit K/V expansion.  Returns (out [B,h,d_v], lse [B,h])."""
+    (q_nope, q_rope, w_uk, w_uv, cache, s, bt, B, h, d_nope, d_R, d_c, d_v, s_max, max_blocks,
+     bs) = _mla_args(q_nope, q_rope, w_uk, w_uv, cache, s, b, block_table, block_size)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_nope + d_R)
+    out = np.zeros((B, h, d_v), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    rc = _load().ref_mla_explicit(_ptr(out), _ptr(lse), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                  _ptr(w_uv), _ptr(cache), _ptr(s), _ptr(bt), max_blocks, bs, B,
+                                  s_max, h, d_c, d_R, d_nope, d_v, b, float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_mla_explicit rejected its arguments ({rc})")
+    return out, lse
+
+
+def kv_append(cache_k, cache_v, k_new, v_new, pos, b, block_table=None, block_size=16):
+    """Reference append on host images (copies; inputs are not modified).
+
+    cache_k/cache_v: [B,s_max,h_kv,d_h] or paged [N_blk,block_size,h_kv,d_h]
+    (cache_v / v_new may be None for an MLA latent buffer, h_kv = 1).
+    Returns the updated (cache_k, cache_v).
+    """
+    ck = _stored(cache_k, b).copy()
+    cv = None if cache_v is None else _stored(cache_v, b).copy()
+    kn = _stored(k_new, b)
+    vn = None if v_new is None else _stored(v_new, b)
+    B, h_kv, d_h = kn.shape
+    pos = _i32(pos)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max, max_blocks, bs = ck.shape[1], 0, 0
+    else:
+        s_max, max_blocks, bs = 0, bt.shape[1], block_size
+        _check_table(bt, ck.shape[0] * ck.shape[1], bs, [int(p) + 1 for p in pos])
+    rc = _load().ref_kv_append(_ptr(ck), _ptr(cv), _ptr(kn), _ptr(vn), _ptr(pos), _ptr(bt),
+                               max_blocks, bs, B, s_max, h_kv, d_h, b)
+    if rc != 0:
+        raise ValueError(f"ref_kv_append rejected its arguments ({rc})")
+    return ck, cv

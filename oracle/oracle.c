@@ -1,0 +1,365 @@
+/*
+ * Plain CPU oracle for single-token decode attention over a stored KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously correct
+ * definition that the HIP library is checked against.  Only the tests, the
+ * smoke check and the benchmark's CPU-baseline leg may load it; the library
+ * never does.  It shares no code, header or table with the HIP path.
+ *
+ * Arithmetic: every stored element (bf16 bits or fp32) is widened exactly to
+ * double; all sums, the softmax and the final division are in double.  The
+ * softmax is two-pass (maximum first, then exponentials), not online.
+ * OpenMP splits only the independent output rows (b, i); the arithmetic of a
+ * row is the plain sequential loop.
+ *
+ * Sources (cited by page title and section):
+ *  - "The KV cache size formula" (mlinterviewnotes.com): attention at decode
+ *    computes softmax(q K^T / sqrt(d_h)) V over all previous positions; the
+ *    per-token cell 2 * L * h_kv * d_h * b; the MLA cell L * (d_c + d_R) * b
+ *    ("Where MLA breaks the formula"); token-major K/V buffers
+ *    [rows, h_kv, d_h] and one latent buffer [rows, 1, d_c + d_R] (listing
+ *    under "SGLang: one cell size, one division"); 16-token pages
+ *    ("vLLM: a per-layer page, then integer division").
+ *  - "MHA -> MQA -> GQA -> MLA" (mlinterviewnotes.com), opening section:
+ *    query heads are broadcast against the h_kv shared KV heads; MHA, MQA,
+ *    GQA are h_kv = h, 1, h/g.
+ *  - "Multi-Head Latent Attention (MLA): Mathematical Foundations ..."
+ *    (llms.blog): sections "Attention Logit Matrix Absorption" (absorbed
+ *    query q~ = W_UK,i^T q^C and score q~^T c + q^R^T k^R) and "Value Output
+ *    Matrix Absorption" (softmax scale 1/sqrt(d_h^C + d_r), latent sum
+ *    u~ = sum_j A_j c_j, deferred u = W_UV,i u~); "Low-Rank Joint Key-Value
+ *    Compression" for the explicit k^C = W_UK c, v^C = W_UV c.
+ *  - "MLA: why one latent can replace a multi-head KV cache"
+ *    (charlestar.github.io): "First matrix absorption", "Second matrix
+ *    absorption", "What a paged KV cache block holds" (row = [c_KV | k_R]),
+ *    "Correctness validation ..." (explicit expansion as the slow reference).
+ *
+ * Readings where the pages are silent (listed again in the design notes):
+ *  - query head i uses KV head floor(i / g) (consecutive heads share);
+ *  - MLA weights are per-head slices W_UK[i] : [d_nope, d_c] and
+ *    W_UV[i] : [d_v, d_c]; the MLA scale is 1/sqrt(d_nope + d_R);
+ *  - s_b = 0 gives an all-zero output row and lse = -inf;
+ *  - paged token t of sequence b lives in physical row
+ *    block_table[b][t / block_size] * block_size + t % block_size.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+
+/* widen one stored element to double; b = 2 -> bf16 bits, b = 4 -> fp32 */
+static double ld(const void* p, size_t idx, int b)
+{
+    if (b == 4) return (double)((const float*)p)[idx];
+    uint32_t bits = ((uint32_t)((const uint16_t*)p)[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* physical row of token t of sequence bb */
+static size_t row_of(const int32_t* bt, int max_blocks, int block_size, int s_max,
+                     int bb, int t)
+{
+    if (!bt) return (size_t)bb * (size_t)s_max + (size_t)t;
+    int blk = bt[(size_t)bb * (size_t)max_blocks + (size_t)(t / block_size)];
+    return (size_t)blk * (size_t)block_size + (size_t)(t % block_size);
+}
+
+unsigned long long ref_kv_cell_bytes(int L, int h_kv, int d_h, int b)
+{
+    return 2ULL * (unsigned long long)L * (unsigned long long)h_kv *
+           (unsigned long long)d_h * (unsigned long long)b;
+}
+
+unsigned long long ref_mla_cell_bytes(int L, int d_c, int d_R, int b)
+{
+    return (unsigned long long)L * ((unsigned long long)d_c + (unsigned long long)d_R) *
+           (unsigned long long)b;
+}
+
+/* every logical block a sequence of n tokens touches must be mapped */
+static int table_ok(const int32_t* bt, int max_blocks, int block_size, int bb, int n)
+{
+    if (!bt) return 1;
+    for (int blk = 0; blk * block_size < n; blk++)
+        if (bt[(size_t)bb * (size_t)max_blocks + (size_t)blk] < 0) return 0;
+    return 1;
+}
+
+/* Two-pass softmax-weighted sum over n scores z[]: writes p[t] = exp(z_t - m)
+ * and returns l = sum p; *m_out = max z. */
+static double softmax_weights(const double* z, int n, double* p, double* m_out)
+{
+    double m = -INFINITY;
+    for (int t = 0; t < n; t++)
+        if (z[t] > m) m = z[t];
+    double l = 0.0;
+    for (int t = 0; t < n; t++) {
+        p[t] = exp(z[t] - m);
+        l += p[t];
+    }
+    *m_out = m;
+    return l;
+}
+
+/*
+ * GQA / MQA / MHA decode.
+ *   out [B, h, d_h] double, lse [B, h] double (nullable)
+ *   q   [B, h, d_h]            stored dtype b
+ *   k,v [B, s_max, h_kv, d_h]  (block_table == NULL)  or
+ *       [N_blk, block_size, h_kv, d_h]                 (paged)
+ *   s   [B] host lengths
+ * z_t = scale * sum_d q[b,i,d] K(b,t,j,d), j = floor(i / g);
+ * o = sum_t softmax(z)_t V(b,t,j,:);  lse = m + ln(sum_t exp(z_t - m)).
+ */
+int ref_gqa_decode(double* out, double* lse, const void* q, const void* k, const void* v,
+                   const int32_t* s, const int32_t* block_table, int max_blocks,
+                   int block_size, int B, int s_max, int h, int h_kv, int d_h, int b,
+                   double scale)
+{
+    if (!out || !q || !k || !v || !s) return OR_EINVAL;
+    if (B < 0 || h <= 0 || h_kv <= 0 || d_h <= 0 || (h % h_kv) != 0) return OR_EINVAL;
+    if (b != 2 && b != 4) return OR_EINVAL;
+    if (block_table && (block_size <= 0 || max_blocks <= 0)) return OR_EINVAL;
+    const int g = h / h_kv;
+    const long rows = (long)B * h;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long r = 0; r < rows; r++) {
+        const int bb = (int)(r / h), i = (int)(r % h), j = i / g;
+        const int n = s[bb];
+        double* o = out + (size_t)r * d_h;
+        if (n < 0 || (!block_table && n > s_max) ||
+            (block_table && n > max_blocks * block_size) ||
+            !table_ok(block_table, max_blocks, block_size, bb, n)) {
+            bad = 1;
+            continue;
+        }
+        if (n == 0) {
+            for (int d = 0; d < d_h; d++) o[d] = 0.0;
+            if (lse) lse[r] = -INFINITY;
+            continue;
+        }
+        double* z = (double*)malloc(sizeof(double) * (size_t)n * 2);
+        double* p = z + n;
+        const size_t qoff = (size_t)r * d_h;
+        for (int t = 0; t < n; t++) {
+            const size_t koff =
+                (row_of(block_table, max_blocks, block_size, s_max, bb, t) * h_kv + j) * d_h;
+            double acc = 0.0;
+            for (int d = 0; d < d_h; d++) acc += ld(q, qoff + d, b) * ld(k, koff + d, b);
+            z[t] = scale * acc;
+        }
+        double m;
+        const double l = softmax_weights(z, n, p, &m);
+        for (int d = 0; d < d_h; d++) {
+            double acc = 0.0;
+            for (int t = 0; t < n; t++) {
+                const size_t voff =
+                    (row_of(block_table, max_blocks, block_size, s_max, bb, t) * h_kv + j) *
+                    d_h;
+                acc += p[t] * ld(v, voff + d, b);
+            }
+            o[d] = acc / l;
+        }
+        if (lse) lse[r] = m + log(l);
+        free(z);
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/*
+ * MLA decode in the absorbed ("MQA mode") form.
+ *   out [B, h, d_v] double; u_latent [B, h, d_c] double (nullable);
+ *   lse [B, h] double (nullable)
+ *   q_nope [B, h, d_nope], q_rope [B, h, d_R] (already rotated)
+ *   w_uk [h, d_nope, d_c], w_uv [h, d_v, d_c]
+ *   cache rows [c (d_c) | k_R (d_R)]: [B, s_max, d_c + d_R] or paged
+ *   [N_blk, block_size, d_c + d_R]
+ * Steps in the pages' order: q~ = W_UK,i^T q^C; score_t = q~ . c_t +
+ * q^R . k^R_t; A = softmax(scale * score); u~ = sum_t A_t c_t;
+ * o = W_UV,i u~.
+ */
+int ref_mla_absorbed(double* out, double* u_latent, double* lse, const void* q_nope,
+                     const void* q_rope, const void* w_uk, const void* w_uv,
+                     const void* cache, const int32_t* s, const int32_t* block_table,
+                     int max_blocks, int block_size, int B, int s_max, int h, int d_c,
+                     int d_R, int d_nope, int d_v, int b, double scale)
+{
+    if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s) return OR_EINVAL;
+    if (B < 0 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0) return OR_EINVAL;
+    if (b != 2 && b != 4) return OR_EINVAL;
+    if (block_table && (block_size <= 0 || max_blocks <= 0)) return OR_EINVAL;
+    const int W = d_c + d_R;
+    const long rows = (long)B * h;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long r = 0; r < rows; r++) {
+        const int bb = (int)(r / h), i = (int)(r % h);
+        const int n = s[bb];
+        double* o = out + (size_t)r * d_v;
+        if (n < 0 || (!block_table && n > s_max) ||
+            (block_table && n > max_blocks * block_size) ||
+            !table_ok(block_table, max_blocks, block_size, bb, n)) {
+            bad = 1;
+            continue;
+        }
+        double* qt = (double*)malloc(sizeof(double) * ((size_t)d_c * 2 + (size_t)n * 2));
+        double* ut = qt + d_c;
+        double* z = ut + d_c;
+        double* p = z + n;
+        /* absorbed query: q~[c] = sum_n W_UK[i][n][c] q_nope[n] */
+        for (int c = 0; c < d_c; c++) {
+            double acc = 0.0;
+            for (int e = 0; e < d_nope; e++)
+                acc += ld(w_uk, ((size_t)i * d_nope + e) * d_c + c, b) *
+                       ld(q_nope, (size_t)r * d_nope + e, b);
+            qt[c] = acc;
+        }
+        if (n == 0) {
+            for (int c = 0; c < d_c; c++) ut[c] = 0.0;
+            if (lse) lse[r] = -INFINITY;
+        } else {
+            /* scores over the latent and the decoupled RoPE key */
+            for (int t = 0; t < n; t++) {
+                const size_t roff =
+                    row_of(block_table, max_blocks, block_size, s_max, bb, t) * W;
+                double acc = 0.0;
+                for (int c = 0; c < d_c; c++) acc += qt[c] * ld(cache, roff + c, b);
+                double accr = 0.0;
+                for (int e = 0; e < d_R; e++)
+                    accr += ld(q_rope, (size_t)r * d_R + e, b) * ld(cache, roff + d_c + e, b);
+                z[t] = scale * (acc + accr);
+            }
+            double m;
+            const double l = softmax_weights(z, n, p, &m);
+            /* latent weighted sum u~ = sum_t A_t c_t */
+            for (int c = 0; c < d_c; c++) {
+                double acc = 0.0;
+                for (int t = 0; t < n; t++) {
+                    const size_t roff =
+                        row_of(block_table, max_blocks, block_size, s_max, bb, t) * W;
+                    acc += p[t] * ld(cache, roff + c, b);
+                }
+                ut[c] = acc / l;
+            }
+            if (lse) lse[r] = m + log(l);
+        }
+        if (u_latent)
+            for (int c = 0; c < d_c; c++) u_latent[(size_t)r * d_c + c] = ut[c];
+        /* deferred value up-projection o = W_UV[i] u~ */
+        for (int e = 0; e < d_v; e++) {
+            double acc = 0.0;
+            for (int c = 0; c < d_c; c++)
+                acc += ld(w_uv, ((size_t)i * d_v + e) * d_c + c, b) * ut[c];
+            o[e] = acc;
+        }
+        free(qt);
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/*
+ * MLA decode by explicit expansion ("MHA mode"): per head and token build
+ * k_t = [W_UK[i] c_t ; k_R,t] and v_t = W_UV[i] c_t, then plain attention
+ * with q = [q_nope ; q_rope].  Slow reference for the absorption identities.
+ */
+int ref_mla_explicit(double* out, double* lse, const void* q_nope, const void* q_rope,
+                     const void* w_uk, const void* w_uv, const void* cache, const int32_t* s,
+                     const int32_t* block_table, int max_blocks, int block_size, int B,
+                     int s_max, int h, int d_c, int d_R, int d_nope, int d_v, int b,
+                     double scale)
+{
+    if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s) return OR_EINVAL;
+    if (B < 0 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0) return OR_EINVAL;
+    if (b != 2 && b != 4) return OR_EINVAL;
+    if (block_table && (block_size <= 0 || max_blocks <= 0)) return OR_EINVAL;
+    const int W = d_c + d_R;
+    const long rows = (long)B * h;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long r = 0; r < rows; r++) {
+        const int bb = (int)(r / h), i = (int)(r % h);
+        const int n = s[bb];
+        double* o = out + (size_t)r * d_v;
+        if (n < 0 || (!block_table && n > s_max) ||
+            (block_table && n > max_blocks * block_size) ||
+            !table_ok(block_table, max_blocks, block_size, bb, n)) {
+            bad = 1;
+            continue;
+        }
+        if (n == 0) {
+            for (int e = 0; e < d_v; e++) o[e] = 0.0;
+            if (lse) lse[r] = -INFINITY;
+            continue;
+        }
+        double* kc = (double*)malloc(sizeof(double) *
+                                     ((size_t)n * d_nope + (size_t)n * d_v + (size_t)n * 2));
+        double* vc = kc + (size_t)n * d_nope;
+        double* z = vc + (size_t)n * d_v;
+        double* p = z + n;
+        for (int t = 0; t < n; t++) {
+            const size_t roff = row_of(block_table, max_blocks, block_size, s_max, bb, t) * W;
+            for (int e = 0; e < d_nope; e++) {
+                double acc = 0.0;
+                for (int c = 0; c < d_c; c++)
+                    acc += ld(w_uk, ((size_t)i * d_nope + e) * d_c + c, b) * ld(cache, roff + c, b);
+                kc[(size_t)t * d_nope + e] = acc;
+            }
+            for (int e = 0; e < d_v; e++) {
+                double acc = 0.0;
+                for (int c = 0; c < d_c; c++)
+                    acc += ld(w_uv, ((size_t)i * d_v + e) * d_c + c, b) * ld(cache, roff + c, b);
+                vc[(size_t)t * d_v + e] = acc;
+            }
+            double acc = 0.0;
+            for (int e = 0; e < d_nope; e++)
+                acc += ld(q_nope, (size_t)r * d_nope + e, b) * kc[(size_t)t * d_nope + e];
+            for (int e = 0; e < d_R; e++)
+                acc += ld(q_rope, (size_t)r * d_R + e, b) * ld(cache, roff + d_c + e, b);
+            z[t] = scale * acc;
+        }
+        double m;
+        const double l = softmax_weights(z, n, p, &m);
+        for (int e = 0; e < d_v; e++) {
+            double acc = 0.0;
+            for (int t = 0; t < n; t++) acc += p[t] * vc[(size_t)t * d_v + e];
+            o[e] = acc / l;
+        }
+        if (lse) lse[r] = m + log(l);
+        free(kc);
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/*
+ * Cache append: copy the new token's rows into a host image of the cache at
+ * slot pos[b] (contiguous row b * s_max + pos[b], or the paged row through
+ * the block table).  cache_v / v_new may be NULL (MLA: one latent buffer,
+ * no V).  Row width is h_kv * d_h elements of b bytes.
+ */
+int ref_kv_append(void* cache_k, void* cache_v, const void* k_new, const void* v_new,
+                  const int32_t* pos, const int32_t* block_table, int max_blocks,
+                  int block_size, int B, int s_max, int h_kv, int d_h, int b)
+{
+    if (!cache_k || !k_new || !pos) return OR_EINVAL;
+    if ((cache_v == NULL) != (v_new == NULL)) return OR_EINVAL;
+    if (B < 0 || h_kv <= 0 || d_h <= 0 || (b != 2 && b != 4)) return OR_EINVAL;
+    const size_t rb = (size_t)h_kv * d_h * b;
+    for (int bb = 0; bb < B; bb++) {
+        const int t = pos[bb];
+        if (t < 0 || (!block_table && t >= s_max) ||
+            (block_table && t >= max_blocks * block_size))
+            return OR_EINVAL;
+        if (block_table && block_table[(size_t)bb * max_blocks + t / block_size] < 0)
+            return OR_EINVAL;
+        const size_t row = row_of(block_table, max_blocks, block_size, s_max, bb, t);
+        memcpy((char*)cache_k + row * rb, (const char*)k_new + (size_t)bb * rb, rb);
+        if (cache_v) memcpy((char*)cache_v + row * rb, (const char*)v_new + (size_t)bb * rb, rb);
+    }
+    return OR_OK;
+}

@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+One step = one attention call over the whole batch for one layer (the
+decode kernel plus, when the context is split, its merge kernel).  The
+headline workload is the Llama-3-8B-shaped GQA layer (B=64, h=32, h_kv=8,
+d_h=128, every s_i = 4096, bf16); the DeepSeek-V3-shaped absorbed MLA layer
+(B=32, h=128, d_c=512, d_R=64, s=8192) is measured in the same run and
+reported under "mla".  Inputs are synthetic (seeded N(0,1)) and resident in
+HBM before timing starts.
+
+Prints ONE JSON line.  --gpus N with N > 1 is refused: this build measures
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn steps/s + achieved HBM GB/s (% of peak), GQA-8 and MLA, 1 GPU"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+
+
+def gqa_alg_bytes(sh):
+    """K+V of every cached token plus q and out (bytes per call)."""
+    return 2 * sum(sh.s) * sh.h_kv * sh.d_h * sh.b + 2 * sh.B * sh.h * sh.d_h * sh.b
+
+
+def gqa_flops(sh):
+    return 4 * sh.h * sh.d_h * sum(sh.s)
+
+
+def mla_alg_bytes(sh):
+    """Latent rows + W_UK + W_UV + q_nope, q_rope, out (bytes per call)."""
+    return (sum(sh.s) * (sh.d_c + sh.d_R) * sh.b + sh.h * (sh.d_nope + sh.d_v) * sh.d_c * sh.b
+            + sh.B * sh.h * (sh.d_nope + sh.d_R + sh.d_v) * sh.b)
+
+
+def mla_flops(sh):
+    return (2 * sh.h * sum(sh.s) * (2 * sh.d_c + sh.d_R)
+            + 2 * sh.B * sh.h * sh.d_c * (sh.d_nope + sh.d_v))
+
+
+def time_calls(fn, steps, warmup, stream):
+    """Run warmup calls, then time `steps` calls: total (events around all)
+    and per-call durations (an event pair around each call, same stream)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+    return total_ms, per
+
+
+def run_gqa(name, steps, warmup, rotate, keep=None):
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = synth.configs()[name]
+    dev = "cuda"
+    sets = [synth.draw_gqa(sh, device=dev, seed=sh.seed + 1000 * r) for r in range(rotate)]
+    out = torch.empty_like(sets[0]["q"])
+    lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device=dev)
+    wsb = A.attn_decode_workspace_bytes(0, sh.B, sh.s_max, sh.h, sh.h_kv, sh.d_h)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    it = [0]
+
+    def call():
+        d = sets[it[0] % rotate]
+        it[0] += 1
+        bt = d.get("block_table")
+        A.attn_decode_gqa(out, lse, d["q"], d["K"], d["V"], d["s"], bt,
+                          0 if bt is None else bt.shape[1], sh.block_size,
+                          0 if bt is None else d["K"].shape[0], sh.B, sh.s_max, sh.h, sh.h_kv,
+                          sh.d_h, sh.b, 0.0, ws, wsb, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    if keep is not None:
+        keep.append(sets[0])
+    return sh, total_ms, per
+
+
+def run_mla(name, steps, warmup, rotate):
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = synth.configs()[name]
+    dev = "cuda"
+    sets = [synth.draw_mla(sh, device=dev, seed=sh.seed + 1000 * r) for r in range(rotate)]
+    out = torch.empty((sh.B, sh.h, sh.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device=dev)
+    wsb = A.attn_decode_workspace_bytes(1, sh.B, sh.s_max, sh.h, 1, sh.d_c, sh.d_R)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    it = [0]
+
+    def call():
+        d = sets[it[0] % rotate]
+        it[0] += 1
+        bt = d.get("block_table")
+        A.attn_decode_mla_absorbed(out, None, lse, d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"],
+                                   d["cache"], d["s"], bt, 0 if bt is None else bt.shape[1],
+                                   sh.block_size, 0 if bt is None else d["cache"].shape[0], sh.B,
+                                   sh.s_max, sh.h, sh.d_c, sh.d_R, sh.d_nope, sh.d_v, 2, 0.0, ws,
+                                   wsb, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    return sh, total_ms, per
+
+
+def cpu_baseline_gqa(sh, d, budget_s=15.0):
+    """Time the oracle (as it stands) on a bounded sample of the same inputs:
+    the first Bs sequences of the batch (all heads, all s_i tokens), copied
+    from the device.  Bs grows until about budget_s of CPU work; the time is
+    scaled to the full batch."""
+    import oracle
+    import synth
+
+    def run(bs):
+        q = synth.host_bits(d["q"][:bs])
+        K = synth.host_bits(d["K"][:bs])
+        V = synth.host_bits(d["V"][:bs])
+        s = d["s_host"][:bs]
+        t0 = time.perf_counter()
+        oracle.gqa_decode(q, K, V, s, sh.b)
+        return time.perf_counter() - t0
+
+    run(1)                                    # page-in, thread pool start
+    bs, dt = 1, run(1)
+    if dt < budget_s / 2 and sh.B > 1:
+        bs = int(min(sh.B, max(2, budget_s / max(dt, 1e-3))))
+        dt = run(bs)
+    step_s = dt * sh.B / bs
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{bs} of {sh.B} sequences (all {sh.h} heads x {sh.s[0]} tokens), "
+                      f"{dt:.1f} s, scaled to the full batch"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama3_8b_gqa")
+    ap.add_argument("--mla-config", default="deepseek_v3_mla")
+    ap.add_argument("--no-mla", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import decode_attention_kv_attn_amd as A
+    A.lib()
+
+    kept = []
+    sh, total_ms, per = run_gqa(args.config, args.steps, args.warmup, rotate=1, keep=kept)
+    ms = total_ms / args.steps
+    call_ms = float(np.mean(per))
+    ab = gqa_alg_bytes(sh)
+    achieved = ab / (call_ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": 1000.0 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{sh.name}: GQA decode layer B={sh.B} h={sh.h} h_kv={sh.h_kv} "
+                               f"d_h={sh.d_h} s_i={sh.s[0]} bf16 (Llama-3-8B shape)",
+                   "B": sh.B, "h": sh.h, "h_kv": sh.h_kv, "d_h": sh.d_h, "s": sh.s[0]},
+        "hbm_gbps": ab / (ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "attention call (gqa_decode_kernel + gqa_combine_kernel)",
+                     "alg_bytes_per_call": ab, "avg_call_us": call_ms * 1e3},
+    }
+    if not args.no_mla:
+        try:
+            msh, mtot, mper = run_mla(args.mla_config, args.steps, args.warmup, rotate=4)
+            mms = mtot / args.steps
+            mcall = float(np.mean(mper))
+            mab = mla_alg_bytes(msh)
+            mfl = mla_flops(msh)
+            gbps = mab / (mcall * 1e-3) / 1e9
+            tfl = mfl / (mcall * 1e-3) / 1e12
+            floor_s = max(mab / (HBM_PEAK_GBPS * 1e9), mfl / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+            rec["mla"] = {"workload": f"{msh.name}: MLA absorbed decode B={msh.B} h={msh.h} "
+                                      f"d_c={msh.d_c} d_R={msh.d_R} s={msh.s[0]} bf16",
+                          "steps_per_s": 1000.0 / mms, "ms_per_step": mms,
+                          "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+                          "mfma_tflops": tfl, "mfma_frac": tfl / MFMA_BF16_PEAK_TFLOPS,
+                          "roofline_frac": floor_s / (mcall * 1e-3),
+                          "alg_bytes_per_call": mab, "flops_per_call": mfl}
+        except Exception as e:  # MLA path reports its own failure, GQA line still prints
+            rec["mla"] = {"error": str(e)[:200]}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_gqa(sh, kept[0], args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+"""Python binding of libattn_decode.so, the MI355X decode-attention library.
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name declared in include/attn_decode.h (torch tensors become device
+pointers, None becomes NULL, the stream defaults to torch's current stream).
+All the computation runs in the library's HIP kernels; there is no fallback.
+If the shared library has not been built this module raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_decode.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_ENOTSUP, ATTN_EWORKSPACE, ATTN_EHIP = 0, -1, -2, -3, -4
+
+EXPORTED = (
+    "attn_kv_cell_bytes",
+    "attn_mla_cell_bytes",
+    "attn_decode_workspace_bytes",
+    "attn_last_error",
+    "kv_cache_append",
+    "attn_decode_gqa",
+    "attn_decode_mla_absorbed",
+)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"status {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() "
+                              "(or python -m decode_attention_kv_attn_amd.build) first")
+        L = C.CDLL(LIB_PATH)
+        P, I, F, Z = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+        L.attn_kv_cell_bytes.restype = Z
+        L.attn_kv_cell_bytes.argtypes = [I, I, I, I]
+        L.attn_mla_cell_bytes.restype = Z
+        L.attn_mla_cell_bytes.argtypes = [I, I, I, I]
+        L.attn_decode_workspace_bytes.restype = Z
+        L.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.attn_last_error.restype = C.c_char_p
+        L.attn_last_error.argtypes = []
+        L.kv_cache_append.restype = I
+        L.kv_cache_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+        L.attn_decode_gqa.restype = I
+        L.attn_decode_gqa.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, Z, P]
+        L.attn_decode_mla_absorbed.restype = I
+        L.attn_decode_mla_absorbed.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                               I, I, I, I, F, P, Z, P]
+        _lib = L
+    return _lib
+
+
+def _p(x):
+    """torch tensor / int address / None -> void*."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc):
+    if rc != ATTN_OK:
+        raise AttnError(rc, lib().attn_last_error().decode())
+    return rc
+
+
+def attn_kv_cell_bytes(L, h_kv, d_h, b):
+    return int(lib().attn_kv_cell_bytes(L, h_kv, d_h, b))
+
+
+def attn_mla_cell_bytes(L, d_c, d_R, b):
+    return int(lib().attn_mla_cell_bytes(L, d_c, d_R, b))
+
+
+def attn_decode_workspace_bytes(is_mla, B, s_max, h, h_kv, d_h_or_dc, d_R=0):
+    return int(lib().attn_decode_workspace_bytes(int(is_mla), B, s_max, h, h_kv, d_h_or_dc, d_R))
+
+
+def attn_last_error():
+    return lib().attn_last_error().decode()
+
+
+def kv_cache_append(cache_k, cache_v, k_new, v_new, pos, block_table, max_blocks, block_size,
+                    num_blocks, B, s_max, h_kv, d_h, b, stream=None, check=True):
+    rc = lib().kv_cache_append(_p(cache_k), _p(cache_v), _p(k_new), _p(v_new), _p(pos),
+                               _p(block_table), max_blocks, block_size, num_blocks, B, s_max,
+                               h_kv, d_h, b, _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
+                    num_blocks, B, s_max, h, h_kv, d_h, b, scale, workspace, workspace_bytes,
+                    stream=None, check=True):
+    rc = lib().attn_decode_gqa(_p(out), _p(lse), _p(q), _p(cache_k), _p(cache_v), _p(s),
+                               _p(block_table), max_blocks, block_size, num_blocks, B, s_max, h,
+                               h_kv, d_h, b, float(scale), _p(workspace), int(workspace_bytes),
+                               _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_mla_absorbed(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, s,
+                             block_table, max_blocks, block_size, num_blocks, B, s_max, h, d_c,
+                             d_R, d_nope, d_v, b, scale, workspace, workspace_bytes, stream=None,
+                             check=True):
+    rc = lib().attn_decode_mla_absorbed(_p(out), _p(u_latent), _p(lse), _p(q_nope), _p(q_rope),
+                                        _p(w_uk), _p(w_uv), _p(cache), _p(s), _p(block_table),
+                                        max_blocks, block_size, num_blocks, B, s_max, h, d_c,
+                                        d_R, d_nope, d_v, b, float(scale), _p(workspace),
+                                        int(workspace_bytes), _stream(stream))
+    return _check(rc) if check else rc
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrappers over torch tensors (shape bookkeeping only; they call
+# the entry points above).
+# ---------------------------------------------------------------------------
+class Workspace:
+    """A reusable device workspace (grown on demand)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        import torch
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf, self.buf.numel()
+
+
+def decode_gqa(q, K, V, s, block_table=None, block_size=16, s_max=None, scale=0.0, lse=True,
+               workspace=None, out=None, stream=None):
+    """q [B,h,d_h]; K,V [B,s_max,h_kv,d_h] or paged pools; s [B] int32 (device)."""
+    import torch
+    B, h, d_h = q.shape
+    h_kv = K.shape[2]
+    b = q.element_size()
+    if block_table is None:
+        s_max = K.shape[1] if s_max is None else s_max
+        max_blocks, num_blocks = 0, 0
+    else:
+        max_blocks = block_table.shape[1]
+        num_blocks = K.shape[0]
+        s_max = max_blocks * block_size if s_max is None else s_max
+    if out is None:
+        out = torch.empty_like(q)
+    l = torch.empty((B, h), dtype=torch.float32, device=q.device) if lse else None
+    ws = workspace or Workspace(q.device)
+    wb, wn = ws.get(attn_decode_workspace_bytes(0, B, s_max, h, h_kv, d_h))
+    attn_decode_gqa(out, l, q, K, V, s, block_table, max_blocks, block_size, num_blocks, B, s_max,
+                    h, h_kv, d_h, b, scale, wb, wn, stream)
+    return out, l
+
+
+def decode_mla(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_size=16,
+               s_max=None, scale=0.0, want_latent=True, workspace=None, stream=None):
+    """Absorbed MLA decode; cache rows [c | k_R] of width d_c + d_R."""
+    import torch
+    B, h, d_nope = q_nope.shape
+    d_R = q_rope.shape[2]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    if block_table is None:
+        s_max = cache.shape[1] if s_max is None else s_max
+        max_blocks, num_blocks = 0, 0
+    else:
+        max_blocks = block_table.shape[1]
+        num_blocks = cache.shape[0]
+        s_max = max_blocks * block_size if s_max is None else s_max
+    out = torch.empty((B, h, d_v), dtype=q_nope.dtype, device=q_nope.device)
+    ul = torch.empty((B, h, d_c), dtype=torch.float32, device=q_nope.device) if want_latent else None
+    l = torch.empty((B, h), dtype=torch.float32, device=q_nope.device)
+    ws = workspace or Workspace(q_nope.device)
+    wb, wn = ws.get(attn_decode_workspace_bytes(1, B, s_max, h, 1, d_c, d_R))
+    attn_decode_mla_absorbed(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache, s, block_table,
+                             max_blocks, block_size, num_blocks, B, s_max, h, d_c, d_R, d_nope,
+                             d_v, 2, scale, wb, wn, stream)
+    return out, ul, l
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

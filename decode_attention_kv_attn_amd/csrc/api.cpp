@@ -1,0 +1,298 @@
+// Host side of the C ABI declared in include/attn_decode.h: argument checks,
+// the split plan, workspace carving and kernel launches.  No allocation, no
+// global state except the thread-local error message.
+#include "attn_decode.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err = "no error";
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int x)
+{
+    int r = 0;
+    while ((1 << r) < x) r++;
+    return r;
+}
+long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- GQA split plan ---------------------------------------------------------
+// Work item = (b, KV head, group of HG query heads, token split).  HG is the
+// largest of 8, 4, 2, 1 dividing g.  Splits are added until about 2048
+// wavefronts are in flight (8 per CU on 256 CUs), but no split is shorter
+// than 256 tokens; split lengths are multiples of the 64-token tile.
+struct GqaPlan {
+    int HG, n_hg, n_split, chunk;
+    size_t part_o_bytes, part_ml_bytes, ws_bytes;
+};
+
+GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h)
+{
+    GqaPlan P{};
+    const int g = h / h_kv;
+    P.HG = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
+    P.n_hg = g / P.HG;
+    const long long T = 64, target = 2048, min_chunk = 256;
+    const long long units = (long long)B * h_kv * P.n_hg;
+    long long ns = units > 0 ? cdiv(target, units) : 1;
+    const long long ns_max = s_max > 0 ? cdiv(s_max, min_chunk) : 1;
+    if (ns > ns_max) ns = ns_max;
+    if (ns < 1) ns = 1;
+    long long chunk = s_max > 0 ? cdiv(cdiv(s_max, ns), T) * T : T;
+    ns = s_max > 0 ? cdiv(s_max, chunk) : 1;
+    P.n_split = (int)ns;
+    P.chunk = (int)chunk;
+    if (P.n_split > 1) {
+        P.part_o_bytes = align256((size_t)B * h * P.n_split * d_h * sizeof(float));
+        P.part_ml_bytes = align256((size_t)B * h * P.n_split * 2 * sizeof(float));
+    }
+    P.ws_bytes = P.part_o_bytes + P.part_ml_bytes;
+    return P;
+}
+
+// ---- MLA split plan -----------------------------------------------------------
+// Work item = (b, token split), all h heads together so every latent tile is
+// read once.  Aim for about 256 workgroups (one 4-wavefront group per CU),
+// splits of at least 256 tokens, multiples of the 32-token tile.
+struct MlaPlan {
+    int n_split, chunk;
+    size_t qhat_bytes, part_u_bytes, part_ml_bytes, ulat_bytes, ws_bytes;
+};
+
+MlaPlan plan_mla(int B, int s_max, int h, int d_c, int d_R)
+{
+    MlaPlan P{};
+    const long long T = 32, target = 256, min_chunk = 256;
+    long long ns = B > 0 ? cdiv(target, B) : 1;
+    const long long ns_max = s_max > 0 ? cdiv(s_max, min_chunk) : 1;
+    if (ns > ns_max) ns = ns_max;
+    if (ns < 1) ns = 1;
+    long long chunk = s_max > 0 ? cdiv(cdiv(s_max, ns), T) * T : T;
+    ns = s_max > 0 ? cdiv(s_max, chunk) : 1;
+    P.n_split = (int)ns;
+    P.chunk = (int)chunk;
+    P.qhat_bytes = align256((size_t)B * h * (d_c + d_R) * 2);
+    P.part_u_bytes = align256((size_t)B * P.n_split * h * d_c * sizeof(float));
+    P.part_ml_bytes = align256((size_t)B * P.n_split * h * 2 * sizeof(float));
+    P.ulat_bytes = align256((size_t)B * h * d_c * sizeof(float));
+    P.ws_bytes = P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.ulat_bytes;
+    return P;
+}
+
+int check_table(const int32_t* bt, int max_blocks, int block_size, int num_blocks, int s_max)
+{
+    if (!bt) {
+        if (s_max <= 0) return fail(ATTN_EINVAL, "contiguous cache needs s_max > 0");
+        return ATTN_OK;
+    }
+    if (!pow2(block_size) || block_size < 16)
+        return fail(ATTN_EINVAL, "block_size must be a power of two >= 16 (got %d)", block_size);
+    if (max_blocks <= 0 || num_blocks <= 0)
+        return fail(ATTN_EINVAL, "paged cache needs max_blocks > 0 and num_blocks > 0");
+    if ((long long)max_blocks * block_size < s_max)
+        return fail(ATTN_EINVAL, "max_blocks * block_size (%lld) < s_max (%d)",
+                    (long long)max_blocks * block_size, s_max);
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_kv_cell_bytes(int L, int h_kv, int d_h, int b)
+{
+    if (L < 0 || h_kv < 0 || d_h < 0 || b < 0) return 0;
+    return (size_t)2 * (size_t)L * (size_t)h_kv * (size_t)d_h * (size_t)b;
+}
+
+size_t attn_mla_cell_bytes(int L, int d_c, int d_R, int b)
+{
+    if (L < 0 || d_c < 0 || d_R < 0 || b < 0) return 0;
+    return (size_t)L * ((size_t)d_c + (size_t)d_R) * (size_t)b;
+}
+
+size_t attn_decode_workspace_bytes(int is_mla, int B, int s_max, int h, int h_kv, int d_h_or_dc,
+                                   int d_R)
+{
+    if (B <= 0 || h <= 0 || s_max < 0 || d_h_or_dc <= 0) return 0;
+    if (is_mla) return plan_mla(B, s_max, h, d_h_or_dc, d_R < 0 ? 0 : d_R).ws_bytes;
+    if (h_kv <= 0 || h % h_kv != 0) return 0;
+    return plan_gqa(B, s_max, h, h_kv, d_h_or_dc).ws_bytes;
+}
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+int kv_cache_append(void* cache_k, void* cache_v, const void* k_new, const void* v_new,
+                    const int32_t* pos, const int32_t* block_table, int max_blocks,
+                    int block_size, int num_blocks, int B, int s_max, int h_kv, int d_h, int b,
+                    void* stream)
+{
+    if (!cache_k || !k_new || !pos) return fail(ATTN_EINVAL, "null cache_k, k_new or pos");
+    if ((cache_v == nullptr) != (v_new == nullptr))
+        return fail(ATTN_EINVAL, "cache_v and v_new must both be set or both be NULL");
+    if (B < 0 || h_kv <= 0 || d_h <= 0) return fail(ATTN_EINVAL, "bad sizes");
+    if (b != 2 && b != 4) return fail(ATTN_EINVAL, "b must be 2 (bf16) or 4 (fp32)");
+    int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
+    if (rc) return rc;
+    attn::AppendParams pk{};
+    pk.cache = cache_k;
+    pk.src = k_new;
+    pk.pos = pos;
+    pk.bt = block_table;
+    pk.max_blocks = max_blocks;
+    pk.bs_log2 = block_table ? ilog2(block_size) : 0;
+    pk.num_blocks = num_blocks;
+    pk.s_max = s_max;
+    pk.row_bytes = (long long)h_kv * d_h * b;
+    attn::AppendParams pv = pk;
+    pv.cache = cache_v;
+    pv.src = v_new;
+    hipError_t e = attn::launch_append(pk, cache_v ? &pv : nullptr, B, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_cache_append launch");
+    return ATTN_OK;
+}
+
+int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
+                    const void* cache_v, const int32_t* s, const int32_t* block_table,
+                    int max_blocks, int block_size, int num_blocks, int B, int s_max, int h,
+                    int h_kv, int d_h, int b, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream)
+{
+    if (!out || !q || !cache_k || !cache_v || !s)
+        return fail(ATTN_EINVAL, "null out, q, cache_k, cache_v or s");
+    if (B < 0 || h <= 0 || h_kv <= 0 || d_h <= 0 || s_max < 0)
+        return fail(ATTN_EINVAL, "bad sizes (B=%d h=%d h_kv=%d d_h=%d s_max=%d)", B, h, h_kv,
+                    d_h, s_max);
+    if (h % h_kv != 0)
+        return fail(ATTN_EINVAL, "num_heads (%d) is not divisible by num_kv_heads (%d)", h, h_kv);
+    if (b != 2 && b != 4) return fail(ATTN_EINVAL, "b must be 2 (bf16) or 4 (fp32)");
+    if (!((b == 2 && (d_h == 64 || d_h == 128)) || (b == 4 && d_h == 64)))
+        return fail(ATTN_ENOTSUP, "unsupported (b=%d, d_h=%d)", b, d_h);
+    if (block_table || s_max > 0) {
+        int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
+        if (rc) return rc;
+    }
+    if (B == 0) return ATTN_OK;
+    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h);
+    if (P.ws_bytes && (!workspace || workspace_bytes < P.ws_bytes))
+        return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    attn::GqaParams p{};
+    p.out = out;
+    p.lse = lse;
+    p.q = q;
+    p.k = cache_k;
+    p.v = cache_v;
+    p.s = s;
+    p.bt = block_table;
+    p.part_o = (float*)workspace;
+    p.part_ml = (float*)((char*)workspace + P.part_o_bytes);
+    p.max_blocks = max_blocks;
+    p.bs_log2 = block_table ? ilog2(block_size) : 0;
+    p.num_blocks = num_blocks;
+    p.B = B;
+    p.s_max = s_max;
+    p.h = h;
+    p.h_kv = h_kv;
+    p.n_hg = P.n_hg;
+    p.n_split = P.n_split;
+    p.chunk = P.chunk;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_h);
+    p.scale_log2 = sc * 1.4426950408889634f;
+    const long long grid = (long long)B * h_kv * P.n_hg * P.n_split;
+    if (grid >= (1LL << 31)) return fail(ATTN_ENOTSUP, "problem too large for one launch");
+    hipError_t e = attn::launch_gqa_decode(p, d_h, b == 4, P.HG, block_table != nullptr,
+                                           (unsigned)grid, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attn_decode_gqa launch");
+    return ATTN_OK;
+}
+
+int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void* q_nope,
+                             const void* q_rope, const void* w_uk, const void* w_uv,
+                             const void* cache, const int32_t* s, const int32_t* block_table,
+                             int max_blocks, int block_size, int num_blocks, int B, int s_max,
+                             int h, int d_c, int d_R, int d_nope, int d_v, int b, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s)
+        return fail(ATTN_EINVAL, "null out, q_nope, q_rope, w_uk, w_uv, cache or s");
+    if (B < 0 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0 || s_max < 0)
+        return fail(ATTN_EINVAL, "bad sizes");
+    if (b != 2) return fail(ATTN_ENOTSUP, "MLA supports bf16 storage only (b=2)");
+    if (d_c != 512 || d_R != 64)
+        return fail(ATTN_ENOTSUP, "MLA supports d_c=512, d_R=64 (got %d, %d)", d_c, d_R);
+    if (h % 16 != 0 || h > 128) return fail(ATTN_ENOTSUP, "MLA needs h a multiple of 16, <= 128");
+    if (d_nope % 16 != 0 || d_nope > 256 || d_v % 16 != 0 || d_v > 256)
+        return fail(ATTN_ENOTSUP, "MLA needs d_nope, d_v multiples of 16 up to 256");
+    if (block_table || s_max > 0) {
+        int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
+        if (rc) return rc;
+    }
+    if (B == 0) return ATTN_OK;
+    const MlaPlan P = plan_mla(B, s_max, h, d_c, d_R);
+    if (!workspace || workspace_bytes < P.ws_bytes)
+        return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    attn::MlaParams p{};
+    p.out = out;
+    p.u_latent = u_latent;
+    p.lse = lse;
+    p.q_nope = q_nope;
+    p.q_rope = q_rope;
+    p.w_uk = w_uk;
+    p.w_uv = w_uv;
+    p.cache = cache;
+    p.s = s;
+    p.bt = block_table;
+    char* ws = (char*)workspace;
+    p.qhat = (uint16_t*)ws;
+    p.part_u = (float*)(ws + P.qhat_bytes);
+    p.part_ml = (float*)(ws + P.qhat_bytes + P.part_u_bytes);
+    float* ulat_ws = (float*)(ws + P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes);
+    if (!p.u_latent) p.u_latent = ulat_ws;
+    p.max_blocks = max_blocks;
+    p.bs_log2 = block_table ? ilog2(block_size) : 0;
+    p.num_blocks = num_blocks;
+    p.B = B;
+    p.s_max = s_max;
+    p.h = h;
+    p.d_c = d_c;
+    p.d_R = d_R;
+    p.d_nope = d_nope;
+    p.d_v = d_v;
+    p.n_split = P.n_split;
+    p.chunk = P.chunk;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)(d_nope + d_R));
+    p.scale_log2 = sc * 1.4426950408889634f;
+    hipError_t e = attn::launch_mla(p, block_table != nullptr, (hipStream_t)stream);
+    if (e == hipErrorNotSupported) return fail(ATTN_ENOTSUP, "MLA kernels not built");
+    if (e != hipSuccess) return hip_fail(e, "attn_decode_mla_absorbed launch");
+    return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Kernel parameter blocks and launchers (host <-> device, library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct GqaParams {
+    void* out;
+    float* lse;
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* s;
+    const int32_t* bt;   // nullptr: contiguous
+    float* part_o;       // [B, h, n_split, d_h]
+    float* part_ml;      // [B, h, n_split, 2]  (m in log2 units, l)
+    int max_blocks, bs_log2, num_blocks;
+    int B, s_max, h, h_kv;
+    int n_hg, n_split, chunk;
+    float scale_log2;    // scale * log2(e)
+};
+
+hipError_t launch_gqa_decode(const GqaParams& p, int d_h, bool f32, int HG, bool paged,
+                             unsigned grid, hipStream_t st);
+
+struct AppendParams {
+    void* cache;
+    const void* src;
+    const int32_t* pos;
+    const int32_t* bt;
+    int max_blocks, bs_log2, num_blocks, s_max;
+    long long row_bytes;
+};
+
+hipError_t launch_append(const AppendParams& k, const AppendParams* v, int B, hipStream_t st);
+
+struct MlaParams {
+    void* out;            // [B, h, d_v] bf16
+    float* u_latent;      // [B, h, d_c] fp32 or nullptr
+    float* lse;           // [B, h] or nullptr
+    const void* q_nope;   // [B, h, d_nope]
+    const void* q_rope;   // [B, h, d_R]
+    const void* w_uk;     // [h, d_nope, d_c]
+    const void* w_uv;     // [h, d_v, d_c]
+    const void* cache;    // rows of d_c + d_R
+    const int32_t* s;
+    const int32_t* bt;
+    uint16_t* qhat;       // [B, h, d_c + d_R] bf16 absorbed query
+    float* part_u;        // [B, n_split, h, d_c]
+    float* part_ml;       // [B, n_split, h, 2]
+    int max_blocks, bs_log2, num_blocks;
+    int B, s_max, h, d_c, d_R, d_nope, d_v;
+    int n_split, chunk;
+    float scale_log2;
+};
+
+hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,192 @@
+/*
+ * attn_decode.h -- C ABI of the MI355X (gfx950) decode-attention library
+ * (libattn_decode.so).
+ *
+ * Single-token decode attention softmax(q K^T / sqrt(d_h)) V over a stored
+ * KV cache, for the four cache layouts of the pages:
+ *   MHA, MQA, GQA  -- h_kv = h, 1, h / g; query head i reads KV head
+ *                     floor(i / g)   ("MHA -> MQA -> GQA -> MLA",
+ *                     mlinterviewnotes.com, opening section; "The KV cache
+ *                     size formula", mlinterviewnotes.com, the attention and
+ *                     cell-size derivation);
+ *   MLA            -- one latent row [c_KV (d_c) | k_R (d_R)] per token,
+ *                     decoded with the absorbed query, a latent weighted sum
+ *                     and a deferred W_UV ("Multi-Head Latent Attention
+ *                     (MLA): Mathematical Foundations ...", llms.blog,
+ *                     sections "Attention Logit Matrix Absorption" and
+ *                     "Value Output Matrix Absorption").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Symbols follow the pages: B sequences, s_i cached tokens of sequence i
+ * (s_max an upper bound), L layers, h query heads, h_kv KV heads, d_h head
+ * dimension, d_c latent width (kv_lora_rank), d_R decoupled-RoPE key width,
+ * b bytes per stored element.
+ *
+ * Element type: b = 2 -> bf16 storage, b = 4 -> fp32 storage.  Arithmetic
+ * accumulates in fp32.  Outputs have the storage type; lse and u_latent are
+ * always fp32.
+ *
+ * Memory: every tensor pointer is device memory owned by the caller; the
+ * library never allocates, frees or keeps a pointer after a call returns.
+ * Tensors are dense, row-major (last index fastest), naturally aligned and
+ * 16-byte aligned at their base.  The library keeps no state apart from a
+ * thread-local error message.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Calls only enqueue work and return; results are ready when the
+ * stream reaches them.  Concurrent calls must not share a workspace.
+ *
+ * Cache layouts:
+ *   contiguous (block_table == NULL): token t of sequence i is row
+ *     i * s_max + t of a [B, s_max, ...] buffer;
+ *   paged (block_table != NULL): token t of sequence i is row
+ *     block_table[i * max_blocks + t / block_size] * block_size
+ *       + t % block_size
+ *     of a [num_blocks, block_size, ...] pool (16-token pages in the
+ *     engines quoted by "The KV cache size formula", section "vLLM: a
+ *     per-layer page, then integer division"; block contents per "MLA: why
+ *     one latent can replace a multi-head KV cache", charlestar.github.io,
+ *     section "What a paged KV cache block holds").  block_size must be a
+ *     power of two >= 16; max_blocks * block_size >= s_max.
+ *
+ * Device-resident lengths and tables (s, pos, block_table) are never read
+ * on the host.  Kernels clamp them so that no access leaves the buffers the
+ * host-side sizes describe: a length is clamped to [0, s_max] (paged: to
+ * [0, max_blocks * block_size]) and a block id to [0, num_blocks); results
+ * for such out-of-range values are unspecified but memory-safe.  A
+ * sequence with s_i = 0 yields an all-zero output row and lse = -inf.
+ *
+ * Return value: ATTN_OK, or a negative status; attn_last_error() then
+ * describes it.  Argument checks happen before anything is enqueued, so a
+ * rejected call has no effect.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK          0
+#define ATTN_EINVAL     (-1) /* null pointer, non-positive size, h % h_kv != 0, bad block_size */
+#define ATTN_ENOTSUP    (-2) /* valid but unsupported shape or dtype (see each call) */
+#define ATTN_EWORKSPACE (-3) /* workspace missing or smaller than attn_decode_workspace_bytes() */
+#define ATTN_EHIP       (-4) /* the HIP runtime reported an error while enqueuing */
+
+/*
+ * Bytes per token of a K/V cache over all layers: 2 * L * h_kv * d_h * b
+ * ("The KV cache size formula", the cell size c; "MHA -> MQA -> GQA ->
+ * MLA", opening section).  The factor 2 is K plus V.  Host-only, pure.
+ * Returns 0 if any argument is negative.
+ */
+size_t attn_kv_cell_bytes(int L, int h_kv, int d_h, int b);
+
+/*
+ * Bytes per token of an MLA latent cache over all layers: L * (d_c + d_R) * b
+ * -- no factor 2 and no head count ("The KV cache size formula", section
+ * "Where MLA breaks the formula").  Host-only, pure.  Returns 0 if any
+ * argument is negative.
+ */
+size_t attn_mla_cell_bytes(int L, int d_c, int d_R, int b);
+
+/*
+ * Workspace bytes the next two calls need for these sizes (0 is possible).
+ * is_mla = 0: GQA/MQA/MHA, d_h_or_dc = d_h, d_R ignored.
+ * is_mla = 1: MLA, h_kv ignored, d_h_or_dc = d_c.
+ * The value depends only on the arguments; a buffer of this size (16-byte
+ * aligned) may be reused across calls on one stream.
+ */
+size_t attn_decode_workspace_bytes(int is_mla, int B, int s_max, int h, int h_kv,
+                                   int d_h_or_dc, int d_R);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* attn_last_error(void);
+
+/*
+ * kv_cache_append -- write the new token's cache rows at slot pos[i] of each
+ * sequence i (the append-by-concatenation step of the absorbed decode module
+ * on the llms.blog MLA page; paged placement per "What a paged KV cache
+ * block holds").
+ *   cache_k, cache_v : [B, s_max, h_kv, d_h] or [num_blocks, block_size,
+ *                      h_kv, d_h]; written in place.
+ *   k_new, v_new     : [B, h_kv, d_h].
+ *   pos              : [B] int32 device; slot to write (normally the current
+ *                      s_i).  The caller keeps the lengths: s is not changed.
+ * MLA: pass cache_v = v_new = NULL, h_kv = 1 and d_h = d_c + d_R (one latent
+ * buffer, no V -- the num_kv_heads = 1, head_size_v = 0 encoding quoted on
+ * "The KV cache size formula").  Rows whose pos or block id is out of range
+ * are not written.  The copy is bit-exact.
+ * Errors: EINVAL (null cache_k/k_new/pos, cache_v and v_new not both null or
+ * both set, B < 0, h_kv <= 0, d_h <= 0, b not 2 or 4, bad block_size,
+ * s_max <= 0 with no table, num_blocks <= 0 with a table), EHIP.
+ */
+int kv_cache_append(void* cache_k, void* cache_v, const void* k_new, const void* v_new,
+                    const int32_t* pos, const int32_t* block_table, int max_blocks,
+                    int block_size, int num_blocks, int B, int s_max, int h_kv, int d_h,
+                    int b, void* stream);
+
+/*
+ * attn_decode_gqa -- decode attention for MHA / MQA / GQA.
+ *   out   : [B, h, d_h], storage type.
+ *   lse   : [B, h] fp32, natural-log log-sum-exp of the scaled scores; may be
+ *           NULL.
+ *   q     : [B, h, d_h], storage type.
+ *   cache_k, cache_v : see "Cache layouts", inner shape [h_kv, d_h].
+ *   s     : [B] int32 device lengths s_i.
+ *   scale : > 0 used as given; <= 0 selects 1 / sqrt(d_h).
+ *   workspace : at least attn_decode_workspace_bytes(0, B, s_max, h, h_kv,
+ *           d_h, 0) bytes of device memory (may be NULL when that is 0).
+ * out[b, i] = sum_t softmax_t(scale * q[b,i] . K[b,t,j]) V[b,t,j],
+ * j = floor(i / (h / h_kv)).
+ * Supported: (b = 2, d_h in {64, 128}) and (b = 4, d_h = 64); h / h_kv any
+ * positive integer.  Other (b, d_h): ENOTSUP.
+ * Errors: EINVAL (null out/q/cache/s, non-positive sizes, h % h_kv != 0,
+ * bad block_size, max_blocks * block_size < s_max), ENOTSUP, EWORKSPACE,
+ * EHIP.
+ */
+int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
+                    const void* cache_v, const int32_t* s, const int32_t* block_table,
+                    int max_blocks, int block_size, int num_blocks, int B, int s_max, int h,
+                    int h_kv, int d_h, int b, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_mla_absorbed -- MLA decode in the absorbed ("MQA mode") form:
+ *   q~[b,i]  = W_UK[i]^T q_nope[b,i]                      (d_c values)
+ *   z_t      = scale * (q~ . c_t + q_rope[b,i] . k_R,t)
+ *   u~[b,i]  = sum_t softmax_t(z) c_t                     (d_c values)
+ *   out[b,i] = W_UV[i] u~[b,i]                            (d_v values)
+ * ("Attention Logit Matrix Absorption" and "Value Output Matrix Absorption"
+ * on the llms.blog MLA page; "First matrix absorption" and "Second matrix
+ * absorption" on the charlestar.github.io MLA page.)
+ *   out      : [B, h, d_v] bf16.
+ *   u_latent : [B, h, d_c] fp32 latent weighted sum u~; may be NULL.
+ *   lse      : [B, h] fp32; may be NULL.
+ *   q_nope   : [B, h, d_nope] bf16; q_rope : [B, h, d_R] bf16, already
+ *              rotated.
+ *   w_uk     : [h, d_nope, d_c] bf16; w_uv : [h, d_v, d_c] bf16.
+ *   cache    : rows [c_KV | k_R] of width d_c + d_R, bf16 (see "Cache
+ *              layouts").
+ *   scale    : > 0 used as given; <= 0 selects 1 / sqrt(d_nope + d_R).
+ *   workspace: at least attn_decode_workspace_bytes(1, B, s_max, h, 1, d_c,
+ *              d_R) bytes.
+ * Supported: b = 2, d_c = 512, d_R = 64, h a multiple of 16 up to 128,
+ * d_nope and d_v multiples of 16 up to 256.  Others: ENOTSUP.
+ * Errors: EINVAL, ENOTSUP, EWORKSPACE, EHIP as above.
+ */
+int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void* q_nope,
+                             const void* q_rope, const void* w_uk, const void* w_uv,
+                             const void* cache, const int32_t* s, const int32_t* block_table,
+                             int max_blocks, int block_size, int num_blocks, int B, int s_max,
+                             int h, int d_c, int d_R, int d_nope, int d_v, int b, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DECODE_H */

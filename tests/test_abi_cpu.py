@@ -1,0 +1,125 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry
+point include/attn_decode.h declares, and its host-only helpers and argument
+checks behave (no kernel is launched here)."""
+import ctypes as C
+import json
+import os
+import re
+
+import pytest
+
+import decode_attention_kv_attn_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "cell_sizes.json")))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_entry_points_and_helpers():
+    names = declared_functions()
+    for n in ("attn_decode_gqa", "attn_decode_mla_absorbed", "kv_cache_append",
+              "attn_decode_workspace_bytes", "attn_kv_cell_bytes", "attn_mla_cell_bytes",
+              "attn_last_error"):
+        assert n in names
+    assert sorted(A.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {A.LIB_PATH}").read()
+    for n in declared_functions():
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_library_is_built_for_gfx950():
+    blob = open(A.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+@pytest.mark.parametrize("case", GOLD["gqa"], ids=lambda c: c["name"])
+def test_kv_cell_bytes_matches_printed(case):
+    assert A.attn_kv_cell_bytes(case["L"], case["h_kv"], case["d_h"], case["b"]) * case["tokens"] \
+        == case["bytes"]
+
+
+@pytest.mark.parametrize("case", GOLD["mla"], ids=lambda c: c["name"])
+def test_mla_cell_bytes_matches_printed(case):
+    assert A.attn_mla_cell_bytes(case["L"], case["d_c"], case["d_R"], case["b"]) * case["tokens"] \
+        == case["bytes"]
+
+
+def test_cell_helpers_reject_negative():
+    assert A.attn_kv_cell_bytes(-1, 8, 128, 2) == 0
+    assert A.attn_mla_cell_bytes(61, -512, 64, 2) == 0
+
+
+def test_workspace_bytes():
+    # a batch big enough to fill the GPU needs no split, hence no workspace
+    assert A.attn_decode_workspace_bytes(0, 4096, 4096, 8, 8, 128) == 0
+    # long context, small batch: split-KV partials
+    ws = A.attn_decode_workspace_bytes(0, 1, 131072, 64, 8, 128)
+    assert ws >= 64 * 2 * 130 * 4
+    assert A.attn_decode_workspace_bytes(0, 1, 131072, 64, 7, 128) == 0   # h % h_kv != 0
+    mla = A.attn_decode_workspace_bytes(1, 32, 8192, 128, 1, 512, 64)
+    assert mla >= 32 * 128 * 576 * 2 + 32 * 128 * 512 * 4
+
+
+FAKE = 256  # never dereferenced: every call below is rejected before any launch
+
+
+def gqa_call(**kw):
+    args = dict(out=FAKE, lse=None, q=FAKE, cache_k=FAKE, cache_v=FAKE, s=FAKE, block_table=None,
+                max_blocks=0, block_size=16, num_blocks=0, B=2, s_max=64, h=8, h_kv=2, d_h=128,
+                b=2, scale=0.0, workspace=None, workspace_bytes=0, stream=0, check=False)
+    args.update(kw)
+    return A.attn_decode_gqa(**args)
+
+
+def test_gqa_argument_errors():
+    assert gqa_call(out=None) == A.ATTN_EINVAL
+    assert gqa_call(h=6, h_kv=4) == A.ATTN_EINVAL
+    assert "not divisible" in A.attn_last_error()
+    assert gqa_call(b=3) == A.ATTN_EINVAL
+    assert gqa_call(d_h=96) == A.ATTN_ENOTSUP
+    assert gqa_call(b=4, d_h=128) == A.ATTN_ENOTSUP
+    assert gqa_call(block_table=FAKE, block_size=24, max_blocks=4, num_blocks=8) == A.ATTN_EINVAL
+    assert gqa_call(block_table=FAKE, block_size=16, max_blocks=2, num_blocks=8) == A.ATTN_EINVAL
+    # long context at B=1 needs a workspace
+    assert gqa_call(B=1, s_max=65536) == A.ATTN_EWORKSPACE
+    assert "workspace" in A.attn_last_error()
+
+
+def mla_call(**kw):
+    args = dict(out=FAKE, u_latent=None, lse=None, q_nope=FAKE, q_rope=FAKE, w_uk=FAKE, w_uv=FAKE,
+                cache=FAKE, s=FAKE, block_table=None, max_blocks=0, block_size=16, num_blocks=0,
+                B=2, s_max=64, h=128, d_c=512, d_R=64, d_nope=128, d_v=128, b=2, scale=0.0,
+                workspace=None, workspace_bytes=0, stream=0, check=False)
+    args.update(kw)
+    return A.attn_decode_mla_absorbed(**args)
+
+
+def test_mla_argument_errors():
+    assert mla_call(cache=None) == A.ATTN_EINVAL
+    assert mla_call(b=4) == A.ATTN_ENOTSUP
+    assert mla_call(d_c=256) == A.ATTN_ENOTSUP
+    assert mla_call(h=24) == A.ATTN_ENOTSUP
+    assert mla_call() == A.ATTN_EWORKSPACE
+
+
+def test_append_argument_errors():
+    kw = dict(cache_k=FAKE, cache_v=FAKE, k_new=FAKE, v_new=None, pos=FAKE, block_table=None,
+              max_blocks=0, block_size=16, num_blocks=0, B=2, s_max=8, h_kv=2, d_h=64, b=2,
+              stream=0, check=False)
+    assert A.kv_cache_append(**kw) == A.ATTN_EINVAL          # v_new missing
+    kw.update(v_new=FAKE, b=8)
+    assert A.kv_cache_append(**kw) == A.ATTN_EINVAL
+    kw.update(b=2, s_max=0)
+    assert A.kv_cache_append(**kw) == A.ATTN_EINVAL

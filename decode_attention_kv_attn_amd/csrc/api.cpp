@@ -88,7 +88,8 @@ MlaPlan plan_mla(int B, int s_max, int h, int d_c, int d_R)
 {
     MlaPlan P{};
     const long long T = 32, target = 256, min_chunk = 256;
-    long long ns = B > 0 ? cdiv(target, B) : 1;
+    const long long groups = (h + 63) / 64;    // workgroups per (b, split)
+    long long ns = B > 0 ? cdiv(target, (long long)B * groups) : 1;
     const long long ns_max = s_max > 0 ? cdiv(s_max, min_chunk) : 1;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
@@ -247,8 +248,10 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     if (d_c != 512 || d_R != 64)
         return fail(ATTN_ENOTSUP, "MLA supports d_c=512, d_R=64 (got %d, %d)", d_c, d_R);
     if (h % 16 != 0 || h > 128) return fail(ATTN_ENOTSUP, "MLA needs h a multiple of 16, <= 128");
-    if (d_nope % 16 != 0 || d_nope > 256 || d_v % 16 != 0 || d_v > 256)
-        return fail(ATTN_ENOTSUP, "MLA needs d_nope, d_v multiples of 16 up to 256");
+    if ((long long)B * plan_mla(B, s_max, h, d_c, d_R).n_split * ((h + 63) / 64) >= (1LL << 31))
+        return fail(ATTN_ENOTSUP, "problem too large for one launch");
+    if (d_nope % 32 != 0 || d_nope > 256 || d_v % 16 != 0 || d_v > 256)
+        return fail(ATTN_ENOTSUP, "MLA needs d_nope a multiple of 32, d_v of 16, both <= 256");
     if (block_table || s_max > 0) {
         int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
         if (rc) return rc;

@@ -102,10 +102,16 @@ __device__ __forceinline__ float uniform(float x)
 // unmapped pages are kept in bounds.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, 32-bit data format
+// Every field must be wave-uniform; readfirstlane pins them to SGPRs so the
+// compiler never wraps the load in a per-lane (waterfall) loop.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int num_records)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                             num_records > 0 ? num_records : 0, kRsrcFlags);
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int nr = __builtin_amdgcn_readfirstlane(num_records > 0 ? num_records : 0);
+    void* ub = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, nr, kRsrcFlags);
 }
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff)
 {

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaParams p)
     const int g = p.h / p.h_kv;
     const int head0 = j * g + hgi * HG;
 
-    int n = s_len[b];
+    int n = __builtin_amdgcn_readfirstlane(s_len[b]);
     n = min(max(n, 0), p.s_max);
     const int t0 = split * p.chunk;
     const int t1 = min(n, t0 + p.chunk);
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaParams p)
                 const int t = tb + k * C::RPI;                       // uniform
                 const int lb = t >> p.bs_log2;
                 const int bstart = lb << p.bs_log2;
-                int blk = btab[(size_t)b * p.max_blocks + min(lb, p.max_blocks - 1)];
+                int blk = __builtin_amdgcn_readfirstlane(btab[(size_t)b * p.max_blocks + min(lb, p.max_blocks - 1)]);
                 blk = min(max(blk, 0), p.num_blocks - 1);
                 const uint8_t* bbase = base + ((size_t)blk << p.bs_log2) * row_stride + (size_t)j * C::RB;
                 const int nrec = (min(t1 - bstart, 1 << p.bs_log2)) * (int)row_stride - j * C::RB;

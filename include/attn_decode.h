@@ -175,7 +175,8 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
  *   workspace: at least attn_decode_workspace_bytes(1, B, s_max, h, 1, d_c,
  *              d_R) bytes.
  * Supported: b = 2, d_c = 512, d_R = 64, h a multiple of 16 up to 128,
- * d_nope and d_v multiples of 16 up to 256.  Others: ENOTSUP.
+ * d_nope a multiple of 32 up to 256, d_v a multiple of 16 up to 256.
+ * Others: ENOTSUP.
  * Errors: EINVAL, ENOTSUP, EWORKSPACE, EHIP as above.
  */
 int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void* q_nope,

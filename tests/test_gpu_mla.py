@@ -1,0 +1,100 @@
+"""GPU parity of attn_decode_mla_absorbed against the CPU oracle (absorbed
+form, itself pinned to explicit K/V expansion).  Output and u_latent use the
+bf16 tolerances (max-abs <= 2e-2, mean-abs <= 2e-3, rel-RMS <= 1e-2); the
+kernel rounds the absorbed query and the probabilities to bf16 for the
+matrix cores and accumulates in fp32."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_kv_attn_amd as A
+import oracle
+import synth
+from tests._gpu import assert_close, assert_lse_close, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run(sh, sample=None):
+    print(f"[mla] {sh.name} B={sh.B} h={sh.h} s={list(sh.s)[:6]} paged={sh.paged}", flush=True)
+    d = synth.draw_mla(sh, device=DEV)
+    out, ul, lse = A.decode_mla(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["cache"], d["s"],
+                                block_table=d.get("block_table"), s_max=sh.s_max)
+    torch.cuda.synchronize()
+    bs = range(sh.B) if sample is None else sample
+    for bi in bs:
+        n = int(sh.s[bi])
+        args = [synth.host_bits(d[k][bi:bi + 1]) for k in ("q_nope", "q_rope")]
+        w = [synth.host_bits(d["w_uk"]), synth.host_bits(d["w_uv"])]
+        if sh.paged:
+            tab = d["block_table_host"][bi]
+            nb = (n + sh.block_size - 1) // sh.block_size
+            idx = torch.as_tensor(tab[:nb], dtype=torch.long, device=DEV)
+            rows = d["cache"].index_select(0, idx).reshape(-1, sh.d_c + sh.d_R)[:max(n, 1)]
+        else:
+            rows = d["cache"][bi, :max(n, 1)]
+        C = synth.host_bits(rows)[None]
+        ro, ru, rl = oracle.mla_absorbed(args[0], args[1], w[0], w[1], C,
+                                         np.array([n], np.int32))
+        assert_close(to_f64(out[bi:bi + 1]), ro, 2, f"out b={bi}")
+        assert_close(to_f64(ul[bi:bi + 1]), ru, 2, f"u_latent b={bi}")
+        assert_lse_close(to_f64(lse[bi:bi + 1]), rl, 2, f"lse b={bi}")
+    return d, out, ul, lse
+
+
+def shape(B, h, s, paged=False, seed=31, d_nope=128, d_v=128):
+    return synth.MlaShape("t", B=B, h=h, d_c=512, d_R=64, d_nope=d_nope, d_v=d_v, s=tuple(s),
+                          paged=paged, seed=seed)
+
+
+@pytest.mark.parametrize("h", [16, 32, 48, 128])
+def test_head_counts(h):
+    run(shape(2, h, (77, 300), seed=h))
+
+
+@pytest.mark.parametrize("s", [(1, 2), (31, 33), (0, 64), (0, 0), (1000, 17)])
+def test_lengths_ragged_empty(s):
+    run(shape(2, 32, s, seed=sum(s) + 1))
+
+
+def test_batch_not_multiple_of_16_and_other_dims():
+    run(shape(19, 16, tuple(range(5, 5 + 19 * 7, 7)), seed=5, d_nope=64, d_v=32))
+
+
+def test_long_context_split():
+    run(shape(1, 128, (12000,), seed=6))
+
+
+def test_paged_shuffled():
+    run(shape(4, 32, (1, 16, 17, 700), paged=True, seed=7))
+
+
+def test_paged_bit_identical_to_identity_table():
+    s = (5, 40, 129, 700)
+    sh = shape(4, 64, s, paged=True, seed=8)
+    d = synth.draw_mla(sh, device=DEV)
+    tab = d["block_table_host"]
+    ident, _ = synth.identity_table(s, 16)
+    order = torch.as_tensor(np.concatenate([tab[i, :(n + 15) // 16] for i, n in enumerate(s)]),
+                            dtype=torch.long, device=DEV)
+    Ci = d["cache"].index_select(0, order)
+    a = A.decode_mla(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["cache"], d["s"],
+                     block_table=d["block_table"], s_max=max(s))
+    b = A.decode_mla(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], Ci, d["s"],
+                     block_table=torch.from_numpy(ident).to(DEV), s_max=max(s))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_deepseek_v3_full_size_sampled():
+    sh = synth.configs()["deepseek_v3_mla"]
+    run(sh, sample=[0, 17, sh.B - 1])
+
+
+def test_paged_mla_full_size_sampled():
+    sh = synth.configs()["paged_mla"]
+    lens = np.asarray(sh.s)
+    pick = [int(np.argmin(lens)), int(np.argmax(lens)), 64]
+    run(sh, sample=pick)

@@ -44,8 +44,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---- GQA split plan ---------------------------------------------------------
 // Work item = (b, KV head, group of HG query heads, token split).  HG is the
 // largest of 8, 4, 2, 1 dividing g.  Splits are added until about 2048
-// wavefronts are in flight (8 per CU on 256 CUs), but no split is shorter
-// than 256 tokens; split lengths are multiples of the 64-token tile.
+// wavefronts are in flight (8 per CU on 256 CUs) and no split is longer than
+// 4096 tokens, but no split is shorter than 256 tokens; split lengths are
+// multiples of the 64-token tile.
 struct GqaPlan {
     int HG, n_hg, n_split, chunk;
     size_t part_o_bytes, part_ml_bytes, ws_bytes;
@@ -57,9 +58,12 @@ GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h)
     const int g = h / h_kv;
     P.HG = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
     P.n_hg = g / P.HG;
-    const long long T = 64, target = 2048, min_chunk = 256;
+    const long long T = 64, target = 2048, min_chunk = 256, max_chunk = 4096;
     const long long units = (long long)B * h_kv * P.n_hg;
     long long ns = units > 0 ? cdiv(target, units) : 1;
+    // no split longer than max_chunk: with mixed lengths the longest
+    // sequences would otherwise set the kernel time
+    if (s_max > 0 && ns < cdiv(s_max, max_chunk)) ns = cdiv(s_max, max_chunk);
     const long long ns_max = s_max > 0 ? cdiv(s_max, min_chunk) : 1;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
@@ -81,15 +85,14 @@ GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h)
 // splits of at least 256 tokens, multiples of the 32-token tile.
 struct MlaPlan {
     int n_split, chunk;
-    size_t qhat_bytes, part_u_bytes, part_ml_bytes, ulat_bytes, ws_bytes;
+    size_t qhat_bytes, part_u_bytes, part_ml_bytes, flag_bytes, ws_bytes;
 };
 
 MlaPlan plan_mla(int B, int s_max, int h, int d_c, int d_R)
 {
     MlaPlan P{};
     const long long T = 32, target = 256, min_chunk = 256;
-    const long long groups = (h + 63) / 64;    // workgroups per (b, split)
-    long long ns = B > 0 ? cdiv(target, (long long)B * groups) : 1;
+    long long ns = B > 0 ? cdiv(target, B) : 1;
     const long long ns_max = s_max > 0 ? cdiv(s_max, min_chunk) : 1;
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
@@ -100,8 +103,8 @@ MlaPlan plan_mla(int B, int s_max, int h, int d_c, int d_R)
     P.qhat_bytes = align256((size_t)B * h * (d_c + d_R) * 2);
     P.part_u_bytes = align256((size_t)B * P.n_split * h * d_c * sizeof(float));
     P.part_ml_bytes = align256((size_t)B * P.n_split * h * 2 * sizeof(float));
-    P.ulat_bytes = align256((size_t)B * h * d_c * sizeof(float));
-    P.ws_bytes = P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.ulat_bytes;
+    P.flag_bytes = align256((size_t)B * P.n_split * sizeof(int32_t));
+    P.ws_bytes = P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.flag_bytes;
     return P;
 }
 
@@ -248,7 +251,7 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     if (d_c != 512 || d_R != 64)
         return fail(ATTN_ENOTSUP, "MLA supports d_c=512, d_R=64 (got %d, %d)", d_c, d_R);
     if (h % 16 != 0 || h > 128) return fail(ATTN_ENOTSUP, "MLA needs h a multiple of 16, <= 128");
-    if ((long long)B * plan_mla(B, s_max, h, d_c, d_R).n_split * ((h + 63) / 64) >= (1LL << 31))
+    if ((long long)B * plan_mla(B, s_max, h, d_c, d_R).n_split >= (1LL << 31))
         return fail(ATTN_ENOTSUP, "problem too large for one launch");
     if (d_nope % 32 != 0 || d_nope > 256 || d_v % 16 != 0 || d_v > 256)
         return fail(ATTN_ENOTSUP, "MLA needs d_nope a multiple of 32, d_v of 16, both <= 256");
@@ -276,8 +279,7 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     p.qhat = (uint16_t*)ws;
     p.part_u = (float*)(ws + P.qhat_bytes);
     p.part_ml = (float*)(ws + P.qhat_bytes + P.part_u_bytes);
-    float* ulat_ws = (float*)(ws + P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes);
-    if (!p.u_latent) p.u_latent = ulat_ws;
+    p.flags = (int32_t*)(ws + P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes);
     p.max_blocks = max_blocks;
     p.bs_log2 = block_table ? ilog2(block_size) : 0;
     p.num_blocks = num_blocks;

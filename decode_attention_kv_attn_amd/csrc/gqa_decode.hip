@@ -44,7 +44,8 @@ struct GqaCfg {
 };
 
 template <int D, int HG, bool F32, bool PAGED>
-__global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaParams p)
+__global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaParams p,
+                                                        const int32_t* __restrict__ btab)
 {
     using C = GqaCfg<D, F32>;
     __shared__ __attribute__((aligned(16))) uint8_t Ks[C::T * C::RB];
@@ -52,7 +53,6 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaParams p)
     __shared__ __attribute__((aligned(16))) uint8_t Ps[HG * C::T * C::PB];
 
     const int32_t* __restrict__ s_len = p.s;
-    const int32_t* __restrict__ btab = p.bt;
     const uint8_t* __restrict__ kbase = (const uint8_t*)p.k;
     const uint8_t* __restrict__ vbase = (const uint8_t*)p.v;
 
@@ -358,9 +358,9 @@ template <int D, int HG, bool F32>
 static hipError_t launch_hg(const GqaParams& p, bool paged, unsigned grid, hipStream_t st)
 {
     if (paged)
-        hipLaunchKernelGGL((gqa_decode_kernel<D, HG, F32, true>), dim3(grid), dim3(64), 0, st, p);
+        hipLaunchKernelGGL((gqa_decode_kernel<D, HG, F32, true>), dim3(grid), dim3(64), 0, st, p, p.bt);
     else
-        hipLaunchKernelGGL((gqa_decode_kernel<D, HG, F32, false>), dim3(grid), dim3(64), 0, st, p);
+        hipLaunchKernelGGL((gqa_decode_kernel<D, HG, F32, false>), dim3(grid), dim3(64), 0, st, p, p.bt);
     return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ struct MlaParams {
     uint16_t* qhat;       // [B, h, d_c + d_R] bf16 absorbed query
     float* part_u;        // [B, n_split, h, d_c]
     float* part_ml;       // [B, n_split, h, 2]
+    int32_t* flags;       // [B, n_split]: split left to the rescaling kernel
     int max_blocks, bs_log2, num_blocks;
     int B, s_max, h, d_c, d_R, d_nope, d_v;
     int n_split, chunk;

@@ -126,3 +126,19 @@ def test_full_size_sampled(name):
         assert_close(o64[bi, j * g:(j + 1) * g], ro, sh.b, f"{name} b={bi} j={j}")
         assert_lse_close(l64[bi, j * g:(j + 1) * g], rl, sh.b, f"{name} b={bi} j={j}")
     assert np.all(np.isfinite(o64))
+
+
+def test_peaked_logits_rescale():
+    # a late key aligned with q makes the running max jump by a large amount
+    sh = synth.GqaShape("t", B=2, h=16, h_kv=2, d_h=128, b=2, s=(700, 5000), seed=15)
+    d = synth.draw_gqa(sh, device=DEV)
+    for bi, t in ((0, 650), (1, 4500)):
+        q0 = d["q"][bi, 0].float()
+        d["K"][bi, t, 0] = (q0 / q0.norm() * 60.0).to(torch.bfloat16)
+    out, lse = A.decode_gqa(d["q"], d["K"], d["V"], d["s"])
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.gqa_decode(*(synth.host_bits(d[k]) for k in ("q", "K", "V")),
+                                     d["s_host"], 2)
+    assert ref_lse[0, 0] > 20
+    assert_close(to_f64(out), ref, 2, "out")
+    assert_lse_close(to_f64(lse), ref_lse, 2, "lse")

@@ -98,3 +98,30 @@ def test_paged_mla_full_size_sampled():
     lens = np.asarray(sh.s)
     pick = [int(np.argmin(lens)), int(np.argmax(lens)), 64]
     run(sh, sample=pick)
+
+
+def test_peaked_logits_take_the_rescaling_path():
+    # One late token whose latent row points along head 0's absorbed query:
+    # its logit exceeds the first tile's maximum by far more than 2^64 in
+    # probability ratio, so that split is recomputed with online rescaling.
+    sh = shape(2, 128, (300, 5000), seed=71)
+    d = synth.draw_mla(sh, device=DEV)
+    qt = torch.einsum("bn,nc->bc", d["q_nope"][:, 0].float(), d["w_uk"][0].float())   # q~ of head 0
+    for bi, t in ((0, 200), (1, 4000)):
+        c = qt[bi] / qt[bi].norm() * 40.0
+        r = d["q_rope"][bi, 0].float()
+        kr = r / r.norm() * 40.0
+        d["cache"][bi, t] = torch.cat([c, kr]).to(torch.bfloat16)
+    out, ul, lse = A.decode_mla(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["cache"], d["s"])
+    torch.cuda.synchronize()
+    for bi in range(2):
+        n = int(sh.s[bi])
+        args = [synth.host_bits(d[k][bi:bi + 1]) for k in ("q_nope", "q_rope")]
+        ro, ru, rl = oracle.mla_absorbed(args[0], args[1], synth.host_bits(d["w_uk"]),
+                                         synth.host_bits(d["w_uv"]),
+                                         synth.host_bits(d["cache"][bi, :n])[None],
+                                         np.array([n], np.int32))
+        assert rl[0, 0] > 50            # the spike dominates head 0
+        assert_close(to_f64(out[bi:bi + 1]), ro, 2, f"out b={bi}")
+        assert_close(to_f64(ul[bi:bi + 1]), ru, 2, f"u_latent b={bi}")
+        assert_lse_close(to_f64(lse[bi:bi + 1]), rl, 2, f"lse b={bi}")

@@ -209,7 +209,7 @@ def main():
         "hbm_gbps": ab / (ms * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "attention call (gqa_decode_kernel + gqa_combine_kernel)",
+                     "kernel": "attention call (gqa_mfma_kernel, plus gqa_combine_kernel when the context is split)",
                      "alg_bytes_per_call": ab, "avg_call_us": call_ms * 1e3},
     }
     if not args.no_mla:

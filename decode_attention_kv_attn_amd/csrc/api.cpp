@@ -42,27 +42,42 @@ long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ---- GQA split plan ---------------------------------------------------------
-// Work item = (b, KV head, group of HG query heads, token split).  HG is the
-// largest of 8, 4, 2, 1 dividing g.  Splits are added until about 2048
-// wavefronts are in flight (8 per CU on 256 CUs) and no split is longer than
-// 4096 tokens, but no split is shorter than 256 tokens; split lengths are
-// multiples of the 64-token tile.
+// bf16 caches with g <= 64 run on the matrix cores: work item = (b, KV head,
+// token split) with all g query heads in one workgroup of ceil(g/16)
+// wavefronts (1, 2 or 4).  A 64 KB LDS ring per workgroup leaves room for
+// two per CU, so splits are added until about 512 workgroups exist.
+// Otherwise (fp32, or g > 64) the vector kernel runs: work item = (b, KV
+// head, group of HG query heads, token split), HG the largest of 8, 4, 2, 1
+// dividing g, one wavefront each, about 2048 of them (8 per CU).
+// Either way no split is longer than 4096 tokens (with mixed lengths the
+// longest sequences would otherwise set the kernel time) or shorter than 256
+// tokens, and split lengths are multiples of 64 tokens.
 struct GqaPlan {
-    int HG, n_hg, n_split, chunk;
+    bool mfma;
+    int HG, n_hg, NW, n_split, chunk;
     size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
-GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h)
+GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h)
 {
     GqaPlan P{};
     const int g = h / h_kv;
-    P.HG = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
-    P.n_hg = g / P.HG;
-    const long long T = 64, target = 2048, min_chunk = 256, max_chunk = 4096;
+    P.mfma = mfma;
+    long long target;
+    if (mfma) {
+        P.HG = g;
+        P.n_hg = 1;
+        P.NW = g <= 16 ? 1 : g <= 32 ? 2 : 4;
+        target = 512;
+    } else {
+        P.HG = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
+        P.n_hg = g / P.HG;
+        P.NW = 1;
+        target = 2048;
+    }
+    const long long T = 64, min_chunk = 256, max_chunk = 4096;
     const long long units = (long long)B * h_kv * P.n_hg;
     long long ns = units > 0 ? cdiv(target, units) : 1;
-    // no split longer than max_chunk: with mixed lengths the longest
-    // sequences would otherwise set the kernel time
     if (s_max > 0 && ns < cdiv(s_max, max_chunk)) ns = cdiv(s_max, max_chunk);
     const long long ns_max = s_max > 0 ? cdiv(s_max, min_chunk) : 1;
     if (ns > ns_max) ns = ns_max;
@@ -77,6 +92,13 @@ GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h)
     }
     P.ws_bytes = P.part_o_bytes + P.part_ml_bytes;
     return P;
+}
+
+bool gqa_uses_mfma(int h, int h_kv, int b) { return b == 2 && h / h_kv <= 64; }
+
+GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b)
+{
+    return plan_gqa_path(gqa_uses_mfma(h, h_kv, b), B, s_max, h, h_kv, d_h);
 }
 
 // ---- MLA split plan -----------------------------------------------------------
@@ -146,7 +168,10 @@ size_t attn_decode_workspace_bytes(int is_mla, int B, int s_max, int h, int h_kv
     if (B <= 0 || h <= 0 || s_max < 0 || d_h_or_dc <= 0) return 0;
     if (is_mla) return plan_mla(B, s_max, h, d_h_or_dc, d_R < 0 ? 0 : d_R).ws_bytes;
     if (h_kv <= 0 || h % h_kv != 0) return 0;
-    return plan_gqa(B, s_max, h, h_kv, d_h_or_dc).ws_bytes;
+    // the storage type is not an argument: size for whichever kernel runs
+    const size_t a = plan_gqa_path(true, B, s_max, h, h_kv, d_h_or_dc).ws_bytes;
+    const size_t v = plan_gqa_path(false, B, s_max, h, h_kv, d_h_or_dc).ws_bytes;
+    return a > v ? a : v;
 }
 
 const char* attn_last_error(void) { return g_err.c_str(); }
@@ -202,7 +227,7 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
         if (rc) return rc;
     }
     if (B == 0) return ATTN_OK;
-    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h);
+    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b);
     if (P.ws_bytes && (!workspace || workspace_bytes < P.ws_bytes))
         return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
                     workspace ? workspace_bytes : (size_t)0);
@@ -230,8 +255,10 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
     p.scale_log2 = sc * 1.4426950408889634f;
     const long long grid = (long long)B * h_kv * P.n_hg * P.n_split;
     if (grid >= (1LL << 31)) return fail(ATTN_ENOTSUP, "problem too large for one launch");
-    hipError_t e = attn::launch_gqa_decode(p, d_h, b == 4, P.HG, block_table != nullptr,
-                                           (unsigned)grid, (hipStream_t)stream);
+    hipError_t e = P.mfma ? attn::launch_gqa_mfma(p, d_h, P.NW, block_table != nullptr,
+                                                  (unsigned)grid, (hipStream_t)stream)
+                          : attn::launch_gqa_decode(p, d_h, b == 4, P.HG, block_table != nullptr,
+                                                    (unsigned)grid, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attn_decode_gqa launch");
     return ATTN_OK;
 }

@@ -120,6 +120,29 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff)
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Physical row of token t of sequence b in a paged pool of 2^bs_log2-row
+// blocks (one scalar load).  Block numbers are clamped into the pool and the
+// logical block into the table, so a bad entry can only misplace rows, never
+// address outside the pool.
+__device__ __forceinline__ size_t paged_row(const int32_t* __restrict__ btab, int b, int t,
+                                            int max_blocks, int bs_log2, int num_blocks)
+{
+    const int lb = min(t >> bs_log2, max_blocks - 1);
+    int blk = __builtin_amdgcn_readfirstlane(btab[(size_t)b * max_blocks + lb]);
+    blk = min(max(blk, 0), num_blocks - 1);
+    return ((size_t)blk << bs_log2) + (t & ((1 << bs_log2) - 1));
+}
+
+// Workgroup j of a launch runs on XCD j % 8 (round-robin dispatch).  This
+// renumbering gives each XCD a contiguous run of work items, so that items
+// that share data (one sequence's splits or KV heads) run under one L2.  A
+// tail of n % 8 workgroups keeps its own numbering.
+__device__ __forceinline__ int xcd_major(int j, int n)
+{
+    const int full = n & ~7;
+    return j < full ? (j & 7) * (full >> 3) + (j >> 3) : j;
+}
+
 // order LDS traffic between the lanes of one wavefront
 __device__ __forceinline__ void wave_lds_sync()
 {

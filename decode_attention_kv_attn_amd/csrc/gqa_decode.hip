@@ -318,32 +318,62 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaParams p,
     }
 }
 
-// Merge of the split partials: m = max m_k, l = sum 2^(m_k-m) l_k,
-// o = sum 2^(m_k-m) o_k / l, lse = (m + log2 l) ln 2.  One wavefront per
-// (b, head), each lane owning D/64 output elements.
+// Merge of the split partials: m = max m_k over splits that saw tokens,
+// l = sum 2^(m_k-m) l_k, o = sum 2^(m_k-m) o_k / l, lse = (m + log2 l) ln 2.
+// One wavefront per (b, head), each lane owning D/64 output elements.  The
+// weights of 64 splits are computed at once (one split per lane) and then
+// broadcast; eight splits' partial rows are in flight at a time.  A split
+// with l = 0 never wrote its partial row: it is loaded but not used.
 template <int D, bool F32>
 __global__ __launch_bounds__(64) void gqa_combine_kernel(const GqaParams p)
 {
     constexpr int PL = D / 64;
     const int lane = threadIdx.x;
     const int bh = blockIdx.x;
-    const float* __restrict__ ml = p.part_ml + (size_t)bh * p.n_split * 2;
-    const float* __restrict__ po = p.part_o + (size_t)bh * p.n_split * D;
+    const int ns = p.n_split;
+    const float2* __restrict__ ml = (const float2*)p.part_ml + (size_t)bh * ns;
+    const float* __restrict__ po = p.part_o + (size_t)bh * ns * D + lane * PL;
     float M = -INFINITY;
-    for (int k = 0; k < p.n_split; k++)
-        if (ml[2 * k + 1] > 0.f) M = fmaxf(M, ml[2 * k]);
+    for (int k = lane; k < ns; k += 64) {
+        const float2 v = ml[k];
+        if (v.y > 0.f) M = fmaxf(M, v.x);
+    }
+    M = wave_max(M);
     float L = 0.f, o[PL];
 #pragma unroll
     for (int e = 0; e < PL; e++) o[e] = 0.f;
-    for (int k = 0; k < p.n_split; k++) {
-        const float lk = ml[2 * k + 1];
-        if (lk > 0.f) {
-            const float wk = __builtin_amdgcn_exp2f(ml[2 * k] - M);
-            L = fmaf(wk, lk, L);
+    for (int k0 = 0; k0 < ns; k0 += 64) {
+        float wk = 0.f;
+        if (k0 + lane < ns) {
+            const float2 v = ml[k0 + lane];
+            if (v.y > 0.f) {
+                wk = __builtin_amdgcn_exp2f(v.x - M);
+                L = fmaf(wk, v.y, L);
+            }
+        }
+        const int cnt = min(64, ns - k0);
+        for (int kk = 0; kk < cnt; kk += 8) {
+            float x[8][PL];
 #pragma unroll
-            for (int e = 0; e < PL; e++) o[e] = fmaf(wk, po[(size_t)k * D + lane * PL + e], o[e]);
+            for (int u = 0; u < 8; u++)
+                if (kk + u < cnt) {
+#pragma unroll
+                    for (int e = 0; e < PL; e++) x[u][e] = po[(size_t)(k0 + kk + u) * D + e];
+                }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                if (kk + u < cnt) {
+                    const float wu = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), kk + u));
+                    if (wu > 0.f) {
+#pragma unroll
+                        for (int e = 0; e < PL; e++) o[e] = fmaf(wu, x[u][e], o[e]);
+                    }
+                }
+            }
         }
     }
+    L = wave_sum(L);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const size_t oo = (size_t)bh * D + lane * PL;
 #pragma unroll
@@ -352,6 +382,15 @@ __global__ __launch_bounds__(64) void gqa_combine_kernel(const GqaParams p)
         else ((uint16_t*)p.out)[oo + e] = (uint16_t)f32_to_bf16_bits(o[e] * inv);
     }
     if (lane == 0 && p.lse) p.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_gqa_combine(const GqaParams& p, int d_h, bool f32, hipStream_t st)
+{
+    const unsigned cg = (unsigned)(p.B * p.h);
+    if (f32) hipLaunchKernelGGL((gqa_combine_kernel<64, true>), dim3(cg), dim3(64), 0, st, p);
+    else if (d_h == 64) hipLaunchKernelGGL((gqa_combine_kernel<64, false>), dim3(cg), dim3(64), 0, st, p);
+    else hipLaunchKernelGGL((gqa_combine_kernel<128, false>), dim3(cg), dim3(64), 0, st, p);
+    return hipGetLastError();
 }
 
 template <int D, int HG, bool F32>
@@ -383,11 +422,7 @@ hipError_t launch_gqa_decode(const GqaParams& p, int d_h, bool f32, int HG, bool
     else if (d_h == 64) e = launch_d<64, false>(p, HG, paged, grid, st);
     else e = launch_d<128, false>(p, HG, paged, grid, st);
     if (e != hipSuccess || p.n_split == 1) return e;
-    const unsigned cg = (unsigned)(p.B * p.h);
-    if (f32) hipLaunchKernelGGL((gqa_combine_kernel<64, true>), dim3(cg), dim3(64), 0, st, p);
-    else if (d_h == 64) hipLaunchKernelGGL((gqa_combine_kernel<64, false>), dim3(cg), dim3(64), 0, st, p);
-    else hipLaunchKernelGGL((gqa_combine_kernel<128, false>), dim3(cg), dim3(64), 0, st, p);
-    return hipGetLastError();
+    return launch_gqa_combine(p, d_h, f32, st);
 }
 
 }  // namespace attn

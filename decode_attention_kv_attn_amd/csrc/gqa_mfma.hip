@@ -1,0 +1,333 @@
+// Decode attention for GQA / MQA / MHA over bf16 caches on the matrix cores.
+//
+// out[b,i] = sum_t softmax_t(scale * q[b,i] . K[b,t,j]) V[b,t,j], j = i / g
+// ("The KV cache size formula", mlinterviewnotes.com: attention against all
+// previous positions; "MHA -> MQA -> GQA -> MLA", opening section: the g
+// query heads of a group share one KV head).
+//
+// The g query heads of one KV head are exactly the "many heads, one shared
+// K/V" shape that MLA decode takes in its MQA mode ("MHA -> MQA -> GQA ->
+// MLA", the MLA-decode-becomes-MQA remark): per token, one K row and one V
+// row serve g dot products each.  The vector form of that work needs about
+// 2g FLOP per cached byte of dot-product instructions, which at g >= 8 runs
+// into the vector ALU before HBM.  Here the products run as bf16 MFMA with
+// the heads padded to 16, so the ALU only carries the softmax:
+//
+//  * workgroup = (b, KV head j, token split); wavefront w takes query heads
+//    16w .. 16w+15 of the group (1 to 4 wavefronts, g <= 64);
+//  * K and V tiles of 32 tokens move HBM -> LDS by LDS-DMA (buffer_load ...
+//    lds) into a ring of NBUF buffers, NBUF - 1 tiles ahead of use; completion is
+//    tracked with explicit vmcnt waits (no other vector-memory instruction is
+//    outstanding inside the loop);
+//  * S^T[32 tok x 16 heads] = K_tile . q^T   (v_mfma_f32_16x16x32_bf16, K rows
+//    from LDS, q in registers);
+//  * online softmax per head (log2 domain, lazily rescaled: the reference max
+//    moves only when a tile exceeds it by more than 8), P rounded to bf16;
+//  * O^T[d_h x 16 heads] += V_tile^T . P^T, the V operand read with
+//    transposing LDS reads; the score output layout is the K order of this
+//    product, so P stays in registers;
+//  * splits write (m, l, o) partials that the merge kernel combines through
+//    their log-sum-exp ("MLA: why one latent can replace a multi-head KV
+//    cache", charlestar.github.io, section on what FlashMLA solves).
+#include "common.h"
+#include "kernels.h"
+#include "mfma_lds.h"
+
+namespace attn {
+
+#ifndef GQA_MFMA_NBUF
+#define GQA_MFMA_NBUF 4
+#endif
+
+template <int D>
+struct MfmaCfg {
+    static constexpr int T = 32;               // tokens per tile
+    static constexpr int RB = D * 2;           // bytes of one row (one KV head)
+    static constexpr int NCH = RB / 16;        // 16-byte chunks per row
+    static constexpr int KT = T * RB;          // bytes of a K (or V) tile
+    static constexpr int RPO = 1024 / RB;      // rows per DMA instruction
+    static constexpr int OPS = 2 * KT / 1024;  // DMA instructions per tile (K, then V)
+    static constexpr int NBUF = GQA_MFMA_NBUF; // ring depth (NBUF - 1 tiles in flight)
+    static constexpr int KS = D / 32;          // score K steps
+    static constexpr int MC = D / 16;          // value M tiles (head dimensions)
+};
+
+// XOR swizzle of the 16-byte chunk position within a row: logical chunk c of
+// tile row r sits at c ^ gswz(r).  Rows r and r + 16 share a value.  For
+// 256-byte rows, rows 0..15 get 16 distinct positions (score operands read
+// 16 rows at one chunk) and every 4 consecutive rows get distinct aligned
+// chunk pairs (the transposing reads take 4 rows x 32 bytes).
+template <int D>
+__device__ __forceinline__ int gswz(int r)
+{
+    r &= 15;
+    if (D == 128) return (2 * r + (r >> 3)) & 15;
+    return (r & 1) ^ (r & 2) ^ ((r & 4) ? 5 : 0) ^ ((r & 8) ? 7 : 0);
+}
+
+// Per-lane byte offsets of the MFMA operands within a K or V tile buffer.
+//   score operand (K step ks, row block mt): row 16 mt + li, chunk 4 ks + G
+//   value operand (M tile mc, token half th): rows 4G + li/4 + 16 th, chunk
+//     2 mc + (li % 4) / 2, byte 8 (li % 2) within it
+template <int D>
+struct GTileOffsets {
+    int sc[D / 32];
+    int tr[D / 16];
+    __device__ __forceinline__ GTileOffsets(int li, int G)
+    {
+        constexpr int RB = D * 2;
+        const int ss = gswz<D>(li);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ks++) sc[ks] = li * RB + (((4 * ks + G) ^ ss) << 4);
+        const int r = 4 * G + li / 4, cp = (li % 4) / 2, st = gswz<D>(r);
+#pragma unroll
+        for (int mc = 0; mc < D / 16; mc++) tr[mc] = r * RB + (((2 * mc + cp) ^ st) << 4) + 8 * (li % 2);
+    }
+};
+
+template <int D, int NW, bool PAGED>
+__global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
+                                                           const int32_t* __restrict__ btab)
+{
+    using C = MfmaCfg<D>;
+    constexpr int OPW = C::OPS / NW;   // DMA instructions per wavefront and tile
+    static_assert(C::OPS % NW == 0, "DMA instructions must split evenly");
+    __shared__ __attribute__((aligned(1024))) uint8_t Ls[C::NBUF * 2 * C::KT];
+
+    const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    // work item (b, split, j) with j fastest, renumbered XCD-major so that the
+    // KV heads and neighbouring splits of one sequence run on one XCD
+    int w = xcd_major(blockIdx.x, gridDim.x);
+    const int j = w % p.h_kv;
+    w /= p.h_kv;
+    const int split = w % p.n_split;
+    const int b = w / p.n_split;
+    const int g = p.h / p.h_kv;
+    const int nh = min(16, g - 16 * wave);          // query heads of this wavefront
+    const bool active = nh > 0;
+    const int head = j * g + 16 * wave + li;        // this lane's head when li < nh
+    const bool hv = li < nh;
+
+    const int32_t* __restrict__ s_len = p.s;
+    int n = __builtin_amdgcn_readfirstlane(s_len[b]);
+    n = min(max(n, 0), p.s_max);
+    const int t0 = split * p.chunk;
+    const int t1 = min(n, t0 + p.chunk);
+
+    if (t0 >= t1) {   // nothing to attend to in this split
+        if (active && hv) {
+            if (p.n_split > 1) {
+                if (G == 0) {
+                    float* ml = p.part_ml + ((size_t)(b * p.h + head) * p.n_split + split) * 2;
+                    ml[0] = -INFINITY;
+                    ml[1] = 0.f;
+                }
+            } else {
+                uint16_t* o = (uint16_t*)p.out + (size_t)(b * p.h + head) * D;
+#pragma unroll
+                for (int mc = 0; mc < C::MC; mc++) *(uint2*)(o + 16 * mc + 4 * G) = make_uint2(0, 0);
+                if (G == 0 && p.lse) p.lse[b * p.h + head] = -INFINITY;
+            }
+        }
+        return;
+    }
+
+    // DMA instruction q of a tile (q < OPS/2: K, else V) moves tile rows
+    // RPO (q % (OPS/2)) .. + RPO-1; lane l writes row l / NCH, physical chunk
+    // l % NCH, i.e. logical chunk (l % NCH) ^ gswz(row).  A tile's two
+    // 16-token halves each lie in one block of a paged pool (blocks hold a
+    // power of two >= 16 of rows), so a tile needs the physical rows of just
+    // its two half starts; they are looked up one iteration before the tile
+    // is issued, keeping the scalar-load latency off the issue path.
+    const size_t rowstride = (size_t)p.h_kv * C::RB;   // bytes between tokens of one head
+    const uint8_t* __restrict__ kb = (const uint8_t*)p.k + (size_t)j * C::RB;
+    const uint8_t* __restrict__ vb = (const uint8_t*)p.v + (size_t)j * C::RB;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Ls;
+    const int lr = lane / C::NCH, lp = lane % C::NCH;
+    auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
+        if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
+        return (size_t)b * p.s_max + t;
+    };
+    auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
+#pragma unroll
+        for (int jj = 0; jj < OPW; jj++) {
+            const int q = wave + NW * jj;
+            const bool isv = q >= C::OPS / 2;
+            const int rb = isv ? q - C::OPS / 2 : q;
+            const int rt = rb * C::RPO;               // first tile row of this instruction
+            const int r0 = tb + rt;
+            const size_t row = (rt < 16 ? row0 : row1) + (rt & 15);
+            const int nv = min(C::RPO, t1 - r0);      // rows inside the split
+            const int nr = nv > 0 ? (nv - 1) * (int)rowstride + C::RB : 0;
+            const rsrc_t rs = make_rsrc((isv ? vb : kb) + row * rowstride, nr);
+            const int c = lp ^ gswz<D>(rt + lr);
+            dma16(rs, (uint32_t)(lr * (int)rowstride + c * 16),
+                  lds0 + buf * 2 * C::KT + (isv ? C::KT : 0) + rb * 1024);
+        }
+    };
+
+    f32x4 O[C::MC];
+#pragma unroll
+    for (int mc = 0; mc < C::MC; mc++) O[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    // two tiles in flight, then q (the B operand of the score product; zero
+    // for padding heads), then the third tile
+    // NBUF - 2 tiles in flight, then q (the B operand of the score product;
+    // zero for padding heads), then one more tile
+#pragma unroll
+    for (int i = 0; i < C::NBUF - 2; i++) {
+        const size_t a0 = half_row(t0 + i * C::T), a1 = half_row(t0 + i * C::T + 16);
+        issue_tile(t0 + i * C::T, i, a0, a1);
+    }
+    bf16x8 Qf[C::KS];
+    {
+        const uint16_t* qrow = (const uint16_t*)p.q + (size_t)(b * p.h + head) * D + 8 * G;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ks++)
+            Qf[ks] = (active && hv) ? *(const bf16x8*)(qrow + 32 * ks)
+                                    : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+    vmem_drain();
+    {
+        constexpr int L = C::NBUF - 2;
+        issue_tile(t0 + L * C::T, L, half_row(t0 + L * C::T), half_row(t0 + L * C::T + 16));
+    }
+
+    const GTileOffsets<D> to(li, G);
+    int buf = 0;
+    for (int tb = t0; tb < t1; tb += C::T) {
+        constexpr int AH = C::NBUF - 1;   // tiles in flight ahead of this one
+        const size_t nx0 = half_row(tb + AH * C::T), nx1 = half_row(tb + AH * C::T + 16);
+        wait_vmcnt<(AH - 1) * OPW>();   // tiles tb + T .. tb + (AH-1) T were issued after this one
+        __syncthreads();
+        // refill the buffer read in the previous iteration (every wavefront is
+        // past it), so that AH tiles stay in flight while this one is used
+        issue_tile(tb + AH * C::T, (buf + AH) % C::NBUF, nx0, nx1);
+        const uint8_t* Kt = Ls + buf * 2 * C::KT;
+        const uint8_t* Vt = Kt + C::KT;
+        if (active) {
+            // ---- scores S^T = K . q^T, operands read one K step ahead
+            f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            bf16x8 a[2][2];
+            a[0][0] = lds_read_16_as_2x8(Kt + to.sc[0]);
+            a[0][1] = lds_read_16_as_2x8(Kt + to.sc[0] + 16 * C::RB);
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ks++) {
+                if (ks + 1 < C::KS) {
+                    a[(ks + 1) & 1][0] = lds_read_16_as_2x8(Kt + to.sc[ks + 1]);
+                    a[(ks + 1) & 1][1] = lds_read_16_as_2x8(Kt + to.sc[ks + 1] + 16 * C::RB);
+                }
+                S[0] = mfma16(a[ks & 1][0], Qf[ks], S[0]);
+                S[1] = mfma16(a[ks & 1][1], Qf[ks], S[1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // ---- online softmax: lane holds head li, tokens 16 mt + 4G + e
+            float z[2][4];
+            float lm = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int tok = tb + 16 * mt + 4 * G + e;
+                    z[mt][e] = tok < t1 ? S[mt][e] * p.scale_log2 : -INFINITY;
+                    lm = fmaxf(lm, z[mt][e]);
+                }
+            lm = fmaxf(lm, xor16(lm));
+            lm = fmaxf(lm, xor32(lm));
+            const bool move = lm > m + 8.f;
+            const float mn = move ? lm : m;
+            const float alpha = move ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+            m = mn;
+            uint32_t pk[4];
+            float ps = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mn),
+                                                    __builtin_amdgcn_exp2f(z[mt][e + 1] - mn));
+                    pk[mt * 2 + e / 2] = wv;
+                    ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
+                }
+            lsum = lsum * alpha + ps;
+            if (__builtin_amdgcn_ballot_w64(move)) {
+#pragma unroll
+                for (int mc = 0; mc < C::MC; mc++) O[mc] *= alpha;
+            }
+            const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            // ---- O^T += V^T . P^T (transposing reads of the V tile)
+            s16x4 lo[2], hi[2];
+            lo[0] = lds_read_tr(Vt + to.tr[0]);
+            hi[0] = lds_read_tr(Vt + to.tr[0] + 16 * C::RB);
+#pragma unroll
+            for (int mc = 0; mc < C::MC; mc++) {
+                if (mc + 1 < C::MC) {
+                    lo[(mc + 1) & 1] = lds_read_tr(Vt + to.tr[mc + 1]);
+                    hi[(mc + 1) & 1] = lds_read_tr(Vt + to.tr[mc + 1] + 16 * C::RB);
+                }
+                O[mc] = mfma16(cat_tr(lo[mc & 1], hi[mc & 1]), P, O[mc]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        buf = (buf + 1) % C::NBUF;
+    }
+    wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
+
+    if (!active) return;
+    float l = lsum;
+    l += xor16(l);
+    l += xor32(l);
+    if (!hv) return;
+    if (p.n_split == 1) {
+        const float inv = 1.f / l;
+        uint16_t* o = (uint16_t*)p.out + (size_t)(b * p.h + head) * D + 4 * G;
+#pragma unroll
+        for (int mc = 0; mc < C::MC; mc++)
+            *(uint2*)(o + 16 * mc) = make_uint2(pack_bf16x2(O[mc][0] * inv, O[mc][1] * inv),
+                                                pack_bf16x2(O[mc][2] * inv, O[mc][3] * inv));
+        if (G == 0 && p.lse) p.lse[b * p.h + head] = (m + __log2f(l)) * kLn2;
+    } else {
+        const size_t pi = (size_t)(b * p.h + head) * p.n_split + split;
+        float* po = p.part_o + pi * D + 4 * G;
+#pragma unroll
+        for (int mc = 0; mc < C::MC; mc++)
+            *(float4*)(po + 16 * mc) = make_float4(O[mc][0], O[mc][1], O[mc][2], O[mc][3]);
+        if (G == 0) {
+            p.part_ml[pi * 2] = m;
+            p.part_ml[pi * 2 + 1] = l;
+        }
+    }
+}
+
+template <int D, int NW>
+static hipError_t launch_nw(const GqaParams& p, bool paged, unsigned grid, hipStream_t st)
+{
+    if (paged)
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+    else
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_mfma_d(const GqaParams& p, int NW, bool paged, unsigned grid, hipStream_t st)
+{
+    switch (NW) {
+    case 1: return launch_nw<D, 1>(p, paged, grid, st);
+    case 2: return launch_nw<D, 2>(p, paged, grid, st);
+    default: return launch_nw<D, 4>(p, paged, grid, st);
+    }
+}
+
+hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, unsigned grid,
+                           hipStream_t st)
+{
+    hipError_t e = d_h == 64 ? launch_mfma_d<64>(p, NW, paged, grid, st)
+                             : launch_mfma_d<128>(p, NW, paged, grid, st);
+    if (e != hipSuccess || p.n_split == 1) return e;
+    return launch_gqa_combine(p, d_h, false, st);
+}
+
+}  // namespace attn

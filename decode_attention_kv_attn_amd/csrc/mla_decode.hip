@@ -17,45 +17,9 @@
 // each latent row is fetched from HBM once per call.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_lds.h"
 
 namespace attn {
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
-// source lane i = a + 4k supplies 4 consecutive 16-bit values M_i[0..3];
-// destination lane 4a + c receives M_{a}[c], M_{a+4}[c], M_{a+8}[c],
-// M_{a+12}[c].  Pointing source lane i at row (row0 + i/4), column
-// (col0 + 4*(i%4)) of a row-major bf16 matrix therefore hands lane j the
-// column col0 + j of rows row0 .. row0+3: an MFMA operand with K along rows.
-__device__ __forceinline__ s16x4 lds_read_tr(const uint8_t* p)
-{
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-}
-
-// 16 bytes of LDS as two 8-byte reads (ds_read_b64 x 2).  The volatile
-// accesses keep the compiler from fusing them into one 16-byte read.
-__device__ __forceinline__ bf16x8 lds_read_16_as_2x8(const uint8_t* p)
-{
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    typedef __attribute__((address_space(3))) volatile const u32x2 lds_u32x2;
-    const u32x2 lo = *(lds_u32x2*)p;
-    const u32x2 hi = *(lds_u32x2*)(p + 8);
-    return __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], hi[0], hi[1]));
-}
-
-__device__ __forceinline__ bf16x8 cat_tr(s16x4 lo, s16x4 hi)
-{
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
 
 // ---------------------------------------------------------------------------
 // 1. absorbed query.  Workgroup (4 wavefronts) per (head i, 128 latent
@@ -171,10 +135,12 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 }
 
 // ---------------------------------------------------------------------------
-// 2. decode.  Workgroup = (b, token split): 8 wavefronts x 16 heads = all
-//    heads, so every latent tile is fetched once.  Tiles of 32 rows move
-//    HBM -> LDS by LDS-DMA (buffer_load ... lds, no staging registers) into a
-//    ring of 4 buffers, three tiles ahead of use.  Per wavefront and tile:
+// 2. decode.  Workgroup = (b, token split) with all heads, so every latent
+//    tile is fetched once: 4 wavefronts x 32 heads in the fast kernel (one
+//    wavefront per SIMD, accumulators in AGPRs), 8 x 16 in the rescaling
+//    fallback.  Tiles of 32 rows move HBM -> LDS by LDS-DMA (buffer_load ...
+//    lds, no staging registers) into a ring of 4 buffers, three tiles ahead
+//    of use.  Per wavefront, 16-head block and tile:
 //      S^T[32 tok x 16 heads] = C_tile[32 x 576] . q^T     (A: LDS, B: q^ in registers)
 //      online softmax on S^T (lane = head, 8 tokens per lane)
 //      U^T[512 x 16] += C_tile^T[512 x 32] . P^T[32 x 16]  (A: transposing LDS reads, B: P)
@@ -249,35 +215,6 @@ struct TileOffsets {
     }
 };
 
-// 16 bytes per lane from the buffer resource to LDS at m0 + 16 * lane.  Issued
-// through asm so that the compiler does not serialise it against every LDS
-// read; completion is awaited explicitly with wait_vmcnt<N>().
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(r), "s"(lds_addr) : "memory");
-}
-// vmcnt(0) through the builtin, so that the compiler knows its own vector
-// loads have completed and inserts no waits for them later
-__device__ __forceinline__ void vmem_drain()
-{
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt unconstrained
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-// Workgroup j of a launch runs on XCD j % 8 (round-robin dispatch).  The
-// decode grid is renumbered so that each XCD receives a contiguous run of
-// (b, split) pairs: the splits of one sequence then share q^[b] in that XCD's
-// L2.  A tail of n % 8 workgroups keeps its own numbering.
-__device__ __forceinline__ int xcd_major(int j, int n)
-{
-    const int full = n & ~7;
-    return j < full ? (j & 7) * (full >> 3) + (j >> 3) : j;
-}
 
 template <int HW, bool PAGED>
 __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const MlaParams p,
@@ -288,6 +225,8 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
     constexpr int SPW = kSlots / NW + (kSlots % NW ? 1 : 0);   // DMA slots per wavefront
     constexpr int KS = 576 / 32;    // score K steps
     constexpr int MC = 512 / 16;    // value M tiles (latent columns)
+    constexpr int PS = 1;   // score operands are read this many K steps ahead
+    constexpr int PV = 1;   // value operands are read this many column tiles ahead
     __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * kTile];
     __shared__ int ovf;   // some head's scores ran past its reference max + 64
 
@@ -325,25 +264,22 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs;
     const int lr = lane / 8;                      // row within the slot
     const int lp = lane % 8;                      // physical chunk within the segment
-    auto issue_tile = [&](int tb, int buf) {
+    // A tile's two 16-row halves each lie in one block of a paged pool
+    // (blocks hold a power of two >= 16 rows); their physical rows are looked
+    // up one iteration before the tile is issued.
+    auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
+        if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
+        return (size_t)b * p.s_max + t;
+    };
+    auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
 #pragma unroll
         for (int j = 0; j < SPW; j++) {
             const int q = wave + NW * j;
             if (q < kSlots) {                      // wave-uniform
                 const int seg = q >> 2, rb = q & 3;
                 const int r0 = tb + 8 * rb;        // first row of the slot
-                const uint8_t* base;
-                if (PAGED) {
-                    const int lb = r0 >> p.bs_log2;
-                    const int bstart = lb << p.bs_log2;
-                    int blk = __builtin_amdgcn_readfirstlane(
-                        btab[(size_t)b * p.max_blocks + min(lb, p.max_blocks - 1)]);
-                    blk = min(max(blk, 0), p.num_blocks - 1);
-                    base = cbase + (((size_t)blk << p.bs_log2) + (r0 - bstart)) * kRow;
-                } else {
-                    base = cbase + ((size_t)b * p.s_max + r0) * kRow;
-                }
-                const rsrc_t rs = make_rsrc(base, max(0, min(8, t1 - r0)) * kRow);
+                const size_t row = (rb < 2 ? row0 : row1) + 8 * (rb & 1);
+                const rsrc_t rs = make_rsrc(cbase + row * kRow, max(0, min(8, t1 - r0)) * kRow);
                 const int c = 8 * seg + (lp ^ swz(8 * rb + lr));
                 dma16(rs, (uint32_t)(lr * kRow + c * 16), lds0 + buf * kTile + q * 1024);
             }
@@ -367,8 +303,12 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
 
     // first two tiles in flight, then the q^ fragments (B operand of the
     // score product; head tiles past h read as zeros), then the third tile
-    issue_tile(t0, 0);
-    issue_tile(t0 + kT, 1);
+    {
+        const size_t a0 = half_row(t0), a1 = half_row(t0 + 16);
+        const size_t b0 = half_row(t0 + kT), b1 = half_row(t0 + kT + 16);
+        issue_tile(t0, 0, a0, a1);
+        issue_tile(t0 + kT, 1, b0, b1);
+    }
     bf16x8 Qf[NT][KS];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++)
@@ -378,16 +318,20 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
                 ? *(const bf16x8*)(p.qhat + ((size_t)b * p.h + head0 + 16 * nt + li) * 576 + ks * 32 + 8 * G)
                 : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     vmem_drain();
-    issue_tile(t0 + 2 * kT, 2);
+    issue_tile(t0 + 2 * kT, 2, half_row(t0 + 2 * kT), half_row(t0 + 2 * kT + 16));
 
     const TileOffsets to(li, G);
     int buf = 0;
     for (int tb = t0; tb < t1; tb += kT) {
+        const size_t nx0 = half_row(tb + 3 * kT), nx1 = half_row(tb + 3 * kT + 16);
         // tiles tb + T and tb + 2T were issued after this one
         if (SPW * NW == kSlots || wave < kSlots % NW) wait_vmcnt<2 * SPW>();
         else wait_vmcnt<2 * (SPW - 1)>();
         __syncthreads();
         if (ovf) break;                      // uniform across the workgroup
+        // refill the buffer read in the previous iteration (every wavefront is
+        // past it), so that three tiles stay in flight while this one is used
+        issue_tile(tb + 3 * kT, (buf + 3) % kNBuf, nx0, nx1);
         const uint8_t* C = Cs + buf * kTile;
         if (active) {
             // ---- scores S^T = C . q^T
@@ -396,19 +340,23 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
             for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int nt = 0; nt < NT; nt++) S[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 a[2][2];   // [K step parity][mt]
-            a[0][0] = lds_read_16_as_2x8(to.score(C, 0, 0));
-            a[0][1] = lds_read_16_as_2x8(to.score(C, 0, 1));
+            bf16x8 a[PS + 1][2];   // ring of operands, PS K steps ahead
+#pragma unroll
+            for (int i = 0; i < PS; i++) {
+                a[i][0] = lds_read_16_as_2x8(to.score(C, i, 0));
+                a[i][1] = lds_read_16_as_2x8(to.score(C, i, 1));
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
-                if (ks + 1 < KS) {
-                    a[(ks + 1) & 1][0] = lds_read_16_as_2x8(to.score(C, ks + 1, 0));
-                    a[(ks + 1) & 1][1] = lds_read_16_as_2x8(to.score(C, ks + 1, 1));
+                if (ks + PS < KS) {
+                    a[(ks + PS) % (PS + 1)][0] = lds_read_16_as_2x8(to.score(C, ks + PS, 0));
+                    a[(ks + PS) % (PS + 1)][1] = lds_read_16_as_2x8(to.score(C, ks + PS, 1));
                 }
 #pragma unroll
                 for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-                    for (int nt = 0; nt < NT; nt++) S[mt][nt] = mfma16(a[ks & 1][mt], Qf[nt][ks], S[mt][nt]);
+                    for (int nt = 0; nt < NT; nt++)
+                        S[mt][nt] = mfma16(a[ks % (PS + 1)][mt], Qf[nt][ks], S[mt][nt]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- softmax weights against the fixed per-head reference m
@@ -448,23 +396,24 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
             }
             if (__builtin_amdgcn_ballot_w64(over) && lane == 0) ovf = 1;
             // ---- latent sum U^T += C^T . P^T (transposing reads of the same tile)
-            s16x4 lo[2], hi[2];
-            lo[0] = lds_read_tr(to.value(C, 0, 0));
-            hi[0] = lds_read_tr(to.value(C, 0, 1));
+            s16x4 lo[PV + 1], hi[PV + 1];   // ring of operands, PV column tiles ahead
+#pragma unroll
+            for (int i = 0; i < PV; i++) {
+                lo[i] = lds_read_tr(to.value(C, i, 0));
+                hi[i] = lds_read_tr(to.value(C, i, 1));
+            }
 #pragma unroll
             for (int mc = 0; mc < MC; mc++) {
-                if (mc + 1 < MC) {
-                    lo[(mc + 1) & 1] = lds_read_tr(to.value(C, mc + 1, 0));
-                    hi[(mc + 1) & 1] = lds_read_tr(to.value(C, mc + 1, 1));
+                if (mc + PV < MC) {
+                    lo[(mc + PV) % (PV + 1)] = lds_read_tr(to.value(C, mc + PV, 0));
+                    hi[(mc + PV) % (PV + 1)] = lds_read_tr(to.value(C, mc + PV, 1));
                 }
-                const bf16x8 av = cat_tr(lo[mc & 1], hi[mc & 1]);
+                const bf16x8 av = cat_tr(lo[mc % (PV + 1)], hi[mc % (PV + 1)]);
 #pragma unroll
                 for (int nt = 0; nt < NT; nt++) U[mc][nt] = mfma16(av, P[nt], U[mc][nt]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // refill the buffer read one iteration ago (all waves are past it)
-        issue_tile(tb + 3 * kT, (buf + 3) % kNBuf);
         buf = (buf + 1) % kNBuf;
     }
     wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
@@ -528,25 +477,22 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs;
     const int lr = lane / 8;                      // row within the slot
     const int lp = lane % 8;                      // physical chunk within the segment
-    auto issue_tile = [&](int tb, int buf) {
+    // A tile's two 16-row halves each lie in one block of a paged pool
+    // (blocks hold a power of two >= 16 rows); their physical rows are looked
+    // up one iteration before the tile is issued.
+    auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
+        if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
+        return (size_t)b * p.s_max + t;
+    };
+    auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
 #pragma unroll
         for (int j = 0; j < 5; j++) {
             const int q = wave + 8 * j;
             if (q < kSlots) {                      // wave-uniform
                 const int seg = q >> 2, rb = q & 3;
                 const int r0 = tb + 8 * rb;        // first row of the slot
-                const uint8_t* base;
-                if (PAGED) {
-                    const int lb = r0 >> p.bs_log2;
-                    const int bstart = lb << p.bs_log2;
-                    int blk = __builtin_amdgcn_readfirstlane(
-                        btab[(size_t)b * p.max_blocks + min(lb, p.max_blocks - 1)]);
-                    blk = min(max(blk, 0), p.num_blocks - 1);
-                    base = cbase + (((size_t)blk << p.bs_log2) + (r0 - bstart)) * kRow;
-                } else {
-                    base = cbase + ((size_t)b * p.s_max + r0) * kRow;
-                }
-                const rsrc_t rs = make_rsrc(base, max(0, min(8, t1 - r0)) * kRow);
+                const size_t row = (rb < 2 ? row0 : row1) + 8 * (rb & 1);
+                const rsrc_t rs = make_rsrc(cbase + row * kRow, max(0, min(8, t1 - r0)) * kRow);
                 const int c = 8 * seg + (lp ^ swz(8 * rb + lr));
                 dma16(rs, (uint32_t)(lr * kRow + c * 16), lds0 + buf * kTile + q * 1024);
             }
@@ -560,23 +506,31 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
 
     // first two tiles in flight, then the q^ fragments (B operand of the
     // score product; zeros for wavefronts past h), then the third tile
-    issue_tile(t0, 0);
-    issue_tile(t0 + kT, 1);
+    {
+        const size_t a0 = half_row(t0), a1 = half_row(t0 + 16);
+        const size_t b0 = half_row(t0 + kT), b1 = half_row(t0 + kT + 16);
+        issue_tile(t0, 0, a0, a1);
+        issue_tile(t0 + kT, 1, b0, b1);
+    }
     bf16x8 Qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
         Qf[ks] = active ? *(const bf16x8*)(p.qhat + ((size_t)b * p.h + head0 + li) * 576 + ks * 32 + 8 * G)
                         : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     vmem_drain();
-    issue_tile(t0 + 2 * kT, 2);
+    issue_tile(t0 + 2 * kT, 2, half_row(t0 + 2 * kT), half_row(t0 + 2 * kT + 16));
 
     const TileOffsets to(li, G);
     int buf = 0;
     for (int tb = t0; tb < t1; tb += kT) {
+        const size_t nx0 = half_row(tb + 3 * kT), nx1 = half_row(tb + 3 * kT + 16);
         // tiles tb + T and tb + 2T were issued after this one
         if (wave < 4) wait_vmcnt<10>();
         else wait_vmcnt<8>();
         __syncthreads();
+        // refill the buffer read in the previous iteration (every wavefront is
+        // past it), so that three tiles stay in flight while this one is used
+        issue_tile(tb + 3 * kT, (buf + 3) % kNBuf, nx0, nx1);
         const uint8_t* C = Cs + buf * kTile;
         if (active) {
             // ---- scores S^T = C . q^T
@@ -649,8 +603,6 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // refill the buffer read one iteration ago (all waves are past it)
-        issue_tile(tb + 3 * kT, (buf + 3) % kNBuf);
         buf = (buf + 1) % kNBuf;
     }
     wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
@@ -819,10 +771,10 @@ hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
     if (e != hipSuccess) return e;
     const unsigned g2 = (unsigned)(p.B * p.n_split);
     if (paged) {
-        hipLaunchKernelGGL((mla_decode_fast_kernel<16, true>), dim3(g2), dim3(512), 0, st, p, p.bt);
+        hipLaunchKernelGGL((mla_decode_fast_kernel<32, true>), dim3(g2), dim3(256), 0, st, p, p.bt);
         hipLaunchKernelGGL((mla_decode_safe_kernel<true>), dim3(g2), dim3(512), 0, st, p, p.bt);
     } else {
-        hipLaunchKernelGGL((mla_decode_fast_kernel<16, false>), dim3(g2), dim3(512), 0, st, p, p.bt);
+        hipLaunchKernelGGL((mla_decode_fast_kernel<32, false>), dim3(g2), dim3(256), 0, st, p, p.bt);
         hipLaunchKernelGGL((mla_decode_safe_kernel<false>), dim3(g2), dim3(512), 0, st, p, p.bt);
     }
     e = hipGetLastError();

@@ -46,7 +46,11 @@ def test_tiny_fp32_uniform_lengths(s):
     run_small(2, 8, 2, 64, s * 2, 4, seed=1)
 
 
-@pytest.mark.parametrize("h,h_kv", [(8, 8), (8, 4), (16, 4), (32, 8), (16, 2), (64, 1), (12, 4), (6, 2)])
+# g = 1 .. 64 run on the matrix-core kernel (one to four wavefronts of 16
+# heads, the last one possibly partial or idle); g = 96 and 128 take the
+# vector kernel
+@pytest.mark.parametrize("h,h_kv", [(8, 8), (8, 4), (16, 4), (32, 8), (16, 2), (64, 1), (12, 4), (6, 2),
+                                    (40, 2), (48, 1), (96, 1), (128, 1)])
 @pytest.mark.parametrize("d_h", [64, 128])
 def test_bf16_group_sizes(h, h_kv, d_h):
     run_small(3, h, h_kv, d_h, (1, 77, 300), 2, seed=h * 100 + h_kv)

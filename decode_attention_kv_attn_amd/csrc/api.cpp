@@ -101,32 +101,29 @@ GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b)
     return plan_gqa_path(gqa_uses_mfma(h, h_kv, b), B, s_max, h, h_kv, d_h);
 }
 
-// ---- MLA split plan -----------------------------------------------------------
-// Work item = (b, token split), all h heads together so every latent tile is
-// read once.  Aim for about 256 workgroups (one 4-wavefront group per CU),
-// splits of at least 256 tokens, multiples of the 32-token tile.
+// ---- MLA plan ----------------------------------------------------------------
+// Decode runs as n_wg = 256 workgroups (one 4-wavefront group per CU), each
+// taking an equal share of all cached 32-token tiles (at least 8 tiles);
+// the shares are computed on the device from the lengths.  A workgroup
+// leaves one partial per sequence it touches, so n_wg + B - 1 partial slots
+// cover every schedule.
 struct MlaPlan {
-    int n_split, chunk;
-    size_t qhat_bytes, part_u_bytes, part_ml_bytes, flag_bytes, ws_bytes;
+    int n_wg, min_tiles;
+    size_t qhat_bytes, part_u_bytes, part_ml_bytes, flag_bytes, sched_bytes, ws_bytes;
 };
 
-MlaPlan plan_mla(int B, int s_max, int h, int d_c, int d_R)
+MlaPlan plan_mla(int B, int h, int d_c, int d_R)
 {
     MlaPlan P{};
-    const long long T = 32, target = 256, min_chunk = 256;
-    long long ns = B > 0 ? cdiv(target, B) : 1;
-    const long long ns_max = s_max > 0 ? cdiv(s_max, min_chunk) : 1;
-    if (ns > ns_max) ns = ns_max;
-    if (ns < 1) ns = 1;
-    long long chunk = s_max > 0 ? cdiv(cdiv(s_max, ns), T) * T : T;
-    ns = s_max > 0 ? cdiv(s_max, chunk) : 1;
-    P.n_split = (int)ns;
-    P.chunk = (int)chunk;
+    P.n_wg = 256;
+    P.min_tiles = 8;
+    const size_t slots = (size_t)P.n_wg + B - 1;
     P.qhat_bytes = align256((size_t)B * h * (d_c + d_R) * 2);
-    P.part_u_bytes = align256((size_t)B * P.n_split * h * d_c * sizeof(float));
-    P.part_ml_bytes = align256((size_t)B * P.n_split * h * 2 * sizeof(float));
-    P.flag_bytes = align256((size_t)B * P.n_split * sizeof(int32_t));
-    P.ws_bytes = P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.flag_bytes;
+    P.part_u_bytes = align256(slots * h * d_c * sizeof(float));
+    P.part_ml_bytes = align256(slots * h * 2 * sizeof(float));
+    P.flag_bytes = align256((size_t)P.n_wg * sizeof(int32_t));
+    P.sched_bytes = align256(((size_t)B + 1 + P.n_wg + 1) * sizeof(int32_t));
+    P.ws_bytes = P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.flag_bytes + P.sched_bytes;
     return P;
 }
 
@@ -166,7 +163,7 @@ size_t attn_decode_workspace_bytes(int is_mla, int B, int s_max, int h, int h_kv
                                    int d_R)
 {
     if (B <= 0 || h <= 0 || s_max < 0 || d_h_or_dc <= 0) return 0;
-    if (is_mla) return plan_mla(B, s_max, h, d_h_or_dc, d_R < 0 ? 0 : d_R).ws_bytes;
+    if (is_mla) return plan_mla(B, h, d_h_or_dc, d_R < 0 ? 0 : d_R).ws_bytes;
     if (h_kv <= 0 || h % h_kv != 0) return 0;
     // the storage type is not an argument: size for whichever kernel runs
     const size_t a = plan_gqa_path(true, B, s_max, h, h_kv, d_h_or_dc).ws_bytes;
@@ -278,7 +275,7 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     if (d_c != 512 || d_R != 64)
         return fail(ATTN_ENOTSUP, "MLA supports d_c=512, d_R=64 (got %d, %d)", d_c, d_R);
     if (h % 16 != 0 || h > 128) return fail(ATTN_ENOTSUP, "MLA needs h a multiple of 16, <= 128");
-    if ((long long)B * plan_mla(B, s_max, h, d_c, d_R).n_split >= (1LL << 31))
+    if ((long long)B * s_max >= (1LL << 31))
         return fail(ATTN_ENOTSUP, "problem too large for one launch");
     if (d_nope % 32 != 0 || d_nope > 256 || d_v % 16 != 0 || d_v > 256)
         return fail(ATTN_ENOTSUP, "MLA needs d_nope a multiple of 32, d_v of 16, both <= 256");
@@ -287,7 +284,7 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
         if (rc) return rc;
     }
     if (B == 0) return ATTN_OK;
-    const MlaPlan P = plan_mla(B, s_max, h, d_c, d_R);
+    const MlaPlan P = plan_mla(B, h, d_c, d_R);
     if (!workspace || workspace_bytes < P.ws_bytes)
         return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
                     workspace ? workspace_bytes : (size_t)0);
@@ -307,6 +304,7 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     p.part_u = (float*)(ws + P.qhat_bytes);
     p.part_ml = (float*)(ws + P.qhat_bytes + P.part_u_bytes);
     p.flags = (int32_t*)(ws + P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes);
+    p.sched = (int32_t*)(ws + P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.flag_bytes);
     p.max_blocks = max_blocks;
     p.bs_log2 = block_table ? ilog2(block_size) : 0;
     p.num_blocks = num_blocks;
@@ -317,8 +315,8 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     p.d_R = d_R;
     p.d_nope = d_nope;
     p.d_v = d_v;
-    p.n_split = P.n_split;
-    p.chunk = P.chunk;
+    p.n_wg = P.n_wg;
+    p.min_tiles = P.min_tiles;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)(d_nope + d_R));
     p.scale_log2 = sc * 1.4426950408889634f;
     hipError_t e = attn::launch_mla(p, block_table != nullptr, (hipStream_t)stream);

@@ -54,12 +54,13 @@ struct MlaParams {
     const int32_t* s;
     const int32_t* bt;
     uint16_t* qhat;       // [B, h, d_c + d_R] bf16 absorbed query
-    float* part_u;        // [B, n_split, h, d_c]
-    float* part_ml;       // [B, n_split, h, 2]
-    int32_t* flags;       // [B, n_split]: split left to the rescaling kernel
+    float* part_u;        // [n_wg + B - 1, h, d_c]: partial of (workgroup w, sequence b) in slot w + b
+    float* part_ml;       // [n_wg + B - 1, h, 2]
+    int32_t* flags;       // [n_wg]: workgroup left to the rescaling kernel
+    int32_t* sched;       // tile_start [B + 1], wstart [n_wg], tpw [1]
     int max_blocks, bs_log2, num_blocks;
     int B, s_max, h, d_c, d_R, d_nope, d_v;
-    int n_split, chunk;
+    int n_wg, min_tiles;  // decode workgroups; fewest 32-token tiles per workgroup
     float scale_log2;
 };
 

@@ -27,12 +27,20 @@ namespace attn {
 //    loads in flight at once and read as the MFMA B operand through
 //    transposing reads; q_nope rows are the A operand, fetched up front.
 // ---------------------------------------------------------------------------
+// the decode tile schedule (defined with the decode kernels below)
+__device__ void mla_schedule(const MlaParams& p, int tid, int nthr, int* sc);
+
 constexpr int kAbsCols = 128;
 constexpr int kAbsRowStride = kAbsCols * 2 + 16;
 
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    if (blockIdx.x == gridDim.x - 1) {   // one extra workgroup: the decode tile schedule
+        __shared__ int sc[256];
+        mla_schedule(p, threadIdx.x, 256, sc);
+        return;
+    }
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int nq = p.d_c / kAbsCols;
@@ -216,13 +224,168 @@ struct TileOffsets {
 };
 
 
+// ---------------------------------------------------------------------------
+// Variable-length tile schedule.  The cached tiles of all sequences are laid
+// end to end, sequence-major: tile_start[b] is the first tile of sequence b
+// and tile_start[B] the total.  Decode workgroup w takes tiles
+// [w tpw, (w + 1) tpw), so every workgroup gets the same amount of cache
+// whatever the mix of lengths, crossing sequence boundaries where it must.
+// It leaves one partial (m, l, u~) per sequence it touches, in slot w + b:
+// along the tile order each step to the next (workgroup, sequence) pair
+// raises w, b or both, so w + b never repeats and n_wg + B - 1 slots do.
+// This is the tile-scheduler metadata that "MLA: why one latent can replace
+// a multi-head KV cache" (charlestar.github.io) puts next to the paged
+// cache in the section on what FlashMLA solves, computed here on the device
+// from the device-resident lengths.
+// Workspace layout (int32): tile_start [B + 1], wstart [n_wg] (sequence of
+// each workgroup's first tile, -1 when it has none), tpw [1].
+// ---------------------------------------------------------------------------
+// Read-only views of the lengths and the schedule.  The kernels take them as
+// separate restrict parameters, so that these wave-uniform reads become
+// scalar loads: a vector load inside the tile loop would make the compiler
+// wait for every outstanding vector-memory operation, DMA included.
+struct SchedView {
+    const int32_t* __restrict__ s;       // lengths [B]
+    const int32_t* __restrict__ sched;   // tile_start [B + 1], wstart [n_wg], tpw
+    int s_max;
+    __device__ __forceinline__ int len(int b) const
+    {
+        return min(max(__builtin_amdgcn_readfirstlane(s[b]), 0), s_max);
+    }
+    __device__ __forceinline__ int at(int i) const { return __builtin_amdgcn_readfirstlane(sched[i]); }
+};
+
+// Computed by one workgroup of nthr threads (a power of two); sc is nthr
+// ints of LDS.
+__device__ void mla_schedule(const MlaParams& p, int tid, int nthr, int* sc)
+{
+    int32_t* ts = p.sched;
+    int32_t* wstart = p.sched + p.B + 1;
+    int carry = 0;
+    for (int base = 0; base < p.B; base += nthr) {
+        const int i = base + tid;
+        const int n = i < p.B ? min(max(p.s[i], 0), p.s_max) : 0;
+        const int tl = (n + kT - 1) / kT;
+        sc[tid] = tl;
+        __syncthreads();
+        for (int off = 1; off < nthr; off <<= 1) {   // inclusive scan
+            const int v = tid >= off ? sc[tid - off] : 0;
+            __syncthreads();
+            sc[tid] += v;
+            __syncthreads();
+        }
+        if (i < p.B) ts[i] = carry + sc[tid] - tl;
+        carry += sc[nthr - 1];
+        __syncthreads();
+    }
+    const int total = carry;
+    const int tpw = max((total + p.n_wg - 1) / p.n_wg, p.min_tiles);
+    if (tid == 0) {
+        ts[p.B] = total;
+        wstart[p.n_wg] = tpw;
+    }
+    __threadfence();
+    __syncthreads();
+    // workgroup w starts at tile w tpw, which lies in exactly one non-empty sequence
+    for (int i = tid; i < p.B; i += nthr) {
+        const int a = ts[i], e = ts[i + 1];
+        for (int w = (a + tpw - 1) / tpw; w * tpw < e; w++) wstart[w] = i;
+    }
+    for (int w = (total + tpw - 1) / tpw + tid; w < p.n_wg; w += nthr) wstart[w] = -1;
+}
+
+// A position in a workgroup's tile stream: sequence b, its tile lt of nt,
+// its clamped length n; g is the global tile index, past the stream once
+// g >= g1 (tiles issued there move nothing).
+struct TileWalk {
+    int b, lt, nt, n, g, g1;
+    __device__ __forceinline__ TileWalk(const SchedView& v, int b0, int g0, int g1_)
+        : b(b0), g(g0), g1(g1_)
+    {
+        const int s0 = v.at(b0), s1 = v.at(b0 + 1);
+        lt = g0 - s0;
+        nt = s1 - s0;
+        n = v.len(b0);
+    }
+    __device__ __forceinline__ bool past() const { return g >= g1; }
+    __device__ __forceinline__ void next(const SchedView& v)
+    {
+        ++g;
+        if (++lt < nt || g >= g1) return;
+        int s0, s1 = v.at(b + 1);
+        do {   // skip empty sequences; one with tiles lies ahead while g < g1
+            ++b;
+            s0 = s1;
+            s1 = v.at(b + 1);
+        } while (s1 == s0);
+        lt = 0;
+        nt = s1 - s0;
+        n = v.len(b);
+    }
+};
+
+// DMA of one tile (all 36 slots of 8 rows x 128 bytes, spread over the
+// wavefronts; slot q fills segment q / 4, rows 8 (q % 4) .. + 7) and the
+// physical rows of its two 16-row halves.  A tile's halves each lie in one
+// block of a paged pool (blocks hold a power of two >= 16 rows).
+template <int NW, bool PAGED>
+struct TileDma {
+    static constexpr int SPW = kSlots / NW + (kSlots % NW ? 1 : 0);   // slots per wavefront
+    const MlaParams& p;
+    const int32_t* __restrict__ btab;
+    const uint8_t* __restrict__ cbase;
+    uint32_t lds0;
+    int wave, lr, lp;
+    __device__ __forceinline__ TileDma(const MlaParams& p_, const int32_t* __restrict__ bt,
+                                       uint32_t lds, int wave_, int lane)
+        : p(p_), btab(bt), cbase((const uint8_t*)p_.cache), lds0(lds), wave(wave_),
+          lr(lane / 8), lp(lane % 8) {}
+    __device__ __forceinline__ size_t half_row(int b, int t) const
+    {
+        if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
+        return (size_t)b * p.s_max + t;
+    }
+    __device__ __forceinline__ void rows(const TileWalk& c, size_t& r0, size_t& r1) const
+    {
+        if (c.past()) {
+            r0 = r1 = 0;
+            return;
+        }
+        r0 = half_row(c.b, c.lt * kT);
+        r1 = half_row(c.b, c.lt * kT + 16);
+    }
+    __device__ __forceinline__ void issue(const TileWalk& c, int buf, size_t row0, size_t row1) const
+    {
+#pragma unroll
+        for (int j = 0; j < SPW; j++) {
+            const int q = wave + NW * j;
+            if (q < kSlots) {                      // wave-uniform
+                const int seg = q >> 2, rb = q & 3;
+                const int r0 = c.lt * kT + 8 * rb; // first token of the slot
+                const size_t row = (rb < 2 ? row0 : row1) + 8 * (rb & 1);
+                const int nr = c.past() ? 0 : max(0, min(8, c.n - r0)) * kRow;
+                const rsrc_t rs = make_rsrc(cbase + row * kRow, nr);
+                const int ch = 8 * seg + (lp ^ swz(8 * rb + lr));
+                dma16(rs, (uint32_t)(lr * kRow + ch * 16), lds0 + buf * kTile + q * 1024);
+            }
+        }
+    }
+    // tiles tb + T and tb + 2T were issued after tile tb
+    __device__ __forceinline__ void wait_tile() const
+    {
+        if (SPW * NW == kSlots || wave < kSlots % NW) wait_vmcnt<2 * SPW>();
+        else wait_vmcnt<2 * (SPW - 1)>();
+    }
+};
+
 template <int HW, bool PAGED>
 __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const MlaParams p,
-                                                                          const int32_t* __restrict__ btab)
+                                                                          const int32_t* __restrict__ btab,
+                                                                          const int32_t* __restrict__ slen,
+                                                                          const int32_t* __restrict__ sched)
 {
     constexpr int NW = 128 / HW;    // wavefronts per workgroup
     constexpr int NT = HW / 16;     // head tiles per wavefront
-    constexpr int SPW = kSlots / NW + (kSlots % NW ? 1 : 0);   // DMA slots per wavefront
     constexpr int KS = 576 / 32;    // score K steps
     constexpr int MC = 512 / 16;    // value M tiles (latent columns)
     constexpr int PS = 1;   // score operands are read this many K steps ahead
@@ -232,107 +395,110 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
 
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int wg = xcd_major(blockIdx.x, gridDim.x);
-    const int split = wg % p.n_split, b = wg / p.n_split;
-    const int32_t* __restrict__ s_len = p.s;
-    int n = __builtin_amdgcn_readfirstlane(s_len[b]);
-    n = min(max(n, 0), p.s_max);
-    const int t0 = split * p.chunk;
-    const int t1 = min(n, t0 + p.chunk);
-    const int head0 = wave * HW;
-    const bool active = head0 < p.h;
-    const size_t pbase = ((size_t)b * p.n_split + split) * p.h;   // partial row of head 0
-
-    if (t0 >= t1) {
-        if (tid == 0) p.flags[wg] = 0;
-        if (active && G == 0) {
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                if (head0 + 16 * nt < p.h) {
-                    float* ml = p.part_ml + (pbase + head0 + 16 * nt + li) * 2;
-                    ml[0] = -INFINITY;
-                    ml[1] = 0.f;
-                }
-            }
-        }
+    const int w = xcd_major(blockIdx.x, gridDim.x);
+    const SchedView sv{slen, sched, p.s_max};
+    const int total = sv.at(p.B);
+    const int tpw = sv.at(p.B + 1 + p.n_wg);
+    const int g0 = w * tpw, g1 = min(g0 + tpw, total);
+    if (g0 >= g1) {
+        if (tid == 0) p.flags[w] = 0;
         return;
     }
+    const int head0 = wave * HW;
+    const bool active = head0 < p.h;
 
-    // DMA slots of this wavefront: q = wave + NW j (q < 36); slot q fills
-    // segment q / 4, rows 8 (q % 4) .. + 7.
-    const uint8_t* __restrict__ cbase = (const uint8_t*)p.cache;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs;
-    const int lr = lane / 8;                      // row within the slot
-    const int lp = lane % 8;                      // physical chunk within the segment
-    // A tile's two 16-row halves each lie in one block of a paged pool
-    // (blocks hold a power of two >= 16 rows); their physical rows are looked
-    // up one iteration before the tile is issued.
-    auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
-        if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
-        return (size_t)b * p.s_max + t;
-    };
-    auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
+    const TileDma<NW, PAGED> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
+                                 wave, lane);
+    TileWalk ic(sv, sv.at(p.B + 1 + w), g0, g1);   // issue cursor
+    TileWalk cc = ic;                                                                // compute cursor
+
+    // q^ fragments of one sequence: B operand of the score product (head
+    // tiles past h read as zeros)
+    bf16x8 Qf[NT][KS];
+    auto load_q = [&](int b) {
 #pragma unroll
-        for (int j = 0; j < SPW; j++) {
-            const int q = wave + NW * j;
-            if (q < kSlots) {                      // wave-uniform
-                const int seg = q >> 2, rb = q & 3;
-                const int r0 = tb + 8 * rb;        // first row of the slot
-                const size_t row = (rb < 2 ? row0 : row1) + 8 * (rb & 1);
-                const rsrc_t rs = make_rsrc(cbase + row * kRow, max(0, min(8, t1 - r0)) * kRow);
-                const int c = 8 * seg + (lp ^ swz(8 * rb + lr));
-                dma16(rs, (uint32_t)(lr * kRow + c * 16), lds0 + buf * kTile + q * 1024);
+        for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                Qf[nt][ks] = head0 + 16 * nt < p.h
+                    ? *(const bf16x8*)(p.qhat + ((size_t)b * p.h + head0 + 16 * nt + li) * 576 + ks * 32 + 8 * G)
+                    : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    };
+
+    // Per head and sequence: m is fixed at the first tile's max (log2 units)
+    // and U, lsum accumulate 2^(z - m).  Later tiles may exceed m by up to 64
+    // (p <= 2^64, far from fp32/bf16 overflow); past that the workgroup is
+    // handed to the rescaling kernel (flag), which real logits essentially
+    // never need.
+    f32x4 U[MC][NT];
+    float m[NT], lsum[NT];
+    auto reset = [&]() {
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) {
+            m[nt] = -INFINITY;
+            lsum[nt] = 0.f;
+#pragma unroll
+            for (int mc = 0; mc < MC; mc++) U[mc][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    // partial state of sequence b: m, l per head and the U^T columns, slot w + b
+    auto write_partial = [&](int b) {
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) {
+            if (head0 + 16 * nt >= p.h) continue;
+            float l = lsum[nt];
+            l += xor16(l);
+            l += xor32(l);
+            const size_t row = (size_t)(w + b) * p.h + head0 + 16 * nt + li;
+            float* pu = p.part_u + row * 512 + 4 * G;
+#pragma unroll
+            for (int mc = 0; mc < MC; mc++)
+                *(float4*)(pu + 16 * mc) = make_float4(U[mc][nt][0], U[mc][nt][1], U[mc][nt][2], U[mc][nt][3]);
+            if (G == 0) {
+                p.part_ml[row * 2] = m[nt];
+                p.part_ml[row * 2 + 1] = l;
             }
         }
     };
-
-    // Per head: m is fixed at the first tile's max (log2 units) and U, lsum
-    // accumulate 2^(z - m).  Later tiles may exceed m by up to 64 (p <= 2^64,
-    // far from fp32/bf16 overflow); past that the split is handed to the
-    // rescaling kernel (flag), which real logits essentially never need.
-    f32x4 U[MC][NT];
-    float m[NT], lsum[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; nt++) {
-        m[nt] = -INFINITY;
-        lsum[nt] = 0.f;
-#pragma unroll
-        for (int mc = 0; mc < MC; mc++) U[mc][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    reset();
     if (tid == 0) ovf = 0;
 
-    // first two tiles in flight, then the q^ fragments (B operand of the
-    // score product; head tiles past h read as zeros), then the third tile
+    // two tiles in flight, then q^ of the first sequence, then the third tile
     {
-        const size_t a0 = half_row(t0), a1 = half_row(t0 + 16);
-        const size_t b0 = half_row(t0 + kT), b1 = half_row(t0 + kT + 16);
-        issue_tile(t0, 0, a0, a1);
-        issue_tile(t0 + kT, 1, b0, b1);
+        size_t r0, r1;
+        dma.rows(ic, r0, r1);
+        dma.issue(ic, 0, r0, r1);
+        ic.next(sv);
+        dma.rows(ic, r0, r1);
+        dma.issue(ic, 1, r0, r1);
+        ic.next(sv);
     }
-    bf16x8 Qf[NT][KS];
-#pragma unroll
-    for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-            Qf[nt][ks] = head0 + 16 * nt < p.h
-                ? *(const bf16x8*)(p.qhat + ((size_t)b * p.h + head0 + 16 * nt + li) * 576 + ks * 32 + 8 * G)
-                : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    load_q(cc.b);
     vmem_drain();
-    issue_tile(t0 + 2 * kT, 2, half_row(t0 + 2 * kT), half_row(t0 + 2 * kT + 16));
+    {
+        size_t r0, r1;
+        dma.rows(ic, r0, r1);
+        dma.issue(ic, 2, r0, r1);
+        ic.next(sv);
+    }
 
     const TileOffsets to(li, G);
     int buf = 0;
-    for (int tb = t0; tb < t1; tb += kT) {
-        const size_t nx0 = half_row(tb + 3 * kT), nx1 = half_row(tb + 3 * kT + 16);
-        // tiles tb + T and tb + 2T were issued after this one
-        if (SPW * NW == kSlots || wave < kSlots % NW) wait_vmcnt<2 * SPW>();
-        else wait_vmcnt<2 * (SPW - 1)>();
+    int g = g0;
+    for (;;) {   // one sequence (or the part of it in this workgroup's range) per pass
+      const int gend = min(g1, g + cc.nt - cc.lt);
+      for (; g < gend; g++) {
+        size_t nx0, nx1;   // rows of the tile issued below, looked up early
+        dma.rows(ic, nx0, nx1);
+        dma.wait_tile();
         __syncthreads();
         if (ovf) break;                      // uniform across the workgroup
         // refill the buffer read in the previous iteration (every wavefront is
         // past it), so that three tiles stay in flight while this one is used
-        issue_tile(tb + 3 * kT, (buf + 3) % kNBuf, nx0, nx1);
+        dma.issue(ic, (buf + 3) % kNBuf, nx0, nx1);
+        ic.next(sv);
         const uint8_t* C = Cs + buf * kTile;
+        const int tbase = cc.lt * kT;
         if (active) {
             // ---- scores S^T = C . q^T
             f32x4 S[2][NT];
@@ -370,11 +536,11 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
                 for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const int tok = tb + 16 * mt + 4 * G + e;
-                        z[mt][e] = tok < t1 ? S[mt][nt][e] * p.scale_log2 : -INFINITY;
+                        const int tok = tbase + 16 * mt + 4 * G + e;
+                        z[mt][e] = tok < cc.n ? S[mt][nt][e] * p.scale_log2 : -INFINITY;
                         lm = fmaxf(lm, z[mt][e]);
                     }
-                if (m[nt] == -INFINITY) {       // first tile: fix the reference
+                if (m[nt] == -INFINITY) {       // first tile of the sequence: fix the reference
                     lm = fmaxf(lm, xor16(lm));
                     lm = fmaxf(lm, xor32(lm));
                     m[nt] = lm;
@@ -386,10 +552,10 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
                 for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                     for (int e = 0; e < 4; e += 2) {
-                        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - m[nt]),
-                                                       __builtin_amdgcn_exp2f(z[mt][e + 1] - m[nt]));
-                        pk[mt * 2 + e / 2] = w;
-                        ps += bf16lo_to_f32(w) + bf16hi_to_f32(w);
+                        const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - m[nt]),
+                                                        __builtin_amdgcn_exp2f(z[mt][e + 1] - m[nt]));
+                        pk[mt * 2 + e / 2] = wv;
+                        ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
                     }
                 lsum[nt] += ps;
                 P[nt] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
@@ -414,35 +580,33 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        cc.lt++;
         buf = (buf + 1) % kNBuf;
+      }
+      if (g < gend) break;                   // left early: flagged for the rescaling kernel
+      if (active) write_partial(cc.b);
+      if (g >= g1) break;
+      // the next sequence: its tile cursor, accumulators and q^
+      cc.lt--;
+      cc.g = g - 1;
+      cc.next(sv);
+      reset();
+      load_q(cc.b);
+      vmem_drain();
     }
     wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
-
     __syncthreads();   // ovf from the last tile
-    if (tid == 0) p.flags[wg] = ovf;
-    if (ovf || !active) return;
-    // ---- partial state of this split: m, l per head, U^T columns
-#pragma unroll
-    for (int nt = 0; nt < NT; nt++) {
-        if (head0 + 16 * nt >= p.h) continue;
-        float l = lsum[nt];
-        l += xor16(l);
-        l += xor32(l);
-        const size_t row = pbase + head0 + 16 * nt + li;
-        float* pu = p.part_u + row * 512 + 4 * G;
-#pragma unroll
-        for (int mc = 0; mc < MC; mc++)
-            *(float4*)(pu + 16 * mc) = make_float4(U[mc][nt][0], U[mc][nt][1], U[mc][nt][2], U[mc][nt][3]);
-        if (G == 0) {
-            p.part_ml[row * 2] = m[nt];
-            p.part_ml[row * 2 + 1] = l;
-        }
-    }
+    if (tid == 0) p.flags[w] = ovf;
 }
 
+// Fallback for a workgroup whose fast pass was flagged: the same tile range,
+// 8 wavefronts x 16 heads, with a lazily moving reference max and in-register
+// rescaling.  Unflagged workgroups return at once.
 template <bool PAGED>
 __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
-                                                              const int32_t* __restrict__ btab)
+                                                              const int32_t* __restrict__ btab,
+                                                              const int32_t* __restrict__ slen,
+                                                              const int32_t* __restrict__ sched)
 {
     constexpr int KS = 576 / 32;    // score K steps
     constexpr int MC = 512 / 16;    // value M tiles (latent columns)
@@ -450,88 +614,85 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
 
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int wg = xcd_major(blockIdx.x, gridDim.x);
-    const int split = wg % p.n_split, b = wg / p.n_split;
-    if (__builtin_amdgcn_readfirstlane(p.flags[wg]) == 0) return;   // fast kernel finished it
-    const int32_t* __restrict__ s_len = p.s;
-    int n = __builtin_amdgcn_readfirstlane(s_len[b]);
-    n = min(max(n, 0), p.s_max);
-    const int t0 = split * p.chunk;
-    const int t1 = min(n, t0 + p.chunk);
+    const int w = xcd_major(blockIdx.x, gridDim.x);
+    if (__builtin_amdgcn_readfirstlane(p.flags[w]) == 0) return;   // the fast kernel finished it
+    const SchedView sv{slen, sched, p.s_max};
+    const int total = sv.at(p.B);
+    const int tpw = sv.at(p.B + 1 + p.n_wg);
+    const int g0 = w * tpw, g1 = min(g0 + tpw, total);
+    if (g0 >= g1) return;
     const int head0 = wave * 16;
     const bool active = head0 < p.h;
-    const size_t pbase = ((size_t)b * p.n_split + split) * p.h;   // partial row of head 0
 
-    if (t0 >= t1) {
-        if (active && G == 0) {
-            float* ml = p.part_ml + (pbase + head0 + li) * 2;
-            ml[0] = -INFINITY;
-            ml[1] = 0.f;
-        }
-        return;
-    }
+    const TileDma<8, PAGED> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
+                                wave, lane);
+    TileWalk ic(sv, sv.at(p.B + 1 + w), g0, g1);
+    TileWalk cc = ic;
 
-    // DMA slots of this wavefront: q = wave + 8 j (j < 5, q < 36); slot q
-    // fills segment q / 4, rows 8 (q % 4) .. + 7.
-    const uint8_t* __restrict__ cbase = (const uint8_t*)p.cache;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs;
-    const int lr = lane / 8;                      // row within the slot
-    const int lp = lane % 8;                      // physical chunk within the segment
-    // A tile's two 16-row halves each lie in one block of a paged pool
-    // (blocks hold a power of two >= 16 rows); their physical rows are looked
-    // up one iteration before the tile is issued.
-    auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
-        if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
-        return (size_t)b * p.s_max + t;
-    };
-    auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
-#pragma unroll
-        for (int j = 0; j < 5; j++) {
-            const int q = wave + 8 * j;
-            if (q < kSlots) {                      // wave-uniform
-                const int seg = q >> 2, rb = q & 3;
-                const int r0 = tb + 8 * rb;        // first row of the slot
-                const size_t row = (rb < 2 ? row0 : row1) + 8 * (rb & 1);
-                const rsrc_t rs = make_rsrc(cbase + row * kRow, max(0, min(8, t1 - r0)) * kRow);
-                const int c = 8 * seg + (lp ^ swz(8 * rb + lr));
-                dma16(rs, (uint32_t)(lr * kRow + c * 16), lds0 + buf * kTile + q * 1024);
-            }
-        }
-    };
-
-    f32x4 U[MC];
-    float m = -INFINITY, lsum = 0.f;
-#pragma unroll
-    for (int mc = 0; mc < MC; mc++) U[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // first two tiles in flight, then the q^ fragments (B operand of the
-    // score product; zeros for wavefronts past h), then the third tile
-    {
-        const size_t a0 = half_row(t0), a1 = half_row(t0 + 16);
-        const size_t b0 = half_row(t0 + kT), b1 = half_row(t0 + kT + 16);
-        issue_tile(t0, 0, a0, a1);
-        issue_tile(t0 + kT, 1, b0, b1);
-    }
     bf16x8 Qf[KS];
+    auto load_q = [&](int b) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ks++)
-        Qf[ks] = active ? *(const bf16x8*)(p.qhat + ((size_t)b * p.h + head0 + li) * 576 + ks * 32 + 8 * G)
-                        : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        for (int ks = 0; ks < KS; ks++)
+            Qf[ks] = active ? *(const bf16x8*)(p.qhat + ((size_t)b * p.h + head0 + li) * 576 + ks * 32 + 8 * G)
+                            : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    };
+    f32x4 U[MC];
+    float m, lsum;
+    auto reset = [&]() {
+        m = -INFINITY;
+        lsum = 0.f;
+#pragma unroll
+        for (int mc = 0; mc < MC; mc++) U[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto write_partial = [&](int b) {
+        float l = lsum;
+        l += xor16(l);
+        l += xor32(l);
+        const size_t row = (size_t)(w + b) * p.h + head0 + li;
+        float* pu = p.part_u + row * 512 + 4 * G;
+#pragma unroll
+        for (int mc = 0; mc < MC; mc++)
+            *(float4*)(pu + 16 * mc) = make_float4(U[mc][0], U[mc][1], U[mc][2], U[mc][3]);
+        if (G == 0) {
+            p.part_ml[row * 2] = m;
+            p.part_ml[row * 2 + 1] = l;
+        }
+    };
+    reset();
+
+    {
+        size_t r0, r1;
+        dma.rows(ic, r0, r1);
+        dma.issue(ic, 0, r0, r1);
+        ic.next(sv);
+        dma.rows(ic, r0, r1);
+        dma.issue(ic, 1, r0, r1);
+        ic.next(sv);
+    }
+    load_q(cc.b);
     vmem_drain();
-    issue_tile(t0 + 2 * kT, 2, half_row(t0 + 2 * kT), half_row(t0 + 2 * kT + 16));
+    {
+        size_t r0, r1;
+        dma.rows(ic, r0, r1);
+        dma.issue(ic, 2, r0, r1);
+        ic.next(sv);
+    }
 
     const TileOffsets to(li, G);
     int buf = 0;
-    for (int tb = t0; tb < t1; tb += kT) {
-        const size_t nx0 = half_row(tb + 3 * kT), nx1 = half_row(tb + 3 * kT + 16);
-        // tiles tb + T and tb + 2T were issued after this one
-        if (wave < 4) wait_vmcnt<10>();
-        else wait_vmcnt<8>();
+    for (int g = g0; g < g1; g++) {
+        size_t nx0, nx1;
+        dma.rows(ic, nx0, nx1);
+        dma.wait_tile();
         __syncthreads();
-        // refill the buffer read in the previous iteration (every wavefront is
-        // past it), so that three tiles stay in flight while this one is used
-        issue_tile(tb + 3 * kT, (buf + 3) % kNBuf, nx0, nx1);
+        dma.issue(ic, (buf + 3) % kNBuf, nx0, nx1);
+        ic.next(sv);
+        if (cc.lt == 0 && g != g0) {
+            load_q(cc.b);
+            vmem_drain();
+        }
         const uint8_t* C = Cs + buf * kTile;
+        const int tbase = cc.lt * kT;
         if (active) {
             // ---- scores S^T = C . q^T
             f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -559,8 +720,8 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
             for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int tok = tb + 16 * mt + 4 * G + e;
-                    z[mt][e] = tok < t1 ? S[mt][e] * p.scale_log2 : -INFINITY;
+                    const int tok = tbase + 16 * mt + 4 * G + e;
+                    z[mt][e] = tok < cc.n ? S[mt][e] * p.scale_log2 : -INFINITY;
                     lm = fmaxf(lm, z[mt][e]);
                 }
             lm = fmaxf(lm, xor16(lm));
@@ -575,10 +736,10 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
             for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int e = 0; e < 4; e += 2) {
-                    const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mn),
-                                                   __builtin_amdgcn_exp2f(z[mt][e + 1] - mn));
-                    pk[mt * 2 + e / 2] = w;
-                    ps += bf16lo_to_f32(w) + bf16hi_to_f32(w);
+                    const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mn),
+                                                    __builtin_amdgcn_exp2f(z[mt][e + 1] - mn));
+                    pk[mt * 2 + e / 2] = wv;
+                    ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
                 }
             lsum = lsum * alpha + ps;
             const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
@@ -603,29 +764,19 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (g + 1 == g1 || cc.lt + 1 == cc.nt) {
+            if (active) write_partial(cc.b);
+            reset();
+        }
+        cc.next(sv);
         buf = (buf + 1) % kNBuf;
     }
     wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
-
-    if (!active) return;
-    // ---- partial state of this split: m, l per head, U^T columns
-    float l = lsum;
-    l += xor16(l);
-    l += xor32(l);
-    const size_t row = pbase + head0 + li;
-    float* pu = p.part_u + row * 512 + 4 * G;
-#pragma unroll
-    for (int mc = 0; mc < MC; mc++)
-        *(float4*)(pu + 16 * mc) = make_float4(U[mc][0], U[mc][1], U[mc][2], U[mc][3]);
-    if (G == 0) {
-        p.part_ml[row * 2] = m;
-        p.part_ml[row * 2 + 1] = l;
-    }
 }
 
 // ---------------------------------------------------------------------------
-// 3. finish.  Workgroup = (head i, 16 sequences).  Merge the split partials
-//    into u~ (fp32; written to u_latent and kept in LDS), then
+// 3. finish.  Workgroup = (head i, 16 sequences).  Merge each sequence's
+//    partials into u~ (fp32; written to u_latent and kept in LDS), then
 //    out[b, i, :] = W_UV[i] u~[b, i, :] on the matrix cores.  u~ is fed as a
 //    bf16 hi/lo pair (u~ = hi + lo exactly to about 2^-16 relative), so the
 //    product keeps u~ at fp32-level precision; W_UV rows are the B operand
@@ -661,24 +812,30 @@ __global__ __launch_bounds__(256) void mla_finish_kernel(const MlaParams p)
         for (int q = 0; q < 8; q++) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
         float M = -INFINITY, L = 0.f;
         if (bb < p.B) {
+            // the partials of sequence bb: slots w + bb of the workgroups w
+            // whose tile ranges overlap its tiles
+            const int s0 = p.sched[bb], s1 = p.sched[bb + 1];
+            const int tpw = p.sched[p.B + 1 + p.n_wg];
+            const int wf = s0 / tpw;
+            const int ns = s1 > s0 ? (s1 - 1) / tpw - wf + 1 : 0;
             const float2* __restrict__ ml = (const float2*)p.part_ml;
-            const size_t row0 = (size_t)bb * p.n_split * p.h + i;   // split k: row0 + k h
-            for (int k0 = 0; k0 < p.n_split; k0 += 8) {
+            const size_t row0 = (size_t)(wf + bb) * p.h + i;   // partial k: row0 + k h
+            for (int k0 = 0; k0 < ns; k0 += 8) {
                 float2 v[8];
 #pragma unroll
                 for (int u = 0; u < 8; u++)
-                    if (k0 + u < p.n_split) v[u] = ml[row0 + (size_t)(k0 + u) * p.h];
+                    if (k0 + u < ns) v[u] = ml[row0 + (size_t)(k0 + u) * p.h];
 #pragma unroll
                 for (int u = 0; u < 8; u++)
-                    if (k0 + u < p.n_split && v[u].y > 0.f) M = fmaxf(M, v[u].x);
+                    if (k0 + u < ns && v[u].y > 0.f) M = fmaxf(M, v[u].x);
             }
             const float4* __restrict__ pu = (const float4*)p.part_u;
-            for (int k0 = 0; k0 < p.n_split; k0 += 4) {
+            for (int k0 = 0; k0 < ns; k0 += 4) {
                 float2 v[4];
                 float4 u[4][8];
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
-                    if (k0 + g < p.n_split) {
+                    if (k0 + g < ns) {
                         const size_t row = row0 + (size_t)(k0 + g) * p.h;
                         v[g] = ml[row];
 #pragma unroll
@@ -687,7 +844,7 @@ __global__ __launch_bounds__(256) void mla_finish_kernel(const MlaParams p)
                 }
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
-                    if (k0 + g < p.n_split && v[g].y > 0.f) {
+                    if (k0 + g < ns && v[g].y > 0.f) {
                         const float wk = __builtin_amdgcn_exp2f(v[g].x - M);
                         L = fmaf(wk, v[g].y, L);
 #pragma unroll
@@ -757,25 +914,26 @@ __global__ __launch_bounds__(256) void mla_finish_kernel(const MlaParams p)
 
 hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
 {
-    const unsigned g1 = (unsigned)(p.h * (p.d_c / kAbsCols));
+    // absorb workgroups, plus one that computes the tile schedule
+    const unsigned g1 = (unsigned)(p.h * (p.d_c / kAbsCols)) + 1;
     const size_t smem1 = (size_t)p.d_nope * kAbsRowStride;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t ea = hipFuncSetAttribute((const void*)mla_absorb_kernel,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);   // d_nope <= 256 rows of 272 bytes
         if (ea != hipSuccess) return ea;
         attr_set = true;
     }
     hipLaunchKernelGGL(mla_absorb_kernel, dim3(g1), dim3(256), smem1, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned g2 = (unsigned)(p.B * p.n_split);
+    const unsigned g2 = (unsigned)p.n_wg;
     if (paged) {
-        hipLaunchKernelGGL((mla_decode_fast_kernel<32, true>), dim3(g2), dim3(256), 0, st, p, p.bt);
-        hipLaunchKernelGGL((mla_decode_safe_kernel<true>), dim3(g2), dim3(512), 0, st, p, p.bt);
+        hipLaunchKernelGGL((mla_decode_fast_kernel<32, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+        hipLaunchKernelGGL((mla_decode_safe_kernel<true>), dim3(g2), dim3(512), 0, st, p, p.bt, p.s, p.sched);
     } else {
-        hipLaunchKernelGGL((mla_decode_fast_kernel<32, false>), dim3(g2), dim3(256), 0, st, p, p.bt);
-        hipLaunchKernelGGL((mla_decode_safe_kernel<false>), dim3(g2), dim3(512), 0, st, p, p.bt);
+        hipLaunchKernelGGL((mla_decode_fast_kernel<32, false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+        hipLaunchKernelGGL((mla_decode_safe_kernel<false>), dim3(g2), dim3(512), 0, st, p, p.bt, p.s, p.sched);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -66,6 +66,26 @@ def test_long_context_split():
     run(shape(1, 128, (12000,), seed=6))
 
 
+# The decode tile schedule gives each of the 256 workgroups an equal run of
+# 32-token tiles across sequence boundaries (at least 8 tiles).  Many short
+# sequences put several sequences, empty ones among them, into one
+# workgroup; uneven long ones split a sequence over several workgroups.
+def test_schedule_many_short_sequences_per_workgroup():
+    rng = np.random.default_rng(40)
+    s = tuple(int(x) for x in rng.integers(0, 70, size=300))
+    run(shape(300, 16, s, seed=40), sample=list(range(0, 300, 7)) + [299])
+
+
+def test_schedule_uneven_lengths():
+    run(shape(6, 32, (1, 9000, 33, 0, 2048, 31), seed=41))
+
+
+def test_schedule_paged_mixed():
+    rng = np.random.default_rng(42)
+    s = tuple(int(x) for x in rng.integers(0, 3000, size=40))
+    run(shape(40, 32, s, paged=True, seed=42), sample=[0, 7, 13, 21, 39])
+
+
 def test_paged_shuffled():
     run(shape(4, 32, (1, 16, 17, 700), paged=True, seed=7))
 

@@ -43,9 +43,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ---- GQA split plan ---------------------------------------------------------
 // bf16 caches with g <= 64 run on the matrix cores: work item = (b, KV head,
-// token split) with all g query heads in one workgroup of ceil(g/16)
-// wavefronts (1, 2 or 4).  A 64 KB LDS ring per workgroup leaves room for
-// two per CU, so splits are added until about 512 workgroups exist.
+// token split) with all g query heads in one workgroup of 2 or 4 wavefronts
+// (16 heads each; a wavefront without heads only issues its share of the
+// tile DMA).  An 80 KB LDS ring per workgroup leaves room for two per CU, so
+// splits are added until about 512 workgroups exist.
 // Otherwise (fp32, or g > 64) the vector kernel runs: work item = (b, KV
 // head, group of HG query heads, token split), HG the largest of 8, 4, 2, 1
 // dividing g, one wavefront each, about 2048 of them (8 per CU).
@@ -67,7 +68,9 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h)
     if (mfma) {
         P.HG = g;
         P.n_hg = 1;
-        P.NW = g <= 16 ? 1 : g <= 32 ? 2 : 4;
+        // two wavefronts at least: both issue the tile DMA, which keeps more
+        // loads in flight per CU than one wavefront's counter allows
+        P.NW = g <= 32 ? 2 : 4;
         target = 512;
     } else {
         P.HG = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;

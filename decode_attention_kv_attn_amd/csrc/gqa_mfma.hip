@@ -14,7 +14,8 @@
 // the heads padded to 16, so the ALU only carries the softmax:
 //
 //  * workgroup = (b, KV head j, token split); wavefront w takes query heads
-//    16w .. 16w+15 of the group (1 to 4 wavefronts, g <= 64);
+//    16w .. 16w+15 of the group (2 or 4 wavefronts, g <= 64; all of them
+//    issue the tile DMA);
 //  * K and V tiles of 32 tokens move HBM -> LDS by LDS-DMA (buffer_load ...
 //    lds) into a ring of NBUF buffers, NBUF - 1 tiles ahead of use; completion is
 //    tracked with explicit vmcnt waits (no other vector-memory instruction is
@@ -36,7 +37,7 @@
 namespace attn {
 
 #ifndef GQA_MFMA_NBUF
-#define GQA_MFMA_NBUF 4
+#define GQA_MFMA_NBUF 5
 #endif
 
 template <int D>
@@ -96,9 +97,11 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
 
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    // work item (b, split, j) with j fastest, renumbered XCD-major so that the
-    // KV heads and neighbouring splits of one sequence run on one XCD
-    int w = xcd_major(blockIdx.x, gridDim.x);
+    // work item (b, split, j) with j fastest.  A paged pool is walked
+    // XCD-major, so that the KV heads of one sequence, which share every
+    // block, run under one L2; a contiguous cache streams faster in plain
+    // order (measured).
+    int w = PAGED ? xcd_major(blockIdx.x, gridDim.x) : (int)blockIdx.x;
     const int j = w % p.h_kv;
     w /= p.h_kv;
     const int split = w % p.n_split;
@@ -314,11 +317,7 @@ static hipError_t launch_nw(const GqaParams& p, bool paged, unsigned grid, hipSt
 template <int D>
 static hipError_t launch_mfma_d(const GqaParams& p, int NW, bool paged, unsigned grid, hipStream_t st)
 {
-    switch (NW) {
-    case 1: return launch_nw<D, 1>(p, paged, grid, st);
-    case 2: return launch_nw<D, 2>(p, paged, grid, st);
-    default: return launch_nw<D, 4>(p, paged, grid, st);
-    }
+    return NW == 2 ? launch_nw<D, 2>(p, paged, grid, st) : launch_nw<D, 4>(p, paged, grid, st);
 }
 
 hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, unsigned grid,

@@ -26,7 +26,7 @@ struct GqaParams {
 // vector kernel (any g; fp32 or bf16), then the split merge when n_split > 1
 hipError_t launch_gqa_decode(const GqaParams& p, int d_h, bool f32, int HG, bool paged,
                              unsigned grid, hipStream_t st);
-// matrix-core kernel (bf16, g <= 16 NW), then the split merge when n_split > 1
+// matrix-core kernel (bf16, g <= 16 NW, NW = 2 or 4), then the split merge when n_split > 1
 hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, unsigned grid,
                            hipStream_t st);
 hipError_t launch_gqa_combine(const GqaParams& p, int d_h, bool f32, hipStream_t st);

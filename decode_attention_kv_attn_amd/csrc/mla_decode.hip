@@ -52,14 +52,17 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 
     // q_nope rows of one 16-sequence block: the A operand (rows past B are zero)
     const int ksteps = p.d_nope / 32;
+    // (loads are unconditional from clamped addresses and masked afterwards,
+    // so that all of them are in flight together)
     auto load_a = [&](int b0, bf16x8* a) {
         const int bb = b0 + li;
+        const int bc = min(bb, p.B - 1);
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            if (k < ksteps && bb < p.B)
-                a[k] = *(const bf16x8*)(qn + ((size_t)bb * p.h + i) * p.d_nope + k * 32 + 8 * G);
-            else
-                a[k] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+            const int kc = min(k, ksteps - 1);
+            const uint4 v = *(const uint4*)(qn + ((size_t)bc * p.h + i) * p.d_nope + kc * 32 + 8 * G);
+            const uint32_t keep = (k < ksteps && bb < p.B) ? 0xffffffffu : 0u;   // mask, not a branch
+            a[k] = __builtin_bit_cast(bf16x8, make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep));
         }
     };
     bf16x8 a[8];
@@ -71,12 +74,11 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
         uint4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; u++) {
-            const int idx = base + u * 256 + tid;
-            if (idx < nchunk) {
-                const int r = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
-                v[u] = *(const uint4*)(wuk + (size_t)r * p.d_c + c0 + c * 8);
-            }
+            const int idx = min(base + u * 256 + tid, nchunk - 1);   // clamped: loads stay unconditional
+            const int r = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
+            v[u] = *(const uint4*)(wuk + (size_t)r * p.d_c + c0 + c * 8);
         }
+        __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first store
 #pragma unroll
         for (int u = 0; u < 8; u++) {
             const int idx = base + u * 256 + tid;
@@ -95,8 +97,8 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
             uint4 v[4];
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                const int idx = base + u * 256 + tid;
-                if (idx < nv) v[u] = *(const uint4*)(qr + ((size_t)(idx / per) * p.h + i) * p.d_R + 8 * (idx % per));
+                const int idx = min(base + u * 256 + tid, nv - 1);
+                v[u] = *(const uint4*)(qr + ((size_t)(idx / per) * p.h + i) * p.d_R + 8 * (idx % per));
             }
 #pragma unroll
             for (int u = 0; u < 4; u++) {
@@ -244,28 +246,54 @@ struct TileOffsets {
 // separate restrict parameters, so that these wave-uniform reads become
 // scalar loads: a vector load inside the tile loop would make the compiler
 // wait for every outstanding vector-memory operation, DMA included.
+// Every value taken from the schedule is clamped into range, so that even a
+// workspace whose schedule was overwritten cannot steer an access outside the
+// lengths, the table, the pool or the partial slots.
 struct SchedView {
     const int32_t* __restrict__ s;       // lengths [B]
     const int32_t* __restrict__ sched;   // tile_start [B + 1], wstart [n_wg], tpw
-    int s_max;
+    int s_max, B, n_wg;
     __device__ __forceinline__ int len(int b) const
     {
         return min(max(__builtin_amdgcn_readfirstlane(s[b]), 0), s_max);
     }
     __device__ __forceinline__ int at(int i) const { return __builtin_amdgcn_readfirstlane(sched[i]); }
+    __device__ __forceinline__ int total() const
+    {
+        return min(max(at(B), 0), B * ((s_max + kT - 1) / kT));
+    }
+    __device__ __forceinline__ int tpw(int tot) const { return min(max(at(B + 1 + n_wg), 1), max(tot, 1)); }
+    __device__ __forceinline__ int first_seq(int w) const { return min(max(at(B + 1 + w), 0), B - 1); }
 };
 
 // Computed by one workgroup of nthr threads (a power of two); sc is nthr
-// ints of LDS.
+// ints of LDS.  Two passes over the lengths: the first only totals the
+// tiles (which fixes tpw), the second scans them again and writes the tile
+// offsets and each workgroup's first sequence; no thread reads back what
+// another wrote to global memory.
 __device__ void mla_schedule(const MlaParams& p, int tid, int nthr, int* sc)
 {
     int32_t* ts = p.sched;
     int32_t* wstart = p.sched + p.B + 1;
+    auto tiles_of = [&](int i) { return i < p.B ? (min(max(p.s[i], 0), p.s_max) + kT - 1) / kT : 0; };
+    // pass 1: total
+    int part = 0;
+    for (int i = tid; i < p.B; i += nthr) part += tiles_of(i);
+    sc[tid] = part;
+    __syncthreads();
+    for (int off = nthr / 2; off > 0; off >>= 1) {
+        if (tid < off) sc[tid] += sc[tid + off];
+        __syncthreads();
+    }
+    const int total = sc[0];
+    const int tpw = max((total + p.n_wg - 1) / p.n_wg, p.min_tiles);
+    __syncthreads();
+    // pass 2: offsets; workgroup w starts at tile w tpw, inside exactly one
+    // non-empty sequence
     int carry = 0;
     for (int base = 0; base < p.B; base += nthr) {
         const int i = base + tid;
-        const int n = i < p.B ? min(max(p.s[i], 0), p.s_max) : 0;
-        const int tl = (n + kT - 1) / kT;
+        const int tl = tiles_of(i);
         sc[tid] = tl;
         __syncthreads();
         for (int off = 1; off < nthr; off <<= 1) {   // inclusive scan
@@ -274,22 +302,17 @@ __device__ void mla_schedule(const MlaParams& p, int tid, int nthr, int* sc)
             sc[tid] += v;
             __syncthreads();
         }
-        if (i < p.B) ts[i] = carry + sc[tid] - tl;
+        if (i < p.B) {
+            const int a = carry + sc[tid] - tl, e = a + tl;
+            ts[i] = a;
+            for (int w = (a + tpw - 1) / tpw; w * tpw < e; w++) wstart[w] = i;
+        }
         carry += sc[nthr - 1];
         __syncthreads();
     }
-    const int total = carry;
-    const int tpw = max((total + p.n_wg - 1) / p.n_wg, p.min_tiles);
     if (tid == 0) {
         ts[p.B] = total;
         wstart[p.n_wg] = tpw;
-    }
-    __threadfence();
-    __syncthreads();
-    // workgroup w starts at tile w tpw, which lies in exactly one non-empty sequence
-    for (int i = tid; i < p.B; i += nthr) {
-        const int a = ts[i], e = ts[i + 1];
-        for (int w = (a + tpw - 1) / tpw; w * tpw < e; w++) wstart[w] = i;
     }
     for (int w = (total + tpw - 1) / tpw + tid; w < p.n_wg; w += nthr) wstart[w] = -1;
 }
@@ -303,8 +326,8 @@ struct TileWalk {
         : b(b0), g(g0), g1(g1_)
     {
         const int s0 = v.at(b0), s1 = v.at(b0 + 1);
-        lt = g0 - s0;
-        nt = s1 - s0;
+        nt = max(s1 - s0, 1);
+        lt = min(max(g0 - s0, 0), nt - 1);
         n = v.len(b0);
     }
     __device__ __forceinline__ bool past() const { return g >= g1; }
@@ -312,14 +335,16 @@ struct TileWalk {
     {
         ++g;
         if (++lt < nt || g >= g1) return;
-        int s0, s1 = v.at(b + 1);
-        do {   // skip empty sequences; one with tiles lies ahead while g < g1
+        // the next sequence with tiles (one lies ahead while g < g1); never past B - 1
+        int s0 = 0, s1 = v.at(b + 1);
+        while (b + 1 < v.B) {
             ++b;
             s0 = s1;
             s1 = v.at(b + 1);
-        } while (s1 == s0);
+            if (s1 != s0) break;
+        }
         lt = 0;
-        nt = s1 - s0;
+        nt = max(s1 - s0, 1);
         n = v.len(b);
     }
 };
@@ -396,10 +421,11 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int w = xcd_major(blockIdx.x, gridDim.x);
-    const SchedView sv{slen, sched, p.s_max};
-    const int total = sv.at(p.B);
-    const int tpw = sv.at(p.B + 1 + p.n_wg);
-    const int g0 = w * tpw, g1 = min(g0 + tpw, total);
+    const SchedView sv{slen, sched, p.s_max, p.B, p.n_wg};
+    const int total = sv.total();
+    const int tpw = sv.tpw(total);
+    const long long g0l = (long long)w * tpw;
+    const int g0 = (int)min(g0l, (long long)total), g1 = min(g0 + tpw, total);
     if (g0 >= g1) {
         if (tid == 0) p.flags[w] = 0;
         return;
@@ -409,7 +435,7 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
 
     const TileDma<NW, PAGED> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
                                  wave, lane);
-    TileWalk ic(sv, sv.at(p.B + 1 + w), g0, g1);   // issue cursor
+    TileWalk ic(sv, sv.first_seq(w), g0, g1);   // issue cursor
     TileWalk cc = ic;                                                                // compute cursor
 
     // q^ fragments of one sequence: B operand of the score product (head
@@ -616,17 +642,18 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int w = xcd_major(blockIdx.x, gridDim.x);
     if (__builtin_amdgcn_readfirstlane(p.flags[w]) == 0) return;   // the fast kernel finished it
-    const SchedView sv{slen, sched, p.s_max};
-    const int total = sv.at(p.B);
-    const int tpw = sv.at(p.B + 1 + p.n_wg);
-    const int g0 = w * tpw, g1 = min(g0 + tpw, total);
+    const SchedView sv{slen, sched, p.s_max, p.B, p.n_wg};
+    const int total = sv.total();
+    const int tpw = sv.tpw(total);
+    const long long g0l = (long long)w * tpw;
+    const int g0 = (int)min(g0l, (long long)total), g1 = min(g0 + tpw, total);
     if (g0 >= g1) return;
     const int head0 = wave * 16;
     const bool active = head0 < p.h;
 
     const TileDma<8, PAGED> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
                                 wave, lane);
-    TileWalk ic(sv, sv.at(p.B + 1 + w), g0, g1);
+    TileWalk ic(sv, sv.first_seq(w), g0, g1);
     TileWalk cc = ic;
 
     bf16x8 Qf[KS];
@@ -814,10 +841,10 @@ __global__ __launch_bounds__(256) void mla_finish_kernel(const MlaParams p)
         if (bb < p.B) {
             // the partials of sequence bb: slots w + bb of the workgroups w
             // whose tile ranges overlap its tiles
-            const int s0 = p.sched[bb], s1 = p.sched[bb + 1];
-            const int tpw = p.sched[p.B + 1 + p.n_wg];
-            const int wf = s0 / tpw;
-            const int ns = s1 > s0 ? (s1 - 1) / tpw - wf + 1 : 0;
+            const int s0 = max(p.sched[bb], 0), s1 = p.sched[bb + 1];
+            const int tpw = max(p.sched[p.B + 1 + p.n_wg], 1);
+            const int wf = min(s0 / tpw, p.n_wg - 1);
+            const int ns = s1 > s0 ? min(max((s1 - 1) / tpw - wf + 1, 0), p.n_wg - wf) : 0;
             const float2* __restrict__ ml = (const float2*)p.part_ml;
             const size_t row0 = (size_t)(wf + bb) * p.h + i;   // partial k: row0 + k h
             for (int k0 = 0; k0 < ns; k0 += 8) {
@@ -883,6 +910,7 @@ __global__ __launch_bounds__(256) void mla_finish_kernel(const MlaParams p)
             const uint16_t* wrow = wuv + (size_t)(nt * 16 + li) * p.d_c + 8 * G;
 #pragma unroll
             for (int k = 0; k < 16; k++) bws[k] = *(const bf16x8*)(wrow + 32 * k);
+            __builtin_amdgcn_sched_barrier(0);   // all 16 loads in flight before the first use
         }
 #pragma unroll
         for (int k = 0; k < 16; k++) {

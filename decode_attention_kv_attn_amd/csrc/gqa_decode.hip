@@ -320,21 +320,28 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaParams p,
 
 // Merge of the split partials: m = max m_k over splits that saw tokens,
 // l = sum 2^(m_k-m) l_k, o = sum 2^(m_k-m) o_k / l, lse = (m + log2 l) ln 2.
-// One wavefront per (b, head), each lane owning D/64 output elements.  The
-// weights of 64 splits are computed at once (one split per lane) and then
-// broadcast; eight splits' partial rows are in flight at a time.  A split
-// with l = 0 never wrote its partial row: it is loaded but not used.
-template <int D, bool F32>
-__global__ __launch_bounds__(64) void gqa_combine_kernel(const GqaParams p)
+// One workgroup of NWV wavefronts per (b, head); each wavefront merges a
+// contiguous range of the splits (its own max, weights and sums, 16 partial
+// rows in flight, lane = D/64 output elements), then the wavefronts' results
+// are merged the same way through LDS.  A split with l = 0 never wrote its
+// partial row: it is loaded but not used.
+template <int D, bool F32, int NWV>
+__global__ __launch_bounds__(64 * NWV) void gqa_combine_kernel(const GqaParams p)
 {
     constexpr int PL = D / 64;
-    const int lane = threadIdx.x;
+    constexpr int U = 16;   // partial rows in flight per wavefront
+    __shared__ float sM[NWV], sL[NWV];
+    __shared__ float so[NWV][D];
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int bh = blockIdx.x;
     const int ns = p.n_split;
+    const int per = (ns + NWV - 1) / NWV;
+    const int k_lo = min(wave * per, ns), k_hi = min(k_lo + per, ns);
     const float2* __restrict__ ml = (const float2*)p.part_ml + (size_t)bh * ns;
     const float* __restrict__ po = p.part_o + (size_t)bh * ns * D + lane * PL;
     float M = -INFINITY;
-    for (int k = lane; k < ns; k += 64) {
+    for (int k = k_lo + lane; k < k_hi; k += 64) {
         const float2 v = ml[k];
         if (v.y > 0.f) M = fmaxf(M, v.x);
     }
@@ -342,26 +349,26 @@ __global__ __launch_bounds__(64) void gqa_combine_kernel(const GqaParams p)
     float L = 0.f, o[PL];
 #pragma unroll
     for (int e = 0; e < PL; e++) o[e] = 0.f;
-    for (int k0 = 0; k0 < ns; k0 += 64) {
+    for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
         float wk = 0.f;
-        if (k0 + lane < ns) {
+        if (k0 + lane < k_hi) {
             const float2 v = ml[k0 + lane];
             if (v.y > 0.f) {
                 wk = __builtin_amdgcn_exp2f(v.x - M);
                 L = fmaf(wk, v.y, L);
             }
         }
-        const int cnt = min(64, ns - k0);
-        for (int kk = 0; kk < cnt; kk += 8) {
-            float x[8][PL];
+        const int cnt = min(64, k_hi - k0);
+        for (int kk = 0; kk < cnt; kk += U) {
+            float x[U][PL];
 #pragma unroll
-            for (int u = 0; u < 8; u++)
-                if (kk + u < cnt) {
+            for (int u = 0; u < U; u++) {
+                const int k = k0 + min(kk + u, cnt - 1);   // clamped: loads stay unconditional
 #pragma unroll
-                    for (int e = 0; e < PL; e++) x[u][e] = po[(size_t)(k0 + kk + u) * D + e];
-                }
+                for (int e = 0; e < PL; e++) x[u][e] = po[(size_t)k * D + e];
+            }
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
+            for (int u = 0; u < U; u++) {
                 if (kk + u < cnt) {
                     const float wu = __builtin_bit_cast(
                         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), kk + u));
@@ -374,6 +381,31 @@ __global__ __launch_bounds__(64) void gqa_combine_kernel(const GqaParams p)
         }
     }
     L = wave_sum(L);
+    if (NWV > 1) {
+        if (lane == 0) {
+            sM[wave] = M;
+            sL[wave] = L;
+        }
+#pragma unroll
+        for (int e = 0; e < PL; e++) so[wave][lane * PL + e] = o[e];
+        __syncthreads();
+        if (wave != 0) return;
+        float Mt = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < NWV; v++)
+            if (sL[v] > 0.f) Mt = fmaxf(Mt, sM[v]);
+        L = 0.f;
+#pragma unroll
+        for (int e = 0; e < PL; e++) o[e] = 0.f;
+#pragma unroll
+        for (int v = 0; v < NWV; v++) {
+            const float wv = sL[v] > 0.f ? __builtin_amdgcn_exp2f(sM[v] - Mt) : 0.f;
+            L = fmaf(wv, sL[v], L);
+#pragma unroll
+            for (int e = 0; e < PL; e++) o[e] = fmaf(wv, so[v][lane * PL + e], o[e]);
+        }
+        M = Mt;
+    }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const size_t oo = (size_t)bh * D + lane * PL;
 #pragma unroll
@@ -384,12 +416,24 @@ __global__ __launch_bounds__(64) void gqa_combine_kernel(const GqaParams p)
     if (lane == 0 && p.lse) p.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
+template <int D, bool F32>
+static void launch_combine_d(const GqaParams& p, unsigned cg, hipStream_t st)
+{
+    // more wavefronts per (b, head) when there are many splits to merge
+    if (p.n_split <= 32)
+        hipLaunchKernelGGL((gqa_combine_kernel<D, F32, 1>), dim3(cg), dim3(64), 0, st, p);
+    else if (p.n_split <= 256)
+        hipLaunchKernelGGL((gqa_combine_kernel<D, F32, 4>), dim3(cg), dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((gqa_combine_kernel<D, F32, 16>), dim3(cg), dim3(1024), 0, st, p);
+}
+
 hipError_t launch_gqa_combine(const GqaParams& p, int d_h, bool f32, hipStream_t st)
 {
     const unsigned cg = (unsigned)(p.B * p.h);
-    if (f32) hipLaunchKernelGGL((gqa_combine_kernel<64, true>), dim3(cg), dim3(64), 0, st, p);
-    else if (d_h == 64) hipLaunchKernelGGL((gqa_combine_kernel<64, false>), dim3(cg), dim3(64), 0, st, p);
-    else hipLaunchKernelGGL((gqa_combine_kernel<128, false>), dim3(cg), dim3(64), 0, st, p);
+    if (f32) launch_combine_d<64, true>(p, cg, st);
+    else if (d_h == 64) launch_combine_d<64, false>(p, cg, st);
+    else launch_combine_d<128, false>(p, cg, st);
     return hipGetLastError();
 }
 

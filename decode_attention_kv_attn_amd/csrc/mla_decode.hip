@@ -27,18 +27,51 @@ namespace attn {
 //    loads in flight at once and read as the MFMA B operand through
 //    transposing reads; q_nope rows are the A operand, fetched up front.
 // ---------------------------------------------------------------------------
-// the decode tile schedule (defined with the decode kernels below)
-__device__ void mla_schedule(const MlaParams& p, int tid, int nthr, int* sc);
+// the decode tile schedule (defined with the decode kernels below).  Its
+// inputs are passed by value: a reference to the kernel's parameter block
+// would force a copy of it into scratch memory for every wavefront.
+struct SchedArgs {
+    const int32_t* s;
+    int32_t* sched;
+    int B, s_max, n_wg, min_tiles;
+};
+__device__ __forceinline__ void mla_schedule(SchedArgs p, int tid, int nthr, int* sc);
 
 constexpr int kAbsCols = 128;
 constexpr int kAbsRowStride = kAbsCols * 2 + 16;
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// q_nope rows of one 16-sequence block as the A operand, K steps 0..7 (steps
+// past d_nope / 32 and rows past B are zero).  The loads are unconditional
+// from clamped addresses and masked afterwards, so all of them are in flight
+// together.
+struct AbsA {
+    bf16x8 k[8];
+};
+__device__ __forceinline__ AbsA absorb_load_a(const uint16_t* __restrict__ qn, int b0, int li, int G,
+                                              int B, int h, int i, int d_nope)
+{
+    AbsA a;
+    const int ksteps = d_nope / 32;
+    const int bb = b0 + li, bc = min(bb, B - 1);
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int kc = min(k, ksteps - 1);
+        const u32x4v v = *(const u32x4v*)(qn + ((size_t)bc * h + i) * d_nope + kc * 32 + 8 * G);
+        const unsigned keep = (k < ksteps && bb < B) ? 0xffffffffu : 0u;   // mask, not a branch
+        a.k[k] = __builtin_bit_cast(bf16x8, v & keep);
+    }
+    return a;
+}
+
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ __attribute__((aligned(16))) uint16_t ost[4][16][32 + 8];   // per-wavefront output staging
     if (blockIdx.x == gridDim.x - 1) {   // one extra workgroup: the decode tile schedule
         __shared__ int sc[256];
-        mla_schedule(p, threadIdx.x, 256, sc);
+        mla_schedule(SchedArgs{p.s, p.sched, p.B, p.s_max, p.n_wg, p.min_tiles}, threadIdx.x, 256, sc);
         return;
     }
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
@@ -49,43 +82,28 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
     const int W = p.d_c + p.d_R;
     const uint16_t* __restrict__ wuk = (const uint16_t*)p.w_uk + (size_t)i * p.d_nope * p.d_c;
     const uint16_t* __restrict__ qn = (const uint16_t*)p.q_nope;
-
-    // q_nope rows of one 16-sequence block: the A operand (rows past B are zero)
     const int ksteps = p.d_nope / 32;
-    // (loads are unconditional from clamped addresses and masked afterwards,
-    // so that all of them are in flight together)
-    auto load_a = [&](int b0, bf16x8* a) {
-        const int bb = b0 + li;
-        const int bc = min(bb, p.B - 1);
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const int kc = min(k, ksteps - 1);
-            const uint4 v = *(const uint4*)(qn + ((size_t)bc * p.h + i) * p.d_nope + kc * 32 + 8 * G);
-            const uint32_t keep = (k < ksteps && bb < p.B) ? 0xffffffffu : 0u;   // mask, not a branch
-            a[k] = __builtin_bit_cast(bf16x8, make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep));
-        }
-    };
-    bf16x8 a[8];
-    load_a(0, a);
 
-    // stage W_UK[i][:, c0:c0+128]: d_nope rows x 16 chunks, 8 loads in flight per thread
+    AbsA a = absorb_load_a(qn, 0, li, G, p.B, p.h, i, p.d_nope);
+
+    // stage W_UK[i][:, c0:c0+128]: d_nope rows x 16 chunks, 8 loads in flight
+    // per thread; past the end, lanes load and store the last chunk again
+    // (same place, same value), so nothing branches and the staging values
+    // stay in registers
     const int nchunk = p.d_nope * (kAbsCols / 8);
     for (int base = 0; base < nchunk; base += 256 * 8) {
-        uint4 v[8];
+        u32x4v v[8];
 #pragma unroll
         for (int u = 0; u < 8; u++) {
-            const int idx = min(base + u * 256 + tid, nchunk - 1);   // clamped: loads stay unconditional
+            const int idx = min(base + u * 256 + tid, nchunk - 1);
             const int r = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
-            v[u] = *(const uint4*)(wuk + (size_t)r * p.d_c + c0 + c * 8);
+            v[u] = *(const u32x4v*)(wuk + (size_t)r * p.d_c + c0 + c * 8);
         }
-        __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first store
 #pragma unroll
         for (int u = 0; u < 8; u++) {
-            const int idx = base + u * 256 + tid;
-            if (idx < nchunk) {
-                const int r = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
-                *(uint4*)(smem + r * kAbsRowStride + c * 16) = v[u];
-            }
+            const int idx = min(base + u * 256 + tid, nchunk - 1);
+            const int r = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
+            *(u32x4v*)(smem + r * kAbsRowStride + c * 16) = v[u];
         }
     }
     // the rotary part of q^ is a plain copy (done once per head, 16 bytes per
@@ -94,27 +112,28 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
         const int per = p.d_R / 8, nv = p.B * per;
         const uint16_t* __restrict__ qr = (const uint16_t*)p.q_rope;
         for (int base = 0; base < nv; base += 4 * 256) {
-            uint4 v[4];
+            u32x4v v[4];
 #pragma unroll
             for (int u = 0; u < 4; u++) {
                 const int idx = min(base + u * 256 + tid, nv - 1);
-                v[u] = *(const uint4*)(qr + ((size_t)(idx / per) * p.h + i) * p.d_R + 8 * (idx % per));
+                v[u] = *(const u32x4v*)(qr + ((size_t)(idx / per) * p.h + i) * p.d_R + 8 * (idx % per));
             }
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                const int idx = base + u * 256 + tid;
-                if (idx < nv) *(uint4*)(p.qhat + ((size_t)(idx / per) * p.h + i) * W + p.d_c + 8 * (idx % per)) = v[u];
+                const int idx = min(base + u * 256 + tid, nv - 1);   // duplicates rewrite the same value
+                *(u32x4v*)(p.qhat + ((size_t)(idx / per) * p.h + i) * W + p.d_c + 8 * (idx % per)) = v[u];
             }
         }
     }
 
     __syncthreads();
 
-    // wavefront w computes column tiles 2w and 2w+1 for every 16-row block of
-    // b; the next block's q_nope is fetched while this one is multiplied
+    // wavefront w computes column tiles 2w and 2w+1 (32 columns) for every
+    // 16-row block of b; the next block's q_nope is fetched while this one
+    // is multiplied.  The block's 16 x 32 results go through LDS so that
+    // each lane stores 16 contiguous bytes.
     for (int b0 = 0; b0 < p.B; b0 += 16) {
-        bf16x8 an[8];
-        if (b0 + 16 < p.B) load_a(b0 + 16, an);
+        const AbsA an = absorb_load_a(qn, min(b0 + 16, p.B - 1), li, G, p.B, p.h, i, p.d_nope);
 #pragma unroll
         for (int t = 0; t < 2; t++) {
             const int nt = 2 * wave + t;
@@ -126,21 +145,22 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
                     const int col = nt * 16 + 4 * (li % 4);
                     const s16x4 lo = lds_read_tr(smem + row * kAbsRowStride + col * 2);
                     const s16x4 hi = lds_read_tr(smem + (row + 4) * kAbsRowStride + col * 2);
-                    acc = mfma16(a[k], cat_tr(lo, hi), acc);
+                    acc = mfma16(a.k[k], cat_tr(lo, hi), acc);
                 }
             }
             // lane holds q~[b0 + 4G + e][c0 + 16 nt + li]
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int br = b0 + 4 * G + e;
-                if (br < p.B)
-                    p.qhat[((size_t)br * p.h + i) * W + c0 + nt * 16 + li] = (uint16_t)f32_to_bf16_bits(acc[e]);
-            }
+            for (int e = 0; e < 4; e++) ost[wave][4 * G + e][16 * t + li] = (uint16_t)f32_to_bf16_bits(acc[e]);
         }
-        if (b0 + 16 < p.B) {
-#pragma unroll
-            for (int k = 0; k < 8; k++) a[k] = an[k];
+        __syncthreads();
+        {
+            const int r = lane / 4, sg = lane % 4;   // row of the block, 16-byte segment
+            const u32x4v v = *(const u32x4v*)&ost[wave][r][8 * sg];
+            if (b0 + r < p.B)
+                *(u32x4v*)(p.qhat + ((size_t)(b0 + r) * p.h + i) * W + c0 + 32 * wave + 8 * sg) = v;
         }
+        __syncthreads();
+        a = an;
     }
 }
 
@@ -271,7 +291,7 @@ struct SchedView {
 // tiles (which fixes tpw), the second scans them again and writes the tile
 // offsets and each workgroup's first sequence; no thread reads back what
 // another wrote to global memory.
-__device__ void mla_schedule(const MlaParams& p, int tid, int nthr, int* sc)
+__device__ __forceinline__ void mla_schedule(SchedArgs p, int tid, int nthr, int* sc)
 {
     int32_t* ts = p.sched;
     int32_t* wstart = p.sched + p.B + 1;
@@ -802,20 +822,38 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
 }
 
 // ---------------------------------------------------------------------------
-// 3. finish.  Workgroup = (head i, 16 sequences).  Merge each sequence's
-//    partials into u~ (fp32; written to u_latent and kept in LDS), then
-//    out[b, i, :] = W_UV[i] u~[b, i, :] on the matrix cores.  u~ is fed as a
-//    bf16 hi/lo pair (u~ = hi + lo exactly to about 2^-16 relative), so the
-//    product keeps u~ at fp32-level precision; W_UV rows are the B operand
-//    as stored (16 contiguous bytes per lane).
+// 3. finish.  Workgroup = (head i, up to 8 sequences), 8 wavefronts.
+//    Merge: a wavefront takes one sequence, lane l its columns 8l .. 8l+7
+//    (a partial row is read as two contiguous 1 KB spans).  The split maxima
+//    and sums are wave-uniform, so they come in as scalar loads, and up to 8
+//    partials are in flight per wavefront; chunks are folded in with a
+//    running maximum.  When the block holds fewer than 8 sequences the idle
+//    wavefronts take a share of some sequence's partials instead, and the
+//    shares are combined through LDS.
+//    Product: out[b, i, :] = W_UV[i] u~[b, i, :] on the matrix cores, with
+//    u~ fed as a bf16 hi/lo pair (u~ = hi + lo to about 2^-16 relative, so
+//    the product keeps u~ at fp32-level precision): A rows 0..7 are the hi
+//    parts of the 8 sequences, rows 8..15 their lo parts, and the two halves
+//    of the result are added across lanes.  W_UV rows are the B operand as
+//    stored (16 contiguous bytes per lane).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void mla_finish_kernel(const MlaParams p)
+constexpr int kFinSeq = 8;     // sequences (and wavefronts) per workgroup
+constexpr int kFinChunk = 8;   // partials in flight per wavefront
+constexpr int kAbStride = 512 + 8;   // bf16 per A-operand row in LDS
+
+__global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParams p)
 {
-    __shared__ __attribute__((aligned(16))) float Us[16][512 + 4];
+    __shared__ __attribute__((aligned(16))) float Acc[kFinSeq][512];      // shares, when split
+    __shared__ float Mls[kFinSeq][2];
+    __shared__ __attribute__((aligned(16))) uint16_t Ab[2 * kFinSeq][kAbStride];
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int i = blockIdx.x % p.h;
-    const int b0 = (blockIdx.x / p.h) * 16;
+    const int b0 = (blockIdx.x / p.h) * kFinSeq;
+    const int nb = min(kFinSeq, p.B - b0);   // >= 1: the grid covers exactly the sequences
+    const int sq = wave % nb, sub = wave / nb;
+    const int nsub = (kFinSeq - sq + nb - 1) / nb;   // wavefronts sharing sequence sq
+    const int bb = b0 + sq;
 
     // W_UV fragments of this wavefront's first column tile, fetched now so
     // that their latency hides behind the merge
@@ -827,84 +865,117 @@ __global__ __launch_bounds__(256) void mla_finish_kernel(const MlaParams p)
         for (int k = 0; k < 16; k++) bws[k] = *(const bf16x8*)(wrow + 32 * k);
     }
 
-    // merge: thread -> sequence r = tid / 16 of the block, 32 columns at
-    // 32 * (tid % 16).  Pass 1 takes the largest split max over the splits
-    // that saw tokens; pass 2 adds the partial sums, four splits' loads in
-    // flight at once.  An empty split (l = 0) leaves its partial sum
-    // unwritten: it is loaded (the workspace holds it) but never used.
-    {
-        const int r = tid / 16, cseg = (tid % 16) * 32, bb = b0 + r;
-        float4 acc[8];
+    // the partials of sequence bb: slots w + bb of the workgroups w whose
+    // tile ranges overlap its tiles; this wavefront takes k = sub + nsub j
+    const int32_t* __restrict__ sched = p.sched;
+    const int s0 = max(sched[bb], 0), s1 = sched[bb + 1];
+    const int tpw = max(sched[p.B + 1 + p.n_wg], 1);
+    const int wf = min(s0 / tpw, p.n_wg - 1);
+    const int ns = s1 > s0 ? min(max((s1 - 1) / tpw - wf + 1, 0), p.n_wg - wf) : 0;
+    const int nj = ns > sub ? (ns - sub + nsub - 1) / nsub : 0;
+    const size_t row0 = (size_t)(wf + bb) * p.h + i;   // partial k: row0 + k h
+    const float2* __restrict__ ml = (const float2*)p.part_ml;
+    const float4* __restrict__ pu = (const float4*)p.part_u;
+
+    float M = -INFINITY, L = 0.f;
+    float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+    for (int j0 = 0; j0 < nj; j0 += kFinChunk) {
+        float2 v[kFinChunk];
+        float4 u[kFinChunk][2];
 #pragma unroll
-        for (int q = 0; q < 8; q++) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-        float M = -INFINITY, L = 0.f;
-        if (bb < p.B) {
-            // the partials of sequence bb: slots w + bb of the workgroups w
-            // whose tile ranges overlap its tiles
-            const int s0 = max(p.sched[bb], 0), s1 = p.sched[bb + 1];
-            const int tpw = max(p.sched[p.B + 1 + p.n_wg], 1);
-            const int wf = min(s0 / tpw, p.n_wg - 1);
-            const int ns = s1 > s0 ? min(max((s1 - 1) / tpw - wf + 1, 0), p.n_wg - wf) : 0;
-            const float2* __restrict__ ml = (const float2*)p.part_ml;
-            const size_t row0 = (size_t)(wf + bb) * p.h + i;   // partial k: row0 + k h
-            for (int k0 = 0; k0 < ns; k0 += 8) {
-                float2 v[8];
-#pragma unroll
-                for (int u = 0; u < 8; u++)
-                    if (k0 + u < ns) v[u] = ml[row0 + (size_t)(k0 + u) * p.h];
-#pragma unroll
-                for (int u = 0; u < 8; u++)
-                    if (k0 + u < ns && v[u].y > 0.f) M = fmaxf(M, v[u].x);
-            }
-            const float4* __restrict__ pu = (const float4*)p.part_u;
-            for (int k0 = 0; k0 < ns; k0 += 4) {
-                float2 v[4];
-                float4 u[4][8];
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    if (k0 + g < ns) {
-                        const size_t row = row0 + (size_t)(k0 + g) * p.h;
-                        v[g] = ml[row];
-#pragma unroll
-                        for (int q = 0; q < 8; q++) u[g][q] = pu[(row * 512 + cseg) / 4 + q];
-                    }
-                }
-#pragma unroll
-                for (int g = 0; g < 4; g++) {
-                    if (k0 + g < ns && v[g].y > 0.f) {
-                        const float wk = __builtin_amdgcn_exp2f(v[g].x - M);
-                        L = fmaf(wk, v[g].y, L);
-#pragma unroll
-                        for (int q = 0; q < 8; q++) {
-                            acc[q].x = fmaf(wk, u[g][q].x, acc[q].x);
-                            acc[q].y = fmaf(wk, u[g][q].y, acc[q].y);
-                            acc[q].z = fmaf(wk, u[g][q].z, acc[q].z);
-                            acc[q].w = fmaf(wk, u[g][q].w, acc[q].w);
-                        }
-                    }
-                }
-            }
-            const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                acc[q].x *= inv; acc[q].y *= inv; acc[q].z *= inv; acc[q].w *= inv;
-            }
-            if (p.u_latent) {
-                float4* dst = (float4*)(p.u_latent + ((size_t)bb * p.h + i) * 512 + cseg);
-#pragma unroll
-                for (int q = 0; q < 8; q++) dst[q] = acc[q];
-            }
-            if ((tid % 16) == 0 && p.lse)
-                p.lse[(size_t)bb * p.h + i] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+        for (int c = 0; c < kFinChunk; c++) {   // clamped, unconditional loads
+            const int jj = min(j0 + c, nj - 1);
+            const size_t row = row0 + (size_t)(sub + nsub * jj) * p.h;
+            v[c] = ml[row];
+            u[c][0] = pu[row * 128 + 2 * lane];
+            u[c][1] = pu[row * 128 + 2 * lane + 1];
         }
+        float Mc = M;
 #pragma unroll
-        for (int q = 0; q < 8; q++) *(float4*)&Us[r][cseg + 4 * q] = acc[q];
+        for (int c = 0; c < kFinChunk; c++)
+            if (j0 + c < nj && v[c].y > 0.f) Mc = fmaxf(Mc, v[c].x);
+        if (Mc == -INFINITY) continue;   // nothing seen yet
+        const float sc = __builtin_amdgcn_exp2f(M - Mc);   // 0 while M = -inf
+        L *= sc;
+        a0 *= sc;
+        a1 *= sc;
+#pragma unroll
+        for (int c = 0; c < kFinChunk; c++) {
+            if (j0 + c < nj && v[c].y > 0.f) {   // wave-uniform
+                const float wk = __builtin_amdgcn_exp2f(v[c].x - Mc);
+                L = fmaf(wk, v[c].y, L);
+                a0.x = fmaf(wk, u[c][0].x, a0.x); a0.y = fmaf(wk, u[c][0].y, a0.y);
+                a0.z = fmaf(wk, u[c][0].z, a0.z); a0.w = fmaf(wk, u[c][0].w, a0.w);
+                a1.x = fmaf(wk, u[c][1].x, a1.x); a1.y = fmaf(wk, u[c][1].y, a1.y);
+                a1.z = fmaf(wk, u[c][1].z, a1.z); a1.w = fmaf(wk, u[c][1].w, a1.w);
+            }
+        }
+        M = Mc;
+    }
+
+    // combine the shares of a sequence split over several wavefronts
+    if (nb < kFinSeq) {   // workgroup-uniform
+        *(float4*)&Acc[wave][8 * lane] = a0;
+        *(float4*)&Acc[wave][8 * lane + 4] = a1;
+        if (lane == 0) {
+            Mls[wave][0] = M;
+            Mls[wave][1] = L;
+        }
+        __syncthreads();
+        if (wave < nb) {
+            float Mt = -INFINITY;
+            for (int t = 0; t < nsub; t++) Mt = fmaxf(Mt, Mls[wave + nb * t][0]);
+            L = 0.f;
+            a0 = make_float4(0.f, 0.f, 0.f, 0.f);
+            a1 = a0;
+            if (Mt != -INFINITY) {
+                for (int t = 0; t < nsub; t++) {
+                    const int src = wave + nb * t;
+                    const float wt = __builtin_amdgcn_exp2f(Mls[src][0] - Mt);   // 0 for an empty share
+                    L = fmaf(wt, Mls[src][1], L);
+                    const float4 x0 = *(const float4*)&Acc[src][8 * lane];
+                    const float4 x1 = *(const float4*)&Acc[src][8 * lane + 4];
+                    a0.x = fmaf(wt, x0.x, a0.x); a0.y = fmaf(wt, x0.y, a0.y);
+                    a0.z = fmaf(wt, x0.z, a0.z); a0.w = fmaf(wt, x0.w, a0.w);
+                    a1.x = fmaf(wt, x1.x, a1.x); a1.y = fmaf(wt, x1.y, a1.y);
+                    a1.z = fmaf(wt, x1.z, a1.z); a1.w = fmaf(wt, x1.w, a1.w);
+                }
+            }
+            M = Mt;
+        }
+    }
+
+    // u~ = U / L: written out if asked, and split into the A operand rows
+    if (wave < nb) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        a0 *= inv;
+        a1 *= inv;
+        if (p.u_latent) {
+            float4* dst = (float4*)(p.u_latent + ((size_t)bb * p.h + i) * 512) + 2 * lane;
+            dst[0] = a0;
+            dst[1] = a1;
+        }
+        if (lane == 0 && p.lse)
+            p.lse[(size_t)bb * p.h + i] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+        const float xs[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const uint32_t h2 = pack_bf16x2(xs[e], xs[e + 1]);
+            hi[e / 2] = h2;
+            lo[e / 2] = pack_bf16x2(xs[e] - bf16lo_to_f32(h2), xs[e + 1] - bf16hi_to_f32(h2));
+        }
+        *(uint4*)&Ab[wave][8 * lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *(uint4*)&Ab[kFinSeq + wave][8 * lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    } else {   // rows of absent sequences: zeros
+        *(uint4*)&Ab[wave][8 * lane] = make_uint4(0, 0, 0, 0);
+        *(uint4*)&Ab[kFinSeq + wave][8 * lane] = make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
 
-    // out[b0 + m, i, n] = sum_c u~[m][c] W_UV[i][n][c]: M = 16 sequences,
-    // N = d_v (wavefront w takes column tiles w, w+4, ...), K = d_c
-    for (int nt = wave; nt < p.d_v / 16; nt += 4) {
+    // out[b0 + r, i, n] = sum_c u~[r][c] W_UV[i][n][c]: wavefront w takes
+    // column tiles w, w + 8, ...; result row r (< 8) is hi, r + 8 its lo part
+    for (int nt = wave; nt < p.d_v / 16; nt += kFinSeq) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (nt != wave) {
             const uint16_t* wrow = wuv + (size_t)(nt * 16 + li) * p.d_c + 8 * G;
@@ -913,29 +984,16 @@ __global__ __launch_bounds__(256) void mla_finish_kernel(const MlaParams p)
             __builtin_amdgcn_sched_barrier(0);   // all 16 loads in flight before the first use
         }
 #pragma unroll
-        for (int k = 0; k < 16; k++) {
-            const int k0 = 32 * k;
-            const bf16x8 bw = bws[k];
-            const float4 x0 = *(const float4*)&Us[li][k0 + 8 * G];
-            const float4 x1 = *(const float4*)&Us[li][k0 + 8 * G + 4];
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const uint32_t h2 = pack_bf16x2(xs[e], xs[e + 1]);
-                hi[e / 2] = h2;
-                lo[e / 2] = pack_bf16x2(xs[e] - bf16lo_to_f32(h2), xs[e + 1] - bf16hi_to_f32(h2));
-            }
-            acc = mfma16(__builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3])), bw, acc);
-            acc = mfma16(__builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3])), bw, acc);
-        }
-        // lane holds out[b0 + 4G + e][i][16 nt + li]
+        for (int k = 0; k < 16; k++)
+            acc = mfma16(*(const bf16x8*)&Ab[li][32 * k + 8 * G], bws[k], acc);
+        // lane (G, li) holds row 4G + e of column 16 nt + li; rows 8.. sit 32 lanes up
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const int bb = b0 + 4 * G + e;
-            if (bb < p.B)
-                ((uint16_t*)p.out)[((size_t)bb * p.h + i) * p.d_v + nt * 16 + li] =
-                    (uint16_t)f32_to_bf16_bits(acc[e]);
+            const float o = acc[e] + xor32(acc[e]);
+            const int r = 4 * G + e;
+            if (G < 2 && r < nb)
+                ((uint16_t*)p.out)[((size_t)(b0 + r) * p.h + i) * p.d_v + nt * 16 + li] =
+                    (uint16_t)f32_to_bf16_bits(o);
         }
     }
 }
@@ -965,8 +1023,8 @@ hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned g3 = (unsigned)(p.h * ((p.B + 15) / 16));
-    hipLaunchKernelGGL(mla_finish_kernel, dim3(g3), dim3(256), 0, st, p);
+    const unsigned g3 = (unsigned)(p.h * ((p.B + kFinSeq - 1) / kFinSeq));
+    hipLaunchKernelGGL(mla_finish_kernel, dim3(g3), dim3(64 * kFinSeq), 0, st, p);
     return hipGetLastError();
 }
 

@@ -66,6 +66,18 @@ def test_long_context_split():
     run(shape(1, 128, (12000,), seed=6))
 
 
+def test_many_partials_per_sequence():
+    # ~240 workgroups share one sequence: the merge folds its partials in
+    # several chunks on each of the wavefronts that split them
+    run(shape(1, 16, (70000,), seed=43))
+
+
+def test_nine_sequences_wide_value():
+    # one full block of 8 sequences and one of a single sequence; d_v = 256
+    # gives each wavefront two output column tiles
+    run(shape(9, 16, tuple(range(300, 300 + 9 * 450, 450)), seed=44, d_v=256))
+
+
 # The decode tile schedule gives each of the 256 workgroups an equal run of
 # 32-token tiles across sequence boundaries (at least 8 tiles).  Many short
 # sequences put several sequences, empty ones among them, into one

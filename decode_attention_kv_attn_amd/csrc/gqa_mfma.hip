@@ -142,31 +142,44 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     // 16-token halves each lie in one block of a paged pool (blocks hold a
     // power of two >= 16 of rows), so a tile needs the physical rows of just
     // its two half starts; they are looked up one iteration before the tile
-    // is issued, keeping the scalar-load latency off the issue path.
+    // is issued, keeping the scalar-load latency off the issue path.  One
+    // buffer resource per (K or V, half) covers the rows of that half inside
+    // the split (rows past it read as zero); an instruction's lanes reach
+    // their row and chunk through a per-lane offset that is the same for
+    // every tile.
     const size_t rowstride = (size_t)p.h_kv * C::RB;   // bytes between tokens of one head
     const uint8_t* __restrict__ kb = (const uint8_t*)p.k + (size_t)j * C::RB;
     const uint8_t* __restrict__ vb = (const uint8_t*)p.v + (size_t)j * C::RB;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Ls;
-    const int lr = lane / C::NCH, lp = lane % C::NCH;
+    uint32_t voff[OPW];
+    {
+        const int lr = lane / C::NCH, lp = lane % C::NCH;
+#pragma unroll
+        for (int jj = 0; jj < OPW; jj++) {
+            const int q = wave + NW * jj;
+            const int rt = (q % (C::OPS / 2)) * C::RPO;   // first tile row of this instruction
+            voff[jj] = (uint32_t)(((rt & 15) + lr) * (int)rowstride + ((lp ^ gswz<D>(rt + lr)) << 4));
+        }
+    }
     auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
         if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
         return (size_t)b * p.s_max + t;
     };
     auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
+        const int nv0 = min(max(t1 - tb, 0), 16), nv1 = min(max(t1 - tb - 16, 0), 16);
+        const int nr0 = nv0 > 0 ? (nv0 - 1) * (int)rowstride + C::RB : 0;
+        const int nr1 = nv1 > 0 ? (nv1 - 1) * (int)rowstride + C::RB : 0;
+        const rsrc_t k0 = make_rsrc(kb + row0 * rowstride, nr0), k1 = make_rsrc(kb + row1 * rowstride, nr1);
+        const rsrc_t v0 = make_rsrc(vb + row0 * rowstride, nr0), v1 = make_rsrc(vb + row1 * rowstride, nr1);
+        const uint32_t lb = lds0 + (uint32_t)(buf * 2 * C::KT);
 #pragma unroll
         for (int jj = 0; jj < OPW; jj++) {
             const int q = wave + NW * jj;
             const bool isv = q >= C::OPS / 2;
             const int rb = isv ? q - C::OPS / 2 : q;
-            const int rt = rb * C::RPO;               // first tile row of this instruction
-            const int r0 = tb + rt;
-            const size_t row = (rt < 16 ? row0 : row1) + (rt & 15);
-            const int nv = min(C::RPO, t1 - r0);      // rows inside the split
-            const int nr = nv > 0 ? (nv - 1) * (int)rowstride + C::RB : 0;
-            const rsrc_t rs = make_rsrc((isv ? vb : kb) + row * rowstride, nr);
-            const int c = lp ^ gswz<D>(rt + lr);
-            dma16(rs, (uint32_t)(lr * (int)rowstride + c * 16),
-                  lds0 + buf * 2 * C::KT + (isv ? C::KT : 0) + rb * 1024);
+            const bool h1 = rb * C::RPO >= 16;
+            const rsrc_t rs = isv ? (h1 ? v1 : v0) : (h1 ? k1 : k0);
+            dma16(rs, voff[jj], lb + (isv ? C::KT : 0) + rb * 1024);
         }
     };
 

@@ -372,19 +372,26 @@ struct TileWalk {
 // DMA of one tile (all 36 slots of 8 rows x 128 bytes, spread over the
 // wavefronts; slot q fills segment q / 4, rows 8 (q % 4) .. + 7) and the
 // physical rows of its two 16-row halves.  A tile's halves each lie in one
-// block of a paged pool (blocks hold a power of two >= 16 rows).
+// block of a paged pool (blocks hold a power of two >= 16 rows).  With NW a
+// multiple of 4 a wavefront's slots all cover the same 8 rows (q % 4 =
+// wave % 4), so one buffer resource per tile serves all of them and a slot
+// differs only in its segment's byte offset and LDS destination.
 template <int NW, bool PAGED>
 struct TileDma {
+    static_assert(NW % 4 == 0, "a wavefront's slots must share their rows");
     static constexpr int SPW = kSlots / NW + (kSlots % NW ? 1 : 0);   // slots per wavefront
     const MlaParams& p;
     const int32_t* __restrict__ btab;
     const uint8_t* __restrict__ cbase;
-    uint32_t lds0;
-    int wave, lr, lp;
+    uint32_t lds0, vbase;
+    int wave, rb;
     __device__ __forceinline__ TileDma(const MlaParams& p_, const int32_t* __restrict__ bt,
                                        uint32_t lds, int wave_, int lane)
-        : p(p_), btab(bt), cbase((const uint8_t*)p_.cache), lds0(lds), wave(wave_),
-          lr(lane / 8), lp(lane % 8) {}
+        : p(p_), btab(bt), cbase((const uint8_t*)p_.cache), lds0(lds), wave(wave_), rb(wave_ & 3)
+    {
+        const int lr = lane / 8, lp = lane % 8;   // row of the 8, 16-byte position in the segment
+        vbase = (uint32_t)(lr * kRow + 16 * (lp ^ swz(8 * rb + lr)));
+    }
     __device__ __forceinline__ size_t half_row(int b, int t) const
     {
         if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
@@ -401,18 +408,16 @@ struct TileDma {
     }
     __device__ __forceinline__ void issue(const TileWalk& c, int buf, size_t row0, size_t row1) const
     {
+        const size_t row = (rb < 2 ? row0 : row1) + 8 * (rb & 1);   // first row of this wavefront's 8
+        const int t0 = c.lt * kT + 8 * rb;                            // its token index
+        const int nr = c.past() ? 0 : max(0, min(8, c.n - t0)) * kRow;   // rows past the length read 0
+        const rsrc_t rs = make_rsrc(cbase + row * kRow, nr);
+        const uint32_t lb = lds0 + (uint32_t)(buf * kTile);
 #pragma unroll
         for (int j = 0; j < SPW; j++) {
             const int q = wave + NW * j;
-            if (q < kSlots) {                      // wave-uniform
-                const int seg = q >> 2, rb = q & 3;
-                const int r0 = c.lt * kT + 8 * rb; // first token of the slot
-                const size_t row = (rb < 2 ? row0 : row1) + 8 * (rb & 1);
-                const int nr = c.past() ? 0 : max(0, min(8, c.n - r0)) * kRow;
-                const rsrc_t rs = make_rsrc(cbase + row * kRow, nr);
-                const int ch = 8 * seg + (lp ^ swz(8 * rb + lr));
-                dma16(rs, (uint32_t)(lr * kRow + ch * 16), lds0 + buf * kTile + q * 1024);
-            }
+            if (kSlots % NW == 0 || q < kSlots)   // wave-uniform, static when NW divides the slots
+                dma16(rs, vbase + 128u * (uint32_t)(q >> 2), lb + (uint32_t)q * 1024u);
         }
     }
     // tiles tb + T and tb + 2T were issued after tile tb

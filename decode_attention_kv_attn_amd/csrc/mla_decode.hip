@@ -165,18 +165,27 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 }
 
 // ---------------------------------------------------------------------------
-// 2. decode.  Workgroup = (b, token split) with all heads, so every latent
-//    tile is fetched once: 4 wavefronts x 32 heads in the fast kernel (one
-//    wavefront per SIMD, accumulators in AGPRs), 8 x 16 in the rescaling
-//    fallback.  Tiles of 32 rows move HBM -> LDS by LDS-DMA (buffer_load ...
-//    lds, no staging registers) into a ring of 4 buffers, three tiles ahead
-//    of use.  Per wavefront, 16-head block and tile:
-//      S^T[32 tok x 16 heads] = C_tile[32 x 576] . q^T     (A: LDS, B: q^ in registers)
-//      online softmax on S^T (lane = head, 8 tokens per lane)
-//      U^T[512 x 16] += C_tile^T[512 x 32] . P^T[32 x 16]  (A: transposing LDS reads, B: P)
+// 2. decode.  Workgroup = a run of tiles with all heads, so every latent
+//    tile is fetched once.  Tiles of 32 rows move HBM -> LDS by LDS-DMA
+//    (buffer_load ... lds, no staging registers) into a ring of 4 buffers,
+//    three tiles ahead of use.
+//    Fast kernel, 4 wavefronts (one per SIMD, accumulators in AGPRs):
+//      scores   wavefront w, heads 32w .. 32w+31, per 16-head block:
+//               S^T[32 tok x 16 heads] = C_tile[32 x 576] . q^T  (A: LDS, B: q^ in registers),
+//               softmax weights P on S^T (lane = head, 8 tokens per lane);
+//      exchange P of all heads through LDS (8 KB per tile);
+//      latent   wavefront w, latent columns 128w .. 128w+127, all heads:
+//               U^T[128 x 128] += C_tile^T[128 x 32] . P^T[32 x 128]
+//               (A: transposing LDS reads of a quarter of the tile, B: P).
+//    Splitting the latent sum by columns instead of heads means each latent
+//    byte is read from LDS by one wavefront there instead of four; with the
+//    score reads this cuts the LDS traffic per tile from 288 KB to 208 KB,
+//    and LDS bandwidth (about 100 B/clock per CU for these patterns, as
+//    measured) is what bounds this loop alongside the matrix cores.
+//    The fallback kernel uses 8 wavefronts x 16 heads for both products.
 //    The token order of the value product's K axis is the score product's
 //    output layout (lane group G holds tokens 4G..4G+3 and 16+4G..16+4G+3),
-//    so P never leaves the registers.
+//    so P keeps the layout it was computed in.
 //
 //    LDS tile layout (one buffer, 36 KB): 9 segments of 128 bytes per row,
 //    segment-major: byte (s * 4096 + r * 128 + 16 * p) holds row r, 16-byte
@@ -428,19 +437,19 @@ struct TileDma {
     }
 };
 
-template <int HW, bool PAGED>
-__global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const MlaParams p,
-                                                                          const int32_t* __restrict__ btab,
-                                                                          const int32_t* __restrict__ slen,
-                                                                          const int32_t* __restrict__ sched)
+template <bool PAGED>
+__global__ __launch_bounds__(256) void mla_decode_fast_kernel(const MlaParams p,
+                                                              const int32_t* __restrict__ btab,
+                                                              const int32_t* __restrict__ slen,
+                                                              const int32_t* __restrict__ sched)
 {
-    constexpr int NW = 128 / HW;    // wavefronts per workgroup
-    constexpr int NT = HW / 16;     // head tiles per wavefront
+    constexpr int NW = 4;           // wavefronts per workgroup
+    constexpr int NT = 8 / NW;      // score head tiles per wavefront (32 heads)
     constexpr int KS = 576 / 32;    // score K steps
-    constexpr int MC = 512 / 16;    // value M tiles (latent columns)
-    constexpr int PS = 1;   // score operands are read this many K steps ahead
-    constexpr int PV = 1;   // value operands are read this many column tiles ahead
+    constexpr int VMC = 512 / NW / 16;   // latent column tiles per wavefront
+    constexpr int VNT = 128 / 16;   // head tiles of the latent sum (all heads; zeros past h)
     __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * kTile];
+    __shared__ __attribute__((aligned(16))) bf16x8 Pb[VNT][64];   // P of every head tile, B-operand layout
     __shared__ int ovf;   // some head's scores ran past its reference max + 64
 
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
@@ -455,13 +464,13 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
         if (tid == 0) p.flags[w] = 0;
         return;
     }
-    const int head0 = wave * HW;
-    const bool active = head0 < p.h;
+    const int head0 = wave * 16 * NT;
+    const bool active = head0 < p.h;   // this wavefront has score heads
 
     const TileDma<NW, PAGED> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
                                  wave, lane);
     TileWalk ic(sv, sv.first_seq(w), g0, g1);   // issue cursor
-    TileWalk cc = ic;                                                                // compute cursor
+    TileWalk cc = ic;                            // compute cursor
 
     // q^ fragments of one sequence: B operand of the score product (head
     // tiles past h read as zeros)
@@ -480,19 +489,23 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
     // and U, lsum accumulate 2^(z - m).  Later tiles may exceed m by up to 64
     // (p <= 2^64, far from fp32/bf16 overflow); past that the workgroup is
     // handed to the rescaling kernel (flag), which real logits essentially
-    // never need.
-    f32x4 U[MC][NT];
+    // never need.  m and lsum belong to this wavefront's score heads, U to
+    // its latent columns (all heads).
+    f32x4 U[VMC][VNT];
     float m[NT], lsum[NT];
     auto reset = [&]() {
 #pragma unroll
         for (int nt = 0; nt < NT; nt++) {
             m[nt] = -INFINITY;
             lsum[nt] = 0.f;
-#pragma unroll
-            for (int mc = 0; mc < MC; mc++) U[mc][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int mc = 0; mc < VMC; mc++)
+#pragma unroll
+            for (int t = 0; t < VNT; t++) U[mc][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    // partial state of sequence b: m, l per head and the U^T columns, slot w + b
+    // partial state of sequence b, slot w + b: (m, l) of the score heads and
+    // the U^T columns 128 wave .. + 127 of every head
     auto write_partial = [&](int b) {
 #pragma unroll
         for (int nt = 0; nt < NT; nt++) {
@@ -501,14 +514,19 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
             l += xor16(l);
             l += xor32(l);
             const size_t row = (size_t)(w + b) * p.h + head0 + 16 * nt + li;
-            float* pu = p.part_u + row * 512 + 4 * G;
-#pragma unroll
-            for (int mc = 0; mc < MC; mc++)
-                *(float4*)(pu + 16 * mc) = make_float4(U[mc][nt][0], U[mc][nt][1], U[mc][nt][2], U[mc][nt][3]);
             if (G == 0) {
                 p.part_ml[row * 2] = m[nt];
                 p.part_ml[row * 2 + 1] = l;
             }
+        }
+#pragma unroll
+        for (int t = 0; t < VNT; t++) {
+            if (16 * t >= p.h) continue;
+            const size_t row = (size_t)(w + b) * p.h + 16 * t + li;
+            float* pu = p.part_u + row * 512 + (512 / NW) * wave + 4 * G;
+#pragma unroll
+            for (int mc = 0; mc < VMC; mc++)
+                *(float4*)(pu + 16 * mc) = make_float4(U[mc][t][0], U[mc][t][1], U[mc][t][2], U[mc][t][3]);
         }
     };
     reset();
@@ -534,6 +552,7 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
     }
 
     const TileOffsets to(li, G);
+    const int cseg = 2 * wave * 4096;   // this wavefront's latent columns: segments 2w, 2w + 1
     int buf = 0;
     int g = g0;
     for (;;) {   // one sequence (or the part of it in this workgroup's range) per pass
@@ -550,34 +569,31 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
         ic.next(sv);
         const uint8_t* C = Cs + buf * kTile;
         const int tbase = cc.lt * kT;
+        bf16x8 P[NT];
         if (active) {
-            // ---- scores S^T = C . q^T
+            // ---- scores S^T = C . q^T, operands read one K step ahead
             f32x4 S[2][NT];
 #pragma unroll
             for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int nt = 0; nt < NT; nt++) S[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 a[PS + 1][2];   // ring of operands, PS K steps ahead
-#pragma unroll
-            for (int i = 0; i < PS; i++) {
-                a[i][0] = lds_read_16_as_2x8(to.score(C, i, 0));
-                a[i][1] = lds_read_16_as_2x8(to.score(C, i, 1));
-            }
+            bf16x8 a[2][2];
+            a[0][0] = lds_read_16_as_2x8(to.score(C, 0, 0));
+            a[0][1] = lds_read_16_as_2x8(to.score(C, 0, 1));
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
-                if (ks + PS < KS) {
-                    a[(ks + PS) % (PS + 1)][0] = lds_read_16_as_2x8(to.score(C, ks + PS, 0));
-                    a[(ks + PS) % (PS + 1)][1] = lds_read_16_as_2x8(to.score(C, ks + PS, 1));
+                if (ks + 1 < KS) {
+                    a[(ks + 1) & 1][0] = lds_read_16_as_2x8(to.score(C, ks + 1, 0));
+                    a[(ks + 1) & 1][1] = lds_read_16_as_2x8(to.score(C, ks + 1, 1));
                 }
 #pragma unroll
                 for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                     for (int nt = 0; nt < NT; nt++)
-                        S[mt][nt] = mfma16(a[ks % (PS + 1)][mt], Qf[nt][ks], S[mt][nt]);
+                        S[mt][nt] = mfma16(a[ks & 1][mt], Qf[nt][ks], S[mt][nt]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- softmax weights against the fixed per-head reference m
-            bf16x8 P[NT];
             bool over = false;
 #pragma unroll
             for (int nt = 0; nt < NT; nt++) {
@@ -612,30 +628,33 @@ __global__ __launch_bounds__(64 * (128 / HW)) void mla_decode_fast_kernel(const 
                 P[nt] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
             }
             if (__builtin_amdgcn_ballot_w64(over) && lane == 0) ovf = 1;
-            // ---- latent sum U^T += C^T . P^T (transposing reads of the same tile)
-            s16x4 lo[PV + 1], hi[PV + 1];   // ring of operands, PV column tiles ahead
+        } else {
 #pragma unroll
-            for (int i = 0; i < PV; i++) {
-                lo[i] = lds_read_tr(to.value(C, i, 0));
-                hi[i] = lds_read_tr(to.value(C, i, 1));
-            }
+            for (int nt = 0; nt < NT; nt++) P[nt] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        }
 #pragma unroll
-            for (int mc = 0; mc < MC; mc++) {
-                if (mc + PV < MC) {
-                    lo[(mc + PV) % (PV + 1)] = lds_read_tr(to.value(C, mc + PV, 0));
-                    hi[(mc + PV) % (PV + 1)] = lds_read_tr(to.value(C, mc + PV, 1));
-                }
-                const bf16x8 av = cat_tr(lo[mc % (PV + 1)], hi[mc % (PV + 1)]);
+        for (int nt = 0; nt < NT; nt++) Pb[NT * wave + nt][lane] = P[nt];
+        __syncthreads();                     // P of every head visible
+        // ---- latent sum U^T += C^T . P^T over this wavefront's columns: the
+        // A operands of all its column tiles, then one head tile of P at a time
+        bf16x8 av[VMC];
 #pragma unroll
-                for (int nt = 0; nt < NT; nt++) U[mc][nt] = mfma16(av, P[nt], U[mc][nt]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int mc = 0; mc < VMC; mc++)
+            av[mc] = cat_tr(lds_read_tr(to.value(C + cseg, mc, 0)), lds_read_tr(to.value(C + cseg, mc, 1)));
+        bf16x8 Pt[2];
+        Pt[0] = Pb[0][lane];
+#pragma unroll
+        for (int t = 0; t < VNT; t++) {
+            if (t + 1 < VNT) Pt[(t + 1) & 1] = Pb[t + 1][lane];
+#pragma unroll
+            for (int mc = 0; mc < VMC; mc++) U[mc][t] = mfma16(av[mc], Pt[t & 1], U[mc][t]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         cc.lt++;
         buf = (buf + 1) % kNBuf;
       }
       if (g < gend) break;                   // left early: flagged for the rescaling kernel
-      if (active) write_partial(cc.b);
+      write_partial(cc.b);
       if (g >= g1) break;
       // the next sequence: its tile cursor, accumulators and q^
       cc.lt--;
@@ -1020,10 +1039,10 @@ hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
     if (e != hipSuccess) return e;
     const unsigned g2 = (unsigned)p.n_wg;
     if (paged) {
-        hipLaunchKernelGGL((mla_decode_fast_kernel<32, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+        hipLaunchKernelGGL((mla_decode_fast_kernel<true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
         hipLaunchKernelGGL((mla_decode_safe_kernel<true>), dim3(g2), dim3(512), 0, st, p, p.bt, p.s, p.sched);
     } else {
-        hipLaunchKernelGGL((mla_decode_fast_kernel<32, false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+        hipLaunchKernelGGL((mla_decode_fast_kernel<false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
         hipLaunchKernelGGL((mla_decode_safe_kernel<false>), dim3(g2), dim3(512), 0, st, p, p.bt, p.s, p.sched);
     }
     e = hipGetLastError();

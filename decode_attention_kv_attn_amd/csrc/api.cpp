@@ -2,6 +2,7 @@
 // the split plan, workspace carving and kernel launches.  No allocation, no
 // global state except the thread-local error message.
 #include "attn_decode.h"
+#include "attn_stream_probe.h"
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -51,7 +52,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // head, group of HG query heads, token split), HG the largest of 8, 4, 2, 1
 // dividing g, one wavefront each, about 2048 of them (8 per CU).
 // Either way no split is longer than 4096 tokens (with mixed lengths the
-// longest sequences would otherwise set the kernel time) or shorter than 256
+// longest sequences would otherwise set the kernel time) or shorter than 512
 // tokens, and split lengths are multiples of 64 tokens.
 struct GqaPlan {
     bool mfma;
@@ -78,7 +79,7 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h)
         P.NW = 1;
         target = 2048;
     }
-    const long long T = 64, min_chunk = 256, max_chunk = 4096;
+    const long long T = 64, min_chunk = 512, max_chunk = 4096;
     const long long units = (long long)B * h_kv * P.n_hg;
     long long ns = units > 0 ? cdiv(target, units) : 1;
     if (s_max > 0 && ns < cdiv(s_max, max_chunk)) ns = cdiv(s_max, max_chunk);
@@ -326,6 +327,16 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     if (e == hipErrorNotSupported) return fail(ATTN_ENOTSUP, "MLA kernels not built");
     if (e != hipSuccess) return hip_fail(e, "attn_decode_mla_absorbed launch");
     return ATTN_OK;
+}
+
+int attn_stream_read_probe(const void* src, size_t bytes, unsigned int* sink, void* stream)
+{
+    if (!src || !sink) return fail(ATTN_EINVAL, "null src or sink");
+    const size_t unit = (size_t)attn::kProbeGrid * 16384;
+    if (bytes == 0 || bytes % unit != 0)
+        return fail(ATTN_EINVAL, "bytes must be a positive multiple of %zu", unit);
+    const hipError_t e = attn::launch_stream_probe(src, bytes, sink, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "stream probe launch");
 }
 
 }  // extern "C"

@@ -66,4 +66,9 @@ struct MlaParams {
 
 hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st);
 
+// read-bandwidth probe: kProbeGrid workgroups, bytes / kProbeGrid each (a
+// multiple of 16 KB)
+constexpr unsigned kProbeGrid = 2048;
+hipError_t launch_stream_probe(const void* src, size_t bytes, unsigned* sink, hipStream_t st);
+
 }  // namespace attn

@@ -1,5 +1,5 @@
 """CPU-side checks of the C ABI: the library loads, exports every entry
-point include/attn_decode.h declares, and its host-only helpers and argument
+point the headers in include/ declare, and its host-only helpers and argument
 checks behave (no kernel is launched here)."""
 import ctypes as C
 import json
@@ -11,14 +11,17 @@ import pytest
 import decode_attention_kv_attn_amd as A
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "cell_sizes.json")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_three_entry_points_and_helpers():
@@ -123,3 +126,12 @@ def test_append_argument_errors():
     assert A.kv_cache_append(**kw) == A.ATTN_EINVAL
     kw.update(b=2, s_max=0)
     assert A.kv_cache_append(**kw) == A.ATTN_EINVAL
+
+
+def test_stream_probe_rejects_bad_arguments():
+    unit = 2048 * 16384
+    assert A.attn_stream_read_probe(None, unit, FAKE, stream=0, check=False) == A.ATTN_EINVAL
+    assert A.attn_stream_read_probe(FAKE, unit, None, stream=0, check=False) == A.ATTN_EINVAL
+    assert A.attn_stream_read_probe(FAKE, 0, FAKE, stream=0, check=False) == A.ATTN_EINVAL
+    assert A.attn_stream_read_probe(FAKE, unit + 16, FAKE, stream=0, check=False) == A.ATTN_EINVAL
+    assert "multiple" in A.attn_last_error()

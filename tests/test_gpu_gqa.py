@@ -72,6 +72,12 @@ def test_split_kv_long_context_small_batch():
     run_small(1, 8, 2, 64, (5000,), 4, seed=11)
 
 
+def test_split_kv_more_than_256_splits():
+    # one KV head over 140,000 tokens: about 270 splits of 512 tokens, merged
+    # by the 16-wavefront form of the merge kernel
+    run_small(1, 16, 1, 128, (140000,), 2, seed=12)
+
+
 @pytest.mark.parametrize("b", [2, 4])
 def test_paged_shuffled_table(b):
     run_small(4, 8, 2, 64, (1, 16, 17, 500), b, seed=12, paged=True)

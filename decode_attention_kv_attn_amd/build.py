@@ -19,6 +19,13 @@ HIP_FLAGS = [
     "-ffp-contract=fast", "-munsafe-fp-atomics", "-Wall",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
+# Per-source extra flags.  The GQA matrix-core kernel keeps its accumulators
+# in ordinary VGPRs (VGPR form of the MFMA instructions): with the default
+# heuristic the compiler places them in AGPRs and copies them to VGPRs and
+# back around the softmax rescale on every tile.
+FILE_FLAGS = {
+    "gqa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def build(verbose: bool = False) -> str:
@@ -30,7 +37,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

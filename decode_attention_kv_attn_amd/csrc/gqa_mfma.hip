@@ -224,20 +224,26 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         const uint8_t* Kt = Ls + buf * 2 * C::KT;
         const uint8_t* Vt = Kt + C::KT;
         if (active) {
-            // ---- scores S^T = K . q^T, operands read one K step ahead
-            f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            bf16x8 a[2][2];
-            a[0][0] = lds_read_16_as_2x8(Kt + to.sc[0]);
-            a[0][1] = lds_read_16_as_2x8(Kt + to.sc[0] + 16 * C::RB);
+            // every operand of the tile is read from LDS up front: the K
+            // operands of the score product, then the V operands of the value
+            // product (which do not depend on P, so their latency hides
+            // behind the score products and the softmax)
+            bf16x8 ka[C::KS][2];
 #pragma unroll
             for (int ks = 0; ks < C::KS; ks++) {
-                if (ks + 1 < C::KS) {
-                    a[(ks + 1) & 1][0] = lds_read_16_as_2x8(Kt + to.sc[ks + 1]);
-                    a[(ks + 1) & 1][1] = lds_read_16_as_2x8(Kt + to.sc[ks + 1] + 16 * C::RB);
-                }
-                S[0] = mfma16(a[ks & 1][0], Qf[ks], S[0]);
-                S[1] = mfma16(a[ks & 1][1], Qf[ks], S[1]);
-                __builtin_amdgcn_sched_barrier(0);
+                ka[ks][0] = lds_read_16_as_2x8(Kt + to.sc[ks]);
+                ka[ks][1] = lds_read_16_as_2x8(Kt + to.sc[ks] + 16 * C::RB);
+            }
+            bf16x8 va[C::MC];
+#pragma unroll
+            for (int mc = 0; mc < C::MC; mc++)
+                va[mc] = cat_tr(lds_read_tr(Vt + to.tr[mc]), lds_read_tr(Vt + to.tr[mc] + 16 * C::RB));
+            // ---- scores S^T = K . q^T
+            f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ks++) {
+                S[0] = mfma16(ka[ks][0], Qf[ks], S[0]);
+                S[1] = mfma16(ka[ks][1], Qf[ks], S[1]);
             }
             // ---- online softmax: lane holds head li, tokens 16 mt + 4G + e
             float z[2][4];
@@ -273,19 +279,9 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                 for (int mc = 0; mc < C::MC; mc++) O[mc] *= alpha;
             }
             const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            // ---- O^T += V^T . P^T (transposing reads of the V tile)
-            s16x4 lo[2], hi[2];
-            lo[0] = lds_read_tr(Vt + to.tr[0]);
-            hi[0] = lds_read_tr(Vt + to.tr[0] + 16 * C::RB);
+            // ---- O^T += V^T . P^T
 #pragma unroll
-            for (int mc = 0; mc < C::MC; mc++) {
-                if (mc + 1 < C::MC) {
-                    lo[(mc + 1) & 1] = lds_read_tr(Vt + to.tr[mc + 1]);
-                    hi[(mc + 1) & 1] = lds_read_tr(Vt + to.tr[mc + 1] + 16 * C::RB);
-                }
-                O[mc] = mfma16(cat_tr(lo[mc & 1], hi[mc & 1]), P, O[mc]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int mc = 0; mc < C::MC; mc++) O[mc] = mfma16(va[mc], P, O[mc]);
         }
         buf = (buf + 1) % C::NBUF;
     }

@@ -122,7 +122,7 @@ MlaPlan plan_mla(int B, int h, int d_c, int d_R)
     P.n_wg = 256;
     P.min_tiles = 8;
     const size_t slots = (size_t)P.n_wg + B - 1;
-    P.qhat_bytes = align256((size_t)B * h * (d_c + d_R) * 2);
+    P.qhat_bytes = align256((size_t)B * ((h + 31) / 32) * 32 * (d_c + d_R) * 2);
     P.part_u_bytes = align256(slots * h * d_c * sizeof(float));
     P.part_ml_bytes = align256(slots * h * 2 * sizeof(float));
     P.flag_bytes = align256((size_t)P.n_wg * sizeof(int32_t));

@@ -7,9 +7,10 @@
 // multi-head KV cache" (charlestar.github.io), "First matrix absorption" /
 // "Second matrix absorption":
 //   1. mla_absorb_kernel    q^[b,i] = [bf16(W_UK[i]^T q_nope[b,i]) | q_rope[b,i]]
-//   2. mla_decode_kernel    per (b, token split), all heads at once:
+//   2. mla_decode_kernel    per run of 32-token tiles, all heads at once:
 //                           S = q^ C^T over the cached rows [c | k_R],
-//                           online softmax, u~ += P c  (same LDS tile)
+//                           softmax against a per-head reference max,
+//                           u~ += P c  (same LDS tile)
 //   3. mla_finish_kernel    merge the splits through their lse -> u~ (fp32),
 //                           then out[b,i] = W_UV[i] u~[b,i]
 // All h heads share every latent row, so the score [h x 576]x[576 x n] and
@@ -36,6 +37,21 @@ struct SchedArgs {
     int B, s_max, n_wg, min_tiles;
 };
 __device__ __forceinline__ void mla_schedule(SchedArgs p, int tid, int nthr, int* sc);
+
+// q^ is stored in the order the decode kernel reads it as the B operand of
+// its score product: wavefront g (heads 32 g .. 32 g + 31), K step ks (16
+// dims), lane l (head 32 g + l % 32, dims 16 ks + 8 (l / 32) .. + 7) own
+// the 16 bytes at ((b NG + g) 36 + ks) 64 + l, NG = ceil(h / 32).  Each
+// 64-lane load is then one contiguous kilobyte; in the row-major
+// [B, h, 576] order every load touched 32 rows and each 128-byte line was
+// fetched four times.  Returns the bf16 index of dims d .. d + 7 (d a
+// multiple of 8) of head i of sequence b.
+__device__ __forceinline__ size_t qhat_index(int b, int i, int d, int h)
+{
+    const int ng = (h + 31) / 32;
+    const int lane = i % 32 + 32 * ((d / 8) % 2);
+    return ((((size_t)b * ng + i / 32) * 36 + d / 16) * 64 + lane) * 8;
+}
 
 constexpr int kAbsCols = 128;
 constexpr int kAbsRowStride = kAbsCols * 2 + 16;
@@ -79,7 +95,6 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
     const int nq = p.d_c / kAbsCols;
     const int i = blockIdx.x / nq, cq = blockIdx.x % nq;
     const int c0 = cq * kAbsCols;
-    const int W = p.d_c + p.d_R;
     const uint16_t* __restrict__ wuk = (const uint16_t*)p.w_uk + (size_t)i * p.d_nope * p.d_c;
     const uint16_t* __restrict__ qn = (const uint16_t*)p.q_nope;
     const int ksteps = p.d_nope / 32;
@@ -121,7 +136,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 #pragma unroll
             for (int u = 0; u < 4; u++) {
                 const int idx = min(base + u * 256 + tid, nv - 1);   // duplicates rewrite the same value
-                *(u32x4v*)(p.qhat + ((size_t)(idx / per) * p.h + i) * W + p.d_c + 8 * (idx % per)) = v[u];
+                *(u32x4v*)(p.qhat + qhat_index(idx / per, i, p.d_c + 8 * (idx % per), p.h)) = v[u];
             }
         }
     }
@@ -157,7 +172,7 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
             const int r = lane / 4, sg = lane % 4;   // row of the block, 16-byte segment
             const u32x4v v = *(const u32x4v*)&ost[wave][r][8 * sg];
             if (b0 + r < p.B)
-                *(u32x4v*)(p.qhat + ((size_t)(b0 + r) * p.h + i) * W + c0 + 32 * wave + 8 * sg) = v;
+                *(u32x4v*)(p.qhat + qhat_index(b0 + r, i, c0 + 32 * wave + 8 * sg, p.h)) = v;
         }
         __syncthreads();
         a = an;
@@ -168,40 +183,38 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 // 2. decode.  Workgroup = a run of tiles with all heads, so every latent
 //    tile is fetched once.  Tiles of 32 rows move HBM -> LDS by LDS-DMA
 //    (buffer_load ... lds, no staging registers) into a ring of 4 buffers,
-//    three tiles ahead of use.
-//    Fast kernel, 4 wavefronts (one per SIMD, accumulators in AGPRs):
-//      scores   wavefront w, heads 32w .. 32w+31, per 16-head block:
-//               S^T[32 tok x 16 heads] = C_tile[32 x 576] . q^T  (A: LDS, B: q^ in registers),
-//               softmax weights P on S^T (lane = head, 8 tokens per lane);
+//    three tiles ahead of use.  4 wavefronts (one per SIMD; the latent-sum
+//    accumulators fill the 256 AGPRs of each):
+//      scores   wavefront w, heads 32w .. 32w+31:
+//               S^T[32 tok x 32 heads] = C_tile[32 x 576] . q^T
+//               (v_mfma_f32_32x32x16_bf16, A: LDS, B: q^ in registers);
+//      softmax  lane = head, 16 tokens per lane; P rounded to bf16;
 //      exchange P of all heads through LDS (8 KB per tile);
 //      latent   wavefront w, latent columns 128w .. 128w+127, all heads:
 //               U^T[128 x 128] += C_tile^T[128 x 32] . P^T[32 x 128]
 //               (A: transposing LDS reads of a quarter of the tile, B: P).
-//    Splitting the latent sum by columns instead of heads means each latent
-//    byte is read from LDS by one wavefront there instead of four; with the
-//    score reads this cuts the LDS traffic per tile from 288 KB to 208 KB,
-//    and LDS bandwidth (about 100 B/clock per CU for these patterns, as
-//    measured) is what bounds this loop alongside the matrix cores.
-//    The fallback kernel uses 8 wavefronts x 16 heads for both products.
-//    The token order of the value product's K axis is the score product's
-//    output layout (lane group G holds tokens 4G..4G+3 and 16+4G..16+4G+3),
-//    so P keeps the layout it was computed in.
+//    The 32 x 32 x 16 products halve the instruction count of the 16 x 16 x
+//    32 ones for the same work, and a wavefront's 16 score registers then
+//    cost as much as its 16 heads x 32 tokens did before.  The score chain
+//    keeps its accumulator in VGPRs (the AGPRs hold U), which the compiler's
+//    MFMA forms cannot express, so it is issued as inline assembly with the
+//    wait states the hardware requires around it.
+//    The value product's K order is the score product's output order: lane
+//    half hh of head j holds tokens 8g + 4hh + e (g < 4, e < 4); K step kk
+//    takes g = 2kk, 2kk + 1, so P keeps the layout it was computed in, and
+//    the transposing reads of C fetch those two groups of 4 rows.
 //
 //    LDS tile layout (one buffer, 36 KB): 9 segments of 128 bytes per row,
 //    segment-major: byte (s * 4096 + r * 128 + 16 * p) holds row r, 16-byte
 //    chunk 8 s + (p ^ swz(r)).  One DMA instruction fills 8 rows of one
-//    segment (1 KB, lane-contiguous as the hardware writes it; each group of 8
-//    lanes still reads one 128-byte line).  The XOR swizzle spreads the rows
-//    of an operand over the banks; score operands are read as two 8-byte
-//    halves, which measured ~1.6x faster than one 16-byte read per lane for
-//    this scattered-row pattern.
+//    segment (1 KB, lane-contiguous as the hardware writes it).  The XOR
+//    swizzle spreads the rows of an operand over the banks.
 //
 //    Completion of the LDS-DMA is tracked with explicit vmcnt waits, so no
 //    other vector-memory instruction may be outstanding inside the tile loop
 //    (a compiler-inserted vmcnt(0) for it would also drain the prefetched
 //    tiles): q^ is loaded and waited for before the loop, and the loop keeps
-//    its state in registers (no spills).  LDS operands are read one K step
-//    ahead of the matrix instructions that use them.
+//    its state in registers (no spills).
 // ---------------------------------------------------------------------------
 constexpr int kT = 32;             // tokens per tile
 constexpr int kRow = 576 * 2;      // bytes per cached latent row
@@ -211,49 +224,73 @@ constexpr int kSlots = kTile / 1024;   // 36 DMA instructions per tile
 
 // XOR swizzle of the 16-byte chunk position within a 128-byte row segment:
 // s(r) = r0 ^ 2 r1 ^ 5 r2 ^ 7 r3 (r_k the bits of r).  Any 8 consecutive
-// rows get distinct positions; among the XOR-linear choices with that
-// property this one measured fastest for the mix of score-operand and
-// transposing reads below (within a few percent of the others).
+// rows get distinct positions.
 __device__ __forceinline__ int swz(int r)
 {
     return (r & 1) ^ (r & 2) ^ ((r & 4) ? 5 : 0) ^ ((r & 8) ? 7 : 0);
 }
-__device__ __forceinline__ int tile_off(int r, int c)   // row r, logical 16-byte chunk c
-{
-    return (c >> 3) * 4096 + r * 128 + (((c & 7) ^ swz(r)) << 4);
-}
 
 // Per-lane byte offsets of the MFMA operands within a tile buffer, split so
-// that everything depending on the K step is a compile-time constant (the
-// immediate offset of the LDS instruction):
-//   score operand, K step ks, row block mt: row 16 mt + li, chunk 4 ks + G
-//     = (ks >> 1) * 4096 + mt * 2048 + [li * 128 + ((4 (ks & 1) + G) ^ s) * 16]
-//   value operand, column tile mc, token half th: rows 4G + li/4 + 16 th,
-//     chunk 2 mc + (li % 4) / 2, byte 8 (li % 2) within it
-//     = (mc >> 2) * 4096 + th * 2048 + [row * 128 + ((2 (mc & 3) + cp) ^ s) * 16 + 8 (li % 2)]
-// (s = swz(row) is the same for row and row + 16).
+// that everything depending on the K step or the column tile is a
+// compile-time constant (the immediate offset of the LDS instruction).
+//   score operand, K step ks: row l % 32, chunk 2 ks + hh (hh = l / 32)
+//     = (ks >> 2) * 4096 + [r * 128 + ((2 (ks & 3) + hh) ^ swz(r)) * 16]
+//   value operand of wavefront w, column tile mc, K step kk, read t (rows
+//     16 kk + 8 t + 4 hh + i / 4 of 16-lane group q, i = l % 16, hh = q / 2):
+//     column 128 w + 32 mc + 16 (q % 2) + 4 (i % 4), i.e. chunk
+//     16 w + 4 mc + 2 (q % 2) + (i % 4) / 2, byte 8 (i % 2) within it
+//     = (2 w + mc / 2) * 4096 + kk * 2048 + [row * 128 + ((4 (mc & 1) + ...) ^ swz(row)) * 16 + 8 (i % 2)]
 struct TileOffsets {
-    int sc[2];   // score, by K-step parity
-    int tr[4];   // value, by mc % 4
-    __device__ __forceinline__ TileOffsets(int li, int G)
+    int sc[4];      // score, by ks & 3
+    int tr[2][2];   // value, by (mc & 1, t)
+    __device__ __forceinline__ TileOffsets(int lane)
     {
-        const int ss = swz(li);
-        sc[0] = li * 128 + ((G ^ ss) << 4);
-        sc[1] = li * 128 + (((4 + G) ^ ss) << 4);
-        const int r = 4 * G + li / 4, cp = (li % 4) / 2, st = swz(r);
+        const int r = lane % 32, hh = lane / 32, s = swz(r);
 #pragma unroll
-        for (int j = 0; j < 4; j++) tr[j] = r * 128 + (((2 * j + cp) ^ st) << 4) + 8 * (li % 2);
+        for (int j = 0; j < 4; j++) sc[j] = r * 128 + (((2 * j + hh) ^ s) << 4);
+        const int q = lane / 16, i = lane % 16;
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int row = 8 * t + 4 * (q / 2) + i / 4, st = swz(row);
+#pragma unroll
+            for (int m1 = 0; m1 < 2; m1++)
+                tr[m1][t] = row * 128 + (((4 * m1 + 2 * (q % 2) + (i % 4) / 2) ^ st) << 4) + 8 * (i % 2);
+        }
     }
-    __device__ __forceinline__ const uint8_t* score(const uint8_t* C, int ks, int mt) const
+    __device__ __forceinline__ const uint8_t* score(const uint8_t* C, int ks) const
     {
-        return C + sc[ks & 1] + (ks >> 1) * 4096 + mt * 2048;
+        return C + sc[ks & 3] + (ks >> 2) * 4096;
     }
-    __device__ __forceinline__ const uint8_t* value(const uint8_t* C, int mc, int th) const
+    __device__ __forceinline__ const uint8_t* value(const uint8_t* C, int w, int mc, int kk, int t) const
     {
-        return C + tr[mc & 3] + (mc >> 2) * 4096 + th * 2048;
+        return C + tr[mc & 1][t] + (2 * w + (mc >> 1)) * 4096 + kk * 2048;
     }
 };
 
+// Score products with the accumulator in VGPRs.  Each instruction is
+// preceded by two wait states (a VALU write of an operand register needs
+// them before a matrix instruction reads it), and the last one of a chain is
+// followed by 20, more than an 8-pass XDL result needs before a VALU reads
+// it.  Back-to-back accumulation into the same registers needs none.
+__device__ __forceinline__ f32x16 mfma32_first(bf16x8 a, bf16x8 b)
+{
+    f32x16 d;
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ void mfma32_acc(f32x16& d, bf16x8 a, bf16x8 b)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_last(f32x16& d, bf16x8 a, bf16x8 b)
+{
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // Variable-length tile schedule.  The cached tiles of all sequences are laid
@@ -438,21 +475,28 @@ struct TileDma {
 };
 
 template <bool PAGED>
-__global__ __launch_bounds__(256) void mla_decode_fast_kernel(const MlaParams p,
-                                                              const int32_t* __restrict__ btab,
-                                                              const int32_t* __restrict__ slen,
-                                                              const int32_t* __restrict__ sched)
+__global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
+                                                         const int32_t* __restrict__ btab,
+                                                         const int32_t* __restrict__ slen,
+                                                         const int32_t* __restrict__ sched)
 {
     constexpr int NW = 4;           // wavefronts per workgroup
-    constexpr int NT = 8 / NW;      // score head tiles per wavefront (32 heads)
-    constexpr int KS = 576 / 32;    // score K steps
-    constexpr int VMC = 512 / NW / 16;   // latent column tiles per wavefront
-    constexpr int VNT = 128 / 16;   // head tiles of the latent sum (all heads; zeros past h)
+    constexpr int KS = 576 / 16;    // score K steps
+#ifndef MLA_PD
+#define MLA_PD 6
+#endif
+    constexpr int PD = MLA_PD;      // score operands read ahead of their product
+#ifndef MLA_SCH
+#define MLA_SCH 2
+#endif
+    constexpr int SCH = MLA_SCH;    // score accumulation chains
+    constexpr int MCW = 4;          // 32-column tiles of the latent sum per wavefront
+    constexpr int NTH = 4;          // 32-head tiles of the latent sum (all heads; zeros past h)
     __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * kTile];
-    __shared__ __attribute__((aligned(16))) bf16x8 Pb[VNT][64];   // P of every head tile, B-operand layout
+    __shared__ __attribute__((aligned(16))) bf16x8 Pb[NTH][2][64];   // P of every head tile, B-operand layout
     __shared__ int ovf;   // some head's scores ran past its reference max + 64
 
-    const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
+    const int tid = threadIdx.x, lane = tid % 64, hh = lane / 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int w = xcd_major(blockIdx.x, gridDim.x);
     const SchedView sv{slen, sched, p.s_max, p.B, p.n_wg};
@@ -464,69 +508,67 @@ __global__ __launch_bounds__(256) void mla_decode_fast_kernel(const MlaParams p,
         if (tid == 0) p.flags[w] = 0;
         return;
     }
-    const int head0 = wave * 16 * NT;
-    const bool active = head0 < p.h;   // this wavefront has score heads
+    const int hs = 32 * wave + lane % 32;   // this lane's score head
+    const bool hv = hs < p.h;
 
     const TileDma<NW, PAGED> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
                                  wave, lane);
     TileWalk ic(sv, sv.first_seq(w), g0, g1);   // issue cursor
     TileWalk cc = ic;                            // compute cursor
 
-    // q^ fragments of one sequence: B operand of the score product (head
-    // tiles past h read as zeros)
-    bf16x8 Qf[NT][KS];
+    // q^ fragments of one sequence: B operand of the score product (heads
+    // past h read as zeros)
+    bf16x8 Qf[KS];
     auto load_q = [&](int b) {
+        const uint16_t* qrow = p.qhat + qhat_index(b, min(hs, p.h - 1), 8 * hh, p.h);
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++)
-#pragma unroll
-            for (int ks = 0; ks < KS; ks++)
-                Qf[nt][ks] = head0 + 16 * nt < p.h
-                    ? *(const bf16x8*)(p.qhat + ((size_t)b * p.h + head0 + 16 * nt + li) * 576 + ks * 32 + 8 * G)
-                    : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        for (int ks = 0; ks < KS; ks++)
+            Qf[ks] = hv ? *(const bf16x8*)(qrow + 64 * 8 * ks) : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     };
 
-    // Per head and sequence: m is fixed at the first tile's max (log2 units)
-    // and U, lsum accumulate 2^(z - m).  Later tiles may exceed m by up to 64
-    // (p <= 2^64, far from fp32/bf16 overflow); past that the workgroup is
-    // handed to the rescaling kernel (flag), which real logits essentially
-    // never need.  m and lsum belong to this wavefront's score heads, U to
-    // its latent columns (all heads).
-    f32x4 U[VMC][VNT];
-    float m[NT], lsum[NT];
+    // Per head and sequence: m is the reference max (log2 units), fixed at
+    // the first tile, and U, lsum accumulate 2^(z - m).  A later tile may
+    // exceed m by up to 64 (p <= 2^64 stays far from fp32/bf16 overflow);
+    // rescaling the AGPR-resident U in place would cost the loop its
+    // register allocation, so past that the workgroup stops and flags
+    // itself, and the merge kernel recomputes its partials exactly (real
+    // logits essentially never get there).  m and lsum belong to this
+    // lane's score head, U to the wavefront's latent columns (all heads).
+    f32x16 U[MCW][NTH];
+    float m, lsum;
     auto reset = [&]() {
+        m = -INFINITY;
+        lsum = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            m[nt] = -INFINITY;
-            lsum[nt] = 0.f;
-        }
+        for (int mc = 0; mc < MCW; mc++)
 #pragma unroll
-        for (int mc = 0; mc < VMC; mc++)
+            for (int nt = 0; nt < NTH; nt++)
 #pragma unroll
-            for (int t = 0; t < VNT; t++) U[mc][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int v = 0; v < 16; v++) U[mc][nt][v] = 0.f;
     };
     // partial state of sequence b, slot w + b: (m, l) of the score heads and
     // the U^T columns 128 wave .. + 127 of every head
+    // The U columns go out as fp32 straight from the accumulation registers
+    // (any vector arithmetic on them here would cost the tile loop its
+    // register allocation).
     auto write_partial = [&](int b) {
-#pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-            if (head0 + 16 * nt >= p.h) continue;
-            float l = lsum[nt];
-            l += xor16(l);
-            l += xor32(l);
-            const size_t row = (size_t)(w + b) * p.h + head0 + 16 * nt + li;
-            if (G == 0) {
-                p.part_ml[row * 2] = m[nt];
-                p.part_ml[row * 2 + 1] = l;
-            }
+        const float l = lsum + xor32(lsum);
+        if (hh == 0 && hv) {
+            const size_t row = (size_t)(w + b) * p.h + hs;
+            p.part_ml[row * 2] = m;
+            p.part_ml[row * 2 + 1] = l;
         }
 #pragma unroll
-        for (int t = 0; t < VNT; t++) {
-            if (16 * t >= p.h) continue;
-            const size_t row = (size_t)(w + b) * p.h + 16 * t + li;
-            float* pu = p.part_u + row * 512 + (512 / NW) * wave + 4 * G;
+        for (int nt = 0; nt < NTH; nt++) {
+            const int head = 32 * nt + lane % 32;
+            if (head >= p.h) continue;
+            float* pu = p.part_u + ((size_t)(w + b) * p.h + head) * 512 + 128 * wave + 4 * hh;
 #pragma unroll
-            for (int mc = 0; mc < VMC; mc++)
-                *(float4*)(pu + 16 * mc) = make_float4(U[mc][t][0], U[mc][t][1], U[mc][t][2], U[mc][t][3]);
+            for (int mc = 0; mc < MCW; mc++)
+#pragma unroll
+                for (int g = 0; g < 4; g++)
+                    *(float4*)(pu + 32 * mc + 8 * g) = make_float4(U[mc][nt][4 * g], U[mc][nt][4 * g + 1],
+                                                                   U[mc][nt][4 * g + 2], U[mc][nt][4 * g + 3]);
         }
     };
     reset();
@@ -551,8 +593,8 @@ __global__ __launch_bounds__(256) void mla_decode_fast_kernel(const MlaParams p,
         ic.next(sv);
     }
 
-    const TileOffsets to(li, G);
-    const int cseg = 2 * wave * 4096;   // this wavefront's latent columns: segments 2w, 2w + 1
+    const TileOffsets to(lane);
+    const float sc = p.scale_log2;
     int buf = 0;
     int g = g0;
     for (;;) {   // one sequence (or the part of it in this workgroup's range) per pass
@@ -562,98 +604,81 @@ __global__ __launch_bounds__(256) void mla_decode_fast_kernel(const MlaParams p,
         dma.rows(ic, nx0, nx1);
         dma.wait_tile();
         __syncthreads();
-        if (ovf) break;                      // uniform across the workgroup
-        // refill the buffer read in the previous iteration (every wavefront is
-        // past it), so that three tiles stay in flight while this one is used
+        // every wavefront is past the previous tile: its buffer can be
+        // refilled, so that three tiles stay in flight
         dma.issue(ic, (buf + 3) % kNBuf, nx0, nx1);
         ic.next(sv);
+        const int flagged = ovf;   // set during an earlier tile; acted on at the end of this one
         const uint8_t* C = Cs + buf * kTile;
         const int tbase = cc.lt * kT;
-        bf16x8 P[NT];
-        if (active) {
-            // ---- scores S^T = C . q^T, operands read one K step ahead
-            f32x4 S[2][NT];
+
+        // ---- scores S^T = C . q^T: SCH interleaved accumulation chains (one
+        // chain would wait out each product's latency), operands PD steps ahead
+        bf16x8 a[PD];
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++)
+        for (int ks = 0; ks < PD; ks++) a[ks] = *(const bf16x8*)to.score(C, ks);
+        f32x16 Sc[SCH];
 #pragma unroll
-                for (int nt = 0; nt < NT; nt++) S[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 a[2][2];
-            a[0][0] = lds_read_16_as_2x8(to.score(C, 0, 0));
-            a[0][1] = lds_read_16_as_2x8(to.score(C, 0, 1));
+        for (int ks = 0; ks < KS; ks++) {
+            const int c = ks % SCH;
+            if (ks < SCH) Sc[c] = mfma32_first(a[ks % PD], Qf[ks]);
+            else if (ks + SCH < KS) mfma32_acc(Sc[c], a[ks % PD], Qf[ks]);
+            else mfma32_last(Sc[c], a[ks % PD], Qf[ks]);
+            if (ks + PD < KS) a[ks % PD] = *(const bf16x8*)to.score(C, ks + PD);
+        }
+        f32x16 S = Sc[0];
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                if (ks + 1 < KS) {
-                    a[(ks + 1) & 1][0] = lds_read_16_as_2x8(to.score(C, ks + 1, 0));
-                    a[(ks + 1) & 1][1] = lds_read_16_as_2x8(to.score(C, ks + 1, 1));
-                }
+        for (int c = 1; c < SCH; c++) S += Sc[c];
+        // the latent-sum operands of this tile do not depend on P: read them now
+        bf16x8 av[2][MCW];
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++)
+        for (int kk = 0; kk < 2; kk++)
 #pragma unroll
-                    for (int nt = 0; nt < NT; nt++)
-                        S[mt][nt] = mfma16(a[ks & 1][mt], Qf[nt][ks], S[mt][nt]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // ---- softmax weights against the fixed per-head reference m
-            bool over = false;
+            for (int mc = 0; mc < MCW; mc++)
+                av[kk][mc] = cat_tr(lds_read_tr(to.value(C, wave, mc, kk, 0)),
+                                    lds_read_tr(to.value(C, wave, mc, kk, 1)));
+
+        // ---- softmax weights: lane holds head hs, tokens 8 (v / 4) + 4 hh + v % 4
+        float lm = -INFINITY;
+        if (tbase + kT > cc.n) {   // the sequence's last tile: mask the rows past its length
 #pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-                float z[2][4];
-                float lm = -INFINITY;
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int tok = tbase + 16 * mt + 4 * G + e;
-                        z[mt][e] = tok < cc.n ? S[mt][nt][e] * p.scale_log2 : -INFINITY;
-                        lm = fmaxf(lm, z[mt][e]);
-                    }
-                if (m[nt] == -INFINITY) {       // first tile of the sequence: fix the reference
-                    lm = fmaxf(lm, xor16(lm));
-                    lm = fmaxf(lm, xor32(lm));
-                    m[nt] = lm;
-                }
-                over |= lm > m[nt] + 64.f;
-                uint32_t pk[4];
-                float ps = 0.f;
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                    for (int e = 0; e < 4; e += 2) {
-                        const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - m[nt]),
-                                                        __builtin_amdgcn_exp2f(z[mt][e + 1] - m[nt]));
-                        pk[mt * 2 + e / 2] = wv;
-                        ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
-                    }
-                lsum[nt] += ps;
-                P[nt] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            }
-            if (__builtin_amdgcn_ballot_w64(over) && lane == 0) ovf = 1;
-        } else {
-#pragma unroll
-            for (int nt = 0; nt < NT; nt++) P[nt] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+            for (int v = 0; v < 16; v++)
+                if (tbase + 8 * (v / 4) + 4 * hh + v % 4 >= cc.n) S[v] = -INFINITY;
         }
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) Pb[NT * wave + nt][lane] = P[nt];
-        __syncthreads();                     // P of every head visible
-        // ---- latent sum U^T += C^T . P^T over this wavefront's columns: the
-        // A operands of all its column tiles, then one head tile of P at a time
-        bf16x8 av[VMC];
+        for (int v = 0; v < 16; v++) lm = fmaxf(lm, S[v]);
+        lm = fmaxf(lm, xor32(lm)) * sc;
+        if (m == -INFINITY) m = lm;   // first tile of the sequence: fix the reference
+        if (__builtin_amdgcn_ballot_w64(lm > m + 64.f) && lane == 0) ovf = 1;
+        uint32_t pk[8];
+        float ps = 0.f;
 #pragma unroll
-        for (int mc = 0; mc < VMC; mc++)
-            av[mc] = cat_tr(lds_read_tr(to.value(C + cseg, mc, 0)), lds_read_tr(to.value(C + cseg, mc, 1)));
-        bf16x8 Pt[2];
-        Pt[0] = Pb[0][lane];
+        for (int v = 0; v < 16; v += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[v], sc, -m));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[v + 1], sc, -m));
+            ps += p0 + p1;
+            pk[v / 2] = pack_bf16x2(p0, p1);
+        }
+        lsum += ps;
+        Pb[wave][0][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        Pb[wave][1][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+        __syncthreads();   // P of every head visible
+        // ---- latent sum U^T += C^T . P^T over this wavefront's columns
 #pragma unroll
-        for (int t = 0; t < VNT; t++) {
-            if (t + 1 < VNT) Pt[(t + 1) & 1] = Pb[t + 1][lane];
+        for (int kk = 0; kk < 2; kk++) {
+            bf16x8 pb[NTH];
 #pragma unroll
-            for (int mc = 0; mc < VMC; mc++) U[mc][t] = mfma16(av[mc], Pt[t & 1], U[mc][t]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int nt = 0; nt < NTH; nt++) pb[nt] = Pb[nt][kk][lane];
+#pragma unroll
+            for (int nt = 0; nt < NTH; nt++)
+#pragma unroll
+                for (int mc = 0; mc < MCW; mc++) U[mc][nt] = mfma32(av[kk][mc], pb[nt], U[mc][nt]);
         }
         cc.lt++;
         buf = (buf + 1) % kNBuf;
+        if (flagged) break;   // workgroup-uniform
       }
-      if (g < gend) break;                   // left early: flagged for the rescaling kernel
+      if (g < gend) break;   // left early: flagged for the merge kernel
       write_partial(cc.b);
       if (g >= g1) break;
       // the next sequence: its tile cursor, accumulators and q^
@@ -669,180 +694,70 @@ __global__ __launch_bounds__(256) void mla_decode_fast_kernel(const MlaParams p,
     if (tid == 0) p.flags[w] = ovf;
 }
 
-// Fallback for a workgroup whose fast pass was flagged: the same tile range,
-// 8 wavefronts x 16 heads, with a lazily moving reference max and in-register
-// rescaling.  Unflagged workgroups return at once.
-template <bool PAGED>
-__global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
-                                                              const int32_t* __restrict__ btab,
-                                                              const int32_t* __restrict__ slen,
-                                                              const int32_t* __restrict__ sched)
+// The partial (m, l, U columns 8 lane .. 8 lane + 7) of head i over the
+// tokens of sequence bb in global tiles [g_lo, g_hi), computed from scratch
+// by one wavefront: the path for decode workgroups that stopped early.  An
+// online softmax in fp32 with the reference moved on every new maximum;
+// the dot products take the stored bf16 q^ and cache bits, lane l holding
+// latent dims 8 l .. 8 l + 7 and rotary dim l (d_c = 8 * 64, d_R = 64).
+// Tokens go 8 at a time so that their row loads are in flight together.
+__device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_lo, int g_hi, int s0,
+                                      int lane, float& M, float& L, float4& u0, float4& u1)
 {
-    constexpr int KS = 576 / 32;    // score K steps
-    constexpr int MC = 512 / 16;    // value M tiles (latent columns)
-    __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * kTile];
-
-    const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int w = xcd_major(blockIdx.x, gridDim.x);
-    if (__builtin_amdgcn_readfirstlane(p.flags[w]) == 0) return;   // the fast kernel finished it
-    const SchedView sv{slen, sched, p.s_max, p.B, p.n_wg};
-    const int total = sv.total();
-    const int tpw = sv.tpw(total);
-    const long long g0l = (long long)w * tpw;
-    const int g0 = (int)min(g0l, (long long)total), g1 = min(g0 + tpw, total);
-    if (g0 >= g1) return;
-    const int head0 = wave * 16;
-    const bool active = head0 < p.h;
-
-    const TileDma<8, PAGED> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
-                                wave, lane);
-    TileWalk ic(sv, sv.first_seq(w), g0, g1);
-    TileWalk cc = ic;
-
-    bf16x8 Qf[KS];
-    auto load_q = [&](int b) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-            Qf[ks] = active ? *(const bf16x8*)(p.qhat + ((size_t)b * p.h + head0 + li) * 576 + ks * 32 + 8 * G)
-                            : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    };
-    f32x4 U[MC];
-    float m, lsum;
-    auto reset = [&]() {
-        m = -INFINITY;
-        lsum = 0.f;
-#pragma unroll
-        for (int mc = 0; mc < MC; mc++) U[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    };
-    auto write_partial = [&](int b) {
-        float l = lsum;
-        l += xor16(l);
-        l += xor32(l);
-        const size_t row = (size_t)(w + b) * p.h + head0 + li;
-        float* pu = p.part_u + row * 512 + 4 * G;
-#pragma unroll
-        for (int mc = 0; mc < MC; mc++)
-            *(float4*)(pu + 16 * mc) = make_float4(U[mc][0], U[mc][1], U[mc][2], U[mc][3]);
-        if (G == 0) {
-            p.part_ml[row * 2] = m;
-            p.part_ml[row * 2 + 1] = l;
-        }
-    };
-    reset();
-
+    const int n = min(max(p.s[bb], 0), p.s_max);
+    const int t_lo = (g_lo - s0) * kT, t_hi = min((g_hi - s0) * kT, n);
+    const uint16_t* qc = p.qhat + qhat_index(bb, i, 8 * lane, p.h);
+    const uint16_t* qr = p.qhat + qhat_index(bb, i, 512 + 8 * (lane / 8), p.h) + lane % 8;
+    float q[9];
     {
-        size_t r0, r1;
-        dma.rows(ic, r0, r1);
-        dma.issue(ic, 0, r0, r1);
-        ic.next(sv);
-        dma.rows(ic, r0, r1);
-        dma.issue(ic, 1, r0, r1);
-        ic.next(sv);
-    }
-    load_q(cc.b);
-    vmem_drain();
-    {
-        size_t r0, r1;
-        dma.rows(ic, r0, r1);
-        dma.issue(ic, 2, r0, r1);
-        ic.next(sv);
-    }
-
-    const TileOffsets to(li, G);
-    int buf = 0;
-    for (int g = g0; g < g1; g++) {
-        size_t nx0, nx1;
-        dma.rows(ic, nx0, nx1);
-        dma.wait_tile();
-        __syncthreads();
-        dma.issue(ic, (buf + 3) % kNBuf, nx0, nx1);
-        ic.next(sv);
-        if (cc.lt == 0 && g != g0) {
-            load_q(cc.b);
-            vmem_drain();
+        const uint4 v = *(const uint4*)qc;
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            q[2 * e] = bf16lo_to_f32(w4[e]);
+            q[2 * e + 1] = bf16hi_to_f32(w4[e]);
         }
-        const uint8_t* C = Cs + buf * kTile;
-        const int tbase = cc.lt * kT;
-        if (active) {
-            // ---- scores S^T = C . q^T
-            f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            bf16x8 a[2][2];   // [K step parity][mt]
-            a[0][0] = lds_read_16_as_2x8(to.score(C, 0, 0));
-            a[0][1] = lds_read_16_as_2x8(to.score(C, 0, 1));
+        q[8] = bf16lo_to_f32(*qr);
+    }
+    const uint16_t* cache = (const uint16_t*)p.cache;
+    float m = -INFINITY, l = 0.f, u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t0 = t_lo; t0 < t_hi; t0 += 8) {
+        uint4 c8[8];
+        uint16_t cr[8];
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                if (ks + 1 < KS) {
-                    a[(ks + 1) & 1][0] = lds_read_16_as_2x8(to.score(C, ks + 1, 0));
-                    a[(ks + 1) & 1][1] = lds_read_16_as_2x8(to.score(C, ks + 1, 1));
-                }
+        for (int k = 0; k < 8; k++) {
+            const int t = min(t0 + k, t_hi - 1);
+            const size_t row = p.bt ? paged_row(p.bt, bb, t, p.max_blocks, p.bs_log2, p.num_blocks)
+                                    : (size_t)bb * p.s_max + t;
+            c8[k] = *(const uint4*)(cache + row * 576 + 8 * lane);
+            cr[k] = cache[row * 576 + 512 + lane];
+        }
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++) S[mt] = mfma16(a[ks & 1][mt], Qf[ks], S[mt]);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < 8; k++) {
+            if (t0 + k >= t_hi) break;   // wave-uniform
+            const uint32_t w4[4] = {c8[k].x, c8[k].y, c8[k].z, c8[k].w};
+            float c[8];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                c[2 * e] = bf16lo_to_f32(w4[e]);
+                c[2 * e + 1] = bf16hi_to_f32(w4[e]);
             }
-            // ---- online softmax: lane holds head (head0 + li), tokens 16 mt + 4G + e.
-            // The reference max m only moves when a tile's max exceeds it by
-            // more than 8 (log2 units); otherwise probabilities up to 2^8 are
-            // accumulated against the old m, which is exact after the final
-            // division and spares rescaling the 512-wide accumulators.
-            float z[2][4];
-            float lm = -INFINITY;
+            float z = q[8] * bf16lo_to_f32(cr[k]);
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++)
+            for (int e = 0; e < 8; e++) z = fmaf(q[e], c[e], z);
+            z = wave_sum(z) * p.scale_log2;
+            const float mn = fmaxf(m, z);
+            const float a = __builtin_amdgcn_exp2f(m - mn), pz = __builtin_amdgcn_exp2f(z - mn);
+            l = fmaf(l, a, pz);
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int tok = tbase + 16 * mt + 4 * G + e;
-                    z[mt][e] = tok < cc.n ? S[mt][e] * p.scale_log2 : -INFINITY;
-                    lm = fmaxf(lm, z[mt][e]);
-                }
-            lm = fmaxf(lm, xor16(lm));
-            lm = fmaxf(lm, xor32(lm));
-            const bool move = lm > m + 8.f;
-            const float mn = move ? lm : m;
-            const float alpha = move ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+            for (int e = 0; e < 8; e++) u[e] = fmaf(u[e], a, pz * c[e]);
             m = mn;
-            uint32_t pk[4];
-            float ps = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                for (int e = 0; e < 4; e += 2) {
-                    const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mn),
-                                                    __builtin_amdgcn_exp2f(z[mt][e + 1] - mn));
-                    pk[mt * 2 + e / 2] = wv;
-                    ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
-                }
-            lsum = lsum * alpha + ps;
-            const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            if (__builtin_amdgcn_ballot_w64(move)) {
-#pragma unroll
-                for (int mc = 0; mc < MC; mc++) {
-                    U[mc] *= alpha;
-                    __builtin_amdgcn_sched_barrier(0);   // a few accumulators at a time
-                }
-            }
-            // ---- latent sum U^T += C^T . P^T (transposing reads of the same tile)
-            s16x4 lo[2], hi[2];
-            lo[0] = lds_read_tr(to.value(C, 0, 0));
-            hi[0] = lds_read_tr(to.value(C, 0, 1));
-#pragma unroll
-            for (int mc = 0; mc < MC; mc++) {
-                if (mc + 1 < MC) {
-                    lo[(mc + 1) & 1] = lds_read_tr(to.value(C, mc + 1, 0));
-                    hi[(mc + 1) & 1] = lds_read_tr(to.value(C, mc + 1, 1));
-                }
-                U[mc] = mfma16(cat_tr(lo[mc & 1], hi[mc & 1]), P, U[mc]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
         }
-        if (g + 1 == g1 || cc.lt + 1 == cc.nt) {
-            if (active) write_partial(cc.b);
-            reset();
-        }
-        cc.next(sv);
-        buf = (buf + 1) % kNBuf;
     }
-    wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
+    M = m;
+    L = l;
+    u0 = make_float4(u[0], u[1], u[2], u[3]);
+    u1 = make_float4(u[4], u[5], u[6], u[7]);
 }
 
 // ---------------------------------------------------------------------------
@@ -851,7 +766,8 @@ __global__ __launch_bounds__(512) void mla_decode_safe_kernel(const MlaParams p,
 //    (a partial row is read as two contiguous 1 KB spans).  The split maxima
 //    and sums are wave-uniform, so they come in as scalar loads, and up to 8
 //    partials are in flight per wavefront; chunks are folded in with a
-//    running maximum.  When the block holds fewer than 8 sequences the idle
+//    running maximum.  The partials of a decode workgroup that stopped early
+//    are recomputed here instead.  When the block holds fewer than 8 sequences the idle
 //    wavefronts take a share of some sequence's partials instead, and the
 //    shares are combined through LDS.
 //    Product: out[b, i, :] = W_UV[i] u~[b, i, :] on the matrix cores, with
@@ -903,7 +819,33 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
 
     float M = -INFINITY, L = 0.f;
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-    for (int j0 = 0; j0 < nj; j0 += kFinChunk) {
+    // a decode workgroup that stopped early left no partials: recompute them
+    bool any_flag = false;
+    for (int jj = 0; jj < nj; jj++) any_flag |= p.flags[wf + sub + nsub * jj] != 0;
+    if (any_flag) {   // wave-uniform; rare
+        for (int jj = 0; jj < nj; jj++) {
+            const int wk = wf + sub + nsub * jj;
+            float mk, lk;
+            float4 k0, k1;
+            if (p.flags[wk]) {
+                mla_partial_recompute(p, bb, i, max(wk * tpw, s0), min((wk + 1) * tpw, s1), s0, lane, mk, lk, k0, k1);
+            } else {
+                const size_t row = row0 + (size_t)(sub + nsub * jj) * p.h;
+                mk = ml[row].x;
+                lk = ml[row].y;
+                k0 = pu[row * 128 + 2 * lane];
+                k1 = pu[row * 128 + 2 * lane + 1];
+            }
+            if (!(lk > 0.f)) continue;
+            const float Mn = fmaxf(M, mk);
+            const float sa = __builtin_amdgcn_exp2f(M - Mn), sb = __builtin_amdgcn_exp2f(mk - Mn);
+            L = L * sa + lk * sb;
+            a0 = a0 * sa + k0 * sb;
+            a1 = a1 * sa + k1 * sb;
+            M = Mn;
+        }
+    }
+    for (int j0 = 0; j0 < (any_flag ? 0 : nj); j0 += kFinChunk) {
         float2 v[kFinChunk];
         float4 u[kFinChunk][2];
 #pragma unroll
@@ -1038,13 +980,10 @@ hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g2 = (unsigned)p.n_wg;
-    if (paged) {
-        hipLaunchKernelGGL((mla_decode_fast_kernel<true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
-        hipLaunchKernelGGL((mla_decode_safe_kernel<true>), dim3(g2), dim3(512), 0, st, p, p.bt, p.s, p.sched);
-    } else {
-        hipLaunchKernelGGL((mla_decode_fast_kernel<false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
-        hipLaunchKernelGGL((mla_decode_safe_kernel<false>), dim3(g2), dim3(512), 0, st, p, p.bt, p.s, p.sched);
-    }
+    if (paged)
+        hipLaunchKernelGGL((mla_decode_kernel<true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+    else
+        hipLaunchKernelGGL((mla_decode_kernel<false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g3 = (unsigned)(p.h * ((p.B + kFinSeq - 1) / kFinSeq));

@@ -123,7 +123,7 @@ MlaPlan plan_mla(int B, int h, int d_c, int d_R)
     P.min_tiles = 8;
     const size_t slots = (size_t)P.n_wg + B - 1;
     P.qhat_bytes = align256((size_t)B * ((h + 31) / 32) * 32 * (d_c + d_R) * 2);
-    P.part_u_bytes = align256(slots * h * d_c * sizeof(float));
+    P.part_u_bytes = align256(slots * h * d_c * 2);   // fp16
     P.part_ml_bytes = align256(slots * h * 2 * sizeof(float));
     P.flag_bytes = align256((size_t)P.n_wg * sizeof(int32_t));
     P.sched_bytes = align256(((size_t)B + 1 + P.n_wg + 1) * sizeof(int32_t));
@@ -305,7 +305,7 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     p.bt = block_table;
     char* ws = (char*)workspace;
     p.qhat = (uint16_t*)ws;
-    p.part_u = (float*)(ws + P.qhat_bytes);
+    p.part_u = (_Float16*)(ws + P.qhat_bytes);
     p.part_ml = (float*)(ws + P.qhat_bytes + P.part_u_bytes);
     p.flags = (int32_t*)(ws + P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes);
     p.sched = (int32_t*)(ws + P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.flag_bytes);

@@ -54,7 +54,7 @@ struct MlaParams {
     const int32_t* s;
     const int32_t* bt;
     uint16_t* qhat;       // bf16 absorbed query, B * ceil(h / 32) blocks of 32 heads x 576 in decode-operand order
-    float* part_u;        // [n_wg + B - 1, h, d_c]: partial of (workgroup w, sequence b) in slot w + b
+    _Float16* part_u;     // [n_wg + B - 1, h, d_c]: U / l of (workgroup w, sequence b) in slot w + b
     float* part_ml;       // [n_wg + B - 1, h, 2]
     int32_t* flags;       // [n_wg]: decode workgroup stopped early; its partials are recomputed by the merge
     int32_t* sched;       // tile_start [B + 1], wstart [n_wg], tpw [1]

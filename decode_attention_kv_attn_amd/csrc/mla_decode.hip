@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
 #endif
     constexpr int PD = MLA_PD;      // score operands read ahead of their product
 #ifndef MLA_SCH
-#define MLA_SCH 2
+#define MLA_SCH 1
 #endif
     constexpr int SCH = MLA_SCH;    // score accumulation chains
     constexpr int MCW = 4;          // 32-column tiles of the latent sum per wavefront
@@ -495,6 +495,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * kTile];
     __shared__ __attribute__((aligned(16))) bf16x8 Pb[NTH][2][64];   // P of every head tile, B-operand layout
     __shared__ int ovf;   // some head's scores ran past its reference max + 64
+    __shared__ float Lx[NTH * 32];   // softmax sums of all heads, for the partial write
 
     const int tid = threadIdx.x, lane = tid % 64, hh = lane / 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -548,28 +549,52 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     };
     // partial state of sequence b, slot w + b: (m, l) of the score heads and
     // the U^T columns 128 wave .. + 127 of every head
-    // The U columns go out as fp32 straight from the accumulation registers
-    // (any vector arithmetic on them here would cost the tile loop its
-    // register allocation).
+    // U / l is a weighted mean of cached latents, so it is stored as fp16
+    // (2^-11 relative), halving the partial traffic of fp32 sums.  The sums l
+    // of all heads go through LDS to the wavefronts holding their columns.
+    // Vector arithmetic on the AGPR-resident U would cost the tile loop its
+    // register allocation, so U leaves through LDS: each wavefront stores 8
+    // of its accumulator registers into its 2 KB of the P buffer (free once
+    // every wavefront has left the tile loop) and reads them back into fresh
+    // registers before scaling and converting them.
     auto write_partial = [&](int b) {
         const float l = lsum + xor32(lsum);
-        if (hh == 0 && hv) {
-            const size_t row = (size_t)(w + b) * p.h + hs;
-            p.part_ml[row * 2] = m;
-            p.part_ml[row * 2 + 1] = l;
+        if (hh == 0) {
+            Lx[hs] = l;
+            if (hv) {
+                const size_t row = (size_t)(w + b) * p.h + hs;
+                p.part_ml[row * 2] = m;
+                p.part_ml[row * 2 + 1] = l;
+            }
         }
+        __syncthreads();   // Lx written, and every wavefront is done with Pb
+        float4* stg = (float4*)&Pb[wave][0][0] + 2 * lane;
+        const uint32_t stg_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stg;
 #pragma unroll
         for (int nt = 0; nt < NTH; nt++) {
             const int head = 32 * nt + lane % 32;
-            if (head >= p.h) continue;
-            float* pu = p.part_u + ((size_t)(w + b) * p.h + head) * 512 + 128 * wave + 4 * hh;
+            const float lh = Lx[head];
+            const float il = lh > 0.f ? 1.f / lh : 0.f;
+            _Float16* pu = p.part_u + ((size_t)(w + b) * p.h + min(head, p.h - 1)) * 512 + 128 * wave + 4 * hh;
 #pragma unroll
             for (int mc = 0; mc < MCW; mc++)
 #pragma unroll
-                for (int g = 0; g < 4; g++)
-                    *(float4*)(pu + 32 * mc + 8 * g) = make_float4(U[mc][nt][4 * g], U[mc][nt][4 * g + 1],
-                                                                   U[mc][nt][4 * g + 2], U[mc][nt][4 * g + 3]);
+                for (int hf = 0; hf < 2; hf++) {
+                    stg[0] = make_float4(U[mc][nt][8 * hf], U[mc][nt][8 * hf + 1], U[mc][nt][8 * hf + 2], U[mc][nt][8 * hf + 3]);
+                    stg[1] = make_float4(U[mc][nt][8 * hf + 4], U[mc][nt][8 * hf + 5], U[mc][nt][8 * hf + 6], U[mc][nt][8 * hf + 7]);
+                    f32x4 x0, x1;
+                    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+                                 : "=v"(x0), "=v"(x1) : "v"(stg_lds) : "memory");
+                    if (head < p.h) {
+                        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                        const h4 v0 = {(_Float16)(x0[0] * il), (_Float16)(x0[1] * il), (_Float16)(x0[2] * il), (_Float16)(x0[3] * il)};
+                        const h4 v1 = {(_Float16)(x1[0] * il), (_Float16)(x1[1] * il), (_Float16)(x1[2] * il), (_Float16)(x1[3] * il)};
+                        *(h4*)(pu + 32 * mc + 16 * hf) = v0;
+                        *(h4*)(pu + 32 * mc + 16 * hf + 8) = v1;
+                    }
+                }
         }
+        __syncthreads();   // Pb and Lx are reused by the next sequence
     };
     reset();
     if (tid == 0) ovf = 0;
@@ -763,10 +788,10 @@ __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_l
 // ---------------------------------------------------------------------------
 // 3. finish.  Workgroup = (head i, up to 8 sequences), 8 wavefronts.
 //    Merge: a wavefront takes one sequence, lane l its columns 8l .. 8l+7
-//    (a partial row is read as two contiguous 1 KB spans).  The split maxima
-//    and sums are wave-uniform, so they come in as scalar loads, and up to 8
-//    partials are in flight per wavefront; chunks are folded in with a
-//    running maximum.  The partials of a decode workgroup that stopped early
+//    (a partial row, U / l in fp16, is one contiguous 1 KB span).  The split
+//    maxima and sums are wave-uniform, so they come in as scalar loads, and
+//    up to 8 partials are in flight per wavefront; chunks are folded in with
+//    a running maximum, each weighted by 2^(m_k - M) l_k.  The partials of a decode workgroup that stopped early
 //    are recomputed here instead.  When the block holds fewer than 8 sequences the idle
 //    wavefronts take a share of some sequence's partials instead, and the
 //    shares are combined through LDS.
@@ -815,7 +840,14 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
     const int nj = ns > sub ? (ns - sub + nsub - 1) / nsub : 0;
     const size_t row0 = (size_t)(wf + bb) * p.h + i;   // partial k: row0 + k h
     const float2* __restrict__ ml = (const float2*)p.part_ml;
-    const float4* __restrict__ pu = (const float4*)p.part_u;
+    const uint4* __restrict__ pu = (const uint4*)p.part_u;   // 8 fp16 of U / l per lane
+    auto unpack = [](uint4 h, float4& lo, float4& hi) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 x = __builtin_bit_cast(h2, h.x), y = __builtin_bit_cast(h2, h.y);
+        const h2 z = __builtin_bit_cast(h2, h.z), t = __builtin_bit_cast(h2, h.w);
+        lo = make_float4((float)x[0], (float)x[1], (float)y[0], (float)y[1]);
+        hi = make_float4((float)z[0], (float)z[1], (float)t[0], (float)t[1]);
+    };
 
     float M = -INFINITY, L = 0.f;
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
@@ -833,8 +865,9 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
                 const size_t row = row0 + (size_t)(sub + nsub * jj) * p.h;
                 mk = ml[row].x;
                 lk = ml[row].y;
-                k0 = pu[row * 128 + 2 * lane];
-                k1 = pu[row * 128 + 2 * lane + 1];
+                unpack(pu[row * 64 + lane], k0, k1);
+                k0 *= lk;
+                k1 *= lk;
             }
             if (!(lk > 0.f)) continue;
             const float Mn = fmaxf(M, mk);
@@ -847,14 +880,13 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
     }
     for (int j0 = 0; j0 < (any_flag ? 0 : nj); j0 += kFinChunk) {
         float2 v[kFinChunk];
-        float4 u[kFinChunk][2];
+        uint4 uh[kFinChunk];
 #pragma unroll
         for (int c = 0; c < kFinChunk; c++) {   // clamped, unconditional loads
             const int jj = min(j0 + c, nj - 1);
             const size_t row = row0 + (size_t)(sub + nsub * jj) * p.h;
             v[c] = ml[row];
-            u[c][0] = pu[row * 128 + 2 * lane];
-            u[c][1] = pu[row * 128 + 2 * lane + 1];
+            uh[c] = pu[row * 64 + lane];
         }
         float Mc = M;
 #pragma unroll
@@ -868,12 +900,14 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
 #pragma unroll
         for (int c = 0; c < kFinChunk; c++) {
             if (j0 + c < nj && v[c].y > 0.f) {   // wave-uniform
-                const float wk = __builtin_amdgcn_exp2f(v[c].x - Mc);
-                L = fmaf(wk, v[c].y, L);
-                a0.x = fmaf(wk, u[c][0].x, a0.x); a0.y = fmaf(wk, u[c][0].y, a0.y);
-                a0.z = fmaf(wk, u[c][0].z, a0.z); a0.w = fmaf(wk, u[c][0].w, a0.w);
-                a1.x = fmaf(wk, u[c][1].x, a1.x); a1.y = fmaf(wk, u[c][1].y, a1.y);
-                a1.z = fmaf(wk, u[c][1].z, a1.z); a1.w = fmaf(wk, u[c][1].w, a1.w);
+                const float wl = __builtin_amdgcn_exp2f(v[c].x - Mc) * v[c].y;   // weight of U / l
+                float4 u0, u1;
+                unpack(uh[c], u0, u1);
+                L += wl;
+                a0.x = fmaf(wl, u0.x, a0.x); a0.y = fmaf(wl, u0.y, a0.y);
+                a0.z = fmaf(wl, u0.z, a0.z); a0.w = fmaf(wl, u0.w, a0.w);
+                a1.x = fmaf(wl, u1.x, a1.x); a1.y = fmaf(wl, u1.y, a1.y);
+                a1.z = fmaf(wl, u1.z, a1.z); a1.w = fmaf(wl, u1.w, a1.w);
             }
         }
         M = Mc;

@@ -65,6 +65,15 @@ def _load():
                                          I, I, D]
         lib.ref_kv_append.restype = I
         lib.ref_kv_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I]
+        lib.ref_fp8_e4m3_decode.restype = D
+        lib.ref_fp8_e4m3_decode.argtypes = [I]
+        lib.ref_fp8_e4m3_encode.restype = I
+        lib.ref_fp8_e4m3_encode.argtypes = [C.c_float]
+        lib.ref_gqa_decode_fp8.restype = I
+        lib.ref_gqa_decode_fp8.argtypes = [P, P, P, P, P, D, D, P, P, I, I, I, I, I, I, I, D]
+        lib.ref_kv_append_fp8.restype = I
+        lib.ref_kv_append_fp8.argtypes = [P, P, P, P, C.c_float, C.c_float, P, P, I, I, I, I,
+                                          I, I]
         _lib = lib
     return _lib
 
@@ -216,4 +225,82 @@ def kv_append(cache_k, cache_v, k_new, v_new, pos, b, block_table=None, block_si
                                max_blocks, bs, B, s_max, h_kv, d_h, b)
     if rc != 0:
         raise ValueError(f"ref_kv_append rejected its arguments ({rc})")
+    return ck, cv
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) caches with one fp32 scale per tensor: value = code * scale.
+# ---------------------------------------------------------------------------
+def fp8_decode(codes) -> np.ndarray:
+    """Values (float64) of E4M3 codes, elementwise, by the format's definition."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib.ref_fp8_e4m3_decode(i) for i in range(256)], dtype=np.float64)
+    return table[c]
+
+
+def fp8_encode(x) -> np.ndarray:
+    """E4M3 codes of fp32 values: nearest, ties to even, saturating at +-448."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float32)
+    flat = np.array([lib.ref_fp8_e4m3_encode(float(v)) for v in x.ravel()], dtype=np.uint8)
+    return flat.reshape(x.shape)
+
+
+def inv_scale(scale) -> np.float32:
+    """The fp32 reciprocal both sides multiply by before encoding."""
+    return np.float32(1.0) / np.float32(scale)
+
+
+def gqa_decode_fp8(q, K8, V8, k_scale, v_scale, s, block_table=None, block_size=16,
+                   scale=None):
+    """Reference decode over FP8 K/V codes (uint8) with bf16 q (uint16 bits).
+
+    Shapes as gqa_decode.  Returns (out [B,h,d_h] float64, lse [B,h] float64).
+    """
+    q = _stored(q, 2)
+    K8 = np.ascontiguousarray(K8, dtype=np.uint8)
+    V8 = np.ascontiguousarray(V8, dtype=np.uint8)
+    B, h, d_h = q.shape
+    h_kv = K8.shape[2]
+    s = _i32(s)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max, max_blocks, bs = K8.shape[1], 0, 0
+    else:
+        s_max, max_blocks, bs = 0, bt.shape[1], block_size
+        _check_table(bt, K8.shape[0] * K8.shape[1], bs, s)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    out = np.zeros((B, h, d_h), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    rc = _load().ref_gqa_decode_fp8(_ptr(out), _ptr(lse), _ptr(q), _ptr(K8), _ptr(V8),
+                                    float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                    _ptr(s), _ptr(bt), max_blocks, bs, B, s_max, h, h_kv, d_h,
+                                    float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_gqa_decode_fp8 rejected its arguments ({rc})")
+    return out, lse
+
+
+def kv_append_fp8(cache_k, cache_v, k_new, v_new, k_scale, v_scale, pos, block_table=None,
+                  block_size=16):
+    """Reference FP8 append on host images (copies): codes of k_new * (1/k_scale) etc."""
+    ck = np.ascontiguousarray(cache_k, dtype=np.uint8).copy()
+    cv = None if cache_v is None else np.ascontiguousarray(cache_v, dtype=np.uint8).copy()
+    kn = _stored(k_new, 2)
+    vn = None if v_new is None else _stored(v_new, 2)
+    B, h_kv, d_h = kn.shape
+    pos = _i32(pos)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max, max_blocks, bs = ck.shape[1], 0, 0
+    else:
+        s_max, max_blocks, bs = 0, bt.shape[1], block_size
+        _check_table(bt, ck.shape[0] * ck.shape[1], bs, [int(p) + 1 for p in pos])
+    rc = _load().ref_kv_append_fp8(_ptr(ck), _ptr(cv), _ptr(kn), _ptr(vn),
+                                   float(inv_scale(k_scale)), float(inv_scale(v_scale)),
+                                   _ptr(pos), _ptr(bt), max_blocks, bs, B, s_max, h_kv, d_h)
+    if rc != 0:
+        raise ValueError(f"ref_kv_append_fp8 rejected its arguments ({rc})")
     return ck, cv

@@ -363,3 +363,153 @@ int ref_kv_append(void* cache_k, void* cache_v, const void* k_new, const void* v
     }
     return OR_OK;
 }
+
+/*
+ * FP8 caches (the ranked next step after the bf16 path: "MHA -> MQA -> GQA ->
+ * MLA" and the charlestar.github.io MLA page both name an 8-bit cache as the
+ * way to halve the bytes per token; the scale granularity is left open).
+ * Reading taken: OCP E4M3 codes ("e4m3fn": 1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN; no
+ * infinities; largest finite 448) with one fp32 scale per tensor, value =
+ * code * scale.
+ */
+
+/* value of an E4M3 code, by the format's definition */
+double ref_fp8_e4m3_decode(int code)
+{
+    const int c = code & 0xff;
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -mag : mag;
+}
+
+/*
+ * E4M3 code of an fp32 value: round to nearest, ties to even, saturating at
+ * +-448 (values at or beyond it, and infinities, give the largest finite
+ * code); NaN gives 0x7F; the sign of zero is kept.
+ */
+int ref_fp8_e4m3_encode(float y)
+{
+    if (isnan(y)) return 0x7f;
+    const int sgn = signbit(y) ? 0x80 : 0;
+    const double a = fabs((double)y);
+    if (a >= 448.0) return sgn | 0x7e;
+    if (a == 0.0) return sgn;
+    int e = (int)floor(log2(a));
+    if (ldexp(1.0, e) > a) e--;          /* guard the log2 rounding */
+    if (ldexp(1.0, e + 1) <= a) e++;
+    if (e < -6) e = -6;                  /* subnormals share the quantum 2^-9 */
+    const double quantum = ldexp(1.0, e - 3);
+    double mq = rint(a / quantum);       /* exact quotient; rint rounds half to even */
+    int code;
+    if (e == -6 && mq < 8.0) {
+        code = (int)mq;                  /* subnormal (mq = 8 is the smallest normal) */
+    } else {
+        if (mq >= 16.0) {                /* rounded up into the next binade */
+            mq = 8.0;
+            e++;
+        }
+        code = ((e + 7) << 3) | ((int)mq - 8);
+    }
+    if (code > 0x7e) code = 0x7e;
+    return sgn | code;
+}
+
+static double ld_fp8(const uint8_t* p, size_t idx, double scale)
+{
+    return ref_fp8_e4m3_decode(p[idx]) * scale;
+}
+
+/*
+ * Decode attention over an FP8 K/V cache: as ref_gqa_decode with bf16 q,
+ * K(b,t,j,d) = decode(k code) * k_scale and V likewise with v_scale.
+ */
+int ref_gqa_decode_fp8(double* out, double* lse, const void* q, const uint8_t* k,
+                       const uint8_t* v, double k_scale, double v_scale, const int32_t* s,
+                       const int32_t* block_table, int max_blocks, int block_size, int B,
+                       int s_max, int h, int h_kv, int d_h, double scale)
+{
+    if (!out || !q || !k || !v || !s) return OR_EINVAL;
+    if (B < 0 || h <= 0 || h_kv <= 0 || d_h <= 0 || (h % h_kv) != 0) return OR_EINVAL;
+    if (block_table && (block_size <= 0 || max_blocks <= 0)) return OR_EINVAL;
+    const int g = h / h_kv;
+    const long rows = (long)B * h;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long r = 0; r < rows; r++) {
+        const int bb = (int)(r / h), i = (int)(r % h), j = i / g;
+        const int n = s[bb];
+        double* o = out + (size_t)r * d_h;
+        if (n < 0 || (!block_table && n > s_max) ||
+            (block_table && n > max_blocks * block_size) ||
+            !table_ok(block_table, max_blocks, block_size, bb, n)) {
+            bad = 1;
+            continue;
+        }
+        if (n == 0) {
+            for (int d = 0; d < d_h; d++) o[d] = 0.0;
+            if (lse) lse[r] = -INFINITY;
+            continue;
+        }
+        double* z = (double*)malloc(sizeof(double) * (size_t)n * 2);
+        double* p = z + n;
+        const size_t qoff = (size_t)r * d_h;
+        for (int t = 0; t < n; t++) {
+            const size_t koff =
+                (row_of(block_table, max_blocks, block_size, s_max, bb, t) * h_kv + j) * d_h;
+            double acc = 0.0;
+            for (int d = 0; d < d_h; d++) acc += ld(q, qoff + d, 2) * ld_fp8(k, koff + d, k_scale);
+            z[t] = scale * acc;
+        }
+        double m;
+        const double l = softmax_weights(z, n, p, &m);
+        for (int d = 0; d < d_h; d++) {
+            double acc = 0.0;
+            for (int t = 0; t < n; t++) {
+                const size_t voff =
+                    (row_of(block_table, max_blocks, block_size, s_max, bb, t) * h_kv + j) *
+                    d_h;
+                acc += p[t] * ld_fp8(v, voff + d, v_scale);
+            }
+            o[d] = acc / l;
+        }
+        if (lse) lse[r] = m + log(l);
+        free(z);
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/*
+ * Append into FP8 caches: each element x of the bf16 rows k_new / v_new
+ * becomes encode(x * inv_scale), the product taken in fp32 (inv_scale is the
+ * fp32 reciprocal of the tensor's scale), at slot pos[b] as ref_kv_append.
+ */
+int ref_kv_append_fp8(uint8_t* cache_k, uint8_t* cache_v, const void* k_new, const void* v_new,
+                      float k_inv_scale, float v_inv_scale, const int32_t* pos,
+                      const int32_t* block_table, int max_blocks, int block_size, int B,
+                      int s_max, int h_kv, int d_h)
+{
+    if (!cache_k || !k_new || !pos) return OR_EINVAL;
+    if ((cache_v == NULL) != (v_new == NULL)) return OR_EINVAL;
+    if (B < 0 || h_kv <= 0 || d_h <= 0) return OR_EINVAL;
+    const size_t n = (size_t)h_kv * d_h;
+    for (int bb = 0; bb < B; bb++) {
+        const int t = pos[bb];
+        if (t < 0 || (!block_table && t >= s_max) ||
+            (block_table && t >= max_blocks * block_size))
+            return OR_EINVAL;
+        if (block_table && block_table[(size_t)bb * max_blocks + t / block_size] < 0)
+            return OR_EINVAL;
+        const size_t row = row_of(block_table, max_blocks, block_size, s_max, bb, t);
+        for (size_t e = 0; e < n; e++) {
+            const float xk = (float)ld(k_new, (size_t)bb * n + e, 2);
+            cache_k[row * n + e] = (uint8_t)ref_fp8_e4m3_encode(xk * k_inv_scale);
+            if (cache_v) {
+                const float xv = (float)ld(v_new, (size_t)bb * n + e, 2);
+                cache_v[row * n + e] = (uint8_t)ref_fp8_e4m3_encode(xv * v_inv_scale);
+            }
+        }
+    }
+    return OR_OK;
+}

@@ -26,6 +26,8 @@ EXPORTED = (
     "attn_decode_gqa",
     "attn_decode_mla_absorbed",
     "attn_stream_read_probe",
+    "kv_cache_append_fp8",
+    "attn_decode_gqa_fp8",
 )
 
 _lib = None
@@ -63,6 +65,11 @@ def lib():
                                                I, I, I, I, F, P, Z, P]
         L.attn_stream_read_probe.restype = I
         L.attn_stream_read_probe.argtypes = [P, Z, P, P]
+        L.kv_cache_append_fp8.restype = I
+        L.kv_cache_append_fp8.argtypes = [P, P, P, P, F, F, P, P, I, I, I, I, I, I, I, P]
+        L.attn_decode_gqa_fp8.restype = I
+        L.attn_decode_gqa_fp8.argtypes = [P, P, P, P, P, F, F, P, P, I, I, I, I, I, I, I, I, F,
+                                          P, Z, P]
         _lib = L
     return _lib
 
@@ -122,6 +129,27 @@ def attn_decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, b
                                _p(block_table), max_blocks, block_size, num_blocks, B, s_max, h,
                                h_kv, d_h, b, float(scale), _p(workspace), int(workspace_bytes),
                                _stream(stream))
+    return _check(rc) if check else rc
+
+
+def kv_cache_append_fp8(cache_k, cache_v, k_new, v_new, k_scale, v_scale, pos, block_table,
+                        max_blocks, block_size, num_blocks, B, s_max, h_kv, d_h, stream=None,
+                        check=True):
+    rc = lib().kv_cache_append_fp8(_p(cache_k), _p(cache_v), _p(k_new), _p(v_new),
+                                   float(k_scale), float(v_scale), _p(pos), _p(block_table),
+                                   max_blocks, block_size, num_blocks, B, s_max, h_kv, d_h,
+                                   _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_gqa_fp8(out, lse, q, cache_k, cache_v, k_scale, v_scale, s, block_table,
+                        max_blocks, block_size, num_blocks, B, s_max, h, h_kv, d_h, scale,
+                        workspace, workspace_bytes, stream=None, check=True):
+    rc = lib().attn_decode_gqa_fp8(_p(out), _p(lse), _p(q), _p(cache_k), _p(cache_v),
+                                   float(k_scale), float(v_scale), _p(s), _p(block_table),
+                                   max_blocks, block_size, num_blocks, B, s_max, h, h_kv, d_h,
+                                   float(scale), _p(workspace), int(workspace_bytes),
+                                   _stream(stream))
     return _check(rc) if check else rc
 
 
@@ -185,6 +213,29 @@ def decode_gqa(q, K, V, s, block_table=None, block_size=16, s_max=None, scale=0.
     wb, wn = ws.get(attn_decode_workspace_bytes(0, B, s_max, h, h_kv, d_h))
     attn_decode_gqa(out, l, q, K, V, s, block_table, max_blocks, block_size, num_blocks, B, s_max,
                     h, h_kv, d_h, b, scale, wb, wn, stream)
+    return out, l
+
+
+def decode_gqa_fp8(q, K8, V8, k_scale, v_scale, s, block_table=None, block_size=16, s_max=None,
+                   scale=0.0, lse=True, workspace=None, out=None, stream=None):
+    """q [B,h,d_h] bf16; K8,V8 uint8 E4M3 codes [B,s_max,h_kv,d_h] or paged pools."""
+    import torch
+    B, h, d_h = q.shape
+    h_kv = K8.shape[2]
+    if block_table is None:
+        s_max = K8.shape[1] if s_max is None else s_max
+        max_blocks, num_blocks = 0, 0
+    else:
+        max_blocks = block_table.shape[1]
+        num_blocks = K8.shape[0]
+        s_max = max_blocks * block_size if s_max is None else s_max
+    if out is None:
+        out = torch.empty_like(q)
+    l = torch.empty((B, h), dtype=torch.float32, device=q.device) if lse else None
+    ws = workspace or Workspace(q.device)
+    wb, wn = ws.get(attn_decode_workspace_bytes(0, B, s_max, h, h_kv, d_h))
+    attn_decode_gqa_fp8(out, l, q, K8, V8, k_scale, v_scale, s, block_table, max_blocks,
+                        block_size, num_blocks, B, s_max, h, h_kv, d_h, scale, wb, wn, stream)
     return out, l
 
 

@@ -207,11 +207,17 @@ int kv_cache_append(void* cache_k, void* cache_v, const void* k_new, const void*
     return ATTN_OK;
 }
 
-int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
-                    const void* cache_v, const int32_t* s, const int32_t* block_table,
-                    int max_blocks, int block_size, int num_blocks, int B, int s_max, int h,
-                    int h_kv, int d_h, int b, float scale, void* workspace,
-                    size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Shared body of the GQA entry points.  b = 2 (bf16) or 4 (fp32) caches, or
+// b = 1: OCP E4M3 caches with per-tensor scales (q and out bf16).
+int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const void* cache_v,
+               const int32_t* s, const int32_t* block_table, int max_blocks, int block_size,
+               int num_blocks, int B, int s_max, int h, int h_kv, int d_h, int b, float scale,
+               float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+               void* stream)
 {
     if (!out || !q || !cache_k || !cache_v || !s)
         return fail(ATTN_EINVAL, "null out, q, cache_k, cache_v or s");
@@ -220,15 +226,17 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
                     d_h, s_max);
     if (h % h_kv != 0)
         return fail(ATTN_EINVAL, "num_heads (%d) is not divisible by num_kv_heads (%d)", h, h_kv);
-    if (b != 2 && b != 4) return fail(ATTN_EINVAL, "b must be 2 (bf16) or 4 (fp32)");
-    if (!((b == 2 && (d_h == 64 || d_h == 128)) || (b == 4 && d_h == 64)))
+    if (b != 1 && b != 2 && b != 4) return fail(ATTN_EINVAL, "b must be 2 (bf16) or 4 (fp32)");
+    if (!((b <= 2 && (d_h == 64 || d_h == 128)) || (b == 4 && d_h == 64)))
         return fail(ATTN_ENOTSUP, "unsupported (b=%d, d_h=%d)", b, d_h);
+    if (b == 1 && h / h_kv > 64)
+        return fail(ATTN_ENOTSUP, "FP8 caches support h / h_kv <= 64 (got %d)", h / h_kv);
     if (block_table || s_max > 0) {
         int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
         if (rc) return rc;
     }
     if (B == 0) return ATTN_OK;
-    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b);
+    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b == 1 ? 2 : b);
     if (P.ws_bytes && (!workspace || workspace_bytes < P.ws_bytes))
         return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
                     workspace ? workspace_bytes : (size_t)0);
@@ -253,15 +261,79 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
     p.n_split = P.n_split;
     p.chunk = P.chunk;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_h);
-    p.scale_log2 = sc * 1.4426950408889634f;
+    p.scale_log2 = sc * k_scale * 1.4426950408889634f;
+    p.v_scale = v_scale;
     const long long grid = (long long)B * h_kv * P.n_hg * P.n_split;
     if (grid >= (1LL << 31)) return fail(ATTN_ENOTSUP, "problem too large for one launch");
-    hipError_t e = P.mfma ? attn::launch_gqa_mfma(p, d_h, P.NW, block_table != nullptr,
+    hipError_t e = P.mfma ? attn::launch_gqa_mfma(p, d_h, P.NW, block_table != nullptr, b == 1,
                                                   (unsigned)grid, (hipStream_t)stream)
                           : attn::launch_gqa_decode(p, d_h, b == 4, P.HG, block_table != nullptr,
                                                     (unsigned)grid, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attn_decode_gqa launch");
     return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_cache_append_fp8(void* cache_k, void* cache_v, const void* k_new, const void* v_new,
+                        float k_scale, float v_scale, const int32_t* pos,
+                        const int32_t* block_table, int max_blocks, int block_size,
+                        int num_blocks, int B, int s_max, int h_kv, int d_h, void* stream)
+{
+    if (!cache_k || !k_new || !pos) return fail(ATTN_EINVAL, "null cache_k, k_new or pos");
+    if ((cache_v == nullptr) != (v_new == nullptr))
+        return fail(ATTN_EINVAL, "cache_v and v_new must both be set or both be NULL");
+    if (B < 0 || h_kv <= 0 || d_h <= 0 || (h_kv * d_h) % 4 != 0)
+        return fail(ATTN_EINVAL, "bad sizes (h_kv * d_h must be a positive multiple of 4)");
+    if (!(k_scale > 0.f) || isinf(k_scale) || (cache_v && (!(v_scale > 0.f) || isinf(v_scale))))
+        return fail(ATTN_EINVAL, "scales must be positive and finite");
+    int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
+    if (rc) return rc;
+    attn::AppendParams pk{};
+    pk.cache = cache_k;
+    pk.src = k_new;
+    pk.pos = pos;
+    pk.bt = block_table;
+    pk.max_blocks = max_blocks;
+    pk.bs_log2 = block_table ? ilog2(block_size) : 0;
+    pk.num_blocks = num_blocks;
+    pk.s_max = s_max;
+    pk.row_bytes = (long long)h_kv * d_h;   // one byte per code
+    pk.inv_scale = 1.0f / k_scale;
+    attn::AppendParams pv = pk;
+    pv.cache = cache_v;
+    pv.src = v_new;
+    pv.inv_scale = cache_v ? 1.0f / v_scale : 1.0f;
+    hipError_t e = attn::launch_append_fp8(pk, cache_v ? &pv : nullptr, B, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_cache_append_fp8 launch");
+    return ATTN_OK;
+}
+
+int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
+                    const void* cache_v, const int32_t* s, const int32_t* block_table,
+                    int max_blocks, int block_size, int num_blocks, int B, int s_max, int h,
+                    int h_kv, int d_h, int b, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream)
+{
+    if (b != 2 && b != 4) return fail(ATTN_EINVAL, "b must be 2 (bf16) or 4 (fp32)");
+    return decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
+                      num_blocks, B, s_max, h, h_kv, d_h, b, scale, 1.f, 1.f, workspace,
+                      workspace_bytes, stream);
+}
+
+int attn_decode_gqa_fp8(void* out, float* lse, const void* q, const void* cache_k,
+                        const void* cache_v, float k_scale, float v_scale, const int32_t* s,
+                        const int32_t* block_table, int max_blocks, int block_size,
+                        int num_blocks, int B, int s_max, int h, int h_kv, int d_h, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || isinf(k_scale) || isinf(v_scale))
+        return fail(ATTN_EINVAL, "k_scale and v_scale must be positive and finite");
+    return decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
+                      num_blocks, B, s_max, h, h_kv, d_h, 1, scale, k_scale, v_scale, workspace,
+                      workspace_bytes, stream);
 }
 
 int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void* q_nope,

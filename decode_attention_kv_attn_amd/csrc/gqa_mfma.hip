@@ -40,10 +40,10 @@ namespace attn {
 #define GQA_MFMA_NBUF 4
 #endif
 
-template <int D>
+template <int D, bool F8>
 struct MfmaCfg {
     static constexpr int T = 32;               // tokens per tile
-    static constexpr int RB = D * 2;           // bytes of one row (one KV head)
+    static constexpr int RB = D * (F8 ? 1 : 2);  // bytes of one row (one KV head)
     static constexpr int NCH = RB / 16;        // 16-byte chunks per row
     static constexpr int KT = T * RB;          // bytes of a K (or V) tile
     static constexpr int RPO = 1024 / RB;      // rows per DMA instruction
@@ -58,39 +58,61 @@ struct MfmaCfg {
 // 256-byte rows, rows 0..15 get 16 distinct positions (score operands read
 // 16 rows at one chunk) and every 4 consecutive rows get distinct aligned
 // chunk pairs (the transposing reads take 4 rows x 32 bytes).
-template <int D>
+// FP8 rows (D bytes, D / 16 chunks): position c ^ ((r / 2) mod (D / 16)).
+// The score operands (16 rows, 8 bytes each at one column) then cover every
+// (row parity, chunk) pair once, and so do the transposing reads (pairs of
+// consecutive rows, 16 bytes each).
+template <int D, bool F8>
 __device__ __forceinline__ int gswz(int r)
 {
+    if (F8) return (r >> 1) & (D / 16 - 1);
     r &= 15;
     if (D == 128) return (2 * r + (r >> 3)) & 15;
     return (r & 1) ^ (r & 2) ^ ((r & 4) ? 5 : 0) ^ ((r & 8) ? 7 : 0);
 }
 
-// Per-lane byte offsets of the MFMA operands within a K or V tile buffer.
+// Per-lane byte offsets of the MFMA operands within a K or V tile buffer
+// (row block mt = 1 adds 16 rows).
+// bf16:
 //   score operand (K step ks, row block mt): row 16 mt + li, chunk 4 ks + G
 //   value operand (M tile mc, token half th): rows 4G + li/4 + 16 th, chunk
 //     2 mc + (li % 4) / 2, byte 8 (li % 2) within it
-template <int D>
+// FP8 (converted to bf16 after the read):
+//   score operand: row 16 mt + li, byte 32 ks + 8 G: chunk 2 ks + G / 2,
+//     byte 8 (G % 2) within it
+//   value operand (M tile mc): a transposing 8-bit read; source lane li reads
+//     row tau(G, li / 2), bytes 16 mc + 8 (li % 2), where tau(G, k) = 4 G + k
+//     for k < 4 and 16 + 4 G + k - 4 otherwise -- the token order of the
+//     score product's output, which is the K order of the value product
+template <int D, bool F8>
 struct GTileOffsets {
     int sc[D / 32];
     int tr[D / 16];
     __device__ __forceinline__ GTileOffsets(int li, int G)
     {
-        constexpr int RB = D * 2;
-        const int ss = gswz<D>(li);
+        constexpr int RB = D * (F8 ? 1 : 2);
+        const int ss = gswz<D, F8>(li);
+        if (F8) {
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ks++) sc[ks] = li * RB + (((4 * ks + G) ^ ss) << 4);
-        const int r = 4 * G + li / 4, cp = (li % 4) / 2, st = gswz<D>(r);
+            for (int ks = 0; ks < D / 32; ks++) sc[ks] = li * RB + (((2 * ks + G / 2) ^ ss) << 4) + 8 * (G % 2);
+            const int k = li / 2, r = k < 4 ? 4 * G + k : 16 + 4 * G + k - 4, st = gswz<D, F8>(r);
 #pragma unroll
-        for (int mc = 0; mc < D / 16; mc++) tr[mc] = r * RB + (((2 * mc + cp) ^ st) << 4) + 8 * (li % 2);
+            for (int mc = 0; mc < D / 16; mc++) tr[mc] = r * RB + ((mc ^ st) << 4) + 8 * (li % 2);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ks++) sc[ks] = li * RB + (((4 * ks + G) ^ ss) << 4);
+            const int r = 4 * G + li / 4, cp = (li % 4) / 2, st = gswz<D, F8>(r);
+#pragma unroll
+            for (int mc = 0; mc < D / 16; mc++) tr[mc] = r * RB + (((2 * mc + cp) ^ st) << 4) + 8 * (li % 2);
+        }
     }
 };
 
-template <int D, int NW, bool PAGED>
+template <int D, int NW, bool PAGED, bool F8>
 __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                                                            const int32_t* __restrict__ btab)
 {
-    using C = MfmaCfg<D>;
+    using C = MfmaCfg<D, F8>;
     constexpr int OPW = C::OPS / NW;   // DMA instructions per wavefront and tile
     static_assert(C::OPS % NW == 0, "DMA instructions must split evenly");
     __shared__ __attribute__((aligned(1024))) uint8_t Ls[C::NBUF * 2 * C::KT];
@@ -158,7 +180,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         for (int jj = 0; jj < OPW; jj++) {
             const int q = wave + NW * jj;
             const int rt = (q % (C::OPS / 2)) * C::RPO;   // first tile row of this instruction
-            voff[jj] = (uint32_t)(((rt & 15) + lr) * (int)rowstride + ((lp ^ gswz<D>(rt + lr)) << 4));
+            voff[jj] = (uint32_t)(((rt & 15) + lr) * (int)rowstride + ((lp ^ gswz<D, F8>(rt + lr)) << 4));
         }
     }
     auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
@@ -211,7 +233,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         issue_tile(t0 + L * C::T, L, half_row(t0 + L * C::T), half_row(t0 + L * C::T + 16));
     }
 
-    const GTileOffsets<D> to(li, G);
+    const GTileOffsets<D, F8> to(li, G);
     int buf = 0;
     for (int tb = t0; tb < t1; tb += C::T) {
         constexpr int AH = C::NBUF - 1;   // tiles in flight ahead of this one
@@ -231,13 +253,19 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
             bf16x8 ka[C::KS][2];
 #pragma unroll
             for (int ks = 0; ks < C::KS; ks++) {
-                ka[ks][0] = lds_read_16_as_2x8(Kt + to.sc[ks]);
-                ka[ks][1] = lds_read_16_as_2x8(Kt + to.sc[ks] + 16 * C::RB);
+                if (F8) {
+                    ka[ks][0] = fp8x8_to_bf16(lds_read_8(Kt + to.sc[ks]));
+                    ka[ks][1] = fp8x8_to_bf16(lds_read_8(Kt + to.sc[ks] + 16 * C::RB));
+                } else {
+                    ka[ks][0] = lds_read_16_as_2x8(Kt + to.sc[ks]);
+                    ka[ks][1] = lds_read_16_as_2x8(Kt + to.sc[ks] + 16 * C::RB);
+                }
             }
             bf16x8 va[C::MC];
 #pragma unroll
             for (int mc = 0; mc < C::MC; mc++)
-                va[mc] = cat_tr(lds_read_tr(Vt + to.tr[mc]), lds_read_tr(Vt + to.tr[mc] + 16 * C::RB));
+                va[mc] = F8 ? fp8x8_to_bf16(lds_read_tr8(Vt + to.tr[mc]))
+                            : cat_tr(lds_read_tr(Vt + to.tr[mc]), lds_read_tr(Vt + to.tr[mc] + 16 * C::RB));
             // ---- scores S^T = K . q^T
             f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -292,6 +320,10 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     l += xor16(l);
     l += xor32(l);
     if (!hv) return;
+    if (F8) {   // the V scale of an FP8 cache (the K scale is folded into scale_log2)
+#pragma unroll
+        for (int mc = 0; mc < C::MC; mc++) O[mc] *= p.v_scale;
+    }
     if (p.n_split == 1) {
         const float inv = 1.f / l;
         uint16_t* o = (uint16_t*)p.out + (size_t)(b * p.h + head) * D + 4 * G;
@@ -313,27 +345,30 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool F8>
 static hipError_t launch_nw(const GqaParams& p, bool paged, unsigned grid, hipStream_t st)
 {
     if (paged)
-        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
     else
-        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false, F8>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool F8>
 static hipError_t launch_mfma_d(const GqaParams& p, int NW, bool paged, unsigned grid, hipStream_t st)
 {
-    return NW == 2 ? launch_nw<D, 2>(p, paged, grid, st) : launch_nw<D, 4>(p, paged, grid, st);
+    return NW == 2 ? launch_nw<D, 2, F8>(p, paged, grid, st) : launch_nw<D, 4, F8>(p, paged, grid, st);
 }
 
-hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, unsigned grid,
+hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, bool f8, unsigned grid,
                            hipStream_t st)
 {
-    hipError_t e = d_h == 64 ? launch_mfma_d<64>(p, NW, paged, grid, st)
-                             : launch_mfma_d<128>(p, NW, paged, grid, st);
+    hipError_t e;
+    if (f8) e = d_h == 64 ? launch_mfma_d<64, true>(p, NW, paged, grid, st)
+                          : launch_mfma_d<128, true>(p, NW, paged, grid, st);
+    else e = d_h == 64 ? launch_mfma_d<64, false>(p, NW, paged, grid, st)
+                       : launch_mfma_d<128, false>(p, NW, paged, grid, st);
     if (e != hipSuccess || p.n_split == 1) return e;
     return launch_gqa_combine(p, d_h, false, st);
 }

@@ -20,14 +20,16 @@ struct GqaParams {
     int max_blocks, bs_log2, num_blocks;
     int B, s_max, h, h_kv;
     int n_hg, n_split, chunk;
-    float scale_log2;    // scale * log2(e)
+    float scale_log2;    // scale * log2(e) (times the K scale of an FP8 cache)
+    float v_scale;       // V scale of an FP8 cache (1 otherwise)
 };
 
 // vector kernel (any g; fp32 or bf16), then the split merge when n_split > 1
 hipError_t launch_gqa_decode(const GqaParams& p, int d_h, bool f32, int HG, bool paged,
                              unsigned grid, hipStream_t st);
-// matrix-core kernel (bf16, g <= 16 NW, NW = 2 or 4), then the split merge when n_split > 1
-hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, unsigned grid,
+// matrix-core kernel (bf16 or FP8 E4M3 caches, g <= 16 NW, NW = 2 or 4), then the split
+// merge when n_split > 1
+hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, bool f8, unsigned grid,
                            hipStream_t st);
 hipError_t launch_gqa_combine(const GqaParams& p, int d_h, bool f32, hipStream_t st);
 
@@ -37,10 +39,13 @@ struct AppendParams {
     const int32_t* pos;
     const int32_t* bt;
     int max_blocks, bs_log2, num_blocks, s_max;
-    long long row_bytes;
+    long long row_bytes;   // bytes of one cache row (FP8: elements of one row)
+    float inv_scale;       // FP8 append: fp32 reciprocal of the tensor's scale
 };
 
 hipError_t launch_append(const AppendParams& k, const AppendParams* v, int B, hipStream_t st);
+// bf16 rows -> OCP E4M3 codes of x * inv_scale (nearest, ties to even, saturating at +-448)
+hipError_t launch_append_fp8(const AppendParams& k, const AppendParams* v, int B, hipStream_t st);
 
 struct MlaParams {
     void* out;            // [B, h, d_v] bf16

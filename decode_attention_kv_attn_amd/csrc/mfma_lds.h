@@ -35,6 +35,40 @@ __device__ __forceinline__ bf16x8 lds_read_16_as_2x8(const uint8_t* p)
     return __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], hi[0], hi[1]));
 }
 
+// 8 bytes of LDS (ds_read_b64)
+__device__ __forceinline__ uint2 lds_read_8(const uint8_t* p)
+{
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+    const u32x2 v = *(lds_u32x2*)p;
+    return make_uint2(v[0], v[1]);
+}
+
+// Transposing LDS read of 8-bit elements (ds_read_b64_tr_b8).  Within each
+// 16-lane group, source lane i supplies 8 consecutive bytes M_i[0..7];
+// destination lane 8a + c receives M_a[c], M_{a+2}[c], ..., M_{a+14}[c].
+// Pointing source lane i at row R(i / 2), byte 8 (i % 2) of a 16-byte-wide
+// column block therefore hands lane j the column j of rows R(0) .. R(7).
+__device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* p)
+{
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i lds_v2i;
+    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
+    return make_uint2((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+// 8 OCP E4M3 codes (byte k of w is element k) -> 8 bf16, exactly (every E4M3
+// value is a bf16 value), with v_cvt_scalef32_pk_bf16_fp8 at scale 1
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 w)
+{
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.f, true);
+    const bf16x8 v = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return v;
+}
+
 __device__ __forceinline__ bf16x8 cat_tr(s16x4 lo, s16x4 hi)
 {
     typedef short s16x8 __attribute__((ext_vector_type(8)));

@@ -155,6 +155,46 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
                     size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 caches.  An 8-bit cache halves the bytes per token that decode streams
+ * (the pages name it as the next step and leave the scale granularity open).
+ * Reading taken here: OCP E4M3 codes ("e4m3fn": bias 7, subnormals, no
+ * infinities, 0x7F / 0xFF NaN, largest finite 448), one byte per element,
+ * with one fp32 scale per tensor: element value = code * scale.  The rows and
+ * layouts are those of the bf16 caches with b = 1.
+ */
+
+/*
+ * kv_cache_append_fp8 -- kv_cache_append for FP8 caches: element x of the
+ * bf16 rows k_new / v_new ([B, h_kv, d_h]) is stored as the E4M3 code of
+ * x * (1 / k_scale) (resp. v_scale), the reciprocal and the product taken in
+ * fp32, rounded to nearest with ties to even and saturated at +-448; NaN
+ * stores 0x7F.  MLA: cache_v = v_new = NULL, h_kv = 1, d_h = d_c + d_R.
+ * Errors: as kv_cache_append, plus EINVAL for a non-positive or infinite
+ * scale or h_kv * d_h not a multiple of 4.
+ */
+int kv_cache_append_fp8(void* cache_k, void* cache_v, const void* k_new, const void* v_new,
+                        float k_scale, float v_scale, const int32_t* pos,
+                        const int32_t* block_table, int max_blocks, int block_size,
+                        int num_blocks, int B, int s_max, int h_kv, int d_h, void* stream);
+
+/*
+ * attn_decode_gqa_fp8 -- attn_decode_gqa over FP8 caches: q and out bf16
+ * [B, h, d_h], cache_k / cache_v E4M3 codes with scales k_scale, v_scale:
+ *   out[b, i] = sum_t softmax_t(scale * q[b,i] . k_scale K8[b,t,j])
+ *                 v_scale V8[b,t,j].
+ * The codes are widened to bf16 exactly in the kernel, products accumulate
+ * in fp32; lse is that of the scaled scores.  Workspace as attn_decode_gqa
+ * (b = 2).  Supported: d_h in {64, 128}, h / h_kv <= 64.  Others: ENOTSUP.
+ * Errors: as attn_decode_gqa, plus EINVAL for a non-positive or infinite
+ * scale.
+ */
+int attn_decode_gqa_fp8(void* out, float* lse, const void* q, const void* cache_k,
+                        const void* cache_v, float k_scale, float v_scale, const int32_t* s,
+                        const int32_t* block_table, int max_blocks, int block_size,
+                        int num_blocks, int B, int s_max, int h, int h_kv, int d_h, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_decode_mla_absorbed -- MLA decode in the absorbed ("MQA mode") form:
  *   q~[b,i]  = W_UK[i]^T q_nope[b,i]                      (d_c values)
  *   z_t      = scale * (q~ . c_t + q_rope[b,i] . k_R,t)

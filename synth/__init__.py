@@ -209,6 +209,36 @@ def draw_gqa(shape: GqaShape, device="cpu", seed=None):
     return d
 
 
+def fp8_codes(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """E4M3 codes (uint8) that a quantizer with this per-tensor scale stores
+    for x: torch's float8_e4m3fn conversion of x / scale, clamped to +-448."""
+    y = (x.float() / float(np.float32(scale))).clamp_(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def draw_gqa_fp8(shape: GqaShape, k_scale: float, v_scale: float, device="cpu", seed=None):
+    """draw_gqa with the K/V caches stored as E4M3 codes: q is bf16, K8 and
+    V8 are uint8 codes of the same N(0,1) draws divided by the scales."""
+    seed = shape.seed if seed is None else seed
+    g = _gen(device, seed)
+    q = _randn((shape.B, shape.h, shape.d_h), g, device, torch.bfloat16)
+    if shape.paged:
+        tab, n_blk = block_table(shape.s, shape.block_size, seed)
+        rows = (n_blk, shape.block_size)
+    else:
+        tab, n_blk = None, 0
+        rows = (shape.B, max(shape.s_max, 1))
+    K8 = fp8_codes(_randn(rows + (shape.h_kv, shape.d_h), g, device, torch.float32), k_scale)
+    V8 = fp8_codes(_randn(rows + (shape.h_kv, shape.d_h), g, device, torch.float32), v_scale)
+    s = torch.tensor(shape.s, dtype=torch.int32, device=device)
+    d = dict(q=q, K8=K8, V8=V8, s=s, s_host=np.asarray(shape.s, dtype=np.int32))
+    if tab is not None:
+        d["block_table"] = torch.from_numpy(tab).to(device)
+        d["block_table_host"] = tab
+        d["n_blk"] = n_blk
+    return d
+
+
 def draw_mla(shape: MlaShape, device="cpu", seed=None):
     """Draw q_nope [B,h,d_nope], q_rope [B,h,d_R], latent cache, W_UK, W_UV.
 
@@ -250,5 +280,7 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.float32:
         return t.numpy()
     if t.dtype == torch.int32:
+        return t.numpy()
+    if t.dtype == torch.uint8:
         return t.numpy()
     raise TypeError(t.dtype)

@@ -1,0 +1,124 @@
+"""GPU parity of the FP8 (OCP E4M3) cache path against the CPU oracle.
+
+attn_decode_gqa_fp8 is compared element by element with
+oracle.gqa_decode_fp8 on the same codes and scales (small cases spanning
+several tiles and ragged tails, every group size of the matrix-core kernel,
+paged with a shuffled table, split contexts), and on sampled KV-head groups
+at the Llama-3-8B shape.  The codes widen to bf16 exactly, so the tolerances
+are those of the bf16 path (max-abs <= 2e-2, mean-abs <= 2e-3, rel-RMS <=
+1e-2).  kv_cache_append_fp8 is bit-exact against oracle.kv_append_fp8,
+including ties, saturation, NaN and signed zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_kv_attn_amd as A
+import oracle
+import synth
+from tests._gpu import assert_close, assert_lse_close, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+KS, VS = 1.0 / 64, 0.0123   # per-tensor scales (one power of two, one not)
+
+
+def run_fp8(B, h, h_kv, d_h, s, seed, paged=False, k_scale=KS, v_scale=VS):
+    sh = synth.GqaShape("t", B=B, h=h, h_kv=h_kv, d_h=d_h, b=2, s=tuple(s), paged=paged, seed=seed)
+    print(f"[fp8] B={B} h={h} h_kv={h_kv} d_h={d_h} s={list(s)[:6]} paged={paged}", flush=True)
+    d = synth.draw_gqa_fp8(sh, k_scale, v_scale, device=DEV)
+    bt = d.get("block_table")
+    out, lse = A.decode_gqa_fp8(d["q"], d["K8"], d["V8"], k_scale, v_scale, d["s"], block_table=bt,
+                                s_max=sh.s_max)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.gqa_decode_fp8(synth.host_bits(d["q"]), synth.host_bits(d["K8"]),
+                                         synth.host_bits(d["V8"]), k_scale, v_scale, d["s_host"],
+                                         block_table=d.get("block_table_host"))
+    assert_close(to_f64(out), ref, 2, "out")
+    assert_lse_close(to_f64(lse), ref_lse, 2, "lse")
+
+
+@pytest.mark.parametrize("h,h_kv", [(8, 8), (16, 4), (32, 8), (16, 2), (64, 1), (12, 4), (40, 2)])
+@pytest.mark.parametrize("d_h", [64, 128])
+def test_fp8_group_sizes(h, h_kv, d_h):
+    run_fp8(3, h, h_kv, d_h, (1, 77, 300), seed=h * 10 + h_kv)
+
+
+@pytest.mark.parametrize("s", [(0, 5), (0, 0), (1, 1), (31, 33), (32, 64), (63, 65)])
+def test_fp8_ragged_and_degenerate(s):
+    run_fp8(2, 16, 2, 128, s, seed=5)
+
+
+def test_fp8_paged_shuffled():
+    run_fp8(4, 32, 8, 128, (16, 17, 250, 1000), seed=6, paged=True)
+
+
+def test_fp8_split_context():
+    # one sequence of 9000 tokens over one KV head: several splits and the merge
+    run_fp8(1, 8, 1, 128, (9000,), seed=7)
+
+
+def test_fp8_scales_enter_scores_and_values():
+    run_fp8(2, 16, 4, 128, (200, 65), seed=8, k_scale=0.037, v_scale=2.5)
+
+
+def test_fp8_llama3_8b_shape_sampled():
+    sh = synth.GqaShape("t", B=64, h=32, h_kv=8, d_h=128, b=2, s=(4096,) * 64, seed=2)
+    d = synth.draw_gqa_fp8(sh, KS, VS, device=DEV)
+    out, lse = A.decode_gqa_fp8(d["q"], d["K8"], d["V8"], KS, VS, d["s"])
+    torch.cuda.synchronize()
+    g = 4
+    for (bi, j) in [(0, 0), (17, 3), (63, 7)]:
+        q = synth.host_bits(d["q"][bi:bi + 1, j * g:(j + 1) * g])
+        K = synth.host_bits(d["K8"][bi, :, j])[None, :, None, :]
+        V = synth.host_bits(d["V8"][bi, :, j])[None, :, None, :]
+        ref, rl = oracle.gqa_decode_fp8(q, K, V, KS, VS, np.array([4096], np.int32))
+        assert_close(to_f64(out[bi, j * g:(j + 1) * g]), ref[0], 2, f"b={bi} j={j}")
+        assert_lse_close(to_f64(lse[bi, j * g:(j + 1) * g]), rl[0], 2, f"b={bi} j={j}")
+
+
+def test_fp8_rejects_bad_arguments():
+    q = torch.zeros(1, 128, 128, dtype=torch.bfloat16, device=DEV)
+    K8 = torch.zeros(1, 16, 1, 128, dtype=torch.uint8, device=DEV)
+    s = torch.tensor([16], dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    rc = A.attn_decode_gqa_fp8(out, None, q, K8, K8, KS, VS, s, None, 0, 16, 0, 1, 16, 128, 1,
+                               128, 0.0, None, 0, check=False)
+    assert rc == A.ATTN_ENOTSUP   # g = 128 > 64
+    rc = A.attn_decode_gqa_fp8(out, None, q[:, :8], K8, K8, 0.0, VS, s, None, 0, 16, 0, 1, 16, 8,
+                               1, 128, 0.0, None, 0, check=False)
+    assert rc == A.ATTN_EINVAL    # non-positive scale
+
+
+def special_rows(B, h_kv, d_h, scale):
+    """bf16 rows with ties, saturating values, NaN, infinities, signed zeros."""
+    x = torch.randn(B, h_kv, d_h, device=DEV) * 40 * scale
+    flat = x.view(-1)
+    codes = torch.arange(0, 0x7e, device=DEV, dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+    mids = (codes[:-1] + codes[1:]) / 2 * scale          # ties (exact in bf16 where representable)
+    n = min(mids.numel(), flat.numel() // 4)
+    flat[:n] = mids[:n]
+    flat[n:n + 8] = torch.tensor([500.0, -1e4, float("inf"), float("-inf"), float("nan"), 0.0, -0.0,
+                                  448.0], device=DEV) * scale
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_fp8_append_bit_exact(paged):
+    B, s_max, h_kv, d_h = 5, 40, 8, 128
+    k_scale, v_scale = 0.02, 0.5
+    sh = synth.GqaShape("t", B=B, h=h_kv, h_kv=h_kv, d_h=d_h, b=2, s=(s_max,) * B, paged=paged,
+                        seed=23)
+    d = synth.draw_gqa_fp8(sh, k_scale, v_scale, device=DEV)
+    kn, vn = special_rows(B, h_kv, d_h, k_scale), special_rows(B, h_kv, d_h, v_scale)
+    pos = torch.tensor([0, 39, 7, 16, 31], dtype=torch.int32, device=DEV)
+    bt = d.get("block_table")
+    refK, refV = oracle.kv_append_fp8(synth.host_bits(d["K8"]), synth.host_bits(d["V8"]),
+                                      synth.host_bits(kn), synth.host_bits(vn), k_scale, v_scale,
+                                      pos.cpu().numpy(), block_table=d.get("block_table_host"))
+    A.kv_cache_append_fp8(d["K8"], d["V8"], kn, vn, k_scale, v_scale, pos, bt,
+                          0 if bt is None else bt.shape[1], 16,
+                          0 if bt is None else d["K8"].shape[0], B, s_max, h_kv, d_h)
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.host_bits(d["K8"]), refK)
+    assert np.array_equal(synth.host_bits(d["V8"]), refV)

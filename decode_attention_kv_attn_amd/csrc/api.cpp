@@ -60,7 +60,10 @@ struct GqaPlan {
     size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
-GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h)
+#ifndef GQA_F8_TARGET
+#define GQA_F8_TARGET 512
+#endif
+GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, bool f8 = false)
 {
     GqaPlan P{};
     const int g = h / h_kv;
@@ -72,7 +75,7 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h)
         // two wavefronts at least: both issue the tile DMA, which keeps more
         // loads in flight per CU than one wavefront's counter allows
         P.NW = g <= 32 ? 2 : 4;
-        target = 512;
+        target = f8 ? GQA_F8_TARGET : 512;
     } else {
         P.HG = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
         P.n_hg = g / P.HG;
@@ -102,6 +105,7 @@ bool gqa_uses_mfma(int h, int h_kv, int b) { return b == 2 && h / h_kv <= 64; }
 
 GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b)
 {
+    if (b == 1) return plan_gqa_path(true, B, s_max, h, h_kv, d_h, true);
     return plan_gqa_path(gqa_uses_mfma(h, h_kv, b), B, s_max, h, h_kv, d_h);
 }
 
@@ -172,7 +176,8 @@ size_t attn_decode_workspace_bytes(int is_mla, int B, int s_max, int h, int h_kv
     // the storage type is not an argument: size for whichever kernel runs
     const size_t a = plan_gqa_path(true, B, s_max, h, h_kv, d_h_or_dc).ws_bytes;
     const size_t v = plan_gqa_path(false, B, s_max, h, h_kv, d_h_or_dc).ws_bytes;
-    return a > v ? a : v;
+    const size_t f = plan_gqa_path(true, B, s_max, h, h_kv, d_h_or_dc, true).ws_bytes;
+    return a > v ? (a > f ? a : f) : (v > f ? v : f);
 }
 
 const char* attn_last_error(void) { return g_err.c_str(); }
@@ -236,7 +241,7 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
         if (rc) return rc;
     }
     if (B == 0) return ATTN_OK;
-    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b == 1 ? 2 : b);
+    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b);
     if (P.ws_bytes && (!workspace || workspace_bytes < P.ws_bytes))
         return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
                     workspace ? workspace_bytes : (size_t)0);

@@ -39,6 +39,9 @@ namespace attn {
 #ifndef GQA_MFMA_NBUF
 #define GQA_MFMA_NBUF 4
 #endif
+#ifndef GQA_MFMA_NBUF_F8
+#define GQA_MFMA_NBUF_F8 4
+#endif
 
 template <int D, bool F8>
 struct MfmaCfg {
@@ -48,7 +51,7 @@ struct MfmaCfg {
     static constexpr int KT = T * RB;          // bytes of a K (or V) tile
     static constexpr int RPO = 1024 / RB;      // rows per DMA instruction
     static constexpr int OPS = 2 * KT / 1024;  // DMA instructions per tile (K, then V)
-    static constexpr int NBUF = GQA_MFMA_NBUF; // ring depth (NBUF - 1 tiles in flight)
+    static constexpr int NBUF = F8 ? GQA_MFMA_NBUF_F8 : GQA_MFMA_NBUF;   // ring depth (NBUF - 1 tiles in flight)
     static constexpr int KS = D / 32;          // score K steps
     static constexpr int MC = D / 16;          // value M tiles (head dimensions)
 };

@@ -155,9 +155,13 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
                     size_t workspace_bytes, void* stream);
 
 /*
- * FP8 caches.  An 8-bit cache halves the bytes per token that decode streams
- * (the pages name it as the next step and leave the scale granularity open).
- * Reading taken here: OCP E4M3 codes ("e4m3fn": bias 7, subnormals, no
+ * FP8 caches.  An 8-bit cache halves the bytes per token that decode streams.
+ * "Multi-Head Latent Attention (MLA): Mathematical Foundations ...", section
+ * "High-Throughput Serving Kernels: FlashMLA and SGLang", names E4M3 codes
+ * with scaling factors for a decode cache; "MLA: why one latent can replace a
+ * multi-head KV cache", section "MLA and KV-cache quantization stack" (by
+ * gloss), treats the element width as independent of the head layout and
+ * leaves the scale granularity open.  Reading taken here: OCP E4M3 codes ("e4m3fn": bias 7, subnormals, no
  * infinities, 0x7F / 0xFF NaN, largest finite 448), one byte per element,
  * with one fp32 scale per tensor: element value = code * scale.  The rows and
  * layouts are those of the bf16 caches with b = 1.

@@ -74,6 +74,8 @@ def _load():
         lib.ref_kv_append_fp8.restype = I
         lib.ref_kv_append_fp8.argtypes = [P, P, P, P, C.c_float, C.c_float, P, P, I, I, I, I,
                                           I, I]
+        lib.ref_merge_partials.restype = I
+        lib.ref_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I]
         _lib = lib
     return _lib
 
@@ -304,3 +306,27 @@ def kv_append_fp8(cache_k, cache_v, k_new, v_new, k_scale, v_scale, pos, block_t
     if rc != 0:
         raise ValueError(f"ref_kv_append_fp8 rejected its arguments ({rc})")
     return ck, cv
+
+
+def merge_partials(o_parts, lse_parts, b):
+    """Merge decode outputs over disjoint token slices of the same sequences.
+
+    o_parts [n,B,h,d] stored bits (uint16 bf16 or float32), lse_parts [n,B,h]
+    float32 (-inf for an empty slice).  Returns (out [B,h,d] float64, lse
+    [B,h] float64): lse = ln sum_k exp(lse_k), out = sum_k exp(lse_k - lse)
+    o_k ("What FlashMLA solves is not the model formula itself",
+    charlestar.github.io MLA page: per-block maximum, normaliser and output,
+    combined stably).
+    """
+    o_parts = _stored(o_parts, b)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float32)
+    n, B, h, d = o_parts.shape
+    if lse_parts.shape != (n, B, h):
+        raise ValueError("lse_parts must be [n, B, h]")
+    out = np.zeros((B, h, d), dtype=np.float64)
+    lse = np.zeros((B, h), dtype=np.float64)
+    rc = _load().ref_merge_partials(_ptr(out), _ptr(lse), _ptr(o_parts), _ptr(lse_parts),
+                                    n, B, h, d, b)
+    if rc != 0:
+        raise ValueError(f"ref_merge_partials rejected its arguments ({rc})")
+    return out, lse

@@ -32,7 +32,10 @@
  *  - "MLA: why one latent can replace a multi-head KV cache"
  *    (charlestar.github.io): "First matrix absorption", "Second matrix
  *    absorption", "What a paged KV cache block holds" (row = [c_KV | k_R]),
- *    "Correctness validation ..." (explicit expansion as the slow reference).
+ *    "Correctness validation ..." (explicit expansion as the slow reference),
+ *    "What FlashMLA solves is not the model formula itself" (each block of
+ *    keys yields its own maximum, normaliser and output, and the blocks are
+ *    combined stably: the merge of ref_merge_partials).
  *
  * Readings where the pages are silent (listed again in the design notes):
  *  - query head i uses KV head floor(i / g) (consecutive heads share);
@@ -510,6 +513,49 @@ int ref_kv_append_fp8(uint8_t* cache_k, uint8_t* cache_v, const void* k_new, con
                 cache_v[row * n + e] = (uint8_t)ref_fp8_e4m3_encode(xv * v_inv_scale);
             }
         }
+    }
+    return OR_OK;
+}
+
+/*
+ * Merge of attention computed over disjoint slices of the same tokens.
+ * Slice k of row r (= b * h + i) holds o_k, the softmax-weighted output over
+ * its own tokens, and lse_k = ln sum_{t in k} exp(z_t) (-inf for an empty
+ * slice).  Because exp(z_t) = exp(lse_k) * (weight of t inside slice k), the
+ * output over all tokens is
+ *   lse = ln sum_k exp(lse_k),  o = sum_k exp(lse_k - lse) o_k,
+ * evaluated with M = max_k lse_k subtracted first.  A row whose slices are
+ * all empty gives o = 0 and lse = -inf, as an empty decode does.
+ *   out [B, h, d] double, lse [B, h] double (nullable)
+ *   o_parts [n, B, h, d] stored dtype b, lse_parts [n, B, h] fp32
+ */
+int ref_merge_partials(double* out, double* lse, const void* o_parts, const float* lse_parts,
+                       int n, int B, int h, int d, int b)
+{
+    if (!out || !o_parts || !lse_parts) return OR_EINVAL;
+    if (n <= 0 || B < 0 || h <= 0 || d <= 0 || (b != 2 && b != 4)) return OR_EINVAL;
+    const long rows = (long)B * h;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; r++) {
+        double* o = out + (size_t)r * d;
+        double M = -INFINITY;
+        for (int k = 0; k < n; k++) {
+            const double x = (double)lse_parts[(size_t)k * rows + r];
+            if (x > M) M = x;
+        }
+        for (int c = 0; c < d; c++) o[c] = 0.0;
+        if (M == -INFINITY) {
+            if (lse) lse[r] = -INFINITY;
+            continue;
+        }
+        double L = 0.0;
+        for (int k = 0; k < n; k++) {
+            const double w = exp((double)lse_parts[(size_t)k * rows + r] - M);
+            L += w;
+            for (int c = 0; c < d; c++) o[c] += w * ld(o_parts, ((size_t)k * rows + r) * d + c, b);
+        }
+        for (int c = 0; c < d; c++) o[c] /= L;
+        if (lse) lse[r] = M + log(L);
     }
     return OR_OK;
 }

@@ -143,6 +143,62 @@ def gqa_fp8_alg_bytes(sh):
     return 2 * sum(sh.s) * sh.h_kv * sh.d_h + 2 * sh.B * sh.h * sh.d_h * 2
 
 
+def run_merge(n, B, h, d, steps, warmup, rotate=8):
+    """attn_merge_partials over n fp32 slice partials [n,B,h,d] (+ lse) into
+    fp32 [B,h,d]; input sets rotate so the Infinity Cache cannot hold them."""
+    import torch
+    import decode_attention_kv_attn_amd as A
+    g = torch.Generator(device="cuda").manual_seed(7)
+    sets = [(torch.randn((n, B, h, d), generator=g, device="cuda"),
+             torch.randn((n, B, h), generator=g, device="cuda") * 4) for _ in range(rotate)]
+    out = torch.empty((B, h, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, h), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    it = [0]
+
+    def call():
+        o, l = sets[it[0] % rotate]
+        it[0] += 1
+        A.attn_merge_partials(out, lse, o, l, n, B, h, d, 4, 4, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    alg = (n + 1) * B * h * (d + 1) * 4
+    return total_ms / steps, per, alg
+
+
+def run_dcp_gqa(name, n, steps, warmup):
+    """One GPU's share of context-parallel decode over n GPUs: the decode of
+    a 1/n token slice of every sequence, then the merge of n such partials."""
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = synth.configs()[name]
+    S = (sh.s_max + n - 1) // n
+    q = torch.randn((sh.B, sh.h, sh.d_h), device="cuda").to(torch.bfloat16)
+    K = torch.randn((sh.B, S, sh.h_kv, sh.d_h), device="cuda").to(torch.bfloat16)
+    V = torch.randn_like(K)
+    s = torch.full((sh.B,), S, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    parts_o = torch.empty((n, sh.B, sh.h, sh.d_h), dtype=torch.bfloat16, device="cuda")
+    parts_l = torch.zeros((n, sh.B, sh.h), dtype=torch.float32, device="cuda")
+    lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device="cuda")
+    wsb = A.attn_decode_workspace_bytes(0, sh.B, S, sh.h, sh.h_kv, sh.d_h)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def call():
+        # this GPU's slice writes its own row of the gathered partials; the
+        # other rows stand for the slices received from the other GPUs
+        A.attn_decode_gqa(parts_o[0], parts_l[0], q, K, V, s, None, 0, 16, 0, sh.B, S, sh.h,
+                          sh.h_kv, sh.d_h, 2, 0.0, ws, wsb, sp)
+        A.attn_merge_partials(out, lse, parts_o, parts_l, n, sh.B, sh.h, sh.d_h, 2, 2, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    return sh, S, total_ms / steps, per
+
+
 def run_mla(name, steps, warmup, rotate):
     import torch
     import synth
@@ -267,6 +323,7 @@ def main():
     ap.add_argument("--mla-config", default="deepseek_v3_mla")
     ap.add_argument("--no-mla", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-dcp", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -365,6 +422,22 @@ def main():
                           "speedup_vs_bf16": ms / fms}
         except Exception as e:  # the FP8 leg reports its own failure, the line still prints
             rec["fp8"] = {"error": str(e)[:200]}
+    if not args.no_dcp:
+        try:   # the exchange step of context-parallel decode, on one GPU
+            mms_, mper, malg = run_merge(8, 32, 128, 512, args.steps, args.warmup)
+            dsh, S, dms, dper = run_dcp_gqa("llama3_70b_gqa8_b1", 8, args.steps, args.warmup)
+            rec["dcp"] = {
+                "merge": {"workload": "attn_merge_partials: 8 slices of fp32 MLA latent partials "
+                                      "(B=32, h=128, d_c=512) + lse -> fp32",
+                          "us_per_call": mms_ * 1e3, "median_us": float(np.median(mper)) * 1e3,
+                          "alg_bytes_per_call": malg,
+                          "hbm_gbps": malg / (mms_ * 1e-3) / 1e9,
+                          "hbm_frac": malg / (mms_ * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                "gqa_slice": {"workload": f"{dsh.name}: one GPU's 1/8 token slice (s={S}) decode "
+                                          f"+ merge of 8 slice partials",
+                              "us_per_step": dms * 1e3, "median_us": float(np.median(dper)) * 1e3}}
+        except Exception as e:  # reports its own failure, the line still prints
+            rec["dcp"] = {"error": str(e)[:200]}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_gqa(sh, kept[0], args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -28,6 +28,7 @@ EXPORTED = (
     "attn_stream_read_probe",
     "kv_cache_append_fp8",
     "attn_decode_gqa_fp8",
+    "attn_merge_partials",
 )
 
 _lib = None
@@ -70,6 +71,8 @@ def lib():
         L.attn_decode_gqa_fp8.restype = I
         L.attn_decode_gqa_fp8.argtypes = [P, P, P, P, P, F, F, P, P, I, I, I, I, I, I, I, I, F,
                                           P, Z, P]
+        L.attn_merge_partials.restype = I
+        L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
     return _lib
 
@@ -150,6 +153,13 @@ def attn_decode_gqa_fp8(out, lse, q, cache_k, cache_v, k_scale, v_scale, s, bloc
                                    max_blocks, block_size, num_blocks, B, s_max, h, h_kv, d_h,
                                    float(scale), _p(workspace), int(workspace_bytes),
                                    _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_merge_partials(out, lse, o_parts, lse_parts, n_parts, B, h, d, b_parts, b_out,
+                        stream=None, check=True):
+    rc = lib().attn_merge_partials(_p(out), _p(lse), _p(o_parts), _p(lse_parts), n_parts, B, h,
+                                   d, b_parts, b_out, _stream(stream))
     return _check(rc) if check else rc
 
 
@@ -267,3 +277,19 @@ def decode_mla(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_siz
 
 def default_scale(d):
     return 1.0 / math.sqrt(d)
+
+
+def merge_partials(o_parts, lse_parts, out_dtype=None, lse=True, stream=None):
+    """Tensor form of attn_merge_partials: o_parts [n,B,h,d] (bf16 or fp32),
+    lse_parts [n,B,h] fp32 -> (out [B,h,d], lse [B,h] or None)."""
+    import torch
+    n, B, h, d = o_parts.shape
+    if tuple(lse_parts.shape) != (n, B, h) or lse_parts.dtype != torch.float32:
+        raise ValueError("lse_parts must be float32 [n, B, h]")
+    out_dtype = o_parts.dtype if out_dtype is None else out_dtype
+    bsz = {torch.bfloat16: 2, torch.float32: 4}
+    out = torch.empty((B, h, d), dtype=out_dtype, device=o_parts.device)
+    l = torch.empty((B, h), dtype=torch.float32, device=o_parts.device) if lse else None
+    attn_merge_partials(out, l, o_parts.contiguous(), lse_parts.contiguous(), n, B, h, d,
+                        bsz[o_parts.dtype], bsz[out_dtype], stream)
+    return out, l

@@ -406,6 +406,31 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     return ATTN_OK;
 }
 
+int attn_merge_partials(void* out, float* lse, const void* o_parts, const float* lse_parts,
+                        int n_parts, int B, int h, int d, int b_parts, int b_out, void* stream)
+{
+    if (!out || !o_parts || !lse_parts) return fail(ATTN_EINVAL, "out, o_parts and lse_parts must be non-null");
+    if (n_parts <= 0 || B < 0 || h <= 0 || d <= 0)
+        return fail(ATTN_EINVAL, "n_parts, h and d must be positive, B non-negative");
+    if ((b_parts != 2 && b_parts != 4) || (b_out != 2 && b_out != 4))
+        return fail(ATTN_ENOTSUP, "b_parts and b_out must be 2 (bf16) or 4 (fp32)");
+    if (d % 4 != 0 || d > 1024) return fail(ATTN_ENOTSUP, "d must be a multiple of 4, at most 1024");
+    if (((uintptr_t)out | (uintptr_t)o_parts) % 16 != 0 || (uintptr_t)lse_parts % 4 != 0 ||
+        (uintptr_t)lse % 4 != 0)
+        return fail(ATTN_EINVAL, "out and o_parts must be 16-byte aligned, lse arrays 4-byte aligned");
+    if (B == 0) return ATTN_OK;
+    attn::MergeParams p{};
+    p.out = out;
+    p.lse = lse;
+    p.o_parts = o_parts;
+    p.lse_parts = lse_parts;
+    p.rows = (long)B * h;
+    p.n = n_parts;
+    p.d = d;
+    const hipError_t e = attn::launch_merge_partials(p, b_parts == 4, b_out == 4, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : hip_fail(e, "merge launch");
+}
+
 int attn_stream_read_probe(const void* src, size_t bytes, unsigned int* sink, void* stream)
 {
     if (!src || !sink) return fail(ATTN_EINVAL, "null src or sink");

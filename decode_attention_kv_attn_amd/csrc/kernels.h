@@ -71,6 +71,17 @@ struct MlaParams {
 
 hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st);
 
+// merge of decode outputs over disjoint token slices
+struct MergeParams {
+    void* out;               // [rows, d] bf16 or fp32
+    float* lse;              // [rows] or null
+    const void* o_parts;     // [n, rows, d] bf16 or fp32
+    const float* lse_parts;  // [n, rows]
+    long rows;               // B * h
+    int n, d;                // d % 4 == 0, d <= 1024
+};
+hipError_t launch_merge_partials(const MergeParams& p, bool in_f32, bool out_f32, hipStream_t st);
+
 // read-bandwidth probe: kProbeGrid workgroups, bytes / kProbeGrid each (a
 // multiple of 16 KB)
 constexpr unsigned kProbeGrid = 2048;

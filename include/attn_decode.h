@@ -230,6 +230,37 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
                              int h, int d_c, int d_R, int d_nope, int d_v, int b, float scale,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_merge_partials -- combine decode results computed over disjoint token
+ * slices of the same sequences into the result over all their tokens: the
+ * exchange step of context-parallel decode, where each GPU holds a slice of
+ * every sequence's cache, runs attn_decode_gqa (or _fp8, or
+ * attn_decode_mla_absorbed) over it, and the per-slice out and lse are
+ * gathered.  "MHA -> MQA -> GQA -> MLA" names decode context parallelism
+ * (sharding the sequence axis, the route left once heads cannot be split);
+ * the combination is the stable merge of per-block maximum, normaliser and
+ * output of "MLA: why one latent can replace a multi-head KV cache", section
+ * "What FlashMLA solves is not the model formula itself":
+ *   lse[r] = ln sum_k exp(lse_parts[k, r]),
+ *   out[r] = sum_k exp(lse_parts[k, r] - lse[r]) o_parts[k, r].
+ * For MLA the per-slice out (after W_UV) merges the same way as u~, since
+ * W_UV is linear.
+ *   out       : [B, h, d], dtype b_out (2 = bf16, 4 = fp32).
+ *   lse       : [B, h] fp32 (natural log); may be NULL.
+ *   o_parts   : [n_parts, B, h, d], dtype b_parts; slice k is one decode's
+ *               out.
+ *   lse_parts : [n_parts, B, h] fp32, slice k's lse; -inf marks an empty
+ *               slice, whose o_parts row is not read into the sum.
+ * A row whose slices are all empty gives out = 0 and lse = -inf.  All
+ * pointers are device memory owned by the caller; out and o_parts 16-byte
+ * aligned.  Accumulation is fp32.  Asynchronous on `stream`.
+ * Supported: d a multiple of 4 up to 1024.  Others: ENOTSUP.
+ * Errors: EINVAL (null pointer, n_parts <= 0, B < 0, h or d <= 0,
+ * misalignment), ENOTSUP (b_parts or b_out not 2 or 4, d), EHIP.
+ */
+int attn_merge_partials(void* out, float* lse, const void* o_parts, const float* lse_parts,
+                        int n_parts, int B, int h, int d, int b_parts, int b_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

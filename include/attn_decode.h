@@ -236,8 +236,9 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
  * exchange step of context-parallel decode, where each GPU holds a slice of
  * every sequence's cache, runs attn_decode_gqa (or _fp8, or
  * attn_decode_mla_absorbed) over it, and the per-slice out and lse are
- * gathered.  "MHA -> MQA -> GQA -> MLA" names decode context parallelism
- * (sharding the sequence axis, the route left once heads cannot be split);
+ * gathered.  "MHA -> MQA -> GQA -> MLA", section "Where the head count
+ * becomes bytes", names decode context parallelism (sharding the sequence
+ * axis, the route left once heads cannot be split);
  * the combination is the stable merge of per-block maximum, normaliser and
  * output of "MLA: why one latent can replace a multi-head KV cache", section
  * "What FlashMLA solves is not the model formula itself":

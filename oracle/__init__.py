@@ -74,6 +74,9 @@ def _load():
         lib.ref_kv_append_fp8.restype = I
         lib.ref_kv_append_fp8.argtypes = [P, P, P, P, C.c_float, C.c_float, P, P, I, I, I, I,
                                           I, I]
+        lib.ref_gqa_decode_multi.restype = I
+        lib.ref_gqa_decode_multi.argtypes = [P, P, P, P, P, D, D, P, P, I, I, I, I, I, I, I, I,
+                                             I, D]
         lib.ref_merge_partials.restype = I
         lib.ref_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I]
         _lib = lib
@@ -329,4 +332,42 @@ def merge_partials(o_parts, lse_parts, b):
                                     n, B, h, d, b)
     if rc != 0:
         raise ValueError(f"ref_merge_partials rejected its arguments ({rc})")
+    return out, lse
+
+
+def gqa_decode_multi(q, K, V, s, b, block_table=None, block_size=16, scale=None,
+                     k_scale=1.0, v_scale=1.0):
+    """Reference decode of q_len new tokens per sequence (causal among them).
+
+    q [B,q_len,h,d_h]; K, V as gqa_decode (b = 2 or 4: stored bits; b = 1:
+    E4M3 codes, uint8, with per-tensor scales and bf16 q).  s[b] counts the
+    cached tokens including the q_len new ones; position jq sees the first
+    s[b] - q_len + 1 + jq tokens.  Returns (out [B,q_len,h,d_h] float64,
+    lse [B,q_len,h] float64).
+    """
+    q = _stored(q, 2 if b == 1 else b)
+    if b == 1:
+        K = np.ascontiguousarray(K, dtype=np.uint8)
+        V = np.ascontiguousarray(V, dtype=np.uint8)
+    else:
+        K, V = _stored(K, b), _stored(V, b)
+    B, q_len, h, d_h = q.shape
+    h_kv = K.shape[2]
+    s = _i32(s)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max, max_blocks, bs = K.shape[1], 0, 0
+    else:
+        s_max, max_blocks, bs = 0, bt.shape[1], block_size
+        _check_table(bt, K.shape[0] * K.shape[1], bs, s)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    out = np.zeros((B, q_len, h, d_h), dtype=np.float64)
+    lse = np.zeros((B, q_len, h), dtype=np.float64)
+    rc = _load().ref_gqa_decode_multi(_ptr(out), _ptr(lse), _ptr(q), _ptr(K), _ptr(V),
+                                      float(np.float32(k_scale)), float(np.float32(v_scale)),
+                                      _ptr(s), _ptr(bt), max_blocks, bs, B, q_len, s_max, h,
+                                      h_kv, d_h, b, float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_gqa_decode_multi rejected its arguments ({rc})")
     return out, lse

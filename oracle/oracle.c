@@ -559,3 +559,82 @@ int ref_merge_partials(double* out, double* lse, const void* o_parts, const floa
     }
     return OR_OK;
 }
+
+/* one cache element: b = 1 -> E4M3 code times its scale, else stored bits */
+static double ld_cache(const void* p, size_t idx, int b, double scale)
+{
+    if (b == 1) return ld_fp8((const uint8_t*)p, idx, scale);
+    return ld(p, idx, b);
+}
+
+/*
+ * Decode attention for q_len new tokens per sequence at once (the tokens a
+ * speculative step verifies; "MLA: why one latent can replace a multi-head
+ * KV cache" lists their number among the inputs of a decode kernel).
+ * All q_len tokens are already in the cache, so s_b counts them; query
+ * position jq (0-based) sits at cache position s_b - q_len + jq and attends
+ * to the n = s_b - q_len + 1 + jq tokens up to and including itself (causal
+ * among the new tokens).  n <= 0 gives out = 0, lse = -inf.
+ *   out [B, q_len, h, d_h] double, lse [B, q_len, h] double (nullable)
+ *   q   [B, q_len, h, d_h]   bf16 bits when b = 1, else stored dtype b
+ *   k,v as ref_gqa_decode; b = 1: E4M3 codes, element = code * k_scale
+ *       (v_scale), else k_scale and v_scale are ignored
+ */
+int ref_gqa_decode_multi(double* out, double* lse, const void* q, const void* k, const void* v,
+                         double k_scale, double v_scale, const int32_t* s,
+                         const int32_t* block_table, int max_blocks, int block_size, int B,
+                         int q_len, int s_max, int h, int h_kv, int d_h, int b, double scale)
+{
+    if (!out || !q || !k || !v || !s) return OR_EINVAL;
+    if (B < 0 || q_len < 1 || h <= 0 || h_kv <= 0 || d_h <= 0 || (h % h_kv) != 0)
+        return OR_EINVAL;
+    if (b != 1 && b != 2 && b != 4) return OR_EINVAL;
+    if (block_table && (block_size <= 0 || max_blocks <= 0)) return OR_EINVAL;
+    const int g = h / h_kv, bq = b == 1 ? 2 : b;
+    const long rows = (long)B * q_len * h;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long r = 0; r < rows; r++) {
+        const int bb = (int)(r / ((long)q_len * h));
+        const int jq = (int)((r / h) % q_len), i = (int)(r % h), j = i / g;
+        const int sb = s[bb];
+        double* o = out + (size_t)r * d_h;
+        if (sb < 0 || (!block_table && sb > s_max) ||
+            (block_table && sb > max_blocks * block_size) ||
+            !table_ok(block_table, max_blocks, block_size, bb, sb)) {
+            bad = 1;
+            continue;
+        }
+        const int n = sb - (q_len - 1 - jq);   /* visible tokens of this position */
+        if (n <= 0) {
+            for (int d = 0; d < d_h; d++) o[d] = 0.0;
+            if (lse) lse[r] = -INFINITY;
+            continue;
+        }
+        double* z = (double*)malloc(sizeof(double) * (size_t)n * 2);
+        double* p = z + n;
+        const size_t qoff = (size_t)r * d_h;
+        for (int t = 0; t < n; t++) {
+            const size_t koff =
+                (row_of(block_table, max_blocks, block_size, s_max, bb, t) * h_kv + j) * d_h;
+            double acc = 0.0;
+            for (int d = 0; d < d_h; d++) acc += ld(q, qoff + d, bq) * ld_cache(k, koff + d, b, k_scale);
+            z[t] = scale * acc;
+        }
+        double m;
+        const double l = softmax_weights(z, n, p, &m);
+        for (int d = 0; d < d_h; d++) {
+            double acc = 0.0;
+            for (int t = 0; t < n; t++) {
+                const size_t voff =
+                    (row_of(block_table, max_blocks, block_size, s_max, bb, t) * h_kv + j) *
+                    d_h;
+                acc += p[t] * ld_cache(v, voff + d, b, v_scale);
+            }
+            o[d] = acc / l;
+        }
+        if (lse) lse[r] = m + log(l);
+        free(z);
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}

@@ -29,6 +29,9 @@ EXPORTED = (
     "kv_cache_append_fp8",
     "attn_decode_gqa_fp8",
     "attn_merge_partials",
+    "attn_decode_gqa_multi",
+    "attn_decode_gqa_multi_fp8",
+    "attn_decode_gqa_multi_workspace_bytes",
 )
 
 _lib = None
@@ -71,6 +74,14 @@ def lib():
         L.attn_decode_gqa_fp8.restype = I
         L.attn_decode_gqa_fp8.argtypes = [P, P, P, P, P, F, F, P, P, I, I, I, I, I, I, I, I, F,
                                           P, Z, P]
+        L.attn_decode_gqa_multi.restype = I
+        L.attn_decode_gqa_multi.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F,
+                                            P, Z, P]
+        L.attn_decode_gqa_multi_fp8.restype = I
+        L.attn_decode_gqa_multi_fp8.argtypes = [P, P, P, P, P, F, F, P, P, I, I, I, I, I, I, I,
+                                                I, I, F, P, Z, P]
+        L.attn_decode_gqa_multi_workspace_bytes.restype = Z
+        L.attn_decode_gqa_multi_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -154,6 +165,31 @@ def attn_decode_gqa_fp8(out, lse, q, cache_k, cache_v, k_scale, v_scale, s, bloc
                                    float(scale), _p(workspace), int(workspace_bytes),
                                    _stream(stream))
     return _check(rc) if check else rc
+
+
+def attn_decode_gqa_multi(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
+                          num_blocks, B, q_len, s_max, h, h_kv, d_h, b, scale, workspace,
+                          workspace_bytes, stream=None, check=True):
+    rc = lib().attn_decode_gqa_multi(_p(out), _p(lse), _p(q), _p(cache_k), _p(cache_v), _p(s),
+                                     _p(block_table), max_blocks, block_size, num_blocks, B,
+                                     q_len, s_max, h, h_kv, d_h, b, float(scale), _p(workspace),
+                                     int(workspace_bytes), _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_gqa_multi_fp8(out, lse, q, cache_k, cache_v, k_scale, v_scale, s, block_table,
+                              max_blocks, block_size, num_blocks, B, q_len, s_max, h, h_kv, d_h,
+                              scale, workspace, workspace_bytes, stream=None, check=True):
+    rc = lib().attn_decode_gqa_multi_fp8(_p(out), _p(lse), _p(q), _p(cache_k), _p(cache_v),
+                                         float(k_scale), float(v_scale), _p(s), _p(block_table),
+                                         max_blocks, block_size, num_blocks, B, q_len, s_max, h,
+                                         h_kv, d_h, float(scale), _p(workspace),
+                                         int(workspace_bytes), _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_gqa_multi_workspace_bytes(B, q_len, s_max, h, h_kv, d_h):
+    return int(lib().attn_decode_gqa_multi_workspace_bytes(B, q_len, s_max, h, h_kv, d_h))
 
 
 def attn_merge_partials(out, lse, o_parts, lse_parts, n_parts, B, h, d, b_parts, b_out,
@@ -292,4 +328,34 @@ def merge_partials(o_parts, lse_parts, out_dtype=None, lse=True, stream=None):
     l = torch.empty((B, h), dtype=torch.float32, device=o_parts.device) if lse else None
     attn_merge_partials(out, l, o_parts.contiguous(), lse_parts.contiguous(), n, B, h, d,
                         bsz[o_parts.dtype], bsz[out_dtype], stream)
+    return out, l
+
+
+def decode_gqa_multi(q, K, V, s, block_table=None, block_size=16, s_max=None, scale=0.0,
+                     lse=True, k_scale=None, v_scale=None, workspace=None, stream=None):
+    """Decode of q_len new tokens per sequence: q [B,q_len,h,d_h] bf16.
+
+    K/V bf16, or uint8 E4M3 codes when k_scale and v_scale are given.
+    Returns (out [B,q_len,h,d_h] bf16, lse [B,q_len,h] fp32 or None).
+    """
+    import torch
+    B, q_len, h, d_h = q.shape
+    h_kv = K.shape[2]
+    if block_table is None:
+        s_max = K.shape[1] if s_max is None else s_max
+        max_blocks, num_blocks = 0, 0
+    else:
+        max_blocks, num_blocks = block_table.shape[1], K.shape[0]
+        s_max = max_blocks * block_size if s_max is None else s_max
+    out = torch.empty_like(q)
+    l = torch.empty((B, q_len, h), dtype=torch.float32, device=q.device) if lse else None
+    ws = workspace or Workspace(q.device)
+    wb, wn = ws.get(attn_decode_gqa_multi_workspace_bytes(B, q_len, s_max, h, h_kv, d_h))
+    if k_scale is None:
+        attn_decode_gqa_multi(out, l, q, K, V, s, block_table, max_blocks, block_size,
+                              num_blocks, B, q_len, s_max, h, h_kv, d_h, 2, scale, wb, wn, stream)
+    else:
+        attn_decode_gqa_multi_fp8(out, l, q, K, V, k_scale, v_scale, s, block_table, max_blocks,
+                                  block_size, num_blocks, B, q_len, s_max, h, h_kv, d_h, scale,
+                                  wb, wn, stream)
     return out, l

@@ -54,27 +54,34 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Either way no split is longer than 4096 tokens (with mixed lengths the
 // longest sequences would otherwise set the kernel time) or shorter than 512
 // tokens, and split lengths are multiples of 64 tokens.
+// Several query positions per sequence (q_len > 1) always take the matrix
+// cores: the g * q_len rows of a work item fill the 16-row tiles, in blocks
+// of 64 rows (n_rb blocks, each its own workgroup, when g * q_len > 64).
 struct GqaPlan {
     bool mfma;
-    int HG, n_hg, NW, n_split, chunk;
+    int HG, n_hg, NW, n_split, chunk, n_rb;
     size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
 #ifndef GQA_F8_TARGET
 #define GQA_F8_TARGET 512
 #endif
-GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, bool f8 = false)
+GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, bool f8 = false,
+                      int q_len = 1)
 {
     GqaPlan P{};
     const int g = h / h_kv;
+    const int rows = g * q_len;
     P.mfma = mfma;
+    P.n_rb = 1;
     long long target;
     if (mfma) {
         P.HG = g;
         P.n_hg = 1;
+        P.n_rb = (rows + 63) / 64;
         // two wavefronts at least: both issue the tile DMA, which keeps more
         // loads in flight per CU than one wavefront's counter allows
-        P.NW = g <= 32 ? 2 : 4;
+        P.NW = rows <= 32 ? 2 : 4;
         target = f8 ? GQA_F8_TARGET : 512;
     } else {
         P.HG = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
@@ -83,7 +90,7 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
         target = 2048;
     }
     const long long T = 64, min_chunk = 512, max_chunk = 4096;
-    const long long units = (long long)B * h_kv * P.n_hg;
+    const long long units = (long long)B * h_kv * P.n_hg * P.n_rb;
     long long ns = units > 0 ? cdiv(target, units) : 1;
     if (s_max > 0 && ns < cdiv(s_max, max_chunk)) ns = cdiv(s_max, max_chunk);
     const long long ns_max = s_max > 0 ? cdiv(s_max, min_chunk) : 1;
@@ -94,8 +101,8 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
     P.n_split = (int)ns;
     P.chunk = (int)chunk;
     if (P.n_split > 1) {
-        P.part_o_bytes = align256((size_t)B * h * P.n_split * d_h * sizeof(float));
-        P.part_ml_bytes = align256((size_t)B * h * P.n_split * 2 * sizeof(float));
+        P.part_o_bytes = align256((size_t)B * q_len * h * P.n_split * d_h * sizeof(float));
+        P.part_ml_bytes = align256((size_t)B * q_len * h * P.n_split * 2 * sizeof(float));
     }
     P.ws_bytes = P.part_o_bytes + P.part_ml_bytes;
     return P;
@@ -103,9 +110,10 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
 
 bool gqa_uses_mfma(int h, int h_kv, int b) { return b == 2 && h / h_kv <= 64; }
 
-GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b)
+GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b, int q_len = 1)
 {
-    if (b == 1) return plan_gqa_path(true, B, s_max, h, h_kv, d_h, true);
+    if (b == 1) return plan_gqa_path(true, B, s_max, h, h_kv, d_h, true, q_len);
+    if (q_len > 1) return plan_gqa_path(true, B, s_max, h, h_kv, d_h, false, q_len);
     return plan_gqa_path(gqa_uses_mfma(h, h_kv, b), B, s_max, h, h_kv, d_h);
 }
 
@@ -222,7 +230,7 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
                const int32_t* s, const int32_t* block_table, int max_blocks, int block_size,
                int num_blocks, int B, int s_max, int h, int h_kv, int d_h, int b, float scale,
                float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-               void* stream)
+               void* stream, int q_len = 1)
 {
     if (!out || !q || !cache_k || !cache_v || !s)
         return fail(ATTN_EINVAL, "null out, q, cache_k, cache_v or s");
@@ -236,12 +244,14 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
         return fail(ATTN_ENOTSUP, "unsupported (b=%d, d_h=%d)", b, d_h);
     if (b == 1 && h / h_kv > 64)
         return fail(ATTN_ENOTSUP, "FP8 caches support h / h_kv <= 64 (got %d)", h / h_kv);
+    if (q_len < 1 || q_len > 64) return fail(ATTN_EINVAL, "q_len must be 1 .. 64 (got %d)", q_len);
+    if (q_len > 1 && b == 4) return fail(ATTN_ENOTSUP, "q_len > 1 needs a bf16 or FP8 cache");
     if (block_table || s_max > 0) {
         int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
         if (rc) return rc;
     }
     if (B == 0) return ATTN_OK;
-    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b);
+    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b, q_len);
     if (P.ws_bytes && (!workspace || workspace_bytes < P.ws_bytes))
         return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
                     workspace ? workspace_bytes : (size_t)0);
@@ -265,10 +275,12 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     p.n_hg = P.n_hg;
     p.n_split = P.n_split;
     p.chunk = P.chunk;
+    p.q_len = q_len;
+    p.n_rb = P.n_rb;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_h);
     p.scale_log2 = sc * k_scale * 1.4426950408889634f;
     p.v_scale = v_scale;
-    const long long grid = (long long)B * h_kv * P.n_hg * P.n_split;
+    const long long grid = (long long)B * h_kv * P.n_hg * P.n_split * P.n_rb;
     if (grid >= (1LL << 31)) return fail(ATTN_ENOTSUP, "problem too large for one launch");
     hipError_t e = P.mfma ? attn::launch_gqa_mfma(p, d_h, P.NW, block_table != nullptr, b == 1,
                                                   (unsigned)grid, (hipStream_t)stream)
@@ -404,6 +416,42 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     if (e == hipErrorNotSupported) return fail(ATTN_ENOTSUP, "MLA kernels not built");
     if (e != hipSuccess) return hip_fail(e, "attn_decode_mla_absorbed launch");
     return ATTN_OK;
+}
+
+int attn_decode_gqa_multi(void* out, float* lse, const void* q, const void* cache_k,
+                          const void* cache_v, const int32_t* s, const int32_t* block_table,
+                          int max_blocks, int block_size, int num_blocks, int B, int q_len,
+                          int s_max, int h, int h_kv, int d_h, int b, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream)
+{
+    if (b != 2) return fail(ATTN_ENOTSUP, "attn_decode_gqa_multi needs a bf16 cache (b = 2)");
+    return decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
+                      num_blocks, B, s_max, h, h_kv, d_h, b, scale, 1.f, 1.f, workspace,
+                      workspace_bytes, stream, q_len);
+}
+
+int attn_decode_gqa_multi_fp8(void* out, float* lse, const void* q, const void* cache_k,
+                              const void* cache_v, float k_scale, float v_scale, const int32_t* s,
+                              const int32_t* block_table, int max_blocks, int block_size,
+                              int num_blocks, int B, int q_len, int s_max, int h, int h_kv,
+                              int d_h, float scale, void* workspace, size_t workspace_bytes,
+                              void* stream)
+{
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || isinf(k_scale) || isinf(v_scale))
+        return fail(ATTN_EINVAL, "k_scale and v_scale must be positive and finite");
+    return decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
+                      num_blocks, B, s_max, h, h_kv, d_h, 1, scale, k_scale, v_scale, workspace,
+                      workspace_bytes, stream, q_len);
+}
+
+size_t attn_decode_gqa_multi_workspace_bytes(int B, int q_len, int s_max, int h, int h_kv, int d_h)
+{
+    if (B <= 0 || q_len < 1 || q_len > 64 || h <= 0 || h_kv <= 0 || h % h_kv || d_h <= 0 ||
+        s_max < 0)
+        return 0;
+    const size_t a = plan_gqa_path(true, B, s_max, h, h_kv, d_h, false, q_len).ws_bytes;
+    const size_t f = plan_gqa_path(true, B, s_max, h, h_kv, d_h, true, q_len).ws_bytes;
+    return a > f ? a : f;
 }
 
 int attn_merge_partials(void* out, float* lse, const void* o_parts, const float* lse_parts,

@@ -430,7 +430,7 @@ static void launch_combine_d(const GqaParams& p, unsigned cg, hipStream_t st)
 
 hipError_t launch_gqa_combine(const GqaParams& p, int d_h, bool f32, hipStream_t st)
 {
-    const unsigned cg = (unsigned)(p.B * p.h);
+    const unsigned cg = (unsigned)(p.B * p.q_len * p.h);
     if (f32) launch_combine_d<64, true>(p, cg, st);
     else if (d_h == 64) launch_combine_d<64, false>(p, cg, st);
     else launch_combine_d<128, false>(p, cg, st);

@@ -127,35 +127,48 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     // block, run under one L2; a contiguous cache streams faster in plain
     // order (measured).
     int w = PAGED ? xcd_major(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    const int rb = w % p.n_rb;
+    w /= p.n_rb;
     const int j = w % p.h_kv;
     w /= p.h_kv;
     const int split = w % p.n_split;
     const int b = w / p.n_split;
     const int g = p.h / p.h_kv;
-    const int nh = min(16, g - 16 * wave);          // query heads of this wavefront
+    // The rows of a work item are the (query position jq, head of the group)
+    // pairs, r = jq * g + gi: g rows for one new token, g * q_len when
+    // several new tokens are verified at once.  Row block rb holds rows
+    // 64 rb .. 64 rb + 63, wavefront w rows 16 w .. 16 w + 15 of them.
+    const int r0 = 64 * rb + 16 * wave;
+    const int nh = min(16, g * p.q_len - r0);       // rows of this wavefront
     const bool active = nh > 0;
-    const int head = j * g + 16 * wave + li;        // this lane's head when li < nh
-    const bool hv = li < nh;
+    const bool hv = li < nh;                        // this lane's row exists
+    const int r = hv ? r0 + li : r0;
+    const int jq = r / g;
+    const int head = j * g + r % g;
+    const size_t orow = (size_t)(b * p.q_len + jq) * p.h + head;   // row of q, out and lse
 
     const int32_t* __restrict__ s_len = p.s;
     int n = __builtin_amdgcn_readfirstlane(s_len[b]);
     n = min(max(n, 0), p.s_max);
     const int t0 = split * p.chunk;
     const int t1 = min(n, t0 + p.chunk);
+    // query position jq sits at cache position n - q_len + jq and sees the
+    // tokens before it and itself (causal among the new tokens)
+    const int tl = min(t1, n - (p.q_len - 1 - jq));
 
     if (t0 >= t1) {   // nothing to attend to in this split
         if (active && hv) {
             if (p.n_split > 1) {
                 if (G == 0) {
-                    float* ml = p.part_ml + ((size_t)(b * p.h + head) * p.n_split + split) * 2;
+                    float* ml = p.part_ml + (orow * p.n_split + split) * 2;
                     ml[0] = -INFINITY;
                     ml[1] = 0.f;
                 }
             } else {
-                uint16_t* o = (uint16_t*)p.out + (size_t)(b * p.h + head) * D;
+                uint16_t* o = (uint16_t*)p.out + orow * D;
 #pragma unroll
                 for (int mc = 0; mc < C::MC; mc++) *(uint2*)(o + 16 * mc + 4 * G) = make_uint2(0, 0);
-                if (G == 0 && p.lse) p.lse[b * p.h + head] = -INFINITY;
+                if (G == 0 && p.lse) p.lse[orow] = -INFINITY;
             }
         }
         return;
@@ -224,7 +237,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     }
     bf16x8 Qf[C::KS];
     {
-        const uint16_t* qrow = (const uint16_t*)p.q + (size_t)(b * p.h + head) * D + 8 * G;
+        const uint16_t* qrow = (const uint16_t*)p.q + orow * D + 8 * G;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ks++)
             Qf[ks] = (active && hv) ? *(const bf16x8*)(qrow + 32 * ks)
@@ -284,7 +297,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int tok = tb + 16 * mt + 4 * G + e;
-                    z[mt][e] = tok < t1 ? S[mt][e] * p.scale_log2 : -INFINITY;
+                    z[mt][e] = tok < tl ? S[mt][e] * p.scale_log2 : -INFINITY;
                     lm = fmaxf(lm, z[mt][e]);
                 }
             lm = fmaxf(lm, xor16(lm));
@@ -293,14 +306,17 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
             const float mn = move ? lm : m;
             const float alpha = move ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
             m = mn;
+            // a row that has seen no visible token yet (possible only for the
+            // earlier of several query positions) keeps m = -inf: weights 0
+            const float mb = mn == -INFINITY ? 0.f : mn;
             uint32_t pk[4];
             float ps = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int e = 0; e < 4; e += 2) {
-                    const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mn),
-                                                    __builtin_amdgcn_exp2f(z[mt][e + 1] - mn));
+                    const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mb),
+                                                    __builtin_amdgcn_exp2f(z[mt][e + 1] - mb));
                     pk[mt * 2 + e / 2] = wv;
                     ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
                 }
@@ -328,15 +344,15 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         for (int mc = 0; mc < C::MC; mc++) O[mc] *= p.v_scale;
     }
     if (p.n_split == 1) {
-        const float inv = 1.f / l;
-        uint16_t* o = (uint16_t*)p.out + (size_t)(b * p.h + head) * D + 4 * G;
+        const float inv = l > 0.f ? 1.f / l : 0.f;   // l = 0: no visible token (0 and -inf)
+        uint16_t* o = (uint16_t*)p.out + orow * D + 4 * G;
 #pragma unroll
         for (int mc = 0; mc < C::MC; mc++)
             *(uint2*)(o + 16 * mc) = make_uint2(pack_bf16x2(O[mc][0] * inv, O[mc][1] * inv),
                                                 pack_bf16x2(O[mc][2] * inv, O[mc][3] * inv));
-        if (G == 0 && p.lse) p.lse[b * p.h + head] = (m + __log2f(l)) * kLn2;
+        if (G == 0 && p.lse) p.lse[orow] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     } else {
-        const size_t pi = (size_t)(b * p.h + head) * p.n_split + split;
+        const size_t pi = orow * p.n_split + split;
         float* po = p.part_o + pi * D + 4 * G;
 #pragma unroll
         for (int mc = 0; mc < C::MC; mc++)

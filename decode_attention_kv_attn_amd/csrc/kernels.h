@@ -15,11 +15,13 @@ struct GqaParams {
     const void* v;
     const int32_t* s;
     const int32_t* bt;   // nullptr: contiguous
-    float* part_o;       // [B, h, n_split, d_h]
-    float* part_ml;      // [B, h, n_split, 2]  (m in log2 units, l)
+    float* part_o;       // [B, q_len, h, n_split, d_h]
+    float* part_ml;      // [B, q_len, h, n_split, 2]  (m in log2 units, l)
     int max_blocks, bs_log2, num_blocks;
     int B, s_max, h, h_kv;
     int n_hg, n_split, chunk;
+    int q_len;           // query positions per sequence (matrix-core kernel only; 1 otherwise)
+    int n_rb;            // 64-row blocks per (b, KV head) work item (matrix-core kernel)
     float scale_log2;    // scale * log2(e) (times the K scale of an FP8 cache)
     float v_scale;       // V scale of an FP8 cache (1 otherwise)
 };

@@ -199,6 +199,48 @@ int attn_decode_gqa_fp8(void* out, float* lse, const void* q, const void* cache_
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_gqa_multi -- decode of q_len new tokens per sequence in one
+ * call, as a speculative step verifies several drafted tokens ("MLA: why
+ * one latent can replace a multi-head KV cache", section "MHA mode and MQA
+ * mode are execution forms" (by gloss), counts the tokens one speculative
+ * verification checks among what selects a decode kernel).  The q_len tokens are already appended, so s[b]
+ * counts them; query position jq (0-based) sits at cache position
+ * s[b] - q_len + jq and attends causally to the first s[b] - q_len + 1 + jq
+ * tokens:
+ *   out[b,jq,i] = sum_{t <= s_b - q_len + jq} softmax_t(scale q[b,jq,i] .
+ *                 K[b,t,j]) V[b,t,j],  j = floor(i / g).
+ * A position that sees no token (s[b] < q_len - jq) gives 0 and lse -inf.
+ *   out : [B, q_len, h, d_h] bf16;  lse : [B, q_len, h] fp32, may be NULL.
+ *   q   : [B, q_len, h, d_h] bf16.  Caches, table and lengths as
+ *         attn_decode_gqa (b = 2 only).
+ *   workspace : at least attn_decode_gqa_multi_workspace_bytes(B, q_len,
+ *         s_max, h, h_kv, d_h) bytes.
+ * Supported: d_h in {64, 128}, 1 <= q_len <= 64 (q_len = 1 equals
+ * attn_decode_gqa on the same inputs up to rounding order; any h / h_kv).
+ * Errors: as attn_decode_gqa; EINVAL for q_len outside 1 .. 64; ENOTSUP
+ * for b != 2.
+ */
+int attn_decode_gqa_multi(void* out, float* lse, const void* q, const void* cache_k,
+                          const void* cache_v, const int32_t* s, const int32_t* block_table,
+                          int max_blocks, int block_size, int num_blocks, int B, int q_len,
+                          int s_max, int h, int h_kv, int d_h, int b, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_gqa_multi_fp8 -- attn_decode_gqa_multi over FP8 (E4M3)
+ * caches with per-tensor scales, as attn_decode_gqa_fp8.  h / h_kv <= 64.
+ */
+int attn_decode_gqa_multi_fp8(void* out, float* lse, const void* q, const void* cache_k,
+                              const void* cache_v, float k_scale, float v_scale, const int32_t* s,
+                              const int32_t* block_table, int max_blocks, int block_size,
+                              int num_blocks, int B, int q_len, int s_max, int h, int h_kv,
+                              int d_h, float scale, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Workspace bytes for attn_decode_gqa_multi(_fp8); 0 for invalid sizes. */
+size_t attn_decode_gqa_multi_workspace_bytes(int B, int q_len, int s_max, int h, int h_kv, int d_h);
+
+/*
  * attn_decode_mla_absorbed -- MLA decode in the absorbed ("MQA mode") form:
  *   q~[b,i]  = W_UK[i]^T q_nope[b,i]                      (d_c values)
  *   z_t      = scale * (q~ . c_t + q_rope[b,i] . k_R,t)

@@ -138,6 +138,41 @@ def run_gqa_fp8(name, steps, warmup, rotate, k_scale=1.0 / 64, v_scale=1.0 / 64)
     return sh, total_ms, per
 
 
+def run_gqa_multi(name, q_len, steps, warmup, rotate):
+    """The GQA workload with q_len new tokens per sequence (bf16 cache)."""
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = synth.configs()[name]
+    sets = [synth.draw_gqa(sh, device="cuda", seed=sh.seed + 1000 * r) for r in range(rotate)]
+    g = torch.Generator(device="cuda").manual_seed(sh.seed)
+    q = torch.randn((sh.B, q_len, sh.h, sh.d_h), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lse = torch.empty((sh.B, q_len, sh.h), dtype=torch.float32, device="cuda")
+    wsb = A.attn_decode_gqa_multi_workspace_bytes(sh.B, q_len, sh.s_max, sh.h, sh.h_kv, sh.d_h)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    it = [0]
+
+    def call():
+        d = sets[it[0] % rotate]
+        it[0] += 1
+        bt = d.get("block_table")
+        A.attn_decode_gqa_multi(out, lse, q, d["K"], d["V"], d["s"], bt,
+                                0 if bt is None else bt.shape[1], sh.block_size,
+                                0 if bt is None else d["K"].shape[0], sh.B, q_len, sh.s_max, sh.h,
+                                sh.h_kv, sh.d_h, 2, 0.0, ws, wsb, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    return sh, total_ms, per
+
+
+def gqa_multi_alg_bytes(sh, q_len):
+    """K+V of every cached token once, plus q and out of every query position."""
+    return 2 * sum(sh.s) * sh.h_kv * sh.d_h * sh.b + 2 * sh.B * q_len * sh.h * sh.d_h * 2
+
+
 def gqa_fp8_alg_bytes(sh):
     """K+V codes (one byte each) of every cached token plus bf16 q and out."""
     return 2 * sum(sh.s) * sh.h_kv * sh.d_h + 2 * sh.B * sh.h * sh.d_h * 2
@@ -324,6 +359,8 @@ def main():
     ap.add_argument("--no-mla", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-dcp", action="store_true")
+    ap.add_argument("--no-multi", action="store_true")
+    ap.add_argument("--q-len", type=int, default=4, help="drafted tokens in the multi-token leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -422,6 +459,22 @@ def main():
                           "speedup_vs_bf16": ms / fms}
         except Exception as e:  # the FP8 leg reports its own failure, the line still prints
             rec["fp8"] = {"error": str(e)[:200]}
+    if not args.no_multi:
+        try:   # the same layer verifying q_len drafted tokens per sequence in one call
+            qsh, qtot, qper = run_gqa_multi(args.config, args.q_len, args.steps, args.warmup, rotate=1)
+            qms = qtot / args.steps
+            qab = gqa_multi_alg_bytes(qsh, args.q_len)
+            rec["multi"] = {"workload": f"{qsh.name}: {args.q_len} new tokens per sequence "
+                                        f"(causal among them), bf16 cache",
+                            "q_len": args.q_len, "steps_per_s": 1000.0 / qms, "ms_per_step": qms,
+                            "query_tokens_per_s": qsh.B * args.q_len * 1000.0 / qms,
+                            "hbm_gbps": qab / (qms * 1e-3) / 1e9,
+                            "hbm_frac": qab / (qms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                            "alg_bytes_per_call": qab,
+                            "median_call_us": float(np.median(qper)) * 1e3,
+                            "time_vs_one_token": qms / ms}
+        except Exception as e:  # reports its own failure, the line still prints
+            rec["multi"] = {"error": str(e)[:200]}
     if not args.no_dcp:
         try:   # the exchange step of context-parallel decode, on one GPU
             mms_, mper, malg = run_merge(8, 32, 128, 512, args.steps, args.warmup)

@@ -77,6 +77,11 @@ def _load():
         lib.ref_gqa_decode_multi.restype = I
         lib.ref_gqa_decode_multi.argtypes = [P, P, P, P, P, D, D, P, P, I, I, I, I, I, I, I, I,
                                              I, D]
+        lib.ref_mla_absorbed_fp8.restype = I
+        lib.ref_mla_absorbed_fp8.argtypes = [P, P, P, P, P, P, P, P, D, D, P, P, I, I, I, I, I,
+                                             I, I, I, I, D]
+        lib.ref_kv_append_mla_fp8.restype = I
+        lib.ref_kv_append_mla_fp8.argtypes = [P, P, C.c_float, C.c_float, P, P, I, I, I, I, I, I]
         lib.ref_merge_partials.restype = I
         lib.ref_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I]
         _lib = lib
@@ -371,3 +376,60 @@ def gqa_decode_multi(q, K, V, s, b, block_table=None, block_size=16, scale=None,
     if rc != 0:
         raise ValueError(f"ref_gqa_decode_multi rejected its arguments ({rc})")
     return out, lse
+
+
+def mla_absorbed_fp8(q_nope, q_rope, w_uk, w_uv, cache8, c_scale, r_scale, s, block_table=None,
+                     block_size=16, scale=None):
+    """Reference absorbed MLA decode over an FP8 latent cache.
+
+    cache8: uint8 E4M3 codes, rows [c (d_c) | k_R (d_R)], [B,s_max,W] or
+    [N_blk,block_size,W]; element = code * c_scale (latent) or * r_scale
+    (rotary).  q_nope, q_rope, w_uk, w_uv: bf16 bits.  Returns (out,
+    u_latent, lse) as mla_absorbed.
+    """
+    q_nope, q_rope, w_uk, w_uv = (_stored(x, 2) for x in (q_nope, q_rope, w_uk, w_uv))
+    cache8 = np.ascontiguousarray(cache8, dtype=np.uint8)
+    B, h, d_nope = q_nope.shape
+    d_R = q_rope.shape[2]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    s = _i32(s)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max, max_blocks, bs = cache8.shape[1], 0, 0
+    else:
+        s_max, max_blocks, bs = 0, bt.shape[1], block_size
+        _check_table(bt, cache8.shape[0] * cache8.shape[1], bs, s)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_nope + d_R)
+    out = np.zeros((B, h, d_v))
+    ul = np.zeros((B, h, d_c))
+    lse = np.zeros((B, h))
+    rc = _load().ref_mla_absorbed_fp8(_ptr(out), _ptr(ul), _ptr(lse), _ptr(q_nope), _ptr(q_rope),
+                                      _ptr(w_uk), _ptr(w_uv), _ptr(cache8),
+                                      float(np.float32(c_scale)), float(np.float32(r_scale)),
+                                      _ptr(s), _ptr(bt), max_blocks, bs, B, s_max, h, d_c, d_R,
+                                      d_nope, d_v, float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_mla_absorbed_fp8 rejected its arguments ({rc})")
+    return out, ul, lse
+
+
+def kv_append_mla_fp8(cache8, kv_new, c_scale, r_scale, pos, d_c, block_table=None,
+                      block_size=16):
+    """Host image of kv_cache_append_mla_fp8: returns a new uint8 cache with
+    row b of kv_new (bf16 bits [B, d_c + d_R]) encoded at slot pos[b]."""
+    c = np.array(cache8, dtype=np.uint8, copy=True)
+    kv_new = _stored(kv_new, 2)
+    B, W = kv_new.shape
+    pos = _i32(pos)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max, max_blocks, bs = c.shape[1], 0, 0
+    else:
+        s_max, max_blocks, bs = 0, bt.shape[1], block_size
+    rc = _load().ref_kv_append_mla_fp8(_ptr(c), _ptr(kv_new), inv_scale(c_scale), inv_scale(r_scale),
+                                       _ptr(pos), _ptr(bt), max_blocks, bs, B, s_max, d_c, W - d_c)
+    if rc != 0:
+        raise ValueError(f"ref_kv_append_mla_fp8 rejected its arguments ({rc})")
+    return c

@@ -187,11 +187,25 @@ int ref_gqa_decode(double* out, double* lse, const void* q, const void* k, const
  * q^R . k^R_t; A = softmax(scale * score); u~ = sum_t A_t c_t;
  * o = W_UV,i u~.
  */
-int ref_mla_absorbed(double* out, double* u_latent, double* lse, const void* q_nope,
-                     const void* q_rope, const void* w_uk, const void* w_uv,
-                     const void* cache, const int32_t* s, const int32_t* block_table,
-                     int max_blocks, int block_size, int B, int s_max, int h, int d_c,
-                     int d_R, int d_nope, int d_v, int b, double scale)
+double ref_fp8_e4m3_decode(int code);
+static double ld_fp8(const uint8_t* p, size_t idx, double scale);
+
+/* element e of cached latent row roff: stored bits of dtype cb (2 or 4), or
+ * (cb = 1) an E4M3 code times c_scale (latent part, e < d_c) or r_scale
+ * (rotary part) */
+static double ld_latent(const void* cache, size_t roff, int e, int cb, int d_c, double c_scale,
+                        double r_scale)
+{
+    if (cb == 1) return ld_fp8((const uint8_t*)cache, roff + e, e < d_c ? c_scale : r_scale);
+    return ld(cache, roff + e, cb);
+}
+
+static int mla_absorbed_impl(double* out, double* u_latent, double* lse, const void* q_nope,
+                             const void* q_rope, const void* w_uk, const void* w_uv,
+                             const void* cache, int cb, double c_scale, double r_scale,
+                             const int32_t* s, const int32_t* block_table, int max_blocks,
+                             int block_size, int B, int s_max, int h, int d_c, int d_R,
+                             int d_nope, int d_v, int b, double scale)
 {
     if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s) return OR_EINVAL;
     if (B < 0 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0) return OR_EINVAL;
@@ -232,10 +246,12 @@ int ref_mla_absorbed(double* out, double* u_latent, double* lse, const void* q_n
                 const size_t roff =
                     row_of(block_table, max_blocks, block_size, s_max, bb, t) * W;
                 double acc = 0.0;
-                for (int c = 0; c < d_c; c++) acc += qt[c] * ld(cache, roff + c, b);
+                for (int c = 0; c < d_c; c++)
+                    acc += qt[c] * ld_latent(cache, roff, c, cb, d_c, c_scale, r_scale);
                 double accr = 0.0;
                 for (int e = 0; e < d_R; e++)
-                    accr += ld(q_rope, (size_t)r * d_R + e, b) * ld(cache, roff + d_c + e, b);
+                    accr += ld(q_rope, (size_t)r * d_R + e, b) *
+                            ld_latent(cache, roff, d_c + e, cb, d_c, c_scale, r_scale);
                 z[t] = scale * (acc + accr);
             }
             double m;
@@ -246,7 +262,7 @@ int ref_mla_absorbed(double* out, double* u_latent, double* lse, const void* q_n
                 for (int t = 0; t < n; t++) {
                     const size_t roff =
                         row_of(block_table, max_blocks, block_size, s_max, bb, t) * W;
-                    acc += p[t] * ld(cache, roff + c, b);
+                    acc += p[t] * ld_latent(cache, roff, c, cb, d_c, c_scale, r_scale);
                 }
                 ut[c] = acc / l;
             }
@@ -264,6 +280,36 @@ int ref_mla_absorbed(double* out, double* u_latent, double* lse, const void* q_n
         free(qt);
     }
     return bad ? OR_EINVAL : OR_OK;
+}
+
+int ref_mla_absorbed(double* out, double* u_latent, double* lse, const void* q_nope,
+                     const void* q_rope, const void* w_uk, const void* w_uv,
+                     const void* cache, const int32_t* s, const int32_t* block_table,
+                     int max_blocks, int block_size, int B, int s_max, int h, int d_c,
+                     int d_R, int d_nope, int d_v, int b, double scale)
+{
+    return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, b, 1.0, 1.0,
+                             s, block_table, max_blocks, block_size, B, s_max, h, d_c, d_R,
+                             d_nope, d_v, b, scale);
+}
+
+/*
+ * MLA decode over an FP8 latent cache: rows of d_c + d_R E4M3 codes, the
+ * latent part scaled by c_scale and the rotary part by r_scale (one scale
+ * per tensor part; "MLA: why one latent can replace a multi-head KV cache",
+ * section "MLA and KV-cache quantization stack" (by gloss), notes the two
+ * parts may need separate scales).  q_nope, q_rope, W_UK, W_UV are bf16.
+ * Otherwise as ref_mla_absorbed.
+ */
+int ref_mla_absorbed_fp8(double* out, double* u_latent, double* lse, const void* q_nope,
+                         const void* q_rope, const void* w_uk, const void* w_uv,
+                         const uint8_t* cache, double c_scale, double r_scale, const int32_t* s,
+                         const int32_t* block_table, int max_blocks, int block_size, int B,
+                         int s_max, int h, int d_c, int d_R, int d_nope, int d_v, double scale)
+{
+    return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1, c_scale,
+                             r_scale, s, block_table, max_blocks, block_size, B, s_max, h, d_c,
+                             d_R, d_nope, d_v, 2, scale);
 }
 
 /*
@@ -518,6 +564,35 @@ int ref_kv_append_fp8(uint8_t* cache_k, uint8_t* cache_v, const void* k_new, con
 }
 
 /*
+ * Append into an FP8 latent cache: element e of the bf16 row kv_new[b]
+ * ([c | k_R], d_c + d_R wide) becomes encode(x * c_inv) for e < d_c and
+ * encode(x * r_inv) after, the products in fp32, at slot pos[b].
+ */
+int ref_kv_append_mla_fp8(uint8_t* cache, const void* kv_new, float c_inv_scale,
+                          float r_inv_scale, const int32_t* pos, const int32_t* block_table,
+                          int max_blocks, int block_size, int B, int s_max, int d_c, int d_R)
+{
+    if (!cache || !kv_new || !pos) return OR_EINVAL;
+    if (B < 0 || d_c <= 0 || d_R < 0) return OR_EINVAL;
+    const size_t n = (size_t)d_c + d_R;
+    for (int bb = 0; bb < B; bb++) {
+        const int t = pos[bb];
+        if (t < 0 || (!block_table && t >= s_max) ||
+            (block_table && t >= max_blocks * block_size))
+            return OR_EINVAL;
+        if (block_table && block_table[(size_t)bb * max_blocks + t / block_size] < 0)
+            return OR_EINVAL;
+        const size_t row = row_of(block_table, max_blocks, block_size, s_max, bb, t);
+        for (size_t e = 0; e < n; e++) {
+            const float x = (float)ld(kv_new, (size_t)bb * n + e, 2);
+            cache[row * n + e] =
+                (uint8_t)ref_fp8_e4m3_encode(x * ((int)e < d_c ? c_inv_scale : r_inv_scale));
+        }
+    }
+    return OR_OK;
+}
+
+/*
  * Merge of attention computed over disjoint slices of the same tokens.
  * Slice k of row r (= b * h + i) holds o_k, the softmax-weighted output over
  * its own tokens, and lse_k = ln sum_{t in k} exp(z_t) (-inf for an empty
@@ -570,7 +645,8 @@ static double ld_cache(const void* p, size_t idx, int b, double scale)
 /*
  * Decode attention for q_len new tokens per sequence at once (the tokens a
  * speculative step verifies; "MLA: why one latent can replace a multi-head
- * KV cache" lists their number among the inputs of a decode kernel).
+ * KV cache", section "MHA mode and MQA mode are execution forms" (by gloss),
+ * lists their number among what selects a decode kernel).
  * All q_len tokens are already in the cache, so s_b counts them; query
  * position jq (0-based) sits at cache position s_b - q_len + jq and attends
  * to the n = s_b - q_len + 1 + jq tokens up to and including itself (causal

@@ -32,6 +32,8 @@ EXPORTED = (
     "attn_decode_gqa_multi",
     "attn_decode_gqa_multi_fp8",
     "attn_decode_gqa_multi_workspace_bytes",
+    "attn_decode_mla_absorbed_fp8",
+    "kv_cache_append_mla_fp8",
 )
 
 _lib = None
@@ -82,6 +84,11 @@ def lib():
                                                 I, I, F, P, Z, P]
         L.attn_decode_gqa_multi_workspace_bytes.restype = Z
         L.attn_decode_gqa_multi_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.attn_decode_mla_absorbed_fp8.restype = I
+        L.attn_decode_mla_absorbed_fp8.argtypes = [P, P, P, P, P, P, P, P, F, F, P, P, I, I, I,
+                                                   I, I, I, I, I, I, I, F, P, Z, P]
+        L.kv_cache_append_mla_fp8.restype = I
+        L.kv_cache_append_mla_fp8.argtypes = [P, P, F, F, P, P, I, I, I, I, I, I, I, P]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -192,6 +199,27 @@ def attn_decode_gqa_multi_workspace_bytes(B, q_len, s_max, h, h_kv, d_h):
     return int(lib().attn_decode_gqa_multi_workspace_bytes(B, q_len, s_max, h, h_kv, d_h))
 
 
+def attn_decode_mla_absorbed_fp8(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, c_scale,
+                                 r_scale, s, block_table, max_blocks, block_size, num_blocks, B,
+                                 s_max, h, d_c, d_R, d_nope, d_v, scale, workspace,
+                                 workspace_bytes, stream=None, check=True):
+    rc = lib().attn_decode_mla_absorbed_fp8(_p(out), _p(u_latent), _p(lse), _p(q_nope),
+                                            _p(q_rope), _p(w_uk), _p(w_uv), _p(cache),
+                                            float(c_scale), float(r_scale), _p(s),
+                                            _p(block_table), max_blocks, block_size, num_blocks,
+                                            B, s_max, h, d_c, d_R, d_nope, d_v, float(scale),
+                                            _p(workspace), int(workspace_bytes), _stream(stream))
+    return _check(rc) if check else rc
+
+
+def kv_cache_append_mla_fp8(cache, kv_new, c_scale, r_scale, pos, block_table, max_blocks,
+                            block_size, num_blocks, B, s_max, d_c, d_R, stream=None, check=True):
+    rc = lib().kv_cache_append_mla_fp8(_p(cache), _p(kv_new), float(c_scale), float(r_scale),
+                                       _p(pos), _p(block_table), max_blocks, block_size,
+                                       num_blocks, B, s_max, d_c, d_R, _stream(stream))
+    return _check(rc) if check else rc
+
+
 def attn_merge_partials(out, lse, o_parts, lse_parts, n_parts, B, h, d, b_parts, b_out,
                         stream=None, check=True):
     rc = lib().attn_merge_partials(_p(out), _p(lse), _p(o_parts), _p(lse_parts), n_parts, B, h,
@@ -286,8 +314,10 @@ def decode_gqa_fp8(q, K8, V8, k_scale, v_scale, s, block_table=None, block_size=
 
 
 def decode_mla(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_size=16,
-               s_max=None, scale=0.0, want_latent=True, workspace=None, stream=None):
-    """Absorbed MLA decode; cache rows [c | k_R] of width d_c + d_R."""
+               s_max=None, scale=0.0, want_latent=True, workspace=None, stream=None,
+               c_scale=None, r_scale=None):
+    """Absorbed MLA decode; cache rows [c | k_R] of width d_c + d_R (bf16,
+    or uint8 E4M3 codes when c_scale and r_scale are given)."""
     import torch
     B, h, d_nope = q_nope.shape
     d_R = q_rope.shape[2]
@@ -305,9 +335,14 @@ def decode_mla(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_siz
     l = torch.empty((B, h), dtype=torch.float32, device=q_nope.device)
     ws = workspace or Workspace(q_nope.device)
     wb, wn = ws.get(attn_decode_workspace_bytes(1, B, s_max, h, 1, d_c, d_R))
-    attn_decode_mla_absorbed(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache, s, block_table,
-                             max_blocks, block_size, num_blocks, B, s_max, h, d_c, d_R, d_nope,
-                             d_v, 2, scale, wb, wn, stream)
+    if c_scale is None:
+        attn_decode_mla_absorbed(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache, s, block_table,
+                                 max_blocks, block_size, num_blocks, B, s_max, h, d_c, d_R,
+                                 d_nope, d_v, 2, scale, wb, wn, stream)
+    else:
+        attn_decode_mla_absorbed_fp8(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache, c_scale,
+                                     r_scale, s, block_table, max_blocks, block_size, num_blocks,
+                                     B, s_max, h, d_c, d_R, d_nope, d_v, scale, wb, wn, stream)
     return out, ul, l
 
 

@@ -319,12 +319,45 @@ int kv_cache_append_fp8(void* cache_k, void* cache_v, const void* k_new, const v
     pk.s_max = s_max;
     pk.row_bytes = (long long)h_kv * d_h;   // one byte per code
     pk.inv_scale = 1.0f / k_scale;
+    pk.inv_scale2 = pk.inv_scale;
+    pk.split = pk.row_bytes;
     attn::AppendParams pv = pk;
     pv.cache = cache_v;
     pv.src = v_new;
     pv.inv_scale = cache_v ? 1.0f / v_scale : 1.0f;
+    pv.inv_scale2 = pv.inv_scale;
     hipError_t e = attn::launch_append_fp8(pk, cache_v ? &pv : nullptr, B, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "kv_cache_append_fp8 launch");
+    return ATTN_OK;
+}
+
+int kv_cache_append_mla_fp8(void* cache, const void* kv_new, float c_scale, float r_scale,
+                            const int32_t* pos, const int32_t* block_table, int max_blocks,
+                            int block_size, int num_blocks, int B, int s_max, int d_c, int d_R,
+                            void* stream)
+{
+    if (!cache || !kv_new || !pos) return fail(ATTN_EINVAL, "null cache, kv_new or pos");
+    if (B < 0 || d_c <= 0 || d_R < 0 || d_c % 4 != 0 || d_R % 4 != 0)
+        return fail(ATTN_EINVAL, "bad sizes (d_c and d_R must be multiples of 4)");
+    if (!(c_scale > 0.f) || isinf(c_scale) || !(r_scale > 0.f) || isinf(r_scale))
+        return fail(ATTN_EINVAL, "scales must be positive and finite");
+    int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
+    if (rc) return rc;
+    attn::AppendParams pk{};
+    pk.cache = cache;
+    pk.src = kv_new;
+    pk.pos = pos;
+    pk.bt = block_table;
+    pk.max_blocks = max_blocks;
+    pk.bs_log2 = block_table ? ilog2(block_size) : 0;
+    pk.num_blocks = num_blocks;
+    pk.s_max = s_max;
+    pk.row_bytes = (long long)d_c + d_R;
+    pk.inv_scale = 1.0f / c_scale;
+    pk.inv_scale2 = 1.0f / r_scale;
+    pk.split = d_c;
+    hipError_t e = attn::launch_append_fp8(pk, nullptr, B, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_cache_append_mla_fp8 launch");
     return ATTN_OK;
 }
 
@@ -353,18 +386,24 @@ int attn_decode_gqa_fp8(void* out, float* lse, const void* q, const void* cache_
                       workspace_bytes, stream);
 }
 
-int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void* q_nope,
-                             const void* q_rope, const void* w_uk, const void* w_uv,
-                             const void* cache, const int32_t* s, const int32_t* block_table,
-                             int max_blocks, int block_size, int num_blocks, int B, int s_max,
-                             int h, int d_c, int d_R, int d_nope, int d_v, int b, float scale,
-                             void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Shared body of the MLA entry points: b = 2 (bf16 cache) or b = 1 (E4M3
+// cache codes with a latent and a rotary scale).
+int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const void* q_rope,
+               const void* w_uk, const void* w_uv, const void* cache, float c_scale,
+               float r_scale, const int32_t* s, const int32_t* block_table, int max_blocks,
+               int block_size, int num_blocks, int B, int s_max, int h, int d_c, int d_R,
+               int d_nope, int d_v, int b, float scale, void* workspace, size_t workspace_bytes,
+               void* stream)
 {
     if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s)
         return fail(ATTN_EINVAL, "null out, q_nope, q_rope, w_uk, w_uv, cache or s");
     if (B < 0 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0 || s_max < 0)
         return fail(ATTN_EINVAL, "bad sizes");
-    if (b != 2) return fail(ATTN_ENOTSUP, "MLA supports bf16 storage only (b=2)");
+    if (b != 2 && b != 1) return fail(ATTN_ENOTSUP, "MLA supports bf16 storage only (b=2)");
     if (d_c != 512 || d_R != 64)
         return fail(ATTN_ENOTSUP, "MLA supports d_c=512, d_R=64 (got %d, %d)", d_c, d_R);
     if (h % 16 != 0 || h > 128) return fail(ATTN_ENOTSUP, "MLA needs h a multiple of 16, <= 128");
@@ -412,10 +451,45 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
     p.min_tiles = P.min_tiles;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)(d_nope + d_R));
     p.scale_log2 = sc * 1.4426950408889634f;
+    p.f8 = b == 1;
+    p.c_scale = c_scale;
+    p.r_scale = r_scale;
     hipError_t e = attn::launch_mla(p, block_table != nullptr, (hipStream_t)stream);
     if (e == hipErrorNotSupported) return fail(ATTN_ENOTSUP, "MLA kernels not built");
     if (e != hipSuccess) return hip_fail(e, "attn_decode_mla_absorbed launch");
     return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void* q_nope,
+                             const void* q_rope, const void* w_uk, const void* w_uv,
+                             const void* cache, const int32_t* s, const int32_t* block_table,
+                             int max_blocks, int block_size, int num_blocks, int B, int s_max,
+                             int h, int d_c, int d_R, int d_nope, int d_v, int b, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (b != 2) return fail(ATTN_ENOTSUP, "MLA supports bf16 storage only (b=2)");
+    return decode_mla(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1.f, 1.f, s,
+                      block_table, max_blocks, block_size, num_blocks, B, s_max, h, d_c, d_R,
+                      d_nope, d_v, b, scale, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_mla_absorbed_fp8(void* out, float* u_latent, float* lse, const void* q_nope,
+                                 const void* q_rope, const void* w_uk, const void* w_uv,
+                                 const void* cache, float c_scale, float r_scale,
+                                 const int32_t* s, const int32_t* block_table, int max_blocks,
+                                 int block_size, int num_blocks, int B, int s_max, int h, int d_c,
+                                 int d_R, int d_nope, int d_v, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream)
+{
+    if (!(c_scale > 0.f) || isinf(c_scale) || !(r_scale > 0.f) || isinf(r_scale))
+        return fail(ATTN_EINVAL, "c_scale and r_scale must be positive and finite");
+    return decode_mla(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, c_scale, r_scale, s,
+                      block_table, max_blocks, block_size, num_blocks, B, s_max, h, d_c, d_R,
+                      d_nope, d_v, 1, scale, workspace, workspace_bytes, stream);
 }
 
 int attn_decode_gqa_multi(void* out, float* lse, const void* q, const void* cache_k,

@@ -100,10 +100,11 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendParams pk, 
     const uint2* src = (const uint2*)((const uint16_t*)p.src + (size_t)b * p.row_bytes);
     for (long long i = threadIdx.x; i < n4; i += blockDim.x) {
         const uint2 w = src[i];
-        const uint32_t c0 = e4m3_code(bf16lo_to_f32(w.x) * p.inv_scale);
-        const uint32_t c1 = e4m3_code(bf16hi_to_f32(w.x) * p.inv_scale);
-        const uint32_t c2 = e4m3_code(bf16lo_to_f32(w.y) * p.inv_scale);
-        const uint32_t c3 = e4m3_code(bf16hi_to_f32(w.y) * p.inv_scale);
+        const float is = 4 * i < p.split ? p.inv_scale : p.inv_scale2;   // MLA: latent, then rotary part
+        const uint32_t c0 = e4m3_code(bf16lo_to_f32(w.x) * is);
+        const uint32_t c1 = e4m3_code(bf16hi_to_f32(w.x) * is);
+        const uint32_t c2 = e4m3_code(bf16lo_to_f32(w.y) * is);
+        const uint32_t c3 = e4m3_code(bf16hi_to_f32(w.y) * is);
         dst[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
     }
 }

@@ -43,6 +43,8 @@ struct AppendParams {
     int max_blocks, bs_log2, num_blocks, s_max;
     long long row_bytes;   // bytes of one cache row (FP8: elements of one row)
     float inv_scale;       // FP8 append: fp32 reciprocal of the tensor's scale
+    float inv_scale2;      // FP8 append: reciprocal scale of elements split .. row end
+    long long split;       // FP8 append: first element under inv_scale2 (a multiple of 4)
 };
 
 hipError_t launch_append(const AppendParams& k, const AppendParams* v, int B, hipStream_t st);
@@ -69,6 +71,9 @@ struct MlaParams {
     int B, s_max, h, d_c, d_R, d_nope, d_v;
     int n_wg, min_tiles;  // decode workgroups; fewest 32-token tiles per workgroup
     float scale_log2;
+    int f8;               // cache rows are E4M3 codes (else bf16)
+    float c_scale;        // FP8: scale of the latent part (1 for bf16); folded into q^ and u~
+    float r_scale;        // FP8: scale of the rotary part (1 for bf16); folded into q^
 };
 
 hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st);

@@ -121,8 +121,9 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
             *(u32x4v*)(smem + r * kAbsRowStride + c * 16) = v[u];
         }
     }
-    // the rotary part of q^ is a plain copy (done once per head, 16 bytes per
-    // lane, four copies in flight); d_R is a multiple of 8
+    // the rotary part of q^ is q_rope times the rotary scale of an FP8 cache
+    // (a plain copy for bf16: the scale is 1); once per head, 16 bytes per
+    // lane, four copies in flight; d_R is a multiple of 8
     if (cq == 0) {
         const int per = p.d_R / 8, nv = p.B * per;
         const uint16_t* __restrict__ qr = (const uint16_t*)p.q_rope;
@@ -136,7 +137,13 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 #pragma unroll
             for (int u = 0; u < 4; u++) {
                 const int idx = min(base + u * 256 + tid, nv - 1);   // duplicates rewrite the same value
-                *(u32x4v*)(p.qhat + qhat_index(idx / per, i, p.d_c + 8 * (idx % per), p.h)) = v[u];
+                u32x4v x = v[u];
+                if (p.f8) {   // workgroup-uniform
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        x[e] = pack_bf16x2(bf16lo_to_f32(x[e]) * p.r_scale, bf16hi_to_f32(x[e]) * p.r_scale);
+                }
+                *(u32x4v*)(p.qhat + qhat_index(idx / per, i, p.d_c + 8 * (idx % per), p.h)) = x;
             }
         }
     }
@@ -163,9 +170,11 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
                     acc = mfma16(a.k[k], cat_tr(lo, hi), acc);
                 }
             }
-            // lane holds q~[b0 + 4G + e][c0 + 16 nt + li]
+            // lane holds q~[b0 + 4G + e][c0 + 16 nt + li], times the latent
+            // scale of an FP8 cache (1 for bf16)
 #pragma unroll
-            for (int e = 0; e < 4; e++) ost[wave][4 * G + e][16 * t + li] = (uint16_t)f32_to_bf16_bits(acc[e]);
+            for (int e = 0; e < 4; e++)
+                ost[wave][4 * G + e][16 * t + li] = (uint16_t)f32_to_bf16_bits(acc[e] * p.c_scale);
         }
         __syncthreads();
         {
@@ -217,10 +226,20 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 //    its state in registers (no spills).
 // ---------------------------------------------------------------------------
 constexpr int kT = 32;             // tokens per tile
-constexpr int kRow = 576 * 2;      // bytes per cached latent row
-constexpr int kTile = kT * kRow;   // 36,864 bytes
 constexpr int kNBuf = 4;           // LDS ring depth
-constexpr int kSlots = kTile / 1024;   // 36 DMA instructions per tile
+
+// Tile geometry by cache format.  bf16: 9 segments of 128 bytes per row,
+// one DMA instruction = 8 rows of a segment.  E4M3 (576-byte rows): 9
+// segments of 64 bytes, one DMA instruction = 16 rows of a segment.
+template <bool F8>
+struct MlaTile {
+    static constexpr int ROW = F8 ? 576 : 1152;       // bytes per cached row
+    static constexpr int TILE = kT * ROW;             // bytes per tile
+    static constexpr int SLOTS = TILE / 1024;         // DMA instructions per tile
+    static constexpr int SEG = F8 ? 64 : 128;         // bytes per row segment
+    static constexpr int RPS = 1024 / SEG;            // rows per DMA instruction
+    static constexpr int SPS = kT / RPS;              // DMA instructions per segment
+};
 
 // XOR swizzle of the 16-byte chunk position within a 128-byte row segment:
 // s(r) = r0 ^ 2 r1 ^ 5 r2 ^ 7 r3 (r_k the bits of r).  Any 8 consecutive
@@ -264,6 +283,46 @@ struct TileOffsets {
     __device__ __forceinline__ const uint8_t* value(const uint8_t* C, int w, int mc, int kk, int t) const
     {
         return C + tr[mc & 1][t] + (2 * w + (mc >> 1)) * 4096 + kk * 2048;
+    }
+};
+
+// E4M3 tiles (576-byte rows in 64-byte segments: byte s * 2048 + r * 64 +
+// 16 p holds row r, 16-byte chunk 4 s + (p ^ swz8(r))).
+//   swz8(r) = ((r >> 1) & 3) ^ 2 ((r >> 3) & 1)
+// Score operands: a lane reads one whole chunk (16 codes) per pair of K
+// steps: lane (row r = l % 32, hh = l / 32) reads chunk 2 j + hh, whose
+// first 8 codes are its operand of step 2 j and the last 8 of step 2 j + 1
+// (the K order inside a step is free as long as q^ follows it).  8
+// consecutive rows then cover the 8 (row parity, position) bank groups.
+// Value operands: an 8-bit transposing read per (column tile, K step).  In
+// 16-lane group q (= l / 16), source lane i reads 8 bytes of row
+// 16 kk + tau(q / 2, i / 2), columns 128 w + 32 mc + 16 (q % 2) + 8 (i % 2),
+// with tau(hh, k) = 4 hh + k for k < 4 and 4 hh + k + 4 otherwise -- the
+// score output's token order; the read hands lane 8 a + c byte c of source
+// lanes a, a + 2, .., a + 14, i.e. column 16 (q % 2) + 8 a + c for its 8
+// tokens.  Rows {0-3, 8-11} and {4-7, 12-15} each cover the 8 bank groups.
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 3) ^ (((r >> 3) & 1) << 1); }
+
+struct TileOffsets8 {
+    int sc[2];   // score, by j & 1
+    int tr[2];   // value, by mc & 1
+    __device__ __forceinline__ TileOffsets8(int lane)
+    {
+        const int r = lane % 32, hh = lane / 32, s = swz8(r);
+#pragma unroll
+        for (int j = 0; j < 2; j++) sc[j] = r * 64 + (((2 * j + hh) ^ s) << 4);
+        const int q = lane / 16, i = lane % 16, k = i / 2;
+        const int row = 4 * (q / 2) + (k < 4 ? k : k + 4), st = swz8(row);
+#pragma unroll
+        for (int m1 = 0; m1 < 2; m1++) tr[m1] = row * 64 + (((2 * m1 + q % 2) ^ st) << 4) + 8 * (i % 2);
+    }
+    __device__ __forceinline__ const uint8_t* score(const uint8_t* C, int j) const
+    {
+        return C + sc[j & 1] + (j >> 1) * 2048;
+    }
+    __device__ __forceinline__ const uint8_t* value(const uint8_t* C, int w, int mc, int kk) const
+    {
+        return C + tr[mc & 1] + (2 * w + (mc >> 1)) * 2048 + kk * 1024;
     }
 };
 
@@ -415,16 +474,20 @@ struct TileWalk {
     }
 };
 
-// DMA of one tile (all 36 slots of 8 rows x 128 bytes, spread over the
-// wavefronts; slot q fills segment q / 4, rows 8 (q % 4) .. + 7) and the
-// physical rows of its two 16-row halves.  A tile's halves each lie in one
+// DMA of one tile (bf16: 36 slots of 8 rows x 128 bytes, slot q filling
+// segment q / 4, rows 8 (q % 4) .. + 7; E4M3: 18 slots of 16 rows x 64
+// bytes, slot q filling segment q / 2, rows 16 (q % 2) .. + 15; spread over
+// the wavefronts) and the physical rows of its two 16-row halves.  A tile's halves each lie in one
 // block of a paged pool (blocks hold a power of two >= 16 rows).  With NW a
-// multiple of 4 a wavefront's slots all cover the same 8 rows (q % 4 =
-// wave % 4), so one buffer resource per tile serves all of them and a slot
+// multiple of 4 a wavefront's slots all cover the same rows (q % SPS =
+// wave % SPS), so one buffer resource per tile serves all of them and a slot
 // differs only in its segment's byte offset and LDS destination.
-template <int NW, bool PAGED>
+template <int NW, bool PAGED, bool F8>
 struct TileDma {
-    static_assert(NW % 4 == 0, "a wavefront's slots must share their rows");
+    using TL = MlaTile<F8>;
+    static_assert(NW % TL::SPS == 0, "a wavefront's slots must share their rows");
+    static constexpr int kSlots = TL::SLOTS;
+    static constexpr int kRow = TL::ROW;
     static constexpr int SPW = kSlots / NW + (kSlots % NW ? 1 : 0);   // slots per wavefront
     const MlaParams& p;
     const int32_t* __restrict__ btab;
@@ -433,10 +496,12 @@ struct TileDma {
     int wave, rb;
     __device__ __forceinline__ TileDma(const MlaParams& p_, const int32_t* __restrict__ bt,
                                        uint32_t lds, int wave_, int lane)
-        : p(p_), btab(bt), cbase((const uint8_t*)p_.cache), lds0(lds), wave(wave_), rb(wave_ & 3)
+        : p(p_), btab(bt), cbase((const uint8_t*)p_.cache), lds0(lds), wave(wave_), rb(wave_ % TL::SPS)
     {
-        const int lr = lane / 8, lp = lane % 8;   // row of the 8, 16-byte position in the segment
-        vbase = (uint32_t)(lr * kRow + 16 * (lp ^ swz(8 * rb + lr)));
+        constexpr int PPS = TL::SEG / 16;   // 16-byte positions per segment
+        const int lr = lane / PPS, lp = lane % PPS;   // row of the RPS, 16-byte position in the segment
+        const int sw = F8 ? swz8(TL::RPS * rb + lr) : swz(TL::RPS * rb + lr);
+        vbase = (uint32_t)(lr * kRow + 16 * (lp ^ sw));
     }
     __device__ __forceinline__ size_t half_row(int b, int t) const
     {
@@ -454,16 +519,17 @@ struct TileDma {
     }
     __device__ __forceinline__ void issue(const TileWalk& c, int buf, size_t row0, size_t row1) const
     {
-        const size_t row = (rb < 2 ? row0 : row1) + 8 * (rb & 1);   // first row of this wavefront's 8
-        const int t0 = c.lt * kT + 8 * rb;                            // its token index
-        const int nr = c.past() ? 0 : max(0, min(8, c.n - t0)) * kRow;   // rows past the length read 0
+        // first row of this wavefront's RPS rows (a 16-row half lies in one block)
+        const size_t row = F8 ? (rb == 0 ? row0 : row1) : (rb < 2 ? row0 : row1) + 8 * (rb & 1);
+        const int t0 = c.lt * kT + TL::RPS * rb;                      // its token index
+        const int nr = c.past() ? 0 : max(0, min(TL::RPS, c.n - t0)) * kRow;   // rows past the length read 0
         const rsrc_t rs = make_rsrc(cbase + row * kRow, nr);
-        const uint32_t lb = lds0 + (uint32_t)(buf * kTile);
+        const uint32_t lb = lds0 + (uint32_t)(buf * TL::TILE);
 #pragma unroll
         for (int j = 0; j < SPW; j++) {
             const int q = wave + NW * j;
             if (kSlots % NW == 0 || q < kSlots)   // wave-uniform, static when NW divides the slots
-                dma16(rs, vbase + 128u * (uint32_t)(q >> 2), lb + (uint32_t)q * 1024u);
+                dma16(rs, vbase + (uint32_t)TL::SEG * (uint32_t)(q / TL::SPS), lb + (uint32_t)q * 1024u);
         }
     }
     // tiles tb + T and tb + 2T were issued after tile tb
@@ -474,7 +540,7 @@ struct TileDma {
     }
 };
 
-template <bool PAGED>
+template <bool PAGED, bool F8>
 __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                                                          const int32_t* __restrict__ btab,
                                                          const int32_t* __restrict__ slen,
@@ -492,7 +558,8 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     constexpr int SCH = MLA_SCH;    // score accumulation chains
     constexpr int MCW = 4;          // 32-column tiles of the latent sum per wavefront
     constexpr int NTH = 4;          // 32-head tiles of the latent sum (all heads; zeros past h)
-    __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * kTile];
+    using TL = MlaTile<F8>;
+    __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * TL::TILE];
     __shared__ __attribute__((aligned(16))) bf16x8 Pb[NTH][2][64];   // P of every head tile, B-operand layout
     __shared__ int ovf;   // some head's scores ran past its reference max + 64
     __shared__ float Lx[NTH * 32];   // softmax sums of all heads, for the partial write
@@ -512,19 +579,26 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     const int hs = 32 * wave + lane % 32;   // this lane's score head
     const bool hv = hs < p.h;
 
-    const TileDma<NW, PAGED> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
+    const TileDma<NW, PAGED, F8> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
                                  wave, lane);
     TileWalk ic(sv, sv.first_seq(w), g0, g1);   // issue cursor
     TileWalk cc = ic;                            // compute cursor
 
     // q^ fragments of one sequence: B operand of the score product (heads
     // past h read as zeros)
+    // An E4M3 tile feeds steps 2j and 2j + 1 from one chunk per lane (see
+    // TileOffsets8): lane half hh takes dims 16 (2j + hh) .. + 7 at step 2j
+    // and the next 8 at step 2j + 1, so q^ is read in that order.
     bf16x8 Qf[KS];
+    // (dims d = 32 (ks / 2) + 16 hh + 8 (ks % 2): in the q^ layout that is
+    // the element at qhat_index(b, i, 16 hh) + 1024 (ks / 2) + 256 (ks % 2))
     auto load_q = [&](int b) {
-        const uint16_t* qrow = p.qhat + qhat_index(b, min(hs, p.h - 1), 8 * hh, p.h);
+        const uint16_t* qrow = p.qhat + qhat_index(b, min(hs, p.h - 1), F8 ? 16 * hh : 8 * hh, p.h);
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++)
-            Qf[ks] = hv ? *(const bf16x8*)(qrow + 64 * 8 * ks) : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        for (int ks = 0; ks < KS; ks++) {
+            const int off = F8 ? 1024 * (ks / 2) + 256 * (ks % 2) : 512 * ks;
+            Qf[ks] = hv ? *(const bf16x8*)(qrow + off) : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        }
     };
 
     // Per head and sequence: m is the reference max (log2 units), fixed at
@@ -619,6 +693,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     }
 
     const TileOffsets to(lane);
+    const TileOffsets8 to8(lane);
     const float sc = p.scale_log2;
     int buf = 0;
     int g = g0;
@@ -634,22 +709,48 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         dma.issue(ic, (buf + 3) % kNBuf, nx0, nx1);
         ic.next(sv);
         const int flagged = ovf;   // set during an earlier tile; acted on at the end of this one
-        const uint8_t* C = Cs + buf * kTile;
+        const uint8_t* C = Cs + buf * TL::TILE;
         const int tbase = cc.lt * kT;
 
         // ---- scores S^T = C . q^T: SCH interleaved accumulation chains (one
         // chain would wait out each product's latency), operands PD steps ahead
-        bf16x8 a[PD];
-#pragma unroll
-        for (int ks = 0; ks < PD; ks++) a[ks] = *(const bf16x8*)to.score(C, ks);
         f32x16 Sc[SCH];
+        if (!F8) {
+            bf16x8 a[PD];
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-            const int c = ks % SCH;
-            if (ks < SCH) Sc[c] = mfma32_first(a[ks % PD], Qf[ks]);
-            else if (ks + SCH < KS) mfma32_acc(Sc[c], a[ks % PD], Qf[ks]);
-            else mfma32_last(Sc[c], a[ks % PD], Qf[ks]);
-            if (ks + PD < KS) a[ks % PD] = *(const bf16x8*)to.score(C, ks + PD);
+            for (int ks = 0; ks < PD; ks++) a[ks] = *(const bf16x8*)to.score(C, ks);
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                const int c = ks % SCH;
+                if (ks < SCH) Sc[c] = mfma32_first(a[ks % PD], Qf[ks]);
+                else if (ks + SCH < KS) mfma32_acc(Sc[c], a[ks % PD], Qf[ks]);
+                else mfma32_last(Sc[c], a[ks % PD], Qf[ks]);
+                if (ks + PD < KS) a[ks % PD] = *(const bf16x8*)to.score(C, ks + PD);
+            }
+        } else {
+            // one 16-byte read per pair of steps, PJ pairs ahead; the codes
+            // widen to bf16 exactly just before their product
+#ifndef MLA_PJ8
+#define MLA_PJ8 2
+#endif
+            constexpr int PJ = MLA_PJ8, KJ = KS / 2;
+            uint4 raw[PJ];
+#pragma unroll
+            for (int j = 0; j < PJ; j++) raw[j] = *(const uint4*)to8.score(C, j);
+            bf16x8 a0, a1;
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) {
+                const int c = ks % SCH, j = ks / 2;
+                if (ks % 2 == 0) {
+                    a0 = fp8x8_to_bf16(make_uint2(raw[j % PJ].x, raw[j % PJ].y));
+                    a1 = fp8x8_to_bf16(make_uint2(raw[j % PJ].z, raw[j % PJ].w));
+                    if (j + PJ < KJ) raw[j % PJ] = *(const uint4*)to8.score(C, j + PJ);
+                }
+                const bf16x8 av8 = ks % 2 ? a1 : a0;
+                if (ks < SCH) Sc[c] = mfma32_first(av8, Qf[ks]);
+                else if (ks + SCH < KS) mfma32_acc(Sc[c], av8, Qf[ks]);
+                else mfma32_last(Sc[c], av8, Qf[ks]);
+            }
         }
         f32x16 S = Sc[0];
 #pragma unroll
@@ -660,8 +761,9 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         for (int kk = 0; kk < 2; kk++)
 #pragma unroll
             for (int mc = 0; mc < MCW; mc++)
-                av[kk][mc] = cat_tr(lds_read_tr(to.value(C, wave, mc, kk, 0)),
-                                    lds_read_tr(to.value(C, wave, mc, kk, 1)));
+                av[kk][mc] = F8 ? fp8x8_to_bf16(lds_read_tr8(to8.value(C, wave, mc, kk)))
+                                : cat_tr(lds_read_tr(to.value(C, wave, mc, kk, 0)),
+                                         lds_read_tr(to.value(C, wave, mc, kk, 1)));
 
         // ---- softmax weights: lane holds head hs, tokens 8 (v / 4) + 4 hh + v % 4
         float lm = -INFINITY;
@@ -722,6 +824,8 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
 // The partial (m, l, U columns 8 lane .. 8 lane + 7) of head i over the
 // tokens of sequence bb in global tiles [g_lo, g_hi), computed from scratch
 // by one wavefront: the path for decode workgroups that stopped early.  An
+// E4M3 cache is read as codes (U stays in code units, as in the decode
+// kernel; q^ already carries the scales).  An
 // online softmax in fp32 with the reference moved on every new maximum;
 // the dot products take the stored bf16 q^ and cache bits, lane l holding
 // latent dims 8 l .. 8 l + 7 and rotary dim l (d_c = 8 * 64, d_R = 64).
@@ -754,8 +858,14 @@ __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_l
             const int t = min(t0 + k, t_hi - 1);
             const size_t row = p.bt ? paged_row(p.bt, bb, t, p.max_blocks, p.bs_log2, p.num_blocks)
                                     : (size_t)bb * p.s_max + t;
-            c8[k] = *(const uint4*)(cache + row * 576 + 8 * lane);
-            cr[k] = cache[row * 576 + 512 + lane];
+            if (p.f8) {   // E4M3 codes, widened to bf16 exactly
+                const uint8_t* c8p = (const uint8_t*)p.cache + row * 576;
+                c8[k] = __builtin_bit_cast(uint4, fp8x8_to_bf16(*(const uint2*)(c8p + 8 * lane)));
+                cr[k] = (uint16_t)(__builtin_bit_cast(uint4, fp8x8_to_bf16(make_uint2(c8p[512 + lane], 0u))).x & 0xffffu);
+            } else {
+                c8[k] = *(const uint4*)(cache + row * 576 + 8 * lane);
+                cr[k] = cache[row * 576 + 512 + lane];
+            }
         }
 #pragma unroll
         for (int k = 0; k < 8; k++) {
@@ -947,7 +1057,8 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
 
     // u~ = U / L: written out if asked, and split into the A operand rows
     if (wave < nb) {
-        const float inv = L > 0.f ? 1.f / L : 0.f;
+        // u~ = U / L, in cache units: times the latent scale of an FP8 cache
+        const float inv = L > 0.f ? p.c_scale / L : 0.f;
         a0 *= inv;
         a1 *= inv;
         if (p.u_latent) {
@@ -1014,10 +1125,17 @@ hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g2 = (unsigned)p.n_wg;
-    if (paged)
-        hipLaunchKernelGGL((mla_decode_kernel<true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
-    else
-        hipLaunchKernelGGL((mla_decode_kernel<false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+    if (p.f8) {
+        if (paged)
+            hipLaunchKernelGGL((mla_decode_kernel<true, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+        else
+            hipLaunchKernelGGL((mla_decode_kernel<false, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+    } else {
+        if (paged)
+            hipLaunchKernelGGL((mla_decode_kernel<true, false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+        else
+            hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g3 = (unsigned)(p.h * ((p.B + kFinSeq - 1) / kFinSeq));

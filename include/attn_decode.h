@@ -273,6 +273,46 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_mla_absorbed_fp8 -- attn_decode_mla_absorbed over an FP8
+ * latent cache: rows of d_c + d_R E4M3 codes [c_KV | k_R] (one byte each,
+ * d_c + d_R bytes per token), element value = code * c_scale in the latent
+ * part and code * r_scale in the rotary part.  "Multi-Head Latent Attention
+ * (MLA): Mathematical Foundations ...", section "High-Throughput Serving
+ * Kernels: FlashMLA and SGLang", describes DeepSeek-V3's latent cache in
+ * E4M3 at 576 bytes per token; "MLA: why one latent can replace a
+ * multi-head KV cache", section "MLA and KV-cache quantization stack" (by
+ * gloss), notes that the latent and rotary parts may need separate scales.
+ * Reading taken here: one fp32 scale per part for the whole cache.
+ * q_nope, q_rope, W_UK, W_UV, out as attn_decode_mla_absorbed (bf16).  The
+ * codes widen to bf16 exactly in the kernel; c_scale is folded into the
+ * absorbed query and into u~, r_scale into the rotary query.  Workspace,
+ * supported shapes and errors as attn_decode_mla_absorbed, plus EINVAL for a
+ * non-positive or infinite scale.
+ */
+int attn_decode_mla_absorbed_fp8(void* out, float* u_latent, float* lse, const void* q_nope,
+                                 const void* q_rope, const void* w_uk, const void* w_uv,
+                                 const void* cache, float c_scale, float r_scale,
+                                 const int32_t* s, const int32_t* block_table, int max_blocks,
+                                 int block_size, int num_blocks, int B, int s_max, int h, int d_c,
+                                 int d_R, int d_nope, int d_v, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * kv_cache_append_mla_fp8 -- append one latent row per sequence to an FP8
+ * latent cache: element x of kv_new[b] ([B, d_c + d_R] bf16, [c | k_R]) is
+ * stored as the E4M3 code of x * (1 / c_scale) in the latent part and of
+ * x * (1 / r_scale) in the rotary part (reciprocal and product in fp32,
+ * nearest with ties to even, saturated at +-448, NaN -> 0x7F), at slot
+ * pos[b] as kv_cache_append.  d_c and d_R multiples of 4.
+ * Errors: as kv_cache_append, plus EINVAL for a non-positive or infinite
+ * scale.
+ */
+int kv_cache_append_mla_fp8(void* cache, const void* kv_new, float c_scale, float r_scale,
+                            const int32_t* pos, const int32_t* block_table, int max_blocks,
+                            int block_size, int num_blocks, int B, int s_max, int d_c, int d_R,
+                            void* stream);
+
+/*
  * attn_merge_partials -- combine decode results computed over disjoint token
  * slices of the same sequences into the result over all their tokens: the
  * exchange step of context-parallel decode, where each GPU holds a slice of

@@ -272,6 +272,37 @@ def draw_mla(shape: MlaShape, device="cpu", seed=None):
     return d
 
 
+def draw_mla_fp8(shape: MlaShape, c_scale: float, r_scale: float, device="cpu", seed=None):
+    """draw_mla with the latent cache stored as E4M3 codes (uint8, key
+    "cache8"): the same N(0,1) rows, latent part divided by c_scale and
+    rotary part by r_scale before the conversion."""
+    seed = shape.seed if seed is None else seed
+    g = _gen(device, seed)
+    q_nope = _randn((shape.B, shape.h, shape.d_nope), g, device, torch.bfloat16)
+    q_rope = _randn((shape.B, shape.h, shape.d_R), g, device, torch.bfloat16)
+    if shape.paged:
+        tab, n_blk = block_table(shape.s, shape.block_size, seed)
+        rows = (n_blk, shape.block_size)
+    else:
+        tab, n_blk = None, 0
+        rows = (shape.B, max(shape.s_max, 1))
+    lat = _randn(rows + (shape.d_c + shape.d_R,), g, device, torch.float32)
+    cache8 = torch.cat([fp8_codes(lat[..., :shape.d_c], c_scale),
+                        fp8_codes(lat[..., shape.d_c:], r_scale)], dim=-1).contiguous()
+    del lat
+    sig = 1.0 / math.sqrt(shape.d_c)
+    w_uk = _randn((shape.h, shape.d_nope, shape.d_c), g, device, torch.bfloat16, std=sig)
+    w_uv = _randn((shape.h, shape.d_v, shape.d_c), g, device, torch.bfloat16, std=sig)
+    s = torch.tensor(shape.s, dtype=torch.int32, device=device)
+    d = dict(q_nope=q_nope, q_rope=q_rope, cache8=cache8, w_uk=w_uk, w_uv=w_uv, s=s,
+             s_host=np.asarray(shape.s, dtype=np.int32))
+    if tab is not None:
+        d["block_table"] = torch.from_numpy(tab).to(device)
+        d["block_table_host"] = tab
+        d["n_blk"] = n_blk
+    return d
+
+
 def host_bits(t: torch.Tensor) -> np.ndarray:
     """Stored bits of a tensor as a host numpy array (bf16 -> uint16, fp32 -> float32)."""
     t = t.detach().contiguous().cpu()

@@ -45,6 +45,12 @@ def mla_alg_bytes(sh):
             + sh.B * sh.h * (sh.d_nope + sh.d_R + sh.d_v) * sh.b)
 
 
+def mla_fp8_alg_bytes(sh):
+    """As mla_alg_bytes with one byte per cached latent element."""
+    return (sum(sh.s) * (sh.d_c + sh.d_R) + sh.h * (sh.d_nope + sh.d_v) * sh.d_c * 2
+            + sh.B * sh.h * (sh.d_nope + sh.d_R + sh.d_v) * 2)
+
+
 def mla_flops(sh):
     return (2 * sh.h * sum(sh.s) * (2 * sh.d_c + sh.d_R)
             + 2 * sh.B * sh.h * sh.d_c * (sh.d_nope + sh.d_v))
@@ -263,6 +269,36 @@ def run_mla(name, steps, warmup, rotate):
     return sh, total_ms, per
 
 
+def run_mla_fp8(name, steps, warmup, rotate, c_scale=1.0 / 32, r_scale=1.0 / 32):
+    """The MLA workload with its latent cache stored as E4M3 codes."""
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = synth.configs()[name]
+    sets = [synth.draw_mla_fp8(sh, c_scale, r_scale, device="cuda", seed=sh.seed + 1000 * r)
+            for r in range(rotate)]
+    out = torch.empty((sh.B, sh.h, sh.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device="cuda")
+    wsb = A.attn_decode_workspace_bytes(1, sh.B, sh.s_max, sh.h, 1, sh.d_c, sh.d_R)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    it = [0]
+
+    def call():
+        d = sets[it[0] % rotate]
+        it[0] += 1
+        bt = d.get("block_table")
+        A.attn_decode_mla_absorbed_fp8(out, None, lse, d["q_nope"], d["q_rope"], d["w_uk"],
+                                       d["w_uv"], d["cache8"], c_scale, r_scale, d["s"], bt,
+                                       0 if bt is None else bt.shape[1], sh.block_size,
+                                       0 if bt is None else d["cache8"].shape[0], sh.B, sh.s_max,
+                                       sh.h, sh.d_c, sh.d_R, sh.d_nope, sh.d_v, 0.0, ws, wsb, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    return sh, total_ms, per
+
+
 def cpu_baseline_gqa(sh, d, budget_s=15.0):
     """Time the oracle (as it stands) on a bounded sample of the same inputs,
     copied from the device: the first Bs sequences of the batch (all heads,
@@ -444,6 +480,20 @@ def main():
                           "alg_bytes_per_call": mab, "flops_per_call": mfl}
         except Exception as e:  # MLA path reports its own failure, GQA line still prints
             rec["mla"] = {"error": str(e)[:200]}
+        try:   # the same MLA layer over an E4M3 latent cache
+            fsh, ftot, fper = run_mla_fp8(args.mla_config, args.steps, args.warmup, rotate=7)
+            fms = ftot / args.steps
+            fab = mla_fp8_alg_bytes(fsh)
+            ffl = mla_flops(fsh)
+            floor8 = max(fab / (HBM_PEAK_GBPS * 1e9), ffl / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+            rec["mla"]["fp8"] = {"workload": f"{fsh.name}: latent cache as E4M3 codes (latent and "
+                                             f"rotary scales), bf16 q, weights and out",
+                                 "steps_per_s": 1000.0 / fms, "ms_per_step": fms,
+                                 "hbm_gbps": fab / (fms * 1e-3) / 1e9,
+                                 "roofline_frac": floor8 / (fms * 1e-3),
+                                 "alg_bytes_per_call": fab}
+        except Exception as e:
+            rec["mla"]["fp8"] = {"error": str(e)[:200]}
     if not args.no_fp8:
         try:   # the same workload over an E4M3 cache with per-tensor scales
             fsh, ftot, fper = run_gqa_fp8(args.config, args.steps, args.warmup, rotate=2)

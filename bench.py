@@ -240,7 +240,7 @@ def run_dcp_gqa(name, n, steps, warmup):
     return sh, S, total_ms / steps, per
 
 
-def run_mla(name, steps, warmup, rotate):
+def run_mla(name, steps, warmup, rotate, keep=None):
     import torch
     import synth
     import decode_attention_kv_attn_amd as A
@@ -266,6 +266,8 @@ def run_mla(name, steps, warmup, rotate):
                                    wsb, sp)
 
     total_ms, per = time_calls(call, steps, warmup, stream)
+    if keep is not None:
+        keep.append(sets[0])
     return sh, total_ms, per
 
 
@@ -327,8 +329,46 @@ def cpu_baseline_gqa(sh, d, budget_s=15.0):
         times.append(run(bs))
     step_s = float(np.median(times)) * sh.B / bs
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{bs} of {sh.B} sequences (all {sh.h} heads x {sh.s[0]} tokens); median of "
                       f"{len(times)} passes ({sum(times):.1f} s of CPU work), scaled to the full batch"}
+
+
+def cpu_baseline_mla(sh, d, budget_s=5.0):
+    """The absorbed MLA oracle timed the same way on the MLA workload: the
+    first sequence (all heads, all its tokens) per pass, scaled to the batch."""
+    import oracle
+    import synth
+    args = [synth.host_bits(d[k][:1]) for k in ("q_nope", "q_rope")]
+    w = [synth.host_bits(d["w_uk"]), synth.host_bits(d["w_uv"])]
+    C = synth.host_bits(d["cache"][:1])
+    s = d["s_host"][:1]
+
+    def run():
+        t0 = time.perf_counter()
+        oracle.mla_absorbed(args[0], args[1], w[0], w[1], C, s)
+        return time.perf_counter() - t0
+
+    run()
+    times = [run()]
+    while sum(times) < budget_s and len(times) < 20:
+        times.append(run())
+    step_s = float(np.median(times)) * sh.B
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"1 of {sh.B} sequences (all {sh.h} heads x {sh.s[0]} tokens); median of "
+                      f"{len(times)} passes ({sum(times):.1f} s of CPU work), scaled to the full batch"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # HBM traffic of the headline kernel from rocprofv3 counter passes (FETCH_SIZE
@@ -388,7 +428,7 @@ def stream_read_gbps(reps=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama3_8b_gqa")
     ap.add_argument("--mla-config", default="deepseek_v3_mla")
@@ -463,7 +503,8 @@ def main():
         rec["roofline"]["stream_read_error"] = str(e)[:200]
     if not args.no_mla:
         try:
-            msh, mtot, mper = run_mla(args.mla_config, args.steps, args.warmup, rotate=4)
+            mkept = []
+            msh, mtot, mper = run_mla(args.mla_config, args.steps, args.warmup, rotate=4, keep=mkept)
             mms = mtot / args.steps
             mcall = mtot / args.steps
             mab = mla_alg_bytes(msh)
@@ -478,6 +519,9 @@ def main():
                           "mfma_tflops": tfl, "mfma_frac": tfl / MFMA_BF16_PEAK_TFLOPS,
                           "roofline_frac": floor_s / (mcall * 1e-3),
                           "alg_bytes_per_call": mab, "flops_per_call": mfl}
+            if not args.no_cpu_baseline:
+                rec["mla"]["cpu_baseline"] = cpu_baseline_mla(msh, mkept[0])
+            del mkept
         except Exception as e:  # MLA path reports its own failure, GQA line still prints
             rec["mla"] = {"error": str(e)[:200]}
         try:   # the same MLA layer over an E4M3 latent cache

@@ -89,7 +89,10 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
         P.NW = 1;
         target = 2048;
     }
-    const long long T = 64, min_chunk = 512, max_chunk = 4096;
+#ifndef GQA_MAX_CHUNK
+#define GQA_MAX_CHUNK 4096
+#endif
+    const long long T = 64, min_chunk = 512, max_chunk = GQA_MAX_CHUNK;
     const long long units = (long long)B * h_kv * P.n_hg * P.n_rb;
     long long ns = units > 0 ? cdiv(target, units) : 1;
     if (s_max > 0 && ns < cdiv(s_max, max_chunk)) ns = cdiv(s_max, max_chunk);
@@ -280,7 +283,12 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_h);
     p.scale_log2 = sc * k_scale * 1.4426950408889634f;
     p.v_scale = v_scale;
-    const long long grid = (long long)B * h_kv * P.n_hg * P.n_split * P.n_rb;
+    // matrix-core kernel over a paged pool with splits: workgroups go to the
+    // non-empty (b, split) pairs only (each workgroup scans the B lengths to
+    // find its pair, so only for moderate B); the grid is then a multiple of 8
+    p.compact = P.mfma && block_table != nullptr && P.n_split > 1 && B <= 16 * 64;
+    long long grid = (long long)B * h_kv * P.n_hg * P.n_split * P.n_rb;
+    if (p.compact) grid = (grid + 7) & ~7LL;
     if (grid >= (1LL << 31)) return fail(ATTN_ENOTSUP, "problem too large for one launch");
     hipError_t e = P.mfma ? attn::launch_gqa_mfma(p, d_h, P.NW, block_table != nullptr, b == 1,
                                                   (unsigned)grid, (hipStream_t)stream)

@@ -92,6 +92,19 @@ __device__ __forceinline__ float wave_sum(float x)
     x += xor32(x);
     return x;
 }
+// inclusive prefix sum over the 64 lanes of a wavefront (lane l gets the sum
+// of lanes 0 .. l)
+__device__ __forceinline__ int wave_scan_incl(int x)
+{
+    const int lane = threadIdx.x % 64;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(x, d, 64);
+        if (lane >= d) x += t;
+    }
+    return x;
+}
+
 __device__ __forceinline__ float uniform(float x)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));

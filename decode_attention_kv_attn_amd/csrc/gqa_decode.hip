@@ -336,8 +336,11 @@ __global__ __launch_bounds__(64 * NWV) void gqa_combine_kernel(const GqaParams p
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int bh = blockIdx.x;
     const int ns = p.n_split;
-    const int per = (ns + NWV - 1) / NWV;
-    const int k_lo = min(wave * per, ns), k_hi = min(k_lo + per, ns);
+    // only the splits that hold tokens of this row's sequence were written
+    const int len = min(max(p.s[bh / (p.q_len * p.h)], 0), p.s_max);
+    const int nsb = min(ns, (len + p.chunk - 1) / p.chunk);
+    const int per = (nsb + NWV - 1) / NWV;
+    const int k_lo = min(wave * per, nsb), k_hi = min(k_lo + per, nsb);
     const float2* __restrict__ ml = (const float2*)p.part_ml + (size_t)bh * ns;
     const float* __restrict__ po = p.part_o + (size_t)bh * ns * D + lane * PL;
     float M = -INFINITY;

@@ -111,6 +111,50 @@ struct GTileOffsets {
     }
 };
 
+// Splits of every sequence for the compacted grid: sequence 64 c + lane has
+// nb[c] = ceil(min(max(s, 0), s_max) / chunk) splits.  All B lengths are
+// loaded at once (B <= 64 kMaxChunks), so finding a workgroup's pair costs one
+// round trip to memory, as reading its own length would.
+constexpr int kMaxChunks = 16;
+struct SplitCounts {
+    int nb[kMaxChunks];
+    int total;   // wave-uniform
+    __device__ __forceinline__ SplitCounts(const int32_t* __restrict__ s, int B, int s_max, int chunk)
+    {
+        const int lane = threadIdx.x % 64;
+        int t = 0;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; c++) {
+            const int i = 64 * c + lane;
+            nb[c] = i < B ? (min(max(s[i], 0), s_max) + chunk - 1) / chunk : 0;
+            t += nb[c];
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+        total = __builtin_amdgcn_readfirstlane(t);
+    }
+    // the k-th pair (k < total) in sequence-major order: sequence b, split
+    __device__ __forceinline__ void locate(int k, int& b, int& split) const
+    {
+        int carry = 0;
+        b = 0;
+        split = 0;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; c++) {
+            const int incl = wave_scan_incl(nb[c]);
+            const int lo = carry + incl - nb[c];
+            const unsigned long long hit = __builtin_amdgcn_ballot_w64(k >= lo && k < carry + incl);
+            if (hit) {
+                const int L = __builtin_ctzll(hit);
+                b = 64 * c + L;
+                split = k - __builtin_amdgcn_readlane(lo, L);
+                return;
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
+        }
+    }
+};
+
 template <int D, int NW, bool PAGED, bool F8>
 __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                                                            const int32_t* __restrict__ btab)
@@ -126,13 +170,36 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     // XCD-major, so that the KV heads of one sequence, which share every
     // block, run under one L2; a contiguous cache streams faster in plain
     // order (measured).
-    int w = PAGED ? xcd_major(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    // With mixed lengths most (sequence, split) pairs of a grid sized for
+    // s_max are empty, and an empty workgroup still holds a slot while it
+    // loads its length.  Compacted (the grid then has a multiple of 8
+    // workgroups): only the n_real = pairs x KV heads x row blocks items of
+    // the non-empty pairs are numbered, XCD-major, and the surplus
+    // workgroups, last in every XCD's dispatch order, leave at once (the
+    // merge kernel reads only the splits a sequence has).
+    // (paged pools only: mixed lengths are their normal case, and the scan
+    // costs a contiguous cache's uniform batches more than it saves)
+    int w;
+    int split = 0, b = 0;
+    const bool compact = PAGED && p.compact;
+    if (compact) {
+        const SplitCounts sc(p.s, p.B, p.s_max, p.chunk);
+        const int n_real = sc.total * p.h_kv * p.n_rb;
+        const int per = (n_real + 7) / 8, slot = blockIdx.x >> 3;
+        w = (blockIdx.x & 7) * per + slot;
+        if (slot >= per || w >= n_real) return;   // wave-uniform
+        sc.locate(w / (p.h_kv * p.n_rb), b, split);
+    } else {
+        w = PAGED ? xcd_major(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+    }
     const int rb = w % p.n_rb;
     w /= p.n_rb;
     const int j = w % p.h_kv;
     w /= p.h_kv;
-    const int split = w % p.n_split;
-    const int b = w / p.n_split;
+    if (!compact) {
+        split = w % p.n_split;
+        b = w / p.n_split;
+    }
     const int g = p.h / p.h_kv;
     // The rows of a work item are the (query position jq, head of the group)
     // pairs, r = jq * g + gi: g rows for one new token, g * q_len when

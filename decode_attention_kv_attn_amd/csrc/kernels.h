@@ -22,6 +22,7 @@ struct GqaParams {
     int n_hg, n_split, chunk;
     int q_len;           // query positions per sequence (matrix-core kernel only; 1 otherwise)
     int n_rb;            // 64-row blocks per (b, KV head) work item (matrix-core kernel)
+    int compact;         // matrix-core kernel: workgroups map to the non-empty (b, split) pairs only
     float scale_log2;    // scale * log2(e) (times the K scale of an FP8 cache)
     float v_scale;       // V scale of an FP8 cache (1 otherwise)
 };

@@ -122,3 +122,7 @@ def test_fp8_append_bit_exact(paged):
     torch.cuda.synchronize()
     assert np.array_equal(synth.host_bits(d["K8"]), refK)
     assert np.array_equal(synth.host_bits(d["V8"]), refV)
+
+
+def test_fp8_paged_mixed_lengths_many_splits():
+    run_fp8(8, 32, 8, 128, (0, 5000, 1, 700, 0, 9000, 33, 4097), seed=18, paged=True)

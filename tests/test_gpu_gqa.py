@@ -152,3 +152,12 @@ def test_peaked_logits_rescale():
     assert ref_lse[0, 0] > 20
     assert_close(to_f64(out), ref, 2, "out")
     assert_lse_close(to_f64(lse), ref_lse, 2, "lse")
+
+
+def test_paged_mixed_lengths_many_splits():
+    # empty sequences, one-token ones and several splits per sequence in one
+    # paged batch: the workgroups map onto the non-empty (sequence, split)
+    # pairs only, and the merge reads only the splits each sequence has
+    s = (0, 5000, 1, 700, 0, 9000, 33, 4096, 4097, 0, 12000, 64)
+    run_small(12, 16, 2, 128, s, 2, seed=16, paged=True)
+    run_small(12, 8, 8, 64, s, 2, seed=17, paged=True)

@@ -155,3 +155,9 @@ def test_bad_arguments():
                                      q_len, sh.s_max, 8, 2, 128, b, 0.0, None, 0, check=False)
         assert rc == code, (q_len, b, rc, A.attn_last_error())
     assert A.attn_decode_gqa_multi_workspace_bytes(1, 0, 10, 8, 2, 128) == 0
+
+
+def test_paged_mixed_lengths_many_splits():
+    s = (0, 5000, 2, 700, 0, 9000, 33, 4096, 4097, 3)
+    run(10, 4, 32, 8, 128, s, seed=70, paged=True)
+    run(10, 2, 16, 4, 128, s, seed=71, paged=True, fp8=(1 / 64, 1 / 32))

@@ -135,3 +135,77 @@ def test_stream_probe_rejects_bad_arguments():
     assert A.attn_stream_read_probe(FAKE, 0, FAKE, stream=0, check=False) == A.ATTN_EINVAL
     assert A.attn_stream_read_probe(FAKE, unit + 16, FAKE, stream=0, check=False) == A.ATTN_EINVAL
     assert "multiple" in A.attn_last_error()
+
+
+def test_fp8_gqa_argument_errors():
+    kw = dict(out=FAKE, lse=None, q=FAKE, cache_k=FAKE, cache_v=FAKE, k_scale=0.5, v_scale=0.5,
+              s=FAKE, block_table=None, max_blocks=0, block_size=16, num_blocks=0, B=2, s_max=64,
+              h=8, h_kv=2, d_h=128, scale=0.0, workspace=None, workspace_bytes=0, stream=0,
+              check=False)
+    for bad in (dict(k_scale=0.0), dict(v_scale=-1.0), dict(k_scale=float("inf")),
+                dict(v_scale=float("nan"))):
+        assert A.attn_decode_gqa_fp8(**{**kw, **bad}) == A.ATTN_EINVAL, bad
+    assert A.attn_decode_gqa_fp8(**{**kw, "h": 128, "h_kv": 1}) == A.ATTN_ENOTSUP   # g > 64
+    assert A.attn_decode_gqa_fp8(**{**kw, "d_h": 96}) == A.ATTN_ENOTSUP
+    assert A.attn_decode_gqa_fp8(**{**kw, "B": 1, "s_max": 65536}) == A.ATTN_EWORKSPACE
+
+
+def multi_call(**kw):
+    args = dict(out=FAKE, lse=None, q=FAKE, cache_k=FAKE, cache_v=FAKE, s=FAKE, block_table=None,
+                max_blocks=0, block_size=16, num_blocks=0, B=2, q_len=4, s_max=64, h=8, h_kv=2,
+                d_h=128, b=2, scale=0.0, workspace=None, workspace_bytes=0, stream=0, check=False)
+    args.update(kw)
+    return A.attn_decode_gqa_multi(**args)
+
+
+def test_multi_token_argument_errors_and_workspace():
+    assert multi_call(q_len=0) == A.ATTN_EINVAL
+    assert multi_call(q_len=65) == A.ATTN_EINVAL
+    assert multi_call(b=4) == A.ATTN_ENOTSUP
+    assert multi_call(b=1) == A.ATTN_ENOTSUP          # FP8 has its own entry point
+    assert multi_call(h=6, h_kv=4) == A.ATTN_EINVAL
+    assert multi_call(B=1, s_max=65536) == A.ATTN_EWORKSPACE
+    # partials for every (position, head) row of every split
+    ws1 = A.attn_decode_gqa_multi_workspace_bytes(1, 1, 65536, 64, 8, 128)
+    ws4 = A.attn_decode_gqa_multi_workspace_bytes(1, 4, 65536, 64, 8, 128)
+    assert ws1 > 0 and ws4 >= 4 * 64 * 2 * (128 + 2) * 4
+    assert A.attn_decode_gqa_multi_workspace_bytes(1, 0, 64, 8, 2, 128) == 0
+    assert A.attn_decode_gqa_multi_workspace_bytes(1, 65, 64, 8, 2, 128) == 0
+    assert A.attn_decode_gqa_multi_workspace_bytes(1, 2, 64, 6, 4, 128) == 0
+    # for q_len = 1 the plan is the single-token one, whose workspace query covers it
+    assert ws1 <= A.attn_decode_workspace_bytes(0, 1, 65536, 64, 8, 128)
+
+
+def test_merge_argument_errors():
+    kw = dict(out=FAKE, lse=None, o_parts=FAKE, lse_parts=FAKE, n_parts=4, B=2, h=8, d=128,
+              b_parts=2, b_out=2, stream=0, check=False)
+    assert A.attn_merge_partials(**{**kw, "out": None}) == A.ATTN_EINVAL
+    assert A.attn_merge_partials(**{**kw, "n_parts": 0}) == A.ATTN_EINVAL
+    assert A.attn_merge_partials(**{**kw, "h": 0}) == A.ATTN_EINVAL
+    assert A.attn_merge_partials(**{**kw, "d": 6}) == A.ATTN_ENOTSUP
+    assert A.attn_merge_partials(**{**kw, "d": 2048}) == A.ATTN_ENOTSUP
+    assert A.attn_merge_partials(**{**kw, "b_parts": 1}) == A.ATTN_ENOTSUP
+    assert A.attn_merge_partials(**{**kw, "o_parts": FAKE + 8}) == A.ATTN_EINVAL   # not 16-byte aligned
+    assert A.attn_merge_partials(**{**kw, "B": 0}) == A.ATTN_OK                   # nothing to merge
+
+
+def test_mla_fp8_and_fp8_append_argument_errors():
+    kw = dict(out=FAKE, u_latent=None, lse=None, q_nope=FAKE, q_rope=FAKE, w_uk=FAKE, w_uv=FAKE,
+              cache=FAKE, c_scale=0.5, r_scale=0.5, s=FAKE, block_table=None, max_blocks=0,
+              block_size=16, num_blocks=0, B=2, s_max=64, h=128, d_c=512, d_R=64, d_nope=128,
+              d_v=128, scale=0.0, workspace=None, workspace_bytes=0, stream=0, check=False)
+    assert A.attn_decode_mla_absorbed_fp8(**{**kw, "c_scale": 0.0}) == A.ATTN_EINVAL
+    assert A.attn_decode_mla_absorbed_fp8(**{**kw, "r_scale": float("inf")}) == A.ATTN_EINVAL
+    assert A.attn_decode_mla_absorbed_fp8(**{**kw, "d_c": 256}) == A.ATTN_ENOTSUP
+    assert A.attn_decode_mla_absorbed_fp8(**kw) == A.ATTN_EWORKSPACE
+    ak = dict(cache=FAKE, kv_new=FAKE, c_scale=0.5, r_scale=0.5, pos=FAKE, block_table=None,
+              max_blocks=0, block_size=16, num_blocks=0, B=2, s_max=8, d_c=512, d_R=64, stream=0,
+              check=False)
+    assert A.kv_cache_append_mla_fp8(**{**ak, "r_scale": 0.0}) == A.ATTN_EINVAL
+    assert A.kv_cache_append_mla_fp8(**{**ak, "d_c": 510}) == A.ATTN_EINVAL
+    assert A.kv_cache_append_mla_fp8(**{**ak, "kv_new": None}) == A.ATTN_EINVAL
+    fk = dict(cache_k=FAKE, cache_v=FAKE, k_new=FAKE, v_new=FAKE, k_scale=0.5, v_scale=0.5,
+              pos=FAKE, block_table=None, max_blocks=0, block_size=16, num_blocks=0, B=2, s_max=8,
+              h_kv=2, d_h=64, stream=0, check=False)
+    assert A.kv_cache_append_fp8(**{**fk, "v_scale": -2.0}) == A.ATTN_EINVAL
+    assert A.kv_cache_append_fp8(**{**fk, "v_new": None}) == A.ATTN_EINVAL

@@ -6,11 +6,13 @@ decode kernel plus, when the context is split, its merge kernel).  The
 headline workload is the Llama-3-8B-shaped GQA layer (B=64, h=32, h_kv=8,
 d_h=128, every s_i = 4096, bf16); the DeepSeek-V3-shaped absorbed MLA layer
 (B=32, h=128, d_c=512, d_R=64, s=8192) is measured in the same run and
-reported under "mla".  Inputs are synthetic (seeded N(0,1)) and resident in
-HBM before timing starts.
+reported under "mla", together with the E4M3-cache legs ("fp8", "mla.fp8"),
+the 4-token verification leg ("multi") and the context-parallel merge
+("dcp").  Inputs are synthetic (seeded N(0,1)) and resident in HBM before
+timing starts.
 
-Prints ONE JSON line.  --gpus N with N > 1 is refused: this build measures
-one GPU.
+Prints ONE JSON line.  --gpus N with N > 1 is refused: the library has no
+multi-GPU path, and the benchmark measures one GPU.
 """
 from __future__ import annotations
 

@@ -161,3 +161,27 @@ def test_paged_mixed_lengths_many_splits():
     s = (0, 5000, 1, 700, 0, 9000, 33, 4096, 4097, 0, 12000, 64)
     run_small(12, 16, 2, 128, s, 2, seed=16, paged=True)
     run_small(12, 8, 8, 64, s, 2, seed=17, paged=True)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_large_batch_short_sequences(paged):
+    # more sequences than the compacted split mapping scans (B > 1024), with
+    # empty and one-token ones among them; sampled rows against the oracle
+    B = 1500
+    rng = np.random.default_rng(18)
+    s = tuple(int(x) for x in rng.integers(0, 300, size=B))
+    s = (0, 1) + s[2:]
+    sh = synth.GqaShape("t", B=B, h=32, h_kv=8, d_h=128, b=2, s=s, paged=paged, seed=18)
+    print(f"[gqa-largeB] paged={paged}", flush=True)
+    d = synth.draw_gqa(sh, device=DEV)
+    out, lse = A.decode_gqa(d["q"], d["K"], d["V"], d["s"], block_table=d.get("block_table"),
+                            s_max=sh.s_max)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (1, 3), (2, 7), (700, 2), (B - 1, 5)]
+    ref = gqa_sample_reference(d, sh, pairs)
+    g = sh.h // sh.h_kv
+    o64, l64 = to_f64(out), to_f64(lse)
+    for (bi, j), (ro, rl) in ref.items():
+        assert_close(o64[bi, j * g:(j + 1) * g], ro, 2, f"b={bi} j={j}")
+        assert_lse_close(l64[bi, j * g:(j + 1) * g], rl, 2, f"b={bi} j={j}")
+    assert np.all(np.isfinite(o64))

@@ -157,3 +157,9 @@ def test_peaked_logits_take_the_rescaling_path():
         assert_close(to_f64(out[bi:bi + 1]), ro, 2, f"out b={bi}")
         assert_close(to_f64(ul[bi:bi + 1]), ru, 2, f"u_latent b={bi}")
         assert_lse_close(to_f64(lse[bi:bi + 1]), rl, 2, f"lse b={bi}")
+
+
+def test_large_batch_short_sequences():
+    rng = np.random.default_rng(45)
+    s = tuple(int(x) for x in rng.integers(0, 120, size=1200))
+    run(shape(1200, 16, s, seed=45), sample=[0, 1, 599, 1199])

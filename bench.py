@@ -427,6 +427,45 @@ def stream_read_gbps(reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+SWEEP = ["llama3_8b_gqa", "llama3_70b_mha_b16", "llama3_70b_mha_b1", "llama3_70b_gqa8_b16",
+         "llama3_70b_gqa8_b1", "llama3_70b_mqa_b16", "llama3_70b_mqa_b1", "paged_gqa8",
+         "deepseek_v3_mla", "paged_mla"]
+
+
+def sweep(args):
+    """Back-to-back call time of every named workload through the library."""
+    import torch
+    import synth
+    fp8, ql = args.sweep_cache == "fp8", args.sweep_q_len
+    for name in SWEEP:
+        sh = synth.configs()[name]
+        gqa = isinstance(sh, synth.GqaShape)
+        if not gqa and ql > 1:
+            continue
+        if gqa and ql > 1:
+            by = gqa_multi_alg_bytes(sh, ql)
+            run = lambda r: run_gqa_multi(name, ql, args.steps, args.warmup, r)
+        elif gqa and fp8:
+            by = gqa_fp8_alg_bytes(sh)
+            run = lambda r: run_gqa_fp8(name, args.steps, args.warmup, r)
+        elif gqa:
+            by = gqa_alg_bytes(sh)
+            run = lambda r: run_gqa(name, args.steps, args.warmup, r)
+        elif fp8:
+            by = mla_fp8_alg_bytes(sh)
+            run = lambda r: run_mla_fp8(name, args.steps, args.warmup, r)
+        else:
+            by = mla_alg_bytes(sh)
+            run = lambda r: run_mla(name, args.steps, args.warmup, r)
+        rot = max(1, min(16, int(np.ceil(1.2e9 / by))))   # >= 1.2 GB of inputs per rotation
+        _, tot, per = run(rot)
+        us = tot * 1e3 / args.steps
+        print(f"{name:22s} {args.sweep_cache} q_len={ql} rotate={rot:2d}  {us:9.1f} us/call  "
+              f"median {float(np.median(per)) * 1e3:9.1f} us  {by / us / 1e3:7.0f} GB/s  "
+              f"frac {by / us / 1e3 / HBM_PEAK_GBPS:.3f}", flush=True)
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -439,6 +478,12 @@ def main():
     ap.add_argument("--no-dcp", action="store_true")
     ap.add_argument("--no-multi", action="store_true")
     ap.add_argument("--q-len", type=int, default=4, help="drafted tokens in the multi-token leg")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the JSON line: one line per named workload (all GQA/MQA/MHA and "
+                         "MLA shapes), with input sets rotated so the Infinity Cache cannot hold them")
+    ap.add_argument("--sweep-cache", choices=["bf16", "fp8"], default="bf16",
+                    help="cache format of the sweep")
+    ap.add_argument("--sweep-q-len", type=int, default=1, help="new tokens per sequence in the sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -455,6 +500,9 @@ def main():
         sys.exit(2)
     import decode_attention_kv_attn_amd as A
     A.lib()
+    if args.sweep:
+        sweep(args)
+        return
 
     if args.calib_copy:   # a plain copy of known size, for the counter calibration
         x = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB

@@ -98,7 +98,10 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
 #ifndef GQA_MAX_CHUNK
 #define GQA_MAX_CHUNK 4096
 #endif
-    const long long T = 64, min_chunk = 512, max_chunk = GQA_MAX_CHUNK;
+#ifndef GQA_MIN_CHUNK
+#define GQA_MIN_CHUNK 512
+#endif
+    const long long T = 64, min_chunk = GQA_MIN_CHUNK, max_chunk = GQA_MAX_CHUNK;
     const long long units = (long long)B * h_kv * P.n_hg * P.n_rb;
     long long ns = units > 0 ? cdiv(target, units) : 1;
     if (s_max > 0 && ns < cdiv(s_max, max_chunk)) ns = cdiv(s_max, max_chunk);
@@ -559,6 +562,7 @@ int attn_merge_partials(void* out, float* lse, const void* o_parts, const float*
         (uintptr_t)lse % 4 != 0)
         return fail(ATTN_EINVAL, "out and o_parts must be 16-byte aligned, lse arrays 4-byte aligned");
     if (B == 0) return ATTN_OK;
+    if (((long long)B * h + 3) / 4 >= (1LL << 31)) return fail(ATTN_ENOTSUP, "problem too large for one launch");
     attn::MergeParams p{};
     p.out = out;
     p.lse = lse;

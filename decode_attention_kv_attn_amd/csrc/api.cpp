@@ -55,11 +55,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // longest sequences would otherwise set the kernel time) or shorter than 512
 // tokens, and split lengths are multiples of 64 tokens.
 // Several query positions per sequence (q_len > 1) always take the matrix
-// cores: the g * q_len rows of a work item fill the 16-row tiles, in blocks
-// of 64 rows (n_rb blocks, each its own workgroup, when g * q_len > 64).
+// cores: the g * q_len rows of a work item fill the 16-row tiles.  Up to 64
+// rows take one workgroup of 16-row wavefronts; more take 4 wavefronts of
+// two 16-row blocks each (rpw = 2), which read each tile once for 128 rows,
+// in n_rb such workgroups.
 struct GqaPlan {
     bool mfma;
-    int HG, n_hg, NW, n_split, chunk, n_rb;
+    int HG, n_hg, NW, n_split, chunk, n_rb, rpw;
     size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
@@ -74,11 +76,13 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
     const int rows = g * q_len;
     P.mfma = mfma;
     P.n_rb = 1;
+    P.rpw = 1;
     long long target;
     if (mfma) {
         P.HG = g;
         P.n_hg = 1;
-        P.n_rb = (rows + 63) / 64;
+        P.rpw = rows > 64 ? 2 : 1;
+        P.n_rb = (rows + 64 * P.rpw - 1) / (64 * P.rpw);
         // two wavefronts at least: both issue the tile DMA, which keeps more
         // loads in flight per CU than one wavefront's counter allows
 #ifndef GQA_NW_ROWS
@@ -303,7 +307,7 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     // their DMA in flight than two (measured 1-2 % faster; contiguous
     // caches are faster with two when the group has <= 32 rows)
     const int NW = block_table && P.mfma ? 4 : P.NW;
-    hipError_t e = P.mfma ? attn::launch_gqa_mfma(p, d_h, NW, block_table != nullptr, b == 1,
+    hipError_t e = P.mfma ? attn::launch_gqa_mfma(p, d_h, NW, P.rpw, block_table != nullptr, b == 1,
                                                   (unsigned)grid, (hipStream_t)stream)
                           : attn::launch_gqa_decode(p, d_h, b == 4, P.HG, block_table != nullptr,
                                                     (unsigned)grid, (hipStream_t)stream);

@@ -155,7 +155,7 @@ struct SplitCounts {
     }
 };
 
-template <int D, int NW, bool PAGED, bool F8>
+template <int D, int NW, bool PAGED, bool F8, int RPW>
 __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                                                            const int32_t* __restrict__ btab)
 {
@@ -204,15 +204,25 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     // The rows of a work item are the (query position jq, head of the group)
     // pairs, r = jq * g + gi: g rows for one new token, g * q_len when
     // several new tokens are verified at once.  Row block rb holds rows
-    // 64 rb .. 64 rb + 63, wavefront w rows 16 w .. 16 w + 15 of them.
-    const int r0 = 64 * rb + 16 * wave;
-    const int nh = min(16, g * p.q_len - r0);       // rows of this wavefront
-    const bool active = nh > 0;
-    const bool hv = li < nh;                        // this lane's row exists
-    const int r = hv ? r0 + li : r0;
-    const int jq = r / g;
-    const int head = j * g + r % g;
-    const size_t orow = (size_t)(b * p.q_len + jq) * p.h + head;   // row of q, out and lse
+    // 64 RPW rb .. + 64 RPW - 1; wavefront w takes the RPW 16-row blocks
+    // 16 (k NW + w) .. + 15 of them (k < RPW), all fed by the same LDS
+    // operand reads of each tile.
+    const int n_rows = g * p.q_len;
+    bool act[RPW], hv[RPW];
+    size_t orow[RPW];   // row of q, out and lse
+    int jq[RPW];
+    bool active = false;
+#pragma unroll
+    for (int k = 0; k < RPW; k++) {
+        const int r0 = 64 * RPW * rb + 16 * (k * NW + wave);
+        const int nh = min(16, n_rows - r0);        // rows of this block
+        act[k] = nh > 0;
+        active |= act[k];
+        hv[k] = li < nh;                            // this lane's row exists
+        const int r = hv[k] ? r0 + li : r0;
+        jq[k] = r / g;
+        orow[k] = (size_t)(b * p.q_len + jq[k]) * p.h + j * g + r % g;
+    }
 
     const int32_t* __restrict__ s_len = p.s;
     int n = __builtin_amdgcn_readfirstlane(s_len[b]);
@@ -221,21 +231,25 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     const int t1 = min(n, t0 + p.chunk);
     // query position jq sits at cache position n - q_len + jq and sees the
     // tokens before it and itself (causal among the new tokens)
-    const int tl = min(t1, n - (p.q_len - 1 - jq));
+    int tl[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; k++) tl[k] = min(t1, n - (p.q_len - 1 - jq[k]));
 
     if (t0 >= t1) {   // nothing to attend to in this split
-        if (active && hv) {
+#pragma unroll
+        for (int k = 0; k < RPW; k++) {
+            if (!(act[k] && hv[k])) continue;
             if (p.n_split > 1) {
                 if (G == 0) {
-                    float* ml = p.part_ml + (orow * p.n_split + split) * 2;
+                    float* ml = p.part_ml + (orow[k] * p.n_split + split) * 2;
                     ml[0] = -INFINITY;
                     ml[1] = 0.f;
                 }
             } else {
-                uint16_t* o = (uint16_t*)p.out + orow * D;
+                uint16_t* o = (uint16_t*)p.out + orow[k] * D;
 #pragma unroll
                 for (int mc = 0; mc < C::MC; mc++) *(uint2*)(o + 16 * mc + 4 * G) = make_uint2(0, 0);
-                if (G == 0 && p.lse) p.lse[orow] = -INFINITY;
+                if (G == 0 && p.lse) p.lse[orow[k]] = -INFINITY;
             }
         }
         return;
@@ -288,10 +302,15 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         }
     };
 
-    f32x4 O[C::MC];
+    f32x4 O[RPW][C::MC];
+    float m[RPW], lsum[RPW];
 #pragma unroll
-    for (int mc = 0; mc < C::MC; mc++) O[mc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, lsum = 0.f;
+    for (int k = 0; k < RPW; k++) {
+#pragma unroll
+        for (int mc = 0; mc < C::MC; mc++) O[k][mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[k] = -INFINITY;
+        lsum[k] = 0.f;
+    }
 
     // two tiles in flight, then q (the B operand of the score product; zero
     // for padding heads), then the third tile
@@ -302,13 +321,14 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         const size_t a0 = half_row(t0 + i * C::T), a1 = half_row(t0 + i * C::T + 16);
         issue_tile(t0 + i * C::T, i, a0, a1);
     }
-    bf16x8 Qf[C::KS];
-    {
-        const uint16_t* qrow = (const uint16_t*)p.q + orow * D + 8 * G;
+    bf16x8 Qf[RPW][C::KS];
+#pragma unroll
+    for (int k = 0; k < RPW; k++) {
+        const uint16_t* qrow = (const uint16_t*)p.q + orow[k] * D + 8 * G;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ks++)
-            Qf[ks] = (active && hv) ? *(const bf16x8*)(qrow + 32 * ks)
-                                    : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+            Qf[k][ks] = (act[k] && hv[k]) ? *(const bf16x8*)(qrow + 32 * ks)
+                                          : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     }
     vmem_drain();
     {
@@ -349,112 +369,124 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
             for (int mc = 0; mc < C::MC; mc++)
                 va[mc] = F8 ? fp8x8_to_bf16(lds_read_tr8(Vt + to.tr[mc]))
                             : cat_tr(lds_read_tr(Vt + to.tr[mc]), lds_read_tr(Vt + to.tr[mc] + 16 * C::RB));
-            // ---- scores S^T = K . q^T
-            f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ks++) {
-                S[0] = mfma16(ka[ks][0], Qf[ks], S[0]);
-                S[1] = mfma16(ka[ks][1], Qf[ks], S[1]);
-            }
-            // ---- online softmax: lane holds head li, tokens 16 mt + 4G + e
-            float z[2][4];
-            float lm = -INFINITY;
+            for (int k = 0; k < RPW; k++) {
+                if (RPW > 1 && !act[k]) continue;   // wave-uniform
+                // ---- scores S^T = K . q^T
+                f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int tok = tb + 16 * mt + 4 * G + e;
-                    z[mt][e] = tok < tl ? S[mt][e] * p.scale_log2 : -INFINITY;
-                    lm = fmaxf(lm, z[mt][e]);
+                for (int ks = 0; ks < C::KS; ks++) {
+                    S[0] = mfma16(ka[ks][0], Qf[k][ks], S[0]);
+                    S[1] = mfma16(ka[ks][1], Qf[k][ks], S[1]);
                 }
-            lm = fmaxf(lm, xor16(lm));
-            lm = fmaxf(lm, xor32(lm));
-            const bool move = lm > m + 8.f;
-            const float mn = move ? lm : m;
-            const float alpha = move ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
-            m = mn;
-            // a row that has seen no visible token yet (possible only for the
-            // earlier of several query positions) keeps m = -inf: weights 0
-            const float mb = mn == -INFINITY ? 0.f : mn;
-            uint32_t pk[4];
-            float ps = 0.f;
+                // ---- online softmax: lane holds row li, tokens 16 mt + 4G + e
+                float z[2][4];
+                float lm = -INFINITY;
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++)
+                for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-                for (int e = 0; e < 4; e += 2) {
-                    const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mb),
-                                                    __builtin_amdgcn_exp2f(z[mt][e + 1] - mb));
-                    pk[mt * 2 + e / 2] = wv;
-                    ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
+                    for (int e = 0; e < 4; e++) {
+                        const int tok = tb + 16 * mt + 4 * G + e;
+                        z[mt][e] = tok < tl[k] ? S[mt][e] * p.scale_log2 : -INFINITY;
+                        lm = fmaxf(lm, z[mt][e]);
+                    }
+                lm = fmaxf(lm, xor16(lm));
+                lm = fmaxf(lm, xor32(lm));
+                const bool move = lm > m[k] + 8.f;
+                const float mn = move ? lm : m[k];
+                const float alpha = move ? __builtin_amdgcn_exp2f(m[k] - mn) : 1.f;
+                m[k] = mn;
+                // a row that has seen no visible token yet (possible only for
+                // the earlier of several query positions) keeps m = -inf:
+                // weights 0
+                const float mb = mn == -INFINITY ? 0.f : mn;
+                uint32_t pk[4];
+                float ps = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                    for (int e = 0; e < 4; e += 2) {
+                        const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mb),
+                                                        __builtin_amdgcn_exp2f(z[mt][e + 1] - mb));
+                        pk[mt * 2 + e / 2] = wv;
+                        ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
+                    }
+                lsum[k] = lsum[k] * alpha + ps;
+                if (__builtin_amdgcn_ballot_w64(move)) {
+#pragma unroll
+                    for (int mc = 0; mc < C::MC; mc++) O[k][mc] *= alpha;
                 }
-            lsum = lsum * alpha + ps;
-            if (__builtin_amdgcn_ballot_w64(move)) {
+                const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                // ---- O^T += V^T . P^T
 #pragma unroll
-                for (int mc = 0; mc < C::MC; mc++) O[mc] *= alpha;
+                for (int mc = 0; mc < C::MC; mc++) O[k][mc] = mfma16(va[mc], P, O[k][mc]);
             }
-            const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-            // ---- O^T += V^T . P^T
-#pragma unroll
-            for (int mc = 0; mc < C::MC; mc++) O[mc] = mfma16(va[mc], P, O[mc]);
         }
         buf = (buf + 1) % C::NBUF;
     }
     wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
 
     if (!active) return;
-    float l = lsum;
-    l += xor16(l);
-    l += xor32(l);
-    if (!hv) return;
-    if (F8) {   // the V scale of an FP8 cache (the K scale is folded into scale_log2)
 #pragma unroll
-        for (int mc = 0; mc < C::MC; mc++) O[mc] *= p.v_scale;
-    }
-    if (p.n_split == 1) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;   // l = 0: no visible token (0 and -inf)
-        uint16_t* o = (uint16_t*)p.out + orow * D + 4 * G;
+    for (int k = 0; k < RPW; k++) {
+        if (!act[k]) continue;   // wave-uniform
+        float l = lsum[k];
+        l += xor16(l);
+        l += xor32(l);
+        if (!hv[k]) continue;
+        if (F8) {   // the V scale of an FP8 cache (the K scale is folded into scale_log2)
 #pragma unroll
-        for (int mc = 0; mc < C::MC; mc++)
-            *(uint2*)(o + 16 * mc) = make_uint2(pack_bf16x2(O[mc][0] * inv, O[mc][1] * inv),
-                                                pack_bf16x2(O[mc][2] * inv, O[mc][3] * inv));
-        if (G == 0 && p.lse) p.lse[orow] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-    } else {
-        const size_t pi = orow * p.n_split + split;
-        float* po = p.part_o + pi * D + 4 * G;
+            for (int mc = 0; mc < C::MC; mc++) O[k][mc] *= p.v_scale;
+        }
+        if (p.n_split == 1) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;   // l = 0: no visible token (0 and -inf)
+            uint16_t* o = (uint16_t*)p.out + orow[k] * D + 4 * G;
 #pragma unroll
-        for (int mc = 0; mc < C::MC; mc++)
-            *(float4*)(po + 16 * mc) = make_float4(O[mc][0], O[mc][1], O[mc][2], O[mc][3]);
-        if (G == 0) {
-            p.part_ml[pi * 2] = m;
-            p.part_ml[pi * 2 + 1] = l;
+            for (int mc = 0; mc < C::MC; mc++)
+                *(uint2*)(o + 16 * mc) = make_uint2(pack_bf16x2(O[k][mc][0] * inv, O[k][mc][1] * inv),
+                                                    pack_bf16x2(O[k][mc][2] * inv, O[k][mc][3] * inv));
+            if (G == 0 && p.lse) p.lse[orow[k]] = l > 0.f ? (m[k] + __log2f(l)) * kLn2 : -INFINITY;
+        } else {
+            const size_t pi = orow[k] * p.n_split + split;
+            float* po = p.part_o + pi * D + 4 * G;
+#pragma unroll
+            for (int mc = 0; mc < C::MC; mc++)
+                *(float4*)(po + 16 * mc) = make_float4(O[k][mc][0], O[k][mc][1], O[k][mc][2], O[k][mc][3]);
+            if (G == 0) {
+                p.part_ml[pi * 2] = m[k];
+                p.part_ml[pi * 2 + 1] = l;
+            }
         }
     }
 }
 
-template <int D, int NW, bool F8>
+template <int D, int NW, bool F8, int RPW>
 static hipError_t launch_nw(const GqaParams& p, bool paged, unsigned grid, hipStream_t st)
 {
     if (paged)
-        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
     else
-        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false, F8>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false, F8, RPW>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
     return hipGetLastError();
 }
 
+// (NW, RPW) in {(2, 1), (4, 1), (4, 2)}: 32, 64 or 128 rows per workgroup
 template <int D, bool F8>
-static hipError_t launch_mfma_d(const GqaParams& p, int NW, bool paged, unsigned grid, hipStream_t st)
+static hipError_t launch_mfma_d(const GqaParams& p, int NW, int rpw, bool paged, unsigned grid,
+                                hipStream_t st)
 {
-    return NW == 2 ? launch_nw<D, 2, F8>(p, paged, grid, st) : launch_nw<D, 4, F8>(p, paged, grid, st);
+    if (NW == 2) return launch_nw<D, 2, F8, 1>(p, paged, grid, st);
+    return rpw == 2 ? launch_nw<D, 4, F8, 2>(p, paged, grid, st) : launch_nw<D, 4, F8, 1>(p, paged, grid, st);
 }
 
-hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, bool f8, unsigned grid,
-                           hipStream_t st)
+hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, int rpw, bool paged, bool f8,
+                           unsigned grid, hipStream_t st)
 {
     hipError_t e;
-    if (f8) e = d_h == 64 ? launch_mfma_d<64, true>(p, NW, paged, grid, st)
-                          : launch_mfma_d<128, true>(p, NW, paged, grid, st);
-    else e = d_h == 64 ? launch_mfma_d<64, false>(p, NW, paged, grid, st)
-                       : launch_mfma_d<128, false>(p, NW, paged, grid, st);
+    if (f8) e = d_h == 64 ? launch_mfma_d<64, true>(p, NW, rpw, paged, grid, st)
+                          : launch_mfma_d<128, true>(p, NW, rpw, paged, grid, st);
+    else e = d_h == 64 ? launch_mfma_d<64, false>(p, NW, rpw, paged, grid, st)
+                       : launch_mfma_d<128, false>(p, NW, rpw, paged, grid, st);
     if (e != hipSuccess || p.n_split == 1) return e;
     return launch_gqa_combine(p, d_h, false, st);
 }

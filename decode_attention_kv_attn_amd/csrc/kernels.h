@@ -21,7 +21,7 @@ struct GqaParams {
     int B, s_max, h, h_kv;
     int n_hg, n_split, chunk;
     int q_len;           // query positions per sequence (matrix-core kernel only; 1 otherwise)
-    int n_rb;            // 64-row blocks per (b, KV head) work item (matrix-core kernel)
+    int n_rb;            // row blocks (64 or 128 rows) per (b, KV head) work item (matrix-core kernel)
     int compact;         // matrix-core kernel: workgroups map to the non-empty (b, split) pairs only
     float scale_log2;    // scale * log2(e) (times the K scale of an FP8 cache)
     float v_scale;       // V scale of an FP8 cache (1 otherwise)
@@ -32,8 +32,8 @@ hipError_t launch_gqa_decode(const GqaParams& p, int d_h, bool f32, int HG, bool
                              unsigned grid, hipStream_t st);
 // matrix-core kernel (bf16 or FP8 E4M3 caches, g <= 16 NW, NW = 2 or 4), then the split
 // merge when n_split > 1
-hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, bool paged, bool f8, unsigned grid,
-                           hipStream_t st);
+hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, int rpw, bool paged, bool f8,
+                           unsigned grid, hipStream_t st);
 hipError_t launch_gqa_combine(const GqaParams& p, int d_h, bool f32, hipStream_t st);
 
 struct AppendParams {

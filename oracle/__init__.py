@@ -23,6 +23,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# a copy of oracle.c built elsewhere, loaded instead of liboracle.so: the
+# planted-mistake tests run the pins against such copies in a subprocess
+_OVERRIDE = os.environ.get("ATTN_ORACLE_LIB")
 _lib = None
 
 
@@ -47,9 +50,12 @@ def threads() -> int:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        lib = C.CDLL(_LIB)
+        if _OVERRIDE:
+            lib = C.CDLL(_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            lib = C.CDLL(_LIB)
         P, I, D = C.c_void_p, C.c_int, C.c_double
         lib.ref_kv_cell_bytes.restype = C.c_ulonglong
         lib.ref_kv_cell_bytes.argtypes = [I, I, I, I]

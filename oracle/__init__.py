@@ -88,6 +88,11 @@ def _load():
                                              I, I, I, I, D]
         lib.ref_kv_append_mla_fp8.restype = I
         lib.ref_kv_append_mla_fp8.argtypes = [P, P, C.c_float, C.c_float, P, P, I, I, I, I, I, I]
+        lib.ref_gqa_decode_fp8_paged_scales.restype = I
+        lib.ref_gqa_decode_fp8_paged_scales.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I,
+                                                        I, D]
+        lib.ref_kv_append_fp8_paged_scales.restype = I
+        lib.ref_kv_append_fp8_paged_scales.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I]
         lib.ref_merge_partials.restype = I
         lib.ref_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I]
         _lib = lib
@@ -439,3 +444,47 @@ def kv_append_mla_fp8(cache8, kv_new, c_scale, r_scale, pos, d_c, block_table=No
     if rc != 0:
         raise ValueError(f"ref_kv_append_mla_fp8 rejected its arguments ({rc})")
     return c
+
+
+def gqa_decode_fp8_paged_scales(q, K8, V8, k_scales, v_scales, s, block_table, block_size=16,
+                                scale=None):
+    """Reference decode over a paged E4M3 cache with one scale per page and KV
+    head (k_scales, v_scales float32 [N_blk, h_kv]).  Shapes as gqa_decode."""
+    q = _stored(q, 2)
+    K8 = np.ascontiguousarray(K8, dtype=np.uint8)
+    V8 = np.ascontiguousarray(V8, dtype=np.uint8)
+    ks = np.ascontiguousarray(k_scales, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scales, dtype=np.float32)
+    B, h, d_h = q.shape
+    h_kv = K8.shape[2]
+    s = _i32(s)
+    bt = _i32(block_table)
+    _check_table(bt, K8.shape[0] * K8.shape[1], block_size, s)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    out = np.zeros((B, h, d_h))
+    lse = np.zeros((B, h))
+    rc = _load().ref_gqa_decode_fp8_paged_scales(_ptr(out), _ptr(lse), _ptr(q), _ptr(K8), _ptr(V8),
+                                                 _ptr(ks), _ptr(vs), _ptr(s), _ptr(bt), bt.shape[1],
+                                                 block_size, B, h, h_kv, d_h, float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_gqa_decode_fp8_paged_scales rejected its arguments ({rc})")
+    return out, lse
+
+
+def kv_append_fp8_paged_scales(cache_k, cache_v, k_new, v_new, k_scales, v_scales, pos,
+                               block_table, block_size=16):
+    """Host image of kv_cache_append_fp8_paged_scales (new uint8 pools)."""
+    ck = np.array(cache_k, dtype=np.uint8, copy=True)
+    cv = np.array(cache_v, dtype=np.uint8, copy=True)
+    k_new, v_new = _stored(k_new, 2), _stored(v_new, 2)
+    B, h_kv, d_h = k_new.shape
+    bt = _i32(block_table)
+    rc = _load().ref_kv_append_fp8_paged_scales(
+        _ptr(ck), _ptr(cv), _ptr(k_new), _ptr(v_new),
+        _ptr(np.ascontiguousarray(k_scales, dtype=np.float32)),
+        _ptr(np.ascontiguousarray(v_scales, dtype=np.float32)), _ptr(_i32(pos)), _ptr(bt),
+        bt.shape[1], block_size, B, h_kv, d_h)
+    if rc != 0:
+        raise ValueError(f"ref_kv_append_fp8_paged_scales rejected its arguments ({rc})")
+    return ck, cv

@@ -714,3 +714,100 @@ int ref_gqa_decode_multi(double* out, double* lse, const void* q, const void* k,
     }
     return bad ? OR_EINVAL : OR_OK;
 }
+
+/*
+ * Decode attention over a paged FP8 cache with one scale per page and KV
+ * head: K(b,t,j,d) = decode(code) * k_scales[blk * h_kv + j] with blk =
+ * block_table[b][t / block_size] (V likewise), the per-block scaling of a
+ * quantised cache that "Multi-Head Latent Attention (MLA): Mathematical
+ * Foundations ...", section "High-Throughput Serving Kernels: FlashMLA and
+ * SGLang", describes.  Otherwise as ref_gqa_decode_fp8 (block_table
+ * required).
+ */
+int ref_gqa_decode_fp8_paged_scales(double* out, double* lse, const void* q, const uint8_t* k,
+                                    const uint8_t* v, const float* k_scales,
+                                    const float* v_scales, const int32_t* s,
+                                    const int32_t* block_table, int max_blocks, int block_size,
+                                    int B, int h, int h_kv, int d_h, double scale)
+{
+    if (!out || !q || !k || !v || !k_scales || !v_scales || !s || !block_table) return OR_EINVAL;
+    if (B < 0 || h <= 0 || h_kv <= 0 || d_h <= 0 || (h % h_kv) != 0) return OR_EINVAL;
+    if (block_size <= 0 || max_blocks <= 0) return OR_EINVAL;
+    const int g = h / h_kv;
+    const long rows = (long)B * h;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long r = 0; r < rows; r++) {
+        const int bb = (int)(r / h), i = (int)(r % h), j = i / g;
+        const int n = s[bb];
+        double* o = out + (size_t)r * d_h;
+        if (n < 0 || n > max_blocks * block_size ||
+            !table_ok(block_table, max_blocks, block_size, bb, n)) {
+            bad = 1;
+            continue;
+        }
+        if (n == 0) {
+            for (int d = 0; d < d_h; d++) o[d] = 0.0;
+            if (lse) lse[r] = -INFINITY;
+            continue;
+        }
+        double* z = (double*)malloc(sizeof(double) * (size_t)n * 2);
+        double* p = z + n;
+        const size_t qoff = (size_t)r * d_h;
+        for (int t = 0; t < n; t++) {
+            const int blk = block_table[(size_t)bb * max_blocks + t / block_size];
+            const double ks = (double)k_scales[(size_t)blk * h_kv + j];
+            const size_t koff = (row_of(block_table, max_blocks, block_size, 0, bb, t) * h_kv + j) * d_h;
+            double acc = 0.0;
+            for (int d = 0; d < d_h; d++) acc += ld(q, qoff + d, 2) * ld_fp8(k, koff + d, ks);
+            z[t] = scale * acc;
+        }
+        double m;
+        const double l = softmax_weights(z, n, p, &m);
+        for (int d = 0; d < d_h; d++) {
+            double acc = 0.0;
+            for (int t = 0; t < n; t++) {
+                const int blk = block_table[(size_t)bb * max_blocks + t / block_size];
+                const double vs = (double)v_scales[(size_t)blk * h_kv + j];
+                const size_t voff = (row_of(block_table, max_blocks, block_size, 0, bb, t) * h_kv + j) * d_h;
+                acc += p[t] * ld_fp8(v, voff + d, vs);
+            }
+            o[d] = acc / l;
+        }
+        if (lse) lse[r] = m + log(l);
+        free(z);
+    }
+    return bad ? OR_EINVAL : OR_OK;
+}
+
+/*
+ * Append into a paged FP8 cache with per-page scales: element x of the bf16
+ * rows becomes encode(x * (1 / scale of its page and KV head)), the
+ * reciprocal and the product in fp32, at slot pos[b].
+ */
+int ref_kv_append_fp8_paged_scales(uint8_t* cache_k, uint8_t* cache_v, const void* k_new,
+                                   const void* v_new, const float* k_scales,
+                                   const float* v_scales, const int32_t* pos,
+                                   const int32_t* block_table, int max_blocks, int block_size,
+                                   int B, int h_kv, int d_h)
+{
+    if (!cache_k || !cache_v || !k_new || !v_new || !k_scales || !v_scales || !pos || !block_table)
+        return OR_EINVAL;
+    if (B < 0 || h_kv <= 0 || d_h <= 0 || block_size <= 0 || max_blocks <= 0) return OR_EINVAL;
+    const size_t n = (size_t)h_kv * d_h;
+    for (int bb = 0; bb < B; bb++) {
+        const int t = pos[bb];
+        if (t < 0 || t >= max_blocks * block_size) return OR_EINVAL;
+        const int blk = block_table[(size_t)bb * max_blocks + t / block_size];
+        if (blk < 0) return OR_EINVAL;
+        const size_t row = row_of(block_table, max_blocks, block_size, 0, bb, t);
+        for (size_t e = 0; e < n; e++) {
+            const int j = (int)(e / d_h);
+            const float ik = 1.0f / k_scales[(size_t)blk * h_kv + j];
+            const float iv = 1.0f / v_scales[(size_t)blk * h_kv + j];
+            cache_k[row * n + e] = (uint8_t)ref_fp8_e4m3_encode((float)ld(k_new, (size_t)bb * n + e, 2) * ik);
+            cache_v[row * n + e] = (uint8_t)ref_fp8_e4m3_encode((float)ld(v_new, (size_t)bb * n + e, 2) * iv);
+        }
+    }
+    return OR_OK;
+}

@@ -139,3 +139,62 @@ def test_fp8_append_matches_numpy_scatter():
         ek[bi, pos[bi]] = torch_codes(np.clip(yk, -448, 448))
         ev[bi, pos[bi]] = torch_codes(np.clip(yv, -448, 448))
     assert np.array_equal(nk, ek) and np.array_equal(nv, ev)
+
+
+def paged_fp8_case(seed, B=3, h=8, h_kv=2, d=64, s=(40, 17, 70)):
+    rng = np.random.default_rng(seed)
+    nblk = [(n + 15) // 16 for n in s]
+    N = sum(nblk)
+    perm = rng.permutation(N)
+    bt = np.full((B, max(nblk)), -1, np.int32)
+    k = 0
+    for bi in range(B):
+        for jb in range(nblk[bi]):
+            bt[bi, jb] = perm[k]
+            k += 1
+    q = bf16_bits(rng.standard_normal((B, h, d)))
+    # per (page, KV head) powers of two, so that dequantised values are exact in fp32
+    ks = (2.0 ** rng.integers(-8, -2, size=(N, h_kv))).astype(np.float32)
+    vs = (2.0 ** rng.integers(-8, -2, size=(N, h_kv))).astype(np.float32)
+    K8 = oracle.fp8_encode((rng.standard_normal((N, 16, h_kv, d)) / ks[:, None, :, None]).astype(np.float32))
+    V8 = oracle.fp8_encode((rng.standard_normal((N, 16, h_kv, d)) / vs[:, None, :, None]).astype(np.float32))
+    return q, K8, V8, ks, vs, np.array(s, np.int32), bt
+
+
+def test_per_page_scales_equal_the_dequantised_paged_oracle():
+    q, K8, V8, ks, vs, s, bt = paged_fp8_case(7)
+    out, lse = oracle.gqa_decode_fp8_paged_scales(q, K8, V8, ks, vs, s, bt)
+    Kd = (oracle.fp8_decode(K8) * ks[:, None, :, None]).astype(np.float32)
+    Vd = (oracle.fp8_decode(V8) * vs[:, None, :, None]).astype(np.float32)
+    ro, rl = oracle.gqa_decode(widen(q).astype(np.float32), Kd, Vd, s, 4, block_table=bt)
+    assert np.max(np.abs(out - ro)) < 1e-12 and np.max(np.abs(lse - rl)) < 1e-12
+
+
+def test_uniform_per_page_scales_equal_the_per_tensor_oracle():
+    q, K8, V8, ks, vs, s, bt = paged_fp8_case(8)
+    ks[:] = 0.03
+    vs[:] = 0.07
+    out, lse = oracle.gqa_decode_fp8_paged_scales(q, K8, V8, ks, vs, s, bt)
+    ro, rl = oracle.gqa_decode_fp8(q, K8, V8, 0.03, 0.07, s, block_table=bt)
+    assert np.array_equal(out, ro) and np.array_equal(lse, rl)
+
+
+def test_per_page_append_uses_its_pages_scale():
+    rng = np.random.default_rng(9)
+    q, K8, V8, ks, vs, s, bt = paged_fp8_case(9)
+    B, h_kv, d = 3, 2, 64
+    kn = bf16_bits(rng.standard_normal((B, h_kv, d)) * 0.3)
+    vn = bf16_bits(rng.standard_normal((B, h_kv, d)) * 0.3)
+    pos = np.array([39, 0, 69], np.int32)
+    ck, cv = oracle.kv_append_fp8_paged_scales(K8, V8, kn, vn, ks, vs, pos, bt)
+    wk, wv = K8.copy(), V8.copy()
+    for bi in range(B):
+        blk = bt[bi, pos[bi] // 16]
+        for j in range(h_kv):
+            ik = np.float32(1.0) / ks[blk, j]
+            iv = np.float32(1.0) / vs[blk, j]
+            xk = torch.from_numpy(widen(kn[bi, j]).astype(np.float32) * ik)
+            xv = torch.from_numpy(widen(vn[bi, j]).astype(np.float32) * iv)
+            wk[blk, pos[bi] % 16, j] = xk.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            wv[blk, pos[bi] % 16, j] = xv.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ck, wk) and np.array_equal(cv, wv)

@@ -44,6 +44,9 @@ MUTANTS = [
     ("append_neighbour_element", "const float xk = (float)ld(k_new, (size_t)bb * n + e, 2);",
      "const float xk = (float)ld(k_new, (size_t)bb * n + (e ^ 1), 2);", 0,
      ["test_oracle_fp8.py"]),
+    ("page_scale_by_logical_block", "const double ks = (double)k_scales[(size_t)blk * h_kv + j];",
+     "const double ks = (double)k_scales[(size_t)(t / block_size) * h_kv + j];", 0,
+     ["test_oracle_fp8.py"]),
     ("cell_factor_two_dropped", "return 2ULL * (unsigned long long)L", "return 1ULL * (unsigned long long)L",
      0, ["test_oracle_cells.py"]),
 ]

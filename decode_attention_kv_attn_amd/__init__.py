@@ -34,6 +34,8 @@ EXPORTED = (
     "attn_decode_gqa_multi_workspace_bytes",
     "attn_decode_mla_absorbed_fp8",
     "kv_cache_append_mla_fp8",
+    "attn_decode_gqa_fp8_paged_scales",
+    "kv_cache_append_fp8_paged_scales",
 )
 
 _lib = None
@@ -89,6 +91,12 @@ def lib():
                                                    I, I, I, I, I, I, I, F, P, Z, P]
         L.kv_cache_append_mla_fp8.restype = I
         L.kv_cache_append_mla_fp8.argtypes = [P, P, F, F, P, P, I, I, I, I, I, I, I, P]
+        L.attn_decode_gqa_fp8_paged_scales.restype = I
+        L.attn_decode_gqa_fp8_paged_scales.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                                       I, I, F, P, Z, P]
+        L.kv_cache_append_fp8_paged_scales.restype = I
+        L.kv_cache_append_fp8_paged_scales.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                                       P]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -217,6 +225,28 @@ def kv_cache_append_mla_fp8(cache, kv_new, c_scale, r_scale, pos, block_table, m
     rc = lib().kv_cache_append_mla_fp8(_p(cache), _p(kv_new), float(c_scale), float(r_scale),
                                        _p(pos), _p(block_table), max_blocks, block_size,
                                        num_blocks, B, s_max, d_c, d_R, _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_gqa_fp8_paged_scales(out, lse, q, cache_k, cache_v, k_scales, v_scales, s,
+                                     block_table, max_blocks, block_size, num_blocks, B, s_max, h,
+                                     h_kv, d_h, scale, workspace, workspace_bytes, stream=None,
+                                     check=True):
+    rc = lib().attn_decode_gqa_fp8_paged_scales(_p(out), _p(lse), _p(q), _p(cache_k), _p(cache_v),
+                                                _p(k_scales), _p(v_scales), _p(s), _p(block_table),
+                                                max_blocks, block_size, num_blocks, B, s_max, h,
+                                                h_kv, d_h, float(scale), _p(workspace),
+                                                int(workspace_bytes), _stream(stream))
+    return _check(rc) if check else rc
+
+
+def kv_cache_append_fp8_paged_scales(cache_k, cache_v, k_new, v_new, k_scales, v_scales, pos,
+                                     block_table, max_blocks, block_size, num_blocks, B, s_max,
+                                     h_kv, d_h, stream=None, check=True):
+    rc = lib().kv_cache_append_fp8_paged_scales(_p(cache_k), _p(cache_v), _p(k_new), _p(v_new),
+                                                _p(k_scales), _p(v_scales), _p(pos),
+                                                _p(block_table), max_blocks, block_size,
+                                                num_blocks, B, s_max, h_kv, d_h, _stream(stream))
     return _check(rc) if check else rc
 
 

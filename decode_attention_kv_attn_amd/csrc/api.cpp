@@ -246,7 +246,8 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
                const int32_t* s, const int32_t* block_table, int max_blocks, int block_size,
                int num_blocks, int B, int s_max, int h, int h_kv, int d_h, int b, float scale,
                float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
-               void* stream, int q_len = 1)
+               void* stream, int q_len = 1, const float* k_scales = nullptr,
+               const float* v_scales = nullptr)
 {
     if (!out || !q || !cache_k || !cache_v || !s)
         return fail(ATTN_EINVAL, "null out, q, cache_k, cache_v or s");
@@ -296,6 +297,8 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d_h);
     p.scale_log2 = sc * k_scale * 1.4426950408889634f;
     p.v_scale = v_scale;
+    p.k_scales = k_scales;
+    p.v_scales = v_scales;
     // matrix-core kernel over a paged pool with splits: workgroups go to the
     // non-empty (b, split) pairs only (each workgroup scans the B lengths to
     // find its pair, so only for moderate B); the grid is then a multiple of 8
@@ -541,6 +544,58 @@ int attn_decode_gqa_multi_fp8(void* out, float* lse, const void* q, const void* 
     return decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
                       num_blocks, B, s_max, h, h_kv, d_h, 1, scale, k_scale, v_scale, workspace,
                       workspace_bytes, stream, q_len);
+}
+
+int attn_decode_gqa_fp8_paged_scales(void* out, float* lse, const void* q, const void* cache_k,
+                                     const void* cache_v, const float* k_scales,
+                                     const float* v_scales, const int32_t* s,
+                                     const int32_t* block_table, int max_blocks, int block_size,
+                                     int num_blocks, int B, int s_max, int h, int h_kv, int d_h,
+                                     float scale, void* workspace, size_t workspace_bytes,
+                                     void* stream)
+{
+    if (!k_scales || !v_scales) return fail(ATTN_EINVAL, "null k_scales or v_scales");
+    if (!block_table) return fail(ATTN_EINVAL, "per-page scales need a paged cache (block_table)");
+    return decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
+                      num_blocks, B, s_max, h, h_kv, d_h, 1, scale, 1.f, 1.f, workspace,
+                      workspace_bytes, stream, 1, k_scales, v_scales);
+}
+
+int kv_cache_append_fp8_paged_scales(void* cache_k, void* cache_v, const void* k_new,
+                                     const void* v_new, const float* k_scales,
+                                     const float* v_scales, const int32_t* pos,
+                                     const int32_t* block_table, int max_blocks, int block_size,
+                                     int num_blocks, int B, int s_max, int h_kv, int d_h,
+                                     void* stream)
+{
+    if (!cache_k || !cache_v || !k_new || !v_new || !pos || !k_scales || !v_scales)
+        return fail(ATTN_EINVAL, "null cache, new rows, pos or scales");
+    if (!block_table) return fail(ATTN_EINVAL, "per-page scales need a paged cache (block_table)");
+    if (B < 0 || h_kv <= 0 || d_h <= 0 || d_h % 4 != 0)
+        return fail(ATTN_EINVAL, "bad sizes (d_h must be a positive multiple of 4)");
+    int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
+    if (rc) return rc;
+    attn::AppendParams pk{};
+    pk.cache = cache_k;
+    pk.src = k_new;
+    pk.pos = pos;
+    pk.bt = block_table;
+    pk.max_blocks = max_blocks;
+    pk.bs_log2 = ilog2(block_size);
+    pk.num_blocks = num_blocks;
+    pk.s_max = s_max;
+    pk.row_bytes = (long long)h_kv * d_h;
+    pk.inv_scale = pk.inv_scale2 = 1.f;
+    pk.split = pk.row_bytes;
+    pk.page_scales = k_scales;
+    pk.d_h = d_h;
+    attn::AppendParams pv = pk;
+    pv.cache = cache_v;
+    pv.src = v_new;
+    pv.page_scales = v_scales;
+    hipError_t e = attn::launch_append_fp8(pk, &pv, B, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_cache_append_fp8_paged_scales launch");
+    return ATTN_OK;
 }
 
 size_t attn_decode_gqa_multi_workspace_bytes(int B, int q_len, int s_max, int h, int h_kv, int d_h)

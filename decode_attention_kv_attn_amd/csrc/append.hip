@@ -86,9 +86,10 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendParams pk, 
     const int t = p.pos[b];
     if (t < 0) return;
     size_t row;
+    int blk = 0;
     if (p.bt) {
         if (t >= (p.max_blocks << p.bs_log2)) return;
-        const int blk = p.bt[(size_t)b * p.max_blocks + (t >> p.bs_log2)];
+        blk = p.bt[(size_t)b * p.max_blocks + (t >> p.bs_log2)];
         if (blk < 0 || blk >= p.num_blocks) return;
         row = ((size_t)blk << p.bs_log2) + (size_t)(t & ((1 << p.bs_log2) - 1));
     } else {
@@ -100,7 +101,9 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendParams pk, 
     const uint2* src = (const uint2*)((const uint16_t*)p.src + (size_t)b * p.row_bytes);
     for (long long i = threadIdx.x; i < n4; i += blockDim.x) {
         const uint2 w = src[i];
-        const float is = 4 * i < p.split ? p.inv_scale : p.inv_scale2;   // MLA: latent, then rotary part
+        float is = 4 * i < p.split ? p.inv_scale : p.inv_scale2;   // MLA: latent, then rotary part
+        if (p.page_scales)   // this page's scale for the KV head of these 4 elements
+            is = 1.0f / p.page_scales[(size_t)blk * (p.row_bytes / p.d_h) + (4 * i) / p.d_h];
         const uint32_t c0 = e4m3_code(bf16lo_to_f32(w.x) * is);
         const uint32_t c1 = e4m3_code(bf16hi_to_f32(w.x) * is);
         const uint32_t c2 = e4m3_code(bf16lo_to_f32(w.y) * is);

@@ -155,7 +155,7 @@ struct SplitCounts {
     }
 };
 
-template <int D, int NW, bool PAGED, bool F8, int RPW>
+template <int D, int NW, bool PAGED, bool F8, int RPW, bool PS = false>
 __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                                                            const int32_t* __restrict__ btab)
 {
@@ -316,10 +316,29 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     // for padding heads), then the third tile
     // NBUF - 2 tiles in flight, then q (the B operand of the score product;
     // zero for padding heads), then one more tile
+    // Per-page scales of a paged E4M3 cache (one per page and KV head):
+    // a tile's two 16-token halves lie in one page each, so each half has one
+    // K and one V scale.  They are read (scalar loads) when the tile is
+    // issued and carried in a queue of AH entries to its compute iteration.
+    constexpr int AH = C::NBUF - 1;   // tiles in flight ahead of the one in use
+    constexpr bool ps = F8 && PAGED && PS;
+    const float* __restrict__ ksp = p.k_scales;
+    const float* __restrict__ vsp = p.v_scales;
+    float qk[AH][2], qv[AH][2];
+    auto page_scales = [&](size_t row0, size_t row1, float* ks, float* vs) {
+        const size_t i0 = (row0 >> p.bs_log2) * p.h_kv + j, i1 = (row1 >> p.bs_log2) * p.h_kv + j;
+        ks[0] = ksp[i0];
+        ks[1] = ksp[i1];
+        vs[0] = vsp[i0];
+        vs[1] = vsp[i1];
+    };
+#pragma unroll
+    for (int i = 0; i < AH; i++) qk[i][0] = qk[i][1] = qv[i][0] = qv[i][1] = 1.f;
 #pragma unroll
     for (int i = 0; i < C::NBUF - 2; i++) {
         const size_t a0 = half_row(t0 + i * C::T), a1 = half_row(t0 + i * C::T + 16);
         issue_tile(t0 + i * C::T, i, a0, a1);
+        if (ps) page_scales(a0, a1, qk[i], qv[i]);
     }
     bf16x8 Qf[RPW][C::KS];
 #pragma unroll
@@ -333,19 +352,29 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     vmem_drain();
     {
         constexpr int L = C::NBUF - 2;
-        issue_tile(t0 + L * C::T, L, half_row(t0 + L * C::T), half_row(t0 + L * C::T + 16));
+        const size_t a0 = half_row(t0 + L * C::T), a1 = half_row(t0 + L * C::T + 16);
+        issue_tile(t0 + L * C::T, L, a0, a1);
+        if (ps) page_scales(a0, a1, qk[L], qv[L]);
     }
 
     const GTileOffsets<D, F8> to(li, G);
     int buf = 0;
     for (int tb = t0; tb < t1; tb += C::T) {
-        constexpr int AH = C::NBUF - 1;   // tiles in flight ahead of this one
         const size_t nx0 = half_row(tb + AH * C::T), nx1 = half_row(tb + AH * C::T + 16);
         wait_vmcnt<(AH - 1) * OPW>();   // tiles tb + T .. tb + (AH-1) T were issued after this one
         __syncthreads();
         // refill the buffer read in the previous iteration (every wavefront is
         // past it), so that AH tiles stay in flight while this one is used
         issue_tile(tb + AH * C::T, (buf + AH) % C::NBUF, nx0, nx1);
+        // this tile's page scales, then the queue moves on by one tile
+        float tks[2] = {1.f, 1.f}, tvs[2] = {1.f, 1.f};
+        if (ps) {
+            tks[0] = qk[0][0], tks[1] = qk[0][1], tvs[0] = qv[0][0], tvs[1] = qv[0][1];
+#pragma unroll
+            for (int i = 0; i + 1 < AH; i++)
+                qk[i][0] = qk[i + 1][0], qk[i][1] = qk[i + 1][1], qv[i][0] = qv[i + 1][0], qv[i][1] = qv[i + 1][1];
+            page_scales(nx0, nx1, qk[AH - 1], qv[AH - 1]);
+        }
         const uint8_t* Kt = Ls + buf * 2 * C::KT;
         const uint8_t* Vt = Kt + C::KT;
         if (active) {
@@ -387,7 +416,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const int tok = tb + 16 * mt + 4 * G + e;
-                        z[mt][e] = tok < tl[k] ? S[mt][e] * p.scale_log2 : -INFINITY;
+                        z[mt][e] = tok < tl[k] ? S[mt][e] * (p.scale_log2 * tks[mt]) : -INFINITY;
                         lm = fmaxf(lm, z[mt][e]);
                     }
                 lm = fmaxf(lm, xor16(lm));
@@ -401,17 +430,23 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                 // weights 0
                 const float mb = mn == -INFINITY ? 0.f : mn;
                 uint32_t pk[4];
-                float ps = 0.f;
+                float psum = 0.f;
 #pragma unroll
                 for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                     for (int e = 0; e < 4; e += 2) {
-                        const uint32_t wv = pack_bf16x2(__builtin_amdgcn_exp2f(z[mt][e] - mb),
-                                                        __builtin_amdgcn_exp2f(z[mt][e + 1] - mb));
-                        pk[mt * 2 + e / 2] = wv;
-                        ps += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
+                        const float e0 = __builtin_amdgcn_exp2f(z[mt][e] - mb);
+                        const float e1 = __builtin_amdgcn_exp2f(z[mt][e + 1] - mb);
+                        if (ps) {   // the page's V scale rides on P; the sum takes the weights
+                            pk[mt * 2 + e / 2] = pack_bf16x2(e0 * tvs[mt], e1 * tvs[mt]);
+                            psum += e0 + e1;
+                        } else {
+                            const uint32_t wv = pack_bf16x2(e0, e1);
+                            pk[mt * 2 + e / 2] = wv;
+                            psum += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
+                        }
                     }
-                lsum[k] = lsum[k] * alpha + ps;
+                lsum[k] = lsum[k] * alpha + psum;
                 if (__builtin_amdgcn_ballot_w64(move)) {
 #pragma unroll
                     for (int mc = 0; mc < C::MC; mc++) O[k][mc] *= alpha;
@@ -463,7 +498,9 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
 template <int D, int NW, bool F8, int RPW>
 static hipError_t launch_nw(const GqaParams& p, bool paged, unsigned grid, hipStream_t st)
 {
-    if (paged)
+    if (F8 && paged && p.k_scales)   // per-page scales
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW, F8>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+    else if (paged)
         hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
     else
         hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false, F8, RPW>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);

@@ -25,6 +25,8 @@ struct GqaParams {
     int compact;         // matrix-core kernel: workgroups map to the non-empty (b, split) pairs only
     float scale_log2;    // scale * log2(e) (times the K scale of an FP8 cache)
     float v_scale;       // V scale of an FP8 cache (1 otherwise)
+    const float* k_scales;   // paged FP8 cache with one scale per page and KV head: [num_blocks, h_kv]
+    const float* v_scales;   // (nullptr: the per-tensor scales above)
 };
 
 // vector kernel (any g; fp32 or bf16), then the split merge when n_split > 1
@@ -46,6 +48,8 @@ struct AppendParams {
     float inv_scale;       // FP8 append: fp32 reciprocal of the tensor's scale
     float inv_scale2;      // FP8 append: reciprocal scale of elements split .. row end
     long long split;       // FP8 append: first element under inv_scale2 (a multiple of 4)
+    const float* page_scales;   // FP8 append into a paged pool with one scale per page and
+    int d_h;                    // KV head ([num_blocks, row_bytes / d_h]); nullptr: the above
 };
 
 hipError_t launch_append(const AppendParams& k, const AppendParams* v, int B, hipStream_t st);

@@ -241,6 +241,44 @@ int attn_decode_gqa_multi_fp8(void* out, float* lse, const void* q, const void* 
 size_t attn_decode_gqa_multi_workspace_bytes(int B, int q_len, int s_max, int h, int h_kv, int d_h);
 
 /*
+ * attn_decode_gqa_fp8_paged_scales -- attn_decode_gqa_fp8 over a paged E4M3
+ * cache with one scale per page and KV head instead of one per tensor: the
+ * per-block scaling factors that "Multi-Head Latent Attention (MLA):
+ * Mathematical Foundations ...", section "High-Throughput Serving Kernels:
+ * FlashMLA and SGLang", pairs with an E4M3 cache.  Element (t, j, d) of K
+ * is code * k_scales[blk * h_kv + j] with blk = block_table[b][t /
+ * block_size] (V likewise with v_scales); k_scales, v_scales are fp32
+ * [num_blocks, h_kv] in device memory (their values are not checked; a
+ * non-positive or non-finite scale gives an unspecified result, never an
+ * access outside the arrays).  block_table is required.  Other arguments,
+ * workspace and errors as attn_decode_gqa_fp8; EINVAL for null scales or
+ * no block table.
+ */
+int attn_decode_gqa_fp8_paged_scales(void* out, float* lse, const void* q, const void* cache_k,
+                                     const void* cache_v, const float* k_scales,
+                                     const float* v_scales, const int32_t* s,
+                                     const int32_t* block_table, int max_blocks, int block_size,
+                                     int num_blocks, int B, int s_max, int h, int h_kv, int d_h,
+                                     float scale, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
+ * kv_cache_append_fp8_paged_scales -- kv_cache_append_fp8 into a paged pool
+ * with one scale per page and KV head: element x of k_new[b, j] is stored as
+ * the E4M3 code of x * (1 / k_scales[blk * h_kv + j]), blk the page of slot
+ * pos[b] (reciprocal and product in fp32, nearest with ties to even,
+ * saturated at +-448, NaN -> 0x7F); V likewise.  The caller sets a page's
+ * scales before its first append.  d_h a multiple of 4.  Errors: as
+ * kv_cache_append_fp8, plus EINVAL for null scales or no block table.
+ */
+int kv_cache_append_fp8_paged_scales(void* cache_k, void* cache_v, const void* k_new,
+                                     const void* v_new, const float* k_scales,
+                                     const float* v_scales, const int32_t* pos,
+                                     const int32_t* block_table, int max_blocks, int block_size,
+                                     int num_blocks, int B, int s_max, int h_kv, int d_h,
+                                     void* stream);
+
+/*
  * attn_decode_mla_absorbed -- MLA decode in the absorbed ("MQA mode") form:
  *   q~[b,i]  = W_UK[i]^T q_nope[b,i]                      (d_c values)
  *   z_t      = scale * (q~ . c_t + q_rope[b,i] . k_R,t)

@@ -16,6 +16,8 @@
 // All h heads share every latent row, so the score [h x 576]x[576 x n] and
 // value [h x n]x[n x 512] products are dense and run on the matrix cores;
 // each latent row is fetched from HBM once per call.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_lds.h"
@@ -1114,12 +1116,18 @@ hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
     // absorb workgroups, plus one that computes the tile schedule
     const unsigned g1 = (unsigned)(p.h * (p.d_c / kAbsCols)) + 1;
     const size_t smem1 = (size_t)p.d_nope * kAbsRowStride;
-    static bool attr_set = false;
-    if (!attr_set) {
+    // the absorb kernel's dynamic LDS limit, raised once per device (d_nope
+    // <= 256 rows of 272 bytes); a per-device bit, safe across host threads
+    static std::atomic<unsigned long long> attr_set{0};
+    int dev = 0;
+    hipError_t ed = hipGetDevice(&dev);
+    if (ed != hipSuccess) return ed;
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (!(attr_set.load(std::memory_order_acquire) & bit)) {
         hipError_t ea = hipFuncSetAttribute((const void*)mla_absorb_kernel,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);   // d_nope <= 256 rows of 272 bytes
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
         if (ea != hipSuccess) return ea;
-        attr_set = true;
+        attr_set.fetch_or(bit, std::memory_order_release);
     }
     hipLaunchKernelGGL(mla_absorb_kernel, dim3(g1), dim3(256), smem1, st, p);
     hipError_t e = hipGetLastError();

@@ -303,6 +303,17 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     // non-empty (b, split) pairs only (each workgroup scans the B lengths to
     // find its pair, so only for moderate B); the grid is then a multiple of 8
     p.compact = P.mfma && block_table != nullptr && P.n_split > 1 && B <= 16 * 64;
+    // matrix-core kernel over a contiguous cache: the KV heads are permuted so
+    // that the XCD streaming a head column and the column's address bit 8
+    // differ in parity (needs one workgroup per (b, head, split), h_kv a
+    // multiple of the permuted group, and a 256-byte aligned cache)
+    p.xpair = -1;
+    {
+        const int rbytes = d_h * (b == 1 ? 1 : 2);
+        const int group = rbytes >= 256 ? 2 : rbytes == 128 ? 4 : 8;
+        if (P.mfma && !block_table && P.n_rb == 1 && h_kv % group == 0 && (uintptr_t)cache_k % 256 == 0)
+            p.xpair = (int)(((uintptr_t)cache_k >> 8) & 1);
+    }
     long long grid = (long long)B * h_kv * P.n_hg * P.n_split * P.n_rb;
     if (p.compact) grid = (grid + 7) & ~7LL;
     if (grid >= (1LL << 31)) return fail(ATTN_ENOTSUP, "problem too large for one launch");

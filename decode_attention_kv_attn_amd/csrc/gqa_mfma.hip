@@ -155,6 +155,29 @@ struct SplitCounts {
     }
 };
 
+// Head order against the XCDs.  Workgroup i runs on XCD i mod 8, so with the
+// plain order (KV head fastest, h_kv a multiple of 8) XCD x streams only
+// head columns j = x mod 8, and one head's 256-byte column sits at the same
+// address bit 8 in every token row once a row (h_kv * row bytes) is a
+// multiple of 512.  Measured on the Llama-3 layers: when that address bit
+// equals the parity of the XCD reading it, the batch streams 5-6 % slower
+// than when the two differ (every odd shift of the heads against the XCDs
+// was fast, every even one slow; mixing all heads on every XCD was slower
+// still).  pair_head permutes the low bits of j -- a bijection on every
+// group of 2 << kb heads, so any dispatch order stays correct -- such that
+// the column's address bit 8 is the opposite of bit 0 of the original
+// index, which under the plain order is the XCD's parity.  kb is the bit of
+// j that moves address bit 8 (256 / row bytes = 2^kb); flip is bit 8 of the
+// cache's own address.
+template <int RB>
+__device__ __forceinline__ int pair_head(int j, int flip)
+{
+    constexpr int kb = RB >= 256 ? 0 : RB == 128 ? 1 : 2;
+    constexpr int msk = (2 << kb) - 1;
+    const int lo = j & msk;
+    return (j & ~msk) | (((lo & 1) ^ 1 ^ flip) << kb) | (lo >> 1);
+}
+
 template <int D, int NW, bool PAGED, bool F8, int RPW, bool PS = false>
 __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                                                            const int32_t* __restrict__ btab)
@@ -194,8 +217,9 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     }
     const int rb = w % p.n_rb;
     w /= p.n_rb;
-    const int j = w % p.h_kv;
+    int j = w % p.h_kv;
     w /= p.h_kv;
+    if (!PAGED && p.xpair >= 0) j = pair_head<C::RB>(j, p.xpair);
     if (!compact) {
         split = w % p.n_split;
         b = w / p.n_split;

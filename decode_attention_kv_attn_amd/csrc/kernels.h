@@ -23,6 +23,8 @@ struct GqaParams {
     int q_len;           // query positions per sequence (matrix-core kernel only; 1 otherwise)
     int n_rb;            // row blocks (64 or 128 rows) per (b, KV head) work item (matrix-core kernel)
     int compact;         // matrix-core kernel: workgroups map to the non-empty (b, split) pairs only
+    int xpair;           // matrix-core kernel, contiguous cache: -1, or bit 8 of the K cache's address
+                         // (the KV heads are then permuted against the XCD parity)
     float scale_log2;    // scale * log2(e) (times the K scale of an FP8 cache)
     float v_scale;       // V scale of an FP8 cache (1 otherwise)
     const float* k_scales;   // paged FP8 cache with one scale per page and KV head: [num_blocks, h_kv]

@@ -185,3 +185,39 @@ def test_large_batch_short_sequences(paged):
         assert_close(o64[bi, j * g:(j + 1) * g], ro, 2, f"b={bi} j={j}")
         assert_lse_close(l64[bi, j * g:(j + 1) * g], rl, 2, f"b={bi} j={j}")
     assert np.all(np.isfinite(o64))
+
+
+def at_offset(x, offset):
+    # a copy of x whose storage starts `offset` bytes past a fresh allocation
+    nb = x.numel() * x.element_size()
+    flat = torch.empty(nb + offset, dtype=torch.uint8, device=DEV)
+    v = flat[offset:offset + nb].view(x.dtype).view(x.shape)
+    v.copy_(x)
+    return v
+
+
+@pytest.mark.parametrize("offset", [0, 128, 256, 768])
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("h,h_kv,d_h", [(32, 8, 128), (16, 4, 64), (64, 64, 128)])
+def test_cache_alignment_and_head_order(offset, fp8, h, h_kv, d_h):
+    # contiguous caches on the matrix cores take their KV heads in an order
+    # set by bit 8 of the cache's address (plain order when it is not
+    # 256-byte aligned): every alignment gives the oracle's results
+    print(f"[gqa-align] offset={offset} fp8={fp8} h={h} h_kv={h_kv} d_h={d_h}", flush=True)
+    sh = synth.GqaShape("t", B=3, h=h, h_kv=h_kv, d_h=d_h, b=2, s=(5, 700, 4500), seed=800 + offset + h)
+    if fp8:
+        ks, vs = 1 / 64, 1 / 32
+        d = synth.draw_gqa_fp8(sh, ks, vs, device=DEV)
+        K, V = at_offset(d["K8"], offset), at_offset(d["V8"], offset)
+        out, lse = A.decode_gqa_fp8(d["q"], K, V, ks, vs, d["s"])
+        ref, ref_lse = oracle.gqa_decode_fp8(synth.host_bits(d["q"]), synth.host_bits(d["K8"]),
+                                             synth.host_bits(d["V8"]), ks, vs, d["s_host"])
+    else:
+        d = synth.draw_gqa(sh, device=DEV)
+        K, V = at_offset(d["K"], offset), at_offset(d["V"], offset)
+        out, lse = A.decode_gqa(d["q"], K, V, d["s"])
+        ref, ref_lse = oracle.gqa_decode(*(synth.host_bits(d[k]) for k in ("q", "K", "V")),
+                                         d["s_host"], 2)
+    torch.cuda.synchronize()
+    assert_close(to_f64(out), ref, 2, "out")
+    assert_lse_close(to_f64(lse), ref_lse, 2, "lse")

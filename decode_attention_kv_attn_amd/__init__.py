@@ -9,7 +9,6 @@ If the shared library has not been built this module raises on first use.
 from __future__ import annotations
 
 import ctypes as C
-import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -374,10 +373,6 @@ def decode_mla(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_siz
                                      r_scale, s, block_table, max_blocks, block_size, num_blocks,
                                      B, s_max, h, d_c, d_R, d_nope, d_v, scale, wb, wn, stream)
     return out, ul, l
-
-
-def default_scale(d):
-    return 1.0 / math.sqrt(d)
 
 
 def merge_partials(o_parts, lse_parts, out_dtype=None, lse=True, stream=None):

@@ -16,8 +16,6 @@
 // All h heads share every latent row, so the score [h x 576]x[576 x n] and
 // value [h x n]x[n x 512] products are dense and run on the matrix cores;
 // each latent row is fetched from HBM once per call.
-#include <atomic>
-
 #include "common.h"
 #include "kernels.h"
 #include "mfma_lds.h"
@@ -83,9 +81,14 @@ __device__ __forceinline__ AbsA absorb_load_a(const uint16_t* __restrict__ qn, i
     return a;
 }
 
+constexpr int kAbsMaxNope = 256;   // largest d_nope the staging area holds
+
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // W_UK staging, sized statically for the largest d_nope: a static
+    // allocation above the 64 KB default of dynamic LDS needs no per-kernel
+    // attribute set at run time
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kAbsMaxNope * kAbsRowStride];
     __shared__ __attribute__((aligned(16))) uint16_t ost[4][16][32 + 8];   // per-wavefront output staging
     if (blockIdx.x == gridDim.x - 1) {   // one extra workgroup: the decode tile schedule
         __shared__ int sc[256];
@@ -710,7 +713,6 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         // refilled, so that three tiles stay in flight
         dma.issue(ic, (buf + 3) % kNBuf, nx0, nx1);
         ic.next(sv);
-        const int flagged = ovf;   // set during an earlier tile; acted on at the end of this one
         const uint8_t* C = Cs + buf * TL::TILE;
         const int tbase = cc.lt * kT;
 
@@ -792,6 +794,11 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         Pb[wave][0][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
         Pb[wave][1][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
         __syncthreads();   // P of every head visible
+        // Every wavefront set ovf for this tile before the barrier above, and
+        // none can set it for the next tile before all of them have passed
+        // the barrier at the top of the next iteration: read here, the flag
+        // is the same in every wavefront, so the break below is uniform.
+        const int flagged = ovf;
         // ---- latent sum U^T += C^T . P^T over this wavefront's columns
 #pragma unroll
         for (int kk = 0; kk < 2; kk++) {
@@ -805,7 +812,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         }
         cc.lt++;
         buf = (buf + 1) % kNBuf;
-        if (flagged) break;   // workgroup-uniform
+        if (flagged) break;   // workgroup-uniform (read between two barriers)
       }
       if (g < gend) break;   // left early: flagged for the merge kernel
       write_partial(cc.b);
@@ -1114,22 +1121,9 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
 hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
 {
     // absorb workgroups, plus one that computes the tile schedule
+    if (p.d_nope > kAbsMaxNope) return hipErrorInvalidValue;
     const unsigned g1 = (unsigned)(p.h * (p.d_c / kAbsCols)) + 1;
-    const size_t smem1 = (size_t)p.d_nope * kAbsRowStride;
-    // the absorb kernel's dynamic LDS limit, raised once per device (d_nope
-    // <= 256 rows of 272 bytes); a per-device bit, safe across host threads
-    static std::atomic<unsigned long long> attr_set{0};
-    int dev = 0;
-    hipError_t ed = hipGetDevice(&dev);
-    if (ed != hipSuccess) return ed;
-    const unsigned long long bit = 1ull << (dev & 63);
-    if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-        hipError_t ea = hipFuncSetAttribute((const void*)mla_absorb_kernel,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-        if (ea != hipSuccess) return ea;
-        attr_set.fetch_or(bit, std::memory_order_release);
-    }
-    hipLaunchKernelGGL(mla_absorb_kernel, dim3(g1), dim3(256), smem1, st, p);
+    hipLaunchKernelGGL(mla_absorb_kernel, dim3(g1), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g2 = (unsigned)p.n_wg;

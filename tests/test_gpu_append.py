@@ -27,6 +27,28 @@ def test_contiguous_append_bit_exact(b):
     assert np.array_equal(synth.host_bits(d["V"]), refV)
 
 
+@pytest.mark.parametrize("b", [2, 4])
+def test_paged_kv_append_bit_exact(b):
+    # K and V rows through a shuffled block table, positions on both sides
+    # of block boundaries (first and last row of a block, a fresh block)
+    s = (0, 15, 16, 31, 200)
+    sh = synth.GqaShape("t", B=5, h=8, h_kv=4, d_h=128, b=b, s=tuple(x + 1 for x in s),
+                        paged=True, seed=24)
+    d = synth.draw_gqa(sh, device=DEV)
+    kn = torch.randn(5, 4, 128, device=DEV).to(d["K"].dtype)
+    vn = torch.randn(5, 4, 128, device=DEV).to(d["K"].dtype)
+    pos = torch.tensor(s, dtype=torch.int32, device=DEV)
+    tab = d["block_table"]
+    refK, refV = oracle.kv_append(synth.host_bits(d["K"]), synth.host_bits(d["V"]),
+                                  synth.host_bits(kn), synth.host_bits(vn), np.array(s, np.int32),
+                                  b, block_table=d["block_table_host"])
+    A.kv_cache_append(d["K"], d["V"], kn, vn, pos, tab, tab.shape[1], 16, d["K"].shape[0], 5, 0,
+                      4, 128, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.host_bits(d["K"]), refK)
+    assert np.array_equal(synth.host_bits(d["V"]), refV)
+
+
 def test_paged_mla_latent_append_bit_exact():
     s = (0, 15, 16, 300)
     sh = synth.MlaShape("t", B=4, h=16, d_c=512, d_R=64, d_nope=128, d_v=128,

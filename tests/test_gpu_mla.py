@@ -133,13 +133,18 @@ def test_paged_mla_full_size_sampled():
 
 
 def test_peaked_logits_take_the_rescaling_path():
-    # One late token whose latent row points along head 0's absorbed query:
-    # its logit exceeds the first tile's maximum by far more than 2^64 in
-    # probability ratio, so that split is recomputed with online rescaling.
+    # Tokens whose latent row points along head 0's absorbed query: each
+    # logit exceeds its tile run's first maximum by far more than 2^64 in
+    # probability ratio, so the workgroup holding it stops and its partials
+    # are recomputed with online rescaling.  With 167 tiles over 256
+    # workgroups every workgroup takes 8 tiles: token 200 sits in the middle
+    # of workgroup 0's run, token 80 of sequence 1 in the middle of
+    # workgroup 1's run after it has finished sequence 0's last two tiles,
+    # and token 4000 on the last tile of workgroup 16's run.
     sh = shape(2, 128, (300, 5000), seed=71)
     d = synth.draw_mla(sh, device=DEV)
-    qt = torch.einsum("bn,nc->bc", d["q_nope"][:, 0].float(), d["w_uk"][0].float())   # q~ of head 0
-    for bi, t in ((0, 200), (1, 4000)):
+    qt = torch.matmul(d["q_nope"][:, 0].float(), d["w_uk"][0].float())   # q~ of head 0
+    for bi, t in ((0, 200), (1, 80), (1, 4000)):
         c = qt[bi] / qt[bi].norm() * 40.0
         r = d["q_rope"][bi, 0].float()
         kr = r / r.norm() * 40.0

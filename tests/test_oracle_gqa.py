@@ -179,3 +179,67 @@ def test_rejects_indivisible_heads_and_bad_lengths():
         oracle.gqa_decode(q, d["K"], d["V"], d["s"], 4)
     with pytest.raises(ValueError):
         oracle.gqa_decode(d["q"], d["K"], d["V"], [5], 4)    # s > s_max
+
+
+def test_zero_query_gives_mean_of_values():
+    # q = 0 makes every score 0: the softmax is uniform over the s_b tokens,
+    # so each head returns the plain mean of its KV head's value rows and
+    # lse = ln s_b
+    d = gqa_host(2, 8, 2, 32, (13, 96), 4, seed=37)
+    q = np.zeros_like(d["q"])
+    out, lse = oracle.gqa_decode(q, d["K"], d["V"], d["s"], 4)
+    V = widen(d["V"])
+    for bi, n in enumerate(d["s"]):
+        for i in range(8):
+            np.testing.assert_allclose(out[bi, i], V[bi, :n, i // 4].mean(axis=0), atol=1e-12)
+            assert abs(lse[bi, i] - np.log(n)) < 1e-12
+
+
+def _mha_loop(q, K, V, s, scale):
+    """An independently written MHA decode: plain Python loops per head, a
+    max-subtracted softmax over the token list, float64 throughout."""
+    B, h, d = q.shape
+    out = np.zeros((B, h, d))
+    lse = np.zeros((B, h))
+    for bi in range(B):
+        for i in range(h):
+            z = [scale * float(np.dot(q[bi, i], K[bi, t, i])) for t in range(int(s[bi]))]
+            m = max(z)
+            w = [np.exp(x - m) for x in z]
+            tot = sum(w)
+            acc = np.zeros(d)
+            for t, wt in enumerate(w):
+                acc += wt * V[bi, t, i]
+            out[bi, i] = acc / tot
+            lse[bi, i] = m + np.log(tot)
+    return out, lse
+
+
+def test_g1_equals_independent_mha_loop():
+    # GQA with g = 1 is MHA ("MHA -> MQA -> GQA -> MLA", opening section)
+    d = gqa_host(2, 5, 5, 16, (7, 31), 4, seed=41)
+    out, lse = oracle.gqa_decode(d["q"], d["K"], d["V"], d["s"], 4)
+    ref, ref_lse = _mha_loop(widen(d["q"]), widen(d["K"]), widen(d["V"]), d["s"], 1.0 / 4.0)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-13)
+
+
+def test_shift_of_all_scores_moves_only_lse():
+    # Adding one vector u to every key of an MHA head adds scale * q . u to
+    # every score of that head: the softmax, hence o, is unchanged and lse
+    # moves by exactly that constant.  Values are small integers over 8 so
+    # K + u is exact in fp32.
+    rng = np.random.default_rng(43)
+    B, h, d_h, s = 1, 3, 16, (40,)
+    q = (rng.integers(-8, 9, (B, h, d_h)) / 8).astype(np.float32)
+    K = (rng.integers(-8, 9, (B, s[0], h, d_h)) / 8).astype(np.float32)
+    V = rng.standard_normal((B, s[0], h, d_h)).astype(np.float32)
+    u = (rng.integers(-8, 9, (h, d_h)) / 8).astype(np.float32)
+    K2 = (K + u[None, None]).astype(np.float32)
+    assert np.array_equal(K2.astype(np.float64), K.astype(np.float64) + u.astype(np.float64))
+    o1, l1 = oracle.gqa_decode(q, K, V, s, 4)
+    o2, l2 = oracle.gqa_decode(q, K2, V, s, 4)
+    shift = np.einsum("bhd,hd->bh", q.astype(np.float64), u.astype(np.float64)) / 4.0
+    np.testing.assert_allclose(o2, o1, atol=1e-13)
+    np.testing.assert_allclose(l2, l1 + shift, atol=1e-12)
+    assert np.max(np.abs(shift)) > 0.1   # the shift is not trivially zero

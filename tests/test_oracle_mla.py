@@ -12,9 +12,10 @@
     page);
   * reduction to MQA: with d_nope = d_c and W_UK = W_UV = I the absorbed path
     is plain one-KV-head attention over the latent rows, so torch's library
-    attention over [c | k_R] (values c) must give both out and u_latent
-    ("MHA -> MQA -> GQA -> MLA": "When using MLA during decode it becomes MQA"
-    in the quoted engine code);
+    attention over [c | k_R] (values c) must give both out and u_latent, and
+    so must the GQA oracle with one KV head ("MHA -> MQA -> GQA -> MLA",
+    sections "Where h_kv comes from" and "Where the head count becomes
+    bytes": an MLA layer decodes as one KV head shared by every query head);
   * paged == contiguous gathered, bit for bit.
 """
 import numpy as np
@@ -139,3 +140,28 @@ def test_empty_sequence():
                                   d["s"])
     assert np.all(o[0] == 0) and np.all(u[0] == 0) and np.all(np.isneginf(l[0]))
     assert np.all(np.isfinite(o[1]))
+
+
+def test_identity_weights_reduce_to_the_gqa_oracle_with_one_kv_head():
+    # With d_nope = d_c and W_UK = W_UV = I, absorbed MLA is MQA over the
+    # latent rows ("MHA -> MQA -> GQA -> MLA", the MLA section: decode in the
+    # absorbed form is MQA): keys [c | k_R], values c, queries [q_nope | q_rope],
+    # one KV head.  The GQA oracle takes equal key and value widths, so the
+    # values are padded with d_R zero columns, which come back as zeros.
+    B, h, d_c, d_R = 2, 4, 32, 8
+    d = mla_host(B, h, d_c, d_R, d_c, d_c, (9, 37), seed=71)
+    eye = np.broadcast_to(np.eye(d_c, dtype=np.float32), (h, d_c, d_c))
+    d["w_uk"] = bf16_bits(eye)
+    d["w_uv"] = bf16_bits(eye)
+    out, ul, lse = oracle.mla_absorbed(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"],
+                                       d["cache"], d["s"])
+    C = d["cache"]                                      # [B, s_max, d_c + d_R] bf16 bits
+    K = np.ascontiguousarray(C[:, :, None, :])          # h_kv = 1
+    V = np.zeros_like(K)
+    V[:, :, 0, :d_c] = C[:, :, :d_c]
+    q = np.ascontiguousarray(np.concatenate([d["q_nope"], d["q_rope"]], axis=2))
+    go, gl = oracle.gqa_decode(q, K, V, d["s"], 2, scale=1.0 / np.sqrt(d_c + d_R))
+    np.testing.assert_allclose(ul, go[:, :, :d_c], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out, go[:, :, :d_c], rtol=0, atol=1e-12)
+    assert np.all(go[:, :, d_c:] == 0.0)
+    np.testing.assert_allclose(lse, gl, rtol=0, atol=1e-12)

@@ -35,6 +35,7 @@ EXPORTED = (
     "kv_cache_append_mla_fp8",
     "attn_decode_gqa_fp8_paged_scales",
     "kv_cache_append_fp8_paged_scales",
+    "attn_decode_gqa_noalloc",
 )
 
 _lib = None
@@ -96,6 +97,8 @@ def lib():
         L.kv_cache_append_fp8_paged_scales.restype = I
         L.kv_cache_append_fp8_paged_scales.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                        P]
+        L.attn_decode_gqa_noalloc.restype = I
+        L.attn_decode_gqa_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -158,6 +161,14 @@ def attn_decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, b
                                h_kv, d_h, b, float(scale), _p(workspace), int(workspace_bytes),
                                _stream(stream))
     return _check(rc) if check else rc
+
+
+def attn_decode_gqa_noalloc(out, lse, q, cache_k, cache_v, s, block_table, max_blocks,
+                            block_size, num_blocks, B, s_max, h, h_kv, d_h, b, scale=0.0,
+                            stream=None):
+    return _check(lib().attn_decode_gqa_noalloc(
+        _p(out), _p(lse), _p(q), _p(cache_k), _p(cache_v), _p(s), _p(block_table), max_blocks,
+        block_size, num_blocks, B, s_max, h, h_kv, d_h, b, scale, _stream(stream)))
 
 
 def kv_cache_append_fp8(cache_k, cache_v, k_new, v_new, k_scale, v_scale, pos, block_table,

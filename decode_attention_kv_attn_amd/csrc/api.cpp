@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/attn_decode.h: argument checks,
-// the split plan, workspace carving and kernel launches.  No allocation, no
-// global state except the thread-local error message.
+// the split plan, workspace carving and kernel launches.  No allocation; no
+// global state except the thread-local error message and, for the no-alloc
+// entry point, each device's scratch address (noalloc.hip).
 #include "attn_decode.h"
 #include "attn_stream_probe.h"
 
@@ -247,7 +248,7 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
                int num_blocks, int B, int s_max, int h, int h_kv, int d_h, int b, float scale,
                float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
                void* stream, int q_len = 1, const float* k_scales = nullptr,
-               const float* v_scales = nullptr)
+               const float* v_scales = nullptr, bool noalloc = false)
 {
     if (!out || !q || !cache_k || !cache_v || !s)
         return fail(ATTN_EINVAL, "null out, q, cache_k, cache_v or s");
@@ -269,6 +270,14 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     }
     if (B == 0) return ATTN_OK;
     const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b, q_len);
+    if (noalloc) {   // the fixed per-device scratch replaces the caller's workspace
+        if (P.ws_bytes > attn::kNoAllocScratchBytes)
+            return fail(ATTN_ENOTSUP,
+                        "attn_decode_gqa_noalloc: these sizes need %zu bytes of scratch, more than "
+                        "its fixed %zu; use attn_decode_gqa with a workspace",
+                        P.ws_bytes, attn::kNoAllocScratchBytes);
+        workspace_bytes = attn::kNoAllocScratchBytes;
+    }
     if (P.ws_bytes && (!workspace || workspace_bytes < P.ws_bytes))
         return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
                     workspace ? workspace_bytes : (size_t)0);
@@ -410,6 +419,21 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
     return decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
                       num_blocks, B, s_max, h, h_kv, d_h, b, scale, 1.f, 1.f, workspace,
                       workspace_bytes, stream);
+}
+
+int attn_decode_gqa_noalloc(void* out, float* lse, const void* q, const void* cache_k,
+                            const void* cache_v, const int32_t* s, const int32_t* block_table,
+                            int max_blocks, int block_size, int num_blocks, int B, int s_max,
+                            int h, int h_kv, int d_h, int b, float scale, void* stream)
+{
+    // the device's scratch address, looked up on the first call on it
+    void* ws = nullptr;
+    const hipError_t e = attn::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "attn_decode_gqa_noalloc scratch lookup");
+    if (b != 2 && b != 4) return fail(ATTN_EINVAL, "b must be 2 (bf16) or 4 (fp32)");
+    return decode_gqa(out, lse, q, cache_k, cache_v, s, block_table, max_blocks, block_size,
+                      num_blocks, B, s_max, h, h_kv, d_h, b, scale, 1.f, 1.f, ws, 0, stream, 1,
+                      nullptr, nullptr, true);
 }
 
 int attn_decode_gqa_fp8(void* out, float* lse, const void* q, const void* cache_k,

@@ -96,6 +96,12 @@ struct MergeParams {
 };
 hipError_t launch_merge_partials(const MergeParams& p, bool in_f32, bool out_f32, hipStream_t st);
 
+// Device scratch of the entry point that allocates nothing: one fixed array
+// per GPU (noalloc.hip).  The address of the current device's copy, looked
+// up on the first call on that device and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** out);
+
 // read-bandwidth probe: kProbeGrid workgroups, bytes / kProbeGrid each (a
 // multiple of 16 KB)
 constexpr unsigned kProbeGrid = 2048;

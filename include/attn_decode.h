@@ -31,7 +31,8 @@
  * library never allocates, frees or keeps a pointer after a call returns.
  * Tensors are dense, row-major (last index fastest), naturally aligned and
  * 16-byte aligned at their base.  The library keeps no state apart from a
- * thread-local error message.
+ * thread-local error message, and, for attn_decode_gqa_noalloc only, a fixed
+ * scratch array per GPU and its looked-up address.
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Calls only enqueue work and return; results are ready when the
@@ -153,6 +154,29 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
                     int max_blocks, int block_size, int num_blocks, int B, int s_max, int h,
                     int h_kv, int d_h, int b, float scale, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_gqa_noalloc -- attn_decode_gqa without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It calls
+ * no allocating routine: the split partials go to a fixed scratch array in
+ * the library's device memory, 64 MiB per GPU (one copy on every GPU the
+ * library runs on, held until the process ends).  Its address on a device is
+ * looked up on the first call made with that device current.
+ * Arguments, results, supported shapes and errors as attn_decode_gqa, and
+ * the outputs are bit-identical to attn_decode_gqa's for the same inputs;
+ * plus ENOTSUP when the sizes need more scratch than 64 MiB (the message
+ * gives the amount; attn_decode_workspace_bytes() reports it too) and EHIP if
+ * the scratch lookup fails.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (different streams, or host threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the scratch has
+ * to start at zero.
+ */
+int attn_decode_gqa_noalloc(void* out, float* lse, const void* q, const void* cache_k,
+                            const void* cache_v, const int32_t* s, const int32_t* block_table,
+                            int max_blocks, int block_size, int num_blocks, int B, int s_max,
+                            int h, int h_kv, int d_h, int b, float scale, void* stream);
 
 /*
  * FP8 caches.  An 8-bit cache halves the bytes per token that decode streams.

@@ -16,6 +16,8 @@
 // All h heads share every latent row, so the score [h x 576]x[576 x n] and
 // value [h x n]x[n x 512] products are dense and run on the matrix cores;
 // each latent row is fetched from HBM once per call.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_lds.h"
@@ -83,12 +85,14 @@ __device__ __forceinline__ AbsA absorb_load_a(const uint16_t* __restrict__ qn, i
 
 constexpr int kAbsMaxNope = 256;   // largest d_nope the staging area holds
 
+// MAXN: the largest d_nope this instantiation stages (128 or 256).  The
+// W_UK staging is a static allocation sized for it, so no per-kernel
+// attribute is set at run time; the 128-row instantiation (34 KB) lets four
+// workgroups share a CU, the 256-row one (68 KB) two.
+template <int MAXN>
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 {
-    // W_UK staging, sized statically for the largest d_nope: a static
-    // allocation above the 64 KB default of dynamic LDS needs no per-kernel
-    // attribute set at run time
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kAbsMaxNope * kAbsRowStride];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[MAXN * kAbsRowStride];
     __shared__ __attribute__((aligned(16))) uint16_t ost[4][16][32 + 8];   // per-wavefront output staging
     if (blockIdx.x == gridDim.x - 1) {   // one extra workgroup: the decode tile schedule
         __shared__ int sc[256];
@@ -522,20 +526,33 @@ struct TileDma {
         r0 = half_row(c.b, c.lt * kT);
         r1 = half_row(c.b, c.lt * kT + 16);
     }
-    __device__ __forceinline__ void issue(const TileWalk& c, int buf, size_t row0, size_t row1) const
+    // A tile's DMA, prepared (buffer resource and LDS base, wave-uniform)
+    // and then issued one instruction at a time, so that the issue can be
+    // spread between other work.
+    struct Pending {
+        rsrc_t rs;
+        uint32_t lb;
+    };
+    __device__ __forceinline__ Pending prepare(const TileWalk& c, int buf, size_t row0, size_t row1) const
     {
         // first row of this wavefront's RPS rows (a 16-row half lies in one block)
         const size_t row = F8 ? (rb == 0 ? row0 : row1) : (rb < 2 ? row0 : row1) + 8 * (rb & 1);
         const int t0 = c.lt * kT + TL::RPS * rb;                      // its token index
         const int nr = c.past() ? 0 : max(0, min(TL::RPS, c.n - t0)) * kRow;   // rows past the length read 0
-        const rsrc_t rs = make_rsrc(cbase + row * kRow, nr);
-        const uint32_t lb = lds0 + (uint32_t)(buf * TL::TILE);
+        return Pending{make_rsrc(cbase + row * kRow, nr), lds0 + (uint32_t)(buf * TL::TILE)};
+    }
+    // instruction j < SPW of this wavefront's share
+    __device__ __forceinline__ void issue_slot(const Pending& pd, int j) const
+    {
+        const int q = wave + NW * j;
+        if (kSlots % NW == 0 || q < kSlots)   // wave-uniform, static when NW divides the slots
+            dma16(pd.rs, vbase + (uint32_t)TL::SEG * (uint32_t)(q / TL::SPS), pd.lb + (uint32_t)q * 1024u);
+    }
+    __device__ __forceinline__ void issue(const TileWalk& c, int buf, size_t row0, size_t row1) const
+    {
+        const Pending pd = prepare(c, buf, row0, row1);
 #pragma unroll
-        for (int j = 0; j < SPW; j++) {
-            const int q = wave + NW * j;
-            if (kSlots % NW == 0 || q < kSlots)   // wave-uniform, static when NW divides the slots
-                dma16(rs, vbase + (uint32_t)TL::SEG * (uint32_t)(q / TL::SPS), lb + (uint32_t)q * 1024u);
-        }
+        for (int j = 0; j < SPW; j++) issue_slot(pd, j);
     }
     // tiles tb + T and tb + 2T were issued after tile tb
     __device__ __forceinline__ void wait_tile() const
@@ -554,20 +571,32 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     constexpr int NW = 4;           // wavefronts per workgroup
     constexpr int KS = 576 / 16;    // score K steps
 #ifndef MLA_PD
-#define MLA_PD 6
+#define MLA_PD 4
 #endif
-    constexpr int PD = MLA_PD;      // score operands read ahead of their product
+    // score operands read ahead of their product (bf16); one fewer over a
+    // paged pool, whose block-table walk needs registers of its own
+    constexpr int PD = PAGED ? MLA_PD - 1 : MLA_PD;
+#ifndef MLA_NU1
+#define MLA_NU1 16
+#endif
+    // latent-sum products of the previous tile issued between the score
+    // products (the others run beside the softmax)
+    constexpr int NU1 = MLA_NU1;
+    constexpr int MCW = 4;          // 32-column tiles of the latent sum per wavefront
+    constexpr int NTH = 4;          // 32-head tiles of the latent sum (all heads; zeros past h)
 #ifndef MLA_SCH
 #define MLA_SCH 1
 #endif
-    constexpr int SCH = MLA_SCH;    // score accumulation chains
-    constexpr int MCW = 4;          // 32-column tiles of the latent sum per wavefront
-    constexpr int NTH = 4;          // 32-head tiles of the latent sum (all heads; zeros past h)
+    constexpr int SCH = MLA_SCH;    // score accumulation chains (1 or 2)
+    static_assert((NU1 == 0 || NU1 == 16 || NU1 == 32) && (SCH == 1 || SCH == 2), "interleave");
     using TL = MlaTile<F8>;
     __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * TL::TILE];
-    __shared__ __attribute__((aligned(16))) bf16x8 Pb[NTH][2][64];   // P of every head tile, B-operand layout
-    __shared__ int ovf;   // some head's scores ran past its reference max + 64
-    __shared__ float Lx[NTH * 32];   // softmax sums of all heads, for the partial write
+    // P of every head tile in B-operand layout, for two tiles: the value
+    // product of tile g - 1 reads one buffer while the softmax of tile g
+    // writes the other, so one barrier per tile orders both
+    __shared__ __attribute__((aligned(16))) bf16x8 Pb[2][NTH][2][64];
+    // partial-write staging of E4M3 tiles (bf16 tiles use a free ring buffer)
+    __shared__ __attribute__((aligned(16))) uint8_t Stg8[F8 ? 4 * 32 * 272 : 16];
 
     const int tid = threadIdx.x, lane = tid % 64, hh = lane / 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -587,7 +616,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     const TileDma<NW, PAGED, F8> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
                                  wave, lane);
     TileWalk ic(sv, sv.first_seq(w), g0, g1);   // issue cursor
-    TileWalk cc = ic;                            // compute cursor
+    TileWalk cc = ic;                            // compute cursor (the tile being scored)
 
     // q^ fragments of one sequence: B operand of the score product (heads
     // past h read as zeros)
@@ -610,12 +639,14 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     // the first tile, and U, lsum accumulate 2^(z - m).  A later tile may
     // exceed m by up to 64 (p <= 2^64 stays far from fp32/bf16 overflow);
     // rescaling the AGPR-resident U in place would cost the loop its
-    // register allocation, so past that the workgroup stops and flags
-    // itself, and the merge kernel recomputes its partials exactly (real
-    // logits essentially never get there).  m and lsum belong to this
+    // register allocation, so past that the wavefront only notes it: after
+    // the loop the workgroup flags itself, and the merge kernel recomputes
+    // all of its partials exactly (the partials it wrote are never read).
+    // Real logits essentially never get there.  m and lsum belong to this
     // lane's score head, U to the wavefront's latent columns (all heads).
     f32x16 U[MCW][NTH];
     float m, lsum;
+    int ovf_w = 0;   // wave-uniform: some score of this wavefront's heads ran past m + 64
     auto reset = [&]() {
         m = -INFINITY;
         lsum = 0.f;
@@ -627,17 +658,27 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                 for (int v = 0; v < 16; v++) U[mc][nt][v] = 0.f;
     };
     // partial state of sequence b, slot w + b: (m, l) of the score heads and
-    // the U^T columns 128 wave .. + 127 of every head
+    // the U^T columns 128 wave .. + 127 of every head.
     // U / l is a weighted mean of cached latents, so it is stored as fp16
     // (2^-11 relative), halving the partial traffic of fp32 sums.  The sums l
-    // of all heads go through LDS to the wavefronts holding their columns.
-    // Vector arithmetic on the AGPR-resident U would cost the tile loop its
-    // register allocation, so U leaves through LDS: each wavefront stores 8
-    // of its accumulator registers into its 2 KB of the P buffer (free once
-    // every wavefront has left the tile loop) and reads them back into fresh
-    // registers before scaling and converting them.
-    auto write_partial = [&](int b) {
+    // of all heads go through LDS (the second P buffer) to the wavefronts
+    // holding their columns.  Vector arithmetic on the AGPR-resident U would
+    // cost the tile loop its register allocation, so U leaves through LDS:
+    // per round (a head tile and 64 of the wavefront's columns) each
+    // wavefront stores its accumulators as they are into its own staging
+    // rows [32 heads][64 columns] fp32 (rows padded to 272 bytes, so that 16
+    // lanes' 16-byte accesses fall in distinct banks), reads back 8
+    // consecutive columns of one head per lane, scales them by 1 / l,
+    // converts them and writes 16 contiguous bytes: 8 lanes cover one head's
+    // 128 bytes of the round.  The staging area is the ring buffer of the
+    // last scored tile (free once every wavefront has passed the first
+    // barrier below; the next refill of it is issued after this returns),
+    // or a separate area for E4M3 tiles, which are smaller than it.
+    float* const Lx = (float*)&Pb[1][0][0][0];   // NTH * 32 sums
+    constexpr int kStgRow = 272, kStgWave = 32 * kStgRow;
+    auto write_partial = [&](int b, uint8_t* stage) {
         const float l = lsum + xor32(lsum);
+        __syncthreads();   // every wavefront is done with both P buffers and the staging buffer
         if (hh == 0) {
             Lx[hs] = l;
             if (hv) {
@@ -646,37 +687,58 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                 p.part_ml[row * 2 + 1] = l;
             }
         }
-        __syncthreads();   // Lx written, and every wavefront is done with Pb
-        float4* stg = (float4*)&Pb[wave][0][0] + 2 * lane;
-        const uint32_t stg_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stg;
+        __syncthreads();   // Lx written
+        uint8_t* const st = stage + wave * kStgWave;
 #pragma unroll
         for (int nt = 0; nt < NTH; nt++) {
-            const int head = 32 * nt + lane % 32;
-            const float lh = Lx[head];
-            const float il = lh > 0.f ? 1.f / lh : 0.f;
-            _Float16* pu = p.part_u + ((size_t)(w + b) * p.h + min(head, p.h - 1)) * 512 + 128 * wave + 4 * hh;
 #pragma unroll
-            for (int mc = 0; mc < MCW; mc++)
+            for (int half = 0; half < 2; half++) {
+                // accumulator lane l, register 4 gq + e holds head 32 nt + l % 32,
+                // column 32 mc + 8 gq + 4 (l / 32) + e of the wavefront's 128
 #pragma unroll
-                for (int hf = 0; hf < 2; hf++) {
-                    stg[0] = make_float4(U[mc][nt][8 * hf], U[mc][nt][8 * hf + 1], U[mc][nt][8 * hf + 2], U[mc][nt][8 * hf + 3]);
-                    stg[1] = make_float4(U[mc][nt][8 * hf + 4], U[mc][nt][8 * hf + 5], U[mc][nt][8 * hf + 6], U[mc][nt][8 * hf + 7]);
-                    f32x4 x0, x1;
-                    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-                                 : "=v"(x0), "=v"(x1) : "v"(stg_lds) : "memory");
+                for (int mm = 0; mm < 2; mm++)
+#pragma unroll
+                    for (int gq = 0; gq < 4; gq++) {
+                        const f32x16& u = U[2 * half + mm][nt];
+                        *(float4*)(st + (lane % 32) * kStgRow + (32 * mm + 8 * gq + 4 * hh) * 4) =
+                            make_float4(u[4 * gq], u[4 * gq + 1], u[4 * gq + 2], u[4 * gq + 3]);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+                // the round's output base, opaque to the compiler: computed
+                // here, it is not hoisted out of the tile loops into a
+                // register that would be spilled and reloaded (a reload
+                // waits for every outstanding store of the round before)
+                uint64_t obase = (uint64_t)(uintptr_t)(p.part_u + ((size_t)(w + b) * p.h + 32 * nt) * 512 +
+                                                       128 * wave + 64 * half);
+                asm volatile("" : "+s"(obase));
+#pragma unroll 1
+                for (int r = 0; r < 4; r++) {
+                    const int q = 64 * r + lane, hd = q / 8, c8 = q % 8;
+                    const float4 x0 = *(const float4*)(st + hd * kStgRow + c8 * 32);
+                    const float4 x1 = *(const float4*)(st + hd * kStgRow + c8 * 32 + 16);
+                    const int head = 32 * nt + hd;
+                    const float lh = Lx[head];
+                    const float il = lh > 0.f ? __builtin_amdgcn_rcpf(lh) : 0.f;
+                    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+                    const h8 v = {(_Float16)(x0.x * il), (_Float16)(x0.y * il), (_Float16)(x0.z * il),
+                                  (_Float16)(x0.w * il), (_Float16)(x1.x * il), (_Float16)(x1.y * il),
+                                  (_Float16)(x1.z * il), (_Float16)(x1.w * il)};
+#ifndef MLA_PSTORE
+#define MLA_PSTORE 0
+#endif
                     if (head < p.h) {
-                        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-                        const h4 v0 = {(_Float16)(x0[0] * il), (_Float16)(x0[1] * il), (_Float16)(x0[2] * il), (_Float16)(x0[3] * il)};
-                        const h4 v1 = {(_Float16)(x1[0] * il), (_Float16)(x1[1] * il), (_Float16)(x1[2] * il), (_Float16)(x1[3] * il)};
-                        *(h4*)(pu + 32 * mc + 16 * hf) = v0;
-                        *(h4*)(pu + 32 * mc + 16 * hf + 8) = v1;
+                        h8* dst = (h8*)((_Float16*)(uintptr_t)obase + hd * 512 + 8 * c8);
+                        if (MLA_PSTORE == 0) *dst = v;
+                        else if (MLA_PSTORE == 1) __builtin_nontemporal_store(v, dst);
+                        else if (MLA_PSTORE == 2 && v[0] == (_Float16)12345.f) *dst = v;   // ablation: no store
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        __syncthreads();   // Pb and Lx are reused by the next sequence
+        __syncthreads();   // P buffers and staging are reused next
     };
     reset();
-    if (tid == 0) ovf = 0;
 
     // two tiles in flight, then q^ of the first sequence, then the third tile
     {
@@ -700,134 +762,214 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     const TileOffsets to(lane);
     const TileOffsets8 to8(lane);
     const float sc = p.scale_log2;
-    int buf = 0;
-    int g = g0;
-    for (;;) {   // one sequence (or the part of it in this workgroup's range) per pass
-      const int gend = min(g1, g + cc.nt - cc.lt);
-      for (; g < gend; g++) {
+
+    // Latent-sum operands of the last scored tile (its transposing reads,
+    // taken right after its scores), used by the next step's value products.
+    // E4M3 tiles keep the raw codes (half the registers) and widen them
+    // just before each product.
+    bf16x8 av[2][F8 ? 1 : MCW];
+    uint2 av8[2][F8 ? MCW : 1];
+
+    // The tile ring: wait until this wavefront's share of the tile in
+    // buffer `buf` has landed, then a barrier (everyone's share landed, and
+    // every wavefront is past the previous step, so the buffer read there
+    // can be refilled and the P it wrote is visible), then refill that
+    // buffer three tiles ahead.  The refill's instructions go out one by one
+    // between the score products of the step, where the wavefront would
+    // otherwise wait on the matrix core, instead of stalling here while the
+    // load unit takes them.
+    using Dma = TileDma<NW, PAGED, F8>;
+    typename Dma::Pending pend;
+    auto tile_top = [&](int buf) {
         size_t nx0, nx1;   // rows of the tile issued below, looked up early
         dma.rows(ic, nx0, nx1);
         dma.wait_tile();
         __syncthreads();
-        // every wavefront is past the previous tile: its buffer can be
-        // refilled, so that three tiles stay in flight
-        dma.issue(ic, (buf + 3) % kNBuf, nx0, nx1);
+        pend = dma.prepare(ic, (buf + 3) % kNBuf, nx0, nx1);   // issued during the step's products
         ic.next(sv);
-        const uint8_t* C = Cs + buf * TL::TILE;
-        const int tbase = cc.lt * kT;
+    };
 
-        // ---- scores S^T = C . q^T: SCH interleaved accumulation chains (one
-        // chain would wait out each product's latency), operands PD steps ahead
-        f32x16 Sc[SCH];
-        if (!F8) {
-            bf16x8 a[PD];
+    // One step of the pipeline.  With DS: the score product of the tile in
+    // C (rows from tbase), its softmax into P buffer pw, and its latent-sum
+    // operands into av.  With DV: the latent-sum product of the previous
+    // tile, from av and P buffer pr.  The two products' instructions are
+    // interleaved -- two score accumulation chains alternating, with one
+    // value product after every second score product -- so the matrix core
+    // always has an independent product to start; the rest of the value
+    // products run beside the softmax.
+    auto step = [&](auto DS, auto DV, const uint8_t* C, int tbase, int n, int pr, int pw) {
+        constexpr bool do_s = decltype(DS)::value, do_v = decltype(DV)::value;
+        // Value product j of 32: K half kk = j / 16, head tile nt = j / 4 % 4,
+        // column tile mc = j % 4.  The P operands of group j / 4 (one K half,
+        // one head tile) stream through two slots: group q + 1 is read when
+        // group q starts.
+        bf16x8 pbr[2];
+        auto load_pb = [&](int q) {
+            if (q < 8) pbr[q % 2] = Pb[pr][q % 4][q / 4][lane];
+        };
+        auto vprod = [&](int j) {
+            if (j % 4 == 0) load_pb(j / 4 + 1);
+            const int kk = j / 16, nt = (j / 4) % 4, mc = j % 4;
+            const bf16x8 a = F8 ? fp8x8_to_bf16(av8[kk][F8 ? mc : 0]) : av[kk][F8 ? 0 : mc];
+            U[mc][nt] = mfma32(a, pbr[(j / 4) % 2], U[mc][nt]);
+        };
+        if constexpr (do_v) load_pb(0);
+        // in the score phase: value products 0 .. NU1 - 1, one after each
+        // score product (NU1 = 32) or after every second one (NU1 = 16)
+        auto interleave = [&](int ks) {
+            if (NU1 == 32 && ks < 32) vprod(ks);
+            if (NU1 == 16 && ks % 2 == 1 && ks < 32) vprod(ks / 2);
+        };
+        // the prepared refill, one instruction every DMA_EVERY score products
+        constexpr int DMA_EVERY = KS / Dma::SPW;
+        auto dma_slot = [&](int ks) {
+            if (ks % DMA_EVERY == 0 && ks / DMA_EVERY < Dma::SPW) dma.issue_slot(pend, ks / DMA_EVERY);
+        };
+        f32x16 S;
+        if constexpr (do_s) {
+            f32x16 Sc[SCH];
+            if (!F8) {
+                bf16x8 a[PD];
 #pragma unroll
-            for (int ks = 0; ks < PD; ks++) a[ks] = *(const bf16x8*)to.score(C, ks);
+                for (int ks = 0; ks < PD; ks++) a[ks] = *(const bf16x8*)to.score(C, ks);
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                const int c = ks % SCH;
-                if (ks < SCH) Sc[c] = mfma32_first(a[ks % PD], Qf[ks]);
-                else if (ks + SCH < KS) mfma32_acc(Sc[c], a[ks % PD], Qf[ks]);
-                else mfma32_last(Sc[c], a[ks % PD], Qf[ks]);
-                if (ks + PD < KS) a[ks % PD] = *(const bf16x8*)to.score(C, ks + PD);
-            }
-        } else {
-            // one 16-byte read per pair of steps, PJ pairs ahead; the codes
-            // widen to bf16 exactly just before their product
+                for (int ks = 0; ks < KS; ks++) {
+                    const int c = ks % SCH;
+                    if (ks < SCH) Sc[c] = mfma32_first(a[ks % PD], Qf[ks]);
+                    else if (ks + SCH < KS) mfma32_acc(Sc[c], a[ks % PD], Qf[ks]);
+                    else mfma32_last(Sc[c], a[ks % PD], Qf[ks]);
+                    if (ks + PD < KS) a[ks % PD] = *(const bf16x8*)to.score(C, ks + PD);
+                    if constexpr (do_v) interleave(ks);
+                    dma_slot(ks);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // one 16-byte read per pair of steps, PJ pairs ahead; the codes
+                // widen to bf16 exactly just before their product
 #ifndef MLA_PJ8
 #define MLA_PJ8 2
 #endif
-            constexpr int PJ = MLA_PJ8, KJ = KS / 2;
-            uint4 raw[PJ];
+                constexpr int PJ = MLA_PJ8, KJ = KS / 2;
+                uint4 raw[PJ];
 #pragma unroll
-            for (int j = 0; j < PJ; j++) raw[j] = *(const uint4*)to8.score(C, j);
-            bf16x8 a0, a1;
+                for (int j = 0; j < PJ; j++) raw[j] = *(const uint4*)to8.score(C, j);
+                bf16x8 a0, a1;
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++) {
-                const int c = ks % SCH, j = ks / 2;
-                if (ks % 2 == 0) {
-                    a0 = fp8x8_to_bf16(make_uint2(raw[j % PJ].x, raw[j % PJ].y));
-                    a1 = fp8x8_to_bf16(make_uint2(raw[j % PJ].z, raw[j % PJ].w));
-                    if (j + PJ < KJ) raw[j % PJ] = *(const uint4*)to8.score(C, j + PJ);
+                for (int ks = 0; ks < KS; ks++) {
+                    const int c = ks % SCH, j = ks / 2;
+                    if (ks % 2 == 0) {
+                        a0 = fp8x8_to_bf16(make_uint2(raw[j % PJ].x, raw[j % PJ].y));
+                        a1 = fp8x8_to_bf16(make_uint2(raw[j % PJ].z, raw[j % PJ].w));
+                        if (j + PJ < KJ) raw[j % PJ] = *(const uint4*)to8.score(C, j + PJ);
+                    }
+                    const bf16x8 av8 = ks % 2 ? a1 : a0;
+                    if (ks < SCH) Sc[c] = mfma32_first(av8, Qf[ks]);
+                    else if (ks + SCH < KS) mfma32_acc(Sc[c], av8, Qf[ks]);
+                    else mfma32_last(Sc[c], av8, Qf[ks]);
+                    if constexpr (do_v) interleave(ks);
+                    dma_slot(ks);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                const bf16x8 av8 = ks % 2 ? a1 : a0;
-                if (ks < SCH) Sc[c] = mfma32_first(av8, Qf[ks]);
-                else if (ks + SCH < KS) mfma32_acc(Sc[c], av8, Qf[ks]);
-                else mfma32_last(Sc[c], av8, Qf[ks]);
+            }
+            S = Sc[0];
+            if constexpr (SCH == 2) S += Sc[1];
+        } else if constexpr (do_v) {
+#pragma unroll
+            for (int j = 0; j < NU1; j++) vprod(j);
+        }
+        // the remaining value products, independent of the softmax below:
+        // the wavefront issues the softmax's vector instructions while each
+        // product runs on the matrix core
+        if constexpr (do_v) {
+#pragma unroll
+            for (int j = NU1; j < 32; j++) vprod(j);
+        }
+        if constexpr (do_s) {
+            // ---- softmax weights: lane holds head hs, tokens 8 (v / 4) + 4 hh + v % 4;
+            // rows past the sequence's length (its last tile) are masked
+            // without a branch, so the whole phase is one scheduling region
+            float lm = -INFINITY;
+            const int nv = n - tbase - 4 * hh;   // this lane's rows r < nv are valid
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                S[v] = 8 * (v / 4) + v % 4 < nv ? S[v] : -INFINITY;
+                lm = fmaxf(lm, S[v]);
+            }
+            lm = fmaxf(lm, xor32(lm)) * sc;
+            m = m == -INFINITY ? lm : m;   // first tile of the sequence: fix the reference
+            ovf_w |= __builtin_amdgcn_ballot_w64(lm > m + 64.f) != 0;
+            uint32_t pk[8];
+            float ps = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[v], sc, -m));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[v + 1], sc, -m));
+                ps += p0 + p1;
+                pk[v / 2] = pack_bf16x2(p0, p1);
+            }
+            lsum += ps;
+            Pb[pw][wave][0][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            Pb[pw][wave][1][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+            // this tile's latent-sum operands, for the next step
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                for (int mc = 0; mc < MCW; mc++) {
+                    if (F8) av8[kk][F8 ? mc : 0] = lds_read_tr8(to8.value(C, wave, mc, kk));
+                    else av[kk][F8 ? 0 : mc] = cat_tr(lds_read_tr(to.value(C, wave, mc, kk, 0)),
+                                                      lds_read_tr(to.value(C, wave, mc, kk, 1)));
+                }
+        }
+#ifndef MLA_VPG
+#define MLA_VPG 6
+#endif
+        if constexpr (do_s && do_v) {
+            // one value product, then MLA_VPG vector instructions, and so on
+#pragma unroll
+            for (int j = NU1; j < 32; j++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, MLA_VPG, 0);
             }
         }
-        f32x16 S = Sc[0];
-#pragma unroll
-        for (int c = 1; c < SCH; c++) S += Sc[c];
-        // the latent-sum operands of this tile do not depend on P: read them now
-        bf16x8 av[2][MCW];
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-            for (int mc = 0; mc < MCW; mc++)
-                av[kk][mc] = F8 ? fp8x8_to_bf16(lds_read_tr8(to8.value(C, wave, mc, kk)))
-                                : cat_tr(lds_read_tr(to.value(C, wave, mc, kk, 0)),
-                                         lds_read_tr(to.value(C, wave, mc, kk, 1)));
+    };
 
-        // ---- softmax weights: lane holds head hs, tokens 8 (v / 4) + 4 hh + v % 4
-        float lm = -INFINITY;
-        if (tbase + kT > cc.n) {   // the sequence's last tile: mask the rows past its length
-#pragma unroll
-            for (int v = 0; v < 16; v++)
-                if (tbase + 8 * (v / 4) + 4 * hh + v % 4 >= cc.n) S[v] = -INFINITY;
-        }
-#pragma unroll
-        for (int v = 0; v < 16; v++) lm = fmaxf(lm, S[v]);
-        lm = fmaxf(lm, xor32(lm)) * sc;
-        if (m == -INFINITY) m = lm;   // first tile of the sequence: fix the reference
-        if (__builtin_amdgcn_ballot_w64(lm > m + 64.f) && lane == 0) ovf = 1;
-        uint32_t pk[8];
-        float ps = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[v], sc, -m));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[v + 1], sc, -m));
-            ps += p0 + p1;
-            pk[v / 2] = pack_bf16x2(p0, p1);
-        }
-        lsum += ps;
-        Pb[wave][0][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        Pb[wave][1][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-        __syncthreads();   // P of every head visible
-        // Every wavefront set ovf for this tile before the barrier above, and
-        // none can set it for the next tile before all of them have passed
-        // the barrier at the top of the next iteration: read here, the flag
-        // is the same in every wavefront, so the break below is uniform.
-        const int flagged = ovf;
-        // ---- latent sum U^T += C^T . P^T over this wavefront's columns
-#pragma unroll
-        for (int kk = 0; kk < 2; kk++) {
-            bf16x8 pb[NTH];
-#pragma unroll
-            for (int nt = 0; nt < NTH; nt++) pb[nt] = Pb[nt][kk][lane];
-#pragma unroll
-            for (int nt = 0; nt < NTH; nt++)
-#pragma unroll
-                for (int mc = 0; mc < MCW; mc++) U[mc][nt] = mfma32(av[kk][mc], pb[nt], U[mc][nt]);
-        }
+    std::true_type Y;
+    std::false_type N;
+    int buf = 0;
+    int g = g0;
+    for (;;) {   // one sequence (or the part of it in this workgroup's range) per pass
+        const int gend = min(g1, g + cc.nt - cc.lt);
+        // first tile: scores only
+        tile_top(buf);
+        step(Y, N, Cs + buf * TL::TILE, cc.lt * kT, cc.n, 0, g & 1);
         cc.lt++;
         buf = (buf + 1) % kNBuf;
-        if (flagged) break;   // workgroup-uniform (read between two barriers)
-      }
-      if (g < gend) break;   // left early: flagged for the merge kernel
-      write_partial(cc.b);
-      if (g >= g1) break;
-      // the next sequence: its tile cursor, accumulators and q^
-      cc.lt--;
-      cc.g = g - 1;
-      cc.next(sv);
-      reset();
-      load_q(cc.b);
-      vmem_drain();
+        // then each tile's scores beside the previous tile's latent sum
+        for (++g; g < gend; g++) {
+            tile_top(buf);
+            step(Y, Y, Cs + buf * TL::TILE, cc.lt * kT, cc.n, (g - 1) & 1, g & 1);
+            cc.lt++;
+            buf = (buf + 1) % kNBuf;
+        }
+        // last tile's latent sum
+        __syncthreads();   // its P visible
+        step(N, Y, Cs, 0, 0, (g - 1) & 1, 0);
+        write_partial(cc.b, F8 ? Stg8 : Cs + ((buf + kNBuf - 1) % kNBuf) * TL::TILE);
+        if (g >= g1) break;
+        // the next sequence: its tile cursor, accumulators and q^
+        cc.lt--;
+        cc.g = g - 1;
+        cc.next(sv);
+        reset();
+        load_q(cc.b);
+        vmem_drain();
     }
     wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
-    __syncthreads();   // ovf from the last tile
-    if (tid == 0) p.flags[w] = ovf;
+    // the workgroup's flag: any wavefront that saw a score past its reference
+    int* const ovf_s = (int*)&Pb[1][1][0][0];
+    if (lane == 0) ovf_s[wave] = ovf_w;
+    __syncthreads();
+    if (tid == 0) p.flags[w] = (ovf_s[0] | ovf_s[1] | ovf_s[2] | ovf_s[3]) ? 1 : 0;
 }
 
 // The partial (m, l, U columns 8 lane .. 8 lane + 7) of head i over the
@@ -838,7 +980,8 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
 // online softmax in fp32 with the reference moved on every new maximum;
 // the dot products take the stored bf16 q^ and cache bits, lane l holding
 // latent dims 8 l .. 8 l + 7 and rotary dim l (d_c = 8 * 64, d_R = 64).
-// Tokens go 8 at a time so that their row loads are in flight together.
+// Tokens go kRcRows at a time so that their row loads are in flight together.
+constexpr int kRcRows = 4;   // rows in flight in the exact recompute
 __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_lo, int g_hi, int s0,
                                       int lane, float& M, float& L, float4& u0, float4& u1)
 {
@@ -859,11 +1002,11 @@ __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_l
     }
     const uint16_t* cache = (const uint16_t*)p.cache;
     float m = -INFINITY, l = 0.f, u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int t0 = t_lo; t0 < t_hi; t0 += 8) {
-        uint4 c8[8];
-        uint16_t cr[8];
+    for (int t0 = t_lo; t0 < t_hi; t0 += kRcRows) {
+        uint4 c8[kRcRows];
+        uint16_t cr[kRcRows];
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
+        for (int k = 0; k < kRcRows; k++) {
             const int t = min(t0 + k, t_hi - 1);
             const size_t row = p.bt ? paged_row(p.bt, bb, t, p.max_blocks, p.bs_log2, p.num_blocks)
                                     : (size_t)bb * p.s_max + t;
@@ -877,7 +1020,7 @@ __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_l
             }
         }
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
+        for (int k = 0; k < kRcRows; k++) {
             if (t0 + k >= t_hi) break;   // wave-uniform
             const uint32_t w4[4] = {c8[k].x, c8[k].y, c8[k].z, c8[k].w};
             float c[8];
@@ -925,7 +1068,7 @@ constexpr int kFinSeq = 8;     // sequences (and wavefronts) per workgroup
 constexpr int kFinChunk = 8;   // partials in flight per wavefront
 constexpr int kAbStride = 512 + 8;   // bf16 per A-operand row in LDS
 
-__global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParams p)
+__global__ __launch_bounds__(64 * kFinSeq, 4) void mla_finish_kernel(const MlaParams p)
 {
     __shared__ __attribute__((aligned(16))) float Acc[kFinSeq][512];      // shares, when split
     __shared__ float Mls[kFinSeq][2];
@@ -939,14 +1082,17 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
     const int nsub = (kFinSeq - sq + nb - 1) / nb;   // wavefronts sharing sequence sq
     const int bb = b0 + sq;
 
-    // W_UV fragments of this wavefront's first column tile, fetched now so
-    // that their latency hides behind the merge
+    // W_UV fragments of this wavefront's first column tile: the first
+    // kWuvPre K steps are fetched now, so that their latency hides behind
+    // the merge, the rest once the merge is done (all 16 up front would
+    // push the kernel past 128 registers, i.e. below two workgroups per CU)
     const uint16_t* __restrict__ wuv = (const uint16_t*)p.w_uv + (size_t)i * p.d_v * p.d_c;
+    constexpr int kWuvPre = 8;
     bf16x8 bws[16];   // d_c = 512: 16 K steps
     if (wave < p.d_v / 16) {
         const uint16_t* wrow = wuv + (size_t)(wave * 16 + li) * p.d_c + 8 * G;
 #pragma unroll
-        for (int k = 0; k < 16; k++) bws[k] = *(const bf16x8*)(wrow + 32 * k);
+        for (int k = 0; k < kWuvPre; k++) bws[k] = *(const bf16x8*)(wrow + 32 * k);
     }
 
     // the partials of sequence bb: slots w + bb of the workgroups w whose
@@ -1064,6 +1210,11 @@ __global__ __launch_bounds__(64 * kFinSeq) void mla_finish_kernel(const MlaParam
         }
     }
 
+    if (wave < p.d_v / 16) {
+        const uint16_t* wrow = wuv + (size_t)(wave * 16 + li) * p.d_c + 8 * G;
+#pragma unroll
+        for (int k = kWuvPre; k < 16; k++) bws[k] = *(const bf16x8*)(wrow + 32 * k);
+    }
     // u~ = U / L: written out if asked, and split into the A operand rows
     if (wave < nb) {
         // u~ = U / L, in cache units: times the latent scale of an FP8 cache
@@ -1123,7 +1274,10 @@ hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
     // absorb workgroups, plus one that computes the tile schedule
     if (p.d_nope > kAbsMaxNope) return hipErrorInvalidValue;
     const unsigned g1 = (unsigned)(p.h * (p.d_c / kAbsCols)) + 1;
-    hipLaunchKernelGGL(mla_absorb_kernel, dim3(g1), dim3(256), 0, st, p);
+    if (p.d_nope <= 128)
+        hipLaunchKernelGGL(mla_absorb_kernel<128>, dim3(g1), dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL(mla_absorb_kernel<kAbsMaxNope>, dim3(g1), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g2 = (unsigned)p.n_wg;

@@ -96,7 +96,7 @@ def run_gqa(name, steps, warmup, rotate, keep=None):
     out = torch.empty_like(sets[0]["q"])
     lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device=dev)
     wsb = A.attn_decode_workspace_bytes(0, sh.B, sh.s_max, sh.h, sh.h_kv, sh.d_h)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     it = [0]
@@ -128,7 +128,7 @@ def run_gqa_fp8(name, steps, warmup, rotate, k_scale=1.0 / 64, v_scale=1.0 / 64)
     out = torch.empty_like(sets[0]["q"])
     lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device=dev)
     wsb = A.attn_decode_workspace_bytes(0, sh.B, sh.s_max, sh.h, sh.h_kv, sh.d_h)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     it = [0]
@@ -158,7 +158,7 @@ def run_gqa_multi(name, q_len, steps, warmup, rotate):
     out = torch.empty_like(q)
     lse = torch.empty((sh.B, q_len, sh.h), dtype=torch.float32, device="cuda")
     wsb = A.attn_decode_gqa_multi_workspace_bytes(sh.B, q_len, sh.s_max, sh.h, sh.h_kv, sh.d_h)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     it = [0]
@@ -227,7 +227,7 @@ def run_dcp_gqa(name, n, steps, warmup):
     parts_l = torch.zeros((n, sh.B, sh.h), dtype=torch.float32, device="cuda")
     lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device="cuda")
     wsb = A.attn_decode_workspace_bytes(0, sh.B, S, sh.h, sh.h_kv, sh.d_h)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
@@ -252,7 +252,7 @@ def run_mla(name, steps, warmup, rotate, keep=None):
     out = torch.empty((sh.B, sh.h, sh.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device=dev)
     wsb = A.attn_decode_workspace_bytes(1, sh.B, sh.s_max, sh.h, 1, sh.d_c, sh.d_R)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     it = [0]
@@ -284,7 +284,7 @@ def run_mla_fp8(name, steps, warmup, rotate, c_scale=1.0 / 32, r_scale=1.0 / 32)
     out = torch.empty((sh.B, sh.h, sh.d_v), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device="cuda")
     wsb = A.attn_decode_workspace_bytes(1, sh.B, sh.s_max, sh.h, 1, sh.d_c, sh.d_R)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     it = [0]

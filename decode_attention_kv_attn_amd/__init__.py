@@ -291,7 +291,8 @@ def attn_decode_mla_absorbed(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cac
 # the entry points above).
 # ---------------------------------------------------------------------------
 class Workspace:
-    """A reusable device workspace (grown on demand)."""
+    """A reusable device workspace (grown on demand), zero-filled when
+    allocated as the GQA calls require; the calls leave it that way."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -302,7 +303,7 @@ class Workspace:
         if nbytes == 0:
             return None, 0
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf, self.buf.numel()
 
 

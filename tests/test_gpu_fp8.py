@@ -151,7 +151,7 @@ def test_fp8_per_page_scales(B, h, h_kv, d_h, s):
     out = torch.empty_like(d["q"])
     lse = torch.empty((B, h), dtype=torch.float32, device=DEV)
     wsb = A.attn_decode_workspace_bytes(0, B, sh.s_max, h, h_kv, d_h)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=DEV)
     A.attn_decode_gqa_fp8_paged_scales(out, lse, d["q"], K8, V8, ks, vs, d["s"], bt, bt.shape[1], 16,
                                        K8.shape[0], B, sh.s_max, h, h_kv, d_h, 0.0, ws, wsb)
     torch.cuda.synchronize()
@@ -176,7 +176,7 @@ def test_fp8_per_page_scales_uniform_equal_per_tensor_call():
     o2 = torch.empty_like(o1)
     l2 = torch.empty_like(l1)
     wsb = A.attn_decode_workspace_bytes(0, 3, sh.s_max, 32, 8, 128)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=DEV)
     A.attn_decode_gqa_fp8_paged_scales(o2, l2, d["q"], K8, V8, ks, vs, d["s"], bt, bt.shape[1], 16,
                                        K8.shape[0], 3, sh.s_max, 32, 8, 128, 0.0, ws, wsb)
     torch.cuda.synchronize()

@@ -34,7 +34,7 @@ def test_gqa_split_context_graph():
     out = torch.empty_like(d["q"])
     lse = torch.empty((2, 32), dtype=torch.float32, device=DEV)
     wsb = A.attn_decode_workspace_bytes(0, 2, sh.s_max, 32, 8, 128)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     s = torch.cuda.Stream()
 
     def call(o, l, stream):
@@ -68,7 +68,7 @@ def test_mla_graph():
     ul = torch.empty((3, 64, 512), dtype=torch.float32, device=DEV)
     lse = torch.empty((3, 64), dtype=torch.float32, device=DEV)
     wsb = A.attn_decode_workspace_bytes(1, 3, sh.s_max, 64, 1, 512, 64)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     s = torch.cuda.Stream()
 
     def call(o, u, l, stream):
@@ -109,7 +109,7 @@ def test_append_then_decode_graph():
     pos = torch.tensor([99, 699, 32, 0], dtype=torch.int32, device=DEV)   # last slot of each sequence
     out = torch.empty((4, 16, 128), dtype=torch.bfloat16, device=DEV)
     wsb = A.attn_decode_workspace_bytes(0, 4, smax, 16, 4, 128)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=DEV)
     s = torch.cuda.Stream()
 
     def step(o, stream):

@@ -1,0 +1,151 @@
+"""GPU parity of the tile-run schedule of the GQA/MQA/MHA matrix-core kernel.
+
+With at least 64 (sequence, KV head, row block) segments the library spreads
+equal runs of 32-token tiles over 512 workgroups whatever the mix of lengths,
+and a segment split between workgroups is merged by the last of them to
+finish (a counter per segment in the workspace, set back to zero by that
+workgroup).  These cases exercise that path against the oracle: mixed and
+empty lengths, one segment split over more than 256 workgroups, paged pools,
+E4M3 caches (per-tensor and per-page scales), several new tokens per sequence
+(two row blocks per KV head), and repeated calls on one workspace.
+"""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_kv_attn_amd as A
+import oracle
+import synth
+from tests._gpu import assert_close, assert_lse_close, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def lengths(B, seed, lo=0, hi=3000, zeros=()):
+    rng = np.random.default_rng(seed)
+    s = rng.integers(lo, hi + 1, size=B)
+    for i in zeros:
+        s[i] = 0
+    return tuple(int(x) for x in s)
+
+
+def check_gqa(sh, d, out, lse, what):
+    ref, ref_lse = oracle.gqa_decode(*(synth.host_bits(d[k]) for k in ("q", "K", "V")), d["s_host"],
+                                     sh.b, block_table=d.get("block_table_host"))
+    assert_close(to_f64(out), ref, sh.b, what)
+    assert_lse_close(to_f64(lse), ref_lse, sh.b, what)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("h,h_kv,d_h", [(16, 2, 128), (8, 1, 128), (64, 2, 64)])
+def test_mixed_lengths_fused_merge(paged, h, h_kv, d_h):
+    B = 64 if h_kv == 1 else 40
+    s = lengths(B, seed=h + h_kv + d_h, hi=4000, zeros=(0, 7))
+    s = s[:3] + (1, 31, 33) + s[6:]
+    print(f"[sched] B={B} h={h} h_kv={h_kv} d_h={d_h} paged={paged}", flush=True)
+    sh = synth.GqaShape("t", B=B, h=h, h_kv=h_kv, d_h=d_h, b=2, s=s, paged=paged, seed=900 + h)
+    d = synth.draw_gqa(sh, device=DEV)
+    out, lse = A.decode_gqa(d["q"], d["K"], d["V"], d["s"], block_table=d.get("block_table"),
+                            s_max=sh.s_max)
+    torch.cuda.synchronize()
+    check_gqa(sh, d, out, lse, "out")
+
+
+def test_one_segment_split_over_more_than_256_workgroups_with_empties():
+    # 63 empty or one-token sequences and one of 140,000 tokens over one KV
+    # head: the long segment's 4,375 tiles are cut into runs of 16, so about
+    # 274 workgroups share it and the last one merges all their partials
+    s = tuple([0, 1] * 31 + [0]) + (140000,)
+    print("[sched] one long segment, 63 short ones", flush=True)
+    sh = synth.GqaShape("t", B=64, h=8, h_kv=1, d_h=128, b=2, s=s, seed=911)
+    d = synth.draw_gqa(sh, device=DEV)
+    out, lse = A.decode_gqa(d["q"], d["K"], d["V"], d["s"])
+    torch.cuda.synchronize()
+    check_gqa(sh, d, out, lse, "out")
+    o = to_f64(out)
+    assert np.all(o[0::2][:32] == 0.0) and np.all(np.isneginf(to_f64(lse)[0:62:2]))
+
+
+def test_repeated_calls_share_one_workspace():
+    # the counters return to zero after every call: the same workspace gives
+    # the same bits on a repeat, and serves calls of other shapes in between
+    ws = A.Workspace(DEV)
+    sh1 = synth.GqaShape("t", B=48, h=32, h_kv=4, d_h=128, b=2, s=lengths(48, 3, hi=5000), seed=921)
+    sh2 = synth.GqaShape("t", B=70, h=8, h_kv=1, d_h=64, b=2, s=lengths(70, 4, hi=2500), paged=True,
+                         seed=922)
+    d1 = synth.draw_gqa(sh1, device=DEV)
+    d2 = synth.draw_gqa(sh2, device=DEV)
+    print("[sched] repeated calls on one workspace", flush=True)
+    o1, l1 = A.decode_gqa(d1["q"], d1["K"], d1["V"], d1["s"], workspace=ws)
+    o2, l2 = A.decode_gqa(d2["q"], d2["K"], d2["V"], d2["s"], block_table=d2["block_table"],
+                          s_max=sh2.s_max, workspace=ws)
+    o3, l3 = A.decode_gqa(d1["q"], d1["K"], d1["V"], d1["s"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(l1, l3)
+    check_gqa(sh1, d1, o1, l1, "first shape")
+    check_gqa(sh2, d2, o2, l2, "second shape")
+    # every counter (the first 256 KiB of the workspace) is zero again
+    assert int(ws.buf[:256 * 1024].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_fp8_per_tensor_scales(paged):
+    ks, vs = 1.0 / 64, 0.0123
+    s = lengths(64, 5, hi=3000, zeros=(3,))
+    sh = synth.GqaShape("t", B=64, h=16, h_kv=2, d_h=128, b=2, s=s, paged=paged, seed=931)
+    print(f"[sched] fp8 paged={paged}", flush=True)
+    d = synth.draw_gqa_fp8(sh, ks, vs, device=DEV)
+    out, lse = A.decode_gqa_fp8(d["q"], d["K8"], d["V8"], ks, vs, d["s"],
+                                block_table=d.get("block_table"), s_max=sh.s_max)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.gqa_decode_fp8(synth.host_bits(d["q"]), synth.host_bits(d["K8"]),
+                                         synth.host_bits(d["V8"]), ks, vs, d["s_host"],
+                                         block_table=d.get("block_table_host"))
+    assert_close(to_f64(out), ref, 2, "out")
+    assert_lse_close(to_f64(lse), ref_lse, 2, "lse")
+
+
+def test_fp8_per_page_scales():
+    from tests.test_gpu_fp8 import page_scaled_pool
+    B, h, h_kv, d_h = 40, 16, 2, 128
+    s = lengths(B, 6, hi=4000, zeros=(1,))
+    sh = synth.GqaShape("t", B=B, h=h, h_kv=h_kv, d_h=d_h, b=2, s=s, paged=True, seed=941)
+    print("[sched] fp8 per-page scales", flush=True)
+    d, K8, V8, ksc, vsc = page_scaled_pool(sh, seed=941)
+    bt = d["block_table"]
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((B, h), dtype=torch.float32, device=DEV)
+    wsb = A.attn_decode_workspace_bytes(0, B, sh.s_max, h, h_kv, d_h)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    A.attn_decode_gqa_fp8_paged_scales(out, lse, d["q"], K8, V8, ksc, vsc, d["s"], bt, bt.shape[1],
+                                       16, K8.shape[0], B, sh.s_max, h, h_kv, d_h, 0.0, ws, wsb)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.gqa_decode_fp8_paged_scales(synth.host_bits(d["q"]), synth.host_bits(K8),
+                                                      synth.host_bits(V8), ksc.cpu().numpy(),
+                                                      vsc.cpu().numpy(), d["s_host"],
+                                                      d["block_table_host"])
+    assert_close(to_f64(out), ref, 2, "out")
+    assert_lse_close(to_f64(lse), ref_lse, 2, "lse")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_several_new_tokens_two_row_blocks(paged):
+    # g = 32 query heads per KV head and 8 new tokens: 256 rows per KV head,
+    # two row blocks of 128; 16 sequences x 2 KV heads x 2 blocks = 64 segments
+    B, q_len, h, h_kv, d_h = 16, 8, 64, 2, 128
+    s = lengths(B, 7, lo=3, hi=3000)
+    s = (5, 8) + s[2:]
+    sh = synth.GqaShape("t", B=B, h=h, h_kv=h_kv, d_h=d_h, b=2, s=s, paged=paged, seed=951)
+    print(f"[sched] q_len={q_len} paged={paged}", flush=True)
+    d = synth.draw_gqa(sh, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(952)
+    q = torch.randn((B, q_len, h, d_h), generator=g, device=DEV).to(torch.bfloat16)
+    out, lse = A.decode_gqa_multi(q, d["K"], d["V"], d["s"], block_table=d.get("block_table"),
+                                  s_max=sh.s_max)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.gqa_decode_multi(synth.host_bits(q), synth.host_bits(d["K"]),
+                                           synth.host_bits(d["V"]), d["s_host"], 2,
+                                           block_table=d.get("block_table_host"))
+    assert_close(to_f64(out), ref, 2, "out")
+    assert_lse_close(to_f64(lse), ref_lse, 2, "lse")

@@ -291,8 +291,7 @@ def attn_decode_mla_absorbed(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cac
 # the entry points above).
 # ---------------------------------------------------------------------------
 class Workspace:
-    """A reusable device workspace (grown on demand), zero-filled when
-    allocated as the GQA calls require; the calls leave it that way."""
+    """A reusable device workspace (grown on demand)."""
 
     def __init__(self, device="cuda"):
         self.device = device

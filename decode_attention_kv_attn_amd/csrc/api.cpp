@@ -60,23 +60,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // rows take one workgroup of 16-row wavefronts; more take 4 wavefronts of
 // two 16-row blocks each (rpw = 2), which read each tile once for 128 rows,
 // in n_rb such workgroups.
-// With enough (b, KV head, row block) segments the matrix-core kernel runs
-// the tile-run schedule instead of the chunked grid: n_wg workgroups take
-// equal runs of tiles across the segments (balanced whatever the mix of
-// lengths), and a segment split between workgroups is merged by the last of
-// them (no second launch).  Its split counters sit at the head of the
-// workspace, at a fixed place so that calls of any shape can share one
-// workspace; they are zero between calls.  With few segments and long
-// contexts a segment would be split many ways and its last workgroup would
-// merge a long list alone, so the chunked grid and the merge kernel remain.
-constexpr long long kGqaMaxSegs = 65536;
-constexpr size_t kGqaCounterBytes = (size_t)kGqaMaxSegs * sizeof(int32_t);
-constexpr long long kGqaMinSchedSegs = 64;
-
 struct GqaPlan {
-    bool mfma, sched;
+    bool mfma;
     int HG, n_hg, NW, n_split, chunk, n_rb, rpw;
-    int n_wg, min_tiles, slot_rows;
     size_t part_o_bytes, part_ml_bytes, ws_bytes;
 };
 
@@ -84,7 +70,7 @@ struct GqaPlan {
 #define GQA_F8_TARGET 512
 #endif
 GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, bool f8 = false,
-                      int q_len = 1, bool allow_sched = true)
+                      int q_len = 1)
 {
     GqaPlan P{};
     const int g = h / h_kv;
@@ -114,32 +100,6 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
         P.NW = 1;
         target = 2048;
     }
-#ifndef GQA_SCHED_ENABLE
-#define GQA_SCHED_ENABLE 1
-#endif
-    if (mfma && allow_sched && GQA_SCHED_ENABLE) {
-        const long long n_seg = (long long)B * h_kv * P.n_rb;
-        const long long tiles = n_seg * (s_max > 0 ? cdiv(s_max, 32) : 1);
-        if (B <= 1024 && n_seg >= kGqaMinSchedSegs && n_seg <= kGqaMaxSegs && tiles < (1LL << 30)) {
-            // runs of tiles over the sequences, each served by one workgroup
-            // per (KV head, row block): about `target` workgroups in all
-            const long long per = (long long)h_kv * P.n_rb;
-            P.sched = true;
-#ifndef GQA_SCHED_ROUNDS
-#define GQA_SCHED_ROUNDS 1
-#endif
-            P.n_wg = (int)(target / per > 0 ? target / per : 1) * GQA_SCHED_ROUNDS;   // runs
-            P.min_tiles = 8;
-            P.slot_rows = rows < 64 * P.rpw ? rows : 64 * P.rpw;
-            P.n_split = 1;
-            P.chunk = 0;
-            const size_t slots = ((size_t)P.n_wg + (size_t)B - 1) * (size_t)per;
-            P.part_o_bytes = align256(slots * P.slot_rows * d_h * sizeof(float));
-            P.part_ml_bytes = align256(slots * P.slot_rows * 2 * sizeof(float));
-            P.ws_bytes = kGqaCounterBytes + P.part_o_bytes + P.part_ml_bytes;
-            return P;
-        }
-    }
 #ifndef GQA_MAX_CHUNK
 #define GQA_MAX_CHUNK 4096
 #endif
@@ -167,12 +127,11 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
 
 bool gqa_uses_mfma(int h, int h_kv, int b) { return b == 2 && h / h_kv <= 64; }
 
-GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b, int q_len = 1,
-                 bool allow_sched = true)
+GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b, int q_len = 1)
 {
-    if (b == 1) return plan_gqa_path(true, B, s_max, h, h_kv, d_h, true, q_len, allow_sched);
-    if (q_len > 1) return plan_gqa_path(true, B, s_max, h, h_kv, d_h, false, q_len, allow_sched);
-    return plan_gqa_path(gqa_uses_mfma(h, h_kv, b), B, s_max, h, h_kv, d_h, false, 1, allow_sched);
+    if (b == 1) return plan_gqa_path(true, B, s_max, h, h_kv, d_h, true, q_len);
+    if (q_len > 1) return plan_gqa_path(true, B, s_max, h, h_kv, d_h, false, q_len);
+    return plan_gqa_path(gqa_uses_mfma(h, h_kv, b), B, s_max, h, h_kv, d_h);
 }
 
 // ---- MLA plan ----------------------------------------------------------------
@@ -310,9 +269,7 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
         if (rc) return rc;
     }
     if (B == 0) return ATTN_OK;
-    // the no-alloc entry point keeps the chunked grid: its scratch then holds
-    // nothing that has to start at zero
-    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b, q_len, !noalloc);
+    const GqaPlan P = plan_gqa(B, s_max, h, h_kv, d_h, b, q_len);
     if (noalloc) {   // the fixed per-device scratch replaces the caller's workspace
         if (P.ws_bytes > attn::kNoAllocScratchBytes)
             return fail(ATTN_ENOTSUP,
@@ -332,18 +289,8 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     p.v = cache_v;
     p.s = s;
     p.bt = block_table;
-    if (P.sched) {
-        p.counters = (int32_t*)workspace;
-        p.part_o = (float*)((char*)workspace + kGqaCounterBytes);
-        p.part_ml = (float*)((char*)workspace + kGqaCounterBytes + P.part_o_bytes);
-        p.sched = 1;
-        p.n_wg = P.n_wg;
-        p.min_tiles = P.min_tiles;
-        p.slot_rows = P.slot_rows;
-    } else {
-        p.part_o = (float*)workspace;
-        p.part_ml = (float*)((char*)workspace + P.part_o_bytes);
-    }
+    p.part_o = (float*)workspace;
+    p.part_ml = (float*)((char*)workspace + P.part_o_bytes);
     p.max_blocks = max_blocks;
     p.bs_log2 = block_table ? ilog2(block_size) : 0;
     p.num_blocks = num_blocks;
@@ -364,7 +311,7 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     // matrix-core kernel over a paged pool with splits: workgroups go to the
     // non-empty (b, split) pairs only (each workgroup scans the B lengths to
     // find its pair, so only for moderate B); the grid is then a multiple of 8
-    p.compact = !P.sched && P.mfma && block_table != nullptr && P.n_split > 1 && B <= 16 * 64;
+    p.compact = P.mfma && block_table != nullptr && P.n_split > 1 && B <= 16 * 64;
     // matrix-core kernel over a contiguous cache: the KV heads are permuted so
     // that the XCD streaming a head column and the column's address bit 8
     // differ in parity (needs one workgroup per (b, head, split), h_kv a
@@ -378,8 +325,6 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     }
     long long grid = (long long)B * h_kv * P.n_hg * P.n_split * P.n_rb;
     if (p.compact) grid = (grid + 7) & ~7LL;
-    if (P.sched) grid = (long long)P.n_wg * h_kv * P.n_rb;   // runs x (KV head, row block)
-    if (P.sched && block_table) grid = (grid + 7) & ~7LL;       // XCD-major numbering needs 8 | grid
     if (grid >= (1LL << 31)) return fail(ATTN_ENOTSUP, "problem too large for one launch");
     // a paged pool's tiles gather 16-row pages: four wavefronts keep more of
     // their DMA in flight than two (measured 1-2 % faster; contiguous

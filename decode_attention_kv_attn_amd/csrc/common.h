@@ -92,12 +92,6 @@ __device__ __forceinline__ float wave_sum(float x)
     x += xor32(x);
     return x;
 }
-__device__ __forceinline__ int wave_sum_int(int x)
-{
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-    return x;
-}
 // inclusive prefix sum over the 64 lanes of a wavefront (lane l gets the sum
 // of lanes 0 .. l)
 __device__ __forceinline__ int wave_scan_incl(int x)

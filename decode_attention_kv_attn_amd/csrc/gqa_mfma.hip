@@ -178,23 +178,6 @@ __device__ __forceinline__ int pair_head(int j, int flip)
     return (j & ~msk) | (((lo & 1) ^ 1 ^ flip) << kb) | (lo >> 1);
 }
 
-// Device-coherent (agent-scope) 32-bit store and load: they reach the point
-// where all XCDs see them, without the whole-L2 writeback and invalidation
-// that a device-scope fence does on this GPU.
-__device__ __forceinline__ void dev_store(float* p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float dev_load(const float* p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Tiles of one (sequence, KV head, row block) segment: a sequence of length n
-// has max(1, ceil(n / 32)) of them (an empty sequence keeps one, whose work
-// item writes its zero output and -inf lse).
-__device__ __forceinline__ int seg_tiles(int n) { return max(1, (n + 31) / 32); }
-
 template <int D, int NW, bool PAGED, bool F8, int RPW, bool PS = false>
 __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                                                            const int32_t* __restrict__ btab)
@@ -203,460 +186,13 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     constexpr int OPW = C::OPS / NW;   // DMA instructions per wavefront and tile
     static_assert(C::OPS % NW == 0, "DMA instructions must split evenly");
     __shared__ __attribute__((aligned(1024))) uint8_t Ls[C::NBUF * 2 * C::KT];
-    __shared__ int last_flag;
 
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int g = p.h / p.h_kv;
-    // The rows of a work item are the (query position jq, head of the group)
-    // pairs, r = jq * g + gi: g rows for one new token, g * q_len when
-    // several new tokens are verified at once.  Row block rb holds rows
-    // 64 RPW rb .. + 64 RPW - 1; wavefront w takes the RPW 16-row blocks
-    // 16 (k NW + w) .. + 15 of them (k < RPW), all fed by the same LDS
-    // operand reads of each tile.
-    const int n_rows = g * p.q_len;
-    const int32_t* __restrict__ s_len = p.s;
-
-    // One piece of work: tokens [t0, t1) of sequence b (length n), KV head j
-    // (its cache columns, query heads and output rows), row block rb.
-    // omode 0: the piece is the whole context, the result goes to out and
-    // lse; 1: split `split` of the chunked grid, partial row (orow n_split +
-    // split); 2: slot `slot` of the tile-run schedule, partial row (slot
-    // slot_rows + row within the block).
-    auto run_piece = [&](int b, int j, int rb, int n, int t0, int t1, int omode, int split, int slot) {
-        bool act[RPW], hv[RPW];
-        size_t orow[RPW];   // row of q, out and lse
-        int jq[RPW], rl[RPW];
-        bool active = false;
-#pragma unroll
-        for (int k = 0; k < RPW; k++) {
-            const int r0 = 64 * RPW * rb + 16 * (k * NW + wave);
-            const int nh = min(16, n_rows - r0);        // rows of this block
-            act[k] = nh > 0;
-            active |= act[k];
-            hv[k] = li < nh;                            // this lane's row exists
-            const int r = hv[k] ? r0 + li : r0;
-            jq[k] = r / g;
-            rl[k] = r - 64 * RPW * rb;
-            orow[k] = (size_t)(b * p.q_len + jq[k]) * p.h + j * g + r % g;
-        }
-        auto part_row = [&](int k) -> size_t {
-            return omode == 1 ? orow[k] * p.n_split + split : (size_t)slot * p.slot_rows + rl[k];
-        };
-        // query position jq sits at cache position n - q_len + jq and sees
-        // the tokens before it and itself (causal among the new tokens)
-        int tl[RPW];
-#pragma unroll
-        for (int k = 0; k < RPW; k++) tl[k] = min(t1, n - (p.q_len - 1 - jq[k]));
-
-        if (t0 >= t1) {   // nothing to attend to in this piece
-#pragma unroll
-            for (int k = 0; k < RPW; k++) {
-                if (!(act[k] && hv[k])) continue;
-                if (omode != 0) {
-                    if (G == 0) {
-                        float* ml = p.part_ml + part_row(k) * 2;
-                        ml[0] = -INFINITY;
-                        ml[1] = 0.f;
-                    }
-                } else {
-                    uint16_t* o = (uint16_t*)p.out + orow[k] * D;
-#pragma unroll
-                    for (int mc = 0; mc < C::MC; mc++) *(uint2*)(o + 16 * mc + 4 * G) = make_uint2(0, 0);
-                    if (G == 0 && p.lse) p.lse[orow[k]] = -INFINITY;
-                }
-            }
-            return;
-        }
-
-        // DMA instruction q of a tile (q < OPS/2: K, else V) moves tile rows
-        // RPO (q % (OPS/2)) .. + RPO-1; lane l writes row l / NCH, physical chunk
-        // l % NCH, i.e. logical chunk (l % NCH) ^ gswz(row).  A tile's two
-        // 16-token halves each lie in one block of a paged pool (blocks hold a
-        // power of two >= 16 of rows), so a tile needs the physical rows of just
-        // its two half starts; they are looked up one iteration before the tile
-        // is issued, keeping the scalar-load latency off the issue path.  One
-        // buffer resource per (K or V, half) covers the rows of that half inside
-        // the piece (rows past it read as zero); an instruction's lanes reach
-        // their row and chunk through a per-lane offset that is the same for
-        // every tile.
-        const size_t rowstride = (size_t)p.h_kv * C::RB;   // bytes between tokens of one head
-        const uint8_t* __restrict__ kb = (const uint8_t*)p.k + (size_t)j * C::RB;
-        const uint8_t* __restrict__ vb = (const uint8_t*)p.v + (size_t)j * C::RB;
-        const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Ls;
-        uint32_t voff[OPW];
-        {
-            const int lr = lane / C::NCH, lp = lane % C::NCH;
-#pragma unroll
-            for (int jj = 0; jj < OPW; jj++) {
-                const int q = wave + NW * jj;
-                const int rt = (q % (C::OPS / 2)) * C::RPO;   // first tile row of this instruction
-                voff[jj] = (uint32_t)(((rt & 15) + lr) * (int)rowstride + ((lp ^ gswz<D, F8>(rt + lr)) << 4));
-            }
-        }
-        auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
-            if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
-            return (size_t)b * p.s_max + t;
-        };
-        auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
-            const int nv0 = min(max(t1 - tb, 0), 16), nv1 = min(max(t1 - tb - 16, 0), 16);
-            const int nr0 = nv0 > 0 ? (nv0 - 1) * (int)rowstride + C::RB : 0;
-            const int nr1 = nv1 > 0 ? (nv1 - 1) * (int)rowstride + C::RB : 0;
-            const rsrc_t k0 = make_rsrc(kb + row0 * rowstride, nr0), k1 = make_rsrc(kb + row1 * rowstride, nr1);
-            const rsrc_t v0 = make_rsrc(vb + row0 * rowstride, nr0), v1 = make_rsrc(vb + row1 * rowstride, nr1);
-            const uint32_t lb = lds0 + (uint32_t)(buf * 2 * C::KT);
-#pragma unroll
-            for (int jj = 0; jj < OPW; jj++) {
-                const int q = wave + NW * jj;
-                const bool isv = q >= C::OPS / 2;
-                const int rq = isv ? q - C::OPS / 2 : q;
-                const bool h1 = rq * C::RPO >= 16;
-                const rsrc_t rs = isv ? (h1 ? v1 : v0) : (h1 ? k1 : k0);
-                dma16(rs, voff[jj], lb + (isv ? C::KT : 0) + rq * 1024);
-            }
-        };
-
-        f32x4 O[RPW][C::MC];
-        float m[RPW], lsum[RPW];
-#pragma unroll
-        for (int k = 0; k < RPW; k++) {
-#pragma unroll
-            for (int mc = 0; mc < C::MC; mc++) O[k][mc] = f32x4{0.f, 0.f, 0.f, 0.f};
-            m[k] = -INFINITY;
-            lsum[k] = 0.f;
-        }
-
-        // NBUF - 2 tiles in flight, then q (the B operand of the score product;
-        // zero for padding heads), then one more tile
-        // Per-page scales of a paged E4M3 cache (one per page and KV head):
-        // a tile's two 16-token halves lie in one page each, so each half has one
-        // K and one V scale.  They are read (scalar loads) when the tile is
-        // issued and carried in a queue of AH entries to its compute iteration.
-        constexpr int AH = C::NBUF - 1;   // tiles in flight ahead of the one in use
-        constexpr bool ps = F8 && PAGED && PS;
-        const float* __restrict__ ksp = p.k_scales;
-        const float* __restrict__ vsp = p.v_scales;
-        float qk[AH][2], qv[AH][2];
-        auto page_scales = [&](size_t row0, size_t row1, float* ks, float* vs) {
-            const size_t i0 = (row0 >> p.bs_log2) * p.h_kv + j, i1 = (row1 >> p.bs_log2) * p.h_kv + j;
-            ks[0] = ksp[i0];
-            ks[1] = ksp[i1];
-            vs[0] = vsp[i0];
-            vs[1] = vsp[i1];
-        };
-#pragma unroll
-        for (int i = 0; i < AH; i++) qk[i][0] = qk[i][1] = qv[i][0] = qv[i][1] = 1.f;
-#pragma unroll
-        for (int i = 0; i < C::NBUF - 2; i++) {
-            const size_t a0 = half_row(t0 + i * C::T), a1 = half_row(t0 + i * C::T + 16);
-            issue_tile(t0 + i * C::T, i, a0, a1);
-            if (ps) page_scales(a0, a1, qk[i], qv[i]);
-        }
-        bf16x8 Qf[RPW][C::KS];
-#pragma unroll
-        for (int k = 0; k < RPW; k++) {
-            const uint16_t* qrow = (const uint16_t*)p.q + orow[k] * D + 8 * G;
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ks++)
-                Qf[k][ks] = (act[k] && hv[k]) ? *(const bf16x8*)(qrow + 32 * ks)
-                                              : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-        }
-        vmem_drain();
-        {
-            constexpr int L = C::NBUF - 2;
-            const size_t a0 = half_row(t0 + L * C::T), a1 = half_row(t0 + L * C::T + 16);
-            issue_tile(t0 + L * C::T, L, a0, a1);
-            if (ps) page_scales(a0, a1, qk[L], qv[L]);
-        }
-
-        const GTileOffsets<D, F8> to(li, G);
-        int buf = 0;
-        for (int tb = t0; tb < t1; tb += C::T) {
-            const size_t nx0 = half_row(tb + AH * C::T), nx1 = half_row(tb + AH * C::T + 16);
-            wait_vmcnt<(AH - 1) * OPW>();   // tiles tb + T .. tb + (AH-1) T were issued after this one
-            __syncthreads();
-            // refill the buffer read in the previous iteration (every wavefront is
-            // past it), so that AH tiles stay in flight while this one is used
-            issue_tile(tb + AH * C::T, (buf + AH) % C::NBUF, nx0, nx1);
-            // this tile's page scales, then the queue moves on by one tile
-            float tks[2] = {1.f, 1.f}, tvs[2] = {1.f, 1.f};
-            if (ps) {
-                tks[0] = qk[0][0], tks[1] = qk[0][1], tvs[0] = qv[0][0], tvs[1] = qv[0][1];
-#pragma unroll
-                for (int i = 0; i + 1 < AH; i++)
-                    qk[i][0] = qk[i + 1][0], qk[i][1] = qk[i + 1][1], qv[i][0] = qv[i + 1][0], qv[i][1] = qv[i + 1][1];
-                page_scales(nx0, nx1, qk[AH - 1], qv[AH - 1]);
-            }
-            const uint8_t* Kt = Ls + buf * 2 * C::KT;
-            const uint8_t* Vt = Kt + C::KT;
-            if (active) {
-                // every operand of the tile is read from LDS up front: the K
-                // operands of the score product, then the V operands of the value
-                // product (which do not depend on P, so their latency hides
-                // behind the score products and the softmax)
-                bf16x8 ka[C::KS][2];
-#pragma unroll
-                for (int ks = 0; ks < C::KS; ks++) {
-                    if (F8) {
-                        ka[ks][0] = fp8x8_to_bf16(lds_read_8(Kt + to.sc[ks]));
-                        ka[ks][1] = fp8x8_to_bf16(lds_read_8(Kt + to.sc[ks] + 16 * C::RB));
-                    } else {
-                        ka[ks][0] = lds_read_16_as_2x8(Kt + to.sc[ks]);
-                        ka[ks][1] = lds_read_16_as_2x8(Kt + to.sc[ks] + 16 * C::RB);
-                    }
-                }
-                bf16x8 va[C::MC];
-#pragma unroll
-                for (int mc = 0; mc < C::MC; mc++)
-                    va[mc] = F8 ? fp8x8_to_bf16(lds_read_tr8(Vt + to.tr[mc]))
-                                : cat_tr(lds_read_tr(Vt + to.tr[mc]), lds_read_tr(Vt + to.tr[mc] + 16 * C::RB));
-#pragma unroll
-                for (int k = 0; k < RPW; k++) {
-                    if (RPW > 1 && !act[k]) continue;   // wave-uniform
-                    // ---- scores S^T = K . q^T
-                    f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-                    for (int ks = 0; ks < C::KS; ks++) {
-                        S[0] = mfma16(ka[ks][0], Qf[k][ks], S[0]);
-                        S[1] = mfma16(ka[ks][1], Qf[k][ks], S[1]);
-                    }
-                    // ---- online softmax: lane holds row li, tokens 16 mt + 4G + e
-                    float z[2][4];
-                    float lm = -INFINITY;
-#pragma unroll
-                    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                        for (int e = 0; e < 4; e++) {
-                            const int tok = tb + 16 * mt + 4 * G + e;
-                            z[mt][e] = tok < tl[k] ? S[mt][e] * (p.scale_log2 * tks[mt]) : -INFINITY;
-                            lm = fmaxf(lm, z[mt][e]);
-                        }
-                    lm = fmaxf(lm, xor16(lm));
-                    lm = fmaxf(lm, xor32(lm));
-                    const bool move = lm > m[k] + 8.f;
-                    const float mn = move ? lm : m[k];
-                    const float alpha = move ? __builtin_amdgcn_exp2f(m[k] - mn) : 1.f;
-                    m[k] = mn;
-                    // a row that has seen no visible token yet (possible only for
-                    // the earlier of several query positions) keeps m = -inf:
-                    // weights 0
-                    const float mb = mn == -INFINITY ? 0.f : mn;
-                    uint32_t pk[4];
-                    float psum = 0.f;
-#pragma unroll
-                    for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-                        for (int e = 0; e < 4; e += 2) {
-                            const float e0 = __builtin_amdgcn_exp2f(z[mt][e] - mb);
-                            const float e1 = __builtin_amdgcn_exp2f(z[mt][e + 1] - mb);
-                            if (ps) {   // the page's V scale rides on P; the sum takes the weights
-                                pk[mt * 2 + e / 2] = pack_bf16x2(e0 * tvs[mt], e1 * tvs[mt]);
-                                psum += e0 + e1;
-                            } else {
-                                const uint32_t wv = pack_bf16x2(e0, e1);
-                                pk[mt * 2 + e / 2] = wv;
-                                psum += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
-                            }
-                        }
-                    lsum[k] = lsum[k] * alpha + psum;
-                    if (__builtin_amdgcn_ballot_w64(move)) {
-#pragma unroll
-                        for (int mc = 0; mc < C::MC; mc++) O[k][mc] *= alpha;
-                    }
-                    const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-                    // ---- O^T += V^T . P^T
-#pragma unroll
-                    for (int mc = 0; mc < C::MC; mc++) O[k][mc] = mfma16(va[mc], P, O[k][mc]);
-                }
-            }
-            buf = (buf + 1) % C::NBUF;
-        }
-        wait_vmcnt<0>();   // no LDS-DMA may outlive the piece
-        __syncthreads();   // every wavefront is done with the ring before the next piece refills it
-
-        if (!active) return;
-#pragma unroll
-        for (int k = 0; k < RPW; k++) {
-            if (!act[k]) continue;   // wave-uniform
-            float l = lsum[k];
-            l += xor16(l);
-            l += xor32(l);
-            if (!hv[k]) continue;
-            if (F8) {   // the V scale of an FP8 cache (the K scale is folded into scale_log2)
-#pragma unroll
-                for (int mc = 0; mc < C::MC; mc++) O[k][mc] *= p.v_scale;
-            }
-            if (omode == 0) {
-                const float inv = l > 0.f ? 1.f / l : 0.f;   // l = 0: no visible token (0 and -inf)
-                uint16_t* o = (uint16_t*)p.out + orow[k] * D + 4 * G;
-#pragma unroll
-                for (int mc = 0; mc < C::MC; mc++)
-                    *(uint2*)(o + 16 * mc) = make_uint2(pack_bf16x2(O[k][mc][0] * inv, O[k][mc][1] * inv),
-                                                        pack_bf16x2(O[k][mc][2] * inv, O[k][mc][3] * inv));
-                if (G == 0 && p.lse) p.lse[orow[k]] = l > 0.f ? (m[k] + __log2f(l)) * kLn2 : -INFINITY;
-            } else if (omode == 1) {   // read by the merge kernel, launched after this one
-                const size_t pi = part_row(k);
-                float* po = p.part_o + pi * D + 4 * G;
-#pragma unroll
-                for (int mc = 0; mc < C::MC; mc++)
-                    *(float4*)(po + 16 * mc) = make_float4(O[k][mc][0], O[k][mc][1], O[k][mc][2], O[k][mc][3]);
-                if (G == 0) {
-                    p.part_ml[pi * 2] = m[k];
-                    p.part_ml[pi * 2 + 1] = l;
-                }
-            } else {   // read by another workgroup of this launch: coherent device-scope stores
-                const size_t pi = part_row(k);
-                float* po = p.part_o + pi * D + 4 * G;
-#pragma unroll
-                for (int mc = 0; mc < C::MC; mc++)
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; e2++) dev_store(po + 16 * mc + e2, O[k][mc][e2]);
-                if (G == 0) {
-                    dev_store(p.part_ml + pi * 2, m[k]);
-                    dev_store(p.part_ml + pi * 2 + 1, l);
-                }
-            }
-        }
-    };
-
-    if (p.sched) {
-        // ---- tile-run schedule.  The tiles of all sequences are laid end to
-        // end (sequence b holds seg_tiles(s_b) tiles from tile P(b) on) and
-        // cut into n_rng equal runs of tpw tiles; run r goes to per = h_kv *
-        // n_rb adjacent workgroups, one per (KV head, row block), so every
-        // run streams whole token rows of the cache together (DRAM pages are
-        // shared by the heads, as in the chunked grid) while the runs are
-        // balanced whatever the mix of lengths: the tile-scheduler metadata
-        // that "MLA: why one latent can replace a multi-head KV cache"
-        // (charlestar.github.io) puts beside the paged cache in the section on
-        // what FlashMLA solves.  Each workgroup derives its run from the
-        // lengths itself (one load of all B of them and a wavefront scan), so
-        // no extra launch computes it.  A run leaves one partial per sequence
-        // it touches, in slot (r + b) per + (head, block): along the tile
-        // order each step to the next (run, sequence) pair raises r, b or
-        // both, so r + b never repeats for one sequence's head.
-        const int per = p.h_kv * p.n_rb;
-#ifndef GQA_SCHED_XCD
-#define GQA_SCHED_XCD 1
-#endif
-        const int w = (PAGED && GQA_SCHED_XCD) ? xcd_major(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-        const int r = w / per, kseg = w % per;
-        if (r >= p.n_wg) return;   // p.n_wg holds the number of runs
-        const int j0 = kseg / p.n_rb, rb = kseg % p.n_rb;
-        // the KV head, permuted against the XCDs as in the chunked grid (a
-        // bijection on groups of heads); slots and counters keep j0
-        const int j = (!PAGED && p.xpair >= 0) ? pair_head<C::RB>(j0, p.xpair) : j0;
-        const int nch = (p.B + 63) / 64;
-        int tot = 0;
-        for (int c = 0; c < nch; c++) {
-            const int i = 64 * c + lane;
-            tot += i < p.B ? seg_tiles(min(max(s_len[i], 0), p.s_max)) : 0;
-        }
-        tot = __builtin_amdgcn_readfirstlane(wave_sum_int(tot));
-        const int tpw = max((tot + p.n_wg - 1) / p.n_wg, p.min_tiles);
-        const long long g0l = (long long)r * tpw;
-        const int g0 = (int)min(g0l, (long long)tot), g1 = min(g0 + tpw, tot);
-        if (g0 >= g1) return;
-        // the sequence holding tile g0, and its first tile
-        int b = 0, sb = 0;
-        {
-            int carry = 0;
-            for (int c = 0; c < nch; c++) {
-                const int i = 64 * c + lane;
-                const int x = i < p.B ? seg_tiles(min(max(s_len[i], 0), p.s_max)) : 0;
-                const int incl = wave_scan_incl(x);
-                const unsigned long long hit = __builtin_amdgcn_ballot_w64(g0 >= carry + incl - x && g0 < carry + incl);
-                if (hit) {
-                    const int L = __builtin_ctzll(hit);
-                    b = 64 * c + L;
-                    sb = carry + __builtin_amdgcn_readlane(incl - x, L);
-                    break;
-                }
-                carry += __builtin_amdgcn_readlane(incl, 63);
-            }
-        }
-        int n = min(max(__builtin_amdgcn_readfirstlane(s_len[b]), 0), p.s_max);
-        int ntb = seg_tiles(n);
-        int* __restrict__ cnt = p.counters;
-        for (int gg = g0; gg < g1;) {
-            const int e = b * per + kseg;      // segment (b, head, block)
-            const int lo = max(gg, sb), hi = min(g1, sb + ntb);
-            const bool whole = lo == sb && hi == sb + ntb;
-            const int t0 = (lo - sb) * C::T, t1 = min(n, (hi - sb) * C::T);
-            run_piece(b, j, rb, n, t0, t1, whole ? 0 : 2, 0, (r + b) * per + kseg);
-            if (!whole) {
-                // ---- merge of a split segment by the last of its workgroups
-                // to finish.  Each writes its partial with device-coherent
-                // stores, waits until they have completed, and only then
-                // counts itself in (one device-scope atomic after a barrier);
-                // the one that completes the count reads the partials with
-                // device-coherent loads, writes the result and sets the counter
-                // back to zero for the next call.  (A device-scope fence would
-                // write back and invalidate the whole L2 of the XCD instead.)
-                const int r_lo = sb / tpw, r_hi = (sb + ntb - 1) / tpw;
-                const int count = r_hi - r_lo + 1;
-                vmem_drain();
-                __syncthreads();
-                if (tid == 0)
-                    last_flag = __hip_atomic_fetch_add(&cnt[e], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                                count - 1;
-                __syncthreads();
-                if (last_flag) {   // workgroup-uniform
-                    const int rows_e = min(64 * RPW, n_rows - 64 * RPW * rb);
-                    constexpr int PL = D / 64;
-                    constexpr int QB = 8;   // partials in flight
-                    for (int rr = wave; rr < rows_e; rr += NW) {   // wave-uniform
-                        float M = -INFINITY, L = 0.f, o[PL];
-#pragma unroll
-                        for (int c = 0; c < PL; c++) o[c] = 0.f;
-                        for (int q0 = 0; q0 < count; q0 += QB) {
-                            float2 ml[QB];
-                            float po[QB][PL];
-#pragma unroll
-                            for (int u = 0; u < QB; u++) {   // clamped: the loads stay unconditional
-                                const int rq = r_lo + min(q0 + u, count - 1);
-                                const size_t pi = ((size_t)(rq + b) * per + kseg) * p.slot_rows + rr;
-                                ml[u] = make_float2(dev_load(p.part_ml + pi * 2), dev_load(p.part_ml + pi * 2 + 1));
-#pragma unroll
-                                for (int c = 0; c < PL; c++) po[u][c] = dev_load(p.part_o + pi * D + lane * PL + c);
-                            }
-#pragma unroll
-                            for (int u = 0; u < QB; u++) {
-                                const float mk = ml[u].x, lk = ml[u].y;
-                                if (q0 + u >= count || !(lk > 0.f)) continue;   // wave-uniform
-                                const float Mn = fmaxf(M, mk);
-                                const float sa = __builtin_amdgcn_exp2f(M - Mn), sw = __builtin_amdgcn_exp2f(mk - Mn);
-                                L = fmaf(L, sa, lk * sw);
-#pragma unroll
-                                for (int c = 0; c < PL; c++) o[c] = fmaf(o[c], sa, sw * po[u][c]);
-                                M = Mn;
-                            }
-                        }
-                        const float inv = L > 0.f ? 1.f / L : 0.f;
-                        const int rg = 64 * RPW * rb + rr;
-                        const size_t orw = (size_t)(b * p.q_len + rg / g) * p.h + j * g + rg % g;
-                        uint16_t* op = (uint16_t*)p.out + orw * D + lane * PL;
-#pragma unroll
-                        for (int c = 0; c < PL; c++) op[c] = (uint16_t)f32_to_bf16_bits(o[c] * inv);
-                        if (lane == 0 && p.lse) p.lse[orw] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-                    }
-                    if (tid == 0) __hip_atomic_store(&cnt[e], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-            gg = hi;
-            if (gg >= g1) break;
-            sb += ntb;   // the next sequence (there is one: gg < g1 <= the total)
-            ++b;
-            n = min(max(__builtin_amdgcn_readfirstlane(s_len[b]), 0), p.s_max);
-            ntb = seg_tiles(n);
-        }
-        return;
-    }
-
-    // ---- chunked grid: work item (b, split, j) with j fastest.  A paged
-    // pool is walked XCD-major, so that the KV heads of one sequence, which
-    // share every block, run under one L2; a contiguous cache streams faster
-    // in plain order (measured).
+    // work item (b, split, j) with j fastest.  A paged pool is walked
+    // XCD-major, so that the KV heads of one sequence, which share every
+    // block, run under one L2; a contiguous cache streams faster in plain
+    // order (measured).
     // With mixed lengths most (sequence, split) pairs of a grid sized for
     // s_max are empty, and an empty workgroup still holds a slot while it
     // loads its length.  Compacted (the grid then has a multiple of 8
@@ -688,11 +224,299 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         split = w % p.n_split;
         b = w / p.n_split;
     }
+    const int g = p.h / p.h_kv;
+    // The rows of a work item are the (query position jq, head of the group)
+    // pairs, r = jq * g + gi: g rows for one new token, g * q_len when
+    // several new tokens are verified at once.  Row block rb holds rows
+    // 64 RPW rb .. + 64 RPW - 1; wavefront w takes the RPW 16-row blocks
+    // 16 (k NW + w) .. + 15 of them (k < RPW), all fed by the same LDS
+    // operand reads of each tile.
+    const int n_rows = g * p.q_len;
+    bool act[RPW], hv[RPW];
+    size_t orow[RPW];   // row of q, out and lse
+    int jq[RPW];
+    bool active = false;
+#pragma unroll
+    for (int k = 0; k < RPW; k++) {
+        const int r0 = 64 * RPW * rb + 16 * (k * NW + wave);
+        const int nh = min(16, n_rows - r0);        // rows of this block
+        act[k] = nh > 0;
+        active |= act[k];
+        hv[k] = li < nh;                            // this lane's row exists
+        const int r = hv[k] ? r0 + li : r0;
+        jq[k] = r / g;
+        orow[k] = (size_t)(b * p.q_len + jq[k]) * p.h + j * g + r % g;
+    }
+
+    const int32_t* __restrict__ s_len = p.s;
     int n = __builtin_amdgcn_readfirstlane(s_len[b]);
     n = min(max(n, 0), p.s_max);
     const int t0 = split * p.chunk;
     const int t1 = min(n, t0 + p.chunk);
-    run_piece(b, j, rb, n, t0, t1, p.n_split > 1 ? 1 : 0, split, 0);
+    // query position jq sits at cache position n - q_len + jq and sees the
+    // tokens before it and itself (causal among the new tokens)
+    int tl[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; k++) tl[k] = min(t1, n - (p.q_len - 1 - jq[k]));
+
+    if (t0 >= t1) {   // nothing to attend to in this split
+#pragma unroll
+        for (int k = 0; k < RPW; k++) {
+            if (!(act[k] && hv[k])) continue;
+            if (p.n_split > 1) {
+                if (G == 0) {
+                    float* ml = p.part_ml + (orow[k] * p.n_split + split) * 2;
+                    ml[0] = -INFINITY;
+                    ml[1] = 0.f;
+                }
+            } else {
+                uint16_t* o = (uint16_t*)p.out + orow[k] * D;
+#pragma unroll
+                for (int mc = 0; mc < C::MC; mc++) *(uint2*)(o + 16 * mc + 4 * G) = make_uint2(0, 0);
+                if (G == 0 && p.lse) p.lse[orow[k]] = -INFINITY;
+            }
+        }
+        return;
+    }
+
+    // DMA instruction q of a tile (q < OPS/2: K, else V) moves tile rows
+    // RPO (q % (OPS/2)) .. + RPO-1; lane l writes row l / NCH, physical chunk
+    // l % NCH, i.e. logical chunk (l % NCH) ^ gswz(row).  A tile's two
+    // 16-token halves each lie in one block of a paged pool (blocks hold a
+    // power of two >= 16 of rows), so a tile needs the physical rows of just
+    // its two half starts; they are looked up one iteration before the tile
+    // is issued, keeping the scalar-load latency off the issue path.  One
+    // buffer resource per (K or V, half) covers the rows of that half inside
+    // the split (rows past it read as zero); an instruction's lanes reach
+    // their row and chunk through a per-lane offset that is the same for
+    // every tile.
+    const size_t rowstride = (size_t)p.h_kv * C::RB;   // bytes between tokens of one head
+    const uint8_t* __restrict__ kb = (const uint8_t*)p.k + (size_t)j * C::RB;
+    const uint8_t* __restrict__ vb = (const uint8_t*)p.v + (size_t)j * C::RB;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Ls;
+    uint32_t voff[OPW];
+    {
+        const int lr = lane / C::NCH, lp = lane % C::NCH;
+#pragma unroll
+        for (int jj = 0; jj < OPW; jj++) {
+            const int q = wave + NW * jj;
+            const int rt = (q % (C::OPS / 2)) * C::RPO;   // first tile row of this instruction
+            voff[jj] = (uint32_t)(((rt & 15) + lr) * (int)rowstride + ((lp ^ gswz<D, F8>(rt + lr)) << 4));
+        }
+    }
+    auto half_row = [&](int t) -> size_t {   // physical row of token t (a multiple of 16)
+        if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
+        return (size_t)b * p.s_max + t;
+    };
+    auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
+        const int nv0 = min(max(t1 - tb, 0), 16), nv1 = min(max(t1 - tb - 16, 0), 16);
+        const int nr0 = nv0 > 0 ? (nv0 - 1) * (int)rowstride + C::RB : 0;
+        const int nr1 = nv1 > 0 ? (nv1 - 1) * (int)rowstride + C::RB : 0;
+        const rsrc_t k0 = make_rsrc(kb + row0 * rowstride, nr0), k1 = make_rsrc(kb + row1 * rowstride, nr1);
+        const rsrc_t v0 = make_rsrc(vb + row0 * rowstride, nr0), v1 = make_rsrc(vb + row1 * rowstride, nr1);
+        const uint32_t lb = lds0 + (uint32_t)(buf * 2 * C::KT);
+#pragma unroll
+        for (int jj = 0; jj < OPW; jj++) {
+            const int q = wave + NW * jj;
+            const bool isv = q >= C::OPS / 2;
+            const int rb = isv ? q - C::OPS / 2 : q;
+            const bool h1 = rb * C::RPO >= 16;
+            const rsrc_t rs = isv ? (h1 ? v1 : v0) : (h1 ? k1 : k0);
+            dma16(rs, voff[jj], lb + (isv ? C::KT : 0) + rb * 1024);
+        }
+    };
+
+    f32x4 O[RPW][C::MC];
+    float m[RPW], lsum[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; k++) {
+#pragma unroll
+        for (int mc = 0; mc < C::MC; mc++) O[k][mc] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[k] = -INFINITY;
+        lsum[k] = 0.f;
+    }
+
+    // two tiles in flight, then q (the B operand of the score product; zero
+    // for padding heads), then the third tile
+    // NBUF - 2 tiles in flight, then q (the B operand of the score product;
+    // zero for padding heads), then one more tile
+    // Per-page scales of a paged E4M3 cache (one per page and KV head):
+    // a tile's two 16-token halves lie in one page each, so each half has one
+    // K and one V scale.  They are read (scalar loads) when the tile is
+    // issued and carried in a queue of AH entries to its compute iteration.
+    constexpr int AH = C::NBUF - 1;   // tiles in flight ahead of the one in use
+    constexpr bool ps = F8 && PAGED && PS;
+    const float* __restrict__ ksp = p.k_scales;
+    const float* __restrict__ vsp = p.v_scales;
+    float qk[AH][2], qv[AH][2];
+    auto page_scales = [&](size_t row0, size_t row1, float* ks, float* vs) {
+        const size_t i0 = (row0 >> p.bs_log2) * p.h_kv + j, i1 = (row1 >> p.bs_log2) * p.h_kv + j;
+        ks[0] = ksp[i0];
+        ks[1] = ksp[i1];
+        vs[0] = vsp[i0];
+        vs[1] = vsp[i1];
+    };
+#pragma unroll
+    for (int i = 0; i < AH; i++) qk[i][0] = qk[i][1] = qv[i][0] = qv[i][1] = 1.f;
+#pragma unroll
+    for (int i = 0; i < C::NBUF - 2; i++) {
+        const size_t a0 = half_row(t0 + i * C::T), a1 = half_row(t0 + i * C::T + 16);
+        issue_tile(t0 + i * C::T, i, a0, a1);
+        if (ps) page_scales(a0, a1, qk[i], qv[i]);
+    }
+    bf16x8 Qf[RPW][C::KS];
+#pragma unroll
+    for (int k = 0; k < RPW; k++) {
+        const uint16_t* qrow = (const uint16_t*)p.q + orow[k] * D + 8 * G;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ks++)
+            Qf[k][ks] = (act[k] && hv[k]) ? *(const bf16x8*)(qrow + 32 * ks)
+                                          : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+    vmem_drain();
+    {
+        constexpr int L = C::NBUF - 2;
+        const size_t a0 = half_row(t0 + L * C::T), a1 = half_row(t0 + L * C::T + 16);
+        issue_tile(t0 + L * C::T, L, a0, a1);
+        if (ps) page_scales(a0, a1, qk[L], qv[L]);
+    }
+
+    const GTileOffsets<D, F8> to(li, G);
+    int buf = 0;
+    for (int tb = t0; tb < t1; tb += C::T) {
+        const size_t nx0 = half_row(tb + AH * C::T), nx1 = half_row(tb + AH * C::T + 16);
+        wait_vmcnt<(AH - 1) * OPW>();   // tiles tb + T .. tb + (AH-1) T were issued after this one
+        __syncthreads();
+        // refill the buffer read in the previous iteration (every wavefront is
+        // past it), so that AH tiles stay in flight while this one is used
+        issue_tile(tb + AH * C::T, (buf + AH) % C::NBUF, nx0, nx1);
+        // this tile's page scales, then the queue moves on by one tile
+        float tks[2] = {1.f, 1.f}, tvs[2] = {1.f, 1.f};
+        if (ps) {
+            tks[0] = qk[0][0], tks[1] = qk[0][1], tvs[0] = qv[0][0], tvs[1] = qv[0][1];
+#pragma unroll
+            for (int i = 0; i + 1 < AH; i++)
+                qk[i][0] = qk[i + 1][0], qk[i][1] = qk[i + 1][1], qv[i][0] = qv[i + 1][0], qv[i][1] = qv[i + 1][1];
+            page_scales(nx0, nx1, qk[AH - 1], qv[AH - 1]);
+        }
+        const uint8_t* Kt = Ls + buf * 2 * C::KT;
+        const uint8_t* Vt = Kt + C::KT;
+        if (active) {
+            // every operand of the tile is read from LDS up front: the K
+            // operands of the score product, then the V operands of the value
+            // product (which do not depend on P, so their latency hides
+            // behind the score products and the softmax)
+            bf16x8 ka[C::KS][2];
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ks++) {
+                if (F8) {
+                    ka[ks][0] = fp8x8_to_bf16(lds_read_8(Kt + to.sc[ks]));
+                    ka[ks][1] = fp8x8_to_bf16(lds_read_8(Kt + to.sc[ks] + 16 * C::RB));
+                } else {
+                    ka[ks][0] = lds_read_16_as_2x8(Kt + to.sc[ks]);
+                    ka[ks][1] = lds_read_16_as_2x8(Kt + to.sc[ks] + 16 * C::RB);
+                }
+            }
+            bf16x8 va[C::MC];
+#pragma unroll
+            for (int mc = 0; mc < C::MC; mc++)
+                va[mc] = F8 ? fp8x8_to_bf16(lds_read_tr8(Vt + to.tr[mc]))
+                            : cat_tr(lds_read_tr(Vt + to.tr[mc]), lds_read_tr(Vt + to.tr[mc] + 16 * C::RB));
+#pragma unroll
+            for (int k = 0; k < RPW; k++) {
+                if (RPW > 1 && !act[k]) continue;   // wave-uniform
+                // ---- scores S^T = K . q^T
+                f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ks++) {
+                    S[0] = mfma16(ka[ks][0], Qf[k][ks], S[0]);
+                    S[1] = mfma16(ka[ks][1], Qf[k][ks], S[1]);
+                }
+                // ---- online softmax: lane holds row li, tokens 16 mt + 4G + e
+                float z[2][4];
+                float lm = -INFINITY;
+#pragma unroll
+                for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int tok = tb + 16 * mt + 4 * G + e;
+                        z[mt][e] = tok < tl[k] ? S[mt][e] * (p.scale_log2 * tks[mt]) : -INFINITY;
+                        lm = fmaxf(lm, z[mt][e]);
+                    }
+                lm = fmaxf(lm, xor16(lm));
+                lm = fmaxf(lm, xor32(lm));
+                const bool move = lm > m[k] + 8.f;
+                const float mn = move ? lm : m[k];
+                const float alpha = move ? __builtin_amdgcn_exp2f(m[k] - mn) : 1.f;
+                m[k] = mn;
+                // a row that has seen no visible token yet (possible only for
+                // the earlier of several query positions) keeps m = -inf:
+                // weights 0
+                const float mb = mn == -INFINITY ? 0.f : mn;
+                uint32_t pk[4];
+                float psum = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                    for (int e = 0; e < 4; e += 2) {
+                        const float e0 = __builtin_amdgcn_exp2f(z[mt][e] - mb);
+                        const float e1 = __builtin_amdgcn_exp2f(z[mt][e + 1] - mb);
+                        if (ps) {   // the page's V scale rides on P; the sum takes the weights
+                            pk[mt * 2 + e / 2] = pack_bf16x2(e0 * tvs[mt], e1 * tvs[mt]);
+                            psum += e0 + e1;
+                        } else {
+                            const uint32_t wv = pack_bf16x2(e0, e1);
+                            pk[mt * 2 + e / 2] = wv;
+                            psum += bf16lo_to_f32(wv) + bf16hi_to_f32(wv);
+                        }
+                    }
+                lsum[k] = lsum[k] * alpha + psum;
+                if (__builtin_amdgcn_ballot_w64(move)) {
+#pragma unroll
+                    for (int mc = 0; mc < C::MC; mc++) O[k][mc] *= alpha;
+                }
+                const bf16x8 P = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+                // ---- O^T += V^T . P^T
+#pragma unroll
+                for (int mc = 0; mc < C::MC; mc++) O[k][mc] = mfma16(va[mc], P, O[k][mc]);
+            }
+        }
+        buf = (buf + 1) % C::NBUF;
+    }
+    wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
+
+    if (!active) return;
+#pragma unroll
+    for (int k = 0; k < RPW; k++) {
+        if (!act[k]) continue;   // wave-uniform
+        float l = lsum[k];
+        l += xor16(l);
+        l += xor32(l);
+        if (!hv[k]) continue;
+        if (F8) {   // the V scale of an FP8 cache (the K scale is folded into scale_log2)
+#pragma unroll
+            for (int mc = 0; mc < C::MC; mc++) O[k][mc] *= p.v_scale;
+        }
+        if (p.n_split == 1) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;   // l = 0: no visible token (0 and -inf)
+            uint16_t* o = (uint16_t*)p.out + orow[k] * D + 4 * G;
+#pragma unroll
+            for (int mc = 0; mc < C::MC; mc++)
+                *(uint2*)(o + 16 * mc) = make_uint2(pack_bf16x2(O[k][mc][0] * inv, O[k][mc][1] * inv),
+                                                    pack_bf16x2(O[k][mc][2] * inv, O[k][mc][3] * inv));
+            if (G == 0 && p.lse) p.lse[orow[k]] = l > 0.f ? (m[k] + __log2f(l)) * kLn2 : -INFINITY;
+        } else {
+            const size_t pi = orow[k] * p.n_split + split;
+            float* po = p.part_o + pi * D + 4 * G;
+#pragma unroll
+            for (int mc = 0; mc < C::MC; mc++)
+                *(float4*)(po + 16 * mc) = make_float4(O[k][mc][0], O[k][mc][1], O[k][mc][2], O[k][mc][3]);
+            if (G == 0) {
+                p.part_ml[pi * 2] = m[k];
+                p.part_ml[pi * 2 + 1] = l;
+            }
+        }
+    }
 }
 
 template <int D, int NW, bool F8, int RPW>

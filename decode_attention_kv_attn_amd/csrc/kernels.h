@@ -29,14 +29,6 @@ struct GqaParams {
     float v_scale;       // V scale of an FP8 cache (1 otherwise)
     const float* k_scales;   // paged FP8 cache with one scale per page and KV head: [num_blocks, h_kv]
     const float* v_scales;   // (nullptr: the per-tensor scales above)
-    // matrix-core kernel, tile-run schedule (sched = 1): n_wg equal runs of
-    // at least min_tiles tiles over the concatenated sequences, each run taken
-    // by h_kv * n_rb workgroups (one per KV head and row block); a split
-    // (sequence, head, block) segment's partials sit in slots (run + b) *
-    // h_kv * n_rb + (head, block) of slot_rows rows each and are merged by
-    // the last of its workgroups, counted in counters[e] (zero between calls)
-    int sched, n_wg, min_tiles, slot_rows;
-    int32_t* counters;
 };
 
 // vector kernel (any g; fp32 or bf16), then the split merge when n_split > 1

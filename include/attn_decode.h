@@ -100,14 +100,6 @@ size_t attn_mla_cell_bytes(int L, int d_c, int d_R, int b);
  * is_mla = 1: MLA, h_kv ignored, d_h_or_dc = d_c.
  * The value depends only on the arguments; a buffer of this size (16-byte
  * aligned) may be reused across calls on one stream.
- *
- * GQA workspaces (attn_decode_gqa, _fp8, _fp8_paged_scales, _multi,
- * _multi_fp8): when the work is spread over tile runs (many (sequence, KV
- * head) pairs), the first 256 KiB of the workspace hold one counter per
- * pair; a workspace must be zero-filled once after allocation (for example
- * with hipMemset), and every call leaves the counters at zero again, so a
- * zeroed workspace stays valid for calls of any shape.  A workspace that
- * was not zeroed gives unspecified results (no access leaves the buffers).
  */
 size_t attn_decode_workspace_bytes(int is_mla, int B, int s_max, int h, int h_kv,
                                    int d_h_or_dc, int d_R);
@@ -172,10 +164,8 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
  * library runs on, held until the process ends).  Its address on a device is
  * looked up on the first call made with that device current.
  * Arguments, results, supported shapes and errors as attn_decode_gqa, and
- * the same kernels run (always with the chunked split grid and its merge
- * launch, so the scratch holds nothing that must start at zero; results can
- * differ from attn_decode_gqa's in rounding where that call would spread
- * the work over tile runs instead); plus ENOTSUP when the sizes need more scratch than 64 MiB (the message
+ * the outputs are bit-identical to attn_decode_gqa's for the same inputs;
+ * plus ENOTSUP when the sizes need more scratch than 64 MiB (the message
  * gives the amount; attn_decode_workspace_bytes() reports it too) and EHIP if
  * the scratch lookup fails.
  * Every call on one GPU shares that GPU's scratch: calls that overlap in time

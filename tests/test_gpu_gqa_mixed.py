@@ -1,13 +1,10 @@
-"""GPU parity of the tile-run schedule of the GQA/MQA/MHA matrix-core kernel.
+"""GPU parity of GQA/MQA/MHA decode over batches of mixed lengths.
 
-With at least 64 (sequence, KV head, row block) segments the library spreads
-equal runs of 32-token tiles over 512 workgroups whatever the mix of lengths,
-and a segment split between workgroups is merged by the last of them to
-finish (a counter per segment in the workspace, set back to zero by that
-workgroup).  These cases exercise that path against the oracle: mixed and
-empty lengths, one segment split over more than 256 workgroups, paged pools,
-E4M3 caches (per-tensor and per-page scales), several new tokens per sequence
-(two row blocks per KV head), and repeated calls on one workspace.
+Batches with many (sequence, KV head) pairs, mixed and empty lengths, one
+long context among many empty or one-token ones, paged pools, E4M3 caches
+(per-tensor and per-page scales), several new tokens per sequence (two row
+blocks per KV head), and calls of different shapes sharing one workspace,
+all against the oracle.
 """
 import numpy as np
 import pytest
@@ -43,7 +40,7 @@ def test_mixed_lengths_fused_merge(paged, h, h_kv, d_h):
     B = 64 if h_kv == 1 else 40
     s = lengths(B, seed=h + h_kv + d_h, hi=4000, zeros=(0, 7))
     s = s[:3] + (1, 31, 33) + s[6:]
-    print(f"[sched] B={B} h={h} h_kv={h_kv} d_h={d_h} paged={paged}", flush=True)
+    print(f"[gqa-mixed] B={B} h={h} h_kv={h_kv} d_h={d_h} paged={paged}", flush=True)
     sh = synth.GqaShape("t", B=B, h=h, h_kv=h_kv, d_h=d_h, b=2, s=s, paged=paged, seed=900 + h)
     d = synth.draw_gqa(sh, device=DEV)
     out, lse = A.decode_gqa(d["q"], d["K"], d["V"], d["s"], block_table=d.get("block_table"),
@@ -52,12 +49,11 @@ def test_mixed_lengths_fused_merge(paged, h, h_kv, d_h):
     check_gqa(sh, d, out, lse, "out")
 
 
-def test_one_segment_split_over_more_than_256_workgroups_with_empties():
+def test_one_long_context_among_empty_and_single_token_ones():
     # 63 empty or one-token sequences and one of 140,000 tokens over one KV
-    # head: the long segment's 4,375 tiles are cut into runs of 16, so about
-    # 274 workgroups share it and the last one merges all their partials
+    # head: the long context is split many ways, the others not at all
     s = tuple([0, 1] * 31 + [0]) + (140000,)
-    print("[sched] one long segment, 63 short ones", flush=True)
+    print("[gqa-mixed] one long segment, 63 short ones", flush=True)
     sh = synth.GqaShape("t", B=64, h=8, h_kv=1, d_h=128, b=2, s=s, seed=911)
     d = synth.draw_gqa(sh, device=DEV)
     out, lse = A.decode_gqa(d["q"], d["K"], d["V"], d["s"])
@@ -68,15 +64,15 @@ def test_one_segment_split_over_more_than_256_workgroups_with_empties():
 
 
 def test_repeated_calls_share_one_workspace():
-    # the counters return to zero after every call: the same workspace gives
-    # the same bits on a repeat, and serves calls of other shapes in between
+    # the same workspace gives the same bits on a repeat, and serves calls of
+    # other shapes in between
     ws = A.Workspace(DEV)
     sh1 = synth.GqaShape("t", B=48, h=32, h_kv=4, d_h=128, b=2, s=lengths(48, 3, hi=5000), seed=921)
     sh2 = synth.GqaShape("t", B=70, h=8, h_kv=1, d_h=64, b=2, s=lengths(70, 4, hi=2500), paged=True,
                          seed=922)
     d1 = synth.draw_gqa(sh1, device=DEV)
     d2 = synth.draw_gqa(sh2, device=DEV)
-    print("[sched] repeated calls on one workspace", flush=True)
+    print("[gqa-mixed] repeated calls on one workspace", flush=True)
     o1, l1 = A.decode_gqa(d1["q"], d1["K"], d1["V"], d1["s"], workspace=ws)
     o2, l2 = A.decode_gqa(d2["q"], d2["K"], d2["V"], d2["s"], block_table=d2["block_table"],
                           s_max=sh2.s_max, workspace=ws)
@@ -85,8 +81,6 @@ def test_repeated_calls_share_one_workspace():
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16)) and torch.equal(l1, l3)
     check_gqa(sh1, d1, o1, l1, "first shape")
     check_gqa(sh2, d2, o2, l2, "second shape")
-    # every counter (the first 256 KiB of the workspace) is zero again
-    assert int(ws.buf[:256 * 1024].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("paged", [False, True])
@@ -94,7 +88,7 @@ def test_fp8_per_tensor_scales(paged):
     ks, vs = 1.0 / 64, 0.0123
     s = lengths(64, 5, hi=3000, zeros=(3,))
     sh = synth.GqaShape("t", B=64, h=16, h_kv=2, d_h=128, b=2, s=s, paged=paged, seed=931)
-    print(f"[sched] fp8 paged={paged}", flush=True)
+    print(f"[gqa-mixed] fp8 paged={paged}", flush=True)
     d = synth.draw_gqa_fp8(sh, ks, vs, device=DEV)
     out, lse = A.decode_gqa_fp8(d["q"], d["K8"], d["V8"], ks, vs, d["s"],
                                 block_table=d.get("block_table"), s_max=sh.s_max)
@@ -111,7 +105,7 @@ def test_fp8_per_page_scales():
     B, h, h_kv, d_h = 40, 16, 2, 128
     s = lengths(B, 6, hi=4000, zeros=(1,))
     sh = synth.GqaShape("t", B=B, h=h, h_kv=h_kv, d_h=d_h, b=2, s=s, paged=True, seed=941)
-    print("[sched] fp8 per-page scales", flush=True)
+    print("[gqa-mixed] fp8 per-page scales", flush=True)
     d, K8, V8, ksc, vsc = page_scaled_pool(sh, seed=941)
     bt = d["block_table"]
     out = torch.empty_like(d["q"])
@@ -137,7 +131,7 @@ def test_several_new_tokens_two_row_blocks(paged):
     s = lengths(B, 7, lo=3, hi=3000)
     s = (5, 8) + s[2:]
     sh = synth.GqaShape("t", B=B, h=h, h_kv=h_kv, d_h=d_h, b=2, s=s, paged=paged, seed=951)
-    print(f"[sched] q_len={q_len} paged={paged}", flush=True)
+    print(f"[gqa-mixed] q_len={q_len} paged={paged}", flush=True)
     d = synth.draw_gqa(sh, device=DEV)
     g = torch.Generator(device=DEV).manual_seed(952)
     q = torch.randn((B, q_len, h, d_h), generator=g, device=DEV).to(torch.bfloat16)

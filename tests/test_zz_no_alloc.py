@@ -1,8 +1,6 @@
 """attn_decode_gqa_noalloc (the entry point that allocates nothing) against
-attn_decode_gqa with a caller workspace, on two calls in a row, the second
-with a smaller input, and against the oracle.  Where both take the chunked
-split grid the outputs are bit-identical; where the workspace entry point
-spreads the work over tile runs they agree to the parity tolerance."""
+attn_decode_gqa with a caller workspace: bit-identical outputs, on two calls
+in a row, the second with a smaller input, and against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -23,7 +21,7 @@ def _both(sh, d):
     nblk = 0 if bt is None else d["K"].shape[0]
     s_max = sh.s_max if bt is None else mb * sh.block_size
     ws_bytes = A.attn_decode_workspace_bytes(0, sh.B, s_max, sh.h, sh.h_kv, sh.d_h)
-    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
     o1 = torch.full_like(d["q"], float("nan"))
     l1 = torch.full((sh.B, sh.h), float("nan"), dtype=torch.float32, device=DEV)
     A.attn_decode_gqa(o1, l1, d["q"], d["K"], d["V"], d["s"], bt, mb, sh.block_size, nblk, sh.B,
@@ -76,15 +74,12 @@ def test_noalloc_paged_then_unsplit():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
     _check_against_oracle(pg, d, o2, l2)
-    # 512 (sequence, KV head) pairs: the workspace entry point spreads them
-    # over tile runs, the no-alloc one keeps the chunked grid (no split, no
-    # scratch use at all); the two agree to the parity tolerance
+    # a batch that needs no split (no scratch use at all)
     un = synth.GqaShape("t", B=64, h=8, h_kv=8, d_h=64, b=2, s=(130,) * 64, seed=84)
     d2 = synth.draw_gqa(un, device=DEV)
     wsb, (o3, l3), (o4, l4) = _both(un, d2)
-    assert_close(to_f64(o4), to_f64(o3), 2, "noalloc vs workspace entry")
-    assert_lse_close(to_f64(l4), to_f64(l3), 2, "noalloc vs workspace entry")
-    _check_against_oracle(un, d2, o4, l4)
+    assert torch.equal(o3.view(torch.int16), o4.view(torch.int16))
+    assert torch.equal(l3.view(torch.int32), l4.view(torch.int32))
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch():

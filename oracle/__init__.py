@@ -86,6 +86,12 @@ def _load():
         lib.ref_mla_absorbed_fp8.restype = I
         lib.ref_mla_absorbed_fp8.argtypes = [P, P, P, P, P, P, P, P, D, D, P, P, I, I, I, I, I,
                                              I, I, I, I, D]
+        lib.ref_mla_absorbed_multi.restype = I
+        lib.ref_mla_absorbed_multi.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                               I, I, I, I, I, D]
+        lib.ref_mla_absorbed_multi_fp8.restype = I
+        lib.ref_mla_absorbed_multi_fp8.argtypes = [P, P, P, P, P, P, P, P, D, D, P, P, I, I, I,
+                                                   I, I, I, I, I, I, I, D]
         lib.ref_kv_append_mla_fp8.restype = I
         lib.ref_kv_append_mla_fp8.argtypes = [P, P, C.c_float, C.c_float, P, P, I, I, I, I, I, I]
         lib.ref_gqa_decode_fp8_paged_scales.restype = I
@@ -203,6 +209,35 @@ def mla_absorbed(q_nope, q_rope, w_uk, w_uv, cache, s, b=2, block_table=None, bl
                                   float(scale))
     if rc != 0:
         raise ValueError(f"ref_mla_absorbed rejected its arguments ({rc})")
+    return out, ul, lse
+
+
+def mla_absorbed_multi(q_nope, q_rope, w_uk, w_uv, cache, s, b=2, block_table=None,
+                       block_size=16, scale=None):
+    """Reference MLA decode of q_len new tokens per sequence, absorbed form.
+
+    q_nope [B, q_len, h, d_nope], q_rope [B, q_len, h, d_R]; the cache already
+    holds the q_len new tokens (s counts them) and position j sees the first
+    s_b - q_len + 1 + j tokens.  Returns (out [B, q_len, h, d_v],
+    u_latent [B, q_len, h, d_c], lse [B, q_len, h]).
+    """
+    if q_nope.ndim != 4 or q_rope.ndim != 4:
+        raise ValueError("q_nope and q_rope must be [B, q_len, h, d]")
+    B, q_len, h = q_nope.shape[:3]
+    (q_nope, q_rope, w_uk, w_uv, cache, s, bt, _, _, d_nope, d_R, d_c, d_v, s_max, max_blocks,
+     bs) = _mla_args(q_nope.reshape(B, q_len * h, -1), q_rope.reshape(B, q_len * h, -1), w_uk,
+                     w_uv, cache, s, b, block_table, block_size)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_nope + d_R)
+    out = np.zeros((B, q_len, h, d_v))
+    ul = np.zeros((B, q_len, h, d_c))
+    lse = np.zeros((B, q_len, h))
+    rc = _load().ref_mla_absorbed_multi(_ptr(out), _ptr(ul), _ptr(lse), _ptr(q_nope),
+                                        _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache),
+                                        _ptr(s), _ptr(bt), max_blocks, bs, B, q_len, s_max, h,
+                                        d_c, d_R, d_nope, d_v, b, float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_mla_absorbed_multi rejected its arguments ({rc})")
     return out, ul, lse
 
 
@@ -423,6 +458,40 @@ def mla_absorbed_fp8(q_nope, q_rope, w_uk, w_uv, cache8, c_scale, r_scale, s, bl
                                       d_nope, d_v, float(scale))
     if rc != 0:
         raise ValueError(f"ref_mla_absorbed_fp8 rejected its arguments ({rc})")
+    return out, ul, lse
+
+
+def mla_absorbed_multi_fp8(q_nope, q_rope, w_uk, w_uv, cache8, c_scale, r_scale, s,
+                           block_table=None, block_size=16, scale=None):
+    """mla_absorbed_multi over an FP8 latent cache (scales as mla_absorbed_fp8)."""
+    if q_nope.ndim != 4 or q_rope.ndim != 4:
+        raise ValueError("q_nope and q_rope must be [B, q_len, h, d]")
+    q_nope, q_rope, w_uk, w_uv = (_stored(x, 2) for x in (q_nope, q_rope, w_uk, w_uv))
+    cache8 = np.ascontiguousarray(cache8, dtype=np.uint8)
+    B, q_len, h, d_nope = q_nope.shape
+    d_R = q_rope.shape[3]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    s = _i32(s)
+    bt = _i32(block_table)
+    if bt is None:
+        s_max, max_blocks, bs = cache8.shape[1], 0, 0
+    else:
+        s_max, max_blocks, bs = 0, bt.shape[1], block_size
+        _check_table(bt, cache8.shape[0] * cache8.shape[1], bs, s)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_nope + d_R)
+    out = np.zeros((B, q_len, h, d_v))
+    ul = np.zeros((B, q_len, h, d_c))
+    lse = np.zeros((B, q_len, h))
+    rc = _load().ref_mla_absorbed_multi_fp8(_ptr(out), _ptr(ul), _ptr(lse), _ptr(q_nope),
+                                            _ptr(q_rope), _ptr(w_uk), _ptr(w_uv), _ptr(cache8),
+                                            float(np.float32(c_scale)),
+                                            float(np.float32(r_scale)), _ptr(s), _ptr(bt),
+                                            max_blocks, bs, B, q_len, s_max, h, d_c, d_R,
+                                            d_nope, d_v, float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_mla_absorbed_multi_fp8 rejected its arguments ({rc})")
     return out, ul, lse
 
 

@@ -200,31 +200,43 @@ static double ld_latent(const void* cache, size_t roff, int e, int cb, int d_c, 
     return ld(cache, roff + e, cb);
 }
 
+/*
+ * Rows r = (bb, jq, i) of q_len query positions per sequence (q_len = 1:
+ * plain single-token decode).  All q_len new tokens are already in the
+ * cache, so s_b counts them; position jq sits at cache position
+ * s_b - q_len + jq and attends to the tokens up to and including itself
+ * (causal among the new tokens, as when a speculative step verifies them).
+ */
 static int mla_absorbed_impl(double* out, double* u_latent, double* lse, const void* q_nope,
                              const void* q_rope, const void* w_uk, const void* w_uv,
                              const void* cache, int cb, double c_scale, double r_scale,
                              const int32_t* s, const int32_t* block_table, int max_blocks,
-                             int block_size, int B, int s_max, int h, int d_c, int d_R,
-                             int d_nope, int d_v, int b, double scale)
+                             int block_size, int B, int q_len, int s_max, int h, int d_c,
+                             int d_R, int d_nope, int d_v, int b, double scale)
 {
     if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s) return OR_EINVAL;
-    if (B < 0 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0) return OR_EINVAL;
+    if (B < 0 || q_len < 1 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0)
+        return OR_EINVAL;
     if (b != 2 && b != 4) return OR_EINVAL;
     if (block_table && (block_size <= 0 || max_blocks <= 0)) return OR_EINVAL;
     const int W = d_c + d_R;
-    const long rows = (long)B * h;
+    const long rows = (long)B * q_len * h;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (long r = 0; r < rows; r++) {
-        const int bb = (int)(r / h), i = (int)(r % h);
-        const int n = s[bb];
+        const int bb = (int)(r / ((long)q_len * h));
+        const int jq = (int)((r / h) % q_len), i = (int)(r % h);
+        const int sb = s[bb];
         double* o = out + (size_t)r * d_v;
-        if (n < 0 || (!block_table && n > s_max) ||
-            (block_table && n > max_blocks * block_size) ||
-            !table_ok(block_table, max_blocks, block_size, bb, n)) {
+        if (sb < 0 || (!block_table && sb > s_max) ||
+            (block_table && sb > max_blocks * block_size) ||
+            !table_ok(block_table, max_blocks, block_size, bb, sb)) {
             bad = 1;
             continue;
         }
+        /* tokens this position sees (none for an early position of a sequence
+           shorter than q_len) */
+        const int n = sb - q_len + 1 + jq > 0 ? sb - q_len + 1 + jq : 0;
         double* qt = (double*)malloc(sizeof(double) * ((size_t)d_c * 2 + (size_t)n * 2));
         double* ut = qt + d_c;
         double* z = ut + d_c;
@@ -289,8 +301,47 @@ int ref_mla_absorbed(double* out, double* u_latent, double* lse, const void* q_n
                      int d_R, int d_nope, int d_v, int b, double scale)
 {
     return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, b, 1.0, 1.0,
-                             s, block_table, max_blocks, block_size, B, s_max, h, d_c, d_R,
+                             s, block_table, max_blocks, block_size, B, 1, s_max, h, d_c, d_R,
                              d_nope, d_v, b, scale);
+}
+
+/*
+ * MLA absorbed decode of q_len new tokens per sequence: the tokens one
+ * speculative step verifies.  "MLA: why one latent can replace a multi-head
+ * KV cache" (charlestar.github.io) lists that token count and the query
+ * length among the inputs of MLA kernel selection (section on why prefill
+ * need not absorb as decode does, by gloss), and the "Kernel" step of its
+ * validation chain compares outputs and log-sum-exp over query/KV lengths
+ * and speculative tokens.  The causal rule among the new tokens is the
+ * plainest reading: each sees the cache up to its own position.
+ *   out [B, q_len, h, d_v], u_latent [B, q_len, h, d_c] (nullable),
+ *   lse [B, q_len, h] (nullable); q_nope [B, q_len, h, d_nope],
+ *   q_rope [B, q_len, h, d_R]; weights, cache and lengths as
+ *   ref_mla_absorbed.  Position jq sees the first s_b - q_len + 1 + jq
+ *   tokens; one that sees none gives 0 and lse = -inf.
+ */
+int ref_mla_absorbed_multi(double* out, double* u_latent, double* lse, const void* q_nope,
+                           const void* q_rope, const void* w_uk, const void* w_uv,
+                           const void* cache, const int32_t* s, const int32_t* block_table,
+                           int max_blocks, int block_size, int B, int q_len, int s_max, int h,
+                           int d_c, int d_R, int d_nope, int d_v, int b, double scale)
+{
+    return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, b, 1.0, 1.0,
+                             s, block_table, max_blocks, block_size, B, q_len, s_max, h, d_c,
+                             d_R, d_nope, d_v, b, scale);
+}
+
+/* ref_mla_absorbed_multi over an FP8 latent cache (as ref_mla_absorbed_fp8) */
+int ref_mla_absorbed_multi_fp8(double* out, double* u_latent, double* lse, const void* q_nope,
+                               const void* q_rope, const void* w_uk, const void* w_uv,
+                               const uint8_t* cache, double c_scale, double r_scale,
+                               const int32_t* s, const int32_t* block_table, int max_blocks,
+                               int block_size, int B, int q_len, int s_max, int h, int d_c,
+                               int d_R, int d_nope, int d_v, double scale)
+{
+    return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1, c_scale,
+                             r_scale, s, block_table, max_blocks, block_size, B, q_len, s_max, h,
+                             d_c, d_R, d_nope, d_v, 2, scale);
 }
 
 /*
@@ -308,7 +359,7 @@ int ref_mla_absorbed_fp8(double* out, double* u_latent, double* lse, const void*
                          int s_max, int h, int d_c, int d_R, int d_nope, int d_v, double scale)
 {
     return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1, c_scale,
-                             r_scale, s, block_table, max_blocks, block_size, B, s_max, h, d_c,
+                             r_scale, s, block_table, max_blocks, block_size, B, 1, s_max, h, d_c,
                              d_R, d_nope, d_v, 2, scale);
 }
 

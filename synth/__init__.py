@@ -81,6 +81,7 @@ class MlaShape:
     paged: bool = False
     block_size: int = BLOCK_SIZE
     seed: int = 0
+    q_len: int = 1    # new tokens per sequence; queries are [B, q_len, h, .] when > 1
 
     @property
     def s_max(self) -> int:
@@ -239,8 +240,17 @@ def draw_gqa_fp8(shape: GqaShape, k_scale: float, v_scale: float, device="cpu", 
     return d
 
 
+def _mla_q_shape(shape: MlaShape, d: int) -> tuple:
+    # [B, h, d] for one new token, [B, q_len, h, d] for several (the same
+    # draws in the same order when q_len = 1)
+    if shape.q_len == 1:
+        return (shape.B, shape.h, d)
+    return (shape.B, shape.q_len, shape.h, d)
+
+
 def draw_mla(shape: MlaShape, device="cpu", seed=None):
-    """Draw q_nope [B,h,d_nope], q_rope [B,h,d_R], latent cache, W_UK, W_UV.
+    """Draw q_nope [B,h,d_nope], q_rope [B,h,d_R] (with a q_len axis after B
+    when q_len > 1), latent cache, W_UK, W_UV.
 
     W_UK is [h, d_nope, d_c] and W_UV is [h, d_v, d_c] (per-head slices of
     the up-projections, viewed (heads, head_dim, d_c)).  Cache rows are
@@ -250,8 +260,8 @@ def draw_mla(shape: MlaShape, device="cpu", seed=None):
     seed = shape.seed if seed is None else seed
     dt = torch_dtype(shape.b)
     g = _gen(device, seed)
-    q_nope = _randn((shape.B, shape.h, shape.d_nope), g, device, dt)
-    q_rope = _randn((shape.B, shape.h, shape.d_R), g, device, dt)
+    q_nope = _randn(_mla_q_shape(shape, shape.d_nope), g, device, dt)
+    q_rope = _randn(_mla_q_shape(shape, shape.d_R), g, device, dt)
     if shape.paged:
         tab, n_blk = block_table(shape.s, shape.block_size, seed)
         rows = (n_blk, shape.block_size)
@@ -278,8 +288,8 @@ def draw_mla_fp8(shape: MlaShape, c_scale: float, r_scale: float, device="cpu", 
     rotary part by r_scale before the conversion."""
     seed = shape.seed if seed is None else seed
     g = _gen(device, seed)
-    q_nope = _randn((shape.B, shape.h, shape.d_nope), g, device, torch.bfloat16)
-    q_rope = _randn((shape.B, shape.h, shape.d_R), g, device, torch.bfloat16)
+    q_nope = _randn(_mla_q_shape(shape, shape.d_nope), g, device, torch.bfloat16)
+    q_rope = _randn(_mla_q_shape(shape, shape.d_R), g, device, torch.bfloat16)
     if shape.paged:
         tab, n_blk = block_table(shape.s, shape.block_size, seed)
         rows = (n_blk, shape.block_size)

@@ -33,9 +33,9 @@ def gqa_host(B, h, h_kv, d_h, s, b, seed, paged=False, block_size=16):
     return out
 
 
-def mla_host(B, h, d_c, d_R, d_nope, d_v, s, seed, paged=False, block_size=16):
+def mla_host(B, h, d_c, d_R, d_nope, d_v, s, seed, paged=False, block_size=16, q_len=1):
     sh = synth.MlaShape("t", B=B, h=h, d_c=d_c, d_R=d_R, d_nope=d_nope, d_v=d_v, s=tuple(s),
-                        paged=paged, block_size=block_size, seed=seed)
+                        paged=paged, block_size=block_size, seed=seed, q_len=q_len)
     d = synth.draw_mla(sh, device="cpu")
     out = {k: synth.host_bits(d[k]) for k in ("q_nope", "q_rope", "cache", "w_uk", "w_uv")}
     out["s"] = d["s_host"]

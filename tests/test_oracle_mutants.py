@@ -32,6 +32,11 @@ MUTANTS = [
      "ld(w_uk, ((size_t)i * d_c + c) * d_nope + e, b)", 0, ["test_oracle_mla.py"]),
     ("multi_visible_off_by_one", "const int n = sb - (q_len - 1 - jq);",
      "const int n = sb - (q_len - jq);", 0, ["test_oracle_multi.py"]),
+    ("mla_multi_visible_off_by_one",
+     "const int n = sb - q_len + 1 + jq > 0 ? sb - q_len + 1 + jq : 0;",
+     "const int n = sb - q_len + jq > 0 ? sb - q_len + jq : 0;", 0, ["test_oracle_mla_multi.py"]),
+    ("mla_multi_position_index", "const int jq = (int)((r / h) % q_len), i = (int)(r % h);",
+     "const int jq = (int)(r % q_len), i = (int)(r % h);", 0, ["test_oracle_mla_multi.py"]),
     ("merge_weight_sign", "const double w = exp((double)lse_parts[(size_t)k * rows + r] - M);",
      "const double w = exp(M - (double)lse_parts[(size_t)k * rows + r]);", 0,
      ["test_oracle_merge.py"]),

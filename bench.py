@@ -273,6 +273,50 @@ def run_mla(name, steps, warmup, rotate, keep=None):
     return sh, total_ms, per
 
 
+def run_mla_multi(name, q_len, steps, warmup, rotate):
+    """The MLA workload with q_len new tokens per sequence (bf16 latent cache)."""
+    import dataclasses
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = dataclasses.replace(synth.configs()[name], q_len=q_len)
+    sets = [synth.draw_mla(sh, device="cuda", seed=sh.seed + 1000 * r) for r in range(rotate)]
+    out = torch.empty((sh.B, q_len, sh.h, sh.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((sh.B, q_len, sh.h), dtype=torch.float32, device="cuda")
+    wsb = A.attn_decode_mla_multi_workspace_bytes(sh.B, q_len, sh.h, sh.d_c, sh.d_R)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    it = [0]
+
+    def call():
+        d = sets[it[0] % rotate]
+        it[0] += 1
+        bt = d.get("block_table")
+        A.attn_decode_mla_absorbed_multi(out, None, lse, d["q_nope"], d["q_rope"], d["w_uk"],
+                                         d["w_uv"], d["cache"], d["s"], bt,
+                                         0 if bt is None else bt.shape[1], sh.block_size,
+                                         0 if bt is None else d["cache"].shape[0], sh.B, q_len,
+                                         sh.s_max, sh.h, sh.d_c, sh.d_R, sh.d_nope, sh.d_v, 2,
+                                         0.0, ws, wsb, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    return sh, total_ms, per
+
+
+def mla_multi_alg_bytes(sh, q_len):
+    """Latent rows once, weights once, q and out of every query position."""
+    return (sum(sh.s) * (sh.d_c + sh.d_R) * sh.b + sh.h * (sh.d_nope + sh.d_v) * sh.d_c * sh.b
+            + sh.B * q_len * sh.h * (sh.d_nope + sh.d_R + sh.d_v) * sh.b)
+
+
+def mla_multi_flops(sh, q_len):
+    """Every position scores and sums over the tokens it sees."""
+    seen = sum(sum(max(n - (q_len - 1 - j), 0) for j in range(q_len)) for n in sh.s)
+    return (2 * sh.h * seen * (2 * sh.d_c + sh.d_R)
+            + 2 * sh.B * q_len * sh.h * sh.d_c * (sh.d_nope + sh.d_v))
+
+
 def run_mla_fp8(name, steps, warmup, rotate, c_scale=1.0 / 32, r_scale=1.0 / 32):
     """The MLA workload with its latent cache stored as E4M3 codes."""
     import torch
@@ -441,12 +485,18 @@ def sweep(args):
     import torch
     import synth
     fp8, ql = args.sweep_cache == "fp8", args.sweep_q_len
+    only = set(args.sweep_only.split(",")) if args.sweep_only else None
     for name in SWEEP:
+        if only is not None and name not in only:
+            continue
         sh = synth.configs()[name]
         gqa = isinstance(sh, synth.GqaShape)
         if not gqa and ql > 1:
-            continue
-        if gqa and ql > 1:
+            if fp8:
+                continue
+            by = mla_multi_alg_bytes(sh, ql)
+            run = lambda r: run_mla_multi(name, ql, args.steps, args.warmup, r)
+        elif gqa and ql > 1:
             by = gqa_multi_alg_bytes(sh, ql)
             run = lambda r: run_gqa_multi(name, ql, args.steps, args.warmup, r)
         elif gqa and fp8:
@@ -470,6 +520,33 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
+LEGS = ["llama3_70b_gqa8_b16", "llama3_70b_gqa8_b1", "llama3_70b_mqa_b16", "paged_gqa8"]
+
+
+def gqa_leg(name, steps, warmup):
+    """One GQA workload's call time and its roofline object.  Input sets
+    rotate (>= 1.2 GB per rotation) so that the Infinity Cache cannot serve
+    a call from the previous one."""
+    import torch
+    import synth
+    sh = synth.configs()[name]
+    ab = gqa_alg_bytes(sh)
+    rot = max(1, min(16, int(np.ceil(1.2e9 / ab))))
+    _, tot, per = run_gqa(name, steps, warmup, rotate=rot)
+    torch.cuda.empty_cache()
+    us = tot * 1e3 / steps
+    achieved = ab / (us * 1e-6) / 1e9
+    lens = np.asarray(sh.s)
+    return {"workload": f"{name}: GQA decode B={sh.B} h={sh.h} h_kv={sh.h_kv} d_h={sh.d_h} "
+                        f"s={int(lens.min())}..{int(lens.max())} (total {int(lens.sum())} tokens)"
+                        f"{' paged, 16-token blocks' if sh.paged else ''}, bf16",
+            "us_per_call": us, "median_call_us": float(np.median(per)) * 1e3,
+            "rotate": rot,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                         "alg_bytes_per_call": ab}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -488,6 +565,12 @@ def main():
     ap.add_argument("--sweep-cache", choices=["bf16", "fp8"], default="bf16",
                     help="cache format of the sweep")
     ap.add_argument("--sweep-q-len", type=int, default=1, help="new tokens per sequence in the sweep")
+    ap.add_argument("--sweep-only", default="",
+                    help="comma-separated workload names: sweep only these (one kernel per trace)")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the Llama-3-70B-shaped and paged GQA legs")
+    ap.add_argument("--mla-q-len", type=int, default=2,
+                    help="new tokens per sequence in the multi-token MLA leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -592,6 +675,27 @@ def main():
                                  "alg_bytes_per_call": fab}
         except Exception as e:
             rec["mla"]["fp8"] = {"error": str(e)[:200]}
+        if not args.no_multi and "steps_per_s" in rec["mla"]:
+            try:   # the same MLA layer verifying mla_q_len new tokens per sequence in one call
+                ql = args.mla_q_len
+                qsh, qtot, qper = run_mla_multi(args.mla_config, ql, args.steps, args.warmup,
+                                                rotate=4)
+                qms = qtot / args.steps
+                qab = mla_multi_alg_bytes(qsh, ql)
+                qfl = mla_multi_flops(qsh, ql)
+                qfloor = max(qab / (HBM_PEAK_GBPS * 1e9), qfl / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                rec["mla"]["multi"] = {
+                    "workload": f"{qsh.name}: {ql} new tokens per sequence (causal among them), "
+                                f"bf16 latent cache",
+                    "q_len": ql, "steps_per_s": 1000.0 / qms, "ms_per_step": qms,
+                    "query_tokens_per_s": qsh.B * ql * 1000.0 / qms,
+                    "median_call_us": float(np.median(qper)) * 1e3,
+                    "alg_bytes_per_call": qab, "flops_per_call": qfl,
+                    "mfma_frac": qfl / (qms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "roofline_frac": qfloor / (qms * 1e-3),
+                    "time_vs_one_token": qms / rec["mla"]["ms_per_step"]}
+            except Exception as e:
+                rec["mla"]["multi"] = {"error": str(e)[:200]}
     if not args.no_fp8:
         try:   # the same workload over an E4M3 cache with per-tensor scales
             fsh, ftot, fper = run_gqa_fp8(args.config, args.steps, args.warmup, rotate=2)
@@ -623,6 +727,13 @@ def main():
                             "time_vs_one_token": qms / ms}
         except Exception as e:  # reports its own failure, the line still prints
             rec["multi"] = {"error": str(e)[:200]}
+    if not args.no_legs:
+        rec["legs"] = {}
+        for leg in LEGS:
+            try:
+                rec["legs"][leg] = gqa_leg(leg, args.steps, args.warmup)
+            except Exception as e:  # each leg reports its own failure
+                rec["legs"][leg] = {"error": str(e)[:200]}
     if not args.no_dcp:
         try:   # the exchange step of context-parallel decode, on one GPU
             mms_, mper, malg = run_merge(8, 32, 128, 512, args.steps, args.warmup)

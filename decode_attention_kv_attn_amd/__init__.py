@@ -36,6 +36,9 @@ EXPORTED = (
     "attn_decode_gqa_fp8_paged_scales",
     "kv_cache_append_fp8_paged_scales",
     "attn_decode_gqa_noalloc",
+    "attn_decode_mla_absorbed_multi",
+    "attn_decode_mla_absorbed_multi_fp8",
+    "attn_decode_mla_multi_workspace_bytes",
 )
 
 _lib = None
@@ -99,6 +102,15 @@ def lib():
                                                        P]
         L.attn_decode_gqa_noalloc.restype = I
         L.attn_decode_gqa_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P]
+        L.attn_decode_mla_absorbed_multi.restype = I
+        L.attn_decode_mla_absorbed_multi.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I,
+                                                     I, I, I, I, I, I, I, I, F, P, Z, P]
+        L.attn_decode_mla_absorbed_multi_fp8.restype = I
+        L.attn_decode_mla_absorbed_multi_fp8.argtypes = [P, P, P, P, P, P, P, P, F, F, P, P, I,
+                                                         I, I, I, I, I, I, I, I, I, I, F, P, Z,
+                                                         P]
+        L.attn_decode_mla_multi_workspace_bytes.restype = Z
+        L.attn_decode_mla_multi_workspace_bytes.argtypes = [I, I, I, I, I]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -286,6 +298,38 @@ def attn_decode_mla_absorbed(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cac
     return _check(rc) if check else rc
 
 
+def attn_decode_mla_absorbed_multi(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, s,
+                                   block_table, max_blocks, block_size, num_blocks, B, q_len,
+                                   s_max, h, d_c, d_R, d_nope, d_v, b, scale, workspace,
+                                   workspace_bytes, stream=None, check=True):
+    rc = lib().attn_decode_mla_absorbed_multi(_p(out), _p(u_latent), _p(lse), _p(q_nope),
+                                              _p(q_rope), _p(w_uk), _p(w_uv), _p(cache), _p(s),
+                                              _p(block_table), max_blocks, block_size,
+                                              num_blocks, B, q_len, s_max, h, d_c, d_R, d_nope,
+                                              d_v, b, float(scale), _p(workspace),
+                                              int(workspace_bytes), _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_mla_absorbed_multi_fp8(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache,
+                                       c_scale, r_scale, s, block_table, max_blocks, block_size,
+                                       num_blocks, B, q_len, s_max, h, d_c, d_R, d_nope, d_v,
+                                       scale, workspace, workspace_bytes, stream=None,
+                                       check=True):
+    rc = lib().attn_decode_mla_absorbed_multi_fp8(_p(out), _p(u_latent), _p(lse), _p(q_nope),
+                                                  _p(q_rope), _p(w_uk), _p(w_uv), _p(cache),
+                                                  float(c_scale), float(r_scale), _p(s),
+                                                  _p(block_table), max_blocks, block_size,
+                                                  num_blocks, B, q_len, s_max, h, d_c, d_R,
+                                                  d_nope, d_v, float(scale), _p(workspace),
+                                                  int(workspace_bytes), _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_mla_multi_workspace_bytes(B, q_len, h, d_c, d_R):
+    return int(lib().attn_decode_mla_multi_workspace_bytes(B, q_len, h, d_c, d_R))
+
+
 # ---------------------------------------------------------------------------
 # Convenience wrappers over torch tensors (shape bookkeeping only; they call
 # the entry points above).
@@ -383,6 +427,43 @@ def decode_mla(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_siz
         attn_decode_mla_absorbed_fp8(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache, c_scale,
                                      r_scale, s, block_table, max_blocks, block_size, num_blocks,
                                      B, s_max, h, d_c, d_R, d_nope, d_v, scale, wb, wn, stream)
+    return out, ul, l
+
+
+def decode_mla_multi(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_size=16,
+                     s_max=None, scale=0.0, want_latent=True, workspace=None, stream=None,
+                     c_scale=None, r_scale=None):
+    """Absorbed MLA decode of q_len new tokens per sequence: q_nope
+    [B,q_len,h,d_nope], q_rope [B,q_len,h,d_R].  Returns (out [B,q_len,h,d_v],
+    u_latent [B,q_len,h,d_c] or None, lse [B,q_len,h])."""
+    import torch
+    B, q_len, h, d_nope = q_nope.shape
+    d_R = q_rope.shape[3]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    if block_table is None:
+        s_max = cache.shape[1] if s_max is None else s_max
+        max_blocks, num_blocks = 0, 0
+    else:
+        max_blocks = block_table.shape[1]
+        num_blocks = cache.shape[0]
+        s_max = max_blocks * block_size if s_max is None else s_max
+    dev = q_nope.device
+    out = torch.empty((B, q_len, h, d_v), dtype=q_nope.dtype, device=dev)
+    ul = (torch.empty((B, q_len, h, d_c), dtype=torch.float32, device=dev) if want_latent
+          else None)
+    l = torch.empty((B, q_len, h), dtype=torch.float32, device=dev)
+    ws = workspace or Workspace(dev)
+    wb, wn = ws.get(attn_decode_mla_multi_workspace_bytes(B, q_len, h, d_c, d_R))
+    if c_scale is None:
+        attn_decode_mla_absorbed_multi(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache, s,
+                                       block_table, max_blocks, block_size, num_blocks, B, q_len,
+                                       s_max, h, d_c, d_R, d_nope, d_v, 2, scale, wb, wn, stream)
+    else:
+        attn_decode_mla_absorbed_multi_fp8(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache,
+                                           c_scale, r_scale, s, block_table, max_blocks,
+                                           block_size, num_blocks, B, q_len, s_max, h, d_c, d_R,
+                                           d_nope, d_v, scale, wb, wn, stream)
     return out, ul, l
 
 

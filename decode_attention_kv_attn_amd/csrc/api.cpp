@@ -140,6 +140,9 @@ GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b, int q_len = 
 // the shares are computed on the device from the lengths.  A workgroup
 // leaves one partial per sequence it touches, so n_wg + B - 1 partial slots
 // cover every schedule.
+// new tokens per sequence that one multi-token MLA call takes
+constexpr int kMlaMaxQLen = 16;
+
 struct MlaPlan {
     int n_wg, min_tiles;
     size_t qhat_bytes, part_u_bytes, part_ml_bytes, flag_bytes, sched_bytes, ws_bytes;
@@ -454,23 +457,26 @@ int attn_decode_gqa_fp8(void* out, float* lse, const void* q, const void* cache_
 namespace {
 
 // Shared body of the MLA entry points: b = 2 (bf16 cache) or b = 1 (E4M3
-// cache codes with a latent and a rotary scale).
+// cache codes with a latent and a rotary scale); q_len new tokens per
+// sequence, each (sequence, position) pair one query row of the kernels.
 int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const void* q_rope,
                const void* w_uk, const void* w_uv, const void* cache, float c_scale,
                float r_scale, const int32_t* s, const int32_t* block_table, int max_blocks,
-               int block_size, int num_blocks, int B, int s_max, int h, int d_c, int d_R,
-               int d_nope, int d_v, int b, float scale, void* workspace, size_t workspace_bytes,
-               void* stream)
+               int block_size, int num_blocks, int B, int q_len, int s_max, int h, int d_c,
+               int d_R, int d_nope, int d_v, int b, float scale, void* workspace,
+               size_t workspace_bytes, void* stream)
 {
     if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s)
         return fail(ATTN_EINVAL, "null out, q_nope, q_rope, w_uk, w_uv, cache or s");
     if (B < 0 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0 || s_max < 0)
         return fail(ATTN_EINVAL, "bad sizes");
+    if (q_len < 1 || q_len > kMlaMaxQLen)
+        return fail(ATTN_EINVAL, "q_len must be in 1 .. %d (got %d)", kMlaMaxQLen, q_len);
     if (b != 2 && b != 1) return fail(ATTN_ENOTSUP, "MLA supports bf16 storage only (b=2)");
     if (d_c != 512 || d_R != 64)
         return fail(ATTN_ENOTSUP, "MLA supports d_c=512, d_R=64 (got %d, %d)", d_c, d_R);
     if (h % 16 != 0 || h > 128) return fail(ATTN_ENOTSUP, "MLA needs h a multiple of 16, <= 128");
-    if ((long long)B * s_max >= (1LL << 31))
+    if ((long long)B * q_len * s_max >= (1LL << 31) || (long long)B * q_len >= (1LL << 24))
         return fail(ATTN_ENOTSUP, "problem too large for one launch");
     if (d_nope % 32 != 0 || d_nope > 256 || d_v % 16 != 0 || d_v > 256)
         return fail(ATTN_ENOTSUP, "MLA needs d_nope a multiple of 32, d_v of 16, both <= 256");
@@ -479,7 +485,7 @@ int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const
         if (rc) return rc;
     }
     if (B == 0) return ATTN_OK;
-    const MlaPlan P = plan_mla(B, h, d_c, d_R);
+    const MlaPlan P = plan_mla(B * q_len, h, d_c, d_R);
     if (!workspace || workspace_bytes < P.ws_bytes)
         return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
                     workspace ? workspace_bytes : (size_t)0);
@@ -503,7 +509,8 @@ int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const
     p.max_blocks = max_blocks;
     p.bs_log2 = block_table ? ilog2(block_size) : 0;
     p.num_blocks = num_blocks;
-    p.B = B;
+    p.B = B * q_len;
+    p.q_len = q_len;
     p.s_max = s_max;
     p.h = h;
     p.d_c = d_c;
@@ -536,7 +543,7 @@ int attn_decode_mla_absorbed(void* out, float* u_latent, float* lse, const void*
 {
     if (b != 2) return fail(ATTN_ENOTSUP, "MLA supports bf16 storage only (b=2)");
     return decode_mla(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1.f, 1.f, s,
-                      block_table, max_blocks, block_size, num_blocks, B, s_max, h, d_c, d_R,
+                      block_table, max_blocks, block_size, num_blocks, B, 1, s_max, h, d_c, d_R,
                       d_nope, d_v, b, scale, workspace, workspace_bytes, stream);
 }
 
@@ -551,8 +558,46 @@ int attn_decode_mla_absorbed_fp8(void* out, float* u_latent, float* lse, const v
     if (!(c_scale > 0.f) || isinf(c_scale) || !(r_scale > 0.f) || isinf(r_scale))
         return fail(ATTN_EINVAL, "c_scale and r_scale must be positive and finite");
     return decode_mla(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, c_scale, r_scale, s,
-                      block_table, max_blocks, block_size, num_blocks, B, s_max, h, d_c, d_R,
+                      block_table, max_blocks, block_size, num_blocks, B, 1, s_max, h, d_c, d_R,
                       d_nope, d_v, 1, scale, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_mla_absorbed_multi(void* out, float* u_latent, float* lse, const void* q_nope,
+                                   const void* q_rope, const void* w_uk, const void* w_uv,
+                                   const void* cache, const int32_t* s,
+                                   const int32_t* block_table, int max_blocks, int block_size,
+                                   int num_blocks, int B, int q_len, int s_max, int h, int d_c,
+                                   int d_R, int d_nope, int d_v, int b, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (b != 2) return fail(ATTN_ENOTSUP, "MLA supports bf16 storage only (b=2)");
+    return decode_mla(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1.f, 1.f, s,
+                      block_table, max_blocks, block_size, num_blocks, B, q_len, s_max, h, d_c,
+                      d_R, d_nope, d_v, b, scale, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_mla_absorbed_multi_fp8(void* out, float* u_latent, float* lse,
+                                       const void* q_nope, const void* q_rope, const void* w_uk,
+                                       const void* w_uv, const void* cache, float c_scale,
+                                       float r_scale, const int32_t* s,
+                                       const int32_t* block_table, int max_blocks,
+                                       int block_size, int num_blocks, int B, int q_len,
+                                       int s_max, int h, int d_c, int d_R, int d_nope, int d_v,
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream)
+{
+    if (!(c_scale > 0.f) || isinf(c_scale) || !(r_scale > 0.f) || isinf(r_scale))
+        return fail(ATTN_EINVAL, "c_scale and r_scale must be positive and finite");
+    return decode_mla(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, c_scale, r_scale, s,
+                      block_table, max_blocks, block_size, num_blocks, B, q_len, s_max, h, d_c,
+                      d_R, d_nope, d_v, 1, scale, workspace, workspace_bytes, stream);
+}
+
+size_t attn_decode_mla_multi_workspace_bytes(int B, int q_len, int h, int d_c, int d_R)
+{
+    if (B <= 0 || q_len < 1 || q_len > kMlaMaxQLen || h <= 0 || d_c <= 0 || d_R < 0) return 0;
+    if ((long long)B * q_len >= (1LL << 24)) return 0;
+    return plan_mla(B * q_len, h, d_c, d_R).ws_bytes;
 }
 
 int attn_decode_gqa_multi(void* out, float* lse, const void* q, const void* cache_k,

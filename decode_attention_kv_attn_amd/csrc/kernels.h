@@ -58,6 +58,9 @@ hipError_t launch_append(const AppendParams& k, const AppendParams* v, int B, hi
 // bf16 rows -> OCP E4M3 codes of x * inv_scale (nearest, ties to even, saturating at +-448)
 hipError_t launch_append_fp8(const AppendParams& k, const AppendParams* v, int B, hipStream_t st);
 
+// B counts query rows: row b is new-token position b % q_len of sequence
+// b / q_len, whose length s and block-table row it reads (q_len = 1: one
+// row per sequence)
 struct MlaParams {
     void* out;            // [B, h, d_v] bf16
     float* u_latent;      // [B, h, d_c] fp32 or nullptr
@@ -76,6 +79,7 @@ struct MlaParams {
     int32_t* sched;       // tile_start [B + 1], wstart [n_wg], tpw [1]
     int max_blocks, bs_log2, num_blocks;
     int B, s_max, h, d_c, d_R, d_nope, d_v;
+    int q_len;            // new tokens per sequence (query rows per sequence)
     int n_wg, min_tiles;  // decode workgroups; fewest 32-token tiles per workgroup
     float scale_log2;
     int f8;               // cache rows are E4M3 codes (else bf16)

@@ -36,8 +36,18 @@ namespace attn {
 struct SchedArgs {
     const int32_t* s;
     int32_t* sched;
-    int B, s_max, n_wg, min_tiles;
+    int B, s_max, n_wg, min_tiles, q_len;
 };
+
+// Query rows: row b is new-token position b % q_len of sequence b / q_len
+// (q_len = 1: one row per sequence).  Its cache is that sequence's, and it
+// sees the sequence's clamped length less the new tokens after it.
+__device__ __forceinline__ int mla_cache_seq(int b, int q_len) { return q_len == 1 ? b : b / q_len; }
+__device__ __forceinline__ int mla_seen(int s_b, int b, int q_len, int s_max)
+{
+    const int n = min(max(s_b, 0), s_max);
+    return q_len == 1 ? n : max(n - (q_len - 1 - b % q_len), 0);
+}
 __device__ __forceinline__ void mla_schedule(SchedArgs p, int tid, int nthr, int* sc);
 
 // q^ is stored in the order the decode kernel reads it as the B operand of
@@ -96,7 +106,8 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
     __shared__ __attribute__((aligned(16))) uint16_t ost[4][16][32 + 8];   // per-wavefront output staging
     if (blockIdx.x == gridDim.x - 1) {   // one extra workgroup: the decode tile schedule
         __shared__ int sc[256];
-        mla_schedule(SchedArgs{p.s, p.sched, p.B, p.s_max, p.n_wg, p.min_tiles}, threadIdx.x, 256, sc);
+        mla_schedule(SchedArgs{p.s, p.sched, p.B, p.s_max, p.n_wg, p.min_tiles, p.q_len}, threadIdx.x, 256,
+                     sc);
         return;
     }
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
@@ -384,12 +395,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 // workspace whose schedule was overwritten cannot steer an access outside the
 // lengths, the table, the pool or the partial slots.
 struct SchedView {
-    const int32_t* __restrict__ s;       // lengths [B]
+    const int32_t* __restrict__ s;       // lengths [B / q_len]
     const int32_t* __restrict__ sched;   // tile_start [B + 1], wstart [n_wg], tpw
-    int s_max, B, n_wg;
+    int s_max, B, n_wg, q_len;
     __device__ __forceinline__ int len(int b) const
     {
-        return min(max(__builtin_amdgcn_readfirstlane(s[b]), 0), s_max);
+        return mla_seen(__builtin_amdgcn_readfirstlane(s[mla_cache_seq(b, q_len)]), b, q_len, s_max);
     }
     __device__ __forceinline__ int at(int i) const { return __builtin_amdgcn_readfirstlane(sched[i]); }
     __device__ __forceinline__ int total() const
@@ -409,7 +420,9 @@ __device__ __forceinline__ void mla_schedule(SchedArgs p, int tid, int nthr, int
 {
     int32_t* ts = p.sched;
     int32_t* wstart = p.sched + p.B + 1;
-    auto tiles_of = [&](int i) { return i < p.B ? (min(max(p.s[i], 0), p.s_max) + kT - 1) / kT : 0; };
+    auto tiles_of = [&](int i) {
+        return i < p.B ? (mla_seen(p.s[mla_cache_seq(i, p.q_len)], i, p.q_len, p.s_max) + kT - 1) / kT : 0;
+    };
     // pass 1: total
     int part = 0;
     for (int i = tid; i < p.B; i += nthr) part += tiles_of(i);
@@ -514,8 +527,9 @@ struct TileDma {
     }
     __device__ __forceinline__ size_t half_row(int b, int t) const
     {
-        if (PAGED) return paged_row(btab, b, t, p.max_blocks, p.bs_log2, p.num_blocks);
-        return (size_t)b * p.s_max + t;
+        const int cb = mla_cache_seq(b, p.q_len);
+        if (PAGED) return paged_row(btab, cb, t, p.max_blocks, p.bs_log2, p.num_blocks);
+        return (size_t)cb * p.s_max + t;
     }
     __device__ __forceinline__ void rows(const TileWalk& c, size_t& r0, size_t& r1) const
     {
@@ -601,7 +615,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     const int tid = threadIdx.x, lane = tid % 64, hh = lane / 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int w = xcd_major(blockIdx.x, gridDim.x);
-    const SchedView sv{slen, sched, p.s_max, p.B, p.n_wg};
+    const SchedView sv{slen, sched, p.s_max, p.B, p.n_wg, p.q_len};
     const int total = sv.total();
     const int tpw = sv.tpw(total);
     const long long g0l = (long long)w * tpw;
@@ -985,7 +999,8 @@ constexpr int kRcRows = 4;   // rows in flight in the exact recompute
 __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_lo, int g_hi, int s0,
                                       int lane, float& M, float& L, float4& u0, float4& u1)
 {
-    const int n = min(max(p.s[bb], 0), p.s_max);
+    const int cb = mla_cache_seq(bb, p.q_len);
+    const int n = mla_seen(p.s[cb], bb, p.q_len, p.s_max);
     const int t_lo = (g_lo - s0) * kT, t_hi = min((g_hi - s0) * kT, n);
     const uint16_t* qc = p.qhat + qhat_index(bb, i, 8 * lane, p.h);
     const uint16_t* qr = p.qhat + qhat_index(bb, i, 512 + 8 * (lane / 8), p.h) + lane % 8;
@@ -1008,8 +1023,8 @@ __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_l
 #pragma unroll
         for (int k = 0; k < kRcRows; k++) {
             const int t = min(t0 + k, t_hi - 1);
-            const size_t row = p.bt ? paged_row(p.bt, bb, t, p.max_blocks, p.bs_log2, p.num_blocks)
-                                    : (size_t)bb * p.s_max + t;
+            const size_t row = p.bt ? paged_row(p.bt, cb, t, p.max_blocks, p.bs_log2, p.num_blocks)
+                                    : (size_t)cb * p.s_max + t;
             if (p.f8) {   // E4M3 codes, widened to bf16 exactly
                 const uint8_t* c8p = (const uint8_t*)p.cache + row * 576;
                 c8[k] = __builtin_bit_cast(uint4, fp8x8_to_bf16(*(const uint2*)(c8p + 8 * lane)));

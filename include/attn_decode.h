@@ -225,9 +225,10 @@ int attn_decode_gqa_fp8(void* out, float* lse, const void* q, const void* cache_
 /*
  * attn_decode_gqa_multi -- decode of q_len new tokens per sequence in one
  * call, as a speculative step verifies several drafted tokens ("MLA: why
- * one latent can replace a multi-head KV cache", section "MHA mode and MQA
- * mode are execution forms" (by gloss), counts the tokens one speculative
- * verification checks among what selects a decode kernel).  The q_len tokens are already appended, so s[b]
+ * one latent can replace a multi-head KV cache", section on why prefill
+ * need not absorb as decode does (by gloss), counts the tokens one
+ * speculative verification checks among what selects a decode kernel).
+ * The q_len tokens are already appended, so s[b]
  * counts them; query position jq (0-based) sits at cache position
  * s[b] - q_len + jq and attends causally to the first s[b] - q_len + 1 + jq
  * tokens:
@@ -358,6 +359,54 @@ int attn_decode_mla_absorbed_fp8(void* out, float* u_latent, float* lse, const v
                                  int block_size, int num_blocks, int B, int s_max, int h, int d_c,
                                  int d_R, int d_nope, int d_v, float scale, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_mla_absorbed_multi -- attn_decode_mla_absorbed for q_len new
+ * tokens per sequence in one call: the tokens a speculative step verifies
+ * ("MLA: why one latent can replace a multi-head KV cache",
+ * charlestar.github.io, lists their count and the query length among the
+ * inputs of MLA kernel selection, section on why prefill need not absorb as
+ * decode does (by gloss); its validation chain's "Kernel" step covers query
+ * lengths and speculative tokens).  The q_len tokens are already appended,
+ * so s[b] counts them; position jq (0-based) sits at cache position
+ * s[b] - q_len + jq and attends to the first s[b] - q_len + 1 + jq tokens
+ * (causal among the new tokens).  A position that sees no token gives 0,
+ * u~ = 0 and lse -inf.
+ *   out      : [B, q_len, h, d_v] bf16;  u_latent : [B, q_len, h, d_c] fp32
+ *              or NULL;  lse : [B, q_len, h] fp32 or NULL.
+ *   q_nope   : [B, q_len, h, d_nope] bf16;  q_rope : [B, q_len, h, d_R].
+ *   Weights, cache, table, lengths, scale: as attn_decode_mla_absorbed.
+ *   workspace: at least attn_decode_mla_multi_workspace_bytes(B, q_len, h,
+ *              d_c, d_R) bytes.
+ * Each (sequence, position) pair is one query row of the kernels, so q_len
+ * = 1 is attn_decode_mla_absorbed exactly.  Supported: 1 <= q_len <= 16
+ * (else EINVAL), B * q_len < 2^24, the rest as attn_decode_mla_absorbed.
+ * Errors: as attn_decode_mla_absorbed.
+ */
+int attn_decode_mla_absorbed_multi(void* out, float* u_latent, float* lse, const void* q_nope,
+                                   const void* q_rope, const void* w_uk, const void* w_uv,
+                                   const void* cache, const int32_t* s,
+                                   const int32_t* block_table, int max_blocks, int block_size,
+                                   int num_blocks, int B, int q_len, int s_max, int h, int d_c,
+                                   int d_R, int d_nope, int d_v, int b, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_mla_absorbed_multi_fp8 -- attn_decode_mla_absorbed_multi over
+ * an FP8 latent cache with the scales of attn_decode_mla_absorbed_fp8.
+ */
+int attn_decode_mla_absorbed_multi_fp8(void* out, float* u_latent, float* lse,
+                                       const void* q_nope, const void* q_rope, const void* w_uk,
+                                       const void* w_uv, const void* cache, float c_scale,
+                                       float r_scale, const int32_t* s,
+                                       const int32_t* block_table, int max_blocks,
+                                       int block_size, int num_blocks, int B, int q_len,
+                                       int s_max, int h, int d_c, int d_R, int d_nope, int d_v,
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* Workspace bytes for attn_decode_mla_absorbed_multi(_fp8); 0 for invalid sizes. */
+size_t attn_decode_mla_multi_workspace_bytes(int B, int q_len, int h, int d_c, int d_R);
 
 /*
  * kv_cache_append_mla_fp8 -- append one latent row per sequence to an FP8

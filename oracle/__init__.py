@@ -92,6 +92,9 @@ def _load():
         lib.ref_mla_absorbed_multi_fp8.restype = I
         lib.ref_mla_absorbed_multi_fp8.argtypes = [P, P, P, P, P, P, P, P, D, D, P, P, I, I, I,
                                                    I, I, I, I, I, I, I, D]
+        lib.ref_mla_output.restype = I
+        lib.ref_mla_output.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
+                                       I, I, I, D]
         lib.ref_kv_append_mla_fp8.restype = I
         lib.ref_kv_append_mla_fp8.argtypes = [P, P, C.c_float, C.c_float, P, P, I, I, I, I, I, I]
         lib.ref_gqa_decode_fp8_paged_scales.restype = I
@@ -239,6 +242,38 @@ def mla_absorbed_multi(q_nope, q_rope, w_uk, w_uv, cache, s, b=2, block_table=No
     if rc != 0:
         raise ValueError(f"ref_mla_absorbed_multi rejected its arguments ({rc})")
     return out, ul, lse
+
+
+def mla_output(q_nope, q_rope, w_uk, w_uv, w_o, cache, s, b=2, block_table=None, block_size=16,
+               scale=None):
+    """Reference MLA decode through the output projection W_O [d_model, h d_v].
+
+    q_nope/q_rope [B, h, .] (one new token) or [B, q_len, h, .].  Returns
+    (o [B, d_model] or [B, q_len, d_model], lse [B, h] or [B, q_len, h]).
+    """
+    multi = q_nope.ndim == 4
+    if multi:
+        B, q_len, h = q_nope.shape[:3]
+    else:
+        (B, h), q_len = q_nope.shape[:2], 1
+    (q_nope, q_rope, w_uk, w_uv, cache, s, bt, _, _, d_nope, d_R, d_c, d_v, s_max, max_blocks,
+     bs) = _mla_args(q_nope.reshape(B, q_len * h, -1), q_rope.reshape(B, q_len * h, -1), w_uk,
+                     w_uv, cache, s, b, block_table, block_size)
+    w_o = _stored(w_o, b)
+    d_model = w_o.shape[0]
+    if w_o.shape[1] != h * d_v:
+        raise ValueError("w_o must be [d_model, h * d_v]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_nope + d_R)
+    o = np.zeros((B, q_len, d_model))
+    lse = np.zeros((B, q_len, h))
+    rc = _load().ref_mla_output(_ptr(o), _ptr(lse), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                _ptr(w_uv), _ptr(w_o), _ptr(cache), _ptr(s), _ptr(bt), max_blocks,
+                                bs, B, q_len, s_max, h, d_c, d_R, d_nope, d_v, d_model, b,
+                                float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_mla_output rejected its arguments ({rc})")
+    return (o, lse) if multi else (o[:, 0], lse[:, 0])
 
 
 def mla_explicit(q_nope, q_rope, w_uk, w_uv, cache, s, b=2, block_table=None, block_size=16,

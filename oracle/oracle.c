@@ -331,6 +331,51 @@ int ref_mla_absorbed_multi(double* out, double* u_latent, double* lse, const voi
                              d_R, d_nope, d_v, b, scale);
 }
 
+/*
+ * MLA decode through the attention block's output projection
+ * ("Multi-Head Latent Attention (MLA): Mathematical Foundations" (llms.blog),
+ * section "Value Output Matrix Absorption"): the heads are aggregated by
+ * W_O = [W_O^1, ..., W_O^h], a [d_model, h d_v] matrix whose columns
+ * i d_v .. i d_v + d_v - 1 are W_O^i, as
+ *   o_t = sum_i W_O^i u_{t,i},   u_{t,i} = W_UV,i u~_{t,i}.
+ * Computed in that order (each head's u in double, then the projection);
+ * the merged weights W_O^i W_UV,i of the same section are the library's
+ * business, and the tests pin that both groupings agree.
+ *   o [B, q_len, d_model]; lse [B, q_len, h] (nullable); the rest as
+ *   ref_mla_absorbed_multi, w_o [d_model, h d_v] stored with b bytes.
+ */
+int ref_mla_output(double* o, double* lse, const void* q_nope, const void* q_rope,
+                   const void* w_uk, const void* w_uv, const void* w_o, const void* cache,
+                   const int32_t* s, const int32_t* block_table, int max_blocks, int block_size,
+                   int B, int q_len, int s_max, int h, int d_c, int d_R, int d_nope, int d_v,
+                   int d_model, int b, double scale)
+{
+    if (!o || !w_o || d_model <= 0 || B < 0 || q_len < 1 || h <= 0 || d_v <= 0)
+        return OR_EINVAL;
+    const size_t rows = (size_t)B * q_len;
+    double* u = (double*)malloc(sizeof(double) * (rows * h * (size_t)d_v + 1));
+    if (!u) return OR_EINVAL;
+    int rc = mla_absorbed_impl(u, NULL, lse, q_nope, q_rope, w_uk, w_uv, cache, b, 1.0, 1.0, s,
+                               block_table, max_blocks, block_size, B, q_len, s_max, h, d_c, d_R,
+                               d_nope, d_v, b, scale);
+    if (rc == OR_OK) {
+        const size_t hd = (size_t)h * d_v;
+#pragma omp parallel for schedule(static)
+        for (long r = 0; r < (long)rows; r++) {
+            for (int n = 0; n < d_model; n++) {
+                double acc = 0.0;
+                for (int i = 0; i < h; i++)
+                    for (int e = 0; e < d_v; e++)
+                        acc += ld(w_o, (size_t)n * hd + (size_t)i * d_v + e, b) *
+                               u[((size_t)r * h + i) * d_v + e];
+                o[(size_t)r * d_model + n] = acc;
+            }
+        }
+    }
+    free(u);
+    return rc;
+}
+
 /* ref_mla_absorbed_multi over an FP8 latent cache (as ref_mla_absorbed_fp8) */
 int ref_mla_absorbed_multi_fp8(double* out, double* u_latent, double* lse, const void* q_nope,
                                const void* q_rope, const void* w_uk, const void* w_uv,

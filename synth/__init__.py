@@ -82,6 +82,7 @@ class MlaShape:
     block_size: int = BLOCK_SIZE
     seed: int = 0
     q_len: int = 1    # new tokens per sequence; queries are [B, q_len, h, .] when > 1
+    d_model: int = 5120   # hidden size the output projection maps to
 
     @property
     def s_max(self) -> int:
@@ -280,6 +281,15 @@ def draw_mla(shape: MlaShape, device="cpu", seed=None):
         d["block_table_host"] = tab
         d["n_blk"] = n_blk
     return d
+
+
+def draw_w_o(shape: MlaShape, device="cpu", seed=None):
+    """Output projection W_O [d_model, h d_v] (torch Linear layout: head i owns
+    columns i d_v .. i d_v + d_v - 1), N(0, 1/sqrt(h d_v)), bf16."""
+    seed = (shape.seed if seed is None else seed) + 7919
+    g = _gen(device, seed)
+    return _randn((shape.d_model, shape.h * shape.d_v), g, device, torch.bfloat16,
+                  std=1.0 / math.sqrt(shape.h * shape.d_v))
 
 
 def draw_mla_fp8(shape: MlaShape, c_scale: float, r_scale: float, device="cpu", seed=None):

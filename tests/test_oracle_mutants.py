@@ -37,6 +37,10 @@ MUTANTS = [
      "const int n = sb - q_len + jq > 0 ? sb - q_len + jq : 0;", 0, ["test_oracle_mla_multi.py"]),
     ("mla_multi_position_index", "const int jq = (int)((r / h) % q_len), i = (int)(r % h);",
      "const int jq = (int)(r % q_len), i = (int)(r % h);", 0, ["test_oracle_mla_multi.py"]),
+    ("mla_output_head_interleaved", "ld(w_o, (size_t)n * hd + (size_t)i * d_v + e, b)",
+     "ld(w_o, (size_t)n * hd + (size_t)e * h + i, b)", 0, ["test_oracle_mla_output.py"]),
+    ("mla_output_w_o_transposed", "ld(w_o, (size_t)n * hd + (size_t)i * d_v + e, b)",
+     "ld(w_o, ((size_t)i * d_v + e) * d_model + n, b)", 0, ["test_oracle_mla_output.py"]),
     ("merge_weight_sign", "const double w = exp((double)lse_parts[(size_t)k * rows + r] - M);",
      "const double w = exp(M - (double)lse_parts[(size_t)k * rows + r]);", 0,
      ["test_oracle_merge.py"]),

@@ -317,6 +317,44 @@ def mla_multi_flops(sh, q_len):
             + 2 * sh.B * q_len * sh.h * sh.d_c * (sh.d_nope + sh.d_v))
 
 
+def run_mla_out(name, merged, steps, warmup, rotate, d_model=5120):
+    """The MLA workload through the output projection W_O [d_model, h d_v]:
+    deferred (heads' outputs, then W_O) or merged (W_O^i W_UV,i, built once
+    before timing)."""
+    import dataclasses
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = dataclasses.replace(synth.configs()[name], d_model=d_model)
+    sets = [synth.draw_mla(sh, device="cuda", seed=sh.seed + 1000 * r) for r in range(rotate)]
+    w_o = synth.draw_w_o(sh, device="cuda")
+    w_abs = A.premerge_weights(w_o, sets[0]["w_uv"]) if merged else None
+    out = torch.empty((sh.B, d_model), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device="cuda")
+    wsb = A.attn_decode_mla_out_workspace_bytes(merged, sh.B, 1, sh.h, sh.d_c, sh.d_R,
+                                                0 if merged else sh.d_v, d_model)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    it = [0]
+
+    def call():
+        d = sets[it[0] % rotate]
+        it[0] += 1
+        if merged:
+            A.attn_decode_mla_out_premerged(out, lse, d["q_nope"], d["q_rope"], d["w_uk"], w_abs,
+                                            d["cache"], d["s"], None, 0, 16, 0, sh.B, 1, sh.s_max,
+                                            sh.h, sh.d_c, sh.d_R, sh.d_nope, d_model, 2, 0.0, ws,
+                                            wsb, sp)
+        else:
+            A.attn_decode_mla_out(out, lse, d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], w_o,
+                                  d["cache"], d["s"], None, 0, 16, 0, sh.B, 1, sh.s_max, sh.h,
+                                  sh.d_c, sh.d_R, sh.d_nope, sh.d_v, d_model, 2, 0.0, ws, wsb, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    return sh, total_ms, per
+
+
 def run_mla_fp8(name, steps, warmup, rotate, c_scale=1.0 / 32, r_scale=1.0 / 32):
     """The MLA workload with its latent cache stored as E4M3 codes."""
     import torch
@@ -558,6 +596,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-dcp", action="store_true")
     ap.add_argument("--no-multi", action="store_true")
+    ap.add_argument("--no-out", action="store_true", help="skip the MLA output-projection legs")
     ap.add_argument("--q-len", type=int, default=4, help="drafted tokens in the multi-token leg")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the JSON line: one line per named workload (all GQA/MQA/MHA and "
@@ -675,6 +714,30 @@ def main():
                                  "alg_bytes_per_call": fab}
         except Exception as e:
             rec["mla"]["fp8"] = {"error": str(e)[:200]}
+        if not args.no_out and "steps_per_s" in rec["mla"]:
+            try:   # the same layer through the output projection, both forms
+                import decode_attention_kv_attn_amd as A
+                res = {}
+                for form, merged in (("deferred", False), ("merged", True)):
+                    osh, otot, oper = run_mla_out(args.mla_config, merged, args.steps,
+                                                  args.warmup, rotate=4)
+                    ous = otot * 1e3 / args.steps
+                    wbytes = (osh.d_model * osh.h * osh.d_c * 2 if merged
+                              else osh.d_model * osh.h * osh.d_v * 2)
+                    res[form] = {"us_per_call": ous,
+                                 "median_call_us": float(np.median(oper)) * 1e3,
+                                 "projection_weight_bytes": wbytes,
+                                 "extra_us_vs_attention": ous - rec["mla"]["ms_per_step"] * 1e3}
+                    torch.cuda.empty_cache()
+                rec["mla"]["out"] = {
+                    "workload": f"{osh.name} through W_O [d_model={osh.d_model}, h d_v], "
+                                f"deferred (heads' outputs, then W_O) vs merged "
+                                f"(W_O^i W_UV,i, [d_model, h d_c])",
+                    **res,
+                    "form_chosen_by_rule": ("merged" if A.attn_mla_out_form(
+                        osh.B, 1, osh.h, osh.d_c, osh.d_v, osh.d_model) == 1 else "deferred")}
+            except Exception as e:
+                rec["mla"]["out"] = {"error": str(e)[:200]}
         if not args.no_multi and "steps_per_s" in rec["mla"]:
             try:   # the same MLA layer verifying mla_q_len new tokens per sequence in one call
                 ql = args.mla_q_len

@@ -39,6 +39,11 @@ EXPORTED = (
     "attn_decode_mla_absorbed_multi",
     "attn_decode_mla_absorbed_multi_fp8",
     "attn_decode_mla_multi_workspace_bytes",
+    "attn_decode_mla_out",
+    "attn_decode_mla_out_premerged",
+    "attn_decode_mla_out_workspace_bytes",
+    "attn_mla_premerge_weights",
+    "attn_mla_out_form",
 )
 
 _lib = None
@@ -111,6 +116,18 @@ def lib():
                                                          P]
         L.attn_decode_mla_multi_workspace_bytes.restype = Z
         L.attn_decode_mla_multi_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.attn_decode_mla_out.restype = I
+        L.attn_decode_mla_out.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                          I, I, I, I, I, F, P, Z, P]
+        L.attn_decode_mla_out_premerged.restype = I
+        L.attn_decode_mla_out_premerged.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                                    I, I, I, I, I, I, F, P, Z, P]
+        L.attn_decode_mla_out_workspace_bytes.restype = Z
+        L.attn_decode_mla_out_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+        L.attn_mla_premerge_weights.restype = I
+        L.attn_mla_premerge_weights.argtypes = [P, P, P, I, I, I, I, P]
+        L.attn_mla_out_form.restype = I
+        L.attn_mla_out_form.argtypes = [I, I, I, I, I, I]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -330,6 +347,47 @@ def attn_decode_mla_multi_workspace_bytes(B, q_len, h, d_c, d_R):
     return int(lib().attn_decode_mla_multi_workspace_bytes(B, q_len, h, d_c, d_R))
 
 
+def attn_decode_mla_out(out, lse, q_nope, q_rope, w_uk, w_uv, w_o, cache, s, block_table,
+                        max_blocks, block_size, num_blocks, B, q_len, s_max, h, d_c, d_R, d_nope,
+                        d_v, d_model, b, scale, workspace, workspace_bytes, stream=None,
+                        check=True):
+    rc = lib().attn_decode_mla_out(_p(out), _p(lse), _p(q_nope), _p(q_rope), _p(w_uk), _p(w_uv),
+                                   _p(w_o), _p(cache), _p(s), _p(block_table), max_blocks,
+                                   block_size, num_blocks, B, q_len, s_max, h, d_c, d_R, d_nope,
+                                   d_v, d_model, b, float(scale), _p(workspace),
+                                   int(workspace_bytes), _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_mla_out_premerged(out, lse, q_nope, q_rope, w_uk, w_absorbed, cache, s,
+                                  block_table, max_blocks, block_size, num_blocks, B, q_len,
+                                  s_max, h, d_c, d_R, d_nope, d_model, b, scale, workspace,
+                                  workspace_bytes, stream=None, check=True):
+    rc = lib().attn_decode_mla_out_premerged(_p(out), _p(lse), _p(q_nope), _p(q_rope), _p(w_uk),
+                                             _p(w_absorbed), _p(cache), _p(s), _p(block_table),
+                                             max_blocks, block_size, num_blocks, B, q_len, s_max,
+                                             h, d_c, d_R, d_nope, d_model, b, float(scale),
+                                             _p(workspace), int(workspace_bytes),
+                                             _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_mla_out_workspace_bytes(premerged, B, q_len, h, d_c, d_R, d_v, d_model):
+    return int(lib().attn_decode_mla_out_workspace_bytes(int(premerged), B, q_len, h, d_c, d_R,
+                                                         d_v, d_model))
+
+
+def attn_mla_premerge_weights(w_absorbed, w_o, w_uv, h, d_c, d_v, d_model, stream=None,
+                              check=True):
+    rc = lib().attn_mla_premerge_weights(_p(w_absorbed), _p(w_o), _p(w_uv), h, d_c, d_v, d_model,
+                                         _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_mla_out_form(B, q_len, h, d_c, d_v, d_model):
+    return int(lib().attn_mla_out_form(B, q_len, h, d_c, d_v, d_model))
+
+
 # ---------------------------------------------------------------------------
 # Convenience wrappers over torch tensors (shape bookkeeping only; they call
 # the entry points above).
@@ -465,6 +523,57 @@ def decode_mla_multi(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, blo
                                            block_size, num_blocks, B, q_len, s_max, h, d_c, d_R,
                                            d_nope, d_v, scale, wb, wn, stream)
     return out, ul, l
+
+
+def decode_mla_out(q_nope, q_rope, w_uk, w_o, cache, s, w_uv=None, w_absorbed=None,
+                   block_table=None, block_size=16, s_max=None, scale=0.0, workspace=None,
+                   stream=None):
+    """MLA decode through the output projection: q_nope [B,h,d_nope] or
+    [B,q_len,h,d_nope] (likewise q_rope).  Deferred form with w_uv and w_o
+    [d_model, h d_v]; merged form with w_absorbed [d_model, h d_c] (from
+    premerge_weights).  Returns (out [B,(q_len,)d_model] bf16, lse)."""
+    import torch
+    multi = q_nope.dim() == 4
+    if not multi:
+        q_nope, q_rope = q_nope[:, None], q_rope[:, None]
+    B, q_len, h, d_nope = q_nope.shape
+    d_R = q_rope.shape[3]
+    d_c = w_uk.shape[2]
+    merged = w_absorbed is not None
+    d_model = (w_absorbed if merged else w_o).shape[0]
+    d_v = 0 if merged else w_uv.shape[1]
+    if block_table is None:
+        s_max = cache.shape[1] if s_max is None else s_max
+        max_blocks, num_blocks = 0, 0
+    else:
+        max_blocks, num_blocks = block_table.shape[1], cache.shape[0]
+        s_max = max_blocks * block_size if s_max is None else s_max
+    dev = q_nope.device
+    out = torch.empty((B, q_len, d_model), dtype=torch.bfloat16, device=dev)
+    l = torch.empty((B, q_len, h), dtype=torch.float32, device=dev)
+    ws = workspace or Workspace(dev)
+    wb, wn = ws.get(attn_decode_mla_out_workspace_bytes(merged, B, q_len, h, d_c, d_R, d_v,
+                                                        d_model))
+    if merged:
+        attn_decode_mla_out_premerged(out, l, q_nope, q_rope, w_uk, w_absorbed, cache, s,
+                                      block_table, max_blocks, block_size, num_blocks, B, q_len,
+                                      s_max, h, d_c, d_R, d_nope, d_model, 2, scale, wb, wn,
+                                      stream)
+    else:
+        attn_decode_mla_out(out, l, q_nope, q_rope, w_uk, w_uv, w_o, cache, s, block_table,
+                            max_blocks, block_size, num_blocks, B, q_len, s_max, h, d_c, d_R,
+                            d_nope, d_v, d_model, 2, scale, wb, wn, stream)
+    return (out, l) if multi else (out[:, 0], l[:, 0])
+
+
+def premerge_weights(w_o, w_uv, stream=None):
+    """W_abs [d_model, h d_c] = W_O^i W_UV[i] side by side (bf16)."""
+    import torch
+    h, d_v, d_c = w_uv.shape
+    d_model = w_o.shape[0]
+    w_abs = torch.empty((d_model, h * d_c), dtype=torch.bfloat16, device=w_o.device)
+    attn_mla_premerge_weights(w_abs, w_o, w_uv, h, d_c, d_v, d_model, stream)
+    return w_abs
 
 
 def merge_partials(o_parts, lse_parts, out_dtype=None, lse=True, stream=None):

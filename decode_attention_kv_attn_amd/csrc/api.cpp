@@ -459,15 +459,19 @@ namespace {
 // Shared body of the MLA entry points: b = 2 (bf16 cache) or b = 1 (E4M3
 // cache codes with a latent and a rotary scale); q_len new tokens per
 // sequence, each (sequence, position) pair one query row of the kernels.
+// out == nullptr (only with u_bf16): no value up-projection; u~ leaves as
+// bf16 [B q_len, h, d_c] in u_bf16 and w_uv, d_v are unused.
 int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const void* q_rope,
                const void* w_uk, const void* w_uv, const void* cache, float c_scale,
                float r_scale, const int32_t* s, const int32_t* block_table, int max_blocks,
                int block_size, int num_blocks, int B, int q_len, int s_max, int h, int d_c,
                int d_R, int d_nope, int d_v, int b, float scale, void* workspace,
-               size_t workspace_bytes, void* stream)
+               size_t workspace_bytes, void* stream, uint16_t* u_bf16 = nullptr)
 {
-    if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s)
+    const bool up = out != nullptr;
+    if ((!up && !u_bf16) || !q_nope || !q_rope || !w_uk || (up && !w_uv) || !cache || !s)
         return fail(ATTN_EINVAL, "null out, q_nope, q_rope, w_uk, w_uv, cache or s");
+    if (!up) d_v = 16;   // unused
     if (B < 0 || h <= 0 || d_c <= 0 || d_R < 0 || d_nope <= 0 || d_v <= 0 || s_max < 0)
         return fail(ATTN_EINVAL, "bad sizes");
     if (q_len < 1 || q_len > kMlaMaxQLen)
@@ -524,6 +528,7 @@ int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const
     p.f8 = b == 1;
     p.c_scale = c_scale;
     p.r_scale = r_scale;
+    p.u_bf16 = u_bf16;
     hipError_t e = attn::launch_mla(p, block_table != nullptr, (hipStream_t)stream);
     if (e == hipErrorNotSupported) return fail(ATTN_ENOTSUP, "MLA kernels not built");
     if (e != hipSuccess) return hip_fail(e, "attn_decode_mla_absorbed launch");
@@ -598,6 +603,178 @@ size_t attn_decode_mla_multi_workspace_bytes(int B, int q_len, int h, int d_c, i
     if (B <= 0 || q_len < 1 || q_len > kMlaMaxQLen || h <= 0 || d_c <= 0 || d_R < 0) return 0;
     if ((long long)B * q_len >= (1LL << 24)) return 0;
     return plan_mla(B * q_len, h, d_c, d_R).ws_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- MLA output projection ------------------------------------------------
+// Y [rows, d_model] = X [rows, K] W^T, K = h d_v (deferred: X = the heads'
+// outputs, W = W_O) or h d_c (merged: X = bf16 u~, W = W_abs).  The K range
+// is split over workgroups until about kProjWgTarget of them exist (4 per
+// CU: the stream over W then has enough loads in flight), each wavefront
+// keeping at least two 128-wide K steps.
+#ifndef ATTN_PROJ_WG_TARGET
+#define ATTN_PROJ_WG_TARGET 1024
+#endif
+constexpr int kProjWgTarget = ATTN_PROJ_WG_TARGET;
+
+int proj_splits(int rows, int d_model, int K)
+{
+    const long long mblk = rows <= 32 ? 1 : cdiv(rows, 64);
+    const long long wg = (long long)(d_model / 32) * mblk;
+    const long long steps = K / 128;
+    long long ks = cdiv(kProjWgTarget, wg);
+    ks = ks < steps / 8 ? ks : steps / 8;
+    return (int)(ks < 1 ? 1 : ks);
+}
+
+struct OutPlan {
+    MlaPlan mla;
+    int ks;
+    size_t x_bytes, part_bytes, ws_bytes;
+};
+
+OutPlan plan_out(bool merged, int rows, int h, int d_c, int d_R, int d_v, int d_model)
+{
+    OutPlan P{};
+    P.mla = plan_mla(rows, h, d_c, d_R);
+    const int K = merged ? h * d_c : h * d_v;
+    P.ks = proj_splits(rows, d_model, K);
+    P.x_bytes = align256((size_t)rows * K * 2);
+    P.part_bytes = P.ks > 1 ? align256((size_t)P.ks * rows * d_model * 4) : 0;
+    P.ws_bytes = P.mla.ws_bytes + P.x_bytes + P.part_bytes;
+    return P;
+}
+
+int check_out_sizes(bool merged, int B, int q_len, int h, int d_c, int d_v, int d_model)
+{
+    if (B < 0 || q_len < 1 || q_len > kMlaMaxQLen || h <= 0 || d_c <= 0 || d_model <= 0 ||
+        (!merged && d_v <= 0))
+        return fail(ATTN_EINVAL, "bad sizes");
+    if (d_model % 32 != 0)
+        return fail(ATTN_ENOTSUP, "d_model must be a multiple of 32 (got %d)", d_model);
+    const long long K = merged ? (long long)h * d_c : (long long)h * d_v;
+    if (K % 128 != 0) return fail(ATTN_ENOTSUP, "h * %s must be a multiple of 128",
+                                  merged ? "d_c" : "d_v");
+    if ((long long)B * q_len * K * 2 + 2 * K >= (1LL << 31) ||
+        (long long)d_model * K * 2 >= (1LL << 32))
+        return fail(ATTN_ENOTSUP, "problem too large for one launch");
+    return ATTN_OK;
+}
+
+// Shared body of the two output-path entry points.
+int decode_mla_out(bool merged, void* out, float* lse, const void* q_nope, const void* q_rope,
+                   const void* w_uk, const void* w_uv, const void* w_proj, const void* cache,
+                   const int32_t* s, const int32_t* block_table, int max_blocks, int block_size,
+                   int num_blocks, int B, int q_len, int s_max, int h, int d_c, int d_R,
+                   int d_nope, int d_v, int d_model, int b, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream)
+{
+    if (!out || !w_proj) return fail(ATTN_EINVAL, "null out or projection weight");
+    if (b != 2) return fail(ATTN_ENOTSUP, "MLA supports bf16 storage only (b=2)");
+    int rc = check_out_sizes(merged, B, q_len, h, d_c, d_v, d_model);
+    if (rc) return rc;
+    if (B == 0) return ATTN_OK;
+    const int rows = B * q_len;
+    const OutPlan P = plan_out(merged, rows, h, d_c, d_R, d_v, d_model);
+    if (!workspace || workspace_bytes < P.ws_bytes)
+        return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    char* ws = (char*)workspace;
+    uint16_t* x = (uint16_t*)(ws + P.mla.ws_bytes);
+    rc = decode_mla(merged ? nullptr : (void*)x, nullptr, lse, q_nope, q_rope, w_uk,
+                    merged ? nullptr : w_uv, cache, 1.f, 1.f, s, block_table, max_blocks,
+                    block_size, num_blocks, B, q_len, s_max, h, d_c, d_R, d_nope, d_v, b, scale,
+                    workspace, P.mla.ws_bytes, stream, merged ? x : nullptr);
+    if (rc) return rc;
+    attn::ProjParams pp{};
+    pp.x = x;
+    pp.w = (const uint16_t*)w_proj;
+    pp.y = out;
+    pp.part = P.ks > 1 ? (float*)(ws + P.mla.ws_bytes + P.x_bytes) : nullptr;
+    pp.M = rows;
+    pp.N = d_model;
+    pp.K = merged ? h * d_c : h * d_v;
+    pp.ks = P.ks;
+    pp.y_f32 = 0;
+    hipError_t e = attn::launch_proj(pp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "MLA output projection launch");
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_mla_out(void* out, float* lse, const void* q_nope, const void* q_rope,
+                        const void* w_uk, const void* w_uv, const void* w_o, const void* cache,
+                        const int32_t* s, const int32_t* block_table, int max_blocks,
+                        int block_size, int num_blocks, int B, int q_len, int s_max, int h,
+                        int d_c, int d_R, int d_nope, int d_v, int d_model, int b, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    return decode_mla_out(false, out, lse, q_nope, q_rope, w_uk, w_uv, w_o, cache, s,
+                          block_table, max_blocks, block_size, num_blocks, B, q_len, s_max, h,
+                          d_c, d_R, d_nope, d_v, d_model, b, scale, workspace, workspace_bytes,
+                          stream);
+}
+
+int attn_decode_mla_out_premerged(void* out, float* lse, const void* q_nope, const void* q_rope,
+                                  const void* w_uk, const void* w_absorbed, const void* cache,
+                                  const int32_t* s, const int32_t* block_table, int max_blocks,
+                                  int block_size, int num_blocks, int B, int q_len, int s_max,
+                                  int h, int d_c, int d_R, int d_nope, int d_model, int b,
+                                  float scale, void* workspace, size_t workspace_bytes,
+                                  void* stream)
+{
+    return decode_mla_out(true, out, lse, q_nope, q_rope, w_uk, nullptr, w_absorbed, cache, s,
+                          block_table, max_blocks, block_size, num_blocks, B, q_len, s_max, h,
+                          d_c, d_R, d_nope, 0, d_model, b, scale, workspace, workspace_bytes,
+                          stream);
+}
+
+size_t attn_decode_mla_out_workspace_bytes(int premerged, int B, int q_len, int h, int d_c,
+                                           int d_R, int d_v, int d_model)
+{
+    const bool merged = premerged != 0;
+    if (B <= 0 || d_R < 0) return 0;
+    const std::string keep = g_err;   // a size query leaves the error message alone
+    const int rc = check_out_sizes(merged, B, q_len, h, d_c, d_v, d_model);
+    g_err = keep;
+    if (rc) return 0;
+    return plan_out(merged, B * q_len, h, d_c, d_R, d_v, d_model).ws_bytes;
+}
+
+int attn_mla_premerge_weights(void* w_absorbed, const void* w_o, const void* w_uv, int h,
+                              int d_c, int d_v, int d_model, void* stream)
+{
+    if (!w_absorbed || !w_o || !w_uv) return fail(ATTN_EINVAL, "null weight");
+    if (h <= 0 || d_c <= 0 || d_v <= 0 || d_model <= 0) return fail(ATTN_EINVAL, "bad sizes");
+    if (d_c % 256 != 0 || d_model % 32 != 0 || d_v > 256)
+        return fail(ATTN_ENOTSUP, "premerge needs d_c %% 256 == 0, d_model %% 32 == 0, d_v <= 256");
+    if ((long long)d_model * h * d_c >= (1LL << 31))
+        return fail(ATTN_ENOTSUP, "merged weight too large");
+    attn::PremergeParams pp{w_absorbed, w_o, w_uv, h, d_c, d_v, d_model};
+    hipError_t e = attn::launch_premerge(pp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attn_mla_premerge_weights launch");
+    return ATTN_OK;
+}
+
+int attn_mla_out_form(int B, int q_len, int h, int d_c, int d_v, int d_model)
+{
+    if (B <= 0 || q_len < 1 || h <= 0 || d_c <= 0 || d_v <= 0 || d_model <= 0) return -1;
+    const double rows = (double)B * q_len;
+    // bytes and matrix-core flops of what differs between the two forms
+    const double bd = 2.0 * h * d_v * d_c + 2.0 * d_model * h * d_v + 4.0 * rows * h * d_v;
+    const double fd = 2.0 * rows * h * d_v * d_c + 2.0 * rows * d_model * h * d_v;
+    const double bm = 2.0 * d_model * h * d_c + 4.0 * rows * h * d_c;
+    const double fm = 2.0 * rows * d_model * h * d_c;
+    const double hbm = 8.0e12, mfma = 2.5e15;   // MI355X HBM3E bytes/s, dense bf16 flop/s
+    const double td = bd / hbm > fd / mfma ? bd / hbm : fd / mfma;
+    const double tm = bm / hbm > fm / mfma ? bm / hbm : fm / mfma;
+    return tm < td ? 1 : 0;
 }
 
 int attn_decode_gqa_multi(void* out, float* lse, const void* q, const void* cache_k,

@@ -62,7 +62,7 @@ hipError_t launch_append_fp8(const AppendParams& k, const AppendParams* v, int B
 // b / q_len, whose length s and block-table row it reads (q_len = 1: one
 // row per sequence)
 struct MlaParams {
-    void* out;            // [B, h, d_v] bf16
+    void* out;            // [B, h, d_v] bf16, or nullptr: no value up-projection
     float* u_latent;      // [B, h, d_c] fp32 or nullptr
     float* lse;           // [B, h] or nullptr
     const void* q_nope;   // [B, h, d_nope]
@@ -82,12 +82,34 @@ struct MlaParams {
     int q_len;            // new tokens per sequence (query rows per sequence)
     int n_wg, min_tiles;  // decode workgroups; fewest 32-token tiles per workgroup
     float scale_log2;
+    uint16_t* u_bf16;     // [B, h, d_c] bf16 u~ for the merged output projection, or nullptr
     int f8;               // cache rows are E4M3 codes (else bf16)
     float c_scale;        // FP8: scale of the latent part (1 for bf16); folded into q^ and u~
     float r_scale;        // FP8: scale of the rotary part (1 for bf16); folded into q^
 };
 
 hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st);
+
+// Y[M, N] = X[M, K] W[N, K]^T (bf16 operands, fp32 sums): the MLA output
+// projection.  N % 32 == 0, K % 128 == 0, M K 2 + 2 K < 2^31.
+struct ProjParams {
+    const uint16_t* x;   // [M, K] bf16
+    const uint16_t* w;   // [N, K] bf16
+    void* y;             // [M, N] bf16, or fp32 when y_f32
+    float* part;         // [ks, M, N] fp32 partial sums when ks > 1
+    int M, N, K, ks;     // ks: K splits over workgroups
+    int y_f32;
+};
+hipError_t launch_proj(const ProjParams& p, hipStream_t st);
+
+// W_abs[n, i d_c + c] = sum_e W_O[n, i d_v + e] W_UV[i, e, c] (bf16 in and out)
+struct PremergeParams {
+    void* w_abs;          // [d_model, h d_c]
+    const void* w_o;      // [d_model, h d_v]
+    const void* w_uv;     // [h, d_v, d_c]
+    int h, d_c, d_v, d_model;   // d_c % 256 == 0, d_model % 32 == 0, d_v <= 256
+};
+hipError_t launch_premerge(const PremergeParams& p, hipStream_t st);
 
 // merge of decode outputs over disjoint token slices
 struct MergeParams {

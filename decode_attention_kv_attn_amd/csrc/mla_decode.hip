@@ -1104,7 +1104,8 @@ __global__ __launch_bounds__(64 * kFinSeq, 4) void mla_finish_kernel(const MlaPa
     const uint16_t* __restrict__ wuv = (const uint16_t*)p.w_uv + (size_t)i * p.d_v * p.d_c;
     constexpr int kWuvPre = 8;
     bf16x8 bws[16];   // d_c = 512: 16 K steps
-    if (wave < p.d_v / 16) {
+    const bool up = p.out != nullptr;   // value up-projection wanted (else only u~ leaves)
+    if (up && wave < p.d_v / 16) {
         const uint16_t* wrow = wuv + (size_t)(wave * 16 + li) * p.d_c + 8 * G;
 #pragma unroll
         for (int k = 0; k < kWuvPre; k++) bws[k] = *(const bf16x8*)(wrow + 32 * k);
@@ -1225,7 +1226,7 @@ __global__ __launch_bounds__(64 * kFinSeq, 4) void mla_finish_kernel(const MlaPa
         }
     }
 
-    if (wave < p.d_v / 16) {
+    if (up && wave < p.d_v / 16) {
         const uint16_t* wrow = wuv + (size_t)(wave * 16 + li) * p.d_c + 8 * G;
 #pragma unroll
         for (int k = kWuvPre; k < 16; k++) bws[k] = *(const bf16x8*)(wrow + 32 * k);
@@ -1251,12 +1252,15 @@ __global__ __launch_bounds__(64 * kFinSeq, 4) void mla_finish_kernel(const MlaPa
             hi[e / 2] = h2;
             lo[e / 2] = pack_bf16x2(xs[e] - bf16lo_to_f32(h2), xs[e + 1] - bf16hi_to_f32(h2));
         }
+        if (p.u_bf16)   // bf16 u~, the X operand of the merged output projection
+            *(uint4*)(p.u_bf16 + ((size_t)bb * p.h + i) * 512 + 8 * lane) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
         *(uint4*)&Ab[wave][8 * lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
         *(uint4*)&Ab[kFinSeq + wave][8 * lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     } else {   // rows of absent sequences: zeros
         *(uint4*)&Ab[wave][8 * lane] = make_uint4(0, 0, 0, 0);
         *(uint4*)&Ab[kFinSeq + wave][8 * lane] = make_uint4(0, 0, 0, 0);
     }
+    if (!up) return;   // kernel-uniform
     __syncthreads();
 
     // out[b0 + r, i, n] = sum_c u~[r][c] W_UV[i][n][c]: wavefront w takes

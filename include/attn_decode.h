@@ -409,6 +409,81 @@ int attn_decode_mla_absorbed_multi_fp8(void* out, float* u_latent, float* lse,
 size_t attn_decode_mla_multi_workspace_bytes(int B, int q_len, int h, int d_c, int d_R);
 
 /*
+ * attn_decode_mla_out -- MLA decode through the attention block's output
+ * projection ("Multi-Head Latent Attention (MLA): Mathematical Foundations",
+ * llms.blog, section "Value Output Matrix Absorption"):
+ *   o[b,jq] = sum_i W_O^i u[b,jq,i],  u[b,jq,i] = W_UV[i] u~[b,jq,i],
+ * W_O = [W_O^1 .. W_O^h], head i owning columns i d_v .. i d_v + d_v - 1.
+ * Deferred form: the heads' outputs u (bf16, as attn_decode_mla_absorbed_multi
+ * returns them) are formed in the workspace, then one projection over all
+ * h d_v columns.
+ *   out  : [B, q_len, d_model] bf16 (q_len = 1: [B, d_model]).
+ *   lse  : [B, q_len, h] fp32 or NULL.
+ *   w_o  : [d_model, h d_v] bf16 (the layout of a linear layer's weight).
+ *   q_nope, q_rope, w_uk, w_uv, cache, table, lengths, q_len, scale: as
+ *   attn_decode_mla_absorbed_multi (the new tokens see their causal prefix).
+ *   workspace : at least attn_decode_mla_out_workspace_bytes(0, B, q_len, h,
+ *         d_c, d_R, d_v, d_model) bytes.
+ * Supported: as attn_decode_mla_absorbed_multi, plus d_model a multiple of
+ * 32 and h d_v a multiple of 128.  Others: ENOTSUP.
+ * Errors: EINVAL, ENOTSUP, EWORKSPACE, EHIP as above.
+ */
+int attn_decode_mla_out(void* out, float* lse, const void* q_nope, const void* q_rope,
+                        const void* w_uk, const void* w_uv, const void* w_o, const void* cache,
+                        const int32_t* s, const int32_t* block_table, int max_blocks,
+                        int block_size, int num_blocks, int B, int q_len, int s_max, int h,
+                        int d_c, int d_R, int d_nope, int d_v, int d_model, int b, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_mla_out_premerged -- the same output in the merged form of
+ * the same section: o[b,jq] = sum_i W_abs^i u~[b,jq,i] with the static
+ * W_abs^i = W_O^i W_UV[i] (d_model x d_c), built once by
+ * attn_mla_premerge_weights.  u~ is rounded to bf16 for the projection; the
+ * per-head d_v-wide outputs are never formed.
+ *   w_absorbed : [d_model, h d_c] bf16, head i owning columns
+ *                i d_c .. i d_c + d_c - 1.
+ *   workspace  : at least attn_decode_mla_out_workspace_bytes(1, B, q_len,
+ *                h, d_c, d_R, 0, d_model) bytes.
+ * The rest as attn_decode_mla_out (no w_uv, no d_v).  Which form moves and
+ * computes less for a shape: attn_mla_out_form.
+ */
+int attn_decode_mla_out_premerged(void* out, float* lse, const void* q_nope, const void* q_rope,
+                                  const void* w_uk, const void* w_absorbed, const void* cache,
+                                  const int32_t* s, const int32_t* block_table, int max_blocks,
+                                  int block_size, int num_blocks, int B, int q_len, int s_max,
+                                  int h, int d_c, int d_R, int d_nope, int d_model, int b,
+                                  float scale, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Workspace bytes for attn_decode_mla_out (premerged = 0) or
+ * attn_decode_mla_out_premerged (premerged = 1); 0 for invalid sizes. */
+size_t attn_decode_mla_out_workspace_bytes(int premerged, int B, int q_len, int h, int d_c,
+                                           int d_R, int d_v, int d_model);
+
+/*
+ * attn_mla_premerge_weights -- w_absorbed[n, i d_c + c] =
+ *   sum_e w_o[n, i d_v + e] w_uv[i, e, c]  (fp32 sums rounded to bf16), the
+ * static merged weight of the section above, computed on the device in one
+ * launch on `stream`.  w_absorbed [d_model, h d_c], w_o [d_model, h d_v],
+ * w_uv [h, d_v, d_c], all bf16, caller-owned.  Supported: d_c a multiple of
+ * 256, d_model a multiple of 32, d_v <= 256, d_model h d_c < 2^31.
+ * Errors: EINVAL (null, bad sizes), ENOTSUP, EHIP.
+ */
+int attn_mla_premerge_weights(void* w_absorbed, const void* w_o, const void* w_uv, int h,
+                              int d_c, int d_v, int d_model, void* stream);
+
+/*
+ * attn_mla_out_form -- which output form is cheaper for a shape, by the
+ * bytes and matrix-core work in which the two differ (deferred: W_UV, W_O
+ * and the heads' outputs; merged: W_abs and bf16 u~), each priced at the
+ * MI355X HBM and dense bf16 peaks: 0 deferred, 1 merged, -1 bad sizes.
+ * With d_c > d_v (DeepSeek: 512 vs 128) the merged weight is d_c / d_v
+ * times larger than W_O and the deferred form always wins.
+ */
+int attn_mla_out_form(int B, int q_len, int h, int d_c, int d_v, int d_model);
+
+/*
  * kv_cache_append_mla_fp8 -- append one latent row per sequence to an FP8
  * latent cache: element x of kv_new[b] ([B, d_c + d_R] bf16, [c | k_R]) is
  * stored as the E4M3 code of x * (1 / c_scale) in the latent part and of

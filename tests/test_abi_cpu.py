@@ -209,3 +209,47 @@ def test_mla_fp8_and_fp8_append_argument_errors():
               h_kv=2, d_h=64, stream=0, check=False)
     assert A.kv_cache_append_fp8(**{**fk, "v_scale": -2.0}) == A.ATTN_EINVAL
     assert A.kv_cache_append_fp8(**{**fk, "v_new": None}) == A.ATTN_EINVAL
+
+
+def test_mla_multi_and_output_path_argument_errors_and_workspace():
+    mk = dict(out=FAKE, u_latent=None, lse=None, q_nope=FAKE, q_rope=FAKE, w_uk=FAKE, w_uv=FAKE,
+              cache=FAKE, s=FAKE, block_table=None, max_blocks=0, block_size=16, num_blocks=0,
+              B=2, q_len=2, s_max=64, h=128, d_c=512, d_R=64, d_nope=128, d_v=128, b=2,
+              scale=0.0, workspace=None, workspace_bytes=0, stream=0, check=False)
+    assert A.attn_decode_mla_absorbed_multi(**{**mk, "q_len": 0}) == A.ATTN_EINVAL
+    assert A.attn_decode_mla_absorbed_multi(**{**mk, "q_len": 17}) == A.ATTN_EINVAL
+    assert A.attn_decode_mla_absorbed_multi(**mk) == A.ATTN_EWORKSPACE
+    # q_len = 1 needs exactly the single-token workspace
+    assert (A.attn_decode_mla_multi_workspace_bytes(4, 1, 128, 512, 64)
+            == A.attn_decode_workspace_bytes(1, 4, 64, 128, 1, 512, 64))
+    assert (A.attn_decode_mla_multi_workspace_bytes(4, 3, 128, 512, 64)
+            == A.attn_decode_workspace_bytes(1, 12, 64, 128, 1, 512, 64))
+    ok = dict(out=FAKE, lse=None, q_nope=FAKE, q_rope=FAKE, w_uk=FAKE, w_uv=FAKE, w_o=FAKE,
+              cache=FAKE, s=FAKE, block_table=None, max_blocks=0, block_size=16, num_blocks=0,
+              B=2, q_len=1, s_max=64, h=128, d_c=512, d_R=64, d_nope=128, d_v=128, d_model=5120,
+              b=2, scale=0.0, workspace=None, workspace_bytes=0, stream=0, check=False)
+    assert A.attn_decode_mla_out(**{**ok, "d_model": 100}) == A.ATTN_ENOTSUP
+    assert A.attn_decode_mla_out(**{**ok, "w_o": None}) == A.ATTN_EINVAL
+    assert A.attn_decode_mla_out(**{**ok, "b": 4}) == A.ATTN_ENOTSUP
+    assert A.attn_decode_mla_out(**ok) == A.ATTN_EWORKSPACE
+    assert A.attn_decode_mla_out(**{**ok, "B": 0}) == A.ATTN_OK
+    wd = A.attn_decode_mla_out_workspace_bytes(0, 32, 1, 128, 512, 64, 128, 5120)
+    wm = A.attn_decode_mla_out_workspace_bytes(1, 32, 1, 128, 512, 64, 0, 5120)
+    base = A.attn_decode_workspace_bytes(1, 32, 64, 128, 1, 512, 64)
+    assert wd >= base + 32 * 128 * 128 * 2 and wm >= base + 32 * 128 * 512 * 2
+    assert A.attn_decode_mla_out_workspace_bytes(0, 32, 1, 128, 512, 64, 128, 100) == 0
+    pm = dict(w_absorbed=FAKE, w_o=FAKE, w_uv=FAKE, h=128, d_c=512, d_v=128, d_model=5120,
+              stream=0, check=False)
+    assert A.attn_mla_premerge_weights(**{**pm, "w_uv": None}) == A.ATTN_EINVAL
+    assert A.attn_mla_premerge_weights(**{**pm, "d_c": 320}) == A.ATTN_ENOTSUP
+    assert A.attn_mla_premerge_weights(**{**pm, "d_v": 512}) == A.ATTN_ENOTSUP
+
+
+def test_output_form_choice():
+    # DeepSeek shapes: the merged weight is d_c / d_v = 4 times W_O, so the
+    # deferred form moves less at every batch size
+    for B in (1, 32, 1024):
+        assert A.attn_mla_out_form(B, 1, 128, 512, 128, 5120) == 0
+    # a latent narrower than the value heads: the merged weight is the smaller one
+    assert A.attn_mla_out_form(32, 1, 8, 64, 128, 4096) == 1
+    assert A.attn_mla_out_form(0, 1, 8, 64, 128, 4096) == -1

@@ -355,6 +355,55 @@ def run_mla_out(name, merged, steps, warmup, rotate, d_model=5120):
     return sh, total_ms, per
 
 
+def run_mla_mode(mha, B, s, q_len, steps, warmup, h=128, seed=77):
+    """One MLA layer (d_c 512, d_R 64, d_nope = d_v = 128, bf16 latent cache)
+    with q_len new tokens per sequence, in MHA mode (explicit per-head K/V)
+    or in the absorbed (MQA) mode."""
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = synth.MlaShape("mode", B=B, h=h, d_c=512, d_R=64, d_nope=128, d_v=128,
+                        s=tuple([s] * B), seed=seed, q_len=q_len)
+    d = synth.draw_mla(sh, device="cuda")
+    qn = d["q_nope"] if q_len > 1 else d["q_nope"][:, None]
+    qr = d["q_rope"] if q_len > 1 else d["q_rope"][:, None]
+    out = torch.empty((B, q_len, h, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, q_len, h), dtype=torch.float32, device="cuda")
+    if mha:
+        wsb = A.attn_decode_mla_mha_workspace_bytes(B, s, h)
+    else:
+        wsb = A.attn_decode_mla_multi_workspace_bytes(B, q_len, h, 512, 64)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def call():
+        if mha:
+            A.attn_decode_mla_mha(out, lse, qn, qr, d["w_uk"], d["w_uv"], d["cache"], d["s"], None,
+                                  0, 16, 0, B, q_len, s, h, 512, 64, 128, 128, 2, 0.0, ws, wsb, sp)
+        else:
+            A.attn_decode_mla_absorbed_multi(out, None, lse, qn, qr, d["w_uk"], d["w_uv"],
+                                             d["cache"], d["s"], None, 0, 16, 0, B, q_len, s, h,
+                                             512, 64, 128, 128, 2, 0.0, ws, wsb, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    del ws, d
+    torch.cuda.empty_cache()
+    return total_ms / steps
+
+
+def mla_modes(args):
+    """Absorbed (MQA) mode vs MHA mode over query-block length and context."""
+    for s in (2048, 8192):
+        for ql in (1, 4, 16, 64, 256, 1024):
+            steps = max(3, min(args.steps, int(2000 / ql)))
+            ta = run_mla_mode(False, args.modes_batch, s, ql, steps, 2)
+            tm = run_mla_mode(True, args.modes_batch, s, ql, steps, 2)
+            print(f"mla-mode B={args.modes_batch} s={s:5d} q_len={ql:4d}  absorbed {ta * 1e3:10.1f} us"
+                  f"  mha {tm * 1e3:10.1f} us  faster: {'mha' if tm < ta else 'absorbed'}",
+                  flush=True)
+
+
 def run_mla_fp8(name, steps, warmup, rotate, c_scale=1.0 / 32, r_scale=1.0 / 32):
     """The MLA workload with its latent cache stored as E4M3 codes."""
     import torch
@@ -597,6 +646,9 @@ def main():
     ap.add_argument("--no-dcp", action="store_true")
     ap.add_argument("--no-multi", action="store_true")
     ap.add_argument("--no-out", action="store_true", help="skip the MLA output-projection legs")
+    ap.add_argument("--mla-modes", action="store_true",
+                    help="instead of the JSON line: MLA absorbed vs MHA mode over q_len and context")
+    ap.add_argument("--modes-batch", type=int, default=4)
     ap.add_argument("--q-len", type=int, default=4, help="drafted tokens in the multi-token leg")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the JSON line: one line per named workload (all GQA/MQA/MHA and "
@@ -628,6 +680,9 @@ def main():
     A.lib()
     if args.sweep:
         sweep(args)
+        return
+    if args.mla_modes:
+        mla_modes(args)
         return
 
     if args.calib_copy:   # a plain copy of known size, for the counter calibration

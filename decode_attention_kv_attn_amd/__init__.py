@@ -44,6 +44,8 @@ EXPORTED = (
     "attn_decode_mla_out_workspace_bytes",
     "attn_mla_premerge_weights",
     "attn_mla_out_form",
+    "attn_decode_mla_mha",
+    "attn_decode_mla_mha_workspace_bytes",
 )
 
 _lib = None
@@ -128,6 +130,11 @@ def lib():
         L.attn_mla_premerge_weights.argtypes = [P, P, P, I, I, I, I, P]
         L.attn_mla_out_form.restype = I
         L.attn_mla_out_form.argtypes = [I, I, I, I, I, I]
+        L.attn_decode_mla_mha.restype = I
+        L.attn_decode_mla_mha.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
+                                          I, I, I, F, P, Z, P]
+        L.attn_decode_mla_mha_workspace_bytes.restype = Z
+        L.attn_decode_mla_mha_workspace_bytes.argtypes = [I, I, I]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -388,6 +395,21 @@ def attn_mla_out_form(B, q_len, h, d_c, d_v, d_model):
     return int(lib().attn_mla_out_form(B, q_len, h, d_c, d_v, d_model))
 
 
+def attn_decode_mla_mha(out, lse, q_nope, q_rope, w_uk, w_uv, cache, s, block_table, max_blocks,
+                        block_size, num_blocks, B, q_len, s_max, h, d_c, d_R, d_nope, d_v, b,
+                        scale, workspace, workspace_bytes, stream=None, check=True):
+    rc = lib().attn_decode_mla_mha(_p(out), _p(lse), _p(q_nope), _p(q_rope), _p(w_uk), _p(w_uv),
+                                   _p(cache), _p(s), _p(block_table), max_blocks, block_size,
+                                   num_blocks, B, q_len, s_max, h, d_c, d_R, d_nope, d_v, b,
+                                   float(scale), _p(workspace), int(workspace_bytes),
+                                   _stream(stream))
+    return _check(rc) if check else rc
+
+
+def attn_decode_mla_mha_workspace_bytes(B, s_max, h):
+    return int(lib().attn_decode_mla_mha_workspace_bytes(B, s_max, h))
+
+
 # ---------------------------------------------------------------------------
 # Convenience wrappers over torch tensors (shape bookkeeping only; they call
 # the entry points above).
@@ -564,6 +586,32 @@ def decode_mla_out(q_nope, q_rope, w_uk, w_o, cache, s, w_uv=None, w_absorbed=No
                             max_blocks, block_size, num_blocks, B, q_len, s_max, h, d_c, d_R,
                             d_nope, d_v, d_model, 2, scale, wb, wn, stream)
     return (out, l) if multi else (out[:, 0], l[:, 0])
+
+
+def decode_mla_mha(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_size=16,
+                   s_max=None, scale=0.0, workspace=None, stream=None):
+    """MLA in MHA mode (explicit per-head K/V): q_nope [B,q_len,h,128],
+    q_rope [B,q_len,h,64].  Returns (out [B,q_len,h,128] bf16, lse [B,q_len,h])."""
+    import torch
+    B, q_len, h, d_nope = q_nope.shape
+    d_R = q_rope.shape[3]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    if block_table is None:
+        s_max = cache.shape[1] if s_max is None else s_max
+        max_blocks, num_blocks = 0, 0
+    else:
+        max_blocks, num_blocks = block_table.shape[1], cache.shape[0]
+        s_max = max_blocks * block_size if s_max is None else s_max
+    dev = q_nope.device
+    out = torch.empty((B, q_len, h, d_v), dtype=torch.bfloat16, device=dev)
+    l = torch.empty((B, q_len, h), dtype=torch.float32, device=dev)
+    ws = workspace or Workspace(dev)
+    wb, wn = ws.get(attn_decode_mla_mha_workspace_bytes(B, s_max, h))
+    attn_decode_mla_mha(out, l, q_nope, q_rope, w_uk, w_uv, cache, s, block_table, max_blocks,
+                        block_size, num_blocks, B, q_len, s_max, h, d_c, d_R, d_nope, d_v, 2,
+                        scale, wb, wn, stream)
+    return out, l
 
 
 def premerge_weights(w_o, w_uv, stream=None):

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_decode.so")
-SOURCES = ["api.cpp", "append.hip", "gqa_decode.hip", "gqa_mfma.hip", "mla_decode.hip", "mla_output.hip", "merge.hip", "noalloc.hip", "stream_probe.hip"]
+SOURCES = ["api.cpp", "append.hip", "gqa_decode.hip", "gqa_mfma.hip", "mla_decode.hip", "mla_output.hip", "mla_mha.hip", "merge.hip", "noalloc.hip", "stream_probe.hip"]
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 HIP_FLAGS = [

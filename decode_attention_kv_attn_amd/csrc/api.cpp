@@ -141,7 +141,7 @@ GqaPlan plan_gqa(int B, int s_max, int h, int h_kv, int d_h, int b, int q_len = 
 // leaves one partial per sequence it touches, so n_wg + B - 1 partial slots
 // cover every schedule.
 // new tokens per sequence that one multi-token MLA call takes
-constexpr int kMlaMaxQLen = 16;
+constexpr int kMlaMaxQLen = 1024;
 
 struct MlaPlan {
     int n_wg, min_tiles;
@@ -759,6 +759,61 @@ int attn_mla_premerge_weights(void* w_absorbed, const void* w_o, const void* w_u
     attn::PremergeParams pp{w_absorbed, w_o, w_uv, h, d_c, d_v, d_model};
     hipError_t e = attn::launch_premerge(pp, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attn_mla_premerge_weights launch");
+    return ATTN_OK;
+}
+
+size_t attn_decode_mla_mha_workspace_bytes(int B, int s_max, int h)
+{
+    if (B <= 0 || s_max <= 0 || h <= 0) return 0;
+    return 2 * align256((size_t)B * s_max * h * 128 * 2);
+}
+
+int attn_decode_mla_mha(void* out, float* lse, const void* q_nope, const void* q_rope,
+                        const void* w_uk, const void* w_uv, const void* cache, const int32_t* s,
+                        const int32_t* block_table, int max_blocks, int block_size,
+                        int num_blocks, int B, int q_len, int s_max, int h, int d_c, int d_R,
+                        int d_nope, int d_v, int b, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream)
+{
+    if (!out || !q_nope || !q_rope || !w_uk || !w_uv || !cache || !s)
+        return fail(ATTN_EINVAL, "null out, q_nope, q_rope, w_uk, w_uv, cache or s");
+    if (B < 0 || q_len < 1 || h <= 0 || s_max <= 0)
+        return fail(ATTN_EINVAL, "bad sizes");
+    if (b != 2) return fail(ATTN_ENOTSUP, "MHA mode supports bf16 storage only (b=2)");
+    if (d_c != 512 || d_R != 64 || d_nope != 128 || d_v != 128)
+        return fail(ATTN_ENOTSUP, "MHA mode supports d_c=512, d_R=64, d_nope=d_v=128");
+    int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
+    if (rc) return rc;
+    if ((long long)B * q_len * h >= (1LL << 31) || (long long)B * s_max >= (1LL << 31))
+        return fail(ATTN_ENOTSUP, "problem too large for one launch");
+    if (B == 0) return ATTN_OK;
+    const size_t need = attn_decode_mla_mha_workspace_bytes(B, s_max, h);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    attn::MhaParams p{};
+    p.out = out;
+    p.lse = lse;
+    p.q_nope = q_nope;
+    p.q_rope = q_rope;
+    p.w_uk = w_uk;
+    p.w_uv = w_uv;
+    p.cache = cache;
+    p.s = s;
+    p.bt = block_table;
+    p.k_exp = (uint16_t*)workspace;
+    p.v_exp = (uint16_t*)((char*)workspace + need / 2);
+    p.max_blocks = max_blocks;
+    p.bs_log2 = block_table ? ilog2(block_size) : 0;
+    p.num_blocks = num_blocks;
+    p.B = B;
+    p.q_len = q_len;
+    p.s_max = s_max;
+    p.h = h;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)(d_nope + d_R));
+    p.scale_log2 = sc * 1.4426950408889634f;
+    hipError_t e = attn::launch_mla_mha(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attn_decode_mla_mha launch");
     return ATTN_OK;
 }
 

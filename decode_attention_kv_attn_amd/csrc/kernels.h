@@ -111,6 +111,25 @@ struct PremergeParams {
 };
 hipError_t launch_premerge(const PremergeParams& p, hipStream_t st);
 
+// MLA in MHA mode: explicit per-head K/V (d_c = 512, d_R = 64, d_nope = d_v = 128)
+struct MhaParams {
+    void* out;             // [B, q_len, h, 128] bf16
+    float* lse;            // [B, q_len, h] or nullptr
+    const void* q_nope;    // [B, q_len, h, 128]
+    const void* q_rope;    // [B, q_len, h, 64]
+    const void* w_uk;      // [h, 128, 512]
+    const void* w_uv;      // [h, 128, 512]
+    const void* cache;     // rows [c (512) | k_R (64)] bf16
+    const int32_t* s;
+    const int32_t* bt;     // nullptr: contiguous [B, s_max, 576]
+    uint16_t* k_exp;       // [B, s_max, h, 128]: W_UK[i] c
+    uint16_t* v_exp;       // [B, s_max, h, 128]: W_UV[i] c
+    int max_blocks, bs_log2, num_blocks;
+    int B, q_len, s_max, h;
+    float scale_log2;
+};
+hipError_t launch_mla_mha(const MhaParams& p, hipStream_t st);
+
 // merge of decode outputs over disjoint token slices
 struct MergeParams {
     void* out;               // [rows, d] bf16 or fp32

@@ -379,8 +379,10 @@ int attn_decode_mla_absorbed_fp8(void* out, float* u_latent, float* lse, const v
  *   workspace: at least attn_decode_mla_multi_workspace_bytes(B, q_len, h,
  *              d_c, d_R) bytes.
  * Each (sequence, position) pair is one query row of the kernels, so q_len
- * = 1 is attn_decode_mla_absorbed exactly.  Supported: 1 <= q_len <= 16
- * (else EINVAL), B * q_len < 2^24, the rest as attn_decode_mla_absorbed.
+ * = 1 is attn_decode_mla_absorbed exactly; each row streams its visible
+ * latent rows once (later rows of a sequence mostly from cache).
+ * Supported: 1 <= q_len <= 1024 (else EINVAL), B * q_len < 2^24, the rest
+ * as attn_decode_mla_absorbed.
  * Errors: as attn_decode_mla_absorbed.
  */
 int attn_decode_mla_absorbed_multi(void* out, float* u_latent, float* lse, const void* q_nope,
@@ -472,6 +474,35 @@ size_t attn_decode_mla_out_workspace_bytes(int premerged, int B, int q_len, int 
  */
 int attn_mla_premerge_weights(void* w_absorbed, const void* w_o, const void* w_uv, int h,
                               int d_c, int d_v, int d_model, void* stream);
+
+/*
+ * attn_decode_mla_mha -- the same result as attn_decode_mla_absorbed_multi
+ * (out and lse; no u~) computed in "MHA mode": every cached token's per-head
+ * key and value are expanded explicitly, K_n[b,t,i] = W_UK[i] c_t and
+ * V[b,t,i] = W_UV[i] c_t (bf16, in the workspace), and attention runs as
+ * plain multi-head attention with key [K_n | k_R] ("MLA: why one latent can
+ * replace a multi-head KV cache", charlestar.github.io, section on MHA mode
+ * and MQA mode being execution forms (by gloss): the form for long query
+ * blocks; llms.blog MLA page, "Low-Rank Joint Key-Value Compression" and
+ * "The Decoupled RoPE Solution" for the expansion).  The expansion costs
+ * 2 d_c h (d_nope + d_v) flops per cached token whatever q_len is, so this
+ * form wins only for long query blocks; attn_mla_mode says which.
+ *   Arguments as attn_decode_mla_absorbed_multi without u_latent; any
+ *   q_len >= 1; s_max bounds every s[b] (paged caches too).
+ *   workspace: at least attn_decode_mla_mha_workspace_bytes(B, s_max, h)
+ *   bytes (the expanded K_n and V, [B, s_max, h, 128] each).
+ * Supported: b = 2, d_c = 512, d_R = 64, d_nope = d_v = 128.  Others:
+ * ENOTSUP.  Errors: EINVAL, ENOTSUP, EWORKSPACE, EHIP as above.
+ */
+int attn_decode_mla_mha(void* out, float* lse, const void* q_nope, const void* q_rope,
+                        const void* w_uk, const void* w_uv, const void* cache, const int32_t* s,
+                        const int32_t* block_table, int max_blocks, int block_size,
+                        int num_blocks, int B, int q_len, int s_max, int h, int d_c, int d_R,
+                        int d_nope, int d_v, int b, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for attn_decode_mla_mha; 0 for invalid sizes. */
+size_t attn_decode_mla_mha_workspace_bytes(int B, int s_max, int h);
 
 /*
  * attn_mla_out_form -- which output form is cheaper for a shape, by the

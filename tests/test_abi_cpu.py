@@ -217,7 +217,7 @@ def test_mla_multi_and_output_path_argument_errors_and_workspace():
               B=2, q_len=2, s_max=64, h=128, d_c=512, d_R=64, d_nope=128, d_v=128, b=2,
               scale=0.0, workspace=None, workspace_bytes=0, stream=0, check=False)
     assert A.attn_decode_mla_absorbed_multi(**{**mk, "q_len": 0}) == A.ATTN_EINVAL
-    assert A.attn_decode_mla_absorbed_multi(**{**mk, "q_len": 17}) == A.ATTN_EINVAL
+    assert A.attn_decode_mla_absorbed_multi(**{**mk, "q_len": 1025}) == A.ATTN_EINVAL
     assert A.attn_decode_mla_absorbed_multi(**mk) == A.ATTN_EWORKSPACE
     # q_len = 1 needs exactly the single-token workspace
     assert (A.attn_decode_mla_multi_workspace_bytes(4, 1, 128, 512, 64)

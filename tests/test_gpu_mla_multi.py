@@ -107,13 +107,13 @@ def test_q_len_bounds_rejected():
     sh = shape(1, 16, (40,), 2, seed=25)
     d = synth.draw_mla(sh, device=DEV)
     B, h = 1, 16
-    out = torch.empty((B, 17, h, 128), dtype=torch.bfloat16, device=DEV)
-    for q_len in (0, 17):
+    out = torch.empty((B, 2, h, 128), dtype=torch.bfloat16, device=DEV)
+    for q_len in (0, 1025):
         rc = A.attn_decode_mla_absorbed_multi(out, None, None, out, out, d["w_uk"], d["w_uv"],
                                               d["cache"], d["s"], None, 0, 16, 0, B, q_len, 40,
                                               h, 512, 64, 128, 128, 2, 0.0, None, 0, check=False)
         assert rc == A.ATTN_EINVAL
-    assert A.attn_decode_mla_multi_workspace_bytes(B, 17, h, 512, 64) == 0
+    assert A.attn_decode_mla_multi_workspace_bytes(B, 1025, h, 512, 64) == 0
 
 
 def test_deepseek_v3_full_size_two_tokens_sampled():

@@ -46,6 +46,7 @@ EXPORTED = (
     "attn_mla_out_form",
     "attn_decode_mla_mha",
     "attn_decode_mla_mha_workspace_bytes",
+    "attn_mla_mode",
 )
 
 _lib = None
@@ -135,6 +136,8 @@ def lib():
                                           I, I, I, F, P, Z, P]
         L.attn_decode_mla_mha_workspace_bytes.restype = Z
         L.attn_decode_mla_mha_workspace_bytes.argtypes = [I, I, I]
+        L.attn_mla_mode.restype = I
+        L.attn_mla_mode.argtypes = [I, I]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -408,6 +411,10 @@ def attn_decode_mla_mha(out, lse, q_nope, q_rope, w_uk, w_uv, cache, s, block_ta
 
 def attn_decode_mla_mha_workspace_bytes(B, s_max, h):
     return int(lib().attn_decode_mla_mha_workspace_bytes(B, s_max, h))
+
+
+def attn_mla_mode(q_len, s):
+    return int(lib().attn_mla_mode(q_len, s))
 
 
 # ---------------------------------------------------------------------------

@@ -817,6 +817,20 @@ int attn_decode_mla_mha(void* out, float* lse, const void* q_nope, const void* q
     return ATTN_OK;
 }
 
+int attn_mla_mode(int q_len, int s)
+{
+    if (q_len < 1 || s < 1) return -1;
+    // Per head, with this library's kernels on MI355X (bf16, d_c 512,
+    // d_R 64, d_nope = d_v = 128): the absorbed form costs about c_a per
+    // (query, token), MHA mode c_e per cached token for the expansion plus
+    // c_m per (query, token).  Measured: c_e = 0.64 ns; c_a - c_m = 2.7 ps at
+    // s = 2048 and 1.7 ps at s = 8192 (taken linear in log2 s between,
+    // constant outside).  MHA mode wins once q_len (c_a - c_m) > c_e.
+    const double ls = log2((double)s);
+    const double gap = ls <= 11.0 ? 2.7e-12 : ls >= 13.0 ? 1.7e-12 : 2.7e-12 - 0.5e-12 * (ls - 11.0);
+    return (double)q_len * gap > 0.64e-9 ? 1 : 0;
+}
+
 int attn_mla_out_form(int B, int q_len, int h, int d_c, int d_v, int d_model)
 {
     if (B <= 0 || q_len < 1 || h <= 0 || d_c <= 0 || d_v <= 0 || d_model <= 0) return -1;

@@ -50,17 +50,19 @@ __device__ __forceinline__ size_t mha_cache_row(const MhaParams& p, int b, int t
 // Expansion GEMM.  Workgroup = (sequence b, 128 tokens, 128 output columns of
 // [K_n | V]); wavefront (wm, wn) takes 64 tokens x 64 columns as 2 x 2
 // v_mfma_f32_32x32x16_bf16 tiles, the latent rows as the A operand and the
-// weight rows as the B operand.  K = d_c = 512 in steps of 64: lane l (row
-// l % 32, half h = l / 32) loads 64 contiguous bytes of its row at
-// k0 + 32 h, and MFMA j of the step uses their j-th 8 elements (the
-// products are summed over all k, so this k order changes no result).
-// Tokens at or past the sequence's length read its last row and store
-// nothing.
-constexpr int kExTok = 128, kExCol = 128;
+// weight rows as the B operand.  K = d_c = 512 in steps of 64: each step's
+// 128 x 64 slices of both operands move global -> registers -> LDS with
+// 16-byte loads, eight lanes per 128-byte row piece (whole lines), one step
+// ahead of the products, which read their operands from LDS.  Tokens at or
+// past the sequence's length read its last row and store nothing.
+constexpr int kExTok = 128, kExCol = 128, kExK = 64;
+constexpr int kExRow = kExK + 8;   // bf16 per LDS row (padded: 16 rows hit distinct banks)
 
 __global__ __launch_bounds__(256, 2) void mla_expand_kernel(const MhaParams p)
 {
-    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kExTok][kExRow];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kExCol][kExRow];
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int wm = wave / 2, wn = wave % 2;
     const int ncol = p.h * 256 / kExCol;                  // column tiles of [K_n | V]
     const int ntok = (p.s_max + kExTok - 1) / kExTok;
@@ -70,22 +72,40 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(const MhaParams p)
     const int n = mha_len(p, b);
     const int t0 = tt * kExTok;
     if (t0 >= n) return;
-    const int r = lane % 32, hh = lane / 32;
-
-    const uint16_t* arow[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-        const int t = min(t0 + 64 * wm + 32 * mt + r, n - 1);
-        arow[mt] = (const uint16_t*)p.cache + mha_cache_row(p, b, t) * 576 + 32 * hh;
-    }
     const int hk = p.h * 128;                             // columns of K_n
-    const uint16_t* brow[2];
+
+    // loader: thread tid moves 16-byte piece tid % 8 of rows tid / 8 + 32 u
+    const int seg = tid % 8, lrow = tid / 8;
+    const uint16_t* ag[4];
+    const uint16_t* bg[4];
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-        const int f = ct * kExCol + 64 * wn + 32 * nt + r;
-        brow[nt] = (f < hk ? (const uint16_t*)p.w_uk + (size_t)f * 512
-                           : (const uint16_t*)p.w_uv + (size_t)(f - hk) * 512) + 32 * hh;
+    for (int u = 0; u < 4; u++) {
+        const int row = lrow + 32 * u;
+        const int t = min(t0 + row, n - 1);
+        ag[u] = (const uint16_t*)p.cache + mha_cache_row(p, b, t) * 576 + 8 * seg;
+        const int f = ct * kExCol + row;
+        bg[u] = (f < hk ? (const uint16_t*)p.w_uk + (size_t)f * 512
+                        : (const uint16_t*)p.w_uv + (size_t)(f - hk) * 512) + 8 * seg;
     }
+    uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define EX_GLOAD(k0)                                 \
+    ra0 = *(const uint4*)(ag[0] + (k0));             \
+    ra1 = *(const uint4*)(ag[1] + (k0));             \
+    ra2 = *(const uint4*)(ag[2] + (k0));             \
+    ra3 = *(const uint4*)(ag[3] + (k0));             \
+    rb0 = *(const uint4*)(bg[0] + (k0));             \
+    rb1 = *(const uint4*)(bg[1] + (k0));             \
+    rb2 = *(const uint4*)(bg[2] + (k0));             \
+    rb3 = *(const uint4*)(bg[3] + (k0));
+#define EX_LSTORE(buf)                               \
+    *(uint4*)&As[buf][lrow][8 * seg] = ra0;          \
+    *(uint4*)&As[buf][lrow + 32][8 * seg] = ra1;     \
+    *(uint4*)&As[buf][lrow + 64][8 * seg] = ra2;     \
+    *(uint4*)&As[buf][lrow + 96][8 * seg] = ra3;     \
+    *(uint4*)&Bs[buf][lrow][8 * seg] = rb0;          \
+    *(uint4*)&Bs[buf][lrow + 32][8 * seg] = rb1;     \
+    *(uint4*)&Bs[buf][lrow + 64][8 * seg] = rb2;     \
+    *(uint4*)&Bs[buf][lrow + 96][8 * seg] = rb3;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -95,34 +115,35 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(const MhaParams p)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[mt][nt][e] = 0.f;
 
-    bf16x8 av[2][2][4], bv[2][2][4];
-    auto load = [&](int buf, int k0) {
+    const int r = lane % 32, hh = lane / 32;
+    EX_GLOAD(0)
+    EX_LSTORE(0)
+    __syncthreads();
+#pragma unroll 1
+    for (int step = 0; step < 512 / kExK; step++) {
+        const int buf = step & 1;
+        if (step + 1 < 512 / kExK) {
+            EX_GLOAD((step + 1) * kExK)
+        }
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++)
+        for (int ks = 0; ks < kExK / 16; ks++) {
+            bf16x8 av[2], bv[2];
 #pragma unroll
-            for (int j = 0; j < 4; j++) av[buf][mt][j] = *(const bf16x8*)(arow[mt] + k0 + 8 * j);
+            for (int mt = 0; mt < 2; mt++) av[mt] = *(const bf16x8*)&As[buf][64 * wm + 32 * mt + r][16 * ks + 8 * hh];
 #pragma unroll
-        for (int nt = 0; nt < 2; nt++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) bv[buf][nt][j] = *(const bf16x8*)(brow[nt] + k0 + 8 * j);
-    };
-    auto compute = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 4; j++)
+            for (int nt = 0; nt < 2; nt++) bv[nt] = *(const bf16x8*)&Bs[buf][64 * wn + 32 * nt + r][16 * ks + 8 * hh];
 #pragma unroll
             for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-                for (int nt = 0; nt < 2; nt++)
-                    acc[mt][nt] = mfma_32x32x16(av[buf][mt][j], bv[buf][nt][j], acc[mt][nt]);
-    };
-    load(0, 0);
-#pragma unroll 1
-    for (int k0 = 0; k0 < 512; k0 += 128) {
-        load(1, k0 + 64);
-        compute(0);
-        if (k0 + 128 < 512) load(0, k0 + 128);
-        compute(1);
+                for (int nt = 0; nt < 2; nt++) acc[mt][nt] = mfma_32x32x16(av[mt], bv[nt], acc[mt][nt]);
+        }
+        if (step + 1 < 512 / kExK) {
+            EX_LSTORE(buf ^ 1)
+        }
+        __syncthreads();
     }
+#undef EX_GLOAD
+#undef EX_LSTORE
 
     // D tile layout: lane l holds column l % 32, rows 8 (e / 4) + 4 (l / 32) + e % 4
 #pragma unroll
@@ -148,26 +169,29 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(const MhaParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Attention.  Workgroup = (sequence b, head i, block of 64 query positions);
-// wavefront w takes positions 16 w .. 16 w + 15 of the block.  Key tiles of
-// 32 tokens go through LDS, double-buffered, loaded by all 256 threads:
-// K rows [K_n (128) | k_R (64)] as stored, V transposed (dimension-major),
-// so that both products read their operands as plain LDS loads.
+// Attention.  Workgroup = (sequence b, head i, block of 128 query positions),
+// eight wavefronts; wavefront w takes positions 16 w .. 16 w + 15 of the
+// block.  Key tiles of 32 tokens go through LDS, double-buffered, loaded by
+// all 512 threads with 16-byte loads: K rows [K_n (128) | k_R (64)] and V
+// rows, both token-major as stored.
 //   S^T[32 tokens x 16 queries] = K_tile . Q^T   (v_mfma_f32_16x16x32_bf16:
 //     K rows as the A operand, the queries' 192 dims in registers as B)
 //   online softmax per query (log2 domain), P rounded to bf16
 //   O^T[128 dims x 16 queries] += V_tile^T . P^T: the score output gives
 //     lane (query q, G) tokens 4 G .. 4 G + 3 and 16 + 4 G .. 16 + 4 G + 3,
-//     which is the K order this product uses for both operands
-constexpr int kMhaQ = 64;                  // query positions per workgroup
+//     the K order this product uses for both operands; the V operand comes
+//     from transposing LDS reads (ds_read_b64_tr_b16) of those token rows
+constexpr int kMhaW = 8;                   // wavefronts per workgroup
+constexpr int kMhaQ = 16 * kMhaW;          // query positions per workgroup
 constexpr int kMhaT = 32;                  // tokens per tile
 constexpr int kKRow = 192 + 8;             // bf16 per K row in LDS (padded)
-constexpr int kVRow = kMhaT + 8;           // bf16 per transposed V row in LDS (padded)
+constexpr int kVRow = 128 + 16;            // bf16 per V row in LDS (padded)
+constexpr int kMhaChunks = kMhaT * 40;     // 16-byte pieces of a tile (16 K_n, 8 k_R, 16 V per row)
 
-__global__ __launch_bounds__(256) void mla_mha_attn_kernel(const MhaParams p)
+__global__ __launch_bounds__(64 * kMhaW) void mla_mha_attn_kernel(const MhaParams p)
 {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kMhaT][kKRow];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][128][kVRow];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kMhaT][kVRow];
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int qi = lane % 16, G = lane / 16;
     const int nqb = (p.q_len + kMhaQ - 1) / kMhaQ;
@@ -182,6 +206,9 @@ __global__ __launch_bounds__(256) void mla_mha_attn_kernel(const MhaParams p)
     const int jmax = min(qb * kMhaQ + kMhaQ, p.q_len) - 1;
     const int t_end = max(min(n, n - p.q_len + jmax + 1), 0);
     const int nt = (t_end + kMhaT - 1) / kMhaT;
+    // tokens this wavefront needs (its tiles past that only wait at barriers)
+    const int wj = min(qb * kMhaQ + 16 * wave + 15, p.q_len - 1);
+    const int w_end = max(min(n, n - p.q_len + wj + 1), 0);
 
     // this lane's query, dims 32 ks + 8 G .. + 7 (ks < 4: q_nope, else q_rope)
     bf16x8 qf[6];
@@ -196,41 +223,21 @@ __global__ __launch_bounds__(256) void mla_mha_attn_kernel(const MhaParams p)
         }
     }
 
-    // tile loads: 32 rows x (16 K_n + 8 k_R + 16 V chunks of 16 bytes) = 1280
-    // chunks, 5 per thread
-    uint4 ld[5];
-    auto load = [&](int g) {
-#pragma unroll
-        for (int u = 0; u < 5; u++) {
-            const int c = tid + 256 * u;
-            const int row = c / 40, k = c % 40;
-            const int t = min(g * kMhaT + row, max(n - 1, 0));
-            const size_t tok = (size_t)b * p.s_max + t;
-            const uint16_t* src;
-            if (k < 16) src = p.k_exp + (tok * p.h + i) * 128 + 8 * k;
-            else if (k < 24) src = (const uint16_t*)p.cache + mha_cache_row(p, b, t) * 576 + 512 + 8 * (k - 16);
-            else src = p.v_exp + (tok * p.h + i) * 128 + 8 * (k - 24);
-            ld[u] = *(const uint4*)src;
-        }
+    // tile loads: thread tid moves pieces tid, tid + 512, tid + 1024 (< 1280)
+    uint4 ld0, ld1, ld2;
+    auto src_of = [&](int c, int g) -> const uint4* {
+        const int row = c / 40, k = c % 40;
+        const int t = min(g * kMhaT + row, max(n - 1, 0));
+        const size_t tok = (size_t)b * p.s_max + t;
+        if (k < 16) return (const uint4*)(p.k_exp + (tok * p.h + i) * 128 + 8 * k);
+        if (k < 24) return (const uint4*)((const uint16_t*)p.cache + mha_cache_row(p, b, t) * 576 + 512 + 8 * (k - 16));
+        return (const uint4*)(p.v_exp + (tok * p.h + i) * 128 + 8 * (k - 24));
     };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < 5; u++) {
-            const int c = tid + 256 * u;
-            const int row = c / 40, k = c % 40;
-            if (k < 24) {
-                *(uint4*)&Ks[buf][row][8 * k] = ld[u];
-            } else {
-                const uint32_t w4[4] = {ld[u].x, ld[u].y, ld[u].z, ld[u].w};
-                const int d0 = 8 * (k - 24);
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    Vt[buf][d0 + 2 * e][row] = (uint16_t)(w4[e] & 0xffffu);
-                    Vt[buf][d0 + 2 * e + 1][row] = (uint16_t)(w4[e] >> 16);
-                }
-            }
-        }
+    auto dst_of = [&](int c, int buf) -> uint4* {
+        const int row = c / 40, k = c % 40;
+        return k < 24 ? (uint4*)&Ks[buf][row][8 * k] : (uint4*)&Vs[buf][row][8 * (k - 24)];
     };
+    const bool third = tid + 1024 < kMhaChunks;
 
     f32x4 o[8];
 #pragma unroll
@@ -238,64 +245,77 @@ __global__ __launch_bounds__(256) void mla_mha_attn_kernel(const MhaParams p)
     float m = -INFINITY, l = 0.f;
 
     if (nt > 0) {
-        load(0);
-        store(0);
+        ld0 = *src_of(tid, 0);
+        ld1 = *src_of(tid + 512, 0);
+        if (third) ld2 = *src_of(tid + 1024, 0);
+        *dst_of(tid, 0) = ld0;
+        *dst_of(tid + 512, 0) = ld1;
+        if (third) *dst_of(tid + 1024, 0) = ld2;
     }
     __syncthreads();
     for (int g = 0; g < nt; g++) {
         const int buf = g & 1;
-        if (g + 1 < nt) load(g + 1);
-        // scores: two 16-token blocks
-        f32x4 s[2];
-#pragma unroll
-        for (int tb = 0; tb < 2; tb++) {
-            s[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 6; ks++)
-                s[tb] = mfma16(*(const bf16x8*)&Ks[buf][16 * tb + qi][32 * ks + 8 * G], qf[ks], s[tb]);
+        if (g + 1 < nt) {
+            ld0 = *src_of(tid, g + 1);
+            ld1 = *src_of(tid + 512, g + 1);
+            if (third) ld2 = *src_of(tid + 1024, g + 1);
         }
-        // lane holds query qi of this wavefront, tokens 16 tb + 4 G + e
-        float z[8];
-        float tm = -INFINITY;
+        if (g * kMhaT < w_end) {   // wave-uniform
+            // scores: two 16-token blocks
+            f32x4 s[2];
 #pragma unroll
-        for (int tb = 0; tb < 2; tb++)
+            for (int tb = 0; tb < 2; tb++) {
+                s[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int t = g * kMhaT + 16 * tb + 4 * G + e;
-                const float v = t <= last && qv ? s[tb][e] * p.scale_log2 : -INFINITY;
-                z[4 * tb + e] = v;
-                tm = fmaxf(tm, v);
+                for (int ks = 0; ks < 6; ks++)
+                    s[tb] = mfma16(*(const bf16x8*)&Ks[buf][16 * tb + qi][32 * ks + 8 * G], qf[ks], s[tb]);
             }
-        tm = fmaxf(tm, xor16(tm));
-        tm = fmaxf(tm, xor32(tm));
-        const float mn = fmaxf(m, tm);
-        // rows that have seen nothing yet keep m = -inf and add nothing
-        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
-        float ps = 0.f;
-        uint32_t pk[4];
+            // lane holds query qi of this wavefront, tokens 16 tb + 4 G + e
+            float z[8];
+            float tm = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const float p0 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[e] - mn);
-            const float p1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[e + 1] - mn);
-            ps += p0 + p1;
-            pk[e / 2] = pack_bf16x2(p0, p1);
-        }
-        ps += xor16(ps);
-        ps += xor32(ps);
-        l = l * alpha + ps;
-        m = mn;
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        // O^T += V^T P^T; lane (d = 16 mc + qi... as A row, G) takes tokens
-        // 4 G .. 4 G + 3 and 16 + 4 G .. 16 + 4 G + 3 of dimension 16 mc + qi
+            for (int tb = 0; tb < 2; tb++)
 #pragma unroll
-        for (int mc = 0; mc < 8; mc++) {
-            o[mc] *= alpha;
-            const uint2 lo = *(const uint2*)&Vt[buf][16 * mc + qi][4 * G];
-            const uint2 hi = *(const uint2*)&Vt[buf][16 * mc + qi][16 + 4 * G];
-            const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            o[mc] = mfma16(va, pb, o[mc]);
+                for (int e = 0; e < 4; e++) {
+                    const int t = g * kMhaT + 16 * tb + 4 * G + e;
+                    const float v = t <= last && qv ? s[tb][e] * p.scale_log2 : -INFINITY;
+                    z[4 * tb + e] = v;
+                    tm = fmaxf(tm, v);
+                }
+            tm = fmaxf(tm, xor16(tm));
+            tm = fmaxf(tm, xor32(tm));
+            const float mn = fmaxf(m, tm);
+            // rows that have seen nothing yet keep m = -inf and add nothing
+            const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+            float ps = 0.f;
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[e] - mn);
+                const float p1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[e + 1] - mn);
+                ps += p0 + p1;
+                pk[e / 2] = pack_bf16x2(p0, p1);
+            }
+            ps += xor16(ps);
+            ps += xor32(ps);
+            l = l * alpha + ps;
+            m = mn;
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+            // V operand of dims 16 mc .. + 15: source lane qi of group G points
+            // at token 4 G + qi / 4 (then 16 + ...), dims 16 mc + 4 (qi % 4) ..
+            const uint8_t* vb = (const uint8_t*)&Vs[buf][4 * G + qi / 4][4 * (qi % 4)];
+#pragma unroll
+            for (int mc = 0; mc < 8; mc++) {
+                o[mc] *= alpha;
+                const bf16x8 va = cat_tr(lds_read_tr(vb + 32 * mc), lds_read_tr(vb + 32 * mc + 16 * kVRow * 2));
+                o[mc] = mfma16(va, pb, o[mc]);
+            }
         }
-        if (g + 1 < nt) store(buf ^ 1);
+        if (g + 1 < nt) {
+            *dst_of(tid, buf ^ 1) = ld0;
+            *dst_of(tid + 512, buf ^ 1) = ld1;
+            if (third) *dst_of(tid + 1024, buf ^ 1) = ld2;
+        }
         __syncthreads();
     }
 
@@ -323,7 +343,7 @@ hipError_t launch_mla_mha(const MhaParams& p, hipStream_t st)
     hipLaunchKernelGGL(mla_expand_kernel, dim3((unsigned)g1), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mla_mha_attn_kernel, dim3((unsigned)g2), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(mla_mha_attn_kernel, dim3((unsigned)g2), dim3(64 * kMhaW), 0, st, p);
     return hipGetLastError();
 }
 

@@ -505,6 +505,16 @@ int attn_decode_mla_mha(void* out, float* lse, const void* q_nope, const void* q
 size_t attn_decode_mla_mha_workspace_bytes(int B, int s_max, int h);
 
 /*
+ * attn_mla_mode -- which MLA execution form is faster for q_len new tokens
+ * over a context of s tokens (the page's kernel selection by query and KV
+ * length): 0 the absorbed (MQA) form, attn_decode_mla_absorbed_multi; 1 MHA
+ * mode, attn_decode_mla_mha; -1 bad sizes.  A cost model of this library's
+ * kernels fitted to MI355X timings: MHA mode from about q_len 240 at
+ * s = 2048 and about 380 at s = 8192.
+ */
+int attn_mla_mode(int q_len, int s);
+
+/*
  * attn_mla_out_form -- which output form is cheaper for a shape, by the
  * bytes and matrix-core work in which the two differ (deferred: W_UV, W_O
  * and the heads' outputs; merged: W_abs and bf16 u~), each priced at the

@@ -253,3 +253,13 @@ def test_output_form_choice():
     # a latent narrower than the value heads: the merged weight is the smaller one
     assert A.attn_mla_out_form(32, 1, 8, 64, 128, 4096) == 1
     assert A.attn_mla_out_form(0, 1, 8, 64, 128, 4096) == -1
+
+
+def test_mla_mode_choice():
+    # measured crossovers: absorbed for decode-sized query blocks, MHA mode
+    # for prefill-sized ones, later for longer contexts
+    assert A.attn_mla_mode(1, 8192) == 0 and A.attn_mla_mode(64, 2048) == 0
+    assert A.attn_mla_mode(256, 2048) == 1 and A.attn_mla_mode(256, 8192) == 0
+    assert A.attn_mla_mode(1024, 8192) == 1
+    assert A.attn_mla_mode(0, 8192) == -1
+    assert A.attn_decode_mla_mha_workspace_bytes(4, 8192, 128) == 2 * 4 * 8192 * 128 * 128 * 2

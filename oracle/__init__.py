@@ -95,6 +95,11 @@ def _load():
         lib.ref_mla_output.restype = I
         lib.ref_mla_output.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I,
                                        I, I, I, D]
+        lib.ref_mla_absorbed_fp8_paged_scales.restype = I
+        lib.ref_mla_absorbed_fp8_paged_scales.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I,
+                                                          I, I, I, I, I, I, I, D]
+        lib.ref_kv_append_mla_fp8_paged_scales.restype = I
+        lib.ref_kv_append_mla_fp8_paged_scales.argtypes = [P, P, P, P, P, P, I, I, I, I, I]
         lib.ref_kv_append_mla_fp8.restype = I
         lib.ref_kv_append_mla_fp8.argtypes = [P, P, C.c_float, C.c_float, P, P, I, I, I, I, I, I]
         lib.ref_gqa_decode_fp8_paged_scales.restype = I
@@ -547,6 +552,58 @@ def kv_append_mla_fp8(cache8, kv_new, c_scale, r_scale, pos, d_c, block_table=No
                                        _ptr(pos), _ptr(bt), max_blocks, bs, B, s_max, d_c, W - d_c)
     if rc != 0:
         raise ValueError(f"ref_kv_append_mla_fp8 rejected its arguments ({rc})")
+    return c
+
+
+def mla_absorbed_fp8_paged_scales(q_nope, q_rope, w_uk, w_uv, cache8, c_scales, r_scales, s,
+                                  block_table, block_size=16, scale=None):
+    """Reference absorbed MLA decode over a paged E4M3 latent pool
+    [N_blk, block_size, d_c + d_R] whose pages carry their own scales
+    (c_scales, r_scales float32 [N_blk]).  Returns (out, u_latent, lse)."""
+    q_nope, q_rope, w_uk, w_uv = (_stored(x, 2) for x in (q_nope, q_rope, w_uk, w_uv))
+    cache8 = np.ascontiguousarray(cache8, dtype=np.uint8)
+    cs = np.ascontiguousarray(c_scales, dtype=np.float32)
+    rs = np.ascontiguousarray(r_scales, dtype=np.float32)
+    if cs.shape != (cache8.shape[0],) or rs.shape != (cache8.shape[0],):
+        raise ValueError("c_scales and r_scales must be [N_blk]")
+    B, h, d_nope = q_nope.shape
+    d_R = q_rope.shape[2]
+    d_c = w_uk.shape[2]
+    d_v = w_uv.shape[1]
+    s = _i32(s)
+    bt = _i32(block_table)
+    _check_table(bt, cache8.shape[0] * cache8.shape[1], block_size, s)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_nope + d_R)
+    out = np.zeros((B, h, d_v))
+    ul = np.zeros((B, h, d_c))
+    lse = np.zeros((B, h))
+    rc = _load().ref_mla_absorbed_fp8_paged_scales(_ptr(out), _ptr(ul), _ptr(lse), _ptr(q_nope),
+                                                   _ptr(q_rope), _ptr(w_uk), _ptr(w_uv),
+                                                   _ptr(cache8), _ptr(cs), _ptr(rs), _ptr(s),
+                                                   _ptr(bt), bt.shape[1], block_size, B, h, d_c,
+                                                   d_R, d_nope, d_v, float(scale))
+    if rc != 0:
+        raise ValueError(f"ref_mla_absorbed_fp8_paged_scales rejected its arguments ({rc})")
+    return out, ul, lse
+
+
+def kv_append_mla_fp8_paged_scales(cache8, kv_new, c_scales, r_scales, pos, d_c, block_table,
+                                   block_size=16):
+    """Host image of kv_cache_append_mla_fp8_paged_scales: a new uint8 pool
+    with row b of kv_new encoded at slot pos[b] under its page's scales."""
+    c = np.array(cache8, dtype=np.uint8, copy=True)
+    kv_new = _stored(kv_new, 2)
+    B, W = kv_new.shape
+    cs = np.ascontiguousarray(c_scales, dtype=np.float32)
+    rs = np.ascontiguousarray(r_scales, dtype=np.float32)
+    pos = _i32(pos)
+    bt = _i32(block_table)
+    rc = _load().ref_kv_append_mla_fp8_paged_scales(_ptr(c), _ptr(kv_new), _ptr(cs), _ptr(rs),
+                                                    _ptr(pos), _ptr(bt), bt.shape[1], block_size,
+                                                    B, d_c, W - d_c)
+    if rc != 0:
+        raise ValueError(f"ref_kv_append_mla_fp8_paged_scales rejected its arguments ({rc})")
     return c
 
 

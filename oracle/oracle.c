@@ -200,6 +200,16 @@ static double ld_latent(const void* cache, size_t roff, int e, int cb, int d_c, 
     return ld(cache, roff + e, cb);
 }
 
+/* the scale of token t of sequence bb: that of its page (the physical block
+ * the table maps it to) when per-page scales are given, else the tensor's */
+static double page_scale(const float* scales, double tensor_scale, const int32_t* block_table,
+                         int max_blocks, int block_size, int bb, int t)
+{
+    if (!scales) return tensor_scale;
+    const int blk = block_table[(size_t)bb * max_blocks + t / block_size];
+    return (double)scales[blk];
+}
+
 /*
  * Rows r = (bb, jq, i) of q_len query positions per sequence (q_len = 1:
  * plain single-token decode).  All q_len new tokens are already in the
@@ -210,6 +220,7 @@ static double ld_latent(const void* cache, size_t roff, int e, int cb, int d_c, 
 static int mla_absorbed_impl(double* out, double* u_latent, double* lse, const void* q_nope,
                              const void* q_rope, const void* w_uk, const void* w_uv,
                              const void* cache, int cb, double c_scale, double r_scale,
+                             const float* c_scales, const float* r_scales,
                              const int32_t* s, const int32_t* block_table, int max_blocks,
                              int block_size, int B, int q_len, int s_max, int h, int d_c,
                              int d_R, int d_nope, int d_v, int b, double scale)
@@ -219,6 +230,8 @@ static int mla_absorbed_impl(double* out, double* u_latent, double* lse, const v
         return OR_EINVAL;
     if (b != 2 && b != 4) return OR_EINVAL;
     if (block_table && (block_size <= 0 || max_blocks <= 0)) return OR_EINVAL;
+    if ((c_scales || r_scales) && (!c_scales || !r_scales || !block_table || cb != 1))
+        return OR_EINVAL;
     const int W = d_c + d_R;
     const long rows = (long)B * q_len * h;
     int bad = 0;
@@ -257,13 +270,17 @@ static int mla_absorbed_impl(double* out, double* u_latent, double* lse, const v
             for (int t = 0; t < n; t++) {
                 const size_t roff =
                     row_of(block_table, max_blocks, block_size, s_max, bb, t) * W;
+                const double cs = page_scale(c_scales, c_scale, block_table, max_blocks,
+                                             block_size, bb, t);
+                const double rs = page_scale(r_scales, r_scale, block_table, max_blocks,
+                                             block_size, bb, t);
                 double acc = 0.0;
                 for (int c = 0; c < d_c; c++)
-                    acc += qt[c] * ld_latent(cache, roff, c, cb, d_c, c_scale, r_scale);
+                    acc += qt[c] * ld_latent(cache, roff, c, cb, d_c, cs, rs);
                 double accr = 0.0;
                 for (int e = 0; e < d_R; e++)
                     accr += ld(q_rope, (size_t)r * d_R + e, b) *
-                            ld_latent(cache, roff, d_c + e, cb, d_c, c_scale, r_scale);
+                            ld_latent(cache, roff, d_c + e, cb, d_c, cs, rs);
                 z[t] = scale * (acc + accr);
             }
             double m;
@@ -274,7 +291,9 @@ static int mla_absorbed_impl(double* out, double* u_latent, double* lse, const v
                 for (int t = 0; t < n; t++) {
                     const size_t roff =
                         row_of(block_table, max_blocks, block_size, s_max, bb, t) * W;
-                    acc += p[t] * ld_latent(cache, roff, c, cb, d_c, c_scale, r_scale);
+                    const double cs = page_scale(c_scales, c_scale, block_table, max_blocks,
+                                                 block_size, bb, t);
+                    acc += p[t] * ld_latent(cache, roff, c, cb, d_c, cs, r_scale);
                 }
                 ut[c] = acc / l;
             }
@@ -301,8 +320,8 @@ int ref_mla_absorbed(double* out, double* u_latent, double* lse, const void* q_n
                      int d_R, int d_nope, int d_v, int b, double scale)
 {
     return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, b, 1.0, 1.0,
-                             s, block_table, max_blocks, block_size, B, 1, s_max, h, d_c, d_R,
-                             d_nope, d_v, b, scale);
+                             NULL, NULL, s, block_table, max_blocks, block_size, B, 1, s_max, h,
+                             d_c, d_R, d_nope, d_v, b, scale);
 }
 
 /*
@@ -327,8 +346,8 @@ int ref_mla_absorbed_multi(double* out, double* u_latent, double* lse, const voi
                            int d_c, int d_R, int d_nope, int d_v, int b, double scale)
 {
     return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, b, 1.0, 1.0,
-                             s, block_table, max_blocks, block_size, B, q_len, s_max, h, d_c,
-                             d_R, d_nope, d_v, b, scale);
+                             NULL, NULL, s, block_table, max_blocks, block_size, B, q_len, s_max,
+                             h, d_c, d_R, d_nope, d_v, b, scale);
 }
 
 /*
@@ -355,9 +374,9 @@ int ref_mla_output(double* o, double* lse, const void* q_nope, const void* q_rop
     const size_t rows = (size_t)B * q_len;
     double* u = (double*)malloc(sizeof(double) * (rows * h * (size_t)d_v + 1));
     if (!u) return OR_EINVAL;
-    int rc = mla_absorbed_impl(u, NULL, lse, q_nope, q_rope, w_uk, w_uv, cache, b, 1.0, 1.0, s,
-                               block_table, max_blocks, block_size, B, q_len, s_max, h, d_c, d_R,
-                               d_nope, d_v, b, scale);
+    int rc = mla_absorbed_impl(u, NULL, lse, q_nope, q_rope, w_uk, w_uv, cache, b, 1.0, 1.0,
+                               NULL, NULL, s, block_table, max_blocks, block_size, B, q_len,
+                               s_max, h, d_c, d_R, d_nope, d_v, b, scale);
     if (rc == OR_OK) {
         const size_t hd = (size_t)h * d_v;
 #pragma omp parallel for schedule(static)
@@ -385,8 +404,8 @@ int ref_mla_absorbed_multi_fp8(double* out, double* u_latent, double* lse, const
                                int d_R, int d_nope, int d_v, double scale)
 {
     return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1, c_scale,
-                             r_scale, s, block_table, max_blocks, block_size, B, q_len, s_max, h,
-                             d_c, d_R, d_nope, d_v, 2, scale);
+                             r_scale, NULL, NULL, s, block_table, max_blocks, block_size, B, q_len,
+                             s_max, h, d_c, d_R, d_nope, d_v, 2, scale);
 }
 
 /*
@@ -404,8 +423,31 @@ int ref_mla_absorbed_fp8(double* out, double* u_latent, double* lse, const void*
                          int s_max, int h, int d_c, int d_R, int d_nope, int d_v, double scale)
 {
     return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1, c_scale,
-                             r_scale, s, block_table, max_blocks, block_size, B, 1, s_max, h, d_c,
-                             d_R, d_nope, d_v, 2, scale);
+                             r_scale, NULL, NULL, s, block_table, max_blocks, block_size, B, 1,
+                             s_max, h, d_c, d_R, d_nope, d_v, 2, scale);
+}
+
+/*
+ * ref_mla_absorbed_fp8 over a paged pool whose pages each carry their own
+ * pair of scales ("Multi-Head Latent Attention (MLA): Mathematical
+ * Foundations" (llms.blog), section "High-Throughput Serving Kernels:
+ * FlashMLA and SGLang": the E4M3 latent is stored with per-block scaling
+ * factors; one block = one page here): element e of token t's row is
+ * code * c_scales[blk] (e < d_c) or code * r_scales[blk], blk the physical
+ * page the table maps t to.  c_scales, r_scales: [num_blocks] fp32.
+ */
+int ref_mla_absorbed_fp8_paged_scales(double* out, double* u_latent, double* lse,
+                                      const void* q_nope, const void* q_rope, const void* w_uk,
+                                      const void* w_uv, const uint8_t* cache,
+                                      const float* c_scales, const float* r_scales,
+                                      const int32_t* s, const int32_t* block_table,
+                                      int max_blocks, int block_size, int B, int h, int d_c,
+                                      int d_R, int d_nope, int d_v, double scale)
+{
+    if (!c_scales || !r_scales || !block_table) return OR_EINVAL;
+    return mla_absorbed_impl(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1, 1.0, 1.0,
+                             c_scales, r_scales, s, block_table, max_blocks, block_size, B, 1, 0,
+                             h, d_c, d_R, d_nope, d_v, 2, scale);
 }
 
 /*
@@ -683,6 +725,35 @@ int ref_kv_append_mla_fp8(uint8_t* cache, const void* kv_new, float c_inv_scale,
             const float x = (float)ld(kv_new, (size_t)bb * n + e, 2);
             cache[row * n + e] =
                 (uint8_t)ref_fp8_e4m3_encode(x * ((int)e < d_c ? c_inv_scale : r_inv_scale));
+        }
+    }
+    return OR_OK;
+}
+
+/*
+ * Append of latent rows into a paged FP8 pool with per-page scales: element
+ * x of kv_new[b] becomes encode(x * (1 / c_scales[blk])) in the latent part
+ * and encode(x * (1 / r_scales[blk])) in the rotary part, the reciprocal and
+ * the product in fp32, blk the page of slot pos[b].
+ */
+int ref_kv_append_mla_fp8_paged_scales(uint8_t* cache, const void* kv_new, const float* c_scales,
+                                       const float* r_scales, const int32_t* pos,
+                                       const int32_t* block_table, int max_blocks,
+                                       int block_size, int B, int d_c, int d_R)
+{
+    if (!cache || !kv_new || !c_scales || !r_scales || !pos || !block_table) return OR_EINVAL;
+    if (B < 0 || d_c <= 0 || d_R < 0 || block_size <= 0 || max_blocks <= 0) return OR_EINVAL;
+    const size_t n = (size_t)d_c + d_R;
+    for (int bb = 0; bb < B; bb++) {
+        const int t = pos[bb];
+        if (t < 0 || t >= max_blocks * block_size) return OR_EINVAL;
+        const int blk = block_table[(size_t)bb * max_blocks + t / block_size];
+        if (blk < 0) return OR_EINVAL;
+        const size_t row = row_of(block_table, max_blocks, block_size, 0, bb, t);
+        const float ic = 1.0f / c_scales[blk], ir = 1.0f / r_scales[blk];
+        for (size_t e = 0; e < n; e++) {
+            const float x = (float)ld(kv_new, (size_t)bb * n + e, 2);
+            cache[row * n + e] = (uint8_t)ref_fp8_e4m3_encode(x * ((int)e < d_c ? ic : ir));
         }
     }
     return OR_OK;

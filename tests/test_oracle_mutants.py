@@ -41,6 +41,12 @@ MUTANTS = [
      "ld(w_o, (size_t)n * hd + (size_t)e * h + i, b)", 0, ["test_oracle_mla_output.py"]),
     ("mla_output_w_o_transposed", "ld(w_o, (size_t)n * hd + (size_t)i * d_v + e, b)",
      "ld(w_o, ((size_t)i * d_v + e) * d_model + n, b)", 0, ["test_oracle_mla_output.py"]),
+    ("mla_page_scale_by_logical_block", "    return (double)scales[blk];",
+     "    return (double)scales[t / block_size];", 0, ["test_oracle_mla_fp8.py"]),
+    ("mla_page_append_scales_swapped",
+     "const float ic = 1.0f / c_scales[blk], ir = 1.0f / r_scales[blk];",
+     "const float ic = 1.0f / r_scales[blk], ir = 1.0f / c_scales[blk];", 0,
+     ["test_oracle_mla_fp8.py"]),
     ("merge_weight_sign", "const double w = exp((double)lse_parts[(size_t)k * rows + r] - M);",
      "const double w = exp(M - (double)lse_parts[(size_t)k * rows + r]);", 0,
      ["test_oracle_merge.py"]),

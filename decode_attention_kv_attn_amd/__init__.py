@@ -47,6 +47,8 @@ EXPORTED = (
     "attn_decode_mla_mha",
     "attn_decode_mla_mha_workspace_bytes",
     "attn_mla_mode",
+    "attn_decode_mla_absorbed_fp8_paged_scales",
+    "kv_cache_append_mla_fp8_paged_scales",
 )
 
 _lib = None
@@ -138,6 +140,13 @@ def lib():
         L.attn_decode_mla_mha_workspace_bytes.argtypes = [I, I, I]
         L.attn_mla_mode.restype = I
         L.attn_mla_mode.argtypes = [I, I]
+        L.attn_decode_mla_absorbed_fp8_paged_scales.restype = I
+        L.attn_decode_mla_absorbed_fp8_paged_scales.argtypes = [P, P, P, P, P, P, P, P, P, P, P,
+                                                                P, I, I, I, I, I, I, I, I, I, I,
+                                                                F, P, Z, P]
+        L.kv_cache_append_mla_fp8_paged_scales.restype = I
+        L.kv_cache_append_mla_fp8_paged_scales.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                                           P]
         L.attn_merge_partials.restype = I
         L.attn_merge_partials.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
         _lib = L
@@ -417,6 +426,29 @@ def attn_mla_mode(q_len, s):
     return int(lib().attn_mla_mode(q_len, s))
 
 
+def attn_decode_mla_absorbed_fp8_paged_scales(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv,
+                                              cache, c_scales, r_scales, s, block_table,
+                                              max_blocks, block_size, num_blocks, B, s_max, h,
+                                              d_c, d_R, d_nope, d_v, scale, workspace,
+                                              workspace_bytes, stream=None, check=True):
+    rc = lib().attn_decode_mla_absorbed_fp8_paged_scales(
+        _p(out), _p(u_latent), _p(lse), _p(q_nope), _p(q_rope), _p(w_uk), _p(w_uv), _p(cache),
+        _p(c_scales), _p(r_scales), _p(s), _p(block_table), max_blocks, block_size, num_blocks,
+        B, s_max, h, d_c, d_R, d_nope, d_v, float(scale), _p(workspace), int(workspace_bytes),
+        _stream(stream))
+    return _check(rc) if check else rc
+
+
+def kv_cache_append_mla_fp8_paged_scales(cache, kv_new, c_scales, r_scales, pos, block_table,
+                                         max_blocks, block_size, num_blocks, B, s_max, d_c, d_R,
+                                         stream=None, check=True):
+    rc = lib().kv_cache_append_mla_fp8_paged_scales(_p(cache), _p(kv_new), _p(c_scales),
+                                                    _p(r_scales), _p(pos), _p(block_table),
+                                                    max_blocks, block_size, num_blocks, B, s_max,
+                                                    d_c, d_R, _stream(stream))
+    return _check(rc) if check else rc
+
+
 # ---------------------------------------------------------------------------
 # Convenience wrappers over torch tensors (shape bookkeeping only; they call
 # the entry points above).
@@ -488,7 +520,8 @@ def decode_mla(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_siz
                s_max=None, scale=0.0, want_latent=True, workspace=None, stream=None,
                c_scale=None, r_scale=None):
     """Absorbed MLA decode; cache rows [c | k_R] of width d_c + d_R (bf16,
-    or uint8 E4M3 codes when c_scale and r_scale are given)."""
+    or uint8 E4M3 codes when c_scale and r_scale are given: floats, or
+    [num_blocks] fp32 device tensors of per-page scales for a paged pool)."""
     import torch
     B, h, d_nope = q_nope.shape
     d_R = q_rope.shape[2]
@@ -510,6 +543,11 @@ def decode_mla(q_nope, q_rope, w_uk, w_uv, cache, s, block_table=None, block_siz
         attn_decode_mla_absorbed(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache, s, block_table,
                                  max_blocks, block_size, num_blocks, B, s_max, h, d_c, d_R,
                                  d_nope, d_v, 2, scale, wb, wn, stream)
+    elif not isinstance(c_scale, (int, float)):
+        attn_decode_mla_absorbed_fp8_paged_scales(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache,
+                                                  c_scale, r_scale, s, block_table, max_blocks,
+                                                  block_size, num_blocks, B, s_max, h, d_c, d_R,
+                                                  d_nope, d_v, scale, wb, wn, stream)
     else:
         attn_decode_mla_absorbed_fp8(out, ul, l, q_nope, q_rope, w_uk, w_uv, cache, c_scale,
                                      r_scale, s, block_table, max_blocks, block_size, num_blocks,

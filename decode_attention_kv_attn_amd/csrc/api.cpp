@@ -412,6 +412,39 @@ int kv_cache_append_mla_fp8(void* cache, const void* kv_new, float c_scale, floa
     return ATTN_OK;
 }
 
+int kv_cache_append_mla_fp8_paged_scales(void* cache, const void* kv_new, const float* c_scales,
+                                         const float* r_scales, const int32_t* pos,
+                                         const int32_t* block_table, int max_blocks,
+                                         int block_size, int num_blocks, int B, int s_max,
+                                         int d_c, int d_R, void* stream)
+{
+    if (!cache || !kv_new || !pos || !c_scales || !r_scales)
+        return fail(ATTN_EINVAL, "null cache, kv_new, pos or scales");
+    if (!block_table) return fail(ATTN_EINVAL, "per-page scales need a paged cache (block_table)");
+    if (B < 0 || d_c <= 0 || d_R < 0 || d_c % 4 != 0 || d_R % 4 != 0)
+        return fail(ATTN_EINVAL, "bad sizes (d_c and d_R must be multiples of 4)");
+    int rc = check_table(block_table, max_blocks, block_size, num_blocks, s_max);
+    if (rc) return rc;
+    attn::AppendParams pk{};
+    pk.cache = cache;
+    pk.src = kv_new;
+    pk.pos = pos;
+    pk.bt = block_table;
+    pk.max_blocks = max_blocks;
+    pk.bs_log2 = ilog2(block_size);
+    pk.num_blocks = num_blocks;
+    pk.s_max = s_max;
+    pk.row_bytes = (long long)d_c + d_R;
+    pk.inv_scale = pk.inv_scale2 = 1.f;
+    pk.split = d_c;
+    pk.page_scales = c_scales;
+    pk.page_scales2 = r_scales;
+    pk.d_h = d_c + d_R;
+    hipError_t e = attn::launch_append_fp8(pk, nullptr, B, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_cache_append_mla_fp8_paged_scales launch");
+    return ATTN_OK;
+}
+
 int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
                     const void* cache_v, const int32_t* s, const int32_t* block_table,
                     int max_blocks, int block_size, int num_blocks, int B, int s_max, int h,
@@ -466,7 +499,8 @@ int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const
                float r_scale, const int32_t* s, const int32_t* block_table, int max_blocks,
                int block_size, int num_blocks, int B, int q_len, int s_max, int h, int d_c,
                int d_R, int d_nope, int d_v, int b, float scale, void* workspace,
-               size_t workspace_bytes, void* stream, uint16_t* u_bf16 = nullptr)
+               size_t workspace_bytes, void* stream, uint16_t* u_bf16 = nullptr,
+               const float* c_scales = nullptr, const float* r_scales = nullptr)
 {
     const bool up = out != nullptr;
     if ((!up && !u_bf16) || !q_nope || !q_rope || !w_uk || (up && !w_uv) || !cache || !s)
@@ -528,6 +562,8 @@ int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const
     p.f8 = b == 1;
     p.c_scale = c_scale;
     p.r_scale = r_scale;
+    p.c_scales = c_scales;
+    p.r_scales = r_scales;
     p.u_bf16 = u_bf16;
     hipError_t e = attn::launch_mla(p, block_table != nullptr, (hipStream_t)stream);
     if (e == hipErrorNotSupported) return fail(ATTN_ENOTSUP, "MLA kernels not built");
@@ -565,6 +601,25 @@ int attn_decode_mla_absorbed_fp8(void* out, float* u_latent, float* lse, const v
     return decode_mla(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, c_scale, r_scale, s,
                       block_table, max_blocks, block_size, num_blocks, B, 1, s_max, h, d_c, d_R,
                       d_nope, d_v, 1, scale, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_mla_absorbed_fp8_paged_scales(void* out, float* u_latent, float* lse,
+                                              const void* q_nope, const void* q_rope,
+                                              const void* w_uk, const void* w_uv,
+                                              const void* cache, const float* c_scales,
+                                              const float* r_scales, const int32_t* s,
+                                              const int32_t* block_table, int max_blocks,
+                                              int block_size, int num_blocks, int B, int s_max,
+                                              int h, int d_c, int d_R, int d_nope, int d_v,
+                                              float scale, void* workspace,
+                                              size_t workspace_bytes, void* stream)
+{
+    if (!c_scales || !r_scales) return fail(ATTN_EINVAL, "null c_scales or r_scales");
+    if (!block_table) return fail(ATTN_EINVAL, "per-page scales need a paged cache (block_table)");
+    return decode_mla(out, u_latent, lse, q_nope, q_rope, w_uk, w_uv, cache, 1.f, 1.f, s,
+                      block_table, max_blocks, block_size, num_blocks, B, 1, s_max, h, d_c, d_R,
+                      d_nope, d_v, 1, scale, workspace, workspace_bytes, stream, nullptr,
+                      c_scales, r_scales);
 }
 
 int attn_decode_mla_absorbed_multi(void* out, float* u_latent, float* lse, const void* q_nope,

@@ -102,7 +102,9 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendParams pk, 
     for (long long i = threadIdx.x; i < n4; i += blockDim.x) {
         const uint2 w = src[i];
         float is = 4 * i < p.split ? p.inv_scale : p.inv_scale2;   // MLA: latent, then rotary part
-        if (p.page_scales)   // this page's scale for the KV head of these 4 elements
+        if (p.page_scales2)   // MLA latent row: this page's latent, then rotary scale
+            is = 1.0f / (4 * i < p.split ? p.page_scales[blk] : p.page_scales2[blk]);
+        else if (p.page_scales)   // this page's scale for the KV head of these 4 elements
             is = 1.0f / p.page_scales[(size_t)blk * (p.row_bytes / p.d_h) + (4 * i) / p.d_h];
         const uint32_t c0 = e4m3_code(bf16lo_to_f32(w.x) * is);
         const uint32_t c1 = e4m3_code(bf16hi_to_f32(w.x) * is);

@@ -52,6 +52,8 @@ struct AppendParams {
     long long split;       // FP8 append: first element under inv_scale2 (a multiple of 4)
     const float* page_scales;   // FP8 append into a paged pool with one scale per page and
     int d_h;                    // KV head ([num_blocks, row_bytes / d_h]); nullptr: the above
+    const float* page_scales2;  // MLA rows with a scale pair per page: page_scales [num_blocks]
+                                // for elements before split, this one after; nullptr: unused
 };
 
 hipError_t launch_append(const AppendParams& k, const AppendParams* v, int B, hipStream_t st);
@@ -86,6 +88,8 @@ struct MlaParams {
     int f8;               // cache rows are E4M3 codes (else bf16)
     float c_scale;        // FP8: scale of the latent part (1 for bf16); folded into q^ and u~
     float r_scale;        // FP8: scale of the rotary part (1 for bf16); folded into q^
+    const float* c_scales;   // paged FP8 pool with a scale pair per page: [num_blocks] latent,
+    const float* r_scales;   // [num_blocks] rotary (c_scale = r_scale = 1 then); nullptr: none
 };
 
 hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st);

@@ -69,6 +69,15 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 w)
     return v;
 }
 
+// 8 bf16 times an fp32 factor, rounded back to bf16 (nearest even)
+__device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 x, float f)
+{
+    const bf16x8 v = {(__bf16)((float)x[0] * f), (__bf16)((float)x[1] * f), (__bf16)((float)x[2] * f),
+                      (__bf16)((float)x[3] * f), (__bf16)((float)x[4] * f), (__bf16)((float)x[5] * f),
+                      (__bf16)((float)x[6] * f), (__bf16)((float)x[7] * f)};
+    return v;
+}
+
 __device__ __forceinline__ bf16x8 cat_tr(s16x4 lo, s16x4 hi)
 {
     typedef short s16x8 __attribute__((ext_vector_type(8)));

@@ -576,12 +576,21 @@ struct TileDma {
     }
 };
 
-template <bool PAGED, bool F8>
+// PS (E4M3 pages with their own scale pair): the scores are summed as
+// q~ . c + rho q_R . k_R with rho = r_scale / c_scale of the token's page
+// folded into the widened rotary codes, then scaled by the page's c_scale;
+// the probabilities that weight the latent sum carry c_scale too (the sums l
+// do not), so U / l comes out in value units.  The scales of a tile's two
+// 16-row halves are looked up when its DMA is issued and wait in LDS.
+template <bool PAGED, bool F8, bool PS = false>
 __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                                                          const int32_t* __restrict__ btab,
                                                          const int32_t* __restrict__ slen,
-                                                         const int32_t* __restrict__ sched)
+                                                         const int32_t* __restrict__ sched,
+                                                         const float* __restrict__ cscl,
+                                                         const float* __restrict__ rscl)
 {
+    static_assert(!PS || (PAGED && F8), "page scales come with a paged E4M3 pool");
     constexpr int NW = 4;           // wavefronts per workgroup
     constexpr int KS = 576 / 16;    // score K steps
 #ifndef MLA_PD
@@ -611,6 +620,8 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     __shared__ __attribute__((aligned(16))) bf16x8 Pb[2][NTH][2][64];
     // partial-write staging of E4M3 tiles (bf16 tiles use a free ring buffer)
     __shared__ __attribute__((aligned(16))) uint8_t Stg8[F8 ? 4 * 32 * 272 : 16];
+    // page scales of the tiles in the ring: [c half 0, c half 1, r half 0, r half 1]
+    __shared__ __attribute__((aligned(16))) float Scl[PS ? kNBuf * 4 : 4];
 
     const int tid = threadIdx.x, lane = tid % 64, hh = lane / 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -629,6 +640,17 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
 
     const TileDma<NW, PAGED, F8> dma(p, btab, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)Cs,
                                  wave, lane);
+    // the page scales of the tile whose rows are r0, r1, for ring slot `slot`
+    // (read by the step that scores it, after a barrier)
+    auto note_scales = [&](int slot, bool past, size_t r0, size_t r1) {
+        if constexpr (PS) {
+            if (!past) {
+                const int b0 = (int)(r0 >> p.bs_log2), b1 = (int)(r1 >> p.bs_log2);
+                const float4 v = make_float4(cscl[b0], cscl[b1], rscl[b0], rscl[b1]);
+                if (tid == 0) *(float4*)&Scl[4 * slot] = v;
+            }
+        }
+    };
     TileWalk ic(sv, sv.first_seq(w), g0, g1);   // issue cursor
     TileWalk cc = ic;                            // compute cursor (the tile being scored)
 
@@ -759,9 +781,11 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         size_t r0, r1;
         dma.rows(ic, r0, r1);
         dma.issue(ic, 0, r0, r1);
+        note_scales(0, ic.past(), r0, r1);
         ic.next(sv);
         dma.rows(ic, r0, r1);
         dma.issue(ic, 1, r0, r1);
+        note_scales(1, ic.past(), r0, r1);
         ic.next(sv);
     }
     load_q(cc.b);
@@ -770,6 +794,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         size_t r0, r1;
         dma.rows(ic, r0, r1);
         dma.issue(ic, 2, r0, r1);
+        note_scales(2, ic.past(), r0, r1);
         ic.next(sv);
     }
 
@@ -800,6 +825,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         dma.wait_tile();
         __syncthreads();
         pend = dma.prepare(ic, (buf + 3) % kNBuf, nx0, nx1);   // issued during the step's products
+        note_scales((buf + 3) % kNBuf, ic.past(), nx0, nx1);
         ic.next(sv);
     };
 
@@ -811,8 +837,17 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     // value product after every second score product -- so the matrix core
     // always has an independent product to start; the rest of the value
     // products run beside the softmax.
-    auto step = [&](auto DS, auto DV, const uint8_t* C, int tbase, int n, int pr, int pw) {
+    auto step = [&](auto DS, auto DV, const uint8_t* C, int tbase, int n, int pr, int pw, int slot) {
         constexpr bool do_s = decltype(DS)::value, do_v = decltype(DV)::value;
+        // page scales of the scored tile (PS): c of each half, and this
+        // lane's rho (its A-operand row is token lane % 32)
+        float cs0 = 1.f, cs1 = 1.f, rho = 1.f;
+        if constexpr (PS && do_s) {
+            const float4 sv4 = *(const float4*)&Scl[4 * slot];
+            cs0 = sv4.x;
+            cs1 = sv4.y;
+            rho = (lane % 32) < 16 ? sv4.z / sv4.x : sv4.w / sv4.y;
+        }
         // Value product j of 32: K half kk = j / 16, head tile nt = j / 4 % 4,
         // column tile mc = j % 4.  The P operands of group j / 4 (one K half,
         // one head tile) stream through two slots: group q + 1 is read when
@@ -874,6 +909,10 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                     if (ks % 2 == 0) {
                         a0 = fp8x8_to_bf16(make_uint2(raw[j % PJ].x, raw[j % PJ].y));
                         a1 = fp8x8_to_bf16(make_uint2(raw[j % PJ].z, raw[j % PJ].w));
+                        if (PS && j >= 16) {   // rotary dims: times this token's rho
+                            a0 = scale_bf16x8(a0, rho);
+                            a1 = scale_bf16x8(a1, rho);
+                        }
                         if (j + PJ < KJ) raw[j % PJ] = *(const uint4*)to8.score(C, j + PJ);
                     }
                     const bf16x8 av8 = ks % 2 ? a1 : a0;
@@ -906,6 +945,7 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
             const int nv = n - tbase - 4 * hh;   // this lane's rows r < nv are valid
 #pragma unroll
             for (int v = 0; v < 16; v++) {
+                if constexpr (PS) S[v] *= v < 8 ? cs0 : cs1;   // rows 0..15, then 16..31
                 S[v] = 8 * (v / 4) + v % 4 < nv ? S[v] : -INFINITY;
                 lm = fmaxf(lm, S[v]);
             }
@@ -919,7 +959,12 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(S[v], sc, -m));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(S[v + 1], sc, -m));
                 ps += p0 + p1;
-                pk[v / 2] = pack_bf16x2(p0, p1);
+                if constexpr (PS) {   // the latent sum's weights carry the page's c_scale
+                    const float cv = v < 8 ? cs0 : cs1;
+                    pk[v / 2] = pack_bf16x2(p0 * cv, p1 * cv);
+                } else {
+                    pk[v / 2] = pack_bf16x2(p0, p1);
+                }
             }
             lsum += ps;
             Pb[pw][wave][0][lane] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
@@ -955,19 +1000,19 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         const int gend = min(g1, g + cc.nt - cc.lt);
         // first tile: scores only
         tile_top(buf);
-        step(Y, N, Cs + buf * TL::TILE, cc.lt * kT, cc.n, 0, g & 1);
+        step(Y, N, Cs + buf * TL::TILE, cc.lt * kT, cc.n, 0, g & 1, buf);
         cc.lt++;
         buf = (buf + 1) % kNBuf;
         // then each tile's scores beside the previous tile's latent sum
         for (++g; g < gend; g++) {
             tile_top(buf);
-            step(Y, Y, Cs + buf * TL::TILE, cc.lt * kT, cc.n, (g - 1) & 1, g & 1);
+            step(Y, Y, Cs + buf * TL::TILE, cc.lt * kT, cc.n, (g - 1) & 1, g & 1, buf);
             cc.lt++;
             buf = (buf + 1) % kNBuf;
         }
         // last tile's latent sum
         __syncthreads();   // its P visible
-        step(N, Y, Cs, 0, 0, (g - 1) & 1, 0);
+        step(N, Y, Cs, 0, 0, (g - 1) & 1, 0, 0);
         write_partial(cc.b, F8 ? Stg8 : Cs + ((buf + kNBuf - 1) % kNBuf) * TL::TILE);
         if (g >= g1) break;
         // the next sequence: its tile cursor, accumulators and q^
@@ -1020,6 +1065,9 @@ __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_l
     for (int t0 = t_lo; t0 < t_hi; t0 += kRcRows) {
         uint4 c8[kRcRows];
         uint16_t cr[kRcRows];
+        float rcs[kRcRows], rrs[kRcRows];   // per-page scales (1: none)
+#pragma unroll
+        for (int k = 0; k < kRcRows; k++) rcs[k] = rrs[k] = 1.f;
 #pragma unroll
         for (int k = 0; k < kRcRows; k++) {
             const int t = min(t0 + k, t_hi - 1);
@@ -1029,6 +1077,11 @@ __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_l
                 const uint8_t* c8p = (const uint8_t*)p.cache + row * 576;
                 c8[k] = __builtin_bit_cast(uint4, fp8x8_to_bf16(*(const uint2*)(c8p + 8 * lane)));
                 cr[k] = (uint16_t)(__builtin_bit_cast(uint4, fp8x8_to_bf16(make_uint2(c8p[512 + lane], 0u))).x & 0xffffu);
+                if (p.c_scales) {   // the page's scales
+                    const int blk = (int)(row >> p.bs_log2);
+                    rcs[k] = p.c_scales[blk];
+                    rrs[k] = p.r_scales[blk];
+                }
             } else {
                 c8[k] = *(const uint4*)(cache + row * 576 + 8 * lane);
                 cr[k] = cache[row * 576 + 512 + lane];
@@ -1041,10 +1094,10 @@ __device__ void mla_partial_recompute(const MlaParams& p, int bb, int i, int g_l
             float c[8];
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                c[2 * e] = bf16lo_to_f32(w4[e]);
-                c[2 * e + 1] = bf16hi_to_f32(w4[e]);
+                c[2 * e] = bf16lo_to_f32(w4[e]) * rcs[k];
+                c[2 * e + 1] = bf16hi_to_f32(w4[e]) * rcs[k];
             }
-            float z = q[8] * bf16lo_to_f32(cr[k]);
+            float z = q[8] * (bf16lo_to_f32(cr[k]) * rrs[k]);
 #pragma unroll
             for (int e = 0; e < 8; e++) z = fmaf(q[e], c[e], z);
             z = wave_sum(z) * p.scale_log2;
@@ -1300,16 +1353,24 @@ hipError_t launch_mla(const MlaParams& p, bool paged, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g2 = (unsigned)p.n_wg;
-    if (p.f8) {
+    if (p.f8 && p.c_scales) {
+        if (!paged || !p.r_scales) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((mla_decode_kernel<true, true, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched,
+                           p.c_scales, p.r_scales);
+    } else if (p.f8) {
         if (paged)
-            hipLaunchKernelGGL((mla_decode_kernel<true, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+            hipLaunchKernelGGL((mla_decode_kernel<true, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched,
+                               nullptr, nullptr);
         else
-            hipLaunchKernelGGL((mla_decode_kernel<false, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+            hipLaunchKernelGGL((mla_decode_kernel<false, true>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched,
+                               nullptr, nullptr);
     } else {
         if (paged)
-            hipLaunchKernelGGL((mla_decode_kernel<true, false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+            hipLaunchKernelGGL((mla_decode_kernel<true, false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched,
+                               nullptr, nullptr);
         else
-            hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched);
+            hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(g2), dim3(256), 0, st, p, p.bt, p.s, p.sched,
+                               nullptr, nullptr);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -361,6 +361,50 @@ int attn_decode_mla_absorbed_fp8(void* out, float* u_latent, float* lse, const v
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_mla_absorbed_fp8_paged_scales -- attn_decode_mla_absorbed_fp8
+ * over a paged pool whose pages each carry their own scale pair
+ * ("Multi-Head Latent Attention (MLA): Mathematical Foundations", llms.blog,
+ * section "High-Throughput Serving Kernels: FlashMLA and SGLang": the E4M3
+ * latent is stored with per-block scaling factors; a block is a page here).
+ * Element e of a row in page blk is code * c_scales[blk] (e < d_c) or
+ * code * r_scales[blk].
+ *   c_scales, r_scales : [num_blocks] fp32, device, caller-owned, positive
+ *                        and finite for every page a sequence reaches.
+ *   block_table        : required.  The rest as attn_decode_mla_absorbed_fp8.
+ * In the kernel the rotary codes are widened times r/c of their page (to
+ * bf16), the scores times the page's c scale, and the latent sum's weights
+ * carry the c scale (the sums do not); q^ carries no scale.
+ * Errors: as attn_decode_mla_absorbed_fp8, plus EINVAL for null scales or no
+ * block table.
+ */
+int attn_decode_mla_absorbed_fp8_paged_scales(void* out, float* u_latent, float* lse,
+                                              const void* q_nope, const void* q_rope,
+                                              const void* w_uk, const void* w_uv,
+                                              const void* cache, const float* c_scales,
+                                              const float* r_scales, const int32_t* s,
+                                              const int32_t* block_table, int max_blocks,
+                                              int block_size, int num_blocks, int B, int s_max,
+                                              int h, int d_c, int d_R, int d_nope, int d_v,
+                                              float scale, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
+/*
+ * kv_cache_append_mla_fp8_paged_scales -- kv_cache_append_mla_fp8 into a
+ * paged pool with a scale pair per page: element x of kv_new[b] is stored as
+ * the E4M3 code of x * (1 / c_scales[blk]) (latent part) or
+ * x * (1 / r_scales[blk]) (rotary part), blk the page of slot pos[b]
+ * (reciprocal and product in fp32, nearest with ties to even, saturated at
+ * +-448).  The caller sets a page's scales before its first append.
+ * Errors: as kv_cache_append_mla_fp8, plus EINVAL for null scales or no
+ * block table.
+ */
+int kv_cache_append_mla_fp8_paged_scales(void* cache, const void* kv_new, const float* c_scales,
+                                         const float* r_scales, const int32_t* pos,
+                                         const int32_t* block_table, int max_blocks,
+                                         int block_size, int num_blocks, int B, int s_max,
+                                         int d_c, int d_R, void* stream);
+
+/*
  * attn_decode_mla_absorbed_multi -- attn_decode_mla_absorbed for q_len new
  * tokens per sequence in one call: the tokens a speculative step verifies
  * ("MLA: why one latent can replace a multi-head KV cache",

@@ -8,7 +8,7 @@ import synth
 # bf16 storage with fp32 accumulation, and fp32 storage
 BF16_MAX_ABS, BF16_MEAN_ABS, BF16_REL_RMS = 2e-2, 2e-3, 1e-2
 F32_MAX_ABS = 1e-5
-LSE_BF16, LSE_F32 = 2e-3, 1e-5
+LSE_F32 = 1e-5
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
@@ -38,9 +38,16 @@ def assert_lse_close(gpu: np.ndarray, ref: np.ndarray, b: int, what=""):
     assert np.array_equal(fin, np.isfinite(gpu)), f"{what}: lse finiteness differs"
     assert np.all(np.isneginf(gpu[~fin])), f"{what}: empty rows must give -inf"
     if fin.any():
-        mx = float(np.max(np.abs(gpu[fin] - ref[fin])))
-        tol = LSE_F32 if b == 4 else LSE_BF16
-        assert mx <= tol * max(1.0, float(np.max(np.abs(ref[fin])))), f"{what}: lse err {mx:.3e}"
+        err = np.abs(gpu[fin] - ref[fin])
+        mx = float(np.max(err))
+        if b == 4:
+            assert mx <= LSE_F32 * max(1.0, float(np.max(np.abs(ref[fin])))), f"{what}: lse err {mx:.3e}"
+        else:
+            # the bf16 bounds on every result: max-abs <= 2e-2, mean-abs <= 2e-3
+            # (a sequence of one token has lse = that token's score, which
+            # carries the bf16 rounding of the absorbed MLA query unaveraged)
+            assert mx <= BF16_MAX_ABS, f"{what}: lse max-abs {mx:.3e}"
+            assert float(np.mean(err)) <= BF16_MEAN_ABS, f"{what}: lse mean-abs {np.mean(err):.3e}"
 
 
 def gqa_sample_reference(d, shape, pairs):

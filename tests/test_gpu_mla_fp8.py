@@ -155,3 +155,123 @@ def test_append_bit_exact(paged):
         want = oracle.kv_append_mla_fp8(host, synth.host_bits(kv.cpu()), cs, rs, pos, 512)
     torch.cuda.synchronize()
     assert np.array_equal(synth.host_bits(cache), want)
+
+
+# ---- one scale pair per page (attn_decode_mla_absorbed_fp8_paged_scales) ----
+def page_scales(n_blk, seed, lo=0.5 * CS, hi=1.5 * CS):
+    """Per-page latent and rotary scales, unrelated across pages and parts
+    (around the scale the codes were drawn with, so that the values stay
+    O(1) like the other tests' and the bf16 bounds mean the same)."""
+    rng = np.random.default_rng(seed)
+    cs = rng.uniform(lo, hi, size=n_blk).astype(np.float32)
+    rs = rng.uniform(lo, hi, size=n_blk).astype(np.float32)
+    return cs, rs
+
+
+def run_paged_scales(sh, sample=None, seed=0, poke=None):
+    print(f"[mla-fp8-pages] B={sh.B} h={sh.h} s={list(sh.s)[:6]}", flush=True)
+    d = synth.draw_mla_fp8(sh, CS, RS, device=DEV)
+    n_blk = d["cache8"].shape[0]
+    cs, rs = page_scales(n_blk, seed)
+    if poke is not None:
+        poke(d, cs, rs)
+    out, ul, lse = A.decode_mla(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["cache8"], d["s"],
+                                block_table=d["block_table"], s_max=sh.s_max,
+                                c_scale=torch.from_numpy(cs).to(DEV),
+                                r_scale=torch.from_numpy(rs).to(DEV))
+    torch.cuda.synchronize()
+    pool = synth.host_bits(d["cache8"])
+    W = [synth.host_bits(d[k]) for k in ("w_uk", "w_uv")]
+    for bi in (range(sh.B) if sample is None else sample):
+        args = [synth.host_bits(d[k][bi:bi + 1]) for k in ("q_nope", "q_rope")]
+        bt = d["block_table_host"][bi:bi + 1]
+        ro, ru, rl = oracle.mla_absorbed_fp8_paged_scales(args[0], args[1], *W, pool, cs, rs,
+                                                          np.array([int(sh.s[bi])], np.int32), bt)
+        assert_close(to_f64(out[bi:bi + 1]), ro, 2, f"out b={bi}")
+        assert_close(to_f64(ul[bi:bi + 1]), ru, 2, f"u_latent b={bi}")
+        assert_lse_close(to_f64(lse[bi:bi + 1]), rl, 2, f"lse b={bi}")
+    return d, out, ul, lse
+
+
+@pytest.mark.parametrize("h", [16, 128])
+def test_page_scales_heads(h):
+    run_paged_scales(shape(3, h, (77, 300, 1025), paged=True, seed=h + 520), seed=h)
+
+
+@pytest.mark.parametrize("s", [(0, 40), (1, 15), (16, 17), (33, 0)])
+def test_page_scales_short_and_empty(s):
+    run_paged_scales(shape(2, 32, s, paged=True, seed=sum(s) + 521), seed=sum(s))
+
+
+def test_page_scales_mixed_lengths_long():
+    rng = np.random.default_rng(522)
+    s = tuple(int(x) for x in rng.integers(0, 6000, size=24)) + (20000,)
+    run_paged_scales(shape(25, 64, s, paged=True, seed=522), sample=[0, 9, 24], seed=522)
+
+
+def test_page_scales_peaked_logits_take_the_rescaling_path():
+    sh = shape(2, 128, (300, 5000), paged=True, seed=523)
+
+    def poke(d, cs, rs):
+        # a spike of value length 40 in both parts (as the bf16 test), on a
+        # page whose scales are set to 0.08: 500 code units
+        qt = torch.matmul(d["q_nope"][:, 0].float(), d["w_uk"][0].float())
+        tab = d["block_table_host"]
+        for bi, t in ((0, 200), (1, 4000)):
+            blk = int(tab[bi, t // 16])
+            cs[blk] = rs[blk] = 0.08
+            c = qt[bi] / qt[bi].norm() * 40.0
+            r = d["q_rope"][bi, 0].float()
+            kr = r / r.norm() * 40.0
+            d["cache8"][blk, t % 16] = torch.cat([synth.fp8_codes(c, 0.08), synth.fp8_codes(kr, 0.08)])
+
+    _, _, _, lse = run_paged_scales(sh, seed=523, poke=poke)
+    assert float(lse[0, 0]) > 50            # the spike dominates head 0
+
+
+def test_page_scales_paged_mla_full_size_sampled():
+    sh = synth.configs()["paged_mla"]
+    lens = np.asarray(sh.s)
+    run_paged_scales(sh, sample=[int(np.argmin(lens)), int(np.argmax(lens))], seed=524)
+
+
+def test_page_scales_append_bit_exact():
+    B, W = 5, 576
+    rng = np.random.default_rng(525)
+    kv = torch.from_numpy(rng.standard_normal((B, W)).astype(np.float32) * 3).to(torch.bfloat16)
+    kv[0, 0], kv[0, 1], kv[0, 513] = float("nan"), 1e6, -1e6
+    kv = kv.to(DEV)
+    pos = np.array([0, 39, 16, 15, 7], np.int32)
+    nblk = B * 3
+    bt = rng.permutation(nblk).astype(np.int32).reshape(B, 3)
+    cs, rs = page_scales(nblk, 525, 0.005, 0.5)
+    cache = torch.from_numpy(rng.integers(0, 256, size=(nblk, 16, W), dtype=np.uint8)).to(DEV)
+    host = synth.host_bits(cache)
+    A.kv_cache_append_mla_fp8_paged_scales(cache, kv, torch.from_numpy(cs).to(DEV),
+                                           torch.from_numpy(rs).to(DEV),
+                                           torch.from_numpy(pos).to(DEV),
+                                           torch.from_numpy(bt).to(DEV), 3, 16, nblk, B, 48, 512, 64)
+    want = oracle.kv_append_mla_fp8_paged_scales(host, synth.host_bits(kv.cpu()), cs, rs, pos, 512,
+                                                 bt)
+    torch.cuda.synchronize()
+    assert np.array_equal(synth.host_bits(cache), want)
+
+
+def test_page_scales_bad_arguments():
+    sh = shape(1, 16, (10,), paged=True, seed=526)
+    d = synth.draw_mla_fp8(sh, CS, RS, device=DEV)
+    out = torch.empty((1, 16, 128), dtype=torch.bfloat16, device=DEV)
+    sc = torch.ones(d["cache8"].shape[0], dtype=torch.float32, device=DEV)
+    bt = d["block_table"]
+    kw = dict(check=False)
+    rc = A.attn_decode_mla_absorbed_fp8_paged_scales(out, None, None, d["q_nope"], d["q_rope"],
+                                                     d["w_uk"], d["w_uv"], d["cache8"], None, sc,
+                                                     d["s"], bt, bt.shape[1], 16,
+                                                     d["cache8"].shape[0], 1, 16, 16, 512, 64, 128,
+                                                     128, 0.0, None, 0, **kw)
+    assert rc == A.ATTN_EINVAL
+    rc = A.attn_decode_mla_absorbed_fp8_paged_scales(out, None, None, d["q_nope"], d["q_rope"],
+                                                     d["w_uk"], d["w_uv"], d["cache8"], sc, sc,
+                                                     d["s"], None, 0, 16, 0, 1, 16, 16, 512, 64,
+                                                     128, 128, 0.0, None, 0, **kw)
+    assert rc == A.ATTN_EINVAL

@@ -678,13 +678,6 @@ def main():
         sys.exit(2)
     import decode_attention_kv_attn_amd as A
     A.lib()
-    if args.sweep:
-        sweep(args)
-        return
-    if args.mla_modes:
-        mla_modes(args)
-        return
-
     if args.calib_copy:   # a plain copy of known size, for the counter calibration
         x = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")   # 1 GiB
         y = torch.empty_like(x)
@@ -692,6 +685,12 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         del x, y
+    if args.sweep:
+        sweep(args)
+        return
+    if args.mla_modes:
+        mla_modes(args)
+        return
 
     kept = []
     sh, total_ms, per = run_gqa(args.config, args.steps, args.warmup, rotate=1, keep=kept)

@@ -321,10 +321,12 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(const GqaParams p,
 // Merge of the split partials: m = max m_k over splits that saw tokens,
 // l = sum 2^(m_k-m) l_k, o = sum 2^(m_k-m) o_k / l, lse = (m + log2 l) ln 2.
 // One workgroup of NWV wavefronts per (b, head); each wavefront merges a
-// contiguous range of the splits (its own max, weights and sums, 16 partial
-// rows in flight, lane = D/64 output elements), then the wavefronts' results
-// are merged the same way through LDS.  A split with l = 0 never wrote its
-// partial row: it is loaded but not used.
+// contiguous range of the splits in chunks of 16 with a running maximum
+// (lane = D/64 output elements), then the wavefronts' results are merged the
+// same way through LDS.  A chunk's (m, l) pairs, its 16 partial rows and the
+// sequence's length are loaded together, so a wavefront with at most 16
+// splits waits for memory once.  Only the splits that hold tokens of the
+// sequence wrote their rows; the others are loaded but not used.
 template <int D, bool F32, int NWV>
 __global__ __launch_bounds__(64 * NWV) void gqa_combine_kernel(const GqaParams p)
 {
@@ -336,54 +338,45 @@ __global__ __launch_bounds__(64 * NWV) void gqa_combine_kernel(const GqaParams p
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int bh = blockIdx.x;
     const int ns = p.n_split;
-    // only the splits that hold tokens of this row's sequence were written
-    const int len = min(max(p.s[bh / (p.q_len * p.h)], 0), p.s_max);
-    const int nsb = min(ns, (len + p.chunk - 1) / p.chunk);
-    const int per = (nsb + NWV - 1) / NWV;
-    const int k_lo = min(wave * per, nsb), k_hi = min(k_lo + per, nsb);
+    const int slen = p.s[bh / (p.q_len * p.h)];   // used once the chunk's loads are out
+    const int per = (ns + NWV - 1) / NWV;
+    const int k_lo = min(wave * per, ns), k_hi = min(k_lo + per, ns);
     const float2* __restrict__ ml = (const float2*)p.part_ml + (size_t)bh * ns;
     const float* __restrict__ po = p.part_o + (size_t)bh * ns * D + lane * PL;
-    float M = -INFINITY;
-    for (int k = k_lo + lane; k < k_hi; k += 64) {
-        const float2 v = ml[k];
-        if (v.y > 0.f) M = fmaxf(M, v.x);
-    }
-    M = wave_max(M);
-    float L = 0.f, o[PL];
+    float M = -INFINITY, L = 0.f, o[PL];
 #pragma unroll
     for (int e = 0; e < PL; e++) o[e] = 0.f;
-    for (int k0 = k_lo; k0 < k_hi; k0 += 64) {
-        float wk = 0.f;
-        if (k0 + lane < k_hi) {
-            const float2 v = ml[k0 + lane];
-            if (v.y > 0.f) {
-                wk = __builtin_amdgcn_exp2f(v.x - M);
-                L = fmaf(wk, v.y, L);
+    for (int k0 = k_lo; k0 < k_hi; k0 += U) {
+        const int cnt = min(U, k_hi - k0);
+        // clamped, unconditional loads: lane u < cnt's pair, and all cnt rows
+        const float2 v = ml[k0 + min(lane % U, cnt - 1)];
+        float x[U][PL];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int k = k0 + min(u, cnt - 1);
+#pragma unroll
+            for (int e = 0; e < PL; e++) x[u][e] = po[(size_t)k * D + e];
+        }
+        const int len = min(max(slen, 0), p.s_max);
+        const int nsb = min(ns, (len + p.chunk - 1) / p.chunk);   // splits that were written
+        const bool use = lane < cnt && k0 + lane < nsb && v.y > 0.f;
+        const float Mc = fmaxf(M, wave_max(use ? v.x : -INFINITY));
+        if (Mc == -INFINITY) continue;   // wave-uniform: nothing seen yet
+        const float sc = __builtin_amdgcn_exp2f(M - Mc);   // 0 while M = -inf
+        const float wk = use ? __builtin_amdgcn_exp2f(v.x - Mc) : 0.f;
+        L = fmaf(L, sc, wave_sum(wk * (use ? v.y : 0.f)));
+#pragma unroll
+        for (int e = 0; e < PL; e++) o[e] *= sc;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), u));
+            if (u < cnt && wu > 0.f) {
+#pragma unroll
+                for (int e = 0; e < PL; e++) o[e] = fmaf(wu, x[u][e], o[e]);
             }
         }
-        const int cnt = min(64, k_hi - k0);
-        for (int kk = 0; kk < cnt; kk += U) {
-            float x[U][PL];
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int k = k0 + min(kk + u, cnt - 1);   // clamped: loads stay unconditional
-#pragma unroll
-                for (int e = 0; e < PL; e++) x[u][e] = po[(size_t)k * D + e];
-            }
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                if (kk + u < cnt) {
-                    const float wu = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), kk + u));
-                    if (wu > 0.f) {
-#pragma unroll
-                        for (int e = 0; e < PL; e++) o[e] = fmaf(wu, x[u][e], o[e]);
-                    }
-                }
-            }
-        }
+        M = Mc;
     }
-    L = wave_sum(L);
     if (NWV > 1) {
         if (lane == 0) {
             sM[wave] = M;
@@ -422,10 +415,11 @@ __global__ __launch_bounds__(64 * NWV) void gqa_combine_kernel(const GqaParams p
 template <int D, bool F32>
 static void launch_combine_d(const GqaParams& p, unsigned cg, hipStream_t st)
 {
-    // more wavefronts per (b, head) when there are many splits to merge
-    if (p.n_split <= 32)
+    // more wavefronts per (b, head) when there are many splits to merge, so
+    // that each wavefront's share fits one chunk of 16 where it can
+    if (p.n_split <= 16)
         hipLaunchKernelGGL((gqa_combine_kernel<D, F32, 1>), dim3(cg), dim3(64), 0, st, p);
-    else if (p.n_split <= 256)
+    else if (p.n_split <= 64)
         hipLaunchKernelGGL((gqa_combine_kernel<D, F32, 4>), dim3(cg), dim3(256), 0, st, p);
     else
         hipLaunchKernelGGL((gqa_combine_kernel<D, F32, 16>), dim3(cg), dim3(1024), 0, st, p);

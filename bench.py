@@ -434,6 +434,43 @@ def run_mla_fp8(name, steps, warmup, rotate, c_scale=1.0 / 32, r_scale=1.0 / 32)
     return sh, total_ms, per
 
 
+def run_mla_fp8_pages(name, steps, warmup, c_scale=1.0 / 32, r_scale=1.0 / 32, pages=True):
+    """The paged MLA workload over E4M3 pages, with one scale pair per page
+    (pages=True, scales drawn around c_scale / r_scale) or per-tensor scales."""
+    import torch
+    import synth
+    import decode_attention_kv_attn_amd as A
+    sh = synth.configs()[name]
+    d = synth.draw_mla_fp8(sh, c_scale, r_scale, device="cuda")
+    n_blk = d["cache8"].shape[0]
+    g = torch.Generator(device="cuda").manual_seed(sh.seed + 17)
+    cs = (0.5 + torch.rand(n_blk, generator=g, device="cuda")) * c_scale
+    rs = (0.5 + torch.rand(n_blk, generator=g, device="cuda")) * r_scale
+    out = torch.empty((sh.B, sh.h, sh.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((sh.B, sh.h), dtype=torch.float32, device="cuda")
+    wsb = A.attn_decode_workspace_bytes(1, sh.B, sh.s_max, sh.h, 1, sh.d_c, sh.d_R)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    bt = d["block_table"]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def call():
+        if pages:
+            A.attn_decode_mla_absorbed_fp8_paged_scales(out, None, lse, d["q_nope"], d["q_rope"],
+                                                        d["w_uk"], d["w_uv"], d["cache8"], cs, rs,
+                                                        d["s"], bt, bt.shape[1], sh.block_size,
+                                                        n_blk, sh.B, sh.s_max, sh.h, sh.d_c, sh.d_R,
+                                                        sh.d_nope, sh.d_v, 0.0, ws, wsb, sp)
+        else:
+            A.attn_decode_mla_absorbed_fp8(out, None, lse, d["q_nope"], d["q_rope"], d["w_uk"],
+                                           d["w_uv"], d["cache8"], c_scale, r_scale, d["s"], bt,
+                                           bt.shape[1], sh.block_size, n_blk, sh.B, sh.s_max, sh.h,
+                                           sh.d_c, sh.d_R, sh.d_nope, sh.d_v, 0.0, ws, wsb, sp)
+
+    total_ms, per = time_calls(call, steps, warmup, stream)
+    return sh, total_ms, per
+
+
 def cpu_baseline_gqa(sh, d, budget_s=15.0):
     """Time the oracle (as it stands) on a bounded sample of the same inputs,
     copied from the device: the first Bs sequences of the batch (all heads,
@@ -768,6 +805,26 @@ def main():
                                  "alg_bytes_per_call": fab}
         except Exception as e:
             rec["mla"]["fp8"] = {"error": str(e)[:200]}
+        if not args.no_fp8:
+            try:   # the paged MLA batch over E4M3 pages: per-tensor scales, then a scale pair per page
+                t = {}
+                for key, pages in (("per_tensor", False), ("per_page", True)):
+                    psh, ptot, pper = run_mla_fp8_pages("paged_mla", args.steps, args.warmup,
+                                                        pages=pages)
+                    t[key] = ptot / args.steps
+                    torch.cuda.empty_cache()
+                pab = mla_fp8_alg_bytes(psh)
+                pfl = mla_flops(psh)
+                pfloor = max(pab / (HBM_PEAK_GBPS * 1e9), pfl / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                rec["mla"]["fp8_pages"] = {
+                    "workload": f"paged_mla: B={psh.B} ragged lengths, E4M3 latent pages, one latent "
+                                f"and one rotary scale per page",
+                    "us_per_call": t["per_page"] * 1e3,
+                    "us_per_call_per_tensor_scales": t["per_tensor"] * 1e3,
+                    "roofline_frac": pfloor / (t["per_page"] * 1e-3),
+                    "alg_bytes_per_call": pab}
+            except Exception as e:
+                rec["mla"]["fp8_pages"] = {"error": str(e)[:200]}
         if not args.no_out and "steps_per_s" in rec["mla"]:
             try:   # the same layer through the output projection, both forms
                 import decode_attention_kv_attn_amd as A

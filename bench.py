@@ -218,9 +218,15 @@ def run_dcp_gqa(name, n, steps, warmup):
     import decode_attention_kv_attn_amd as A
     sh = synth.configs()[name]
     S = (sh.s_max + n - 1) // n
-    q = torch.randn((sh.B, sh.h, sh.d_h), device="cuda").to(torch.bfloat16)
-    K = torch.randn((sh.B, S, sh.h_kv, sh.d_h), device="cuda").to(torch.bfloat16)
-    V = torch.randn_like(K)
+    g = torch.Generator(device="cuda").manual_seed(sh.seed + 31)
+    q = torch.randn((sh.B, sh.h, sh.d_h), generator=g, device="cuda").to(torch.bfloat16)
+    # the slice's K/V rotate over enough sets (>= 1.2 GB) that the Infinity
+    # Cache cannot serve a call from the previous one
+    slice_bytes = 2 * sh.B * S * sh.h_kv * sh.d_h * 2
+    rot = max(1, min(32, -(-1200000000 // slice_bytes)))
+    kv = [(torch.randn((sh.B, S, sh.h_kv, sh.d_h), generator=g, device="cuda").to(torch.bfloat16),
+           torch.randn((sh.B, S, sh.h_kv, sh.d_h), generator=g, device="cuda").to(torch.bfloat16))
+          for _ in range(rot)]
     s = torch.full((sh.B,), S, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     parts_o = torch.empty((n, sh.B, sh.h, sh.d_h), dtype=torch.bfloat16, device="cuda")
@@ -231,15 +237,21 @@ def run_dcp_gqa(name, n, steps, warmup):
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
+    it = [0]
+
     def call():
         # this GPU's slice writes its own row of the gathered partials; the
         # other rows stand for the slices received from the other GPUs
+        K, V = kv[it[0] % rot]
+        it[0] += 1
         A.attn_decode_gqa(parts_o[0], parts_l[0], q, K, V, s, None, 0, 16, 0, sh.B, S, sh.h,
                           sh.h_kv, sh.d_h, 2, 0.0, ws, wsb, sp)
         A.attn_merge_partials(out, lse, parts_o, parts_l, n, sh.B, sh.h, sh.d_h, 2, 2, sp)
 
     total_ms, per = time_calls(call, steps, warmup, stream)
-    return sh, S, total_ms / steps, per
+    del kv
+    torch.cuda.empty_cache()
+    return sh, S, total_ms / steps, per, rot
 
 
 def run_mla(name, steps, warmup, rotate, keep=None):
@@ -911,7 +923,7 @@ def main():
     if not args.no_dcp:
         try:   # the exchange step of context-parallel decode, on one GPU
             mms_, mper, malg = run_merge(8, 32, 128, 512, args.steps, args.warmup)
-            dsh, S, dms, dper = run_dcp_gqa("llama3_70b_gqa8_b1", 8, args.steps, args.warmup)
+            dsh, S, dms, dper, drot = run_dcp_gqa("llama3_70b_gqa8_b1", 8, args.steps, args.warmup)
             rec["dcp"] = {
                 "merge": {"workload": "attn_merge_partials: 8 slices of fp32 MLA latent partials "
                                       "(B=32, h=128, d_c=512) + lse -> fp32",
@@ -920,7 +932,8 @@ def main():
                           "hbm_gbps": malg / (mms_ * 1e-3) / 1e9,
                           "hbm_frac": malg / (mms_ * 1e-3) / 1e9 / HBM_PEAK_GBPS},
                 "gqa_slice": {"workload": f"{dsh.name}: one GPU's 1/8 token slice (s={S}) decode "
-                                          f"+ merge of 8 slice partials",
+                                          f"+ merge of 8 slice partials (slice K/V rotated over "
+                                          f"{drot} sets)",
                               "us_per_step": dms * 1e3, "median_us": float(np.median(dper)) * 1e3}}
         except Exception as e:  # reports its own failure, the line still prints
             rec["dcp"] = {"error": str(e)[:200]}

@@ -134,3 +134,95 @@ def test_append_then_decode_graph():
         vn.copy_(torch.randn_like(vn, dtype=torch.float32).to(torch.bfloat16))
 
     replay_and_compare(g, eager, [out], mutate)
+
+
+def capture_and_check(call, outs, mutate):
+    """Warm up on a side stream, capture call(outs...) there, then replay and
+    compare against eager calls into fresh tensors."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(outs, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(outs, s)
+
+    def eager():
+        fresh = [torch.empty_like(o) for o in outs]
+        call(fresh, torch.cuda.current_stream())
+        return fresh
+
+    replay_and_compare(g, eager, outs, mutate)
+
+
+def mla_shape(B, h, s, q_len=1, d_model=512, seed=95):
+    return synth.MlaShape("t", B=B, h=h, d_c=512, d_R=64, d_nope=128, d_v=128, s=tuple(s),
+                          seed=seed, q_len=q_len, d_model=d_model)
+
+
+def mutate_mla(d, lens):
+    def mutate(r):
+        d["q_nope"].copy_(torch.randn_like(d["q_nope"], dtype=torch.float32).to(torch.bfloat16))
+        d["s"].copy_(torch.tensor([max(n - 97 * r, 0) for n in lens], dtype=torch.int32, device=DEV))
+    return mutate
+
+
+def test_mla_multi_token_graph():
+    lens = (1500, 40)
+    sh = mla_shape(2, 32, lens, q_len=3, seed=96)
+    d = synth.draw_mla(sh, device=DEV)
+    ws = torch.zeros(A.attn_decode_mla_multi_workspace_bytes(2, 3, 32, 512, 64), dtype=torch.uint8,
+                     device=DEV)
+    outs = [torch.empty((2, 3, 32, 128), dtype=torch.bfloat16, device=DEV),
+            torch.empty((2, 3, 32), dtype=torch.float32, device=DEV)]
+
+    def call(o, st):
+        A.attn_decode_mla_absorbed_multi(o[0], None, o[1], d["q_nope"], d["q_rope"], d["w_uk"],
+                                         d["w_uv"], d["cache"], d["s"], None, 0, 16, 0, 2, 3,
+                                         sh.s_max, 32, 512, 64, 128, 128, 2, 0.0, ws, ws.numel(),
+                                         st.cuda_stream)
+
+    capture_and_check(call, outs, mutate_mla(d, lens))
+
+
+@pytest.mark.parametrize("merged", [False, True])
+def test_mla_output_projection_graph(merged):
+    lens = (2000, 333)
+    sh = mla_shape(2, 16, lens, seed=97 + merged)
+    d = synth.draw_mla(sh, device=DEV)
+    w_o = synth.draw_w_o(sh, device=DEV)
+    w_abs = A.premerge_weights(w_o, d["w_uv"]) if merged else None
+    ws = torch.zeros(A.attn_decode_mla_out_workspace_bytes(merged, 2, 1, 16, 512, 64,
+                                                           0 if merged else 128, 512),
+                     dtype=torch.uint8, device=DEV)
+    outs = [torch.empty((2, 512), dtype=torch.bfloat16, device=DEV),
+            torch.empty((2, 16), dtype=torch.float32, device=DEV)]
+
+    def call(o, st):
+        if merged:
+            A.attn_decode_mla_out_premerged(o[0], o[1], d["q_nope"], d["q_rope"], d["w_uk"], w_abs,
+                                            d["cache"], d["s"], None, 0, 16, 0, 2, 1, sh.s_max, 16,
+                                            512, 64, 128, 512, 2, 0.0, ws, ws.numel(), st.cuda_stream)
+        else:
+            A.attn_decode_mla_out(o[0], o[1], d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], w_o,
+                                  d["cache"], d["s"], None, 0, 16, 0, 2, 1, sh.s_max, 16, 512, 64,
+                                  128, 128, 512, 2, 0.0, ws, ws.numel(), st.cuda_stream)
+
+    capture_and_check(call, outs, mutate_mla(d, lens))
+
+
+def test_mla_mha_mode_graph():
+    lens = (700, 90)
+    sh = mla_shape(2, 16, lens, q_len=40, seed=99)
+    d = synth.draw_mla(sh, device=DEV)
+    ws = torch.zeros(A.attn_decode_mla_mha_workspace_bytes(2, sh.s_max, 16), dtype=torch.uint8,
+                     device=DEV)
+    outs = [torch.empty((2, 40, 16, 128), dtype=torch.bfloat16, device=DEV),
+            torch.empty((2, 40, 16), dtype=torch.float32, device=DEV)]
+
+    def call(o, st):
+        A.attn_decode_mla_mha(o[0], o[1], d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["cache"],
+                              d["s"], None, 0, 16, 0, 2, 40, sh.s_max, 16, 512, 64, 128, 128, 2, 0.0,
+                              ws, ws.numel(), st.cuda_stream)
+
+    capture_and_check(call, outs, mutate_mla(d, lens))

@@ -57,7 +57,7 @@ def run(sh, sample=None):
     return d, out, lse
 
 
-@pytest.mark.parametrize("q_len", [1, 5, 64, 100])
+@pytest.mark.parametrize("q_len", [1, 5, 64, 100, 300])
 def test_query_block_lengths(q_len):
     run(shape(2, 16, (130, 777), q_len, seed=60 + q_len))
 

@@ -120,3 +120,8 @@ def test_deepseek_v3_full_size_two_tokens_sampled():
     base = synth.configs()["deepseek_v3_mla"]
     sh = shape(base.B, base.h, base.s, 2, seed=base.seed)
     run(sh, sample=[0, sh.B - 1])
+
+
+def test_long_query_block_paged():
+    # 96 positions per sequence: 192 query rows, several of them seeing nothing
+    run(shape(2, 16, (50, 900), 96, paged=True, seed=26), sample=[0, 1])

@@ -600,18 +600,24 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     // paged pool, whose block-table walk needs registers of its own
     constexpr int PD = PAGED ? MLA_PD - 1 : MLA_PD;
 #ifndef MLA_NU1
-#define MLA_NU1 16
+#define MLA_NU1 0
+#endif
+#ifndef MLA_NU1_F8
+#define MLA_NU1_F8 16
 #endif
     // latent-sum products of the previous tile issued between the score
-    // products (the others run beside the softmax)
-    constexpr int NU1 = MLA_NU1;
+    // products (the others run beside the softmax).  bf16 tiles: none -- the
+    // score chain then runs alone (1,770 cycles a tile against 2,220 with 16
+    // interleaved) and all 32 cover the softmax (1,460 against 1,200 cycles):
+    // 5 % fewer cycles a tile.  E4M3 tiles measured faster with 16.
+    constexpr int NU1 = F8 ? MLA_NU1_F8 : MLA_NU1;
     constexpr int MCW = 4;          // 32-column tiles of the latent sum per wavefront
     constexpr int NTH = 4;          // 32-head tiles of the latent sum (all heads; zeros past h)
 #ifndef MLA_SCH
 #define MLA_SCH 1
 #endif
     constexpr int SCH = MLA_SCH;    // score accumulation chains (1 or 2)
-    static_assert((NU1 == 0 || NU1 == 16 || NU1 == 32) && (SCH == 1 || SCH == 2), "interleave");
+    static_assert((NU1 == 0 || NU1 == 8 || NU1 == 16 || NU1 == 32) && (SCH == 1 || SCH == 2), "interleave");
     using TL = MlaTile<F8>;
     __shared__ __attribute__((aligned(1024))) uint8_t Cs[kNBuf * TL::TILE];
     // P of every head tile in B-operand layout, for two tiles: the value
@@ -866,8 +872,8 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
         // in the score phase: value products 0 .. NU1 - 1, one after each
         // score product (NU1 = 32) or after every second one (NU1 = 16)
         auto interleave = [&](int ks) {
-            if (NU1 == 32 && ks < 32) vprod(ks);
-            if (NU1 == 16 && ks % 2 == 1 && ks < 32) vprod(ks / 2);
+            constexpr int IV = NU1 ? 32 / NU1 : 1;   // score products per interleaved value product
+            if (NU1 && ks < 32 && ks % IV == IV - 1) vprod(ks / IV);
         };
         // the prepared refill, one instruction every DMA_EVERY score products
         constexpr int DMA_EVERY = KS / Dma::SPW;
@@ -980,14 +986,18 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                 }
         }
 #ifndef MLA_VPG
-#define MLA_VPG 6
+#define MLA_VPG 4
+#endif
+#ifndef MLA_VPG_F8
+#define MLA_VPG_F8 6
 #endif
         if constexpr (do_s && do_v) {
-            // one value product, then MLA_VPG vector instructions, and so on
+            // one value product, then VPG vector instructions, and so on
+            constexpr int VPG = F8 ? MLA_VPG_F8 : MLA_VPG;
 #pragma unroll
             for (int j = NU1; j < 32; j++) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, MLA_VPG, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, VPG, 0);
             }
         }
     };

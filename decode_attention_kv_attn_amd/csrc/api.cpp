@@ -9,6 +9,8 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 #include <string>
 
 #include "kernels.h"
@@ -120,8 +122,9 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
     if (P.n_split > 1) {
         P.part_o_bytes = align256((size_t)B * q_len * h * P.n_split * d_h * sizeof(float));
         P.part_ml_bytes = align256((size_t)B * q_len * h * P.n_split * 2 * sizeof(float));
+        // the arrival counters (the workspace's first kArriveBytes), then the partials
+        P.ws_bytes = attn::kArriveBytes + P.part_o_bytes + P.part_ml_bytes;
     }
-    P.ws_bytes = P.part_o_bytes + P.part_ml_bytes;
     return P;
 }
 
@@ -159,7 +162,9 @@ MlaPlan plan_mla(int B, int h, int d_c, int d_R)
     P.part_ml_bytes = align256(slots * h * 2 * sizeof(float));
     P.flag_bytes = align256((size_t)P.n_wg * sizeof(int32_t));
     P.sched_bytes = align256(((size_t)B + 1 + P.n_wg + 1) * sizeof(int32_t));
-    P.ws_bytes = P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.flag_bytes + P.sched_bytes;
+    // after the arrival-counter prefix that every workspace keeps
+    P.ws_bytes = attn::kArriveBytes + P.qhat_bytes + P.part_u_bytes + P.part_ml_bytes + P.flag_bytes +
+                 P.sched_bytes;
     return P;
 }
 
@@ -292,8 +297,8 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     p.v = cache_v;
     p.s = s;
     p.bt = block_table;
-    p.part_o = (float*)workspace;
-    p.part_ml = (float*)((char*)workspace + P.part_o_bytes);
+    p.part_o = (float*)((char*)workspace + attn::kArriveBytes);
+    p.part_ml = (float*)((char*)workspace + attn::kArriveBytes + P.part_o_bytes);
     p.max_blocks = max_blocks;
     p.bs_log2 = block_table ? ilog2(block_size) : 0;
     p.num_blocks = num_blocks;
@@ -311,6 +316,21 @@ int decode_gqa(void* out, float* lse, const void* q, const void* cache_k, const 
     p.v_scale = v_scale;
     p.k_scales = k_scales;
     p.v_scales = v_scales;
+    // Matrix-core kernel with splits: the split partials are merged either
+    // by the separate merge kernel (default) or, with ATTN_GQA_MERGE=fused
+    // in the environment, inside the decode kernel by the last workgroup of
+    // each (b, KV head, row block), which finds out through one arrival
+    // counter per item in the workspace's prefix.  Measured on MI355X the
+    // in-kernel form is no faster: its last workgroup waits for three
+    // device-scope round trips (its stores, the counter, the other
+    // partials), about what the second launch costs, and with many splits
+    // per item one workgroup merges what the merge kernel spreads over many.
+    p.arrive = nullptr;
+    const char* mm = getenv("ATTN_GQA_MERGE");
+    if (mm && strcmp(mm, "fused") == 0 && P.mfma && P.n_split > 1 &&
+        (long long)B * h_kv * P.n_rb <= attn::kArriveCount &&
+        P.part_o_bytes < ((size_t)1 << 31))   // 32-bit byte offsets into the partials
+        p.arrive = (int32_t*)workspace;
     // matrix-core kernel over a paged pool with splits: workgroups go to the
     // non-empty (b, split) pairs only (each workgroup scans the B lengths to
     // find its pair, so only for moderate B); the grid is then a multiple of 8
@@ -538,7 +558,7 @@ int decode_mla(void* out, float* u_latent, float* lse, const void* q_nope, const
     p.cache = cache;
     p.s = s;
     p.bt = block_table;
-    char* ws = (char*)workspace;
+    char* ws = (char*)workspace + attn::kArriveBytes;   // past the arrival counters
     p.qhat = (uint16_t*)ws;
     p.part_u = (_Float16*)(ws + P.qhat_bytes);
     p.part_ml = (float*)(ws + P.qhat_bytes + P.part_u_bytes);
@@ -820,7 +840,8 @@ int attn_mla_premerge_weights(void* w_absorbed, const void* w_o, const void* w_u
 size_t attn_decode_mla_mha_workspace_bytes(int B, int s_max, int h)
 {
     if (B <= 0 || s_max <= 0 || h <= 0) return 0;
-    return 2 * align256((size_t)B * s_max * h * 128 * 2);
+    // the arrival-counter prefix, then the expanded K and V
+    return attn::kArriveBytes + 2 * align256((size_t)B * s_max * h * 128 * 2);
 }
 
 int attn_decode_mla_mha(void* out, float* lse, const void* q_nope, const void* q_rope,
@@ -856,8 +877,9 @@ int attn_decode_mla_mha(void* out, float* lse, const void* q_nope, const void* q
     p.cache = cache;
     p.s = s;
     p.bt = block_table;
-    p.k_exp = (uint16_t*)workspace;
-    p.v_exp = (uint16_t*)((char*)workspace + need / 2);
+    const size_t half = (need - attn::kArriveBytes) / 2;
+    p.k_exp = (uint16_t*)((char*)workspace + attn::kArriveBytes);
+    p.v_exp = (uint16_t*)((char*)workspace + attn::kArriveBytes + half);
     p.max_blocks = max_blocks;
     p.bs_log2 = block_table ? ilog2(block_size) : 0;
     p.num_blocks = num_blocks;

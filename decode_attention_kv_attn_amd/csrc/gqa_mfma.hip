@@ -27,9 +27,12 @@
 //  * O^T[d_h x 16 heads] += V_tile^T . P^T, the V operand read with
 //    transposing LDS reads; the score output layout is the K order of this
 //    product, so P stays in registers;
-//  * splits write (m, l, o) partials that the merge kernel combines through
-//    their log-sum-exp ("MLA: why one latent can replace a multi-head KV
-//    cache", charlestar.github.io, section on what FlashMLA solves).
+//  * splits write (m, l, o) partials that are combined through their
+//    log-sum-exp ("MLA: why one latent can replace a multi-head KV cache",
+//    charlestar.github.io, section on what FlashMLA solves): by the last
+//    workgroup of the (b, KV head, row block) item to finish, which learns
+//    that it is last from an arrival counter, or, without counters, by the
+//    separate merge kernel.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_lds.h"
@@ -112,7 +115,8 @@ struct GTileOffsets {
 };
 
 // Splits of every sequence for the compacted grid: sequence 64 c + lane has
-// nb[c] = ceil(min(max(s, 0), s_max) / chunk) splits.  All B lengths are
+// nb[c] = max(1, ceil(min(max(s, 0), s_max) / chunk)) splits (an empty
+// sequence keeps one workgroup, which writes its zero rows).  All B lengths are
 // loaded at once (B <= 64 kMaxChunks), so finding a workgroup's pair costs one
 // round trip to memory, as reading its own length would.
 constexpr int kMaxChunks = 16;
@@ -126,7 +130,7 @@ struct SplitCounts {
 #pragma unroll
         for (int c = 0; c < kMaxChunks; c++) {
             const int i = 64 * c + lane;
-            nb[c] = i < B ? (min(max(s[i], 0), s_max) + chunk - 1) / chunk : 0;
+            nb[c] = i < B ? max((min(max(s[i], 0), s_max) + chunk - 1) / chunk, 1) : 0;
             t += nb[c];
         }
 #pragma unroll
@@ -176,6 +180,104 @@ __device__ __forceinline__ int pair_head(int j, int flip)
     constexpr int msk = (2 << kb) - 1;
     const int lo = j & msk;
     return (j & ~msk) | (((lo & 1) ^ 1 ^ flip) << kb) | (lo >> 1);
+}
+
+#ifndef GQA_MERGE_U
+#define GQA_MERGE_U 8
+#endif
+// Buffer stores and loads coherent at device scope (cache policy sc1: they
+// pass the XCD's own L2), for the split partials that the last workgroup of
+// an item merges, wherever it runs.  Byte offsets into the partials, which
+// the host keeps below 2^31 when it enables the merge in the kernel.
+constexpr int kPolicyDevice = 16;   // sc1
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+struct PartRsrc {
+    rsrc_t o, ml;
+    __device__ __forceinline__ PartRsrc(const GqaParams& p, int D)
+    {
+        const long long rows = (long long)p.B * p.q_len * p.h * p.n_split;
+        o = make_rsrc(p.part_o, (int)min(rows * D * 4, 0x7fffffffLL));
+        ml = make_rsrc(p.part_ml, (int)min(rows * 8, 0x7fffffffLL));
+    }
+};
+__device__ __forceinline__ void store_dev16(rsrc_t r, uint32_t off, float4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kPolicyDevice);
+}
+__device__ __forceinline__ void store_dev8(rsrc_t r, uint32_t off, float2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, off, 0, kPolicyDevice);
+}
+__device__ __forceinline__ float4 load_dev16(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kPolicyDevice));
+}
+__device__ __forceinline__ float2 load_dev8(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicyDevice));
+}
+// Merge of one item's split partials by its last workgroup: rows r_lo ..
+// r_hi - 1 of (b, KV head j), splits 0 .. nsb - 1, in split order (the
+// result does not depend on the order of arrival).  m = max m_k over splits
+// that saw tokens, l = sum 2^(m_k - m) l_k, o = sum 2^(m_k - m) o_k / l,
+// lse = (m + log2 l) ln 2.  D / 8 threads share a row, 8 output elements
+// each; a thread keeps U splits' loads in flight.
+template <int D, int NT>
+__device__ __forceinline__ void merge_item(const GqaParams& p, int b, int j, int r_lo, int r_hi,
+                                           int nsb, int tid)
+{
+    constexpr int TPR = D / 8;     // threads per row
+    constexpr int RPP = NT / TPR;  // rows per pass
+    constexpr int U = GQA_MERGE_U;
+    const int g = p.h / p.h_kv;
+    const int e0 = 8 * (tid % TPR);
+    const PartRsrc pr(p, D);
+    for (int r = r_lo + tid / TPR; r < r_hi; r += RPP) {
+        const size_t orow = (size_t)(b * p.q_len + r / g) * p.h + j * g + r % g;
+        const uint32_t ml = (uint32_t)(orow * p.n_split * 8);
+        const uint32_t po = (uint32_t)((orow * p.n_split * D + e0) * 4);
+        float M = -INFINITY, L = 0.f, o[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) o[e] = 0.f;
+        for (int k0 = 0; k0 < nsb; k0 += U) {
+            float2 v[U];
+            float4 x[U][2];
+#pragma unroll
+            for (int u = 0; u < U; u++) {   // clamped, unconditional device-scope loads
+                const uint32_t k = min(k0 + u, nsb - 1);
+                v[u] = load_dev8(pr.ml, ml + 8 * k);
+                x[u][0] = load_dev16(pr.o, po + k * D * 4);
+                x[u][1] = load_dev16(pr.o, po + k * D * 4 + 16);
+            }
+            float Mc = M;
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (k0 + u < nsb && v[u].y > 0.f) Mc = fmaxf(Mc, v[u].x);
+            if (Mc == -INFINITY) continue;   // nothing seen yet
+            const float sc = __builtin_amdgcn_exp2f(M - Mc);   // 0 while M = -inf
+            L *= sc;
+#pragma unroll
+            for (int e = 0; e < 8; e++) o[e] *= sc;
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                if (k0 + u < nsb && v[u].y > 0.f) {
+                    const float w = __builtin_amdgcn_exp2f(v[u].x - Mc);
+                    L = fmaf(w, v[u].y, L);
+                    o[0] = fmaf(w, x[u][0].x, o[0]); o[1] = fmaf(w, x[u][0].y, o[1]);
+                    o[2] = fmaf(w, x[u][0].z, o[2]); o[3] = fmaf(w, x[u][0].w, o[3]);
+                    o[4] = fmaf(w, x[u][1].x, o[4]); o[5] = fmaf(w, x[u][1].y, o[5]);
+                    o[6] = fmaf(w, x[u][1].z, o[6]); o[7] = fmaf(w, x[u][1].w, o[7]);
+                }
+            }
+            M = Mc;
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;   // L = 0: no visible token (0 and -inf)
+        *(uint4*)((uint16_t*)p.out + orow * D + e0) =
+            make_uint4(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+                       pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv));
+        if (tid % TPR == 0 && p.lse) p.lse[orow] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    }
 }
 
 template <int D, int NW, bool PAGED, bool F8, int RPW, bool PS = false>
@@ -259,22 +361,19 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
 #pragma unroll
     for (int k = 0; k < RPW; k++) tl[k] = min(t1, n - (p.q_len - 1 - jq[k]));
 
-    if (t0 >= t1) {   // nothing to attend to in this split
+    // splits of this sequence (>= 1; the merge reads partials 0 .. nsb - 1)
+    const int nsb = max((n + p.chunk - 1) / p.chunk, 1);
+    if (t0 >= t1) {
+        // split 0 of an empty sequence: zero rows and lse = -inf; a split
+        // past a sequence's end leaves nothing (the merge does not read it)
+        if (split != 0) return;
 #pragma unroll
         for (int k = 0; k < RPW; k++) {
             if (!(act[k] && hv[k])) continue;
-            if (p.n_split > 1) {
-                if (G == 0) {
-                    float* ml = p.part_ml + (orow[k] * p.n_split + split) * 2;
-                    ml[0] = -INFINITY;
-                    ml[1] = 0.f;
-                }
-            } else {
-                uint16_t* o = (uint16_t*)p.out + orow[k] * D;
+            uint16_t* o = (uint16_t*)p.out + orow[k] * D;
 #pragma unroll
-                for (int mc = 0; mc < C::MC; mc++) *(uint2*)(o + 16 * mc + 4 * G) = make_uint2(0, 0);
-                if (G == 0 && p.lse) p.lse[orow[k]] = -INFINITY;
-            }
+            for (int mc = 0; mc < C::MC; mc++) *(uint2*)(o + 16 * mc + 4 * G) = make_uint2(0, 0);
+            if (G == 0 && p.lse) p.lse[orow[k]] = -INFINITY;
         }
         return;
     }
@@ -485,10 +584,13 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     }
     wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup
 
-    if (!active) return;
+    // the only split of its sequence writes the result itself; with arrival
+    // counters so does any sequence with one split
+    const bool fused = p.arrive != nullptr && nsb > 1;   // workgroup-uniform
+    const bool direct = p.n_split == 1 || (p.arrive != nullptr && nsb == 1);
 #pragma unroll
     for (int k = 0; k < RPW; k++) {
-        if (!act[k]) continue;   // wave-uniform
+        if (!act[k]) continue;   // wave-uniform (false on a wavefront without rows)
         float l = lsum[k];
         l += xor16(l);
         l += xor32(l);
@@ -497,7 +599,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
 #pragma unroll
             for (int mc = 0; mc < C::MC; mc++) O[k][mc] *= p.v_scale;
         }
-        if (p.n_split == 1) {
+        if (direct) {
             const float inv = l > 0.f ? 1.f / l : 0.f;   // l = 0: no visible token (0 and -inf)
             uint16_t* o = (uint16_t*)p.out + orow[k] * D + 4 * G;
 #pragma unroll
@@ -505,6 +607,14 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                 *(uint2*)(o + 16 * mc) = make_uint2(pack_bf16x2(O[k][mc][0] * inv, O[k][mc][1] * inv),
                                                     pack_bf16x2(O[k][mc][2] * inv, O[k][mc][3] * inv));
             if (G == 0 && p.lse) p.lse[orow[k]] = l > 0.f ? (m[k] + __log2f(l)) * kLn2 : -INFINITY;
+        } else if (fused) {   // device-scope stores: the merging workgroup may sit on another XCD
+            const PartRsrc pr(p, D);
+            const uint32_t pi = (uint32_t)(orow[k] * p.n_split + split);
+#pragma unroll
+            for (int mc = 0; mc < C::MC; mc++)
+                store_dev16(pr.o, (pi * D + 16 * mc + 4 * G) * 4,
+                            make_float4(O[k][mc][0], O[k][mc][1], O[k][mc][2], O[k][mc][3]));
+            if (G == 0) store_dev8(pr.ml, pi * 8, make_float2(m[k], l));
         } else {
             const size_t pi = orow[k] * p.n_split + split;
             float* po = p.part_o + pi * D + 4 * G;
@@ -517,6 +627,24 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
             }
         }
     }
+    if (!fused) return;
+    // Arrival.  The partials were written with device-scope stores, which
+    // pass the XCD's own L2; once every wavefront has seen its stores
+    // complete, one lane counts the workgroup in with a device-scope atomic.
+    // The workgroup that brings the count to nsb is the last of its item: it
+    // reads all partials with device-scope loads, merges them and puts the
+    // counter back to zero for the next call.  No workgroup waits for
+    // another, and no L2 is written back or invalidated.
+    __shared__ int s_last;
+    wait_vmcnt<0>();
+    __syncthreads();
+    int32_t* ctr = p.arrive + ((size_t)b * p.h_kv + j) * p.n_rb + rb;
+    if (tid == 0) s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsb - 1;
+    __syncthreads();
+    if (!s_last) return;   // workgroup-uniform
+    const int r_lo = 64 * RPW * rb;
+    merge_item<D, 64 * NW>(p, b, j, r_lo, min(n_rows, r_lo + 64 * RPW), nsb, tid);
+    if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int NW, bool F8, int RPW>
@@ -548,7 +676,7 @@ hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, int rpw, bool pa
                           : launch_mfma_d<128, true>(p, NW, rpw, paged, grid, st);
     else e = d_h == 64 ? launch_mfma_d<64, false>(p, NW, rpw, paged, grid, st)
                        : launch_mfma_d<128, false>(p, NW, rpw, paged, grid, st);
-    if (e != hipSuccess || p.n_split == 1) return e;
+    if (e != hipSuccess || p.n_split == 1 || p.arrive) return e;
     return launch_gqa_combine(p, d_h, false, st);
 }
 

@@ -29,7 +29,17 @@ struct GqaParams {
     float v_scale;       // V scale of an FP8 cache (1 otherwise)
     const float* k_scales;   // paged FP8 cache with one scale per page and KV head: [num_blocks, h_kv]
     const float* v_scales;   // (nullptr: the per-tensor scales above)
+    int32_t* arrive;         // matrix-core kernel with splits: one arrival counter per (b, KV head,
+                             // row block), zero before the call and left zero by it; the last
+                             // workgroup of an item to arrive merges its splits (nullptr: the
+                             // separate merge kernel does)
 };
+
+// Every workspace starts with this many bytes of arrival counters (used by
+// the GQA split merge only, zero-filled when the workspace is allocated and
+// left zero by every call), so that one buffer may serve all entry points.
+constexpr size_t kArriveBytes = (size_t)64 << 10;
+constexpr int kArriveCount = (int)(kArriveBytes / sizeof(int32_t));
 
 // vector kernel (any g; fp32 or bf16), then the split merge when n_split > 1
 hipError_t launch_gqa_decode(const GqaParams& p, int d_h, bool f32, int HG, bool paged,

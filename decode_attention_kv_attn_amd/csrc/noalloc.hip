@@ -6,7 +6,9 @@
 // object on that GPU until the process ends.  In host code the array's name
 // is only a host-side stand-in, never a device address: the address is read
 // once per device with hipGetSymbolAddress (that device current) and kept,
-// and only that address is handed to kernels.
+// and only that address is handed to kernels.  The array has no initialiser,
+// so each copy starts as zeros; its first kArriveBytes serve as the arrival
+// counters of the in-kernel split merge, which every call leaves at zero.
 #include <atomic>
 
 #include "kernels.h"

@@ -38,6 +38,13 @@
  * stream).  Calls only enqueue work and return; results are ready when the
  * stream reaches them.  Concurrent calls must not share a workspace.
  *
+ * Workspaces: every workspace size reported below includes a first 64 KiB
+ * of arrival counters, which only the in-kernel split merge of the GQA
+ * calls uses (see attn_decode_gqa) and no call leaves non-zero.  Zero-fill a
+ * workspace once when it is allocated; after that any call may use it, and
+ * one buffer may serve every entry point.  The rest of a workspace needs no
+ * initialisation.
+ *
  * Cache layouts:
  *   contiguous (block_table == NULL): token t of sequence i is row
  *     i * s_max + t of a [B, s_max, ...] buffer;
@@ -143,6 +150,16 @@ int kv_cache_append(void* cache_k, void* cache_v, const void* k_new, const void*
  *           d_h, 0) bytes of device memory (may be NULL when that is 0).
  * out[b, i] = sum_t softmax_t(scale * q[b,i] . K[b,t,j]) V[b,t,j],
  * j = floor(i / (h / h_kv)).
+ * Long contexts are split over workgroups; the partials are merged through
+ * their log-sum-exp ("MLA: why one latent can replace a multi-head KV
+ * cache", charlestar.github.io, section on what FlashMLA solves) by a
+ * second kernel on the same stream.  With the environment variable
+ * ATTN_GQA_MERGE=fused at the time of the call (bf16 and E4M3 caches), the
+ * last workgroup of each (sequence, KV head) to finish merges them inside
+ * the decode kernel instead, counting arrivals in the workspace's first
+ * 64 KiB (which must then hold zeros, as after every call); batches with
+ * more than 16,384 (sequence, KV head, 64- or 128-row block) items keep the
+ * merge kernel.
  * Supported: (b = 2, d_h in {64, 128}) and (b = 4, d_h = 64); h / h_kv any
  * positive integer.  Other (b, d_h): ENOTSUP.
  * Errors: EINVAL (null out/q/cache/s, non-positive sizes, h % h_kv != 0,
@@ -170,7 +187,9 @@ int attn_decode_gqa(void* out, float* lse, const void* q, const void* cache_k,
  * the scratch lookup fails.
  * Every call on one GPU shares that GPU's scratch: calls that overlap in time
  * on one GPU (different streams, or host threads) race and give undefined
- * results; calls ordered on one stream are safe.  Nothing in the scratch has
+ * results; calls ordered on one stream are safe.  The scratch's first 64 KiB
+ * (the arrival counters of the in-kernel split merge) are zero when the
+ * library is loaded and every call leaves them so; nothing else in it has
  * to start at zero.
  */
 int attn_decode_gqa_noalloc(void* out, float* lse, const void* q, const void* cache_k,

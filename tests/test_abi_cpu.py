@@ -262,4 +262,5 @@ def test_mla_mode_choice():
     assert A.attn_mla_mode(256, 2048) == 1 and A.attn_mla_mode(256, 8192) == 0
     assert A.attn_mla_mode(1024, 8192) == 1
     assert A.attn_mla_mode(0, 8192) == -1
-    assert A.attn_decode_mla_mha_workspace_bytes(4, 8192, 128) == 2 * 4 * 8192 * 128 * 128 * 2
+    # the 64 KiB arrival-counter prefix every workspace keeps, then K and V
+    assert A.attn_decode_mla_mha_workspace_bytes(4, 8192, 128) == 65536 + 2 * 4 * 8192 * 128 * 128 * 2

@@ -65,16 +65,23 @@ def test_fp32_ragged_tail_and_empty():
     run_small(3, 8, 2, 64, (0, 1, 97), 4, seed=8)
 
 
-def test_split_kv_long_context_small_batch():
+@pytest.mark.parametrize("merge", ["kernel", "fused"])
+def test_split_kv_long_context_small_batch(merge, monkeypatch):
+    if merge == "fused":
+        monkeypatch.setenv("ATTN_GQA_MERGE", "fused")
     # B=1 with a long context forces several splits plus the merge kernel
     run_small(1, 16, 2, 128, (20000,), 2, seed=9)
     run_small(2, 8, 1, 128, (9000, 3), 2, seed=10)
     run_small(1, 8, 2, 64, (5000,), 4, seed=11)
 
 
-def test_split_kv_more_than_256_splits():
+@pytest.mark.parametrize("merge", ["kernel", "fused"])
+def test_split_kv_more_than_256_splits(merge, monkeypatch):
+    if merge == "fused":
+        monkeypatch.setenv("ATTN_GQA_MERGE", "fused")
     # one KV head over 140,000 tokens: about 270 splits of 512 tokens, merged
-    # by the 16-wavefront form of the merge kernel
+    # by the 16-wavefront form of the merge kernel, or by the item's last
+    # workgroup
     run_small(1, 16, 1, 128, (140000,), 2, seed=12)
 
 
@@ -154,7 +161,10 @@ def test_peaked_logits_rescale():
     assert_lse_close(to_f64(lse), ref_lse, 2, "lse")
 
 
-def test_paged_mixed_lengths_many_splits():
+@pytest.mark.parametrize("merge", ["kernel", "fused"])
+def test_paged_mixed_lengths_many_splits(merge, monkeypatch):
+    if merge == "fused":
+        monkeypatch.setenv("ATTN_GQA_MERGE", "fused")
     # empty sequences, one-token ones and several splits per sequence in one
     # paged batch: the workgroups map onto the non-empty (sequence, split)
     # pairs only, and the merge reads only the splits each sequence has

@@ -4,7 +4,7 @@ Batches with many (sequence, KV head) pairs, mixed and empty lengths, one
 long context among many empty or one-token ones, paged pools, E4M3 caches
 (per-tensor and per-page scales), several new tokens per sequence (two row
 blocks per KV head), and calls of different shapes sharing one workspace,
-all against the oracle.
+all against the oracle, with either form of the split merge.
 """
 import numpy as np
 import pytest
@@ -17,6 +17,19 @@ from tests._gpu import assert_close, assert_lse_close, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+
+
+@pytest.fixture(autouse=True, params=["kernel", "fused"])
+def merge_form(request, monkeypatch):
+    """Every test runs with both forms of the split merge: the separate merge
+    kernel (default) and the merge by the last workgroup of each item inside
+    the decode kernel (ATTN_GQA_MERGE=fused)."""
+    if request.param == "fused":
+        monkeypatch.setenv("ATTN_GQA_MERGE", "fused")
+    else:
+        monkeypatch.delenv("ATTN_GQA_MERGE", raising=False)
+    print(f"[merge={request.param}]", flush=True)
+    return request.param
 
 
 def lengths(B, seed, lo=0, hi=3000, zeros=()):
@@ -143,3 +156,65 @@ def test_several_new_tokens_two_row_blocks(paged):
                                            block_table=d.get("block_table_host"))
     assert_close(to_f64(out), ref, 2, "out")
     assert_lse_close(to_f64(lse), ref_lse, 2, "lse")
+
+
+def _gqa_call(sh, d, ws, wsb):
+    bt = d.get("block_table")
+    mb = 0 if bt is None else bt.shape[1]
+    out = torch.full_like(d["q"], float("nan"))
+    lse = torch.full((sh.B, sh.h), float("nan"), dtype=torch.float32, device=DEV)
+    rc = A.attn_decode_gqa(out, lse, d["q"], d["K"], d["V"], d["s"], bt, mb, sh.block_size,
+                           0 if bt is None else d["K"].shape[0], sh.B, sh.s_max, sh.h, sh.h_kv,
+                           sh.d_h, sh.b, 0.0, ws, wsb)
+    assert rc == A.ATTN_OK
+    return out, lse
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_many_splits_and_empty_sequences_counters_left_zero(paged):
+    # one item with about 270 splits, one with a few, empty and one-token
+    # sequences (one workgroup each, nothing to merge); with the in-kernel
+    # merge the last workgroup of each item merges its splits, and every
+    # call leaves the workspace's arrival counters at zero, so a second call
+    # on the same workspace gives the same bits
+    s = (0, 140000, 1, 0, 9000, 5)
+    sh = synth.GqaShape("t", B=len(s), h=16, h_kv=1, d_h=128, b=2, s=s, paged=paged, seed=961)
+    print(f"[gqa-fused] paged={paged}", flush=True)
+    d = synth.draw_gqa(sh, device=DEV)
+    wsb = A.attn_decode_workspace_bytes(0, sh.B, sh.s_max, sh.h, sh.h_kv, sh.d_h)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    o1, l1 = _gqa_call(sh, d, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.all(ws[:65536] == 0), "arrival counters not left at zero"
+    o2, l2 = _gqa_call(sh, d, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    assert torch.all(ws[:65536] == 0)
+    check_gqa(sh, d, o1, l1, "out")
+    o = to_f64(o1)
+    assert np.all(o[[0, 3]] == 0.0) and np.all(np.isneginf(to_f64(l1)[[0, 3]]))
+
+
+def test_more_items_than_arrival_counters_use_the_merge_kernel():
+    # 2,100 sequences x 8 KV heads = 16,800 (sequence, KV head) items with
+    # two splits each: more than the 16,384 counters of the workspace
+    # prefix, so the separate merge kernel combines the splits
+    from tests._gpu import gqa_sample_reference
+    B = 2100
+    rng = np.random.default_rng(971)
+    s = [int(x) for x in rng.integers(0, 200, size=B)]
+    s[0], s[1], s[5], s[B - 1] = 8192, 0, 4097, 6000
+    sh = synth.GqaShape("t", B=B, h=32, h_kv=8, d_h=128, b=2, s=tuple(s), paged=True, seed=971)
+    print("[gqa-fused] 16,800 items, merge kernel", flush=True)
+    d = synth.draw_gqa(sh, device=DEV)
+    wsb = A.attn_decode_workspace_bytes(0, sh.B, sh.s_max, sh.h, sh.h_kv, sh.d_h)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    out, lse = _gqa_call(sh, d, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.all(ws[:65536] == 0)
+    g = sh.h // sh.h_kv
+    o64, l64 = to_f64(out), to_f64(lse)
+    for (bi, j), (ro, rl) in gqa_sample_reference(d, sh, [(0, 0), (1, 3), (5, 7), (B - 1, 2), (700, 5)]).items():
+        assert_close(o64[bi, j * g:(j + 1) * g], ro, 2, f"b={bi} j={j}")
+        assert_lse_close(l64[bi, j * g:(j + 1) * g], rl, 2, f"b={bi} j={j}")

@@ -28,7 +28,12 @@ def replay_and_compare(graph, eager, outs, mutate, n=4):
         torch.randn(1 << 20, device=DEV).sum()   # unrelated eager work between replays
 
 
-def test_gqa_split_context_graph():
+@pytest.mark.parametrize("merge", ["kernel", "fused"])
+def test_gqa_split_context_graph(merge, monkeypatch):
+    # the merge form is fixed when the call is captured; with the in-kernel
+    # merge every replay leaves the arrival counters at zero for the next
+    if merge == "fused":
+        monkeypatch.setenv("ATTN_GQA_MERGE", "fused")
     sh = synth.GqaShape("t", B=2, h=32, h_kv=8, d_h=128, b=2, s=(9000, 300), seed=90)
     d = synth.draw_gqa(sh, device=DEV)
     out = torch.empty_like(d["q"])

@@ -21,7 +21,7 @@ def _both(sh, d):
     nblk = 0 if bt is None else d["K"].shape[0]
     s_max = sh.s_max if bt is None else mb * sh.block_size
     ws_bytes = A.attn_decode_workspace_bytes(0, sh.B, s_max, sh.h, sh.h_kv, sh.d_h)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)   # counters start at zero
     o1 = torch.full_like(d["q"], float("nan"))
     l1 = torch.full((sh.B, sh.h), float("nan"), dtype=torch.float32, device=DEV)
     A.attn_decode_gqa(o1, l1, d["q"], d["K"], d["V"], d["s"], bt, mb, sh.block_size, nblk, sh.B,
@@ -41,8 +41,11 @@ def _check_against_oracle(sh, d, o, l):
     assert_lse_close(to_f64(l), ref_lse, sh.b, "noalloc lse")
 
 
+@pytest.mark.parametrize("merge", ["kernel", "fused"])
 @pytest.mark.parametrize("b", [2, 4])
-def test_noalloc_matches_workspace_entry_twice_second_smaller(b):
+def test_noalloc_matches_workspace_entry_twice_second_smaller(b, merge, monkeypatch):
+    if merge == "fused":   # the scratch's first 64 KiB then hold the arrival counters
+        monkeypatch.setenv("ATTN_GQA_MERGE", "fused")
     # first call: split contexts (the scratch holds the partials), a ragged
     # tail, an empty sequence
     big = synth.GqaShape("t", B=3, h=16, h_kv=2, d_h=128 if b == 2 else 64, b=b,

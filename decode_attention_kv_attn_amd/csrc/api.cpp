@@ -94,7 +94,12 @@ GqaPlan plan_gqa_path(bool mfma, int B, int s_max, int h, int h_kv, int d_h, boo
 #ifndef GQA_BF16_TARGET
 #define GQA_BF16_TARGET 512
 #endif
-        P.NW = rows <= GQA_NW_ROWS ? 2 : 4;
+        // E4M3 tiles are half the bytes of bf16 ones: four wavefronts, which
+        // issue the DMA of a tile in two instructions each, measured 5 % faster
+        // than two on the contiguous Llama-3 layers (93.5 against 98.2 us at
+        // 8B, 52.6 against 55.3 us at 70B B = 16); deeper rings or more
+        // splits gave nothing on top
+        P.NW = rows <= GQA_NW_ROWS && !f8 ? 2 : 4;
         target = f8 ? GQA_F8_TARGET : GQA_BF16_TARGET;
     } else {
         P.HG = (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;

@@ -70,25 +70,26 @@ constexpr int kAbsRowStride = kAbsCols * 2 + 16;
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
-// q_nope rows of one 16-sequence block as the A operand, K steps 0..7 (steps
-// past d_nope / 32 and rows past B are zero).  The loads are unconditional
-// from clamped addresses and masked afterwards, so all of them are in flight
-// together.
+// q_nope rows of one 16-sequence block as the A operand, K steps 0..KS-1.
+// The loads are unconditional from clamped addresses and their values are
+// not touched until the products use them, so all of them stay in flight
+// together: K steps past d_nope / 32 are never multiplied, and rows past B
+// (copies of row B - 1) only give result rows that are not stored.
+template <int KS>
 struct AbsA {
-    bf16x8 k[8];
+    bf16x8 k[KS];
 };
-__device__ __forceinline__ AbsA absorb_load_a(const uint16_t* __restrict__ qn, int b0, int li, int G,
-                                              int B, int h, int i, int d_nope)
+template <int KS>
+__device__ __forceinline__ AbsA<KS> absorb_load_a(const uint16_t* __restrict__ qn, int b0, int li, int G,
+                                                  int B, int h, int i, int d_nope)
 {
-    AbsA a;
+    AbsA<KS> a;
     const int ksteps = d_nope / 32;
-    const int bb = b0 + li, bc = min(bb, B - 1);
+    const int bc = min(b0 + li, B - 1);
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
+    for (int k = 0; k < KS; k++) {
         const int kc = min(k, ksteps - 1);
-        const u32x4v v = *(const u32x4v*)(qn + ((size_t)bc * h + i) * d_nope + kc * 32 + 8 * G);
-        const unsigned keep = (k < ksteps && bb < B) ? 0xffffffffu : 0u;   // mask, not a branch
-        a.k[k] = __builtin_bit_cast(bf16x8, v & keep);
+        a.k[k] = *(const bf16x8*)(qn + ((size_t)bc * h + i) * d_nope + kc * 32 + 8 * G);
     }
     return a;
 }
@@ -104,7 +105,9 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[MAXN * kAbsRowStride];
     __shared__ __attribute__((aligned(16))) uint16_t ost[4][16][32 + 8];   // per-wavefront output staging
-    if (blockIdx.x == gridDim.x - 1) {   // one extra workgroup: the decode tile schedule
+    // one extra workgroup, dispatched first so that its loads of the lengths
+    // go out ahead of the W_UK stream: the decode tile schedule
+    if (blockIdx.x == 0) {
         __shared__ int sc[256];
         mla_schedule(SchedArgs{p.s, p.sched, p.B, p.s_max, p.n_wg, p.min_tiles, p.q_len}, threadIdx.x, 256,
                      sc);
@@ -113,13 +116,17 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int nq = p.d_c / kAbsCols;
-    const int i = blockIdx.x / nq, cq = blockIdx.x % nq;
+    const int i = (blockIdx.x - 1) / nq, cq = (blockIdx.x - 1) % nq;
     const int c0 = cq * kAbsCols;
     const uint16_t* __restrict__ wuk = (const uint16_t*)p.w_uk + (size_t)i * p.d_nope * p.d_c;
     const uint16_t* __restrict__ qn = (const uint16_t*)p.q_nope;
     const int ksteps = p.d_nope / 32;
+    constexpr int KS = MAXN / 32;
 
-    AbsA a = absorb_load_a(qn, 0, li, G, p.B, p.h, i, p.d_nope);
+    // the first two 16-sequence blocks of q_nope, in flight with the W_UK
+    // staging below (later blocks are fetched two blocks ahead)
+    AbsA<KS> a0 = absorb_load_a<KS>(qn, 0, li, G, p.B, p.h, i, p.d_nope);
+    AbsA<KS> a1 = absorb_load_a<KS>(qn, 16, li, G, p.B, p.h, i, p.d_nope);   // rows clamped to B - 1
 
     // stage W_UK[i][:, c0:c0+128]: d_nope rows x 16 chunks, 8 loads in flight
     // per thread; past the end, lanes load and store the last chunk again
@@ -171,17 +178,18 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
     __syncthreads();
 
     // wavefront w computes column tiles 2w and 2w+1 (32 columns) for every
-    // 16-row block of b; the next block's q_nope is fetched while this one
-    // is multiplied.  The block's 16 x 32 results go through LDS so that
-    // each lane stores 16 contiguous bytes.
-    for (int b0 = 0; b0 < p.B; b0 += 16) {
-        const AbsA an = absorb_load_a(qn, min(b0 + 16, p.B - 1), li, G, p.B, p.h, i, p.d_nope);
+    // 16-row block of b.  Blocks go in pairs: each one's registers are
+    // refilled with the block two ahead as soon as it has been multiplied,
+    // so the next pair's q_nope is in flight during this pair's work and no
+    // register copy waits for a load.  The block's 16 x 32 results go through
+    // LDS so that each lane stores 16 contiguous bytes.
+    auto block = [&](const AbsA<KS>& a, int b0) {
 #pragma unroll
         for (int t = 0; t < 2; t++) {
             const int nt = 2 * wave + t;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
+            for (int k = 0; k < KS; k++) {
                 if (k < ksteps) {
                     const int row = k * 32 + 8 * G + li / 4;
                     const int col = nt * 16 + 4 * (li % 4);
@@ -204,7 +212,19 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const MlaParams p)
                 *(u32x4v*)(p.qhat + qhat_index(b0 + r, i, c0 + 32 * wave + 8 * sg, p.h)) = v;
         }
         __syncthreads();
-        a = an;
+    };
+    // the first pair outside the loop: straight-line code, so the compiler's
+    // waits there cover exactly the loads a block uses (a wait carried round
+    // a loop would also drain the stores of the block before it)
+    block(a0, 0);
+    if (p.B > 32) a0 = absorb_load_a<KS>(qn, 32, li, G, p.B, p.h, i, p.d_nope);   // uniform
+    if (p.B > 16) block(a1, 16);
+    if (p.B > 48) a1 = absorb_load_a<KS>(qn, 48, li, G, p.B, p.h, i, p.d_nope);
+    for (int b0 = 32; b0 < p.B; b0 += 32) {
+        block(a0, b0);
+        if (b0 + 32 < p.B) a0 = absorb_load_a<KS>(qn, b0 + 32, li, G, p.B, p.h, i, p.d_nope);
+        if (b0 + 16 < p.B) block(a1, b0 + 16);
+        if (b0 + 48 < p.B) a1 = absorb_load_a<KS>(qn, b0 + 48, li, G, p.B, p.h, i, p.d_nope);
     }
 }
 
@@ -411,51 +431,85 @@ struct SchedView {
     __device__ __forceinline__ int first_seq(int w) const { return min(max(at(B + 1 + w), 0), B - 1); }
 };
 
-// Computed by one workgroup of nthr threads (a power of two); sc is nthr
-// ints of LDS.  Two passes over the lengths: the first only totals the
-// tiles (which fixes tpw), the second scans them again and writes the tile
-// offsets and each workgroup's first sequence; no thread reads back what
-// another wrote to global memory.
+// Computed by one workgroup of nthr threads (a multiple of 64, at most 1024);
+// sc is nthr ints of LDS.  Thread t takes rows E t .. E t + E - 1 of each
+// chunk of E nthr rows, so one round trip to memory brings the lengths of up
+// to E nthr rows, which stay in registers for both passes: the first totals
+// the tiles (which fixes tpw), the second scans them (within a thread, then
+// across wavefronts through LDS) and writes the tile offsets and each
+// workgroup's first sequence.  Only longer batches load their lengths again
+// per chunk.  No thread reads back what another wrote to global memory.
 __device__ __forceinline__ void mla_schedule(SchedArgs p, int tid, int nthr, int* sc)
 {
+    constexpr int E = 4;
     int32_t* ts = p.sched;
     int32_t* wstart = p.sched + p.B + 1;
-    auto tiles_of = [&](int i) {
-        return i < p.B ? (mla_seen(p.s[mla_cache_seq(i, p.q_len)], i, p.q_len, p.s_max) + kT - 1) / kT : 0;
+    const int lane = tid % 64, wv = tid / 64, nwv = nthr / 64;
+    const int per = E * nthr;   // rows per chunk
+    auto load = [&](int base, int* tl) {
+        int len[E];
+#pragma unroll
+        for (int k = 0; k < E; k++)   // unconditional, all E loads in flight together
+            len[k] = p.s[mla_cache_seq(min(base + E * tid + k, p.B - 1), p.q_len)];
+#pragma unroll
+        for (int k = 0; k < E; k++) {
+            const int i = base + E * tid + k;
+            const int t = (mla_seen(len[k], i, p.q_len, p.s_max) + kT - 1) / kT;
+            tl[k] = i < p.B ? t : 0;
+        }
     };
-    // pass 1: total
-    int part = 0;
-    for (int i = tid; i < p.B; i += nthr) part += tiles_of(i);
-    sc[tid] = part;
-    __syncthreads();
-    for (int off = nthr / 2; off > 0; off >>= 1) {
-        if (tid < off) sc[tid] += sc[tid + off];
+    // sum over the workgroup (sc[0 .. nwv - 1] hold the wavefront totals)
+    auto block_total = [&](int x) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
         __syncthreads();
+        if (lane == 0) sc[wv] = x;
+        __syncthreads();
+        int t = 0;
+        for (int v = 0; v < nwv; v++) t += sc[v];
+        return t;
+    };
+    int tl[E];
+    load(0, tl);
+    int part = 0;
+#pragma unroll
+    for (int k = 0; k < E; k++) part += tl[k];
+    for (int base = per; base < p.B; base += per) {   // batches of more than E nthr rows
+        int tx[E];
+        load(base, tx);
+#pragma unroll
+        for (int k = 0; k < E; k++) part += tx[k];
     }
-    const int total = sc[0];
+    const int total = block_total(part);
     const int tpw = max((total + p.n_wg - 1) / p.n_wg, p.min_tiles);
-    __syncthreads();
     // pass 2: offsets; workgroup w starts at tile w tpw, inside exactly one
     // non-empty sequence
     int carry = 0;
-    for (int base = 0; base < p.B; base += nthr) {
-        const int i = base + tid;
-        const int tl = tiles_of(i);
-        sc[tid] = tl;
+    for (int base = 0; base < p.B; base += per) {
+        if (base > 0) load(base, tl);
+        int mine = 0;
+#pragma unroll
+        for (int k = 0; k < E; k++) mine += tl[k];
+        const int incl = wave_scan_incl(mine);
+        __syncthreads();   // sc free again
+        if (lane == 63) sc[wv] = incl;
         __syncthreads();
-        for (int off = 1; off < nthr; off <<= 1) {   // inclusive scan
-            const int v = tid >= off ? sc[tid - off] : 0;
-            __syncthreads();
-            sc[tid] += v;
-            __syncthreads();
+        int before = 0, chunk = 0;
+        for (int v = 0; v < nwv; v++) {
+            before += v < wv ? sc[v] : 0;
+            chunk += sc[v];
         }
-        if (i < p.B) {
-            const int a = carry + sc[tid] - tl, e = a + tl;
-            ts[i] = a;
-            for (int w = (a + tpw - 1) / tpw; w * tpw < e; w++) wstart[w] = i;
+        int a = carry + before + incl - mine;
+#pragma unroll
+        for (int k = 0; k < E; k++) {
+            const int i = base + E * tid + k;
+            if (i < p.B) {
+                ts[i] = a;
+                for (int w = (a + tpw - 1) / tpw; w * tpw < a + tl[k]; w++) wstart[w] = i;
+            }
+            a += tl[k];
         }
-        carry += sc[nthr - 1];
-        __syncthreads();
+        carry += chunk;
     }
     if (tid == 0) {
         ts[p.B] = total;
@@ -1165,7 +1219,10 @@ __global__ __launch_bounds__(64 * kFinSeq, 4) void mla_finish_kernel(const MlaPa
     // the merge, the rest once the merge is done (all 16 up front would
     // push the kernel past 128 registers, i.e. below two workgroups per CU)
     const uint16_t* __restrict__ wuv = (const uint16_t*)p.w_uv + (size_t)i * p.d_v * p.d_c;
-    constexpr int kWuvPre = 8;
+#ifndef MLA_WUV_PRE
+#define MLA_WUV_PRE 8
+#endif
+    constexpr int kWuvPre = MLA_WUV_PRE;
     bf16x8 bws[16];   // d_c = 512: 16 K steps
     const bool up = p.out != nullptr;   // value up-projection wanted (else only u~ leaves)
     if (up && wave < p.d_v / 16) {
@@ -1195,6 +1252,20 @@ __global__ __launch_bounds__(64 * kFinSeq, 4) void mla_finish_kernel(const MlaPa
 
     float M = -INFINITY, L = 0.f;
     float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+    // the first chunk of partials is requested before the flags are read,
+    // so that both arrive in one round trip
+    float2 v[kFinChunk];
+    uint4 uh[kFinChunk];
+    auto load_chunk = [&](int j0) {
+#pragma unroll
+        for (int c = 0; c < kFinChunk; c++) {   // clamped, unconditional loads
+            const int jj = min(j0 + c, nj - 1);
+            const size_t row = row0 + (size_t)(sub + nsub * jj) * p.h;
+            v[c] = ml[row];
+            uh[c] = pu[row * 64 + lane];
+        }
+    };
+    if (nj > 0) load_chunk(0);
     // a decode workgroup that stopped early left no partials: recompute them
     bool any_flag = false;
     for (int jj = 0; jj < nj; jj++) any_flag |= p.flags[wf + sub + nsub * jj] != 0;
@@ -1221,40 +1292,33 @@ __global__ __launch_bounds__(64 * kFinSeq, 4) void mla_finish_kernel(const MlaPa
             a1 = a1 * sa + k1 * sb;
             M = Mn;
         }
-    }
-    for (int j0 = 0; j0 < (any_flag ? 0 : nj); j0 += kFinChunk) {
-        float2 v[kFinChunk];
-        uint4 uh[kFinChunk];
+    } else {   // the chunks already requested stay in registers on this path only
+        for (int j0 = 0; j0 < nj; j0 += kFinChunk) {
+            if (j0 > 0) load_chunk(j0);
+            float Mc = M;
 #pragma unroll
-        for (int c = 0; c < kFinChunk; c++) {   // clamped, unconditional loads
-            const int jj = min(j0 + c, nj - 1);
-            const size_t row = row0 + (size_t)(sub + nsub * jj) * p.h;
-            v[c] = ml[row];
-            uh[c] = pu[row * 64 + lane];
-        }
-        float Mc = M;
+            for (int c = 0; c < kFinChunk; c++)
+                if (j0 + c < nj && v[c].y > 0.f) Mc = fmaxf(Mc, v[c].x);
+            if (Mc == -INFINITY) continue;   // nothing seen yet
+            const float sc = __builtin_amdgcn_exp2f(M - Mc);   // 0 while M = -inf
+            L *= sc;
+            a0 *= sc;
+            a1 *= sc;
 #pragma unroll
-        for (int c = 0; c < kFinChunk; c++)
-            if (j0 + c < nj && v[c].y > 0.f) Mc = fmaxf(Mc, v[c].x);
-        if (Mc == -INFINITY) continue;   // nothing seen yet
-        const float sc = __builtin_amdgcn_exp2f(M - Mc);   // 0 while M = -inf
-        L *= sc;
-        a0 *= sc;
-        a1 *= sc;
-#pragma unroll
-        for (int c = 0; c < kFinChunk; c++) {
-            if (j0 + c < nj && v[c].y > 0.f) {   // wave-uniform
-                const float wl = __builtin_amdgcn_exp2f(v[c].x - Mc) * v[c].y;   // weight of U / l
-                float4 u0, u1;
-                unpack(uh[c], u0, u1);
-                L += wl;
-                a0.x = fmaf(wl, u0.x, a0.x); a0.y = fmaf(wl, u0.y, a0.y);
-                a0.z = fmaf(wl, u0.z, a0.z); a0.w = fmaf(wl, u0.w, a0.w);
-                a1.x = fmaf(wl, u1.x, a1.x); a1.y = fmaf(wl, u1.y, a1.y);
-                a1.z = fmaf(wl, u1.z, a1.z); a1.w = fmaf(wl, u1.w, a1.w);
+            for (int c = 0; c < kFinChunk; c++) {
+                if (j0 + c < nj && v[c].y > 0.f) {   // wave-uniform
+                    const float wl = __builtin_amdgcn_exp2f(v[c].x - Mc) * v[c].y;   // weight of U / l
+                    float4 u0, u1;
+                    unpack(uh[c], u0, u1);
+                    L += wl;
+                    a0.x = fmaf(wl, u0.x, a0.x); a0.y = fmaf(wl, u0.y, a0.y);
+                    a0.z = fmaf(wl, u0.z, a0.z); a0.w = fmaf(wl, u0.w, a0.w);
+                    a1.x = fmaf(wl, u1.x, a1.x); a1.y = fmaf(wl, u1.y, a1.y);
+                    a1.z = fmaf(wl, u1.z, a1.z); a1.w = fmaf(wl, u1.w, a1.w);
+                }
             }
+            M = Mc;
         }
-        M = Mc;
     }
 
     // combine the shares of a sequence split over several wavefronts

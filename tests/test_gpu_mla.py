@@ -168,3 +168,60 @@ def test_large_batch_short_sequences():
     rng = np.random.default_rng(45)
     s = tuple(int(x) for x in rng.integers(0, 120, size=1200))
     run(shape(1200, 16, s, seed=45), sample=[0, 1, 599, 1199])
+
+
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+def _expected_schedule(seen, n_wg=256, min_tiles=8, kT=32):
+    """The equal-tile schedule from its rule: the tiles of all query rows end
+    to end, tile_start = exclusive prefix sums, tpw = max(ceil(total / n_wg),
+    min_tiles), and workgroup w starts in the row holding tile w * tpw (-1
+    once past the total)."""
+    tiles = [(n + kT - 1) // kT for n in seen]
+    ts = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int64)
+    total = int(ts[-1])
+    tpw = max(-(-total // n_wg), min_tiles)
+    wstart = []
+    for w in range(n_wg):
+        t = w * tpw
+        if t >= total:
+            wstart.append(-1)
+        else:
+            wstart.append(int(np.searchsorted(ts, t, side="right") - 1))
+    return np.concatenate([ts, wstart, [tpw]]).astype(np.int32)
+
+
+@pytest.mark.parametrize("B,q_len,hi", [(32, 1, 8192), (1100, 1, 300), (7, 3, 2000), (1, 1, 0)])
+def test_schedule_metadata_bit_exact(B, q_len, hi):
+    # the tile schedule the absorb launch writes into the workspace, against
+    # the rule it implements (more than 1,024 rows take several chunks of
+    # the one workgroup that computes it; several new tokens per sequence
+    # count the tokens each position sees)
+    rng = np.random.default_rng(44 + B)
+    s = [int(x) for x in rng.integers(0, hi + 1, size=B)]
+    if B > 3:
+        s[1], s[2] = 0, 1
+    h, d_c, d_R = 16, 512, 64
+    sh = synth.MlaShape("t", B=B, h=h, d_c=d_c, d_R=d_R, d_nope=128, d_v=128, s=tuple(s),
+                        seed=44, q_len=q_len)
+    print(f"[mla-schedule] B={B} q_len={q_len}", flush=True)
+    d = synth.draw_mla(sh, device=DEV)
+    ws = A.Workspace(DEV)
+    if q_len == 1:
+        A.decode_mla(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["cache"], d["s"],
+                     s_max=sh.s_max, workspace=ws)
+    else:
+        A.decode_mla_multi(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["cache"], d["s"],
+                           s_max=sh.s_max, workspace=ws)
+    torch.cuda.synchronize()
+    rows, n_wg = B * q_len, 256
+    slots = n_wg + rows - 1
+    off = (65536 + _align256(rows * ((h + 31) // 32) * 32 * (d_c + d_R) * 2)
+           + _align256(slots * h * d_c * 2) + _align256(slots * h * 2 * 4) + _align256(n_wg * 4))
+    n = rows + 1 + n_wg + 1
+    got = ws.buf[off:off + 4 * n].cpu().numpy().view(np.int32)
+    seen = [max(min(s[r // q_len], sh.s_max) - (q_len - 1 - r % q_len), 0) for r in range(rows)]
+    want = _expected_schedule(seen)
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:10]

@@ -281,12 +281,20 @@ struct MlaTile {
     static constexpr int SPS = kT / RPS;              // DMA instructions per segment
 };
 
-// XOR swizzle of the 16-byte chunk position within a 128-byte row segment:
-// s(r) = r0 ^ 2 r1 ^ 5 r2 ^ 7 r3 (r_k the bits of r).  Any 8 consecutive
-// rows get distinct positions.
+// XOR swizzle of the 16-byte chunk position within a 128-byte row segment.
+// The LDS has 64 four-byte banks and serves 16 lanes of a 16-byte read (32
+// lanes of an 8-byte one) per cycle, so a 16-lane group must cover all 64
+// banks: a row's banks start at 32 (r % 2), so the rows of each parity
+// among 16 consecutive ones need distinct positions.  With u = (r / 2) mod 8,
+// s(r) = 4 (u % 2) + u / 2 does that, and rows 4k and 4k + 2 (4k + 1 and
+// 4k + 3) differ in bit 2, so the transposing reads of 4 rows x 32 bytes
+// per 32-lane group hit 64 distinct banks too.  Measured with an LDS probe:
+// the score pattern under the previous swizzle (any 8 consecutive rows
+// distinct) ran at half rate once 8 wavefronts per CU were reading.
 __device__ __forceinline__ int swz(int r)
 {
-    return (r & 1) ^ (r & 2) ^ ((r & 4) ? 5 : 0) ^ ((r & 8) ? 7 : 0);
+    const int u = (r >> 1) & 7;
+    return ((u & 1) << 2) | (u >> 1);
 }
 
 // Per-lane byte offsets of the MFMA operands within a tile buffer, split so
@@ -328,20 +336,23 @@ struct TileOffsets {
 
 // E4M3 tiles (576-byte rows in 64-byte segments: byte s * 2048 + r * 64 +
 // 16 p holds row r, 16-byte chunk 4 s + (p ^ swz8(r))).
-//   swz8(r) = ((r >> 1) & 3) ^ 2 ((r >> 3) & 1)
+//   swz8(r) = (r >> 2) & 3
 // Score operands: a lane reads one whole chunk (16 codes) per pair of K
 // steps: lane (row r = l % 32, hh = l / 32) reads chunk 2 j + hh, whose
 // first 8 codes are its operand of step 2 j and the last 8 of step 2 j + 1
-// (the K order inside a step is free as long as q^ follows it).  8
-// consecutive rows then cover the 8 (row parity, position) bank groups.
+// (the K order inside a step is free as long as q^ follows it).  A row's
+// banks start at 16 (r % 4), so the 16 rows of a 16-lane group need distinct
+// positions within each residue mod 4: rows c, c + 4, c + 8, c + 12 get
+// positions 0 .. 3.
 // Value operands: an 8-bit transposing read per (column tile, K step).  In
 // 16-lane group q (= l / 16), source lane i reads 8 bytes of row
 // 16 kk + tau(q / 2, i / 2), columns 128 w + 32 mc + 16 (q % 2) + 8 (i % 2),
 // with tau(hh, k) = 4 hh + k for k < 4 and 4 hh + k + 4 otherwise -- the
 // score output's token order; the read hands lane 8 a + c byte c of source
 // lanes a, a + 2, .., a + 14, i.e. column 16 (q % 2) + 8 a + c for its 8
-// tokens.  Rows {0-3, 8-11} and {4-7, 12-15} each cover the 8 bank groups.
-__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 3) ^ (((r >> 3) & 1) << 1); }
+// tokens.  Rows {0-3, 8-11} and {4-7, 12-15} each cover the 64 banks (rows r
+// and r + 8 differ in bit 1 of their position).
+__device__ __forceinline__ int swz8(int r) { return (r >> 2) & 3; }
 
 struct TileOffsets8 {
     int sc[2];   // score, by j & 1

@@ -280,17 +280,25 @@ __device__ __forceinline__ void merge_item(const GqaParams& p, int b, int j, int
     }
 }
 
-template <int D, int NW, bool PAGED, bool F8, int RPW, bool PS = false>
+// NI > 0: the last NI wavefronts issue all of the tile DMA and compute
+// nothing, and the first NW - NI compute and issue nothing (rows must fit
+// them).  Issuing a tile's DMA waits for room in the memory pipeline (about
+// 120 cycles an instruction at full stream), which a wavefront that also
+// computes would add to its compute time every tile.
+template <int D, int NW, bool PAGED, bool F8, int RPW, bool PS = false, int NI = 0>
 __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
                                                            const int32_t* __restrict__ btab)
 {
     using C = MfmaCfg<D, F8>;
-    constexpr int OPW = C::OPS / NW;   // DMA instructions per wavefront and tile
-    static_assert(C::OPS % NW == 0, "DMA instructions must split evenly");
+    constexpr int NIW = NI ? NI : NW;     // wavefronts that issue DMA
+    constexpr int OPW = C::OPS / NIW;     // DMA instructions per issuing wavefront and tile
+    static_assert(C::OPS % NIW == 0 && NI < NW, "DMA instructions must split evenly");
     __shared__ __attribute__((aligned(1024))) uint8_t Ls[C::NBUF * 2 * C::KT];
 
     const int tid = threadIdx.x, lane = tid % 64, G = lane / 16, li = lane % 16;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const bool issuer = NI == 0 || wave >= NW - NI;   // wave-uniform
+    const int iw = NI ? wave - (NW - NI) : wave;      // index among the issuing wavefronts
     // work item (b, split, j) with j fastest.  A paged pool is walked
     // XCD-major, so that the KV heads of one sequence, which share every
     // block, run under one L2; a contiguous cache streams faster in plain
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     for (int k = 0; k < RPW; k++) {
         const int r0 = 64 * RPW * rb + 16 * (k * NW + wave);
         const int nh = min(16, n_rows - r0);        // rows of this block
-        act[k] = nh > 0;
+        act[k] = nh > 0 && (NI == 0 || wave < NW - NI);
         active |= act[k];
         hv[k] = li < nh;                            // this lane's row exists
         const int r = hv[k] ? r0 + li : r0;
@@ -398,7 +406,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         const int lr = lane / C::NCH, lp = lane % C::NCH;
 #pragma unroll
         for (int jj = 0; jj < OPW; jj++) {
-            const int q = wave + NW * jj;
+            const int q = max(iw, 0) + NIW * jj;
             const int rt = (q % (C::OPS / 2)) * C::RPO;   // first tile row of this instruction
             voff[jj] = (uint32_t)(((rt & 15) + lr) * (int)rowstride + ((lp ^ gswz<D, F8>(rt + lr)) << 4));
         }
@@ -408,6 +416,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         return (size_t)b * p.s_max + t;
     };
     auto issue_tile = [&](int tb, int buf, size_t row0, size_t row1) {
+        if (!issuer) return;
         const int nv0 = min(max(t1 - tb, 0), 16), nv1 = min(max(t1 - tb - 16, 0), 16);
         const int nr0 = nv0 > 0 ? (nv0 - 1) * (int)rowstride + C::RB : 0;
         const int nr1 = nv1 > 0 ? (nv1 - 1) * (int)rowstride + C::RB : 0;
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
         const uint32_t lb = lds0 + (uint32_t)(buf * 2 * C::KT);
 #pragma unroll
         for (int jj = 0; jj < OPW; jj++) {
-            const int q = wave + NW * jj;
+            const int q = iw + NIW * jj;
             const bool isv = q >= C::OPS / 2;
             const int rb = isv ? q - C::OPS / 2 : q;
             const bool h1 = rb * C::RPO >= 16;
@@ -647,35 +656,42 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, int NW, bool F8, int RPW>
+template <int D, int NW, bool F8, int RPW, int NI = 0>
 static hipError_t launch_nw(const GqaParams& p, bool paged, unsigned grid, hipStream_t st)
 {
     if (F8 && paged && p.k_scales)   // per-page scales
-        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW, F8>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW, F8, NI>), dim3(grid), dim3(64 * NW), 0, st, p,
+                           p.bt);
     else if (paged)
-        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW, false, NI>), dim3(grid), dim3(64 * NW), 0, st, p,
+                           p.bt);
     else
-        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false, F8, RPW>), dim3(grid), dim3(64 * NW), 0, st, p, p.bt);
+        hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false, F8, RPW, false, NI>), dim3(grid), dim3(64 * NW), 0, st, p,
+                           p.bt);
     return hipGetLastError();
 }
 
-// (NW, RPW) in {(2, 1), (4, 1), (4, 2)}: 32, 64 or 128 rows per workgroup
+// (NW, RPW) in {(2, 1), (4, 1), (4, 2)}: 32, 64 or 128 rows per workgroup,
+// every wavefront issuing DMA; or (E4M3, ni = 1) two wavefronts, one
+// computing (16 rows) and one issuing
 template <int D, bool F8>
-static hipError_t launch_mfma_d(const GqaParams& p, int NW, int rpw, bool paged, unsigned grid,
+static hipError_t launch_mfma_d(const GqaParams& p, int NW, int rpw, int ni, bool paged, unsigned grid,
                                 hipStream_t st)
 {
+    if constexpr (F8)
+        if (ni > 0) return launch_nw<D, 2, F8, 1, 1>(p, paged, grid, st);
     if (NW == 2) return launch_nw<D, 2, F8, 1>(p, paged, grid, st);
     return rpw == 2 ? launch_nw<D, 4, F8, 2>(p, paged, grid, st) : launch_nw<D, 4, F8, 1>(p, paged, grid, st);
 }
 
-hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, int rpw, bool paged, bool f8,
+hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, int rpw, int ni, bool paged, bool f8,
                            unsigned grid, hipStream_t st)
 {
     hipError_t e;
-    if (f8) e = d_h == 64 ? launch_mfma_d<64, true>(p, NW, rpw, paged, grid, st)
-                          : launch_mfma_d<128, true>(p, NW, rpw, paged, grid, st);
-    else e = d_h == 64 ? launch_mfma_d<64, false>(p, NW, rpw, paged, grid, st)
-                       : launch_mfma_d<128, false>(p, NW, rpw, paged, grid, st);
+    if (f8) e = d_h == 64 ? launch_mfma_d<64, true>(p, NW, rpw, ni, paged, grid, st)
+                          : launch_mfma_d<128, true>(p, NW, rpw, ni, paged, grid, st);
+    else e = d_h == 64 ? launch_mfma_d<64, false>(p, NW, rpw, ni, paged, grid, st)
+                       : launch_mfma_d<128, false>(p, NW, rpw, ni, paged, grid, st);
     if (e != hipSuccess || p.n_split == 1 || p.arrive) return e;
     return launch_gqa_combine(p, d_h, false, st);
 }

@@ -46,7 +46,8 @@ hipError_t launch_gqa_decode(const GqaParams& p, int d_h, bool f32, int HG, bool
                              unsigned grid, hipStream_t st);
 // matrix-core kernel (bf16 or FP8 E4M3 caches, g <= 16 NW, NW = 2 or 4), then the split
 // merge when n_split > 1
-hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, int rpw, bool paged, bool f8,
+// ni = 1 (E4M3 caches, at most 16 rows): two wavefronts, one computing and one issuing the DMA
+hipError_t launch_gqa_mfma(const GqaParams& p, int d_h, int NW, int rpw, int ni, bool paged, bool f8,
                            unsigned grid, hipStream_t st);
 hipError_t launch_gqa_combine(const GqaParams& p, int d_h, bool f32, hipStream_t st);
 

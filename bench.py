@@ -116,8 +116,10 @@ def run_gqa(name, steps, warmup, rotate, keep=None):
     return sh, total_ms, per
 
 
-def run_gqa_fp8(name, steps, warmup, rotate, k_scale=1.0 / 64, v_scale=1.0 / 64):
-    """The GQA workload with its K/V caches stored as E4M3 codes."""
+def run_gqa_fp8(name, steps, warmup, rotate, k_scale=1.0 / 64, v_scale=1.0 / 64, pages=False):
+    """The GQA workload with its K/V caches stored as E4M3 codes: per-tensor
+    scales, or (pages=True, paged workloads) one K and one V scale per page
+    and KV head, drawn around k_scale / v_scale."""
     import torch
     import synth
     import decode_attention_kv_attn_amd as A
@@ -132,11 +134,23 @@ def run_gqa_fp8(name, steps, warmup, rotate, k_scale=1.0 / 64, v_scale=1.0 / 64)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     it = [0]
+    if pages:
+        if not sh.paged:
+            raise ValueError(f"{name} is not a paged workload")
+        g = torch.Generator(device=dev).manual_seed(sh.seed + 17)
+        n_blk = sets[0]["K8"].shape[0]
+        ks = (0.5 + torch.rand((n_blk, sh.h_kv), generator=g, device=dev)) * k_scale
+        vs = (0.5 + torch.rand((n_blk, sh.h_kv), generator=g, device=dev)) * v_scale
 
     def call():
         d = sets[it[0] % rotate]
         it[0] += 1
         bt = d.get("block_table")
+        if pages:
+            A.attn_decode_gqa_fp8_paged_scales(out, lse, d["q"], d["K8"], d["V8"], ks, vs, d["s"], bt,
+                                               bt.shape[1], sh.block_size, d["K8"].shape[0], sh.B,
+                                               sh.s_max, sh.h, sh.h_kv, sh.d_h, 0.0, ws, wsb, sp)
+            return
         A.attn_decode_gqa_fp8(out, lse, d["q"], d["K8"], d["V8"], k_scale, v_scale, d["s"], bt,
                               0 if bt is None else bt.shape[1], sh.block_size,
                               0 if bt is None else d["K8"].shape[0], sh.B, sh.s_max, sh.h,
@@ -897,6 +911,24 @@ def main():
                           "speedup_vs_bf16": ms / fms}
         except Exception as e:  # the FP8 leg reports its own failure, the line still prints
             rec["fp8"] = {"error": str(e)[:200]}
+        if "ms_per_step" in rec.get("fp8", {}):
+            try:   # the paged GQA-8 batch over E4M3 pages: per-tensor scales, then one per page
+                t = {}
+                for key, pages in (("per_tensor", False), ("per_page", True)):
+                    psh, ptot, pper = run_gqa_fp8("paged_gqa8", args.steps, args.warmup, rotate=1,
+                                                  pages=pages)
+                    t[key] = ptot / args.steps
+                    torch.cuda.empty_cache()
+                pab = gqa_fp8_alg_bytes(psh)
+                rec["fp8"]["pages"] = {
+                    "workload": f"paged_gqa8: B={psh.B} ragged lengths, E4M3 K/V pages, one K and one V "
+                                f"scale per page and KV head",
+                    "us_per_call": t["per_page"] * 1e3,
+                    "us_per_call_per_tensor_scales": t["per_tensor"] * 1e3,
+                    "hbm_frac": pab / (t["per_page"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "alg_bytes_per_call": pab}
+            except Exception as e:
+                rec["fp8"]["pages"] = {"error": str(e)[:200]}
     if not args.no_multi:
         try:   # the same layer verifying q_len drafted tokens per sequence in one call
             qsh, qtot, qper = run_gqa_multi(args.config, args.q_len, args.steps, args.warmup, rotate=1)

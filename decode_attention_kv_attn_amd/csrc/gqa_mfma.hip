@@ -287,7 +287,9 @@ __device__ __forceinline__ void merge_item(const GqaParams& p, int b, int j, int
 // computes would add to its compute time every tile.
 template <int D, int NW, bool PAGED, bool F8, int RPW, bool PS = false, int NI = 0>
 __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
-                                                           const int32_t* __restrict__ btab)
+                                                           const int32_t* __restrict__ btab,
+                                                           const float* __restrict__ ksp,
+                                                           const float* __restrict__ vsp)
 {
     using C = MfmaCfg<D, F8>;
     constexpr int NIW = NI ? NI : NW;     // wavefronts that issue DMA
@@ -450,15 +452,19 @@ __global__ __launch_bounds__(64 * NW) void gqa_mfma_kernel(const GqaParams p,
     // zero for padding heads), then one more tile
     // Per-page scales of a paged E4M3 cache (one per page and KV head):
     // a tile's two 16-token halves lie in one page each, so each half has one
-    // K and one V scale.  They are read (scalar loads) when the tile is
-    // issued and carried in a queue of AH entries to its compute iteration.
+    // K and one V scale.  They are read when the tile is issued and carried
+    // in a queue of AH entries to its compute iteration.  They come in as
+    // restrict parameters with wave-uniform indices, so the reads are scalar
+    // loads: a vector load here would make the compiler wait for every
+    // outstanding vector-memory operation, the tile DMA included.
     constexpr int AH = C::NBUF - 1;   // tiles in flight ahead of the one in use
     constexpr bool ps = F8 && PAGED && PS;
-    const float* __restrict__ ksp = p.k_scales;
-    const float* __restrict__ vsp = p.v_scales;
     float qk[AH][2], qv[AH][2];
     auto page_scales = [&](size_t row0, size_t row1, float* ks, float* vs) {
-        const size_t i0 = (row0 >> p.bs_log2) * p.h_kv + j, i1 = (row1 >> p.bs_log2) * p.h_kv + j;
+        const int jj = __builtin_amdgcn_readfirstlane(j);
+        const int blk0 = __builtin_amdgcn_readfirstlane((int)(row0 >> p.bs_log2));
+        const int blk1 = __builtin_amdgcn_readfirstlane((int)(row1 >> p.bs_log2));
+        const size_t i0 = (size_t)blk0 * p.h_kv + jj, i1 = (size_t)blk1 * p.h_kv + jj;
         ks[0] = ksp[i0];
         ks[1] = ksp[i1];
         vs[0] = vsp[i0];
@@ -661,13 +667,13 @@ static hipError_t launch_nw(const GqaParams& p, bool paged, unsigned grid, hipSt
 {
     if (F8 && paged && p.k_scales)   // per-page scales
         hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW, F8, NI>), dim3(grid), dim3(64 * NW), 0, st, p,
-                           p.bt);
+                           p.bt, p.k_scales, p.v_scales);
     else if (paged)
         hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, true, F8, RPW, false, NI>), dim3(grid), dim3(64 * NW), 0, st, p,
-                           p.bt);
+                           p.bt, p.k_scales, p.v_scales);
     else
         hipLaunchKernelGGL((gqa_mfma_kernel<D, NW, false, F8, RPW, false, NI>), dim3(grid), dim3(64 * NW), 0, st, p,
-                           p.bt);
+                           p.bt, p.k_scales, p.v_scales);
     return hipGetLastError();
 }
 

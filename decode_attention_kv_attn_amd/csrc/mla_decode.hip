@@ -781,6 +781,8 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
     // last scored tile (free once every wavefront has passed the first
     // barrier below; the next refill of it is issued after this returns),
     // or a separate area for E4M3 tiles, which are smaller than it.
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(1))) h8 gh8;
     float* const Lx = (float*)&Pb[1][0][0][0];   // NTH * 32 sums
     constexpr int kStgRow = 272, kStgWave = 32 * kStgRow;
     auto write_partial = [&](int b, uint8_t* stage) {
@@ -826,19 +828,14 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                     const int head = 32 * nt + hd;
                     const float lh = Lx[head];
                     const float il = lh > 0.f ? __builtin_amdgcn_rcpf(lh) : 0.f;
-                    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
                     const h8 v = {(_Float16)(x0.x * il), (_Float16)(x0.y * il), (_Float16)(x0.z * il),
                                   (_Float16)(x0.w * il), (_Float16)(x1.x * il), (_Float16)(x1.y * il),
                                   (_Float16)(x1.z * il), (_Float16)(x1.w * il)};
-#ifndef MLA_PSTORE
-#define MLA_PSTORE 0
-#endif
-                    if (head < p.h) {
-                        h8* dst = (h8*)((_Float16*)(uintptr_t)obase + hd * 512 + 8 * c8);
-                        if (MLA_PSTORE == 0) *dst = v;
-                        else if (MLA_PSTORE == 1) __builtin_nontemporal_store(v, dst);
-                        else if (MLA_PSTORE == 2 && v[0] == (_Float16)12345.f) *dst = v;   // ablation: no store
-                    }
+                    // a global-space pointer: a generic one would make these
+                    // flat stores, and with a flat operation outstanding the
+                    // compiler's wait counting cannot tell LDS results apart,
+                    // so it drains every LDS read of the score chain
+                    if (head < p.h) ((gh8*)(uintptr_t)obase)[hd * 64 + c8] = v;   // 512 halves a row
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -965,11 +962,15 @@ __global__ __launch_bounds__(256) void mla_decode_kernel(const MlaParams p,
                 }
             } else {
                 // one 16-byte read per pair of steps, PJ pairs ahead; the codes
-                // widen to bf16 exactly just before their product
+                // widen to bf16 exactly just before their product.  With page
+                // scales one pair ahead: the scales' registers would otherwise
+                // push a q^ fragment out to scratch, and its reload inside the
+                // chain makes the compiler wait for all outstanding vector
+                // memory operations, the tile DMA included.
 #ifndef MLA_PJ8
 #define MLA_PJ8 2
 #endif
-                constexpr int PJ = MLA_PJ8, KJ = KS / 2;
+                constexpr int PJ = PS ? 1 : MLA_PJ8, KJ = KS / 2;
                 uint4 raw[PJ];
 #pragma unroll
                 for (int j = 0; j < PJ; j++) raw[j] = *(const uint4*)to8.score(C, j);

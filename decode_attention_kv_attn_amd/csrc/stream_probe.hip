@@ -35,7 +35,10 @@ __global__ __launch_bounds__(256) void stream_probe_kernel(const uint8_t* __rest
     for (int t = 0; t < nt; t++) {
         wait_vmcnt<4 * (kProbeRing - 2)>();   // tile t has landed
         __syncthreads();
-        acc += *(volatile const unsigned*)(L + (t % kProbeRing) * kProbeTile + threadIdx.x * 4);
+        // an LDS-space read: through a generic pointer it would be a flat
+        // load, which the compiler waits for with vmcnt(0), draining the ring
+        acc += *(volatile const __attribute__((address_space(3))) unsigned*)(L + (t % kProbeRing) * kProbeTile +
+                                                                           threadIdx.x * 4);
         issue(t + kProbeRing - 1);            // refills the buffer read one iteration ago
     }
     wait_vmcnt<0>();   // no LDS-DMA may outlive the workgroup

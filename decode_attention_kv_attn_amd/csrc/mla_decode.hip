@@ -602,8 +602,20 @@ struct TileDma {
             r0 = r1 = 0;
             return;
         }
-        r0 = half_row(c.b, c.lt * kT);
-        r1 = half_row(c.b, c.lt * kT + 16);
+        const int t0 = c.lt * kT;
+        if (PAGED) {   // both table entries requested before either is used: one round trip
+            const int32_t* __restrict__ row = btab + (size_t)mla_cache_seq(c.b, p.q_len) * p.max_blocks;
+            const int e0 = row[min(t0 >> p.bs_log2, p.max_blocks - 1)];
+            const int e1 = row[min((t0 + 16) >> p.bs_log2, p.max_blocks - 1)];
+            const int m = (1 << p.bs_log2) - 1;
+            const int b0 = min(max(__builtin_amdgcn_readfirstlane(e0), 0), p.num_blocks - 1);
+            const int b1 = min(max(__builtin_amdgcn_readfirstlane(e1), 0), p.num_blocks - 1);
+            r0 = ((size_t)b0 << p.bs_log2) + (t0 & m);
+            r1 = ((size_t)b1 << p.bs_log2) + ((t0 + 16) & m);
+            return;
+        }
+        r0 = half_row(c.b, t0);
+        r1 = half_row(c.b, t0 + 16);
     }
     // A tile's DMA, prepared (buffer resource and LDS base, wave-uniform)
     // and then issued one instruction at a time, so that the issue can be
